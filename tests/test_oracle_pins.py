@@ -1,0 +1,516 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something it does not compute itself:
+a hand-worked example, a closed form, an invariant, brute force over every
+subset of a tiny input, or a special case that a library routine (numpy,
+scipy, torch CPU) answers exactly. The cases are chosen so that a plausible
+slip -- a dropped 1/G, a wrong head-to-group map, a transposed stride, a
+reversed tie-break, a missing softmax scale -- fails at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from indexer_driven_sparse_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def bits(x):
+    return synth.to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def dec(b):
+    return synth.bf16_bits_to_f32(b).astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# storage rounding
+# --------------------------------------------------------------------------
+
+def _rounding_cases():
+    out = []
+    with open(os.path.join(GOLDEN, "bf16_rounding.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            v, b, why = line.split(None, 2)
+            out.append((float.fromhex(v), int(b, 16), why.strip()))
+    return out
+
+
+@pytest.mark.parametrize("value,expected,why", _rounding_cases())
+def test_bf16_rounding_golden(value, expected, why):
+    assert oracle.round_bf16(value) == expected, why
+
+
+def test_project_keys_rounds_the_exact_sum_once():
+    # k = [1, 1, 0...] so k . W[:, j] = W[0, j] + W[1, j] exactly in double.
+    d, r = 4, 3
+    W = np.zeros((d, r), np.float32)
+    W[0] = [1 + 2**-8, 1 + 2**-8, 1 + 3 * 2**-8]
+    W[1] = [2**-30, 0.0, 0.0]
+    K = np.zeros((1, 1, 1, d), np.float32)
+    K[..., 0:2] = 1.0
+    got = oracle.project_keys(bits(K), W, oracle.BF16)[0, 0, 0]
+    assert [hex(int(x)) for x in got] == ["0x3f81", "0x3f80", "0x3f82"]
+
+
+def test_project_keys_one_hot_rows_and_integer_exactness():
+    rng = np.random.default_rng(0)
+    d, r, T, Hkv = 8, 4, 5, 2
+    # one-hot keys pick rows of W; fp32 W values pass through fp32 storage exactly
+    W = rng.standard_normal((d, r)).astype(np.float32)
+    K = np.zeros((1, T, Hkv, d), np.float32)
+    for t in range(T):
+        for g in range(Hkv):
+            K[0, t, g, (t + 3 * g) % d] = 1.0
+    kf = oracle.project_keys(K, W, oracle.F32)
+    for t in range(T):
+        for g in range(Hkv):
+            np.testing.assert_array_equal(kf[0, g, t], W[(t + 3 * g) % d])
+    # bf16 storage of a one-hot row is the bf16 rounding of W's row (library: fp32 -> bf16 cast)
+    kb = oracle.project_keys(bits(K), W, oracle.BF16)
+    tw = torch.from_numpy(W).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    for t in range(T):
+        for g in range(Hkv):
+            np.testing.assert_array_equal(kb[0, g, t], tw[(t + 3 * g) % d])
+    # small integers: every product and sum is exact, so a library matmul gives the answer
+    Ki = rng.integers(-3, 4, size=(2, T, Hkv, d)).astype(np.float32)
+    Wi = rng.integers(-3, 4, size=(Hkv, d, r)).astype(np.float32)
+    got = oracle.project_keys(Ki, Wi, oracle.F32)
+    for g in range(Hkv):
+        want = np.matmul(Ki[:, :, g, :].astype(np.int64), Wi[g].astype(np.int64))
+        np.testing.assert_array_equal(got[:, g], want.astype(np.float32))
+
+
+def test_project_keys_strided_layout_matches_contiguous():
+    rng = np.random.default_rng(1)
+    N, T, Hkv, d, r = 2, 7, 3, 16, 8
+    Kh = bits(rng.standard_normal((N, Hkv, T, d)))       # [N,Hkv,T,d] storage
+    Kv = Kh.transpose(0, 2, 1, 3)                          # viewed as [N,T,Hkv,d]
+    W = rng.standard_normal((d, r)).astype(np.float32)
+    np.testing.assert_array_equal(oracle.project_keys(Kv, W),
+                                  oracle.project_keys(np.ascontiguousarray(Kv), W))
+
+
+# --------------------------------------------------------------------------
+# worked example (hand-derived, JSSA Fig. 1)
+# --------------------------------------------------------------------------
+
+def test_worked_example():
+    ex = json.load(open(os.path.join(GOLDEN, "worked_example.json")))
+    s = ex["shapes"]
+    Q = np.array(ex["Q"], np.float32)
+    W = np.array(ex["W"], np.float32)
+    K = np.array(ex["K_rows_t"], np.float32).reshape(1, s["T"], 1, s["d"])
+    V = np.array(ex["V_rows_t"], np.float32).reshape(1, s["T"], 1, s["d"])
+    k_idx = oracle.project_keys(K, W, oracle.F32)
+    res = oracle.decode_step(Q, W, k_idx, K, V, s["B"])
+    e = ex["expected"]
+    np.testing.assert_array_equal(res["q_idx"].reshape(-1), e["q_idx"])
+    np.testing.assert_array_equal(res["scores"].reshape(-1), e["scores"])
+    np.testing.assert_array_equal(res["idx"].reshape(-1), e["idx"])
+    for h, (z3, z4) in enumerate(e["logits_per_head"]):
+        w3 = math.exp(z3) / (math.exp(z3) + math.exp(z4))
+        w4 = math.exp(z4) / (math.exp(z3) + math.exp(z4))
+        np.testing.assert_allclose(res["out"][0, h], [w3, w4, 0, 0], rtol=0, atol=1e-15)
+        assert abs(res["lse"][0, h] - math.log(math.exp(z3) + math.exp(z4))) < 1e-15
+
+
+# --------------------------------------------------------------------------
+# scoring preparation: mean of the group's query heads, projected
+# --------------------------------------------------------------------------
+
+def test_query_prep_equal_heads_reduce_to_one_projection():
+    rng = np.random.default_rng(2)
+    N, Hkv, G, d, r = 2, 3, 4, 16, 8
+    q = rng.standard_normal((N, Hkv, 1, d)).astype(np.float32)
+    Q = np.repeat(q, G, axis=2).reshape(N, Hkv * G, d)
+    W = rng.standard_normal((d, r)).astype(np.float32)
+    got = oracle.query_prep(Q, Hkv, W)
+    want = np.matmul(q[:, :, 0].astype(np.float64), W.astype(np.float64))
+    np.testing.assert_allclose(got, want, rtol=1e-14, atol=1e-14)
+
+
+def test_query_prep_group_map_and_mean_not_sum():
+    # Head h of group g carries (g+1) on channel 0 and its within-group rank on
+    # channel 1; W = identity columns. Mean over the group: [(g+1), (G-1)/2].
+    N, Hkv, G, d, r = 1, 4, 4, 8, 2
+    Q = np.zeros((N, Hkv * G, d), np.float32)
+    for h in range(Hkv * G):
+        Q[0, h, 0] = h // G + 1
+        Q[0, h, 1] = h % G
+    W = np.eye(d, r, dtype=np.float32)
+    got = oracle.query_prep(Q, Hkv, W)
+    for g in range(Hkv):
+        np.testing.assert_array_equal(got[0, g], [g + 1, (G - 1) / 2])
+    # per-KV-head projection maps
+    W3 = np.stack([np.eye(d, r, dtype=np.float32) * (g + 1) for g in range(Hkv)])
+    got3 = oracle.query_prep(Q, Hkv, W3)
+    for g in range(Hkv):
+        np.testing.assert_array_equal(got3[0, g], [(g + 1) ** 2, (g + 1) * (G - 1) / 2])
+
+
+# --------------------------------------------------------------------------
+# indexer scores
+# --------------------------------------------------------------------------
+
+def test_scores_one_hot_keys_read_out_query_channels():
+    rng = np.random.default_rng(3)
+    N, Hkv, T, r = 2, 2, 9, 4
+    q = rng.standard_normal((N, Hkv, r))
+    k = np.zeros((N, Hkv, T, r), np.float32)
+    for t in range(T):
+        k[:, :, t, t % r] = 1.0
+    got = oracle.scores(q, k)
+    for t in range(T):
+        np.testing.assert_array_equal(got[:, :, t], q[:, :, t % r])
+
+
+def test_scores_scaled_copies_give_scaled_norms():
+    # k_t = c_t * q with small integers: score_t = c_t * |q|^2 exactly
+    N, Hkv, T, r = 1, 3, 11, 8
+    rng = np.random.default_rng(4)
+    q = rng.integers(-3, 4, size=(N, Hkv, r)).astype(np.float64)
+    c = np.arange(T) - 5
+    k = (c[None, None, :, None] * q[:, :, None, :]).astype(np.float32)
+    got = oracle.scores(q, k)
+    norms = (q * q).sum(-1)
+    np.testing.assert_array_equal(got, c[None, None, :] * norms[:, :, None])
+
+
+def test_scores_candidates_match_full_scores_and_strides():
+    rng = np.random.default_rng(5)
+    N, Hkv, T, r, blk = 2, 2, 256, 8, 16
+    q = rng.standard_normal((N, Hkv, r))
+    store = bits(rng.standard_normal((N, T, Hkv, r)))      # token-major storage
+    k = store.transpose(0, 2, 1, 3)                         # [N,Hkv,T,r] view
+    full = oracle.scores(q, k)
+    np.testing.assert_array_equal(full, oracle.scores(q, np.ascontiguousarray(k)))
+    pos = np.stack([np.sort(rng.choice(T, 10, replace=False)) for _ in range(N * Hkv)])
+    pos = pos.reshape(N, Hkv, 10).astype(np.int32)
+    pos[0, 0, -1] = -1
+    got = oracle.scores(q, k, cand=pos)
+    for n in range(N):
+        for g in range(Hkv):
+            for s, p in enumerate(pos[n, g]):
+                assert got[n, g, s] == (full[n, g, p] if p >= 0 else -np.inf)
+    blocks = np.array([[[3, 0, 15]], [[1, 2, -1]]], np.int32).reshape(N, 1, 3).repeat(Hkv, 1)
+    got = oracle.scores(q, k, cand=blocks, cand_block=blk)
+    for n in range(N):
+        for g in range(Hkv):
+            for s in range(3 * blk):
+                b = blocks[n, g, s // blk]
+                want = full[n, g, b * blk + s % blk] if b >= 0 else -np.inf
+                assert got[n, g, s] == want
+
+
+# --------------------------------------------------------------------------
+# exact top-B selection
+# --------------------------------------------------------------------------
+
+def _brute_force_topk(sc, valid_pos, B):
+    """The unique set S (|S| = min(B, #valid)) such that every member
+    precedes every non-member: higher score, or equal score and lower
+    position; NaN after every number. Found by trying every subset."""
+    def precedes(a, b):
+        sa, sb = sc[a], sc[b]
+        if np.isnan(sa) != np.isnan(sb):
+            return not np.isnan(sa)
+        if not np.isnan(sa) and sa != sb:
+            return sa > sb
+        return a < b
+    k = min(B, len(valid_pos))
+    hits = []
+    for S in itertools.combinations(valid_pos, k):
+        rest = [u for u in valid_pos if u not in S]
+        if all(precedes(s, u) for s in S for u in rest):
+            hits.append(sorted(S))
+    assert len(hits) == 1
+    return hits[0]
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topk_brute_force_tiny(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 10))
+    vals = np.array([-1.0, 0.0, -0.0, 0.5, 2.0, np.nan, -np.inf, np.inf])
+    sc = rng.choice(vals[: 5 if seed % 2 else 8], size=n)
+    B = int(rng.integers(1, n + 3))
+    nv = int(rng.integers(0, n + 1))
+    idx, isc, cnt = oracle.topk(sc[None, :], B, n_valid=np.array([nv], np.int32))
+    want = _brute_force_topk(sc, list(range(nv)), B)
+    assert cnt[0] == len(want)
+    assert list(idx[0, :len(want)]) == want
+    assert all(v == -1 for v in idx[0, len(want):])
+    for j, p in enumerate(want):
+        assert (isc[0, j] == sc[p]) or (np.isnan(isc[0, j]) and np.isnan(sc[p]))
+
+
+def test_topk_matches_library_sort_on_random_rows():
+    # lexsort ranks by (score desc, position asc); its first B, sorted, is the set
+    rng = np.random.default_rng(6)
+    rows, n, B = 6, 5000, 300
+    sc = rng.integers(-40, 40, size=(rows, n)).astype(np.float64)   # many exact ties
+    idx, isc, cnt = oracle.topk(sc, B)
+    for i in range(rows):
+        order = np.lexsort((np.arange(n), -sc[i]))
+        np.testing.assert_array_equal(idx[i], np.sort(order[:B]))
+        np.testing.assert_array_equal(isc[i], sc[i, np.sort(order[:B])])
+    assert (cnt == B).all()
+
+
+def test_topk_closed_forms():
+    n = 50
+    eq = np.full((1, n), 3.25)
+    np.testing.assert_array_equal(oracle.topk(eq, 7)[0][0], np.arange(7))       # all equal
+    sc = np.random.default_rng(7).standard_normal((3, n))
+    idx, _, cnt = oracle.topk(sc, n + 5)                                         # B > n
+    np.testing.assert_array_equal(idx[:, :n], np.tile(np.arange(n), (3, 1)))
+    assert (idx[:, n:] == -1).all() and (cnt == n).all()
+    sc[1, [4, 9]] = sc[1].max() + 1                                              # B = 1: argmax, lowest
+    np.testing.assert_array_equal(oracle.topk(sc, 1)[0][:, 0], np.argmax(sc, axis=1))
+    idx, _, _ = oracle.topk(np.array([[-0.0, 0.0, -0.0]]), 1)                    # -0 == +0
+    assert idx[0, 0] == 0
+
+
+def test_topk_causal_and_candidates():
+    rng = np.random.default_rng(8)
+    L, B = 40, 6
+    sc = rng.standard_normal((L, L))
+    idx, _, cnt = oracle.topk(sc, B, causal_group=1)
+    for i in range(L):
+        want = _brute_force_topk(sc[i], list(range(i + 1)), B) if i < 8 else \
+            sorted(np.lexsort((np.arange(i + 1), -sc[i, :i + 1]))[:B])
+        assert list(idx[i, :cnt[i]]) == list(want)
+        assert cnt[i] == min(B, i + 1)
+    # candidate map: slot -> position, ties broken by position; -1 slots never chosen
+    sc = np.array([[1.0, 5.0, 5.0, 2.0, 9.0, 5.0]])
+    cand = np.array([[10, 3, -1]], np.int32)                   # blocks of 2 tokens
+    idx, isc, cnt = oracle.topk(sc, 3, cand=cand, cand_block=2, n_positions=100)
+    # slots -> positions [20,21,6,7,-,-]; scores [1,5,5,2]; top-3: 21(5), 6(5), 7(2)
+    np.testing.assert_array_equal(idx[0], [6, 7, 21])
+    assert cnt[0] == 3
+    idx, _, cnt = oracle.topk(sc, 3, cand=cand, cand_block=2, n_positions=21)  # position 21 invalid
+    np.testing.assert_array_equal(idx[0], [6, 7, 20])
+
+
+# --------------------------------------------------------------------------
+# indexed attention
+# --------------------------------------------------------------------------
+
+def _dense_sdpa(q, K, V):
+    """Library dense attention (torch CPU, float64), GQA by repeating heads."""
+    N, Hq, d = q.shape
+    Hkv = K.shape[2]
+    G = Hq // Hkv
+    qt = torch.from_numpy(q).double()[:, :, None, :]                   # [N,Hq,1,d]
+    Kt = torch.from_numpy(K).double().permute(0, 2, 1, 3)               # [N,Hkv,T,d]
+    Vt = torch.from_numpy(V).double().permute(0, 2, 1, 3)
+    Kt = Kt.repeat_interleave(G, dim=1).contiguous()
+    Vt = Vt.repeat_interleave(G, dim=1).contiguous()
+    o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt)
+    z = (qt @ Kt.transpose(-1, -2).contiguous())[:, :, 0, :] / math.sqrt(d)
+    lse = scipy.special.logsumexp(z.numpy(), axis=-1)
+    return o[:, :, 0, :].numpy(), lse
+
+
+@pytest.mark.parametrize("dtype", [oracle.F32, oracle.BF16])
+def test_attention_full_index_set_is_dense_attention(dtype):
+    rng = np.random.default_rng(9)
+    N, Hq, Hkv, T, d = 2, 8, 2, 37, 16
+    q = rng.standard_normal((N, Hq, d)).astype(np.float32)
+    K = rng.standard_normal((N, T, Hkv, d)).astype(np.float32)
+    V = rng.standard_normal((N, T, Hkv, d)).astype(np.float32)
+    if dtype == oracle.BF16:
+        q, K, V = bits(q), bits(K), bits(V)
+        qd, Kd, Vd = dec(q), dec(K), dec(V)
+    else:
+        qd, Kd, Vd = q.astype(np.float64), K.astype(np.float64), V.astype(np.float64)
+    idx = np.tile(rng.permutation(T).astype(np.int32), (N, Hkv, 1))    # order must not matter
+    out, lse = oracle.attention(q, K, V, idx)
+    o_ref, lse_ref = _dense_sdpa(qd, Kd, Vd)
+    np.testing.assert_allclose(out, o_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, lse_ref, rtol=0, atol=1e-12)
+
+
+def test_attention_closed_forms():
+    rng = np.random.default_rng(10)
+    N, Hq, Hkv, T, d, B = 1, 4, 2, 20, 8, 5
+    q = rng.standard_normal((N, Hq, d)).astype(np.float32)
+    K = rng.standard_normal((N, T, Hkv, d)).astype(np.float32)
+    V = rng.standard_normal((N, T, Hkv, d)).astype(np.float32)
+    G = Hq // Hkv
+    # B = 1: the output is that V row, lse its logit
+    idx = np.full((N, Hkv, B), -1, np.int32)
+    idx[0, :, 2] = [7, 11]
+    out, lse = oracle.attention(q, K, V, idx)
+    for h in range(Hq):
+        t = [7, 11][h // G]
+        np.testing.assert_allclose(out[0, h], V[0, t, h // G], rtol=0, atol=1e-15)
+        z = float(np.dot(q[0, h].astype(np.float64), K[0, t, h // G].astype(np.float64))) / math.sqrt(d)
+        assert abs(lse[0, h] - z) < 1e-12
+    # q = 0: uniform weights -> mean of the selected V, lse = log |S|
+    sel = np.array([[[1, 4, 9, -1, 19], [0, 2, 3, 5, 8]]], np.int32)
+    out, lse = oracle.attention(np.zeros_like(q), K, V, sel)
+    for h in range(Hq):
+        g = h // G
+        S = [t for t in sel[0, g] if t >= 0]
+        np.testing.assert_allclose(out[0, h], V[0, S, g].astype(np.float64).mean(0), atol=1e-15)
+        assert abs(lse[0, h] - math.log(len(S))) < 1e-15
+    # empty set: o = 0, lse = -inf; out-of-range entries are skipped
+    empty = np.array([[[-1, -1, T, -5, 10**6]] * Hkv], np.int32)
+    out, lse = oracle.attention(q, K, V, empty)
+    assert (out == 0).all() and np.isneginf(lse).all()
+    # an explicit scale replaces 1/sqrt(d): doubling q with scale/2 changes nothing
+    a1 = oracle.attention(q, K, V, sel)
+    a2 = oracle.attention(2 * q, K, V, sel, scale=0.5 / math.sqrt(d))
+    np.testing.assert_allclose(a1[0], a2[0], atol=1e-14)
+
+
+def test_attention_prefill_rows_read_sequence_zero_and_layouts_agree():
+    rng = np.random.default_rng(11)
+    L, Hq, Hkv, d, B = 12, 4, 1, 8, 4
+    q = bits(rng.standard_normal((L, Hq, d)))
+    Kh = bits(rng.standard_normal((1, Hkv, L, d)))                     # head-major storage
+    Vh = bits(rng.standard_normal((1, Hkv, L, d)))
+    K, V = Kh.transpose(0, 2, 1, 3), Vh.transpose(0, 2, 1, 3)
+    idx = np.full((L, Hkv, B), -1, np.int32)
+    for i in range(L):
+        s = np.arange(max(0, i - B + 1), i + 1)
+        idx[i, 0, :len(s)] = s
+    out, lse = oracle.attention(q, K, V, idx, prefill=True)
+    out2, lse2 = oracle.attention(q, np.ascontiguousarray(K), np.ascontiguousarray(V), idx, prefill=True)
+    np.testing.assert_array_equal(out, out2)
+    # each row equals a one-sequence decode over the same set
+    for i in range(L):
+        o1, l1 = oracle.attention(q[i:i + 1], K, V, idx[i:i + 1])
+        np.testing.assert_array_equal(out[i], o1[0])
+        np.testing.assert_array_equal(lse[i], l1[0])
+    # row 0 attends only to token 0
+    np.testing.assert_allclose(out[0], np.repeat(dec(V[0, 0]), Hq, 0), atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# hierarchical indexing and centroids
+# --------------------------------------------------------------------------
+
+def test_centroids_closed_forms():
+    N, Hkv, T, r, blk = 1, 2, 10, 4, 4
+    k = np.zeros((N, Hkv, T, r), np.float32)
+    for t in range(T):
+        k[0, :, t, :] = t // blk + 0.5       # constant per block
+    c = oracle.centroids(k, blk)
+    assert c.shape == (N, Hkv, 3, r)
+    np.testing.assert_array_equal(c[0, 0, :, 0], [0.5, 1.5, 2.5])
+    k2 = np.arange(N * Hkv * T * r, dtype=np.float32).reshape(N, Hkv, T, r)
+    c2 = oracle.centroids(k2, blk)
+    np.testing.assert_array_equal(c2[0, 1, 2], k2[0, 1, 8:10].mean(0))   # partial block: mean of 2
+    kb = bits(k)
+    np.testing.assert_array_equal(oracle.centroids(kb, blk), bits(c))
+
+
+def test_centroid_scores_are_means_of_token_scores():
+    rng = np.random.default_rng(12)
+    N, Hkv, T, r, blk = 1, 2, 512, 16, 64
+    q = rng.standard_normal((N, Hkv, r))
+    k = rng.standard_normal((N, Hkv, T, r)).astype(np.float32)
+    c = oracle.centroids(k, blk)                 # fp32 storage: one rounding per channel
+    cs = oracle.scores(q, c)
+    ts = oracle.scores(q, k).reshape(N, Hkv, T // blk, blk).mean(-1)
+    bound = 2**-24 * np.abs(q).sum(-1)[..., None] * np.abs(c).max() * 2
+    assert (np.abs(cs - ts) <= bound).all()
+
+
+def test_hierarchical_reduces_to_flat_when_every_block_is_kept():
+    case = synth.make_decode_case(N=1, Hq=8, Hkv=2, T=1024, d=32, r=16, B=64, plant="spans",
+                                  n_spans=4, span=16, seed=13)
+    k_idx = oracle.project_keys(case.K, case.W)
+    cent = oracle.centroids(k_idx, 64)
+    flat = oracle.decode_step(case.Q, case.W, k_idx, case.K, case.V, case.B)
+    hier = oracle.hierarchical_decode_step(case.Q, case.W, k_idx, cent, case.K, case.V, 64,
+                                           1024 // 64, case.B)
+    np.testing.assert_array_equal(flat["idx"], hier["idx"])
+    np.testing.assert_array_equal(flat["out"], hier["out"])
+    # fewer kept blocks: the final set lies inside the kept blocks and is the
+    # exact top-B of their union
+    hier = oracle.hierarchical_decode_step(case.Q, case.W, k_idx, cent, case.K, case.V, 64, 4, case.B)
+    for g in range(2):
+        kept = set()
+        for b in hier["blocks"][0, g]:
+            kept.update(range(b * 64, b * 64 + 64))
+        sel = hier["idx"][0, g]
+        assert set(sel.tolist()) <= kept
+        pos = np.array(sorted(kept))
+        sc = flat["scores"][0, g, pos]
+        order = np.lexsort((pos, -sc))
+        np.testing.assert_array_equal(sel, np.sort(pos[order[:case.B]]))
+
+
+# --------------------------------------------------------------------------
+# causal prefill indexer
+# --------------------------------------------------------------------------
+
+def test_prefill_rows_are_prefix_decodes():
+    case = synth.make_prefill_case(L=300, Hq=4, Hkv=2, d=32, r=16, B=20, seed=14)
+    idx, isc = oracle.prefill_topk(case.q_idx, case.k_idx, case.B)
+    full = oracle.prefill_scores(case.q_idx, case.k_idx)
+    for i in [0, 1, 5, 19, 20, 21, 150, 299]:
+        for g in range(2):
+            n = i + 1
+            if n <= case.B:
+                np.testing.assert_array_equal(idx[i, g, :n], np.arange(n))      # whole prefix
+                assert (idx[i, g, n:] == -1).all()
+            assert idx[i, g].max() <= i
+            qd = dec(case.q_idx[i, g])[None, None, :]
+            kd = case.k_idx[:n, g][None, None]                                  # [1,1,n,r]
+            sc = oracle.scores(qd, kd)[0, 0]
+            np.testing.assert_array_equal(sc, full[i, g, :n])
+            assert np.isneginf(full[i, g, n:]).all()
+            order = np.lexsort((np.arange(n), -sc))
+            want = np.sort(order[:min(case.B, n)])
+            np.testing.assert_array_equal(idx[i, g, :len(want)], want)
+    # a row range equals the same rows of the full run
+    part, _ = oracle.prefill_topk(case.q_idx, case.k_idx, case.B, 100, 130)
+    np.testing.assert_array_equal(part, idx[100:130])
+
+
+# --------------------------------------------------------------------------
+# whole decode step: invariants
+# --------------------------------------------------------------------------
+
+def test_decode_step_with_budget_T_is_dense_attention():
+    case = synth.make_decode_case(N=2, Hq=8, Hkv=2, T=96, d=32, r=16, B=96, seed=15)
+    k_idx = oracle.project_keys(case.K, case.W)
+    res = oracle.decode_step(case.Q, case.W, k_idx, case.K, case.V, case.B)
+    o_ref, lse_ref = _dense_sdpa(dec(case.Q), dec(case.K), dec(case.V))
+    np.testing.assert_allclose(res["out"], o_ref, atol=1e-12)
+    np.testing.assert_allclose(res["lse"], lse_ref, atol=1e-12)
+
+
+def test_decode_step_recovers_strongly_planted_spans():
+    # +16 sigma along the mean query: the planted tokens outscore every other
+    case = synth.make_decode_case(N=1, Hq=8, Hkv=2, T=4096, d=64, r=32, B=256, plant="spans",
+                                  plant_sigma=16.0, n_spans=8, span=32, seed=16)
+    k_idx = oracle.project_keys(case.K, case.W)
+    res = oracle.decode_step(case.Q, case.W, k_idx, case.K, case.V, case.B)
+    for g in range(2):
+        np.testing.assert_array_equal(res["idx"][0, g], case.planted[g])
+
+
+def test_generators_are_deterministic():
+    a = synth.workload("decode_t4k_fp32", T=256)
+    b = synth.workload("decode_t4k_fp32", T=256)
+    for x, y in [(a.Q, b.Q), (a.K, b.K), (a.V, b.V), (a.W, b.W)]:
+        np.testing.assert_array_equal(x, y)
+    c = synth.workload("decode_t32k_hitters", T=2048)
+    assert c.K.dtype == np.uint16 and len(c.planted) == 8
+    assert all(len(p) == round(0.01 * 2048) for p in c.planted)
