@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of indexer-driven sparse attention on one MI355X.
+
+Workload: decode, 4 sequences x 131072 cached tokens, GQA 32 query / 8 KV
+heads, head_dim 128, projected rank r=64, top-B = 2048 per KV head (the
+1.5625% budget), bf16 caches, seeded synthetic inputs with 64 planted hot
+spans of 32 tokens per KV head.
+
+A step is the whole hot path for all sequences and heads of one layer:
+scoring preparation + projected-key scoring (one kernel), exact top-B
+selection, indexed attention (+ its split merge). Inputs are resident in HBM
+before timing starts. Two identical cache instances are alternated step by
+step, so no step finds its 2.5 GiB working set in the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout; diagnostics go to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn decode steps/s at 128K,B=2048; indexer keys scored/s; % HBM peak"
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "decode_t128k_b2048"
+SCORE_SOURCES = ["indexer_driven_sparse_amd/csrc/score.hip", "indexer_driven_sparse_amd/csrc/common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_decode_t128k_pmc.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(launch_bytes: int):
+    """HBM bytes per scoring launch from the committed rocprofv3 counter runs,
+    or None when they are missing or the kernel changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash(SCORE_SOURCES):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def to_dev(a, torch):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="wall time budget of the CPU-oracle baseline (0 disables it)")
+    ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing loops")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path shards "
+              "by KV head or sequence with no collective inside the step.", file=sys.stderr)
+        return 2
+
+    import torch
+    from indexer_driven_sparse_amd import lsa, pipeline, synth
+
+    if not torch.cuda.is_available():
+        log("no GPU")
+        return 1
+    dev_name = torch.cuda.get_device_name(0)
+    log(f"device: {dev_name}; library: {lsa.library_path()}")
+
+    t0 = time.time()
+    case = synth.workload(WORKLOAD)
+    log(f"generated inputs in {time.time() - t0:.1f}s")
+    N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
+
+    # two cache instances resident in HBM (identical content, distinct memory)
+    Q, W = to_dev(case.Q, torch), to_dev(case.W, torch)
+    inst = []
+    for _ in range(2):
+        K, V = to_dev(case.K, torch), to_dev(case.V, torch)
+        k_idx = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+        lsa.lsa_project_keys(K, W, k_idx)
+        inst.append((K, V, k_idx))
+    torch.cuda.synchronize()
+    plan = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        K, V, k_idx = inst[i & 1]
+        plan.run(Q, W, k_idx, K, V)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, HIP events around every scoring launch on the
+    # stream the kernels run on
+    steps = args.steps
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        K, V, k_idx = inst[i & 1]
+        ev_s[i].record(stream)
+        plan.score(Q, W, k_idx)
+        ev_e[i].record(stream)
+        plan.select()
+        plan.attend(Q, K, V)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / steps
+    score_ms = float(np.mean([ev_s[i].elapsed_time(ev_e[i]) for i in range(steps)]))
+
+    keys = N * Hkv * T
+    kidx_bytes = keys * r * 2
+    sel_kv_bytes = N * Hkv * B * 2 * d * 2
+    step_bytes = kidx_bytes + sel_kv_bytes + N * Hkv * B * 4 + (N * Hq * d * 2 + N * Hq * d * 4 +
+                                                                 N * Hkv * r * 4)
+    steps_per_s = 1000.0 / ms_per_step
+    score_gbps = kidx_bytes / (score_ms * 1e-3) / 1e9
+
+    stages = None
+    if not args.no_stages:
+        def time_loop(fn, n=100):
+            for i in range(10):
+                fn(i)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(n):
+                fn(i)
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n * 1000.0
+
+        stages = {
+            "score_us": time_loop(lambda i: plan.score(Q, W, inst[i & 1][2])),
+            "select_us": time_loop(lambda i: plan.select()),
+            "attention_us": time_loop(lambda i: plan.attend(Q, inst[i & 1][0], inst[i & 1][1])),
+        }
+        stages["attended_kv_GBps"] = sel_kv_bytes / (stages["attention_us"] * 1e-6) / 1e9
+
+    # the step's outputs on instance 0, for the parity check in the CPU leg
+    step(0)
+    torch.cuda.synchronize()
+    gpu_idx = plan.idx.cpu().numpy()
+    gpu_out = plan.out.cpu().numpy()
+
+    cpu = None
+    parity = None
+    if args.cpu_seconds > 0:
+        import oracle
+        threads = len(os.sched_getaffinity(0))
+        oracle.set_threads(threads)
+        ref_k = oracle.project_keys(case.K, case.W, oracle.BF16)        # setup, untimed
+        t0 = time.time()
+        n_done = 0
+        ref = None
+        while n_done == 0 or time.time() - t0 < args.cpu_seconds:
+            ref = oracle.decode_step(case.Q, case.W, ref_k, case.K, case.V, B)
+            n_done += 1
+        el = time.time() - t0
+        cpu = {"value": n_done / el, "unit": "steps/s", "cores": threads, "kind": "oracle",
+               "sample": f"{n_done} full steps of the same workload (all 32 sequence x KV-head rows, "
+                         f"fp64) in {el:.1f}s on {platform.processor() or platform.machine()}",
+               "keys_scored_per_s": n_done * keys / el}
+        # parity of the timed configuration against the oracle
+        same = int(sum(np.array_equal(gpu_idx[n, g], ref["idx"][n, g])
+                       for n in range(N) for g in range(Hkv)))
+        err = float(np.abs(gpu_out - ref["out"]).max()) if same == N * Hkv else None
+        parity = {"rows_identical_sets": same, "rows": N * Hkv, "max_abs_out_err": err,
+                  "pass": same == N * Hkv and err is not None and err <= 2e-3}
+        log(f"cpu oracle: {cpu['value']:.3f} steps/s on {threads} threads; parity {parity}")
+
+    traffic = measured_traffic(kidx_bytes)
+    line = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode, 4 sequences x 131072 cached tokens, GQA 32/8, d=128, "
+                               "r=64, top-B=2048, bf16, 64 hot spans of 32 tokens per KV head",
+                   "N": N, "T": T, "Hq": Hq, "Hkv": Hkv, "d": d, "r": r, "B": B,
+                   "parallelism": "single GPU"},
+        "keys_scored_per_s": keys * steps_per_s,
+        "hbm_frac_end_to_end": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBPS * 1e9),
+        "algorithmic_bytes_per_step": step_bytes,
+        "roofline": {"kernel": "score_decode_kernel (scoring prep + projected-key scoring)",
+                     "bound": "hbm", "achieved": score_gbps, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
+                     "avg_launch_us": score_ms * 1000.0,
+                     "traffic": traffic},
+        "stages": stages,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "device": dev_name,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,312 @@
+/*
+ * lsa.h -- C ABI of liblsa: indexer-driven sparse attention on AMD MI355X
+ * (gfx950, CDNA4).
+ *
+ * The hot path has three calls, in this order for one decode step:
+ *
+ *   lsa_index_score        a cheap indexer scores every cached key: the mean
+ *                          of a KV head's query heads, projected to r dims,
+ *                          dotted with a projected-key cache (JSSA Fig. 1;
+ *                          Fig. 9 "scoring preparation" and "candidate
+ *                          scoring"). Also the causal prefill indexer (LongCat
+ *                          Sparse Attention abstract: O(L^2) indexer scoring)
+ *                          and the fine pass of coarse-to-fine indexing
+ *                          (same abstract, item 3).
+ *   lsa_topk_select        exact top-B positions per row, lowest position on
+ *                          ties (JSSA Fig. 1; Fig. 9 "top-B selection").
+ *   lsa_indexed_attention  every query head of a GQA group attends only to
+ *                          its KV head's selected positions, read in place
+ *                          from the standard KV-cache layout with no gathered
+ *                          copy (JSSA Key contributions; Fig. 6).
+ *
+ * Setup calls (outside the step): lsa_project_keys builds or appends to the
+ * projected-key cache, lsa_build_centroids builds the block summaries the
+ * coarse pass scores.
+ *
+ * Sources: JSSA = "Joint Subspace Sparse Attention for Efficient
+ * Long-Context Decoding"; LongCat = "LongCat Sparse Attention: Taming the
+ * Lightning via Streaming-aware Hierarchical Cross-Layer Indexing".
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees, synchronises or reads back to the host.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream of the current device) and can be captured in a HIP graph.
+ *   - Every argument is validated BEFORE anything is launched; on any error
+ *     nothing is launched and no output is touched.
+ *   - Outputs are fully overwritten (padding included); callers never clear
+ *     them first. Identical inputs give bit-identical outputs.
+ *   - Strides are in ELEMENTS. Rows read with 128-bit loads need a 16-byte
+ *     aligned base and row strides that are multiples of 16 bytes;
+ *     misalignment is rejected (there is no slow path).
+ *   - Query head h belongs to KV head h / (Hq / Hkv).
+ *   - Reentrant and thread-safe; the only global state is a per-device cache
+ *     of "is this a gfx950" answers.
+ *   - Return value: LSA_OK (0) or a negative lsa_status. After LSA_ERR_HIP,
+ *     lsa_last_hip_error() gives the HIP error code (thread-local).
+ */
+#ifndef LSA_H_
+#define LSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSA_ABI_VERSION 1
+
+/* Storage dtypes. */
+enum { LSA_F32 = 0, LSA_BF16 = 1 };
+
+/* Status codes. */
+enum {
+  LSA_OK = 0,
+  LSA_ERR_INVALID_ARG = -1,    /* null/misaligned pointer, bad size or stride */
+  LSA_ERR_UNSUPPORTED = -2,    /* valid but not built: dtype combo, r, d, G */
+  LSA_ERR_WORKSPACE = -3,      /* workspace missing or smaller than required */
+  LSA_ERR_NO_DEVICE_CODE = -4, /* current device is not gfx950 */
+  LSA_ERR_HIP = -5             /* a HIP call failed; see lsa_last_hip_error */
+};
+
+/* Modes. Decode: a row is one (sequence, KV head). Prefill: a row is one
+ * (query token, KV head) of a single sequence, row index i*Hkv + g. */
+enum { LSA_MODE_DECODE = 0, LSA_MODE_PREFILL_CAUSAL = 1 };
+
+/* ------------------------------------------------------------------------ */
+/* lsa_index_score                                                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * Decode (JSSA Fig. 1): for row (n, g)
+ *     q_idx[n,g,:] = ( (1/G) sum_{i<G} q[n, g*G+i, :] ) . W          (prep)
+ *     scores[row, s] = q_idx[n,g,:] . k_idx[n, g, pos(s), :]          (scoring)
+ *   pos(s) = s for s < n_keys when cand is NULL. With cand, slot s covers
+ *   token cand[row, s / cand_block] * cand_block + s % cand_block
+ *   (cand_block = 1: a position list; cand_block > 1: block ids, the fine
+ *   pass of coarse-to-fine indexing, LongCat abstract item 3); n_cand *
+ *   cand_block slots are written and a slot whose entry is negative or
+ *   whose token is >= n_keys scores -inf. Candidate lists must be strictly
+ *   increasing per row (lsa_topk_select breaks ties in slot order).
+ *   The prep runs inside the scoring kernel when `q` is given (then q_idx,
+ *   if not NULL, receives the fp32 q_idx); otherwise q_idx [N,Hkv,r] fp32
+ *   is read.
+ *
+ * Prefill (LongCat abstract: the indexer's O(L^2) causal scoring):
+ *     S[i,g,j] = q_idx[i,g,:] . k_idx[j,g,:] for j <= i (n_seq must be 1,
+ *   q_idx [L,Hkv,r] in k_idx_dtype, k_idx read through its strides). With
+ *   topk == 0 the full rows are written to scores ([L*Hkv, scores_ld], -inf
+ *   above the diagonal). With topk = B > 0 the selection is fused into the
+ *   scoring and no score matrix is written: out_idx [L,Hkv,B] gets exactly
+ *   what lsa_topk_select would give on the causal rows, and out_score (if
+ *   not NULL) the matching scores. Needs workspace
+ *   (lsa_score_workspace_bytes).
+ *
+ * Accumulation is fp32 over exact products of the stored values.
+ */
+typedef struct lsa_score_desc {
+  uint32_t struct_size;      /* sizeof(lsa_score_desc) */
+  int32_t mode;              /* LSA_MODE_* */
+  int32_t n_seq;             /* N (decode); 1 (prefill) */
+  int32_t n_kv_heads;        /* Hkv >= 1 */
+  int32_t n_keys;            /* T cached positions (decode); L (prefill) */
+  int32_t rank;              /* r; r * element size in {16,32,64,128,256} bytes */
+
+  void* q_idx;               /* see above */
+  const void* q;             /* decode prep input [N,Hq,d] contiguous, or NULL */
+  int32_t q_dtype;           /* LSA_F32 / LSA_BF16 */
+  int32_t n_q_heads;         /* Hq, a multiple of Hkv (with q) */
+  int32_t head_dim;          /* d <= 512 (with q) */
+  int32_t w_per_head;        /* 0: w is [d,r]; 1: w is [Hkv,d,r] */
+  const float* w;            /* fp32 projection (with q) */
+
+  const void* k_idx;         /* projected-key cache, innermost r contiguous */
+  int32_t k_idx_dtype;       /* LSA_F32 / LSA_BF16 */
+  int32_t reserved0;
+  int64_t k_stride_seq;      /* decode: between sequences */
+  int64_t k_stride_head;     /* between KV heads */
+  int64_t k_stride_tok;      /* between positions */
+
+  const int32_t* cand;       /* decode candidate list [N*Hkv, cand_ld] or NULL */
+  int32_t n_cand;
+  int32_t cand_block;        /* >= 1 */
+  int64_t cand_ld;
+
+  float* scores;             /* fp32 [rows, scores_ld] */
+  int64_t scores_ld;
+
+  int32_t topk;              /* prefill fused selection budget B, or 0 */
+  int32_t reserved1;
+  int32_t* out_idx;          /* prefill fused: [L,Hkv,B] ascending, -1 padded */
+  float* out_score;          /* prefill fused: [L,Hkv,B] or NULL */
+} lsa_score_desc;
+
+int lsa_index_score(const lsa_score_desc* desc, void* workspace, size_t workspace_bytes,
+                    void* stream);
+size_t lsa_score_workspace_bytes(const lsa_score_desc* desc);
+
+/* ------------------------------------------------------------------------ */
+/* lsa_topk_select                                                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * Per row, the min(B, #valid) valid slots that come first in the order
+ * (higher score first; equal scores -- +0 and -0 are equal -- to the lower
+ * slot; NaN after every number), i.e. the top-B token positions of JSSA
+ * Fig. 1 with lowest-index tie-break. Their positions are written in
+ * ascending order to out_idx[row, 0..count), then -1 up to B.
+ *
+ * Valid slots: s < n_valid[row] (all n when n_valid is NULL); with
+ * causal_group = k > 0, s < min(n, row / k + 1) instead (causal prefill rows
+ * i*Hkv + g use k = Hkv). With cand, slot s maps to a token as in
+ * lsa_index_score and is valid only if that token is in [0, n_positions);
+ * the map must be increasing so slot order is position order.
+ *
+ * out_score[row, j] (optional) is the score of out_idx[row, j], -inf for
+ * padding; out_count[row] (optional) is the number selected. Exact integer
+ * work on order-preserving 32-bit keys of the fp32 scores: the result does
+ * not depend on launch shape. Rows longer than 262144 slots use workspace.
+ */
+typedef struct lsa_select_desc {
+  uint32_t struct_size;      /* sizeof(lsa_select_desc) */
+  int32_t rows;
+  int32_t n;                 /* slots per row */
+  int32_t topk;              /* B >= 1 */
+  const float* scores;       /* [rows, scores_ld] */
+  int64_t scores_ld;
+  const int32_t* n_valid;    /* [rows] or NULL */
+  int32_t causal_group;      /* 0 or k > 0 */
+  int32_t cand_block;        /* >= 1 (with cand) */
+  const int32_t* cand;       /* [rows, cand_ld] or NULL */
+  int64_t cand_ld;
+  int32_t n_positions;       /* with cand: tokens >= n_positions are invalid */
+  int32_t reserved0;
+  int32_t* out_idx;          /* [rows, B] */
+  float* out_score;          /* [rows, B] or NULL */
+  int32_t* out_count;        /* [rows] or NULL */
+} lsa_select_desc;
+
+int lsa_topk_select(const lsa_select_desc* desc, void* workspace, size_t workspace_bytes,
+                    void* stream);
+size_t lsa_select_workspace_bytes(const lsa_select_desc* desc);
+
+/* ------------------------------------------------------------------------ */
+/* lsa_indexed_attention                                                    */
+/* ------------------------------------------------------------------------ */
+/*
+ * For each row and query head h (KV head g = h / G):
+ *     z_t = scale * q[row,h,:] . K[seq, t, g, :]      for t in idx[row,g,:]
+ *     out[row,h,:] = sum_t softmax(z)_t V[seq, t, g, :]
+ *     lse[row,h]   = log sum_t exp(z_t)
+ * Entries outside [0, n_keys) (e.g. the -1 padding) are skipped; an empty
+ * set gives out = 0 and lse = -inf. Decode: seq = row. Prefill: seq = 0 for
+ * every row. K and V rows are read in place through their strides (the
+ * standard [N,T,Hkv,d] cache, or [N,Hkv,T,d]); nothing is gathered into a
+ * copy (JSSA Key contributions; Fig. 6). Online softmax with fp32
+ * accumulation; idx entries of one row must be distinct. Long index lists
+ * are split across workgroups and merged by log-sum-exp, which needs
+ * workspace (lsa_attention_workspace_bytes).
+ */
+typedef struct lsa_attn_desc {
+  uint32_t struct_size;      /* sizeof(lsa_attn_desc) */
+  int32_t mode;              /* LSA_MODE_* */
+  int32_t rows;              /* N (decode) or L (prefill) */
+  int32_t n_q_heads;         /* Hq */
+  int32_t n_kv_heads;        /* Hkv; G = Hq/Hkv in {1,2,4,8,16} */
+  int32_t head_dim;          /* d in {64, 128} */
+  int32_t topk;              /* B >= 1: entries per (row, KV head) */
+  int32_t n_keys;            /* T */
+  const void* q;             /* [rows,Hq,d] contiguous, q_dtype */
+  int32_t q_dtype;
+  int32_t kv_dtype;          /* K and V share dtype and strides */
+  const void* k;
+  const void* v;
+  int64_t kv_stride_seq;
+  int64_t kv_stride_tok;
+  int64_t kv_stride_head;
+  const int32_t* idx;        /* [rows, Hkv, B] int32 */
+  float scale;               /* <= 0: 1/sqrt(d) */
+  int32_t reserved0;
+  float* out;                /* fp32 [rows,Hq,d] */
+  float* lse;                /* fp32 [rows,Hq] or NULL */
+} lsa_attn_desc;
+
+int lsa_indexed_attention(const lsa_attn_desc* desc, void* workspace, size_t workspace_bytes,
+                          void* stream);
+size_t lsa_attention_workspace_bytes(const lsa_attn_desc* desc);
+
+/* ------------------------------------------------------------------------ */
+/* Setup calls                                                              */
+/* ------------------------------------------------------------------------ */
+/*
+ * lsa_project_keys: out[n,g,t,:] = round(K[n,t,g,:] . W) for tokens t in
+ * [tok_begin, tok_begin + n_tok) -- building the projected-key cache, or
+ * appending the newest token's projected key (JSSA Fig. 9 calls the key
+ * projection negligible). The sum is exact-product fp64, rounded once to
+ * out_dtype (round to nearest even), so the result equals a double-precision
+ * reference bit for bit.
+ */
+typedef struct lsa_project_desc {
+  uint32_t struct_size;      /* sizeof(lsa_project_desc) */
+  int32_t n_seq;
+  int32_t n_kv_heads;
+  int32_t head_dim;          /* d <= 512 */
+  int32_t rank;              /* r <= 256 */
+  int32_t tok_begin;
+  int32_t n_tok;
+  int32_t k_dtype;
+  const void* k;             /* K cache, innermost d contiguous */
+  int64_t k_stride_seq;
+  int64_t k_stride_tok;
+  int64_t k_stride_head;
+  const float* w;            /* [d,r] or [Hkv,d,r] fp32 */
+  int32_t w_per_head;
+  int32_t out_dtype;
+  void* out;                 /* projected-key cache, innermost r contiguous */
+  int64_t out_stride_seq;
+  int64_t out_stride_head;
+  int64_t out_stride_tok;
+} lsa_project_desc;
+
+int lsa_project_keys(const lsa_project_desc* desc, void* stream);
+
+/*
+ * lsa_build_centroids: out[n,g,b,:] = round(mean of in[n,g,t,:] over the
+ * tokens t of block b), blocks of `block` tokens, a partial last block
+ * averaged over its tokens -- the block summaries scored by the coarse pass
+ * of hierarchical indexing (LongCat abstract item 3). fp64 sum, one rounding.
+ */
+typedef struct lsa_centroid_desc {
+  uint32_t struct_size;      /* sizeof(lsa_centroid_desc) */
+  int32_t n_seq;
+  int32_t n_kv_heads;
+  int32_t n_keys;            /* T */
+  int32_t rank;              /* r <= 256 */
+  int32_t block;             /* >= 1 */
+  int32_t dtype;             /* of both in and out */
+  const void* in;            /* projected-key cache */
+  int64_t in_stride_seq;
+  int64_t in_stride_head;
+  int64_t in_stride_tok;
+  void* out;                 /* [.., ceil(T/block), r] */
+  int64_t out_stride_seq;
+  int64_t out_stride_head;
+  int64_t out_stride_blk;
+} lsa_centroid_desc;
+
+int lsa_build_centroids(const lsa_centroid_desc* desc, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Helpers                                                                  */
+/* ------------------------------------------------------------------------ */
+const char* lsa_status_str(int status);   /* static string, never NULL */
+int lsa_last_hip_error(void);             /* HIP error of this thread's last LSA_ERR_HIP */
+int lsa_abi_version(void);                /* LSA_ABI_VERSION */
+/* sizeof of a descriptor, for bindings: 0 score, 1 select, 2 attention,
+ * 3 project, 4 centroid; 0 for anything else. */
+size_t lsa_desc_size(int which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LSA_H_ */

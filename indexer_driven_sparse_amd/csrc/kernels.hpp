@@ -1,0 +1,115 @@
+// Internal launch interface between the C ABI layer (lsa_api.hip) and the
+// kernel translation units. Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lsa {
+
+// ----- indexer scoring -----------------------------------------------------
+struct ScoreDecodeArgs {
+  const void* k_idx;
+  int64_t ks_seq, ks_head, ks_tok;   // elements
+  int Hkv, T, r;
+  const float* q_idx_in;             // [rows, r] fp32 (when q == nullptr)
+  float* q_idx_out;                  // optional fp32 output of the prep
+  const void* q;                     // [N,Hq,d] (prep input) or nullptr
+  int q_bf16, Hq, d, w_per_head;
+  const float* w;
+  const int32_t* cand;               // nullptr: slots are positions
+  int64_t cand_ld;
+  int cand_block;
+  int n_out;                         // slots per row
+  float* scores;
+  int64_t scores_ld;
+  int chunk;                         // slots per workgroup, multiple of 64
+};
+hipError_t launch_score_decode(const ScoreDecodeArgs& a, int rows, bool k_bf16, hipStream_t s);
+
+struct ScorePrefillArgs {
+  const void* q_idx;                 // [L, Hkv, r] (contiguous rows of r)
+  const void* k_idx;
+  int64_t ks_head, ks_tok;
+  int L, Hkv, r;
+  float* scores;
+  int64_t scores_ld;
+};
+hipError_t launch_score_prefill(const ScorePrefillArgs& a, bool bf16, hipStream_t s);
+
+// Fused causal prefill indexer + exact top-B.
+struct PrefillTopkArgs {
+  const uint16_t* q_idx;             // [L, Hkv, r] bf16
+  const uint16_t* k_idx;
+  int64_t ks_head, ks_tok;
+  int L, Hkv, r, B;
+  int32_t* out_idx;                  // [L, Hkv, B]
+  float* out_score;                  // or nullptr
+  void* ws;
+  size_t ws_bytes;
+};
+size_t prefill_topk_workspace(int L, int Hkv, int B);
+hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s);
+bool prefill_topk_supported(int r, int B);
+
+// ----- exact top-B selection -----------------------------------------------
+struct SelectArgs {
+  const float* scores;
+  int64_t scores_ld;
+  int n, B;
+  const int32_t* n_valid;
+  int causal_group;
+  const int32_t* cand;
+  int64_t cand_ld;
+  int cand_block, n_positions;
+  int32_t* out_idx;
+  float* out_score;
+  int32_t* out_count;
+  uint32_t* gbitmap;                 // workspace bitmaps for long rows, or nullptr
+};
+constexpr int kSelectLdsMaxSlots = 262144;
+size_t select_workspace(int rows, int n);
+hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s);
+
+// ----- indexed attention -----------------------------------------------------
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  int64_t s_seq, s_tok, s_head;
+  const int32_t* idx;
+  int rows, Hq, Hkv, d, B, T;
+  int prefill;
+  float scale_log2;                  // scale * log2(e)
+  float* out;
+  float* lse;
+  float* partial;                    // [rows*Hkv, splits, G, d + 2] when splits > 1
+  int splits, keys_per_split;
+};
+void attention_plan(int rows, int Hkv, int G, int d, int B, int* splits, int* keys_per_split);
+size_t attention_workspace(int rows, int Hkv, int G, int d, int B);
+hipError_t launch_attention(const AttnArgs& a, bool q_bf16, bool kv_bf16, hipStream_t s);
+bool attention_supported(int G, int d);
+
+// ----- setup -----------------------------------------------------------------
+struct ProjectArgs {
+  const void* k;
+  int64_t ks_seq, ks_tok, ks_head;
+  const float* w;
+  int w_per_head;
+  void* out;
+  int64_t os_seq, os_head, os_tok;
+  int N, Hkv, d, r, tok_begin, n_tok;
+};
+hipError_t launch_project(const ProjectArgs& a, bool k_bf16, bool out_bf16, hipStream_t s);
+
+struct CentroidArgs {
+  const void* in;
+  int64_t is_seq, is_head, is_tok;
+  void* out;
+  int64_t os_seq, os_head, os_blk;
+  int N, Hkv, T, r, block;
+};
+hipError_t launch_centroids(const CentroidArgs& a, bool bf16, hipStream_t s);
+
+}  // namespace lsa

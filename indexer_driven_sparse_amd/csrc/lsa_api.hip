@@ -1,0 +1,394 @@
+// C ABI of liblsa: argument validation, launch planning and dispatch.
+// Every check runs before the first HIP call of an entry point, so a
+// rejected call launches nothing and touches no output.
+#include <algorithm>
+#include <atomic>
+#include <climits>
+#include <cmath>
+#include <cstring>
+
+#include "lsa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip = 0;
+
+int hip_fail(hipError_t e) {
+  g_last_hip = (int)e;
+  return LSA_ERR_HIP;
+}
+
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+int esize(int dtype) { return dtype == LSA_BF16 ? 2 : dtype == LSA_F32 ? 4 : 0; }
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+bool strides16(int es, int64_t a, int64_t b, int64_t c) {
+  return a >= 0 && b >= 0 && c >= 0 && (a * es) % 16 == 0 && (b * es) % 16 == 0 && (c * es) % 16 == 0;
+}
+
+// gfx950 check, cached per device (the library's only global state).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return LSA_ERR_NO_DEVICE_CODE;
+  int st = g_device_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e);
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_device_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? LSA_OK : LSA_ERR_NO_DEVICE_CODE;
+}
+
+#define LSA_TRY(expr)              \
+  do {                             \
+    int _rc = (expr);              \
+    if (_rc != LSA_OK) return _rc; \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// lsa_index_score
+// ---------------------------------------------------------------------------
+int64_t score_slots(const lsa_score_desc* d) {
+  if (d->mode == LSA_MODE_DECODE && d->cand) return (int64_t)d->n_cand * d->cand_block;
+  return d->n_keys;
+}
+
+int validate_score(const lsa_score_desc* d, size_t* ws_need) {
+  if (!d || d->struct_size != sizeof(lsa_score_desc)) return LSA_ERR_INVALID_ARG;
+  *ws_need = 0;
+  const int ke = esize(d->k_idx_dtype);
+  if (ke == 0) return LSA_ERR_UNSUPPORTED;
+  if (d->n_kv_heads < 1 || d->n_keys < 1 || d->rank < 1) return LSA_ERR_INVALID_ARG;
+  const int64_t rbytes = (int64_t)d->rank * ke;
+  if (!pow2(rbytes) || rbytes < 16 || rbytes > 256) return LSA_ERR_UNSUPPORTED;
+  if (!d->k_idx || !al16(d->k_idx)) return LSA_ERR_INVALID_ARG;
+  if (!strides16(ke, d->k_stride_seq, d->k_stride_head, d->k_stride_tok)) return LSA_ERR_INVALID_ARG;
+  if (d->k_stride_tok < d->rank) return LSA_ERR_INVALID_ARG;
+  if (d->mode == LSA_MODE_DECODE) {
+    if (d->n_seq < 1) return LSA_ERR_INVALID_ARG;
+    const int64_t rows = (int64_t)d->n_seq * d->n_kv_heads;
+    if (rows > 65535) return LSA_ERR_UNSUPPORTED;
+    if (d->q) {
+      if (esize(d->q_dtype) == 0) return LSA_ERR_UNSUPPORTED;
+      if (d->n_q_heads < d->n_kv_heads || d->n_q_heads % d->n_kv_heads != 0) return LSA_ERR_INVALID_ARG;
+      if (d->head_dim < 1 || d->head_dim > 512) return LSA_ERR_UNSUPPORTED;
+      if (!d->w) return LSA_ERR_INVALID_ARG;
+      if (d->w_per_head != 0 && d->w_per_head != 1) return LSA_ERR_INVALID_ARG;
+    } else if (!d->q_idx) {
+      return LSA_ERR_INVALID_ARG;
+    }
+    if (d->cand) {
+      if (d->n_cand < 1 || d->cand_block < 1 || d->cand_ld < d->n_cand) return LSA_ERR_INVALID_ARG;
+      if ((int64_t)d->n_cand * d->cand_block > INT_MAX) return LSA_ERR_UNSUPPORTED;
+    }
+    if (!d->scores || !al16(d->scores) || d->scores_ld % 4 != 0 || d->scores_ld < score_slots(d))
+      return LSA_ERR_INVALID_ARG;
+    if (d->topk != 0 || d->out_idx || d->out_score) return LSA_ERR_INVALID_ARG;
+    return LSA_OK;
+  }
+  if (d->mode == LSA_MODE_PREFILL_CAUSAL) {
+    if (d->n_seq != 1 || !d->q_idx || d->q || d->cand) return LSA_ERR_INVALID_ARG;
+    if (!al16(d->q_idx)) return LSA_ERR_INVALID_ARG;
+    if (d->topk < 0) return LSA_ERR_INVALID_ARG;
+    if (d->topk == 0) {
+      if ((int64_t)d->n_keys * d->n_kv_heads > 65535) return LSA_ERR_UNSUPPORTED;
+      if (!d->scores || !al16(d->scores) || d->scores_ld % 4 != 0 || d->scores_ld < d->n_keys)
+        return LSA_ERR_INVALID_ARG;
+      return LSA_OK;
+    }
+    if (!d->out_idx) return LSA_ERR_INVALID_ARG;
+    if (d->k_idx_dtype != LSA_BF16 || !lsa::prefill_topk_supported(d->rank, d->topk))
+      return LSA_ERR_UNSUPPORTED;
+    *ws_need = lsa::prefill_topk_workspace(d->n_keys, d->n_kv_heads, d->topk);
+    return LSA_OK;
+  }
+  return LSA_ERR_INVALID_ARG;
+}
+
+// ---------------------------------------------------------------------------
+// lsa_topk_select
+// ---------------------------------------------------------------------------
+int validate_select(const lsa_select_desc* d, size_t* ws_need) {
+  if (!d || d->struct_size != sizeof(lsa_select_desc)) return LSA_ERR_INVALID_ARG;
+  if (d->rows < 1 || d->n < 1 || d->topk < 1) return LSA_ERR_INVALID_ARG;
+  if (!d->scores || !al16(d->scores) || d->scores_ld % 4 != 0 || d->scores_ld < d->n)
+    return LSA_ERR_INVALID_ARG;
+  if (!d->out_idx) return LSA_ERR_INVALID_ARG;
+  if (d->causal_group < 0 || (d->causal_group > 0 && d->n_valid)) return LSA_ERR_INVALID_ARG;
+  if (d->cand) {
+    if (d->cand_block < 1 || d->n_positions < 0) return LSA_ERR_INVALID_ARG;
+    if (d->cand_ld < ((int64_t)d->n + d->cand_block - 1) / d->cand_block) return LSA_ERR_INVALID_ARG;
+  }
+  *ws_need = lsa::select_workspace(d->rows, d->n);
+  return LSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// lsa_indexed_attention
+// ---------------------------------------------------------------------------
+int validate_attn(const lsa_attn_desc* d, size_t* ws_need) {
+  if (!d || d->struct_size != sizeof(lsa_attn_desc)) return LSA_ERR_INVALID_ARG;
+  if (d->mode != LSA_MODE_DECODE && d->mode != LSA_MODE_PREFILL_CAUSAL) return LSA_ERR_INVALID_ARG;
+  if (d->rows < 1 || d->n_kv_heads < 1 || d->n_q_heads < d->n_kv_heads || d->topk < 1 || d->n_keys < 1)
+    return LSA_ERR_INVALID_ARG;
+  if (d->n_q_heads % d->n_kv_heads != 0) return LSA_ERR_INVALID_ARG;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (!lsa::attention_supported(G, d->head_dim)) return LSA_ERR_UNSUPPORTED;
+  const int ke = esize(d->kv_dtype);
+  if (ke == 0 || d->q_dtype != d->kv_dtype) return LSA_ERR_UNSUPPORTED;
+  if (!d->q || !d->k || !d->v || !d->idx || !d->out) return LSA_ERR_INVALID_ARG;
+  if (!al16(d->k) || !al16(d->v)) return LSA_ERR_INVALID_ARG;
+  if (!strides16(ke, d->kv_stride_seq, d->kv_stride_tok, d->kv_stride_head)) return LSA_ERR_INVALID_ARG;
+  int sp, kps;
+  lsa::attention_plan(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, &sp, &kps);
+  if ((int64_t)d->rows * d->n_kv_heads * sp > INT_MAX) return LSA_ERR_UNSUPPORTED;
+  *ws_need = lsa::attention_workspace(d->rows, d->n_kv_heads, G, d->head_dim, d->topk);
+  return LSA_OK;
+}
+
+int check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return LSA_OK;
+  if (!ws || have < need || !al16(ws)) return LSA_ERR_WORKSPACE;
+  return LSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int lsa_index_score(const lsa_score_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  LSA_TRY(validate_score(d, &need));
+  LSA_TRY(check_ws(ws, ws_bytes, need));
+  LSA_TRY(check_device());
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  if (d->mode == LSA_MODE_DECODE) {
+    lsa::ScoreDecodeArgs a{};
+    a.k_idx = d->k_idx;
+    a.ks_seq = d->k_stride_seq;
+    a.ks_head = d->k_stride_head;
+    a.ks_tok = d->k_stride_tok;
+    a.Hkv = d->n_kv_heads;
+    a.T = d->n_keys;
+    a.r = d->rank;
+    a.q = d->q;
+    a.q_idx_in = d->q ? nullptr : (const float*)d->q_idx;
+    a.q_idx_out = d->q ? (float*)d->q_idx : nullptr;
+    a.q_bf16 = d->q_dtype == LSA_BF16;
+    a.Hq = d->n_q_heads;
+    a.d = d->head_dim;
+    a.w_per_head = d->w_per_head;
+    a.w = d->w;
+    a.cand = d->cand;
+    a.cand_ld = d->cand_ld;
+    a.cand_block = d->cand_block;
+    a.n_out = (int)score_slots(d);
+    a.scores = d->scores;
+    a.scores_ld = d->scores_ld;
+    const int rows = d->n_seq * d->n_kv_heads;
+    // about 2048 workgroups (8 per CU); chunks are multiples of 512 slots
+    int64_t per_row = (2048 + rows - 1) / rows;
+    int64_t chunk = (a.n_out + per_row - 1) / per_row;
+    chunk = std::max<int64_t>(512, (chunk + 511) / 512 * 512);
+    a.chunk = (int)chunk;
+    e = lsa::launch_score_decode(a, rows, d->k_idx_dtype == LSA_BF16, s);
+  } else if (d->topk == 0) {
+    lsa::ScorePrefillArgs a{};
+    a.q_idx = d->q_idx;
+    a.k_idx = d->k_idx;
+    a.ks_head = d->k_stride_head;
+    a.ks_tok = d->k_stride_tok;
+    a.L = d->n_keys;
+    a.Hkv = d->n_kv_heads;
+    a.r = d->rank;
+    a.scores = d->scores;
+    a.scores_ld = d->scores_ld;
+    e = lsa::launch_score_prefill(a, d->k_idx_dtype == LSA_BF16, s);
+  } else {
+    lsa::PrefillTopkArgs a{};
+    a.q_idx = (const uint16_t*)d->q_idx;
+    a.k_idx = (const uint16_t*)d->k_idx;
+    a.ks_head = d->k_stride_head;
+    a.ks_tok = d->k_stride_tok;
+    a.L = d->n_keys;
+    a.Hkv = d->n_kv_heads;
+    a.r = d->rank;
+    a.B = d->topk;
+    a.out_idx = d->out_idx;
+    a.out_score = d->out_score;
+    a.ws = ws;
+    a.ws_bytes = ws_bytes;
+    e = lsa::launch_prefill_topk(a, s);
+  }
+  return e == hipSuccess ? LSA_OK : hip_fail(e);
+}
+
+size_t lsa_score_workspace_bytes(const lsa_score_desc* d) {
+  size_t need = 0;
+  return validate_score(d, &need) == LSA_OK ? need : 0;
+}
+
+int lsa_topk_select(const lsa_select_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  LSA_TRY(validate_select(d, &need));
+  LSA_TRY(check_ws(ws, ws_bytes, need));
+  LSA_TRY(check_device());
+  lsa::SelectArgs a{};
+  a.scores = d->scores;
+  a.scores_ld = d->scores_ld;
+  a.n = d->n;
+  a.B = d->topk;
+  a.n_valid = d->n_valid;
+  a.causal_group = d->causal_group;
+  a.cand = d->cand;
+  a.cand_ld = d->cand_ld;
+  a.cand_block = d->cand ? d->cand_block : 1;
+  a.n_positions = d->n_positions;
+  a.out_idx = d->out_idx;
+  a.out_score = d->out_score;
+  a.out_count = d->out_count;
+  a.gbitmap = need ? (uint32_t*)ws : nullptr;
+  hipError_t e = lsa::launch_select(a, d->rows, (hipStream_t)stream);
+  return e == hipSuccess ? LSA_OK : hip_fail(e);
+}
+
+size_t lsa_select_workspace_bytes(const lsa_select_desc* d) {
+  size_t need = 0;
+  return validate_select(d, &need) == LSA_OK ? need : 0;
+}
+
+int lsa_indexed_attention(const lsa_attn_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  size_t need = 0;
+  LSA_TRY(validate_attn(d, &need));
+  LSA_TRY(check_ws(ws, ws_bytes, need));
+  LSA_TRY(check_device());
+  lsa::AttnArgs a{};
+  a.q = d->q;
+  a.k = d->k;
+  a.v = d->v;
+  a.s_seq = d->kv_stride_seq;
+  a.s_tok = d->kv_stride_tok;
+  a.s_head = d->kv_stride_head;
+  a.idx = d->idx;
+  a.rows = d->rows;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.d = d->head_dim;
+  a.B = d->topk;
+  a.T = d->n_keys;
+  a.prefill = d->mode == LSA_MODE_PREFILL_CAUSAL;
+  const float scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->head_dim);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = d->out;
+  a.lse = d->lse;
+  a.partial = (float*)ws;
+  lsa::attention_plan(d->rows, d->n_kv_heads, a.Hq / a.Hkv, a.d, a.B, &a.splits, &a.keys_per_split);
+  hipError_t e = lsa::launch_attention(a, d->q_dtype == LSA_BF16, d->kv_dtype == LSA_BF16,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? LSA_OK : hip_fail(e);
+}
+
+size_t lsa_attention_workspace_bytes(const lsa_attn_desc* d) {
+  size_t need = 0;
+  return validate_attn(d, &need) == LSA_OK ? need : 0;
+}
+
+int lsa_project_keys(const lsa_project_desc* d, void* stream) {
+  if (!d || d->struct_size != sizeof(lsa_project_desc)) return LSA_ERR_INVALID_ARG;
+  if (esize(d->k_dtype) == 0 || esize(d->out_dtype) == 0) return LSA_ERR_UNSUPPORTED;
+  if (d->n_seq < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->tok_begin < 0 || d->n_tok < 0)
+    return LSA_ERR_INVALID_ARG;
+  if (d->head_dim > 512 || !pow2(d->rank) || d->rank > 256) return LSA_ERR_UNSUPPORTED;
+  if (d->n_seq > 65535 || d->n_kv_heads > 65535) return LSA_ERR_UNSUPPORTED;
+  if (!d->k || !d->w || !d->out) return LSA_ERR_INVALID_ARG;
+  if (d->w_per_head != 0 && d->w_per_head != 1) return LSA_ERR_INVALID_ARG;
+  if (d->k_stride_seq < 0 || d->k_stride_tok < 0 || d->k_stride_head < 0 || d->out_stride_seq < 0 ||
+      d->out_stride_head < 0 || d->out_stride_tok < 0)
+    return LSA_ERR_INVALID_ARG;
+  LSA_TRY(check_device());
+  lsa::ProjectArgs a{};
+  a.k = d->k;
+  a.ks_seq = d->k_stride_seq;
+  a.ks_tok = d->k_stride_tok;
+  a.ks_head = d->k_stride_head;
+  a.w = d->w;
+  a.w_per_head = d->w_per_head;
+  a.out = d->out;
+  a.os_seq = d->out_stride_seq;
+  a.os_head = d->out_stride_head;
+  a.os_tok = d->out_stride_tok;
+  a.N = d->n_seq;
+  a.Hkv = d->n_kv_heads;
+  a.d = d->head_dim;
+  a.r = d->rank;
+  a.tok_begin = d->tok_begin;
+  a.n_tok = d->n_tok;
+  hipError_t e = lsa::launch_project(a, d->k_dtype == LSA_BF16, d->out_dtype == LSA_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? LSA_OK : hip_fail(e);
+}
+
+int lsa_build_centroids(const lsa_centroid_desc* d, void* stream) {
+  if (!d || d->struct_size != sizeof(lsa_centroid_desc)) return LSA_ERR_INVALID_ARG;
+  if (esize(d->dtype) == 0) return LSA_ERR_UNSUPPORTED;
+  if (d->n_seq < 1 || d->n_kv_heads < 1 || d->n_keys < 1 || d->rank < 1 || d->block < 1)
+    return LSA_ERR_INVALID_ARG;
+  if (d->n_seq > 65535 || d->n_kv_heads > 65535) return LSA_ERR_UNSUPPORTED;
+  if (!d->in || !d->out) return LSA_ERR_INVALID_ARG;
+  if (d->in_stride_seq < 0 || d->in_stride_head < 0 || d->in_stride_tok < 0 || d->out_stride_seq < 0 ||
+      d->out_stride_head < 0 || d->out_stride_blk < 0)
+    return LSA_ERR_INVALID_ARG;
+  LSA_TRY(check_device());
+  lsa::CentroidArgs a{};
+  a.in = d->in;
+  a.is_seq = d->in_stride_seq;
+  a.is_head = d->in_stride_head;
+  a.is_tok = d->in_stride_tok;
+  a.out = d->out;
+  a.os_seq = d->out_stride_seq;
+  a.os_head = d->out_stride_head;
+  a.os_blk = d->out_stride_blk;
+  a.N = d->n_seq;
+  a.Hkv = d->n_kv_heads;
+  a.T = d->n_keys;
+  a.r = d->rank;
+  a.block = d->block;
+  hipError_t e = lsa::launch_centroids(a, d->dtype == LSA_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? LSA_OK : hip_fail(e);
+}
+
+const char* lsa_status_str(int status) {
+  switch (status) {
+    case LSA_OK: return "ok";
+    case LSA_ERR_INVALID_ARG: return "invalid argument";
+    case LSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LSA_ERR_NO_DEVICE_CODE: return "current device is not gfx950";
+    case LSA_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+int lsa_last_hip_error(void) { return g_last_hip; }
+
+int lsa_abi_version(void) { return LSA_ABI_VERSION; }
+
+size_t lsa_desc_size(int which) {
+  switch (which) {
+    case 0: return sizeof(lsa_score_desc);
+    case 1: return sizeof(lsa_select_desc);
+    case 2: return sizeof(lsa_attn_desc);
+    case 3: return sizeof(lsa_project_desc);
+    case 4: return sizeof(lsa_centroid_desc);
+  }
+  return 0;
+}
+
+}  // extern "C"

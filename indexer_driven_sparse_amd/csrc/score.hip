@@ -1,0 +1,224 @@
+// Indexer scoring kernels (gfx950).
+//
+// Decode scoring streams the projected-key cache once: the mean of a KV
+// head's query heads, projected to r dims, is dotted with every cached
+// projected key (JSSA, "Joint Subspace Sparse Attention for Efficient
+// Long-Context Decoding", Fig. 1; Fig. 9 "scoring preparation" and
+// "candidate scoring"). It is HBM-bound (r=64 bf16: 128 bytes and 64 FMAs
+// per key), so the design is about the memory stream:
+//   * LPK = r*esize/16 lanes share one key row and each issues one 128-bit
+//     load, so every wave-wide load instruction reads 1 KiB of consecutive
+//     rows (fully coalesced);
+//   * the partial dot products are summed across those LPK lanes with DPP
+//     (no LDS), and after LPK loads each lane owns one of 64 consecutive
+//     scores, so the fp32 score store is one coalesced 256-byte write;
+//   * the query prep (mean of the G heads, times W) runs at the top of each
+//     workgroup, so the step needs no separate launch for it.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lsa {
+namespace {
+
+constexpr int kScoreThreads = 256;
+constexpr int kMaxD = 512;
+constexpr int kMaxR = 128;
+constexpr int kGroupsInFlight = 2;  // 64-slot groups whose loads are issued together
+
+template <bool BF16>
+__device__ __forceinline__ float dot16(const uint4& w, const float* q) {
+  if constexpr (BF16) {
+    float s = q[0] * bf16_lo(w.x);
+    s = fmaf(q[1], bf16_hi(w.x), s);
+    s = fmaf(q[2], bf16_lo(w.y), s);
+    s = fmaf(q[3], bf16_hi(w.y), s);
+    s = fmaf(q[4], bf16_lo(w.z), s);
+    s = fmaf(q[5], bf16_hi(w.z), s);
+    s = fmaf(q[6], bf16_lo(w.w), s);
+    s = fmaf(q[7], bf16_hi(w.w), s);
+    return s;
+  } else {
+    float s = q[0] * __uint_as_float(w.x);
+    s = fmaf(q[1], __uint_as_float(w.y), s);
+    s = fmaf(q[2], __uint_as_float(w.z), s);
+    s = fmaf(q[3], __uint_as_float(w.w), s);
+    return s;
+  }
+}
+
+// Slot -> token position, or -1 when the slot covers no token.
+template <bool CAND>
+__device__ __forceinline__ int64_t slot_position(const ScoreDecodeArgs& a, const int32_t* crow,
+                                                 int64_t slot) {
+  if constexpr (!CAND) {
+    return slot;
+  } else {
+    int32_t c = crow[slot / a.cand_block];
+    if (c < 0) return -1;
+    int64_t p = (int64_t)c * a.cand_block + slot % a.cand_block;
+    return p < a.T ? p : -1;
+  }
+}
+
+template <bool BF16, int LPK, bool CAND>
+__global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecodeArgs a) {
+  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int E = 16 / ESZ;        // channels per lane
+  constexpr int KPI = kWave / LPK;   // keys per wave-wide load
+  __shared__ float s_qbar[kMaxD];
+  __shared__ float s_part[kScoreThreads];
+  __shared__ float s_q[kMaxR];
+
+  const int row = blockIdx.y;
+  const int n = row / a.Hkv, g = row % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int r = a.r;
+
+  // ---- scoring preparation: q_idx = mean of the group's heads . W ----
+  if (a.q != nullptr) {
+    const int G = a.Hq / a.Hkv;
+    for (int c = tid; c < a.d; c += kScoreThreads) {
+      float s = 0.f;
+      for (int i = 0; i < G; ++i) {
+        int64_t off = ((int64_t)n * a.Hq + (int64_t)g * G + i) * a.d + c;
+        s += a.q_bf16 ? bf16_to_f32(((const uint16_t*)a.q)[off]) : ((const float*)a.q)[off];
+      }
+      s_qbar[c] = s / (float)G;
+    }
+    __syncthreads();
+    const float* W = a.w + (a.w_per_head ? (int64_t)g * a.d * r : 0);
+    const int parts = kScoreThreads / r;  // r is a power of two <= 128
+    const int j = tid % r, p = tid / r;
+    float acc = 0.f;
+    for (int c = p; c < a.d; c += parts) acc = fmaf(s_qbar[c], W[(int64_t)c * r + j], acc);
+    s_part[tid] = acc;
+    __syncthreads();
+    if (tid < r) {
+      float t = 0.f;
+      for (int k = 0; k < parts; ++k) t += s_part[k * r + tid];
+      s_q[tid] = t;
+      if (a.q_idx_out != nullptr && blockIdx.x == 0) a.q_idx_out[(int64_t)row * r + tid] = t;
+    }
+  } else if (tid < r) {
+    s_q[tid] = a.q_idx_in[(int64_t)row * r + tid];
+  }
+  __syncthreads();
+
+  const int l = lane % LPK, kg = lane / LPK;
+  float qv[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) qv[e] = s_q[l * E + e];
+
+  // ---- stream this workgroup's chunk of slots ----
+  const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+  const int64_t c1 = min((int64_t)a.n_out, c0 + a.chunk);
+  const char* kbase =
+      (const char*)a.k_idx + ((int64_t)n * a.ks_seq + (int64_t)g * a.ks_head) * ESZ + l * 16;
+  const int64_t tok_bytes = a.ks_tok * ESZ;
+  float* srow = a.scores + (int64_t)row * a.scores_ld;
+  const int32_t* crow = CAND ? a.cand + (int64_t)row * a.cand_ld : nullptr;
+
+  for (int64_t gb = c0 + (int64_t)wid * 64; gb < c1;
+       gb += (int64_t)kGroupsInFlight * 4 * 64) {
+    uint4 raw[kGroupsInFlight][LPK];
+    bool ok[kGroupsInFlight][LPK];
+#pragma unroll
+    for (int u = 0; u < kGroupsInFlight; ++u) {
+#pragma unroll
+      for (int it = 0; it < LPK; ++it) {
+        const int64_t slot = gb + (int64_t)u * 4 * 64 + it * KPI + kg;
+        bool valid = slot < c1;
+        int64_t pos = 0;
+        if (valid) {
+          pos = slot_position<CAND>(a, crow, slot);
+          valid = pos >= 0;
+        }
+        ok[u][it] = valid;
+        raw[u][it] = valid ? *(const uint4*)(kbase + pos * tok_bytes) : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kGroupsInFlight; ++u) {
+      float mine = 0.f;
+#pragma unroll
+      for (int it = 0; it < LPK; ++it) {
+        float s = sum_lanes<LPK>(dot16<BF16>(raw[u][it], qv));
+        if (!ok[u][it]) s = -INFINITY;
+        if (l == it) mine = s;
+      }
+      const int64_t myslot = gb + (int64_t)u * 4 * 64 + (int64_t)l * KPI + kg;
+      if (myslot < c1) srow[myslot] = mine;
+    }
+  }
+}
+
+// Small-L causal score matrix (unfused prefill scoring, for checking the
+// fused path and for short prompts). One thread per (row, key).
+template <bool BF16>
+__global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) {
+  __shared__ float s_q[kMaxR];
+  const int row = blockIdx.y;  // i * Hkv + g
+  const int i = row / a.Hkv, g = row % a.Hkv;
+  for (int c = threadIdx.x; c < a.r; c += blockDim.x) {
+    int64_t off = (int64_t)row * a.r + c;
+    s_q[c] = BF16 ? bf16_to_f32(((const uint16_t*)a.q_idx)[off]) : ((const float*)a.q_idx)[off];
+  }
+  __syncthreads();
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= a.L) return;
+  float acc = -INFINITY;
+  if (j <= i) {
+    acc = 0.f;
+    int64_t kb = (int64_t)g * a.ks_head + (int64_t)j * a.ks_tok;
+    for (int c = 0; c < a.r; ++c) {
+      float k = BF16 ? bf16_to_f32(((const uint16_t*)a.k_idx)[kb + c]) : ((const float*)a.k_idx)[kb + c];
+      acc = fmaf(s_q[c], k, acc);
+    }
+  }
+  a.scores[(int64_t)row * a.scores_ld + j] = acc;
+}
+
+template <bool BF16, int LPK>
+hipError_t launch_decode_lpk(const ScoreDecodeArgs& a, int rows, hipStream_t s) {
+  dim3 grid((unsigned)((a.n_out + a.chunk - 1) / a.chunk), (unsigned)rows);
+  if (a.cand)
+    hipLaunchKernelGGL((score_decode_kernel<BF16, LPK, true>), grid, dim3(kScoreThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((score_decode_kernel<BF16, LPK, false>), grid, dim3(kScoreThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_score_decode(const ScoreDecodeArgs& a, int rows, bool k_bf16, hipStream_t s) {
+  const int lpk = a.r * (k_bf16 ? 2 : 4) / 16;
+  if (k_bf16) {
+    switch (lpk) {
+      case 1: return launch_decode_lpk<true, 1>(a, rows, s);
+      case 2: return launch_decode_lpk<true, 2>(a, rows, s);
+      case 4: return launch_decode_lpk<true, 4>(a, rows, s);
+      case 8: return launch_decode_lpk<true, 8>(a, rows, s);
+      case 16: return launch_decode_lpk<true, 16>(a, rows, s);
+    }
+  } else {
+    switch (lpk) {
+      case 1: return launch_decode_lpk<false, 1>(a, rows, s);
+      case 2: return launch_decode_lpk<false, 2>(a, rows, s);
+      case 4: return launch_decode_lpk<false, 4>(a, rows, s);
+      case 8: return launch_decode_lpk<false, 8>(a, rows, s);
+      case 16: return launch_decode_lpk<false, 16>(a, rows, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_score_prefill(const ScorePrefillArgs& a, bool bf16, hipStream_t s) {
+  dim3 grid((unsigned)((a.L + 255) / 256), (unsigned)(a.L * a.Hkv));
+  if (bf16)
+    hipLaunchKernelGGL((score_prefill_kernel<true>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((score_prefill_kernel<false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lsa

@@ -1,0 +1,442 @@
+"""Thin ctypes binding of liblsa.so (include/lsa.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+liblsa.so. torch supplies device memory and the stream; tensors are passed as
+raw device pointers plus sizes and element strides. Importing this module
+loads the library and fails loudly if it is missing -- there is no fallback.
+
+The function names match the C entry points. Query head h belongs to KV
+head h // (Hq // Hkv).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsa.so")
+
+F32 = 0
+BF16 = 1
+MODE_DECODE = 0
+MODE_PREFILL_CAUSAL = 1
+
+STATUS = {0: "LSA_OK", -1: "LSA_ERR_INVALID_ARG", -2: "LSA_ERR_UNSUPPORTED",
+          -3: "LSA_ERR_WORKSPACE", -4: "LSA_ERR_NO_DEVICE_CODE", -5: "LSA_ERR_HIP"}
+
+
+class LsaError(RuntimeError):
+    def __init__(self, fn: str, status: int, hip: int = 0):
+        self.status = status
+        self.hip_error = hip
+        msg = f"{fn}: {STATUS.get(status, status)} ({_lib().lsa_status_str(status).decode()})"
+        if status == -5:
+            msg += f", HIP error {hip}"
+        super().__init__(msg)
+
+
+_c = ctypes
+_U32, _I32, _I64, _P, _F = _c.c_uint32, _c.c_int32, _c.c_int64, _c.c_void_p, _c.c_float
+
+
+class ScoreDesc(_c.Structure):
+    _fields_ = [("struct_size", _U32), ("mode", _I32), ("n_seq", _I32), ("n_kv_heads", _I32),
+                ("n_keys", _I32), ("rank", _I32),
+                ("q_idx", _P), ("q", _P), ("q_dtype", _I32), ("n_q_heads", _I32),
+                ("head_dim", _I32), ("w_per_head", _I32), ("w", _P),
+                ("k_idx", _P), ("k_idx_dtype", _I32), ("reserved0", _I32),
+                ("k_stride_seq", _I64), ("k_stride_head", _I64), ("k_stride_tok", _I64),
+                ("cand", _P), ("n_cand", _I32), ("cand_block", _I32), ("cand_ld", _I64),
+                ("scores", _P), ("scores_ld", _I64),
+                ("topk", _I32), ("reserved1", _I32), ("out_idx", _P), ("out_score", _P)]
+
+
+class SelectDesc(_c.Structure):
+    _fields_ = [("struct_size", _U32), ("rows", _I32), ("n", _I32), ("topk", _I32),
+                ("scores", _P), ("scores_ld", _I64), ("n_valid", _P),
+                ("causal_group", _I32), ("cand_block", _I32), ("cand", _P), ("cand_ld", _I64),
+                ("n_positions", _I32), ("reserved0", _I32),
+                ("out_idx", _P), ("out_score", _P), ("out_count", _P)]
+
+
+class AttnDesc(_c.Structure):
+    _fields_ = [("struct_size", _U32), ("mode", _I32), ("rows", _I32), ("n_q_heads", _I32),
+                ("n_kv_heads", _I32), ("head_dim", _I32), ("topk", _I32), ("n_keys", _I32),
+                ("q", _P), ("q_dtype", _I32), ("kv_dtype", _I32), ("k", _P), ("v", _P),
+                ("kv_stride_seq", _I64), ("kv_stride_tok", _I64), ("kv_stride_head", _I64),
+                ("idx", _P), ("scale", _F), ("reserved0", _I32), ("out", _P), ("lse", _P)]
+
+
+class ProjectDesc(_c.Structure):
+    _fields_ = [("struct_size", _U32), ("n_seq", _I32), ("n_kv_heads", _I32), ("head_dim", _I32),
+                ("rank", _I32), ("tok_begin", _I32), ("n_tok", _I32), ("k_dtype", _I32),
+                ("k", _P), ("k_stride_seq", _I64), ("k_stride_tok", _I64), ("k_stride_head", _I64),
+                ("w", _P), ("w_per_head", _I32), ("out_dtype", _I32), ("out", _P),
+                ("out_stride_seq", _I64), ("out_stride_head", _I64), ("out_stride_tok", _I64)]
+
+
+class CentroidDesc(_c.Structure):
+    _fields_ = [("struct_size", _U32), ("n_seq", _I32), ("n_kv_heads", _I32), ("n_keys", _I32),
+                ("rank", _I32), ("block", _I32), ("dtype", _I32), ("in_", _P),
+                ("in_stride_seq", _I64), ("in_stride_head", _I64), ("in_stride_tok", _I64),
+                ("out", _P), ("out_stride_seq", _I64), ("out_stride_head", _I64),
+                ("out_stride_blk", _I64)]
+
+
+DESCS = {0: ScoreDesc, 1: SelectDesc, 2: AttnDesc, 3: ProjectDesc, 4: CentroidDesc}
+
+_SIGS = {
+    "lsa_index_score": (_I32, [_P, _P, _c.c_size_t, _P]),
+    "lsa_topk_select": (_I32, [_P, _P, _c.c_size_t, _P]),
+    "lsa_indexed_attention": (_I32, [_P, _P, _c.c_size_t, _P]),
+    "lsa_project_keys": (_I32, [_P, _P]),
+    "lsa_build_centroids": (_I32, [_P, _P]),
+    "lsa_score_workspace_bytes": (_c.c_size_t, [_P]),
+    "lsa_select_workspace_bytes": (_c.c_size_t, [_P]),
+    "lsa_attention_workspace_bytes": (_c.c_size_t, [_P]),
+    "lsa_status_str": (_c.c_char_p, [_I32]),
+    "lsa_last_hip_error": (_I32, []),
+    "lsa_abi_version": (_I32, []),
+    "lsa_desc_size": (_c.c_size_t, [_I32]),
+}
+
+_handle = None
+
+
+def _lib():
+    global _handle
+    if _handle is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(f"liblsa.so is not built ({_LIB_PATH}); run "
+                              "`python -m indexer_driven_sparse_amd.build`")
+        lib = _c.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        for which, cls in DESCS.items():
+            if lib.lsa_desc_size(which) != _c.sizeof(cls):
+                raise ImportError(f"liblsa.so descriptor {cls.__name__} has size "
+                                  f"{lib.lsa_desc_size(which)}, binding expects {_c.sizeof(cls)}")
+        _handle = lib
+    return _handle
+
+
+def library_path() -> str:
+    _lib()
+    return _LIB_PATH
+
+
+def abi_version() -> int:
+    return int(_lib().lsa_abi_version())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"liblsa takes float32 or bfloat16 tensors, got {t.dtype}")
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        return int(t)
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _rows2d(t: torch.Tensor, rows: int, name: str) -> int:
+    """Leading dimension of `t` read as `rows` evenly spaced rows of its last
+    dimension (e.g. [N, Hkv, n] with any row spacing that is uniform)."""
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: innermost dimension must be contiguous")
+    if t.dim() == 1:
+        ld = t.shape[0]
+    else:
+        ld = t.stride(-2)
+        span = ld
+        for dim in range(t.dim() - 2, -1, -1):
+            if t.shape[dim] > 1 and t.stride(dim) != span:
+                raise ValueError(f"{name}: rows must be evenly spaced")
+            span *= t.shape[dim]
+    if t.numel() // t.shape[-1] != rows:
+        raise ValueError(f"{name}: expected {rows} rows, got {t.numel() // t.shape[-1]}")
+    return ld
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise LsaError(fn, rc, int(_lib().lsa_last_hip_error()))
+
+
+def _workspace(need: int, workspace, device):
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+
+def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score):
+    d = ScoreDesc()
+    d.struct_size = _c.sizeof(ScoreDesc)
+    d.mode = mode
+    d.k_idx = _ptr(k_idx)
+    d.k_idx_dtype = _dt(k_idx)
+    if mode == MODE_DECODE:
+        N, Hkv, T, r = k_idx.shape
+        d.k_stride_seq, d.k_stride_head, d.k_stride_tok = k_idx.stride(0), k_idx.stride(1), k_idx.stride(2)
+    else:
+        L, Hkv, r = k_idx.shape
+        N, T = 1, L
+        d.k_stride_seq, d.k_stride_head, d.k_stride_tok = 0, k_idx.stride(1), k_idx.stride(0)
+    if k_idx.stride(-1) != 1:
+        raise ValueError("k_idx: innermost dimension must be contiguous")
+    d.n_seq, d.n_kv_heads, d.n_keys, d.rank = N, Hkv, T, r
+    if q is not None and (q.dim() != 3 or q.shape[0] != N or not q.is_contiguous()):
+        raise ValueError("q must be contiguous [N,Hq,d]")
+    if q is not None and (w is None or w.shape[-1] != r or w.shape[-2] != q.shape[2]
+                          or not w.is_contiguous() or (w.dim() == 3 and w.shape[0] != Hkv)):
+        raise ValueError("w must be contiguous [d,r] or [Hkv,d,r]")
+    if q_idx is not None and (not q_idx.is_contiguous() or tuple(q_idx.shape) !=
+                              ((N, Hkv, r) if mode == MODE_DECODE else (T, Hkv, r))):
+        raise ValueError("q_idx must be contiguous [N,Hkv,r] (decode) or [L,Hkv,r] (prefill)")
+    if cand is not None and (not cand.is_contiguous() or cand.dtype != torch.int32
+                             or tuple(cand.shape[:-1]) != (N, Hkv)):
+        raise ValueError("cand must be contiguous int32 [N,Hkv,n_cand]")
+    if out_idx is not None and (not out_idx.is_contiguous() or out_idx.numel() != T * Hkv * topk):
+        raise ValueError("out_idx must be contiguous [L,Hkv,B]")
+    if out_score is not None and (not out_score.is_contiguous() or out_score.numel() != T * Hkv * topk):
+        raise ValueError("out_score must be contiguous [L,Hkv,B]")
+    if q is not None:
+        d.q = _ptr(q)
+        d.q_dtype = _dt(q)
+        d.n_q_heads, d.head_dim = q.shape[1], q.shape[2]
+        d.w = _ptr(w)
+        d.w_per_head = 1 if w.dim() == 3 else 0
+    d.q_idx = _ptr(q_idx)
+    if cand is not None:
+        d.cand = _ptr(cand)
+        d.n_cand = cand.shape[-1]
+        d.cand_block = cand_block
+        d.cand_ld = cand.stride(-2) if cand.dim() >= 2 else cand.shape[-1]
+    if scores is not None:
+        d.scores = _ptr(scores)
+        d.scores_ld = _rows2d(scores, N * Hkv if mode == MODE_DECODE else T * Hkv, "scores")
+    d.topk = topk
+    d.out_idx = _ptr(out_idx)
+    d.out_score = _ptr(out_score)
+    return d
+
+
+def lsa_index_score(k_idx: torch.Tensor, scores: torch.Tensor | None, *, q=None, w=None,
+                    q_idx=None, cand=None, cand_block: int = 1, mode: int = MODE_DECODE,
+                    topk: int = 0, out_idx=None, out_score=None, workspace=None,
+                    stream=None) -> None:
+    """Indexer scores. Decode: k_idx [N,Hkv,T,r] (any strides, r contiguous);
+    either q [N,Hq,d] with w [d,r] / [Hkv,d,r] (prep fused; q_idx, if given,
+    receives fp32 [N,Hkv,r]) or q_idx fp32 [N,Hkv,r]; optional cand
+    [N,Hkv,nc] int32 with cand_block; scores fp32 [N,Hkv,n_out].
+    Prefill: k_idx [L,Hkv,r], q_idx [L,Hkv,r]; topk=0 writes scores
+    [L,Hkv,L]; topk=B fills out_idx [L,Hkv,B] (and out_score)."""
+    d = _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score)
+    lib = _lib()
+    ws, wsb = _workspace(lib.lsa_score_workspace_bytes(_c.byref(d)), workspace, k_idx.device)
+    _check("lsa_index_score", lib.lsa_index_score(_c.byref(d), _ptr(ws), wsb, _stream(stream)))
+
+
+def lsa_score_workspace_bytes(k_idx, scores, *, q=None, w=None, q_idx=None, cand=None,
+                              cand_block=1, mode=MODE_DECODE, topk=0, out_idx=None,
+                              out_score=None) -> int:
+    d = _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score)
+    return int(_lib().lsa_score_workspace_bytes(_c.byref(d)))
+
+
+def _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal_group, cand,
+                 cand_block, n_positions):
+    rows = scores.numel() // scores.shape[-1]
+    if not out_idx.is_contiguous() or out_idx.numel() != rows * topk or out_idx.dtype != torch.int32:
+        raise ValueError("out_idx must be contiguous int32 [rows, B]")
+    if out_score is not None and (not out_score.is_contiguous() or out_score.numel() != rows * topk):
+        raise ValueError("out_score must be contiguous [rows, B]")
+    if out_count is not None and (not out_count.is_contiguous() or out_count.numel() != rows):
+        raise ValueError("out_count must be contiguous [rows]")
+    if n_valid is not None and (not n_valid.is_contiguous() or n_valid.numel() != rows):
+        raise ValueError("n_valid must be contiguous [rows]")
+    if n is not None and n > scores.shape[-1]:
+        raise ValueError("n exceeds the row length")
+    if cand is not None and (not cand.is_contiguous() or cand.numel() // cand.shape[-1] != rows
+                             or cand.shape[-1] * cand_block < (scores.shape[-1] if n is None else n)):
+        raise ValueError("cand must be contiguous [rows, n_cand] covering every slot")
+    d = SelectDesc()
+    d.struct_size = _c.sizeof(SelectDesc)
+    d.rows = rows
+    d.n = scores.shape[-1] if n is None else n
+    d.topk = topk
+    d.scores = _ptr(scores)
+    d.scores_ld = _rows2d(scores, rows, "scores")
+    d.n_valid = _ptr(n_valid)
+    d.causal_group = causal_group
+    if cand is not None:
+        d.cand = _ptr(cand)
+        d.cand_block = cand_block
+        d.cand_ld = cand.shape[-1]
+        d.n_positions = n_positions
+    d.out_idx = _ptr(out_idx)
+    d.out_score = _ptr(out_score)
+    d.out_count = _ptr(out_count)
+    return d
+
+
+def lsa_topk_select(scores: torch.Tensor, topk: int, out_idx: torch.Tensor, *, n=None,
+                    out_score=None, out_count=None, n_valid=None, causal_group: int = 0,
+                    cand=None, cand_block: int = 1, n_positions: int = 0, workspace=None,
+                    stream=None) -> None:
+    """Exact top-B per row of scores [..., n] (rows evenly spaced): ascending
+    positions in out_idx [rows, B], -1 padded."""
+    d = _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal_group, cand,
+                     cand_block, n_positions)
+    lib = _lib()
+    ws, wsb = _workspace(lib.lsa_select_workspace_bytes(_c.byref(d)), workspace, scores.device)
+    _check("lsa_topk_select", lib.lsa_topk_select(_c.byref(d), _ptr(ws), wsb, _stream(stream)))
+
+
+def lsa_select_workspace_bytes(scores, topk, out_idx, *, n=None, n_valid=None, causal_group=0,
+                               cand=None, cand_block=1, n_positions=0) -> int:
+    d = _select_desc(scores, topk, out_idx, n, None, None, n_valid, causal_group, cand, cand_block,
+                     n_positions)
+    return int(_lib().lsa_select_workspace_bytes(_c.byref(d)))
+
+
+def _attn_desc(q, k, v, idx, out, lse, mode, scale):
+    rows, Hq, hd = q.shape
+    S, T, Hkv, _ = k.shape
+    if k.stride() != v.stride() or k.shape != v.shape:
+        raise ValueError("k and v must share shape and strides")
+    if mode == MODE_DECODE and S < rows:
+        raise ValueError(f"decode reads sequence `row` of k/v: {S} sequences < {rows} rows")
+    if not q.is_contiguous() or not idx.is_contiguous() or not out.is_contiguous():
+        raise ValueError("q, idx and out must be contiguous")
+    if tuple(idx.shape[:-1]) != (rows, Hkv) or tuple(out.shape) != (rows, Hq, hd):
+        raise ValueError("idx must be [rows,Hkv,B] and out [rows,Hq,d]")
+    d = AttnDesc()
+    d.struct_size = _c.sizeof(AttnDesc)
+    d.mode = mode
+    d.rows, d.n_q_heads, d.n_kv_heads, d.head_dim = rows, Hq, Hkv, hd
+    d.topk = idx.shape[-1]
+    d.n_keys = T
+    d.q = _ptr(q)
+    d.q_dtype = _dt(q)
+    d.kv_dtype = _dt(k)
+    d.k, d.v = _ptr(k), _ptr(v)
+    d.kv_stride_seq, d.kv_stride_tok, d.kv_stride_head = k.stride(0), k.stride(1), k.stride(2)
+    d.idx = _ptr(idx)
+    d.scale = scale
+    d.out = _ptr(out)
+    d.lse = _ptr(lse)
+    return d
+
+
+def lsa_indexed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
+                          out: torch.Tensor, *, lse=None, mode: int = MODE_DECODE,
+                          scale: float = 0.0, workspace=None, stream=None) -> None:
+    """q [rows,Hq,d]; k, v [S,T,Hkv,d] viewed through their strides (same for
+    both); idx [rows,Hkv,B] int32; out fp32 [rows,Hq,d]; lse fp32 [rows,Hq]."""
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale)
+    lib = _lib()
+    ws, wsb = _workspace(lib.lsa_attention_workspace_bytes(_c.byref(d)), workspace, q.device)
+    _check("lsa_indexed_attention",
+           lib.lsa_indexed_attention(_c.byref(d), _ptr(ws), wsb, _stream(stream)))
+
+
+def lsa_attention_workspace_bytes(q, k, v, idx, out, *, lse=None, mode=MODE_DECODE,
+                                  scale=0.0) -> int:
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale)
+    return int(_lib().lsa_attention_workspace_bytes(_c.byref(d)))
+
+
+def attention_workspace_bytes_for(rows: int, Hq: int, Hkv: int, d: int, B: int, T: int,
+                                  kv_dtype: int = BF16, mode: int = MODE_DECODE) -> int:
+    """Workspace lsa_indexed_attention needs for a shape (no tensors needed:
+    the size depends on the shape only)."""
+    dd = AttnDesc()
+    dd.struct_size = _c.sizeof(AttnDesc)
+    dd.mode, dd.rows, dd.n_q_heads, dd.n_kv_heads, dd.head_dim, dd.topk, dd.n_keys = \
+        mode, rows, Hq, Hkv, d, B, T
+    dd.q = dd.k = dd.v = dd.idx = dd.out = 256          # placeholders: sizing never dereferences
+    dd.q_dtype = dd.kv_dtype = kv_dtype
+    dd.kv_stride_seq, dd.kv_stride_tok, dd.kv_stride_head = T * Hkv * d, Hkv * d, d
+    return int(_lib().lsa_attention_workspace_bytes(_c.byref(dd)))
+
+
+def prefill_score_workspace_bytes_for(L: int, Hkv: int, r: int, B: int) -> int:
+    """Workspace of the fused causal prefill indexer (bf16, [L,Hkv,r])."""
+    dd = ScoreDesc()
+    dd.struct_size = _c.sizeof(ScoreDesc)
+    dd.mode, dd.n_seq, dd.n_kv_heads, dd.n_keys, dd.rank = MODE_PREFILL_CAUSAL, 1, Hkv, L, r
+    dd.q_idx = dd.k_idx = dd.out_idx = 256
+    dd.k_idx_dtype = BF16
+    dd.k_stride_head, dd.k_stride_tok = r, Hkv * r
+    dd.topk = B
+    return int(_lib().lsa_score_workspace_bytes(_c.byref(dd)))
+
+
+def lsa_project_keys(k: torch.Tensor, w: torch.Tensor, out: torch.Tensor, *, tok_begin: int = 0,
+                     n_tok: int | None = None, stream=None) -> None:
+    """out[n,g,t,:] = round(k[n,t,g,:] . w) for t in [tok_begin, tok_begin+n_tok).
+    k [N,T,Hkv,d] (strided), w [d,r] / [Hkv,d,r] fp32, out [N,Hkv,T',r]."""
+    N, T, Hkv, hd = k.shape
+    d = ProjectDesc()
+    d.struct_size = _c.sizeof(ProjectDesc)
+    d.n_seq, d.n_kv_heads, d.head_dim, d.rank = N, Hkv, hd, w.shape[-1]
+    d.tok_begin = tok_begin
+    d.n_tok = T - tok_begin if n_tok is None else n_tok
+    if tok_begin < 0 or tok_begin + d.n_tok > T or tok_begin + d.n_tok > out.shape[2]:
+        raise ValueError("token range outside k or out")
+    if tuple(out.shape[:2]) != (N, Hkv) or out.shape[3] != w.shape[-1] or w.shape[-2] != hd:
+        raise ValueError("out must be [N,Hkv,T,r] and w [d,r] or [Hkv,d,r]")
+    d.k_dtype = _dt(k)
+    d.k = _ptr(k)
+    d.k_stride_seq, d.k_stride_tok, d.k_stride_head = k.stride(0), k.stride(1), k.stride(2)
+    d.w = _ptr(w)
+    d.w_per_head = 1 if w.dim() == 3 else 0
+    d.out_dtype = _dt(out)
+    d.out = _ptr(out)
+    d.out_stride_seq, d.out_stride_head, d.out_stride_tok = out.stride(0), out.stride(1), out.stride(2)
+    _check("lsa_project_keys", _lib().lsa_project_keys(_c.byref(d), _stream(stream)))
+
+
+def lsa_build_centroids(k_idx: torch.Tensor, block: int, out: torch.Tensor, *, stream=None) -> None:
+    """out[n,g,b,:] = round(mean of k_idx[n,g,t,:] over block b). k_idx
+    [N,Hkv,T,r], out [N,Hkv,ceil(T/block),r], same dtype."""
+    N, Hkv, T, r = k_idx.shape
+    d = CentroidDesc()
+    d.struct_size = _c.sizeof(CentroidDesc)
+    d.n_seq, d.n_kv_heads, d.n_keys, d.rank, d.block = N, Hkv, T, r, block
+    d.dtype = _dt(k_idx)
+    if out.dtype != k_idx.dtype or tuple(out.shape) != (N, Hkv, (T + block - 1) // block, r):
+        raise ValueError("out must be [N,Hkv,ceil(T/block),r] in k_idx's dtype")
+    d.in_ = _ptr(k_idx)
+    d.in_stride_seq, d.in_stride_head, d.in_stride_tok = k_idx.stride(0), k_idx.stride(1), k_idx.stride(2)
+    d.out = _ptr(out)
+    d.out_stride_seq, d.out_stride_head, d.out_stride_blk = out.stride(0), out.stride(1), out.stride(2)
+    _check("lsa_build_centroids", _lib().lsa_build_centroids(_c.byref(d), _stream(stream)))

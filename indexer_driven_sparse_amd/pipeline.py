@@ -1,0 +1,152 @@
+"""The hot path as a sequence of liblsa calls.
+
+Flat decode step (JSSA, "Joint Subspace Sparse Attention for Efficient
+Long-Context Decoding", Fig. 1 and the Fig. 9 stages):
+    lsa_index_score        scoring preparation fused with candidate scoring
+    lsa_topk_select        top-B per (sequence, KV head)
+    lsa_indexed_attention  the group's heads attend to those B positions
+Hierarchical decode step (LongCat Sparse Attention abstract, item 3): score
+block centroids, keep the top blocks, score only their tokens, keep the
+top-B, attend. Causal prefill (LongCat abstract, O(L^2) indexer): causal
+scores + per-row top-B, then per-query indexed attention.
+
+Plans preallocate every buffer and workspace once, so `run` allocates
+nothing and can be captured in a HIP graph. All arithmetic happens in
+liblsa's kernels; this module only sequences calls and holds buffers.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import lsa
+
+
+def _code(dtype) -> int:
+    return lsa.BF16 if dtype == torch.bfloat16 else lsa.F32
+
+
+def _ld4(n: int) -> int:
+    return (n + 3) // 4 * 4
+
+
+class DecodePlan:
+    """Buffers for one flat decode step of N sequences with T cached tokens."""
+
+    def __init__(self, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int,
+                 device="cuda", kv_dtype=torch.bfloat16):
+        self.N, self.Hq, self.Hkv, self.T, self.d, self.r, self.B = N, Hq, Hkv, T, d, r, B
+        f32 = dict(dtype=torch.float32, device=device)
+        self.scores = torch.empty(N, Hkv, _ld4(T), **f32)[:, :, :T]
+        self.q_idx = torch.empty(N, Hkv, r, **f32)
+        self.idx = torch.empty(N, Hkv, B, dtype=torch.int32, device=device)
+        self.idx_scores = torch.empty(N, Hkv, B, **f32)
+        self.out = torch.empty(N, Hq, d, **f32)
+        self.lse = torch.empty(N, Hq, **f32)
+        # attention workspace, sized by the library for this shape
+        need = lsa.attention_workspace_bytes_for(N, Hq, Hkv, d, B, T, _code(kv_dtype))
+        self.attn_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+    def score(self, q, w, k_idx, stream=None):
+        lsa.lsa_index_score(k_idx, self.scores, q=q, w=w, q_idx=self.q_idx, stream=stream)
+
+    def select(self, stream=None):
+        lsa.lsa_topk_select(self.scores, self.B, self.idx, out_score=self.idx_scores,
+                            stream=stream)
+
+    def attend(self, q, k, v, stream=None):
+        lsa.lsa_indexed_attention(q, k, v, self.idx, self.out, lse=self.lse,
+                                  workspace=self.attn_ws, stream=stream)
+
+    def run(self, q, w, k_idx, k, v, stream=None):
+        self.score(q, w, k_idx, stream)
+        self.select(stream)
+        self.attend(q, k, v, stream)
+        return self
+
+
+def decode_step(q, w, k_idx, k, v, B, stream=None) -> dict:
+    """One flat decode step; returns the step's buffers (device tensors)."""
+    N, Hkv, T, r = k_idx.shape
+    plan = DecodePlan(N, q.shape[1], Hkv, T, q.shape[2], r, B, device=q.device, kv_dtype=k.dtype)
+    plan.run(q, w, k_idx, k, v, stream)
+    return {"q_idx": plan.q_idx, "scores": plan.scores, "idx": plan.idx,
+            "idx_scores": plan.idx_scores, "out": plan.out, "lse": plan.lse}
+
+
+class HierarchicalPlan:
+    """Buffers for one coarse-to-fine decode step: n_blocks centroids per
+    (sequence, KV head), B_coarse kept blocks of `block` tokens, top-B."""
+
+    def __init__(self, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int, block: int,
+                 B_coarse: int, device="cuda", kv_dtype=torch.bfloat16):
+        self.N, self.Hq, self.Hkv, self.T, self.d, self.r = N, Hq, Hkv, T, d, r
+        self.B, self.block, self.B_coarse = B, block, B_coarse
+        self.n_blocks = (T + block - 1) // block
+        f32 = dict(dtype=torch.float32, device=device)
+        self.q_idx = torch.empty(N, Hkv, r, **f32)
+        self.coarse = torch.empty(N, Hkv, _ld4(self.n_blocks), **f32)[:, :, :self.n_blocks]
+        self.blocks = torch.empty(N, Hkv, B_coarse, dtype=torch.int32, device=device)
+        self.n_fine = B_coarse * block
+        self.fine = torch.empty(N, Hkv, _ld4(self.n_fine), **f32)[:, :, :self.n_fine]
+        self.idx = torch.empty(N, Hkv, B, dtype=torch.int32, device=device)
+        self.idx_scores = torch.empty(N, Hkv, B, **f32)
+        self.out = torch.empty(N, Hq, d, **f32)
+        self.lse = torch.empty(N, Hq, **f32)
+        need = lsa.attention_workspace_bytes_for(N, Hq, Hkv, d, B, T, _code(kv_dtype))
+        self.attn_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+    def run(self, q, w, k_idx, centroids, k, v, stream=None):
+        # coarse: score every block summary, keep the top B_coarse blocks
+        lsa.lsa_index_score(centroids, self.coarse, q=q, w=w, q_idx=self.q_idx, stream=stream)
+        lsa.lsa_topk_select(self.coarse, self.B_coarse, self.blocks, stream=stream)
+        # fine: score only the kept blocks' tokens, keep the top-B positions
+        lsa.lsa_index_score(k_idx, self.fine, q_idx=self.q_idx, cand=self.blocks,
+                            cand_block=self.block, stream=stream)
+        lsa.lsa_topk_select(self.fine, self.B, self.idx, out_score=self.idx_scores,
+                            cand=self.blocks, cand_block=self.block, n_positions=self.T,
+                            stream=stream)
+        lsa.lsa_indexed_attention(q, k, v, self.idx, self.out, lse=self.lse,
+                                  workspace=self.attn_ws, stream=stream)
+        return self
+
+
+class PrefillPlan:
+    """Buffers for causal prefill of one sequence of L tokens: per query row
+    the top-B keys of its causal prefix, then indexed attention."""
+
+    def __init__(self, L: int, Hq: int, Hkv: int, d: int, r: int, B: int, device="cuda",
+                 fused: bool = True):
+        self.L, self.Hq, self.Hkv, self.d, self.r, self.B = L, Hq, Hkv, d, r, B
+        self.fused = fused
+        self.idx = torch.empty(L, Hkv, B, dtype=torch.int32, device=device)
+        self.idx_scores = torch.empty(L, Hkv, B, dtype=torch.float32, device=device)
+        self.out = torch.empty(L, Hq, d, dtype=torch.float32, device=device)
+        self.lse = torch.empty(L, Hq, dtype=torch.float32, device=device)
+        self.scores = None
+        self.score_ws = None
+        if fused:
+            need = lsa.prefill_score_workspace_bytes_for(L, Hkv, r, B)
+            self.score_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        else:
+            self.scores = torch.empty(L, Hkv, _ld4(L), dtype=torch.float32, device=device)[:, :, :L]
+
+    def index(self, q_idx, k_idx, stream=None):
+        if self.fused:
+            lsa.lsa_index_score(k_idx, None, q_idx=q_idx, mode=lsa.MODE_PREFILL_CAUSAL,
+                                topk=self.B, out_idx=self.idx, out_score=self.idx_scores,
+                                workspace=self.score_ws, stream=stream)
+        else:
+            lsa.lsa_index_score(k_idx, self.scores, q_idx=q_idx, mode=lsa.MODE_PREFILL_CAUSAL,
+                                stream=stream)
+            lsa.lsa_topk_select(self.scores, self.B, self.idx.view(self.L * self.Hkv, self.B),
+                                out_score=self.idx_scores.view(self.L * self.Hkv, self.B),
+                                causal_group=self.Hkv, stream=stream)
+
+    def attend(self, q, k, v, stream=None):
+        lsa.lsa_indexed_attention(q, k, v, self.idx, self.out, lse=self.lse,
+                                  mode=lsa.MODE_PREFILL_CAUSAL, stream=stream)
+
+    def run(self, q_idx, k_idx, q, k, v, stream=None):
+        self.index(q_idx, k_idx, stream)
+        self.attend(q, k, v, stream)
+        return self
