@@ -103,6 +103,13 @@ enum { LSA_MODE_DECODE = 0, LSA_MODE_PREFILL_CAUSAL = 1 };
  *   (lsa_score_workspace_bytes).
  *
  * Accumulation is fp32 over exact products of the stored values.
+ *
+ * Selection hint (decode, optional): with `hint` set, the call also writes
+ * hint_count entries per row (lsa_score_hint_layout) at hint[row*hint_ld].
+ * Each entry is an order key (the 32-bit key under which larger scores rank
+ * higher) that at least hint_k of the row's scores reach, over disjoint slot
+ * groups. lsa_topk_select uses it to skip its sampling pass; it never
+ * changes a result, only how fast the select gets there.
  */
 typedef struct lsa_score_desc {
   uint32_t struct_size;      /* sizeof(lsa_score_desc) */
@@ -139,11 +146,17 @@ typedef struct lsa_score_desc {
   int32_t reserved1;
   int32_t* out_idx;          /* prefill fused: [L,Hkv,B] ascending, -1 padded */
   float* out_score;          /* prefill fused: [L,Hkv,B] or NULL */
+
+  uint32_t* hint;            /* decode: optional selection hint [rows, hint_ld] */
+  int64_t hint_ld;
 } lsa_score_desc;
 
 int lsa_index_score(const lsa_score_desc* desc, void* workspace, size_t workspace_bytes,
                     void* stream);
 size_t lsa_score_workspace_bytes(const lsa_score_desc* desc);
+/* Hint entries per row and keys each entry vouches for, for a decode
+ * descriptor (0 / 0 when the descriptor is invalid or not decode). */
+int lsa_score_hint_layout(const lsa_score_desc* desc, int32_t* count_per_row, int32_t* k);
 
 /* ------------------------------------------------------------------------ */
 /* lsa_topk_select                                                          */
@@ -165,6 +178,11 @@ size_t lsa_score_workspace_bytes(const lsa_score_desc* desc);
  * padding; out_count[row] (optional) is the number selected. Exact integer
  * work on order-preserving 32-bit keys of the fp32 scores: the result does
  * not depend on launch shape. Rows longer than 262144 slots use workspace.
+ *
+ * hint (optional): the selection hint lsa_index_score wrote with the same
+ * scores (hint_count entries per row, each vouching for hint_k keys). Any
+ * hint -- even a stale or wrong one -- gives the same, exact result: the
+ * select verifies what the hint implies and falls back when it fails.
  */
 typedef struct lsa_select_desc {
   uint32_t struct_size;      /* sizeof(lsa_select_desc) */
@@ -183,6 +201,10 @@ typedef struct lsa_select_desc {
   int32_t* out_idx;          /* [rows, B] */
   float* out_score;          /* [rows, B] or NULL */
   int32_t* out_count;        /* [rows] or NULL */
+  const uint32_t* hint;      /* [rows, hint_ld] or NULL */
+  int64_t hint_ld;
+  int32_t hint_count;        /* entries per row */
+  int32_t hint_k;            /* keys each entry vouches for */
 } lsa_select_desc;
 
 int lsa_topk_select(const lsa_select_desc* desc, void* workspace, size_t workspace_bytes,

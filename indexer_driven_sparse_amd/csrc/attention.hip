@@ -22,8 +22,12 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kGroups = kThreads / 16;   // lane groups per workgroup
-constexpr int kKC = 4;                   // keys per lane group per step
 constexpr float kLn2 = 0.69314718055994530942f;
+
+// keys a lane group loads per step: all of their K and V rows are requested
+// before any math; fewer for wide groups to bound registers
+template <int G>
+constexpr int keys_per_step() { return G <= 4 ? 8 : 4; }
 
 template <bool BF16, int CH>
 struct RowLoad {
@@ -54,6 +58,7 @@ __device__ __forceinline__ float chan(const RowLoad<BF16, CH>& r, int c) {
 
 template <bool BF16, int G, int D>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
+  constexpr int kKC = keys_per_step<G>();
   constexpr int CH = D / 16;             // channels per lane
   constexpr int ESZ = BF16 ? 2 : 4;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -108,10 +113,15 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
       const int i = base + j;
       const int32_t t = i < nk ? s_idx[i] : -1;
       ok[j] = t >= 0 && t < a.T;
-      if (ok[j]) {
-        load_row<BF16, CH>(kr[j], kbase + (int64_t)t * tok_bytes);
-        load_row<BF16, CH>(vr[j], vbase + (int64_t)t * tok_bytes);
-      } else {
+      // unconditional loads (a skipped entry reads row 0, then is zeroed), so
+      // all 2*kKC row requests of the step issue back to back
+      const int64_t tc = ok[j] ? t : 0;
+      load_row<BF16, CH>(kr[j], kbase + tc * tok_bytes);
+      load_row<BF16, CH>(vr[j], vbase + tc * tok_bytes);
+    }
+#pragma unroll
+    for (int j = 0; j < kKC; ++j) {
+      if (!ok[j]) {
 #pragma unroll
         for (int w = 0; w < RowLoad<BF16, CH>::kWords; ++w) kr[j].w[w] = vr[j].w[w] = 0u;
       }
@@ -213,30 +223,47 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   }
 }
 
-// Merge the split partials of one (row, KV head) by log-sum-exp.
+// Merge the split partials of one (row, KV head) by log-sum-exp: one
+// workgroup of G*D threads; thread (h, c) owns output channel c of head h.
+// Every load is issued before any dependent math: (m, l) of all splits into
+// LDS, and this thread's o of every split into registers.
+constexpr int kMaxSplits = 64;
+
 template <int G, int D>
-__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(G * D) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float s_m[kMaxSplits * G], s_l[kMaxSplits * G];
   const int64_t rowg = blockIdx.x;
   const int row = (int)(rowg / a.Hkv), g = (int)(rowg % a.Hkv);
-  for (int e = threadIdx.x; e < G * D; e += 256) {
-    const int h = e / D, c = e % D;
-    const float* p0 = a.partial + (rowg * a.splits * G + h) * (D + 2);
-    const int64_t sstride = (int64_t)G * (D + 2);
-    float M = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) M = fmaxf(M, p0[s * sstride]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < a.splits; ++s) {
-        const float* ps = p0 + s * sstride;
-        const float f = exp2f(ps[0] - M);
-        L += ps[1] * f;
-        O += ps[2 + c] * f;
+  const int t = threadIdx.x, h = t / D, c = t % D;
+  const int S = a.splits;
+  const int64_t sstride = (int64_t)G * (D + 2);
+  const float* base = a.partial + rowg * S * sstride;
+  if (t < S * G) {
+    const int s = t / G, hh = t % G;
+    s_m[t] = base[s * sstride + hh * (D + 2)];
+    s_l[t] = base[s * sstride + hh * (D + 2) + 1];
+  }
+  float o[kMaxSplits];
+#pragma unroll
+  for (int s = 0; s < kMaxSplits; ++s)
+    if (s < S) o[s] = base[s * sstride + h * (D + 2) + 2 + c];
+  __syncthreads();
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, s_m[s * G + h]);
+  float L = 0.f, O = 0.f;
+  if (M != -INFINITY) {
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) {
+      if (s < S) {
+        const float f = exp2f(s_m[s * G + h] - M);
+        L += s_l[s * G + h] * f;
+        O += o[s] * f;
       }
     }
-    const int64_t oh = (int64_t)row * a.Hq + (int64_t)g * G + h;
-    a.out[oh * D + c] = M == -INFINITY ? 0.f : O / L;
-    if (c == 0 && a.lse) a.lse[oh] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
   }
+  const int64_t oh = (int64_t)row * a.Hq + (int64_t)g * G + h;
+  a.out[oh * D + c] = M == -INFINITY ? 0.f : O / L;
+  if (c == 0 && a.lse) a.lse[oh] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2;
 }
 
 template <bool BF16, int G, int D>
@@ -246,7 +273,7 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((attn_kernel<BF16, G, D>), grid, dim3(kThreads), lds, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.splits == 1) return e;
-  hipLaunchKernelGGL((attn_merge_kernel<G, D>), dim3((unsigned)(a.rows * a.Hkv)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_merge_kernel<G, D>), dim3((unsigned)(a.rows * a.Hkv)), dim3(G * D), 0, s, a);
   return hipGetLastError();
 }
 
@@ -268,12 +295,11 @@ bool attention_supported(int G, int d) {
 }
 
 void attention_plan(int rows, int Hkv, int G, int d, int B, int* splits, int* keys_per_split) {
-  (void)G;
   (void)d;
   const int64_t units = (int64_t)rows * Hkv;
-  const int unit_keys = kGroups * kKC;   // keys one workgroup covers per step
-  int max_splits = (B + unit_keys - 1) / unit_keys;
-  int sp = (int)((1024 + units - 1) / units);  // aim for >= 1024 workgroups
+  const int unit_keys = kGroups * (G <= 4 ? 8 : 4);   // keys one workgroup covers per step
+  int max_splits = min(kMaxSplits, (B + unit_keys - 1) / unit_keys);
+  int sp = (int)((512 + units - 1) / units);  // about 2 workgroups per CU, all resident at once
   sp = max(1, min(sp, max_splits));
   int kps = (B + sp - 1) / sp;
   kps = (kps + unit_keys - 1) / unit_keys * unit_keys;

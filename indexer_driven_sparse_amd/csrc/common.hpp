@@ -47,6 +47,11 @@ __device__ __forceinline__ uint32_t order_key(float s) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inverse of order_key (a NaN key gives a NaN; -0 comes back as +0).
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
 // ---------------------------------------------------------------------------
 // Cross-lane sums with DPP (no LDS traffic). After sum_lanes<N>, every lane
 // of each aligned group of N lanes (N in 1..16) holds the group's sum. The

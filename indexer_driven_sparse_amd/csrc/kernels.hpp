@@ -23,8 +23,18 @@ struct ScoreDecodeArgs {
   int n_out;                         // slots per row
   float* scores;
   int64_t scores_ld;
-  int chunk;                         // slots per workgroup, multiple of 64
+  int chunk;                         // slots per workgroup, multiple of the step
+  uint32_t* hint;                    // optional selection hint [rows, hint_ld] (see below)
+  int64_t hint_ld;
 };
+int score_chunk_slots(int n_out, int rows);
+// Selection hint of the decode scoring kernel: the row is cut into groups of
+// kScoreHintGroup slots (one wave's loads of one loop step); for each group
+// the hint is the largest 16-bit order-key prefix p (as p << 16) that at
+// least kScoreHintK of the group's keys reach. Groups are numbered in slot
+// order of their first slot, kScoreHintGroupsPerStep per step.
+int score_hint_count(int n_out);       // hint entries per row
+int score_hint_k();                     // keys each hint vouches for
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, int rows, bool k_bf16, hipStream_t s);
 
 struct ScorePrefillArgs {
@@ -66,6 +76,9 @@ struct SelectArgs {
   float* out_score;
   int32_t* out_count;
   uint32_t* gbitmap;                 // workspace bitmaps for long rows, or nullptr
+  const uint32_t* hint;              // optional: per row hint_count keys, each reached by
+  int64_t hint_ld;                   //   at least hint_k of the row's valid keys
+  int hint_count, hint_k;
 };
 constexpr int kSelectLdsMaxSlots = 262144;
 size_t select_workspace(int rows, int n);

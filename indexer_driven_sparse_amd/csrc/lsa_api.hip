@@ -91,10 +91,12 @@ int validate_score(const lsa_score_desc* d, size_t* ws_need) {
     if (!d->scores || !al16(d->scores) || d->scores_ld % 4 != 0 || d->scores_ld < score_slots(d))
       return LSA_ERR_INVALID_ARG;
     if (d->topk != 0 || d->out_idx || d->out_score) return LSA_ERR_INVALID_ARG;
+    if (d->hint && (((uintptr_t)d->hint & 3u) || d->hint_ld < lsa::score_hint_count((int)score_slots(d))))
+      return LSA_ERR_INVALID_ARG;
     return LSA_OK;
   }
   if (d->mode == LSA_MODE_PREFILL_CAUSAL) {
-    if (d->n_seq != 1 || !d->q_idx || d->q || d->cand) return LSA_ERR_INVALID_ARG;
+    if (d->n_seq != 1 || !d->q_idx || d->q || d->cand || d->hint) return LSA_ERR_INVALID_ARG;
     if (!al16(d->q_idx)) return LSA_ERR_INVALID_ARG;
     if (d->topk < 0) return LSA_ERR_INVALID_ARG;
     if (d->topk == 0) {
@@ -126,6 +128,9 @@ int validate_select(const lsa_select_desc* d, size_t* ws_need) {
     if (d->cand_block < 1 || d->n_positions < 0) return LSA_ERR_INVALID_ARG;
     if (d->cand_ld < ((int64_t)d->n + d->cand_block - 1) / d->cand_block) return LSA_ERR_INVALID_ARG;
   }
+  if (d->hint && (d->hint_count < 1 || d->hint_k < 1 || d->hint_ld < d->hint_count ||
+                  ((uintptr_t)d->hint & 3u)))
+    return LSA_ERR_INVALID_ARG;
   *ws_need = lsa::select_workspace(d->rows, d->n);
   return LSA_OK;
 }
@@ -194,11 +199,9 @@ int lsa_index_score(const lsa_score_desc* d, void* ws, size_t ws_bytes, void* st
     a.scores = d->scores;
     a.scores_ld = d->scores_ld;
     const int rows = d->n_seq * d->n_kv_heads;
-    // about 2048 workgroups (8 per CU); chunks are multiples of 512 slots
-    int64_t per_row = (2048 + rows - 1) / rows;
-    int64_t chunk = (a.n_out + per_row - 1) / per_row;
-    chunk = std::max<int64_t>(512, (chunk + 511) / 512 * 512);
-    a.chunk = (int)chunk;
+    a.chunk = lsa::score_chunk_slots(a.n_out, rows);
+    a.hint = d->hint;
+    a.hint_ld = d->hint_ld;
     e = lsa::launch_score_decode(a, rows, d->k_idx_dtype == LSA_BF16, s);
   } else if (d->topk == 0) {
     lsa::ScorePrefillArgs a{};
@@ -236,6 +239,22 @@ size_t lsa_score_workspace_bytes(const lsa_score_desc* d) {
   return validate_score(d, &need) == LSA_OK ? need : 0;
 }
 
+int lsa_score_hint_layout(const lsa_score_desc* d, int32_t* count_per_row, int32_t* k) {
+  size_t need = 0;
+  int32_t c = 0, kk = 0;
+  if (d && d->struct_size == sizeof(lsa_score_desc) && d->mode == LSA_MODE_DECODE) {
+    lsa_score_desc probe = *d;
+    probe.hint = nullptr;   // the layout does not depend on the hint buffer itself
+    if (validate_score(&probe, &need) == LSA_OK) {
+      c = lsa::score_hint_count((int)score_slots(d));
+      kk = lsa::score_hint_k();
+    }
+  }
+  if (count_per_row) *count_per_row = c;
+  if (k) *k = kk;
+  return c > 0 ? LSA_OK : LSA_ERR_INVALID_ARG;
+}
+
 int lsa_topk_select(const lsa_select_desc* d, void* ws, size_t ws_bytes, void* stream) {
   size_t need = 0;
   LSA_TRY(validate_select(d, &need));
@@ -256,6 +275,10 @@ int lsa_topk_select(const lsa_select_desc* d, void* ws, size_t ws_bytes, void* s
   a.out_score = d->out_score;
   a.out_count = d->out_count;
   a.gbitmap = need ? (uint32_t*)ws : nullptr;
+  a.hint = d->hint;
+  a.hint_ld = d->hint_ld;
+  a.hint_count = d->hint ? d->hint_count : 0;
+  a.hint_k = d->hint ? d->hint_k : 0;
   hipError_t e = lsa::launch_select(a, d->rows, (hipStream_t)stream);
   return e == hipSuccess ? LSA_OK : hip_fail(e);
 }

@@ -14,8 +14,14 @@
 //     scores, so the fp32 score store is one coalesced 256-byte write;
 //   * the query prep (mean of the G heads, times W) runs at the top of each
 //     workgroup, so the step needs no separate launch for it.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
+
+#ifndef LSA_SCORE_WG_TARGET
+#define LSA_SCORE_WG_TARGET 2048   // workgroups per scoring launch (about 8 per CU)
+#endif
 
 namespace lsa {
 namespace {
@@ -23,7 +29,26 @@ namespace {
 constexpr int kScoreThreads = 256;
 constexpr int kMaxD = 512;
 constexpr int kMaxR = 128;
-constexpr int kGroupsInFlight = 2;  // 64-slot groups whose loads are issued together
+
+// Build-time tuning knobs (defaults are the tuned values for gfx950).
+#ifndef LSA_SCORE_GROUPS
+#define LSA_SCORE_GROUPS 2   // 64-slot groups per wave whose loads are issued together
+#endif
+#ifndef LSA_SCORE_NT
+#define LSA_SCORE_NT 1       // stream the projected-key cache with nontemporal loads
+#endif
+constexpr int kGroupsInFlight = LSA_SCORE_GROUPS;
+constexpr int kHintK = 2 * kGroupsInFlight;   // keys a hint vouches for (1 in 32 of its slots)
+
+__device__ __forceinline__ uint4 load_key16(const char* p) {
+#if LSA_SCORE_NT
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *(const uint4*)p;
+#endif
+}
 
 template <bool BF16>
 __device__ __forceinline__ float dot16(const uint4& w, const float* q) {
@@ -75,22 +100,37 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecode
   const int r = a.r;
 
   // ---- scoring preparation: q_idx = mean of the group's heads . W ----
+  // Thread (j, p) owns output channel j over input channels c = p + k*parts.
+  // Its W values are requested up front, before the query mean is formed, so
+  // the prologue costs about one memory round trip.
   if (a.q != nullptr) {
     const int G = a.Hq / a.Hkv;
+    const float* W = a.w + (a.w_per_head ? (int64_t)g * a.d * r : 0);
+    const int parts = kScoreThreads / r;  // r is a power of two <= 128
+    const int j = tid % r, p = tid / r;
+    constexpr int kPre = 32;
+    float wv[kPre];
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int c = p + k * parts;
+      wv[k] = c < a.d ? W[(int64_t)c * r + j] : 0.f;
+    }
     for (int c = tid; c < a.d; c += kScoreThreads) {
       float s = 0.f;
       for (int i = 0; i < G; ++i) {
-        int64_t off = ((int64_t)n * a.Hq + (int64_t)g * G + i) * a.d + c;
+        const int64_t off = ((int64_t)n * a.Hq + (int64_t)g * G + i) * a.d + c;
         s += a.q_bf16 ? bf16_to_f32(((const uint16_t*)a.q)[off]) : ((const float*)a.q)[off];
       }
       s_qbar[c] = s / (float)G;
     }
     __syncthreads();
-    const float* W = a.w + (a.w_per_head ? (int64_t)g * a.d * r : 0);
-    const int parts = kScoreThreads / r;  // r is a power of two <= 128
-    const int j = tid % r, p = tid / r;
     float acc = 0.f;
-    for (int c = p; c < a.d; c += parts) acc = fmaf(s_qbar[c], W[(int64_t)c * r + j], acc);
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      const int c = p + k * parts;
+      if (c < a.d) acc = fmaf(s_qbar[c], wv[k], acc);
+    }
+    for (int c = p + kPre * parts; c < a.d; c += parts) acc = fmaf(s_qbar[c], W[(int64_t)c * r + j], acc);
     s_part[tid] = acc;
     __syncthreads();
     if (tid < r) {
@@ -134,9 +174,10 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecode
           valid = pos >= 0;
         }
         ok[u][it] = valid;
-        raw[u][it] = valid ? *(const uint4*)(kbase + pos * tok_bytes) : make_uint4(0, 0, 0, 0);
+        raw[u][it] = valid ? load_key16(kbase + pos * tok_bytes) : make_uint4(0, 0, 0, 0);
       }
     }
+    uint32_t hkey[kGroupsInFlight];
 #pragma unroll
     for (int u = 0; u < kGroupsInFlight; ++u) {
       float mine = 0.f;
@@ -148,6 +189,25 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecode
       }
       const int64_t myslot = gb + (int64_t)u * 4 * 64 + (int64_t)l * KPI + kg;
       if (myslot < c1) srow[myslot] = mine;
+      hkey[u] = myslot < c1 ? order_key(mine) : 0u;
+    }
+    if (a.hint != nullptr) {
+      // selection hint of this wave's group of kGroupsInFlight*64 slots: the
+      // largest 16-bit key prefix that at least kHintK of them reach, by
+      // bisection with ballots (the same value on every lane)
+      uint32_t p = 0;
+#pragma unroll
+      for (int bit = 15; bit >= 0; --bit) {
+        const uint32_t cand = (p | (1u << bit)) << 16;
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < kGroupsInFlight; ++u) cnt += __popcll(__ballot(hkey[u] >= cand));
+        if (cnt >= kHintK) p |= 1u << bit;
+      }
+      if (lane == 0) {
+        const int64_t step = (gb - (int64_t)wid * 64) / (kGroupsInFlight * 4 * 64);
+        a.hint[(int64_t)row * a.hint_ld + step * 4 + wid] = p << 16;
+      }
     }
   }
 }
@@ -189,6 +249,23 @@ hipError_t launch_decode_lpk(const ScoreDecodeArgs& a, int rows, hipStream_t s) 
 }
 
 }  // namespace
+
+int score_hint_count(int n_out) {
+  const int step = kGroupsInFlight * 4 * 64;
+  return (n_out + step - 1) / step * 4;
+}
+
+int score_hint_k() { return kHintK; }
+
+int score_chunk_slots(int n_out, int rows) {
+  // about LSA_SCORE_WG_TARGET workgroups; a chunk is a whole number of the
+  // slots one workgroup covers per loop step
+  const int64_t step = (int64_t)kGroupsInFlight * 4 * 64;
+  const int64_t per_row = (LSA_SCORE_WG_TARGET + rows - 1) / rows;
+  int64_t chunk = (n_out + per_row - 1) / per_row;
+  chunk = (chunk + step - 1) / step * step;
+  return (int)std::max<int64_t>(step, chunk);
+}
 
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, int rows, bool k_bf16, hipStream_t s) {
   const int lpk = a.r * (k_bf16 ? 2 : 4) / 16;

@@ -49,7 +49,8 @@ class ScoreDesc(_c.Structure):
                 ("k_stride_seq", _I64), ("k_stride_head", _I64), ("k_stride_tok", _I64),
                 ("cand", _P), ("n_cand", _I32), ("cand_block", _I32), ("cand_ld", _I64),
                 ("scores", _P), ("scores_ld", _I64),
-                ("topk", _I32), ("reserved1", _I32), ("out_idx", _P), ("out_score", _P)]
+                ("topk", _I32), ("reserved1", _I32), ("out_idx", _P), ("out_score", _P),
+                ("hint", _P), ("hint_ld", _I64)]
 
 
 class SelectDesc(_c.Structure):
@@ -57,7 +58,8 @@ class SelectDesc(_c.Structure):
                 ("scores", _P), ("scores_ld", _I64), ("n_valid", _P),
                 ("causal_group", _I32), ("cand_block", _I32), ("cand", _P), ("cand_ld", _I64),
                 ("n_positions", _I32), ("reserved0", _I32),
-                ("out_idx", _P), ("out_score", _P), ("out_count", _P)]
+                ("out_idx", _P), ("out_score", _P), ("out_count", _P),
+                ("hint", _P), ("hint_ld", _I64), ("hint_count", _I32), ("hint_k", _I32)]
 
 
 class AttnDesc(_c.Structure):
@@ -93,6 +95,7 @@ _SIGS = {
     "lsa_project_keys": (_I32, [_P, _P]),
     "lsa_build_centroids": (_I32, [_P, _P]),
     "lsa_score_workspace_bytes": (_c.c_size_t, [_P]),
+    "lsa_score_hint_layout": (_I32, [_P, _P, _P]),
     "lsa_select_workspace_bytes": (_c.c_size_t, [_P]),
     "lsa_attention_workspace_bytes": (_c.c_size_t, [_P]),
     "lsa_status_str": (_c.c_char_p, [_I32]),
@@ -196,7 +199,8 @@ def _workspace(need: int, workspace, device):
 # entry points
 # ---------------------------------------------------------------------------
 
-def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score):
+def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score,
+                hint=None):
     d = ScoreDesc()
     d.struct_size = _c.sizeof(ScoreDesc)
     d.mode = mode
@@ -245,12 +249,27 @@ def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_id
     d.topk = topk
     d.out_idx = _ptr(out_idx)
     d.out_score = _ptr(out_score)
+    if hint is not None:
+        if hint.dtype != torch.int32 or not hint.is_contiguous():
+            raise ValueError("hint must be a contiguous int32 (bit pattern uint32) tensor")
+        d.hint = _ptr(hint)
+        d.hint_ld = hint.shape[-1]
     return d
+
+
+def lsa_score_hint_layout(k_idx, scores, *, q=None, w=None, q_idx=None, cand=None,
+                          cand_block=1):
+    """(entries per row, keys per entry) of the selection hint a decode
+    lsa_index_score call with these arguments writes."""
+    d = _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, MODE_DECODE, 0, None, None)
+    c, k = _c.c_int32(0), _c.c_int32(0)
+    _lib().lsa_score_hint_layout(_c.byref(d), _c.byref(c), _c.byref(k))
+    return int(c.value), int(k.value)
 
 
 def lsa_index_score(k_idx: torch.Tensor, scores: torch.Tensor | None, *, q=None, w=None,
                     q_idx=None, cand=None, cand_block: int = 1, mode: int = MODE_DECODE,
-                    topk: int = 0, out_idx=None, out_score=None, workspace=None,
+                    topk: int = 0, out_idx=None, out_score=None, hint=None, workspace=None,
                     stream=None) -> None:
     """Indexer scores. Decode: k_idx [N,Hkv,T,r] (any strides, r contiguous);
     either q [N,Hq,d] with w [d,r] / [Hkv,d,r] (prep fused; q_idx, if given,
@@ -258,7 +277,8 @@ def lsa_index_score(k_idx: torch.Tensor, scores: torch.Tensor | None, *, q=None,
     [N,Hkv,nc] int32 with cand_block; scores fp32 [N,Hkv,n_out].
     Prefill: k_idx [L,Hkv,r], q_idx [L,Hkv,r]; topk=0 writes scores
     [L,Hkv,L]; topk=B fills out_idx [L,Hkv,B] (and out_score)."""
-    d = _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score)
+    d = _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score,
+                    hint)
     lib = _lib()
     ws, wsb = _workspace(lib.lsa_score_workspace_bytes(_c.byref(d)), workspace, k_idx.device)
     _check("lsa_index_score", lib.lsa_index_score(_c.byref(d), _ptr(ws), wsb, _stream(stream)))
@@ -272,7 +292,7 @@ def lsa_score_workspace_bytes(k_idx, scores, *, q=None, w=None, q_idx=None, cand
 
 
 def _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal_group, cand,
-                 cand_block, n_positions):
+                 cand_block, n_positions, hint=None, hint_k=0):
     rows = scores.numel() // scores.shape[-1]
     if not out_idx.is_contiguous() or out_idx.numel() != rows * topk or out_idx.dtype != torch.int32:
         raise ValueError("out_idx must be contiguous int32 [rows, B]")
@@ -304,17 +324,25 @@ def _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal
     d.out_idx = _ptr(out_idx)
     d.out_score = _ptr(out_score)
     d.out_count = _ptr(out_count)
+    if hint is not None:
+        if not hint.is_contiguous() or hint.numel() // hint.shape[-1] != rows:
+            raise ValueError("hint must be contiguous [rows, hint_count]")
+        d.hint = _ptr(hint)
+        d.hint_ld = hint.shape[-1]
+        d.hint_count = hint.shape[-1]
+        d.hint_k = hint_k
     return d
 
 
 def lsa_topk_select(scores: torch.Tensor, topk: int, out_idx: torch.Tensor, *, n=None,
                     out_score=None, out_count=None, n_valid=None, causal_group: int = 0,
-                    cand=None, cand_block: int = 1, n_positions: int = 0, workspace=None,
-                    stream=None) -> None:
+                    cand=None, cand_block: int = 1, n_positions: int = 0, hint=None,
+                    hint_k: int = 0, workspace=None, stream=None) -> None:
     """Exact top-B per row of scores [..., n] (rows evenly spaced): ascending
-    positions in out_idx [rows, B], -1 padded."""
+    positions in out_idx [rows, B], -1 padded. hint/hint_k: the selection
+    hint of the scoring call (speed only, never the result)."""
     d = _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal_group, cand,
-                     cand_block, n_positions)
+                     cand_block, n_positions, hint, hint_k)
     lib = _lib()
     ws, wsb = _workspace(lib.lsa_select_workspace_bytes(_c.byref(d)), workspace, scores.device)
     _check("lsa_topk_select", lib.lsa_topk_select(_c.byref(d), _ptr(ws), wsb, _stream(stream)))
@@ -386,6 +414,21 @@ def attention_workspace_bytes_for(rows: int, Hq: int, Hkv: int, d: int, B: int, 
     dd.q_dtype = dd.kv_dtype = kv_dtype
     dd.kv_stride_seq, dd.kv_stride_tok, dd.kv_stride_head = T * Hkv * d, Hkv * d, d
     return int(_lib().lsa_attention_workspace_bytes(_c.byref(dd)))
+
+
+def score_hint_layout_for(N: int, Hkv: int, n_out: int, r: int = 64, dtype: int = BF16):
+    """(entries per row, keys per entry) of the selection hint written by a
+    decode scoring call over n_out slots per row (shape only)."""
+    dd = ScoreDesc()
+    dd.struct_size = _c.sizeof(ScoreDesc)
+    dd.mode, dd.n_seq, dd.n_kv_heads, dd.n_keys, dd.rank = MODE_DECODE, N, Hkv, n_out, r
+    dd.q_idx = dd.k_idx = dd.scores = 256          # placeholders: sizing never dereferences
+    dd.k_idx_dtype = dtype
+    dd.k_stride_tok, dd.k_stride_head, dd.k_stride_seq = r, n_out * r, Hkv * n_out * r
+    dd.scores_ld = (n_out + 3) // 4 * 4
+    c, k = _c.c_int32(0), _c.c_int32(0)
+    _lib().lsa_score_hint_layout(_c.byref(dd), _c.byref(c), _c.byref(k))
+    return int(c.value), int(k.value)
 
 
 def prefill_score_workspace_bytes_for(L: int, Hkv: int, r: int, B: int) -> int:

@@ -33,8 +33,9 @@ class DecodePlan:
     """Buffers for one flat decode step of N sequences with T cached tokens."""
 
     def __init__(self, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int,
-                 device="cuda", kv_dtype=torch.bfloat16):
+                 device="cuda", kv_dtype=torch.bfloat16, with_idx_scores: bool = False):
         self.N, self.Hq, self.Hkv, self.T, self.d, self.r, self.B = N, Hq, Hkv, T, d, r, B
+        self.with_idx_scores = with_idx_scores
         f32 = dict(dtype=torch.float32, device=device)
         self.scores = torch.empty(N, Hkv, _ld4(T), **f32)[:, :, :T]
         self.q_idx = torch.empty(N, Hkv, r, **f32)
@@ -42,15 +43,21 @@ class DecodePlan:
         self.idx_scores = torch.empty(N, Hkv, B, **f32)
         self.out = torch.empty(N, Hq, d, **f32)
         self.lse = torch.empty(N, Hq, **f32)
+        # selection hint written by the scoring kernel, read by the select
+        self.hint_count, self.hint_k = lsa.score_hint_layout_for(N, Hkv, T, r, _code(kv_dtype))
+        self.hint = torch.empty(N * Hkv, max(1, self.hint_count), dtype=torch.int32, device=device)
         # attention workspace, sized by the library for this shape
         need = lsa.attention_workspace_bytes_for(N, Hq, Hkv, d, B, T, _code(kv_dtype))
         self.attn_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
 
     def score(self, q, w, k_idx, stream=None):
-        lsa.lsa_index_score(k_idx, self.scores, q=q, w=w, q_idx=self.q_idx, stream=stream)
+        lsa.lsa_index_score(k_idx, self.scores, q=q, w=w, q_idx=self.q_idx,
+                            hint=self.hint if self.hint_count else None, stream=stream)
 
     def select(self, stream=None):
-        lsa.lsa_topk_select(self.scores, self.B, self.idx, out_score=self.idx_scores,
+        lsa.lsa_topk_select(self.scores, self.B, self.idx,
+                            out_score=self.idx_scores if self.with_idx_scores else None,
+                            hint=self.hint if self.hint_count else None, hint_k=self.hint_k,
                             stream=stream)
 
     def attend(self, q, k, v, stream=None):
@@ -67,7 +74,8 @@ class DecodePlan:
 def decode_step(q, w, k_idx, k, v, B, stream=None) -> dict:
     """One flat decode step; returns the step's buffers (device tensors)."""
     N, Hkv, T, r = k_idx.shape
-    plan = DecodePlan(N, q.shape[1], Hkv, T, q.shape[2], r, B, device=q.device, kv_dtype=k.dtype)
+    plan = DecodePlan(N, q.shape[1], Hkv, T, q.shape[2], r, B, device=q.device, kv_dtype=k.dtype,
+                      with_idx_scores=True)
     plan.run(q, w, k_idx, k, v, stream)
     return {"q_idx": plan.q_idx, "scores": plan.scores, "idx": plan.idx,
             "idx_scores": plan.idx_scores, "out": plan.out, "lse": plan.lse}
@@ -94,17 +102,24 @@ class HierarchicalPlan:
         self.lse = torch.empty(N, Hq, **f32)
         need = lsa.attention_workspace_bytes_for(N, Hq, Hkv, d, B, T, _code(kv_dtype))
         self.attn_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        code = _code(kv_dtype)
+        self.hc_count, self.hint_k = lsa.score_hint_layout_for(N, Hkv, self.n_blocks, r, code)
+        self.hf_count, _ = lsa.score_hint_layout_for(N, Hkv, self.n_fine, r, code)
+        self.hint_c = torch.empty(N * Hkv, max(1, self.hc_count), dtype=torch.int32, device=device)
+        self.hint_f = torch.empty(N * Hkv, max(1, self.hf_count), dtype=torch.int32, device=device)
 
     def run(self, q, w, k_idx, centroids, k, v, stream=None):
         # coarse: score every block summary, keep the top B_coarse blocks
-        lsa.lsa_index_score(centroids, self.coarse, q=q, w=w, q_idx=self.q_idx, stream=stream)
-        lsa.lsa_topk_select(self.coarse, self.B_coarse, self.blocks, stream=stream)
+        lsa.lsa_index_score(centroids, self.coarse, q=q, w=w, q_idx=self.q_idx, hint=self.hint_c,
+                            stream=stream)
+        lsa.lsa_topk_select(self.coarse, self.B_coarse, self.blocks, hint=self.hint_c,
+                            hint_k=self.hint_k, stream=stream)
         # fine: score only the kept blocks' tokens, keep the top-B positions
         lsa.lsa_index_score(k_idx, self.fine, q_idx=self.q_idx, cand=self.blocks,
-                            cand_block=self.block, stream=stream)
+                            cand_block=self.block, hint=self.hint_f, stream=stream)
         lsa.lsa_topk_select(self.fine, self.B, self.idx, out_score=self.idx_scores,
                             cand=self.blocks, cand_block=self.block, n_positions=self.T,
-                            stream=stream)
+                            hint=self.hint_f, hint_k=self.hint_k, stream=stream)
         lsa.lsa_indexed_attention(q, k, v, self.idx, self.out, lse=self.lse,
                                   workspace=self.attn_ws, stream=stream)
         return self

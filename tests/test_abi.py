@@ -198,3 +198,22 @@ def test_binding_raises_on_bad_arguments():
     with pytest.raises(lsa.LsaError) as e:
         lsa.lsa_index_score(k, s, q_idx=torch.zeros(1, 1, 48), stream=0)
     assert e.value.status == UNSUPPORTED
+
+
+def test_hint_validation_and_layout():
+    lib = lsa._lib()
+    d = _score_desc(hint=0x7002, hint_ld=4)           # misaligned
+    assert _call_score(d) == INVALID
+    d = _score_desc(hint=0x7000, hint_ld=0)           # too short for the layout
+    assert _call_score(d) == INVALID
+    c, k = ctypes.c_int32(0), ctypes.c_int32(0)
+    assert lib.lsa_score_hint_layout(ctypes.byref(_score_desc()), ctypes.byref(c), ctypes.byref(k)) == 0
+    assert c.value >= 1 and k.value >= 1
+    count, kk = lsa.score_hint_layout_for(4, 8, 131072)
+    assert count * kk * 32 == 131072          # one key vouched per 32 slots
+    s = _select_desc(hint=0x5000, hint_count=0, hint_k=4, hint_ld=8)
+    assert lib.lsa_topk_select(ctypes.byref(s), None, 0, None) == INVALID
+    s = _select_desc(hint=0x5000, hint_count=8, hint_k=0, hint_ld=8)
+    assert lib.lsa_topk_select(ctypes.byref(s), None, 0, None) == INVALID
+    s = _select_desc(hint=0x5000, hint_count=8, hint_k=4, hint_ld=7)
+    assert lib.lsa_topk_select(ctypes.byref(s), None, 0, None) == INVALID

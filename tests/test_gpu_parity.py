@@ -446,3 +446,49 @@ def test_decode_step_budget_T_is_dense_attention():
     Vt = torch.from_numpy(decoded(case.V)).permute(0, 2, 1, 3).repeat_interleave(4, 1).contiguous()
     o = torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt)[:, :, 0].numpy()
     np.testing.assert_allclose(g["out"], o, rtol=0, atol=ATTN_ATOL)
+
+
+# --------------------------------------------------------------------------
+# selection hint: speed only, never the result
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,over", [("decode_t128k_b2048", {"N": 1}),
+                                       ("decode_t32k_hitters", {}),
+                                       ("decode_t4k_fp32", {})])
+def test_select_hint_never_changes_the_result(name, over):
+    case = synth.workload(name, **over)
+    say("select hint", name, over)
+    k_idx = oracle.project_keys(case.K, case.W, case.dtype)
+    kd = dev(k_idx)
+    N, Hkv, T, B = case.N, case.Hkv, case.T, case.B
+    sc = torch.empty(N, Hkv, T + (4 - T % 4) % 4, device="cuda")[:, :, :T]
+    count, k = lsa.lsa_score_hint_layout(kd, sc, q=dev(case.Q), w=dev(case.W))
+    assert count > 0 and k > 0
+    hint = torch.full((N * Hkv, count), 0x12345678, dtype=torch.int32, device="cuda")
+    lsa.lsa_index_score(kd, sc, q=dev(case.Q), w=dev(case.W), hint=hint)
+    assert not (hint == 0x12345678).any(), "every hint entry is written"
+    outs = []
+    for h in [hint, None, torch.randint(-2**31, 2**31 - 1, hint.shape, dtype=torch.int32, device="cuda"),
+              torch.zeros_like(hint), torch.full_like(hint, -1)]:
+        idx = torch.empty(N * Hkv, B, dtype=torch.int32, device="cuda")
+        lsa.lsa_topk_select(sc, B, idx, hint=h, hint_k=k)
+        outs.append(host(idx))
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+    ref, _, _ = oracle.topk(host(sc).reshape(N * Hkv, T).astype(np.float64), B)
+    np.testing.assert_array_equal(outs[0], ref)
+    # every entry is reached by at least k keys of its row (its group's claim
+    # implies this), and the entries together vouch for k*count keys
+    keys = host(sc).reshape(N * Hkv, T).view(np.uint32)
+    okey = np.sort(np.where(keys & 0x80000000, ~keys, keys | 0x80000000).astype(np.uint32), axis=1)
+    hv = host(hint).view(np.uint32)
+    r_th = -(-B // k)
+    for row in range(N * Hkv):
+        reach = T - np.searchsorted(okey[row], hv[row], side="left")
+        assert (reach >= k).all()
+        if r_th > count:
+            continue   # the hints cannot vouch for B keys; the select samples instead
+        # the threshold the hints imply keeps at least B keys, and not many more
+        t = np.sort(hv[row])[::-1][r_th - 1]
+        kept = T - np.searchsorted(okey[row], t, side="left")
+        assert B <= kept <= max(8 * B, 2 * B + 4096), (row, kept)
