@@ -94,9 +94,10 @@ __device__ __forceinline__ int rank_below(uint64_t mask) {
 }
 
 // Exclusive prefix sum over a block of NT threads (NT a multiple of 64, at
-// most 1024). `scratch` holds NT/64 + 1 ints of LDS. Returns the exclusive
-// prefix of `v`; *total receives the block sum. Contains barriers: every
-// thread of the block must call it.
+// most 1024). `scratch` holds NT/64 ints of LDS. Returns the exclusive
+// prefix of `v`; *total receives the block sum. Every thread reads all wave
+// totals (broadcast LDS reads), so only two barriers are paid. Every thread
+// of the block must call it.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -108,20 +109,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   }
   if (lane == 63) scratch[wid] = x;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int acc = 0;
-    for (int w = 0; w < NT / 64; ++w) {
-      int t = scratch[w];
-      scratch[w] = acc;
-      acc += t;
-    }
-    scratch[NT / 64] = acc;
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) {
+    const int t = scratch[w];
+    base += w < wid ? t : 0;
+    tot += t;
   }
-  __syncthreads();
-  int res = scratch[wid] + x - v;
-  *total = scratch[NT / 64];
-  __syncthreads();
-  return res;
+  *total = tot;
+  __syncthreads();   // scratch may be reused right after
+  return base + x - v;
 }
 
 }  // namespace lsa

@@ -79,9 +79,21 @@ struct SelectArgs {
   const uint32_t* hint;              // optional: per row hint_count keys, each reached by
   int64_t hint_ld;                   //   at least hint_k of the row's valid keys
   int hint_count, hint_k;
+  // segmented collect (long rows with a hint): per (row, segment) a list of
+  // (score bits, slot) pairs in slot order and its {count, max key, t_lo}
+  int2* seg_list;
+  int4* seg_meta;
+  int nseg;
 };
 constexpr int kSelectLdsMaxSlots = 262144;
-size_t select_workspace(int rows, int n);
+// Workspace of a select: bitmaps of rows longer than kSelectLdsMaxSlots,
+// then the segment lists when the segmented collect applies.
+size_t select_workspace(int rows, int n, int B, bool hint_usable);
+// Segments of the segmented collect for a row of n slots (0: not used).
+int select_segments(int n, int B, bool hint_usable);
+// Points gbitmap / seg_meta / seg_list into ws (select_workspace bytes) and
+// sets nseg; needs n, B and the hint fields set.
+void select_bind_workspace(SelectArgs& a, int rows, void* ws);
 hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s);
 
 // ----- indexed attention -----------------------------------------------------

@@ -131,7 +131,8 @@ int validate_select(const lsa_select_desc* d, size_t* ws_need) {
   if (d->hint && (d->hint_count < 1 || d->hint_k < 1 || d->hint_ld < d->hint_count ||
                   ((uintptr_t)d->hint & 3u)))
     return LSA_ERR_INVALID_ARG;
-  *ws_need = lsa::select_workspace(d->rows, d->n);
+  const bool hint_usable = d->hint && (int64_t)d->hint_count * d->hint_k >= d->topk;
+  *ws_need = lsa::select_workspace(d->rows, d->n, d->topk, hint_usable);
   return LSA_OK;
 }
 
@@ -274,11 +275,11 @@ int lsa_topk_select(const lsa_select_desc* d, void* ws, size_t ws_bytes, void* s
   a.out_idx = d->out_idx;
   a.out_score = d->out_score;
   a.out_count = d->out_count;
-  a.gbitmap = need ? (uint32_t*)ws : nullptr;
   a.hint = d->hint;
   a.hint_ld = d->hint_ld;
   a.hint_count = d->hint ? d->hint_count : 0;
   a.hint_k = d->hint ? d->hint_k : 0;
+  lsa::select_bind_workspace(a, d->rows, ws);
   hipError_t e = lsa::launch_select(a, d->rows, (hipStream_t)stream);
   return e == hipSuccess ? LSA_OK : hip_fail(e);
 }

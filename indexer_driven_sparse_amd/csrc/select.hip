@@ -112,19 +112,20 @@ __device__ __forceinline__ uint32_t word_from_nibbles(uint32_t nib, int lane) {
 // (count above b) < need <= (count above b) + hist[b], for nb <= 2048 bins.
 // Writes sh.bin / sh.above (left unchanged when the total is below need)
 // and returns the total through *total. Contains barriers.
-__device__ __forceinline__ void find_bin(SelShared& sh, int nb, int need, int* total) {
+__device__ __forceinline__ void find_bin(SelShared& sh, const uint32_t* hist, int nb, int need,
+                                         int* total) {
   const int t = threadIdx.x;
   const int per = (nb + kThreads - 1) / kThreads;
   const int hi = nb - 1 - t * per;
   int c = 0;
   for (int k = 0; k < per; ++k)
-    if (hi - k >= 0) c += (int)sh.hist[hi - k];
+    if (hi - k >= 0) c += (int)hist[hi - k];
   int tot;
   const int above = block_exclusive_scan<kThreads>(c, sh.scan, &tot);
   int acc = above;
   for (int k = 0; k < per; ++k) {
     if (hi - k < 0) break;
-    const int h = (int)sh.hist[hi - k];
+    const int h = (int)hist[hi - k];
     if (acc < need && need <= acc + h) {
       sh.bin = hi - k;
       sh.above = acc;
@@ -173,84 +174,242 @@ __device__ __forceinline__ void wave_append(SelShared& sh, const float* val, int
   }
 }
 
-// Orders this wave's LDS accesses across its lanes (wavefront scope).
-__device__ __forceinline__ void wave_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-}
-
-// Same result as refine_range, computed by wave 0 alone: each level's
-// histogram, suffix scan and bin search stay inside one wave, so no block
-// barrier is paid per level. All threads call it; one barrier publishes
-// tau, need and the count of keys equal to tau.
-__device__ __forceinline__ uint32_t refine_range_wave(SelShared& sh, int ncand, uint32_t lo,
-                                                      uint32_t hi, int* need, int* ties) {
-  const int lane = threadIdx.x & 63;
-  if (threadIdx.x < 64) {
-    int fixed = lo == hi ? 32 : __clz(lo ^ hi);
-    uint32_t tau = fixed == 0 ? 0u : (lo & (~0u << (32 - fixed)));
-    int nd = *need;
-    int eq = ncand;   // with no level, every listed key equals tau
-    while (fixed < 32) {
-      const int width = min(11, 32 - fixed);
-      const int shift = 32 - fixed - width;
-      const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
-      const int nb = 1 << width;
-      for (int i = lane; i < nb; i += 64) sh.hist[i] = 0u;
-      wave_sync();
-      for (int i = lane; i < ncand; i += 64) {
-        const uint32_t key = sh.ckey[i];
-        if ((key & pmask) == tau) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
-      }
-      wave_sync();
-      // lane l sums bins [top - per + 1, top] (lane 0 the highest); an
-      // exclusive scan over lanes gives the count above each lane's bins
-      const int per = max(1, nb / 64);
-      const int top = nb - 1 - lane * per;
-      int c = 0;
-      for (int k = 0; k < per; ++k)
-        if (top - k >= 0) c += (int)sh.hist[top - k];
-      int incl = c;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-      }
-      int acc = incl - c, fbin = -1, fabove = 0, fcnt = 0;
-      for (int k = 0; k < per; ++k) {
-        if (top - k < 0) break;
-        const int h = (int)sh.hist[top - k];
-        if (acc < nd && nd <= acc + h) {
-          fbin = top - k;
-          fabove = acc;
-          fcnt = h;
-        }
-        acc += h;
-      }
-      const uint64_t m = ballot64(fbin >= 0);
-      const int src = __ffsll((unsigned long long)m) - 1;
-      const int bin = __shfl(fbin, src, 64);
-      nd -= __shfl(fabove, src, 64);
-      eq = __shfl(fcnt, src, 64);
-      tau |= (uint32_t)bin << shift;
-      fixed += width;
-      wave_sync();
+// Exact refine of an LDS list whose keys all lie in [lo, hi]: radix levels
+// of up to 11 bits below the common prefix of lo and hi, each a block-wide
+// histogram of the listed keys that match the prefix so far. On return tau
+// is the need-th largest listed key, *need the number of keys equal to tau
+// to take and *ties the number of listed keys equal to tau. Contains
+// barriers.
+__device__ __forceinline__ uint32_t refine_list(SelShared& sh, int ncand, uint32_t lo, uint32_t hi,
+                                                int* need, int* ties) {
+  int fixed = lo == hi ? 32 : __clz(lo ^ hi);
+  uint32_t tau = fixed == 0 ? 0u : (lo & (~0u << (32 - fixed)));
+  int nd = *need;
+  int eq = ncand;   // with no level, every listed key equals tau
+  while (fixed < 32) {
+    const int width = min(11, 32 - fixed);
+    const int shift = 32 - fixed - width;
+    const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
+    const int nb = 1 << width;
+    zero_hist(sh);
+    __syncthreads();
+    for (int i = threadIdx.x; i < ncand; i += kThreads) {
+      const uint32_t key = sh.ckey[i];
+      if ((key & pmask) == tau) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
     }
-    if (lane == 0) {
-      sh.wval[0] = (int)tau;
-      sh.wval[1] = nd;
-      sh.wval[2] = eq;
-    }
+    __syncthreads();
+    int tl;
+    find_bin(sh, sh.hist, nb, nd, &tl);
+    const int bin = sh.bin;
+    nd -= sh.above;
+    eq = (int)sh.hist[bin];
+    tau |= (uint32_t)bin << shift;
+    fixed += width;
+    __syncthreads();   // hist and bin are rewritten by the next level
   }
-  __syncthreads();
-  const uint32_t tau = (uint32_t)sh.wval[0];
-  *need = sh.wval[1];
-  *ties = sh.wval[2];
-  __syncthreads();   // wval is reused later
+  *need = nd;
+  *ties = eq;
   return tau;
 }
 
-template <bool CAND, bool GBM>
+// ---------------------------------------------------------------------------
+// Segmented collect (long rows with a selection hint). A row is cut into
+// segments of kSeg slots, one 256-thread workgroup each, so a few rows
+// still spread over every CU. Each workgroup issues its segment's loads,
+// derives the row's threshold t_lo from the hint while they are in flight
+// (every workgroup of the row gets the same value), and writes the
+// segment's slots whose keys reach t_lo, in slot order, as (score bits,
+// slot) pairs, with {count, max key, t_lo}. The row kernel then refines the
+// concatenated lists (see select_kernel, PRE).
+// ---------------------------------------------------------------------------
+constexpr int kSegThreads = 256;
+constexpr int kSegWaves = kSegThreads / 64;
+constexpr int kSegUnroll = 8;
+constexpr int kSeg = kSegThreads * 4 * kSegUnroll;   // 8192 slots
+constexpr int kSegUnits = kSegUnroll * kSegWaves;    // (loop step, wave) units, in slot order
+
+struct SegShared {
+  uint32_t h1[256];
+  uint32_t h2[256];
+  int wsum[kSegWaves];
+  int bin, above;
+  int ucnt[kSegUnits];
+  int uoff[kSegUnits];
+  uint32_t wmax[kSegWaves];
+};
+
+// One 8-bit radix level over a 256-bin histogram: the bin holding the
+// need-th largest value (bins scanned from the top), published in sh.bin /
+// sh.above. sh.bin is left unchanged when the histogram holds fewer than
+// need values. Contains barriers.
+__device__ __forceinline__ void seg_level(SegShared& sh, const uint32_t* h, int need) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int c = (int)h[255 - t];
+  int x = c;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) sh.wsum[w] = x;
+  __syncthreads();
+  int base = 0;
+#pragma unroll
+  for (int q = 0; q < kSegWaves; ++q) base += q < w ? sh.wsum[q] : 0;
+  const int excl = base + x - c;
+  if (excl < need && need <= excl + c) {
+    sh.bin = 255 - t;
+    sh.above = excl;
+  }
+  __syncthreads();
+}
+
+template <bool CAND>
+__global__ __launch_bounds__(kSegThreads) void select_collect_kernel(SelectArgs a) {
+  __shared__ SegShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int row = blockIdx.x / a.nseg, seg = blockIdx.x - row * a.nseg;
+  int64_t nv = a.n;
+  if (a.n_valid) nv = min<int64_t>(nv, (int64_t)max(0, a.n_valid[row]));
+  if (a.causal_group > 0) nv = min<int64_t>(nv, (int64_t)row / a.causal_group + 1);
+  const int64_t s0 = (int64_t)seg * kSeg;
+  int4* meta = a.seg_meta + (int64_t)row * a.nseg + seg;
+  if (s0 >= nv) {   // nothing valid here (block-uniform)
+    if (tid == 0) *meta = make_int4(0, 0, 0, 0);
+    return;
+  }
+  const float* srow = a.scores + (int64_t)row * a.scores_ld;
+  const int32_t* crow = CAND ? a.cand + (int64_t)row * a.cand_ld : nullptr;
+
+  // 1. the segment's loads go out first
+  float v[4 * kSegUnroll];
+  const bool full = s0 + kSeg <= nv;
+  if (full) {
+#pragma unroll
+    for (int j = 0; j < kSegUnroll; ++j) {
+      const float4 x = *(const float4*)(srow + s0 + j * kSegThreads * 4 + tid * 4);
+      v[4 * j] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSegUnroll; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[4 * j + k] = srow[min(s0 + j * kSegThreads * 4 + tid * 4 + k, nv - 1)];
+  }
+
+  // 2. t_lo from the hint. Entry h vouches that hint_k valid keys of its
+  // (disjoint) slot group reach it; folding m entries into their minimum
+  // vouches for m*hint_k keys. The r-th largest folded entry, with
+  // r = ceil(B / (m*hint_k)), is then reached by at least B keys. It is
+  // found on the 16-bit prefixes by two 8-bit radix levels.
+  sh.h1[tid] = 0u;
+  sh.h2[tid] = 0u;
+  if (tid == 0) sh.bin = -1;
+  const uint32_t* hrow = a.hint + (int64_t)row * a.hint_ld;
+  const int m = (a.hint_count + 4 * kSegThreads - 1) / (4 * kSegThreads);
+  const int ne = (a.hint_count + m - 1) / m;
+  const int r = (a.B + m * a.hint_k - 1) / (m * a.hint_k);
+  uint32_t p[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + q * kSegThreads;
+    uint32_t val = 0xffffffffu;
+    for (int mm = 0; mm < m; ++mm) {
+      const int h = e * m + mm;
+      val = min(val, h < a.hint_count ? hrow[h] : 0u);
+    }
+    p[q] = val >> 16;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (tid + q * kSegThreads < ne) atomicAdd(&sh.h1[p[q] >> 8], 1u);
+  __syncthreads();
+  uint32_t t_lo = 0u;
+  if (r <= ne) {
+    seg_level(sh, sh.h1, r);
+    const int b1 = sh.bin, r2 = r - sh.above;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (tid + q * kSegThreads < ne && (int)(p[q] >> 8) == b1) atomicAdd(&sh.h2[p[q] & 255u], 1u);
+    __syncthreads();
+    seg_level(sh, sh.h2, r2);
+    t_lo = ((uint32_t)b1 << 24) | ((uint32_t)sh.bin << 16);
+  }
+
+  // 3. compare (float order is key order, -0 == +0; a threshold at or below
+  // the key of -inf takes every non-NaN score, t_lo == 0 takes everything)
+  const bool take_all = t_lo == 0u;
+  const float t_f = t_lo <= 0x007fffffu ? -INFINITY : key_to_float(t_lo);
+  uint32_t flags = 0;
+  float vmax = v[0];
+#pragma unroll
+  for (int j = 0; j < kSegUnroll; ++j)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t s = s0 + j * kSegThreads * 4 + tid * 4 + k;
+      bool take = take_all || v[4 * j + k] >= t_f;
+      if (!full) take = take && s < nv;
+      if constexpr (CAND) take = take && slot_ok<CAND>(a, crow, s, nv);
+      flags |= (uint32_t)take << (4 * j + k);
+      vmax = fmaxf(vmax, v[4 * j + k]);   // an upper bound of the listed keys
+    }
+
+  // 4. ranks in slot order: unit (j, wave) holds 256 consecutive slots,
+  // lane-major; a lane's entries follow those of the lanes below it
+  int lb[kSegUnroll];
+#pragma unroll
+  for (int j = 0; j < kSegUnroll; ++j) {
+    int cnt = 0, below = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint64_t mk = ballot64((flags >> (4 * j + k)) & 1u);
+      cnt += __popcll(mk);
+      below += rank_below(mk);
+    }
+    lb[j] = below;
+    if (lane == 0) sh.ucnt[j * kSegWaves + wid] = cnt;
+  }
+  uint32_t kmax = order_key(vmax);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  if (lane == 0) sh.wmax[wid] = kmax;
+  __syncthreads();
+  if (tid < 64) {
+    const int c = lane < kSegUnits ? sh.ucnt[lane] : 0;
+    int x = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane < kSegUnits) sh.uoff[lane] = x - c;
+    if (lane == 63) {
+      uint32_t km = sh.wmax[0];
+#pragma unroll
+      for (int q = 1; q < kSegWaves; ++q) km = max(km, sh.wmax[q]);
+      *meta = make_int4(x, (int)km, (int)t_lo, 0);
+    }
+  }
+  __syncthreads();
+
+  // 5. write the listed (score bits, slot) pairs
+  int2* out = a.seg_list + ((int64_t)row * a.nseg + seg) * kSeg;
+#pragma unroll
+  for (int j = 0; j < kSegUnroll; ++j) {
+    uint32_t f = (flags >> (4 * j)) & 15u;
+    int pos = sh.uoff[j * kSegWaves + wid] + lb[j];
+    while (f) {
+      const int k = __ffs(f) - 1;
+      f &= f - 1;
+      const float x = k == 0 ? v[4 * j] : k == 1 ? v[4 * j + 1] : k == 2 ? v[4 * j + 2] : v[4 * j + 3];
+      out[pos++] = make_int2(__float_as_int(x), (int)(s0 + j * kSegThreads * 4 + tid * 4 + k));
+    }
+  }
+}
+
+template <bool CAND, bool GBM, bool PRE>
 __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
   SelShared& sh = *reinterpret_cast<SelShared*>(smem_raw);
@@ -278,9 +437,14 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   const int64_t tile = (int64_t)kThreads * 4 * kUnroll;
 
   zero_hist(sh);
-  for (int i = tid; i < nw; i += kThreads) {
-    bm_sel[i] = 0u;
-    bm_tie[i] = 0u;
+  if constexpr (PRE) {
+    // two more refine histograms, in the (still unused) slot list
+    for (int i = tid; i < 2 * kBins; i += kThreads) sh.cslot[i] = 0;
+  } else {
+    for (int i = tid; i < nw; i += kThreads) {
+      bm_sel[i] = 0u;
+      bm_tie[i] = 0u;
+    }
   }
   if (tid == 0) {
     sh.ncand = 0;
@@ -301,8 +465,137 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   bool list_has_all = false;   // the LDS list holds every selected slot
   int ties_known = -1;         // keys equal to tau, when the list refine counted them
 
+  // ---------------- pre-collected lists (segmented collect) ----------------
+  if constexpr (PRE) {
+    // segment offsets of the concatenated list, in the (unused) key list
+    int32_t* seg_off = reinterpret_cast<int32_t*>(sh.ckey);
+    const int4* meta = a.seg_meta + (int64_t)row * a.nseg;
+    int cnt = 0;
+    uint32_t km = 0u;
+    if (tid < a.nseg) {
+      const int4 mm = meta[tid];
+      cnt = mm.x;
+      km = (uint32_t)mm.y;
+    }
+    const uint32_t t_lo = (uint32_t)meta[0].z;
+    int total;
+    const int off = block_exclusive_scan<kThreads>(cnt, sh.scan, &total);
+    if (tid < a.nseg) seg_off[tid] = off;
+    if (tid == 0) seg_off[a.nseg] = total;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) km = max(km, (uint32_t)__shfl_xor((int)km, o, 64));
+    if (lane == 0) atomicMax(&sh.kmax, km);
+    __syncthreads();
+    if (total >= B && total <= kCap) {
+      // Every key >= t_lo of the row is listed and at least B are, so the
+      // B-th key is among them. Thread t holds entries 8t .. 8t+7 (list
+      // order is slot order) in registers.
+      constexpr int kPer = kCap / kThreads;
+      const int i0 = tid * kPer;
+      int sg = 0;
+      if (i0 < total) {
+        int lo = 0, hi = a.nseg - 1;   // last segment starting at or before i0
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (seg_off[mid] <= i0) lo = mid; else hi = mid - 1;
+        }
+        sg = lo;
+      }
+      const int2* lrow = a.seg_list + (int64_t)row * a.nseg * kSeg;
+      int64_t addr[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int i = i0 + j;
+        if (i < total) {
+          while (seg_off[sg + 1] <= i) ++sg;
+          addr[j] = (int64_t)sg * kSeg + (i - seg_off[sg]);
+        } else {
+          addr[j] = -1;
+        }
+      }
+      uint32_t key[kPer];
+      float val[kPer];
+      int32_t slot[kPer];
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        const int2 e = addr[j] >= 0 ? lrow[addr[j]] : make_int2(0, 0);
+        val[j] = __int_as_float(e.x);
+        key[j] = order_key(val[j]);
+        slot[j] = e.y;
+      }
+      // radix levels below the common prefix of [t_lo, max key]; stop as
+      // soon as every key of the B-th key's bin is taken
+      const uint32_t kmax = sh.kmax;
+      int fixed = t_lo == kmax ? 32 : __clz(t_lo ^ kmax);
+      uint32_t pre = fixed == 0 ? 0u : (t_lo & (~0u << (32 - fixed)));
+      int nd = B;
+      int lev = 0;
+      while (fixed < 32) {
+        const int width = min(11, 32 - fixed);
+        const int shift = 32 - fixed - width;
+        const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
+        const int nb = 1 << width;
+        uint32_t* h = lev == 0 ? sh.hist : reinterpret_cast<uint32_t*>(sh.cslot) + (lev - 1) * kBins;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if (i0 + j < total && (key[j] & pmask) == pre) atomicAdd(&h[(key[j] >> shift) & (nb - 1)], 1u);
+        __syncthreads();
+        int tl;
+        find_bin(sh, h, nb, nd, &tl);
+        const int bin = sh.bin;
+        nd -= sh.above;
+        const int cnt_bin = (int)h[bin];
+        pre |= (uint32_t)bin << shift;
+        fixed += width;
+        ++lev;
+        if (cnt_bin == nd) break;   // the whole bin is taken
+      }
+      // taken: keys above the bin, and the first nd keys inside it (slot
+      // order); one packed scan gives both running counts
+      const uint32_t bmask = fixed >= 32 ? ~0u : (fixed == 0 ? 0u : (~0u << (32 - fixed)));
+      const uint32_t top = pre | ~bmask;
+      int na = 0, ni = 0;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        if (i0 + j < total) {
+          na += key[j] > top;
+          ni += (key[j] & bmask) == pre;
+        }
+      }
+      int tot2;
+      const int pref = block_exclusive_scan<kThreads>(na | (ni << 16), sh.scan, &tot2);
+      int pa = pref & 0xffff, pi = pref >> 16;
+      int32_t* orow = a.out_idx + (int64_t)row * B;
+      float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
+#pragma unroll
+      for (int j = 0; j < kPer; ++j) {
+        if (i0 + j >= total) continue;
+        int pos = -1;
+        if (key[j] > top) {
+          pos = pa + min(pi, nd);
+          ++pa;
+        } else if ((key[j] & bmask) == pre) {
+          if (pi < nd) pos = pa + pi;
+          ++pi;
+        }
+        if (pos >= 0) {
+          orow[pos] = slot_pos<CAND>(a, crow, slot[j]);
+          if (osc) osc[pos] = val[j];
+        }
+      }
+      if (tid == 0 && a.out_count) a.out_count[row] = B;
+      return;
+    }
+    // the lists do not settle it: general path over the row
+    for (int i = tid; i < nw; i += kThreads) {
+      bm_sel[i] = 0u;
+      bm_tie[i] = 0u;
+    }
+    __syncthreads();
+  }
+
   // ---------------- fast path: threshold, then collect keys >= t_lo ----------------
-  if (B <= kCap / 2 && nv > B) {
+  if (!PRE && B <= kCap / 2 && nv > B) {
     uint32_t t_lo = 0u;
     // the hints can vouch for at most hint_count*hint_k keys
     const bool use_hint = a.hint != nullptr && a.hint_k > 0 && a.hint_count > 0 &&
@@ -380,7 +673,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
       const int target = (int)min<double>((double)sh.nsample, ceil(2.0 * B * share) + 64.0);
       if (target >= 1) {
         int tot_s;
-        find_bin(sh, kBins, target, &tot_s);
+        find_bin(sh, sh.hist, kBins, target, &tot_s);
         if (tot_s >= target) {
           const uint32_t sb = (uint32_t)sh.bin;
           const int need_s = target - sh.above;
@@ -391,7 +684,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
             if ((sok & (1u << k)) && (skey[k] >> 21) == sb) atomicAdd(&sh.hist[(skey[k] >> 10) & 2047u], 1u);
           __syncthreads();
           int tot2;
-          find_bin(sh, kBins, need_s, &tot2);
+          find_bin(sh, sh.hist, kBins, need_s, &tot2);
           t_lo = (sb << 21) | ((uint32_t)sh.bin << 10);
         }
       }
@@ -453,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
       if (lane == 0) atomicMax(&sh.kmax, kmax);
       __syncthreads();
       need = B;
-      tau = refine_range_wave(sh, ncand, t_lo, sh.kmax, &need, &ties_known);
+      tau = refine_list(sh, ncand, t_lo, sh.kmax, &need, &ties_known);
     } else {
       zero_hist(sh);   // the guess failed: start the general path clean
       __syncthreads();
@@ -486,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
     }
     __syncthreads();
     int total;
-    find_bin(sh, kBins, B, &total);
+    find_bin(sh, sh.hist, kBins, B, &total);
     if (total <= B) {
       all = true;
     } else {
@@ -521,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
       tau = b0 << 21;
       if (in_lds) {
         ncand = cnt_b0;
-        tau = refine_range_wave(sh, ncand, b0 << 21, (b0 << 21) | 0x1fffffu, &need, &ties_known);
+        tau = refine_list(sh, ncand, b0 << 21, (b0 << 21) | 0x1fffffu, &need, &ties_known);
       } else {
         for (int level = 1; level <= 2; ++level) {
           const int shift = level == 1 ? 10 : 0;
@@ -543,7 +836,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
           }
           __syncthreads();
           int tl;
-          find_bin(sh, nb, need, &tl);
+          find_bin(sh, sh.hist, nb, need, &tl);
           tau |= (uint32_t)sh.bin << shift;
           need -= sh.above;
         }
@@ -675,21 +968,60 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
 template <bool CAND>
 hipError_t launch_select_t(const SelectArgs& a, int rows, hipStream_t s) {
   const int nw = (a.n + 31) / 32;
-  if (a.gbitmap) {
-    hipLaunchKernelGGL((select_kernel<CAND, true>), dim3(rows), dim3(kThreads), sizeof(SelShared), s, a);
+  const size_t lds = a.gbitmap ? sizeof(SelShared) : sizeof(SelShared) + (size_t)2 * nw * sizeof(uint32_t);
+  if (a.nseg > 0) {
+    hipLaunchKernelGGL((select_collect_kernel<CAND>), dim3(rows * a.nseg), dim3(kSegThreads), 0, s, a);
+    if (a.gbitmap)
+      hipLaunchKernelGGL((select_kernel<CAND, true, true>), dim3(rows), dim3(kThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((select_kernel<CAND, false, true>), dim3(rows), dim3(kThreads), lds, s, a);
   } else {
-    const size_t lds = sizeof(SelShared) + (size_t)2 * nw * sizeof(uint32_t);
-    hipLaunchKernelGGL((select_kernel<CAND, false>), dim3(rows), dim3(kThreads), lds, s, a);
+    if (a.gbitmap)
+      hipLaunchKernelGGL((select_kernel<CAND, true, false>), dim3(rows), dim3(kThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((select_kernel<CAND, false, false>), dim3(rows), dim3(kThreads), lds, s, a);
   }
   return hipGetLastError();
 }
 
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t bitmap_bytes(int rows, int n) {
+  if (n <= kSelectLdsMaxSlots) return 0;
+  return (size_t)rows * 2 * (((size_t)n + 31) / 32) * sizeof(uint32_t);
+}
+
 }  // namespace
 
-size_t select_workspace(int rows, int n) {
-  if (n <= kSelectLdsMaxSlots) return 0;
-  const size_t nw = ((size_t)n + 31) / 32;
-  return (size_t)rows * 2 * nw * sizeof(uint32_t);
+int select_segments(int n, int B, bool hint_usable) {
+  if (!hint_usable || B > kCap / 2 || n < 2 * kSeg) return 0;
+  const int nseg = (n + kSeg - 1) / kSeg;
+  return nseg <= kThreads ? nseg : 0;   // the row kernel scans one count per thread
+}
+
+size_t select_workspace(int rows, int n, int B, bool hint_usable) {
+  size_t bytes = bitmap_bytes(rows, n);
+  const int nseg = select_segments(n, B, hint_usable);
+  if (nseg > 0)
+    bytes = align256(bytes) + align256((size_t)rows * nseg * sizeof(int4)) +
+            (size_t)rows * nseg * kSeg * sizeof(int2);
+  return bytes;
+}
+
+void select_bind_workspace(SelectArgs& a, int rows, void* ws) {
+  const bool hint_usable = a.hint != nullptr && a.hint_count > 0 && a.hint_k > 0 &&
+                           (int64_t)a.hint_count * a.hint_k >= a.B;
+  unsigned char* p = static_cast<unsigned char*>(ws);
+  const size_t gb = bitmap_bytes(rows, a.n);
+  a.gbitmap = gb ? reinterpret_cast<uint32_t*>(p) : nullptr;
+  a.nseg = select_segments(a.n, a.B, hint_usable);
+  if (a.nseg > 0) {
+    a.seg_meta = reinterpret_cast<int4*>(p + align256(gb));
+    a.seg_list = reinterpret_cast<int2*>(p + align256(gb) + align256((size_t)rows * a.nseg * sizeof(int4)));
+  } else {
+    a.seg_meta = nullptr;
+    a.seg_list = nullptr;
+  }
 }
 
 hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
@@ -697,11 +1029,15 @@ hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
   // LDS-resident row); a function-local static runs this once, thread-safely
   static const hipError_t attr = [] {
     const int lds = (int)(sizeof(SelShared) + (size_t)2 * (kSelectLdsMaxSlots / 32) * sizeof(uint32_t));
-    hipError_t e1 = hipFuncSetAttribute((const void*)select_kernel<false, false>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    hipError_t e2 = hipFuncSetAttribute((const void*)select_kernel<true, false>,
-                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    return e1 != hipSuccess ? e1 : e2;
+    const void* fns[] = {(const void*)select_kernel<false, false, false>,
+                         (const void*)select_kernel<true, false, false>,
+                         (const void*)select_kernel<false, false, true>,
+                         (const void*)select_kernel<true, false, true>};
+    for (const void* f : fns) {
+      const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }();
   if (attr != hipSuccess) return attr;
   return a.cand ? launch_select_t<true>(a, rows, s) : launch_select_t<false>(a, rows, s);

@@ -349,9 +349,10 @@ def lsa_topk_select(scores: torch.Tensor, topk: int, out_idx: torch.Tensor, *, n
 
 
 def lsa_select_workspace_bytes(scores, topk, out_idx, *, n=None, n_valid=None, causal_group=0,
-                               cand=None, cand_block=1, n_positions=0) -> int:
+                               cand=None, cand_block=1, n_positions=0, hint=None,
+                               hint_k: int = 0) -> int:
     d = _select_desc(scores, topk, out_idx, n, None, None, n_valid, causal_group, cand, cand_block,
-                     n_positions)
+                     n_positions, hint, hint_k)
     return int(_lib().lsa_select_workspace_bytes(_c.byref(d)))
 
 

@@ -29,6 +29,11 @@ def _ld4(n: int) -> int:
     return (n + 3) // 4 * 4
 
 
+def _select_ws(scores, B, idx, device, **kw):
+    need = lsa.lsa_select_workspace_bytes(scores, B, idx, **kw)
+    return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+
+
 class DecodePlan:
     """Buffers for one flat decode step of N sequences with T cached tokens."""
 
@@ -46,9 +51,11 @@ class DecodePlan:
         # selection hint written by the scoring kernel, read by the select
         self.hint_count, self.hint_k = lsa.score_hint_layout_for(N, Hkv, T, r, _code(kv_dtype))
         self.hint = torch.empty(N * Hkv, max(1, self.hint_count), dtype=torch.int32, device=device)
-        # attention workspace, sized by the library for this shape
+        # attention and select workspaces, sized by the library for this shape
         need = lsa.attention_workspace_bytes_for(N, Hq, Hkv, d, B, T, _code(kv_dtype))
         self.attn_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        self.sel_ws = _select_ws(self.scores, B, self.idx, device,
+                                 hint=self.hint if self.hint_count else None, hint_k=self.hint_k)
 
     def score(self, q, w, k_idx, stream=None):
         lsa.lsa_index_score(k_idx, self.scores, q=q, w=w, q_idx=self.q_idx,
@@ -58,7 +65,7 @@ class DecodePlan:
         lsa.lsa_topk_select(self.scores, self.B, self.idx,
                             out_score=self.idx_scores if self.with_idx_scores else None,
                             hint=self.hint if self.hint_count else None, hint_k=self.hint_k,
-                            stream=stream)
+                            workspace=self.sel_ws, stream=stream)
 
     def attend(self, q, k, v, stream=None):
         lsa.lsa_indexed_attention(q, k, v, self.idx, self.out, lse=self.lse,
@@ -107,19 +114,24 @@ class HierarchicalPlan:
         self.hf_count, _ = lsa.score_hint_layout_for(N, Hkv, self.n_fine, r, code)
         self.hint_c = torch.empty(N * Hkv, max(1, self.hc_count), dtype=torch.int32, device=device)
         self.hint_f = torch.empty(N * Hkv, max(1, self.hf_count), dtype=torch.int32, device=device)
+        self.ws_c = _select_ws(self.coarse, B_coarse, self.blocks, device, hint=self.hint_c,
+                               hint_k=self.hint_k)
+        self.ws_f = _select_ws(self.fine, B, self.idx, device, cand=self.blocks, cand_block=block,
+                               n_positions=T, hint=self.hint_f, hint_k=self.hint_k)
 
     def run(self, q, w, k_idx, centroids, k, v, stream=None):
         # coarse: score every block summary, keep the top B_coarse blocks
         lsa.lsa_index_score(centroids, self.coarse, q=q, w=w, q_idx=self.q_idx, hint=self.hint_c,
                             stream=stream)
         lsa.lsa_topk_select(self.coarse, self.B_coarse, self.blocks, hint=self.hint_c,
-                            hint_k=self.hint_k, stream=stream)
+                            hint_k=self.hint_k, workspace=self.ws_c, stream=stream)
         # fine: score only the kept blocks' tokens, keep the top-B positions
         lsa.lsa_index_score(k_idx, self.fine, q_idx=self.q_idx, cand=self.blocks,
                             cand_block=self.block, hint=self.hint_f, stream=stream)
         lsa.lsa_topk_select(self.fine, self.B, self.idx, out_score=self.idx_scores,
                             cand=self.blocks, cand_block=self.block, n_positions=self.T,
-                            hint=self.hint_f, hint_k=self.hint_k, stream=stream)
+                            hint=self.hint_f, hint_k=self.hint_k, workspace=self.ws_f,
+                            stream=stream)
         lsa.lsa_indexed_attention(q, k, v, self.idx, self.out, lse=self.lse,
                                   workspace=self.attn_ws, stream=stream)
         return self

@@ -492,3 +492,118 @@ def test_select_hint_never_changes_the_result(name, over):
         t = np.sort(hv[row])[::-1][r_th - 1]
         kept = T - np.searchsorted(okey[row], t, side="left")
         assert B <= kept <= max(8 * B, 2 * B + 4096), (row, kept)
+
+
+# --------------------------------------------------------------------------
+# segmented select (long rows with a hint): edge cases with hand-made hints
+# --------------------------------------------------------------------------
+
+def _order_keys(x32: np.ndarray) -> np.ndarray:
+    """Order-preserving uint32 keys of float32 scores (-0 as +0, NaN lowest)."""
+    u = x32.view(np.uint32).copy()
+    u[u == 0x80000000] = 0
+    k = np.where(u & 0x80000000, ~u, u | 0x80000000).astype(np.uint32)
+    k[np.isnan(x32)] = 0
+    return k
+
+
+def _group_hint(x32: np.ndarray, valid: np.ndarray, k: int, group: int = 128) -> np.ndarray:
+    """A valid hint: per disjoint group of `group` slots, the 16-bit prefix of
+    the k-th largest valid key (0 where fewer than k are valid)."""
+    rows, n = x32.shape
+    ng = -(-n // group)
+    keys = np.where(valid, _order_keys(x32), 0).astype(np.uint32)
+    pad = np.zeros((rows, ng * group), np.uint32)
+    pad[:, :n] = keys
+    vpad = np.zeros((rows, ng * group), bool)
+    vpad[:, :n] = valid
+    g = np.sort(pad.reshape(rows, ng, group), axis=2)[:, :, group - k]
+    enough = vpad.reshape(rows, ng, group).sum(axis=2) >= k
+    return np.where(enough, g & 0xffff0000, 0).astype(np.uint32).view(np.int32)
+
+
+def _seg_case(kind: str, rows: int, n: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, n)).astype(np.float32)
+    if kind == "ties":
+        x = (np.round(x * 4) / 4).astype(np.float32)
+    elif kind == "recent":
+        x[:, -9000:] += 10.0
+    elif kind == "special":
+        for val in (np.nan, np.inf, -np.inf, -0.0, 0.0):
+            pos = rng.choice(n, size=300, replace=False)
+            x[np.arange(rows)[:, None], pos[None, :]] = val
+    elif kind == "equal":
+        x[:] = 1.5
+    return x
+
+
+@pytest.mark.parametrize("kind,rows,n,B,group", [
+    ("normal", 6, 40000, 2048, 32), ("normal", 4, 40000, 1, 32), ("normal", 3, 40000, 4096, 32),
+    ("normal", 5, 33333, 777, 128), ("ties", 6, 40000, 2048, 32), ("recent", 4, 40000, 2048, 32),
+    ("special", 4, 40000, 2048, 32), ("equal", 2, 40000, 2048, 32),
+    ("normal", 2, 1000003, 2048, 128)])
+def test_segmented_select(kind, rows, n, B, group):
+    say("segmented select", kind, rows, n, B, group)
+    x = _seg_case(kind, rows, n, seed=n + B)
+    k = 4
+    hint = _group_hint(x, np.ones_like(x, dtype=bool), k, group)
+    assert hint.shape[1] * k >= B   # the hint can vouch for B keys: the segmented path runs
+    ld = n + (4 - n % 4) % 4
+    sc = torch.empty(rows, ld, device="cuda")[:, :n]
+    sc.copy_(torch.from_numpy(x))
+    hd = dev(hint)
+    idx = torch.empty(rows, B, dtype=torch.int32, device="cuda")
+    osc = torch.empty(rows, B, device="cuda")
+    cnt = torch.empty(rows, dtype=torch.int32, device="cuda")
+    assert lsa.lsa_select_workspace_bytes(sc, B, idx, hint=hd, hint_k=k) >= rows * n * 8
+    lsa.lsa_topk_select(sc, B, idx, out_score=osc, out_count=cnt, hint=hd, hint_k=k)
+    ref, rs, rc = oracle.topk(x, B)
+    np.testing.assert_array_equal(host(idx), ref)
+    np.testing.assert_array_equal(host(cnt), rc)
+    sel = ref >= 0
+    np.testing.assert_array_equal(host(osc)[sel], rs[sel].astype(np.float32))
+    # a hint that overshoots (too few keys reach it) or takes everything
+    for bad in (np.full_like(hint, np.uint32(0xffff0000).view(np.int32)), np.zeros_like(hint)):
+        idx2 = torch.empty_like(idx)
+        lsa.lsa_topk_select(sc, B, idx2, hint=dev(bad), hint_k=k)
+        np.testing.assert_array_equal(host(idx2), ref)
+
+
+def test_segmented_select_n_valid():
+    rows, n, B, k = 10, 50000, 2048, 4
+    say("segmented select n_valid", rows, n, B)
+    x = _seg_case("normal", rows, n, seed=7)
+    nv = np.array([0, 1, 100, 2048, 2049, 8191, 8192, 9000, 40000, n], np.int32)
+    valid = np.arange(n)[None, :] < nv[:, None]
+    hint = _group_hint(x, valid, k, 32)
+    sc = torch.from_numpy(x).cuda()
+    idx = torch.empty(rows, B, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(rows, dtype=torch.int32, device="cuda")
+    lsa.lsa_topk_select(sc, B, idx, out_count=cnt, n_valid=dev(nv), hint=dev(hint), hint_k=k)
+    ref, _, rc = oracle.topk(x, B, n_valid=nv)
+    np.testing.assert_array_equal(host(idx), ref)
+    np.testing.assert_array_equal(host(cnt), rc)
+
+
+def test_segmented_select_candidates():
+    rows, blk, nb, B, k = 4, 64, 700, 2048, 4
+    n = blk * nb
+    n_positions = 64 * 1500 - 17
+    say("segmented select cand", rows, n, B)
+    rng = np.random.default_rng(11)
+    # an increasing block list (the contract: slot order is position order), with holes
+    cand = np.stack([np.sort(rng.choice(1500, size=nb, replace=False)) for _ in range(rows)])
+    cand = cand.astype(np.int32)
+    cand[rng.random(cand.shape) < 0.1] = -1
+    x = _seg_case("normal", rows, n, seed=12)
+    slot = np.arange(n)
+    pos = cand[:, slot // blk] * blk + slot % blk
+    valid = (cand[:, slot // blk] >= 0) & (pos < n_positions)
+    hint = _group_hint(x, valid, k, 32)
+    sc = torch.from_numpy(x).cuda()
+    idx = torch.empty(rows, B, dtype=torch.int32, device="cuda")
+    lsa.lsa_topk_select(sc, B, idx, cand=dev(cand), cand_block=blk, n_positions=n_positions,
+                        hint=dev(hint), hint_k=k)
+    ref, _, _ = oracle.topk(x, B, cand=cand, cand_block=blk, n_positions=n_positions)
+    np.testing.assert_array_equal(host(idx), ref)
