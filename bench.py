@@ -75,6 +75,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the CPU-oracle baseline (0 disables it)")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing loops")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="finish with three plain device copies of MIB MiB: the reference for "
+                         "scaling rocprofv3's FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path shards "
@@ -196,6 +199,17 @@ def main() -> int:
         parity = {"rows_identical_sets": same, "rows": N * Hkv, "max_abs_out_err": err,
                   "pass": same == N * Hkv and err is not None and err <= 2e-3}
         log(f"cpu oracle: {cpu['value']:.3f} steps/s on {threads} threads; parity {parity}")
+
+    if args.copy_calibration > 0:
+        n_el = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n_el, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: 3 copies of {n_el * 4} bytes")
+        del src, dst
 
     traffic = measured_traffic(kidx_bytes)
     line = {
