@@ -281,7 +281,31 @@ __global__ __launch_bounds__(kSegThreads) void select_collect_kernel(SelectArgs 
   const float* srow = a.scores + (int64_t)row * a.scores_ld;
   const int32_t* crow = CAND ? a.cand + (int64_t)row * a.cand_ld : nullptr;
 
-  // 1. the segment's loads go out first
+  // 1. the hint loads go out first (vector loads return in order, so the
+  // threshold search below then overlaps the segment's loads)
+  const uint32_t* hrow = a.hint + (int64_t)row * a.hint_ld;
+  const int m = (a.hint_count + 4 * kSegThreads - 1) / (4 * kSegThreads);
+  const int ne = (a.hint_count + m - 1) / m;
+  const int r = (a.B + m * a.hint_k - 1) / (m * a.hint_k);
+  uint32_t p[4];
+  if (m == 1) {   // plain loads, first used after the segment's loads are issued
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + q * kSegThreads;
+      p[q] = e < a.hint_count ? hrow[e] : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + q * kSegThreads;
+      uint32_t val = 0xffffffffu;
+      for (int mm = 0; mm < m; ++mm) {
+        const int h = e * m + mm;
+        val = min(val, h < a.hint_count ? hrow[h] : 0u);
+      }
+      p[q] = val;
+    }
+  }
   float v[4 * kSegUnroll];
   const bool full = s0 + kSeg <= nv;
   if (full) {
@@ -296,31 +320,21 @@ __global__ __launch_bounds__(kSegThreads) void select_collect_kernel(SelectArgs 
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         v[4 * j + k] = srow[min(s0 + j * kSegThreads * 4 + tid * 4 + k, nv - 1)];
+    // keeps these clamped loads in this branch: merged with the branch
+    // above, every 128-bit load would become four 32-bit ones
+    asm volatile("" ::: "memory");
   }
 
-  // 2. t_lo from the hint. Entry h vouches that hint_k valid keys of its
-  // (disjoint) slot group reach it; folding m entries into their minimum
-  // vouches for m*hint_k keys. The r-th largest folded entry, with
-  // r = ceil(B / (m*hint_k)), is then reached by at least B keys. It is
-  // found on the 16-bit prefixes by two 8-bit radix levels.
+  // 2. t_lo from the hint (loaded above). Entry h vouches that hint_k valid
+  // keys of its (disjoint) slot group reach it; folding m entries into
+  // their minimum vouches for m*hint_k keys. The r-th largest folded entry,
+  // with r = ceil(B / (m*hint_k)), is then reached by at least B keys. It
+  // is found on the 16-bit prefixes by two 8-bit radix levels.
+#pragma unroll
+  for (int q = 0; q < 4; ++q) p[q] >>= 16;
   sh.h1[tid] = 0u;
   sh.h2[tid] = 0u;
   if (tid == 0) sh.bin = -1;
-  const uint32_t* hrow = a.hint + (int64_t)row * a.hint_ld;
-  const int m = (a.hint_count + 4 * kSegThreads - 1) / (4 * kSegThreads);
-  const int ne = (a.hint_count + m - 1) / m;
-  const int r = (a.B + m * a.hint_k - 1) / (m * a.hint_k);
-  uint32_t p[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = tid + q * kSegThreads;
-    uint32_t val = 0xffffffffu;
-    for (int mm = 0; mm < m; ++mm) {
-      const int h = e * m + mm;
-      val = min(val, h < a.hint_count ? hrow[h] : 0u);
-    }
-    p[q] = val >> 16;
-  }
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < 4; ++q)
