@@ -60,7 +60,13 @@ struct PrefillTopkArgs {
 };
 size_t prefill_topk_workspace(int L, int Hkv, int B);
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s);
-bool prefill_topk_supported(int r, int B);
+bool prefill_topk_supported(int L, int r, int B);
+// Unfused causal scores through the same MFMA tiles as the fused path
+// (bf16, r = 64, 16-byte aligned rows); ScorePrefillArgs' VALU kernel
+// serves the other cases.
+bool prefill_mfma_scores_supported(int r);
+hipError_t launch_prefill_scores_mfma(const PrefillTopkArgs& a, float* scores, int64_t ld,
+                                      hipStream_t s);
 
 // ----- exact top-B selection -----------------------------------------------
 struct SelectArgs {

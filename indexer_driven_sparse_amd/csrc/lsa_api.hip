@@ -20,6 +20,11 @@ int hip_fail(hipError_t e) {
 }
 
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// The MFMA prefill paths read q_idx / k_idx rows as 16-byte fragments.
+bool mfma_rows_ok(const lsa_score_desc* d) {
+  return al16(d->k_idx) && al16(d->q_idx) && d->k_stride_tok % 8 == 0 && d->k_stride_head % 8 == 0;
+}
 int esize(int dtype) { return dtype == LSA_BF16 ? 2 : dtype == LSA_F32 ? 4 : 0; }
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool strides16(int es, int64_t a, int64_t b, int64_t c) {
@@ -100,13 +105,17 @@ int validate_score(const lsa_score_desc* d, size_t* ws_need) {
     if (!al16(d->q_idx)) return LSA_ERR_INVALID_ARG;
     if (d->topk < 0) return LSA_ERR_INVALID_ARG;
     if (d->topk == 0) {
-      if ((int64_t)d->n_keys * d->n_kv_heads > 65535) return LSA_ERR_UNSUPPORTED;
+      const bool mfma = d->k_idx_dtype == LSA_BF16 && lsa::prefill_mfma_scores_supported(d->rank) &&
+                        mfma_rows_ok(d);
+      if (!mfma && (int64_t)d->n_keys * d->n_kv_heads > 65535) return LSA_ERR_UNSUPPORTED;
+      if (mfma && (d->n_keys + 31) / 32 > 65535) return LSA_ERR_UNSUPPORTED;
       if (!d->scores || !al16(d->scores) || d->scores_ld % 4 != 0 || d->scores_ld < d->n_keys)
         return LSA_ERR_INVALID_ARG;
       return LSA_OK;
     }
     if (!d->out_idx) return LSA_ERR_INVALID_ARG;
-    if (d->k_idx_dtype != LSA_BF16 || !lsa::prefill_topk_supported(d->rank, d->topk))
+    if (d->k_idx_dtype != LSA_BF16 || !lsa::prefill_topk_supported(d->n_keys, d->rank, d->topk) ||
+        !mfma_rows_ok(d))
       return LSA_ERR_UNSUPPORTED;
     *ws_need = lsa::prefill_topk_workspace(d->n_keys, d->n_kv_heads, d->topk);
     return LSA_OK;
@@ -204,6 +213,17 @@ int lsa_index_score(const lsa_score_desc* d, void* ws, size_t ws_bytes, void* st
     a.hint = d->hint;
     a.hint_ld = d->hint_ld;
     e = lsa::launch_score_decode(a, rows, d->k_idx_dtype == LSA_BF16, s);
+  } else if (d->topk == 0 && d->k_idx_dtype == LSA_BF16 &&
+             lsa::prefill_mfma_scores_supported(d->rank) && mfma_rows_ok(d)) {
+    lsa::PrefillTopkArgs a{};
+    a.q_idx = (const uint16_t*)d->q_idx;
+    a.k_idx = (const uint16_t*)d->k_idx;
+    a.ks_head = d->k_stride_head;
+    a.ks_tok = d->k_stride_tok;
+    a.L = d->n_keys;
+    a.Hkv = d->n_kv_heads;
+    a.r = d->rank;
+    e = lsa::launch_prefill_scores_mfma(a, d->scores, d->scores_ld, s);
   } else if (d->topk == 0) {
     lsa::ScorePrefillArgs a{};
     a.q_idx = d->q_idx;

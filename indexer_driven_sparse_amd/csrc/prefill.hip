@@ -1,28 +1,666 @@
-// Fused causal prefill indexer + exact top-B (LongCat Sparse Attention,
-// abstract: the indexer's O(L^2) causal scoring). Not built yet: the entry
-// point reports LSA_ERR_UNSUPPORTED for fused selection until it is.
-#include "common.hpp"
-#include "kernels.hpp"
+// Causal prefill indexer (LongCat Sparse Attention, abstract: the indexer's
+// O(L^2) causal scoring) with the per-row exact top-B of JSSA ("Joint
+// Subspace Sparse Attention for Efficient Long-Context Decoding", Fig. 1:
+// top-B positions, lowest position on equal scores) fused in: no L x L score
+// matrix is written.
+//
+// Scores S[i,j] = q_idx[i] . k_idx[j] (j <= i) come from MFMA tiles
+// (v_mfma_f32_32x32x16_bf16, r = 64 as four 16-deep chunks). Every prefill
+// path -- the fused one, its fallback and the unfused score kernel -- runs
+// the same MFMA sequence per tile, so equal inputs give bit-equal scores and
+// the fused selection equals select-over-unfused-scores exactly.
+//
+// Fused selection, four kernels:
+//   sample  per block of 32 query rows, MFMA scores against a jittered
+//           stratified sample of at most 1024 keys of the causal prefix; per
+//           row, two 8-bit radix levels give a threshold tau that the sample
+//           says about B plus a 4-sigma margin of the row's keys reach;
+//   cand    per block of 128 query rows (4 waves x 32), all causal key tiles;
+//           each score >= tau of its row is appended, as (score bits, j), to
+//           one of the row's 8 candidate sub-lists (wave, lane half);
+//   final   per row: if the sub-lists did not overflow and hold at least
+//           min(B, i+1) entries, every key ranking above the B-th one is
+//           among them, so a radix select over them is exact; the positions
+//           go out ascending through an LDS bitmap. Otherwise the row is put
+//           on a redo list (the sample decides speed, never the result);
+//   redo    recomputes each listed row's scores (same MFMA sequence) into a
+//           scratch row and runs the general single-row select on it.
+#include "select_row.hpp"
 
 namespace lsa {
+namespace {
 
-bool prefill_topk_supported(int r, int B) {
-  (void)r;
-  (void)B;
-  return false;
+using namespace sel;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kT = 32;           // keys per MFMA tile = query rows per block
+constexpr int kCh = 4;           // rank 64 = four 16-deep chunks
+constexpr int kRank = 16 * kCh;
+
+constexpr int kSampleMax = 1024; // sampled keys per block of 32 query rows
+constexpr int kRowsA = 128;      // query rows per candidate workgroup
+constexpr int kSub = 8;          // candidate sub-lists per row
+constexpr int kSubCap = 1024;    // entries per sub-list
+constexpr int kFinThreads = 256;
+constexpr int kFinPer = kSub * kSubCap / kFinThreads;  // candidates per thread (32)
+constexpr int kRedoBlocks = 256;
+
+// 8 bf16 of row p for chunk c and lane half h: elements 16c + 8h .. +8.
+__device__ __forceinline__ bf16x8 frag(const uint16_t* p, int c, int h) {
+  return __builtin_bit_cast(bf16x8, *(const u32x4*)(p + 16 * c + 8 * h));
 }
 
+// One tile: D[m][n] = sum_k K[m][k] * Q[n][k] for 32 keys m (operand A) and
+// 32 queries n (operand B). Lane l holds query n = l % 32 and the keys
+// tile_key(v, l / 32), v = 0..15.
+__device__ __forceinline__ f32x16 tile_scores(const bf16x8 (&ka)[kCh], const bf16x8 (&qb)[kCh]) {
+  f32x16 acc = {};
+#pragma unroll
+  for (int c = 0; c < kCh; ++c) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c], qb[c], acc, 0, 0, 0);
+  return acc;
+}
+__device__ __forceinline__ int tile_key(int v, int h) { return 8 * (v >> 2) + 4 * h + (v & 3); }
+
+__device__ __forceinline__ const uint16_t* krow(const PrefillTopkArgs& a, int g, int j) {
+  return a.k_idx + (int64_t)g * a.ks_head + (int64_t)j * a.ks_tok;
+}
+__device__ __forceinline__ const uint16_t* qrow(const PrefillTopkArgs& a, int g, int i) {
+  return a.q_idx + ((int64_t)i * a.Hkv + g) * kRank;
+}
+
+// ---------------------------------------------------------------------------
+// Unfused scores (topk == 0): full causal rows, -inf above the diagonal.
+// One wave per 32 x 32 tile; the tile is transposed through LDS so each
+// row's 32 scores leave as 128 contiguous bytes.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void prefill_scores_mfma_kernel(PrefillTopkArgs a, float* scores,
+                                                                 int64_t ld) {
+  __shared__ float tile[kT][kT + 1];
+  const int lane = threadIdx.x, h = lane >> 5, n = lane & 31;
+  const int kt = blockIdx.x, qt = blockIdx.y, g = blockIdx.z;
+  const int j0 = kt * kT, i0 = qt * kT;
+  if (j0 <= i0 + kT - 1) {   // some key of the tile is causal for some row
+    bf16x8 ka[kCh], qb[kCh];
+    const uint16_t* kp = krow(a, g, min(j0 + n, a.L - 1));
+    const uint16_t* qp = qrow(a, g, min(i0 + n, a.L - 1));
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) {
+      ka[c] = frag(kp, c, h);
+      qb[c] = frag(qp, c, h);
+    }
+    const f32x16 acc = tile_scores(ka, qb);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) tile[n][tile_key(v, h)] = acc[v];
+  }
+  __syncthreads();
+  // lane pair (2r, 2r+1) writes row r's 32 scores, 16 each
+  const int r = lane >> 1, half = lane & 1;
+  const int i = i0 + r;
+  if (i < a.L) {
+    float* out = scores + ((int64_t)i * a.Hkv + g) * ld + j0 + 16 * half;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int j = j0 + 16 * half + q;
+      if (j < a.L) out[q] = (j <= i) ? tile[r][16 * half + q] : -INFINITY;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// sample: per-row threshold tau
+// ---------------------------------------------------------------------------
+struct SampleShared {
+  uint32_t hist[kT][256];
+  int nvalid[kT];
+  int target[kT];   // sample keys that should reach tau (0: no threshold)
+  int bin1[kT];
+  int bin2[kT];
+  int need2[kT];    // of those, the ones inside bin1
+};
+
+// Sample position k of m over the prefix [0, nb): one key per stratum
+// [k nb / m, (k+1) nb / m), at a fixed pseudo-random offset inside it (no
+// aliasing with periodic structure in the keys). Increasing in k.
+__device__ __forceinline__ int sample_pos(int k, int m, int nb) {
+  if (nb <= m) return k;
+  const int lo = (int)((int64_t)k * nb / m), hi = (int)((int64_t)(k + 1) * nb / m);
+  return lo + (int)(((uint32_t)k * 2654435761u >> 8) % (uint32_t)(hi - lo));
+}
+
+// 8 threads per row: the bin where the count from the top of hist[row]
+// reaches tgt; writes *bin_out and need2[row] = tgt - (count above).
+__device__ __forceinline__ void sample_find(SampleShared& sh, const int* tgts, int* bin_out) {
+  const int tid = threadIdx.x, row = tid >> 3, part = tid & 7;
+  const int tgt = tgts[row];
+  int c = 0;
+  for (int q = 0; q < 32; ++q) c += (int)sh.hist[row][255 - 32 * part - q];
+  int incl = c;
+#pragma unroll
+  for (int o = 1; o < 8; o <<= 1) {
+    const int y = __shfl_up(incl, o, 8);
+    if (part >= o) incl += y;
+  }
+  int acc = incl - c;
+  if (tgt > 0 && acc < tgt && tgt <= incl) {
+    for (int q = 0; q < 32; ++q) {
+      const int b = 255 - 32 * part - q;
+      const int hb = (int)sh.hist[row][b];
+      if (acc + hb >= tgt) {
+        bin_out[row] = b;
+        sh.need2[row] = tgt - acc;
+        break;
+      }
+      acc += hb;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, float* tau,
+                                                             int* redo) {
+  __shared__ SampleShared sh;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int qt = blockIdx.x, g = blockIdx.y;
+  const int i0 = qt * kT;
+  if (qt == 0 && g == 0 && tid == 0) redo[0] = 0;   // the redo list starts empty
+  if (i0 + kT <= a.B) {   // every row of the block keeps all its keys
+    if (tid < kT && i0 + tid < a.L) tau[(int64_t)(i0 + tid) * a.Hkv + g] = -INFINITY;
+    return;
+  }
+  const int nb = min(a.L, i0 + kT);          // keys any row of the block can see
+  const int m = min(nb, kSampleMax);
+  const int ntiles = (m + kT - 1) / kT;
+  const int i = i0 + n;                      // this lane's query row
+  bf16x8 qb[kCh];
+  {
+    const uint16_t* qp = qrow(a, g, min(i, a.L - 1));
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) qb[c] = frag(qp, c, h);
+  }
+  for (int q = tid; q < kT * 256; q += 256) (&sh.hist[0][0])[q] = 0u;
+  if (tid < kT) {
+    sh.nvalid[tid] = 0;
+    sh.bin1[tid] = -1;
+    sh.bin2[tid] = -1;
+    sh.need2[tid] = 0;
+  }
+  __syncthreads();
+  for (int pass = 0; pass < 2; ++pass) {
+    int nval = 0;
+    const int b1 = pass ? sh.bin1[n] : 0;
+    for (int t = w; t < ntiles; t += 4) {
+      bf16x8 ka[kCh];
+      const uint16_t* kp = krow(a, g, sample_pos(min(t * kT + n, m - 1), m, nb));
+#pragma unroll
+      for (int c = 0; c < kCh; ++c) ka[c] = frag(kp, c, h);
+      const f32x16 acc = tile_scores(ka, qb);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int k = t * kT + tile_key(v, h);
+        if (k < m && i < a.L && sample_pos(k, m, nb) <= i) {
+          const uint32_t key = order_key(acc[v]);
+          if (pass == 0) {
+            atomicAdd(&sh.hist[n][key >> 24], 1u);
+            ++nval;
+          } else if ((int)(key >> 24) == b1) {
+            atomicAdd(&sh.hist[n][(key >> 16) & 255u], 1u);
+          }
+        }
+      }
+    }
+    if (pass == 0) atomicAdd(&sh.nvalid[n], nval);
+    __syncthreads();
+    if (pass == 0 && tid < kT) {
+      // sample keys expected to rank among the row's top B, plus a 4-sigma
+      // (binomial) margin and 8; 0 (no threshold) when that is the sample
+      const int row = i0 + tid;
+      const int mv = sh.nvalid[tid];
+      int tgt = 0;
+      if (row < a.L && mv > 0) {
+        const double e = (double)a.B * mv / (double)(row + 1);
+        const double k = ceil(e + 4.0 * sqrt(e) + 8.0);
+        tgt = k < (double)mv ? (int)k : 0;
+      }
+      sh.target[tid] = tgt;
+    }
+    __syncthreads();
+    if (pass == 0) sample_find(sh, sh.target, sh.bin1);
+    else sample_find(sh, sh.need2, sh.bin2);
+    __syncthreads();
+    if (pass == 0) {
+      for (int q = tid; q < kT * 256; q += 256) (&sh.hist[0][0])[q] = 0u;
+      __syncthreads();
+    }
+  }
+  if (tid < kT && i0 + tid < a.L) {
+    float t = -INFINITY;
+    if (sh.target[tid] > 0 && sh.bin1[tid] >= 0 && sh.bin2[tid] >= 0) {
+      const uint32_t key = ((uint32_t)sh.bin1[tid] << 24) | ((uint32_t)sh.bin2[tid] << 16);
+      // every score whose key is >= this one; at or below -inf's key, all
+      // scores but NaN
+      t = key <= 0x007fffffu ? -INFINITY : key_to_float(key);
+    }
+    tau[(int64_t)(i0 + tid) * a.Hkv + g] = t;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// cand: MFMA scores of 128 query rows x all their causal keys; every score
+// >= its row's tau goes to the row's sub-list (wave w, lane half h).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, const float* tau,
+                                                           int2* cand, int* cnt) {
+  __shared__ __align__(16) float stash[4][64][20];   // per wave, per lane: 16 scores (+pad)
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int blk = gridDim.x - 1 - blockIdx.x;   // longest prefixes first
+  const int g = blockIdx.y;
+  const int r0 = blk * kRowsA;
+  const int kend = min(a.L, r0 + kRowsA);      // keys [0, kend) reach some row here
+  bf16x8 qb[4][kCh];
+  float tq[4];
+  int c[4];
+  int64_t sub[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int i = r0 + kT * b + n;
+    const uint16_t* qp = qrow(a, g, min(i, a.L - 1));
+#pragma unroll
+    for (int ch = 0; ch < kCh; ++ch) qb[b][ch] = frag(qp, ch, h);
+    tq[b] = i < a.L ? tau[(int64_t)i * a.Hkv + g] : INFINITY;
+    c[b] = 0;
+    sub[b] = (((int64_t)min(i, a.L - 1) * a.Hkv + g) * kSub + 2 * w + h) * kSubCap;
+  }
+  for (int t = w; t * kT < kend; t += 4) {
+    const int j0 = t * kT;
+    bf16x8 ka[kCh];
+    {
+      const uint16_t* kp = krow(a, g, min(j0 + n, a.L - 1));
+#pragma unroll
+      for (int ch = 0; ch < kCh; ++ch) ka[ch] = frag(kp, ch, h);
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const int qlo = r0 + kT * b;
+      if (j0 > qlo + kT - 1) continue;           // the tile is above every row's diagonal
+      const f32x16 acc = tile_scores(ka, qb[b]);
+      const int i = qlo + n;
+      uint32_t flags = 0;
+      if (j0 + kT - 1 <= qlo) {                   // the whole tile is causal for every row
+#pragma unroll
+        for (int v = 0; v < 16; ++v) flags |= (uint32_t)(acc[v] >= tq[b]) << v;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          flags |= (uint32_t)(acc[v] >= tq[b] && j0 + tile_key(v, h) <= i) << v;
+      }
+      if (__ballot(flags != 0)) {
+        float4* st = reinterpret_cast<float4*>(&stash[w][lane][0]);
+        st[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        st[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        st[2] = make_float4(acc[8], acc[9], acc[10], acc[11]);
+        st[3] = make_float4(acc[12], acc[13], acc[14], acc[15]);
+        while (flags) {
+          const int v = __ffs(flags) - 1;
+          flags &= flags - 1;
+          if (c[b] < kSubCap)
+            cand[sub[b] + c[b]] = make_int2(__float_as_int(stash[w][lane][v]), j0 + tile_key(v, h));
+          ++c[b];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const int i = r0 + kT * b + n;
+    if (i < a.L) cnt[((int64_t)i * a.Hkv + g) * kSub + 2 * w + h] = c[b];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// final: exact top-B of each row from its candidates
+// ---------------------------------------------------------------------------
+struct FinShared {
+  uint32_t hist[kBins];
+  int scan[kFinThreads / 64];
+  uint32_t kmin, kmax;
+  int bin, above;
+};
+
+// The bin holding the need-th largest of nb bins (scanned from the top):
+// sh.bin, sh.above. Contains barriers.
+__device__ __forceinline__ void fin_find_bin(FinShared& sh, int nb, int need) {
+  const int t = threadIdx.x;
+  const int per = (nb + kFinThreads - 1) / kFinThreads;
+  const int hi = nb - 1 - t * per;
+  int c = 0;
+  for (int k = 0; k < per; ++k)
+    if (hi - k >= 0) c += (int)sh.hist[hi - k];
+  int tot;
+  int acc = block_exclusive_scan<kFinThreads>(c, sh.scan, &tot);
+  for (int k = 0; k < per; ++k) {
+    if (hi - k < 0) break;
+    const int hb = (int)sh.hist[hi - k];
+    if (acc < need && need <= acc + hb) {
+      sh.bin = hi - k;
+      sh.above = acc;
+    }
+    acc += hb;
+  }
+  __syncthreads();
+}
+
+// Exclusive prefix of popcounts over words[0, nw) into pre[0, nw) (pre may
+// not alias words). Contains barriers.
+__device__ __forceinline__ void word_prefix(FinShared& sh, const uint32_t* words, uint32_t* pre,
+                                            int nw) {
+  const int per = (nw + kFinThreads - 1) / kFinThreads;
+  const int w0 = threadIdx.x * per, w1 = min(nw, w0 + per);
+  int c = 0;
+  for (int q = w0; q < w1; ++q) c += __popc(words[q]);
+  int tot;
+  int off = block_exclusive_scan<kFinThreads>(c, sh.scan, &tot);
+  for (int q = w0; q < w1; ++q) {
+    pre[q] = (uint32_t)off;
+    off += __popc(words[q]);
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkArgs a,
+                                                                   const int2* cand,
+                                                                   const int* cnt, int* redo) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  FinShared& sh = *reinterpret_cast<FinShared*>(smem);
+  const int nw_max = (a.L + 31) >> 5;
+  uint32_t* bm = reinterpret_cast<uint32_t*>(smem + sizeof(FinShared));   // selected
+  uint32_t* aux = bm + nw_max;                                            // ties, then prefixes
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int i = row / a.Hkv;
+  const int nv = i + 1;
+  const int Bq = min(a.B, nv);
+  const int nw = (nv + 31) >> 5;
+  int pre[kSub + 1];
+  pre[0] = 0;
+  bool bad = false;
+#pragma unroll
+  for (int k = 0; k < kSub; ++k) {
+    const int ck = cnt[(int64_t)row * kSub + k];
+    bad = bad || ck > kSubCap;
+    pre[k + 1] = pre[k] + min(ck, kSubCap);
+  }
+  const int total = pre[kSub];
+  if (bad || total < Bq) {   // the threshold missed: recompute this row
+    if (tid == 0) redo[1 + atomicAdd(&redo[0], 1)] = row;
+    return;
+  }
+  for (int q = tid; q < nw; q += kFinThreads) bm[q] = 0u;
+  if (tid == 0) {
+    sh.kmin = 0xffffffffu;
+    sh.kmax = 0u;
+  }
+  // candidates e = tid + 256 k, concatenated over the sub-lists
+  uint32_t key[kFinPer];
+  int32_t jj[kFinPer];
+  const int2* crow = cand + (int64_t)row * kSub * kSubCap;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int k = 0; k < kFinPer; ++k) {
+    const int e = tid + kFinThreads * k;
+    key[k] = 0u;
+    jj[k] = -1;
+    if (e < total) {
+      int s = 0;
+#pragma unroll
+      for (int q = 1; q < kSub; ++q) s += e >= pre[q];
+      const int2 x = crow[(int64_t)s * kSubCap + (e - pre[s])];
+      if (x.y >= 0 && x.y <= i) {   // always, for lists the candidate kernel wrote
+        key[k] = order_key(__int_as_float(x.x));
+        jj[k] = x.y;
+        lo = min(lo, key[k]);
+        hi = max(hi, key[k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  __syncthreads();
+  if (lane == 0) {
+    atomicMin(&sh.kmin, lo);
+    atomicMax(&sh.kmax, hi);
+  }
+  __syncthreads();
+
+  // radix levels below the common prefix of [kmin, kmax], up to 11 bits
+  // each; stop once the need-th key's bin is taken whole
+  uint32_t pfx = 0u, bmask = 0u;
+  int need = Bq, cnt_bin = total;
+  bool all = total <= Bq;
+  if (!all) {
+    const uint32_t kmin = sh.kmin, kmax = sh.kmax;
+    int fixed = kmin == kmax ? 32 : __clz(kmin ^ kmax);
+    pfx = fixed == 0 ? 0u : (kmin & (~0u << (32 - fixed)));
+    while (fixed < 32) {
+      const int width = min(11, 32 - fixed);
+      const int shift = 32 - fixed - width;
+      const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
+      const int nb = 1 << width;
+      for (int q = tid; q < nb; q += kFinThreads) sh.hist[q] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kFinPer; ++k)
+        if (jj[k] >= 0 && (key[k] & pmask) == pfx) atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1u);
+      __syncthreads();
+      fin_find_bin(sh, nb, need);
+      const int bin = sh.bin;
+      need -= sh.above;
+      cnt_bin = (int)sh.hist[bin];
+      pfx |= (uint32_t)bin << shift;
+      fixed += width;
+      __syncthreads();   // hist and bin are rewritten by the next level
+      if (cnt_bin == need) break;
+    }
+    bmask = fixed >= 32 ? ~0u : (~0u << (32 - fixed));
+  }
+  const uint32_t top = pfx | ~bmask;
+
+  // exact ties at the B-th key: the lowest positions win
+  uint32_t tie_take = 0u;   // bit k: candidate k is a tie that is taken
+  if (!all && cnt_bin > need) {
+    for (int q = tid; q < nw; q += kFinThreads) aux[q] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kFinPer; ++k)
+      if (jj[k] >= 0 && key[k] == pfx) atomicOr(&aux[jj[k] >> 5], 1u << (jj[k] & 31));
+    __syncthreads();
+    word_prefix(sh, aux, bm, nw);   // bm holds the tie prefixes for now
+#pragma unroll
+    for (int k = 0; k < kFinPer; ++k) {
+      if (jj[k] >= 0 && key[k] == pfx) {
+        const int j = jj[k];
+        const int rank = (int)bm[j >> 5] + __popc(aux[j >> 5] & ((1u << (j & 31)) - 1u));
+        tie_take |= (uint32_t)(rank < need) << k;
+      }
+    }
+    __syncthreads();
+    for (int q = tid; q < nw; q += kFinThreads) bm[q] = 0u;
+    __syncthreads();
+  }
+
+  // mark the selected positions, then write them in ascending order
+  uint32_t sel = 0u;
+#pragma unroll
+  for (int k = 0; k < kFinPer; ++k) {
+    if (jj[k] < 0) continue;
+    bool take;
+    if (all) take = true;
+    else if (key[k] > top) take = true;
+    else if ((key[k] & bmask) != pfx) take = false;
+    else take = cnt_bin == need || ((tie_take >> k) & 1u);
+    if (take) {
+      sel |= 1u << k;
+      atomicOr(&bm[jj[k] >> 5], 1u << (jj[k] & 31));
+    }
+  }
+  __syncthreads();
+  word_prefix(sh, bm, aux, nw);
+  int32_t* orow = a.out_idx + (int64_t)row * a.B;
+  float* osc = a.out_score ? a.out_score + (int64_t)row * a.B : nullptr;
+#pragma unroll
+  for (int k = 0; k < kFinPer; ++k) {
+    if (!((sel >> k) & 1u)) continue;
+    const int j = jj[k];
+    const int pos = (int)aux[j >> 5] + __popc(bm[j >> 5] & ((1u << (j & 31)) - 1u));
+    if (pos < a.B) {
+      orow[pos] = j;
+      if (osc) osc[pos] = key_to_float(key[k]);
+    }
+  }
+  for (int p = Bq + tid; p < a.B; p += kFinThreads) {
+    orow[p] = -1;
+    if (osc) osc[p] = -INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// redo: rows whose candidates did not settle the selection. Workgroup b
+// takes redo entries b, b + gridDim.x, ...: the row's causal scores go to
+// its own scratch row (same MFMA sequence, the query in every column), then
+// the general single-row select runs on them.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void prefill_redo_kernel(PrefillTopkArgs a, const int* redo,
+                                                                float* scratch) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  float* srow = scratch + (int64_t)blockIdx.x * a.L;
+  const int count = redo[0];
+  for (int f = blockIdx.x; f < count; f += gridDim.x) {
+    const int row = redo[1 + f];
+    const int i = row / a.Hkv, g = row % a.Hkv;
+    bf16x8 qb[kCh];
+    {
+      const uint16_t* qp = qrow(a, g, i);
+#pragma unroll
+      for (int c = 0; c < kCh; ++c) qb[c] = frag(qp, c, h);
+    }
+    for (int t = w; t * kT <= i; t += kWaves) {
+      const int j0 = t * kT;
+      bf16x8 ka[kCh];
+      const uint16_t* kp = krow(a, g, min(j0 + n, a.L - 1));
+#pragma unroll
+      for (int c = 0; c < kCh; ++c) ka[c] = frag(kp, c, h);
+      const f32x16 acc = tile_scores(ka, qb);
+      if (n == 0) {   // column 0 holds the tile's keys (all columns are equal)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int j = j0 + tile_key(v, h);
+          if (j <= i) srow[j] = acc[v];
+        }
+      }
+    }
+    // the scratch row is complete and visible to the whole workgroup (the
+    // acquire also drops lines the previous row left in the vector L1)
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    SelectArgs s{};
+    s.scores = srow;
+    s.scores_ld = a.L;
+    s.n = i + 1;
+    s.B = a.B;
+    s.cand_block = 1;
+    s.n_positions = i + 1;
+    s.out_idx = a.out_idx;
+    s.out_score = a.out_score;
+    select_row<false, false, false>(s, row, srow, (int64_t)i + 1, smem_raw);
+    __syncthreads();   // done with the scratch row before the next one
+  }
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct PrefillWs {
+  float* tau;
+  int* cnt;
+  int* redo;
+  int2* cand;
+  float* scratch;
+};
+
+size_t prefill_layout(int L, int Hkv, void* base, PrefillWs* ws) {
+  const size_t rows = (size_t)L * Hkv;
+  size_t off = 0;
+  unsigned char* p = static_cast<unsigned char*>(base);
+  const size_t o_tau = off;
+  off = align256(off + rows * sizeof(float));
+  const size_t o_cnt = off;
+  off = align256(off + rows * kSub * sizeof(int));
+  const size_t o_redo = off;
+  off = align256(off + (rows + 1) * sizeof(int));
+  const size_t o_scr = off;
+  off = align256(off + (size_t)kRedoBlocks * L * sizeof(float));
+  const size_t o_cand = off;
+  off += rows * kSub * kSubCap * sizeof(int2);
+  if (ws) {
+    ws->tau = reinterpret_cast<float*>(p + o_tau);
+    ws->cnt = reinterpret_cast<int*>(p + o_cnt);
+    ws->redo = reinterpret_cast<int*>(p + o_redo);
+    ws->scratch = reinterpret_cast<float*>(p + o_scr);
+    ws->cand = reinterpret_cast<int2*>(p + o_cand);
+  }
+  return off;
+}
+
+size_t fin_lds(int L) { return sizeof(FinShared) + (size_t)2 * ((L + 31) / 32) * sizeof(uint32_t); }
+size_t redo_lds(int L) { return sizeof(SelShared) + (size_t)2 * ((L + 31) / 32) * sizeof(uint32_t); }
+
+}  // namespace
+
+bool prefill_topk_supported(int L, int r, int B) {
+  return r == kRank && B >= 1 && B <= 4096 && L >= 1 && L <= kSelectLdsMaxSlots;
+}
+
+bool prefill_mfma_scores_supported(int r) { return r == kRank; }
+
 size_t prefill_topk_workspace(int L, int Hkv, int B) {
-  (void)L;
-  (void)Hkv;
   (void)B;
-  return 0;
+  return prefill_layout(L, Hkv, nullptr, nullptr);
 }
 
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s) {
-  (void)a;
-  (void)s;
-  return hipErrorInvalidValue;
+  static const hipError_t attr = [] {
+    hipError_t e = hipFuncSetAttribute((const void*)prefill_final_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       (int)fin_lds(kSelectLdsMaxSlots));
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute((const void*)prefill_redo_kernel,
+                               hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)redo_lds(kSelectLdsMaxSlots));
+  }();
+  if (attr != hipSuccess) return attr;
+  PrefillWs ws;
+  prefill_layout(a.L, a.Hkv, a.ws, &ws);
+  const int rows = a.L * a.Hkv;
+  hipLaunchKernelGGL(prefill_sample_kernel, dim3((a.L + kT - 1) / kT, a.Hkv), dim3(256), 0, s, a,
+                     ws.tau, ws.redo);
+  hipLaunchKernelGGL(prefill_cand_kernel, dim3((a.L + kRowsA - 1) / kRowsA, a.Hkv), dim3(256), 0, s,
+                     a, ws.tau, ws.cand, ws.cnt);
+  hipLaunchKernelGGL(prefill_final_kernel, dim3(rows), dim3(kFinThreads), fin_lds(a.L), s, a,
+                     ws.cand, ws.cnt, ws.redo);
+  hipLaunchKernelGGL(prefill_redo_kernel, dim3(kRedoBlocks), dim3(kThreads), redo_lds(a.L), s, a,
+                     ws.redo, ws.scratch);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_scores_mfma(const PrefillTopkArgs& a, float* scores, int64_t ld,
+                                      hipStream_t s) {
+  const dim3 grid((a.L + kT - 1) / kT, (a.L + kT - 1) / kT, a.Hkv);
+  hipLaunchKernelGGL(prefill_scores_mfma_kernel, grid, dim3(64), 0, s, a, scores, ld);
+  return hipGetLastError();
 }
 
 }  // namespace lsa

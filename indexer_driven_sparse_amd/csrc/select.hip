@@ -25,192 +25,12 @@
 // equal to tau through two bitmaps, and write the selected positions in
 // ascending order from a prefix count over the bitmap, then -1 padding.
 // Rows longer than kSelectLdsMaxSlots keep their bitmaps in workspace.
-#include "common.hpp"
-#include "kernels.hpp"
+#include "select_row.hpp"
 
 namespace lsa {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 2048;
-constexpr int kCap = 8192;          // LDS candidate list
-constexpr int kSampleBlocks = 64;   // fast-path sample: blocks ...
-constexpr int kSampleBlock = 128;   // ... of contiguous slots
-constexpr int kUnroll = 8;          // 128-bit loads in flight per thread (general path)
-constexpr int kCollectUnroll = 8;   // ... in the fast path's collect pass
-
-struct SelShared {
-  uint32_t hist[kBins];
-  uint32_t ckey[kCap];
-  int32_t cslot[kCap];
-  int scan[kWaves + 1];
-  int ncand;
-  int nsample;
-  uint32_t kmax;
-  int wval[kWaves];   // per-wave values (sample counts, thresholds)
-  int bin;      // result of find_bin
-  int above;    // keys in higher bins
-};
-
-template <bool CAND>
-__device__ __forceinline__ bool slot_ok(const SelectArgs& a, const int32_t* crow, int64_t slot,
-                                        int64_t nv) {
-  if (slot >= nv) return false;
-  if constexpr (!CAND) {
-    return true;
-  } else {
-    int32_t c = crow[slot / a.cand_block];
-    if (c < 0) return false;
-    int64_t p = (int64_t)c * a.cand_block + slot % a.cand_block;
-    return p < a.n_positions;
-  }
-}
-
-template <bool CAND>
-__device__ __forceinline__ int32_t slot_pos(const SelectArgs& a, const int32_t* crow, int64_t slot) {
-  if constexpr (!CAND) {
-    return (int32_t)slot;
-  } else {
-    return crow[slot / a.cand_block] * a.cand_block + (int32_t)(slot % a.cand_block);
-  }
-}
-
-// Four consecutive slots [s0, s0+4): order keys and validity bits. FULL:
-// the caller knows s0 + 3 < nv, so the 128-bit load is unconditional and
-// several of them issue back to back; otherwise each slot is guarded.
-template <bool CAND, bool FULL = false>
-__device__ __forceinline__ void load4(const SelectArgs& a, const float* srow, const int32_t* crow,
-                                      int64_t s0, int64_t nv, uint32_t key[4], bool ok[4]) {
-  float v[4];
-  if (FULL || s0 + 3 < nv) {
-    const float4 x = *(const float4*)(srow + s0);
-    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
-  } else {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) v[k] = srow[min(s0 + k, nv - 1)];
-  }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    ok[k] = slot_ok<CAND>(a, crow, s0 + k, nv);
-    key[k] = order_key(v[k]);
-  }
-}
-
-// The 32-bit bitmap word of 32 consecutive slots held 4 per lane by 8
-// consecutive lanes: every lane contributes a nibble, OR-combined with DPP.
-// All 8 lanes of the group must be active.
-__device__ __forceinline__ uint32_t word_from_nibbles(uint32_t nib, int lane) {
-  uint32_t w = nib << (4 * (lane & 7));
-  w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, kDppXor1, 0xf, 0xf, false);
-  w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, kDppXor2, 0xf, 0xf, false);
-  w |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w, kDppHalfMirror, 0xf, 0xf, false);
-  return w;
-}
-
-// Find the bin holding the need-th largest key: the highest bin b with
-// (count above b) < need <= (count above b) + hist[b], for nb <= 2048 bins.
-// Writes sh.bin / sh.above (left unchanged when the total is below need)
-// and returns the total through *total. Contains barriers.
-__device__ __forceinline__ void find_bin(SelShared& sh, const uint32_t* hist, int nb, int need,
-                                         int* total) {
-  const int t = threadIdx.x;
-  const int per = (nb + kThreads - 1) / kThreads;
-  const int hi = nb - 1 - t * per;
-  int c = 0;
-  for (int k = 0; k < per; ++k)
-    if (hi - k >= 0) c += (int)hist[hi - k];
-  int tot;
-  const int above = block_exclusive_scan<kThreads>(c, sh.scan, &tot);
-  int acc = above;
-  for (int k = 0; k < per; ++k) {
-    if (hi - k < 0) break;
-    const int h = (int)hist[hi - k];
-    if (acc < need && need <= acc + h) {
-      sh.bin = hi - k;
-      sh.above = acc;
-    }
-    acc += h;
-  }
-  *total = tot;
-  __syncthreads();
-}
-
-__device__ __forceinline__ void zero_hist(SelShared& sh) {
-  for (int i = threadIdx.x; i < kBins; i += kThreads) sh.hist[i] = 0u;
-}
-
-// Append this lane's flagged slots (their order keys and slot numbers) to
-// the LDS list with one LDS atomic per wave; the lane then walks only its
-// set flag bits. Item i = 4*j + k of a lane holds slot first + j*kThreads*4
-// + k. Entries past kCap are dropped while the count still grows, so the
-// caller sees the overflow. All 64 lanes of the wave must call it.
-template <int M>
-__device__ __forceinline__ void wave_append(SelShared& sh, const float* val, int64_t first,
-                                            uint32_t flags, int lane) {
-  const int mine = __popc(flags);
-  int incl = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += y;
-  }
-  const int total = __shfl(incl, 63, 64);
-  if (total == 0) return;
-  int base = 0;
-  if (lane == 63) base = atomicAdd(&sh.ncand, total);
-  base = __shfl(base, 63, 64) + incl - mine;
-  while (flags) {
-    const int i = __ffs(flags) - 1;
-    flags &= flags - 1;
-    if (base < kCap) {
-      float v = val[0];
-#pragma unroll
-      for (int q = 1; q < M; ++q) v = q == i ? val[q] : v;   // register select, no local memory
-      sh.ckey[base] = order_key(v);
-      sh.cslot[base] = (int32_t)(first + (int64_t)(i / 4) * kThreads * 4 + (i % 4));
-    }
-    ++base;
-  }
-}
-
-// Exact refine of an LDS list whose keys all lie in [lo, hi]: radix levels
-// of up to 11 bits below the common prefix of lo and hi, each a block-wide
-// histogram of the listed keys that match the prefix so far. On return tau
-// is the need-th largest listed key, *need the number of keys equal to tau
-// to take and *ties the number of listed keys equal to tau. Contains
-// barriers.
-__device__ __forceinline__ uint32_t refine_list(SelShared& sh, int ncand, uint32_t lo, uint32_t hi,
-                                                int* need, int* ties) {
-  int fixed = lo == hi ? 32 : __clz(lo ^ hi);
-  uint32_t tau = fixed == 0 ? 0u : (lo & (~0u << (32 - fixed)));
-  int nd = *need;
-  int eq = ncand;   // with no level, every listed key equals tau
-  while (fixed < 32) {
-    const int width = min(11, 32 - fixed);
-    const int shift = 32 - fixed - width;
-    const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
-    const int nb = 1 << width;
-    zero_hist(sh);
-    __syncthreads();
-    for (int i = threadIdx.x; i < ncand; i += kThreads) {
-      const uint32_t key = sh.ckey[i];
-      if ((key & pmask) == tau) atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
-    }
-    __syncthreads();
-    int tl;
-    find_bin(sh, sh.hist, nb, nd, &tl);
-    const int bin = sh.bin;
-    nd -= sh.above;
-    eq = (int)sh.hist[bin];
-    tau |= (uint32_t)bin << shift;
-    fixed += width;
-    __syncthreads();   // hist and bin are rewritten by the next level
-  }
-  *need = nd;
-  *ties = eq;
-  return tau;
-}
+using namespace sel;
 
 // ---------------------------------------------------------------------------
 // Segmented collect (long rows with a selection hint). A row is cut into
@@ -222,11 +42,6 @@ __device__ __forceinline__ uint32_t refine_list(SelShared& sh, int ncand, uint32
 // slot) pairs, with {count, max key, t_lo}. The row kernel then refines the
 // concatenated lists (see select_kernel, PRE).
 // ---------------------------------------------------------------------------
-constexpr int kSegThreads = 256;
-constexpr int kSegWaves = kSegThreads / 64;
-constexpr int kSegUnroll = 8;
-constexpr int kSeg = kSegThreads * 4 * kSegUnroll;   // 8192 slots
-constexpr int kSegUnits = kSegUnroll * kSegWaves;    // (loop step, wave) units, in slot order
 
 struct SegShared {
   uint32_t h1[256];
@@ -426,557 +241,11 @@ __global__ __launch_bounds__(kSegThreads) void select_collect_kernel(SelectArgs 
 template <bool CAND, bool GBM, bool PRE>
 __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  SelShared& sh = *reinterpret_cast<SelShared*>(smem_raw);
   const int row = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int64_t n = a.n;
-  const int nw = (int)((n + 31) >> 5);
-  uint32_t* bm_sel;
-  uint32_t* bm_tie;
-  if constexpr (GBM) {
-    bm_sel = a.gbitmap + (int64_t)row * 2 * nw;
-    bm_tie = bm_sel + nw;
-  } else {
-    bm_sel = reinterpret_cast<uint32_t*>(smem_raw + sizeof(SelShared));
-    bm_tie = bm_sel + nw;
-  }
-
-  int64_t nv = n;
-  if (a.n_valid) nv = min<int64_t>(n, (int64_t)max(0, a.n_valid[row]));
-  if (a.causal_group > 0) nv = min<int64_t>(n, (int64_t)row / a.causal_group + 1);
-  const float* srow = a.scores + (int64_t)row * a.scores_ld;
-  const int32_t* crow = CAND ? a.cand + (int64_t)row * a.cand_ld : nullptr;
-  const int B = a.B;
-  // passes over the row walk block-uniform tiles of kThreads * 4 * kUnroll slots
-  const int64_t tile = (int64_t)kThreads * 4 * kUnroll;
-
-  zero_hist(sh);
-  if constexpr (PRE) {
-    // two more refine histograms, in the (still unused) slot list
-    for (int i = tid; i < 2 * kBins; i += kThreads) sh.cslot[i] = 0;
-  } else {
-    for (int i = tid; i < nw; i += kThreads) {
-      bm_sel[i] = 0u;
-      bm_tie[i] = 0u;
-    }
-  }
-  if (tid == 0) {
-    sh.ncand = 0;
-    sh.nsample = 0;
-    sh.kmax = 0u;
-  }
-  __syncthreads();
-
-  // Outcome of the search: tau is the exact B-th key and `need` the number
-  // of keys equal to tau to take (lowest slots first). With in_lds every key
-  // >= tau is in the LDS list (ncand entries). `all`: take every valid slot.
-  uint32_t tau = 0;
-  int need = 0;
-  int ncand = 0;
-  bool in_lds = false;
-  bool all = false;
-  bool found = false;
-  bool list_has_all = false;   // the LDS list holds every selected slot
-  int ties_known = -1;         // keys equal to tau, when the list refine counted them
-
-  // ---------------- pre-collected lists (segmented collect) ----------------
-  if constexpr (PRE) {
-    // segment offsets of the concatenated list, in the (unused) key list
-    int32_t* seg_off = reinterpret_cast<int32_t*>(sh.ckey);
-    const int4* meta = a.seg_meta + (int64_t)row * a.nseg;
-    int cnt = 0;
-    uint32_t km = 0u;
-    if (tid < a.nseg) {
-      const int4 mm = meta[tid];
-      cnt = mm.x;
-      km = (uint32_t)mm.y;
-    }
-    const uint32_t t_lo = (uint32_t)meta[0].z;
-    int total;
-    const int off = block_exclusive_scan<kThreads>(cnt, sh.scan, &total);
-    if (tid < a.nseg) seg_off[tid] = off;
-    if (tid == 0) seg_off[a.nseg] = total;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) km = max(km, (uint32_t)__shfl_xor((int)km, o, 64));
-    if (lane == 0) atomicMax(&sh.kmax, km);
-    __syncthreads();
-    if (total >= B && total <= kCap) {
-      // Every key >= t_lo of the row is listed and at least B are, so the
-      // B-th key is among them. Thread t holds entries 8t .. 8t+7 (list
-      // order is slot order) in registers.
-      constexpr int kPer = kCap / kThreads;
-      const int i0 = tid * kPer;
-      int sg = 0;
-      if (i0 < total) {
-        int lo = 0, hi = a.nseg - 1;   // last segment starting at or before i0
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (seg_off[mid] <= i0) lo = mid; else hi = mid - 1;
-        }
-        sg = lo;
-      }
-      const int2* lrow = a.seg_list + (int64_t)row * a.nseg * kSeg;
-      int64_t addr[kPer];
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int i = i0 + j;
-        if (i < total) {
-          while (seg_off[sg + 1] <= i) ++sg;
-          addr[j] = (int64_t)sg * kSeg + (i - seg_off[sg]);
-        } else {
-          addr[j] = -1;
-        }
-      }
-      uint32_t key[kPer];
-      float val[kPer];
-      int32_t slot[kPer];
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int2 e = addr[j] >= 0 ? lrow[addr[j]] : make_int2(0, 0);
-        val[j] = __int_as_float(e.x);
-        key[j] = order_key(val[j]);
-        slot[j] = e.y;
-      }
-      // radix levels below the common prefix of [t_lo, max key]; stop as
-      // soon as every key of the B-th key's bin is taken
-      const uint32_t kmax = sh.kmax;
-      int fixed = t_lo == kmax ? 32 : __clz(t_lo ^ kmax);
-      uint32_t pre = fixed == 0 ? 0u : (t_lo & (~0u << (32 - fixed)));
-      int nd = B;
-      int lev = 0;
-      while (fixed < 32) {
-        const int width = min(11, 32 - fixed);
-        const int shift = 32 - fixed - width;
-        const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
-        const int nb = 1 << width;
-        uint32_t* h = lev == 0 ? sh.hist : reinterpret_cast<uint32_t*>(sh.cslot) + (lev - 1) * kBins;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j)
-          if (i0 + j < total && (key[j] & pmask) == pre) atomicAdd(&h[(key[j] >> shift) & (nb - 1)], 1u);
-        __syncthreads();
-        int tl;
-        find_bin(sh, h, nb, nd, &tl);
-        const int bin = sh.bin;
-        nd -= sh.above;
-        const int cnt_bin = (int)h[bin];
-        pre |= (uint32_t)bin << shift;
-        fixed += width;
-        ++lev;
-        if (cnt_bin == nd) break;   // the whole bin is taken
-      }
-      // taken: keys above the bin, and the first nd keys inside it (slot
-      // order); one packed scan gives both running counts
-      const uint32_t bmask = fixed >= 32 ? ~0u : (fixed == 0 ? 0u : (~0u << (32 - fixed)));
-      const uint32_t top = pre | ~bmask;
-      int na = 0, ni = 0;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if (i0 + j < total) {
-          na += key[j] > top;
-          ni += (key[j] & bmask) == pre;
-        }
-      }
-      int tot2;
-      const int pref = block_exclusive_scan<kThreads>(na | (ni << 16), sh.scan, &tot2);
-      int pa = pref & 0xffff, pi = pref >> 16;
-      int32_t* orow = a.out_idx + (int64_t)row * B;
-      float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if (i0 + j >= total) continue;
-        int pos = -1;
-        if (key[j] > top) {
-          pos = pa + min(pi, nd);
-          ++pa;
-        } else if ((key[j] & bmask) == pre) {
-          if (pi < nd) pos = pa + pi;
-          ++pi;
-        }
-        if (pos >= 0) {
-          orow[pos] = slot_pos<CAND>(a, crow, slot[j]);
-          if (osc) osc[pos] = val[j];
-        }
-      }
-      if (tid == 0 && a.out_count) a.out_count[row] = B;
-      return;
-    }
-    // the lists do not settle it: general path over the row
-    for (int i = tid; i < nw; i += kThreads) {
-      bm_sel[i] = 0u;
-      bm_tie[i] = 0u;
-    }
-    __syncthreads();
-  }
-
-  // ---------------- fast path: threshold, then collect keys >= t_lo ----------------
-  if (!PRE && B <= kCap / 2 && nv > B) {
-    uint32_t t_lo = 0u;
-    // the hints can vouch for at most hint_count*hint_k keys
-    const bool use_hint = a.hint != nullptr && a.hint_k > 0 && a.hint_count > 0 &&
-                          (int64_t)a.hint_count * a.hint_k >= B;
-    if (use_hint) {
-      // Hints: entry h vouches that at least hint_k valid keys of its group
-      // reach it. Wave 0 folds them into at most 1024 entries (the min of m
-      // hints vouches for m*hint_k keys) and finds the r-th largest entry,
-      // r = ceil(B / (m*hint_k)), by bisection on the 16-bit prefixes: at
-      // least r entries reach it, so at least B keys of the row do.
-      if (tid < 64) {
-        const uint32_t* hrow = a.hint + (int64_t)row * a.hint_ld;
-        const int m = (a.hint_count + 1023) / 1024;
-        const int ne = (a.hint_count + m - 1) / m;
-        const int r = (B + m * a.hint_k - 1) / (m * a.hint_k);
-        uint32_t e[16];
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const int idx = lane + 64 * j;
-          uint32_t v = idx < ne ? 0xffffffffu : 0u;
-          for (int q = 0; q < m; ++q) {
-            const int h = idx * m + q;
-            if (idx < ne) v = min(v, h < a.hint_count ? hrow[h] : 0u);
-          }
-          e[j] = v;
-        }
-        uint32_t p = 0;
-        if (r <= ne) {
-          for (int bit = 15; bit >= 0; --bit) {
-            const uint32_t cand = (p | (1u << bit)) << 16;
-            int cnt = 0;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) cnt += __popcll(ballot64(e[j] >= cand));
-            if (cnt >= r) p |= 1u << bit;
-          }
-        }
-        if (lane == 0) sh.wval[0] = (int)(p << 16);
-      }
-      __syncthreads();
-      t_lo = (uint32_t)sh.wval[0];
-    } else {
-      // No hint: 64 evenly spaced blocks of 128 slots are radix-histogrammed
-      // (top 11 key bits, then the next 11 inside the chosen bin); t_lo sits
-      // where the sample's suffix count passes twice B's share plus 64.
-      const int64_t nblk = (nv + kSampleBlock - 1) / kSampleBlock;
-      const int64_t stride = max<int64_t>(1, nblk / kSampleBlocks);
-      constexpr int kPer = kSampleBlocks * kSampleBlock / kThreads;
-      float sval[kPer];
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int i = tid + k * kThreads;
-        const int64_t s = (int64_t)(i / kSampleBlock) * stride * kSampleBlock + (i % kSampleBlock);
-        sval[k] = srow[min(s, nv - 1)];   // clamped: every load issues unconditionally
-      }
-      uint32_t skey[kPer];
-      uint32_t sok = 0;
-      int mine = 0;
-#pragma unroll
-      for (int k = 0; k < kPer; ++k) {
-        const int i = tid + k * kThreads;
-        const int64_t s = (int64_t)(i / kSampleBlock) * stride * kSampleBlock + (i % kSampleBlock);
-        const bool ok = slot_ok<CAND>(a, crow, s, nv);
-        skey[k] = ok ? order_key(sval[k]) : 0u;
-        sok |= (uint32_t)ok << k;
-        if (ok) {
-          atomicAdd(&sh.hist[skey[k] >> 21], 1u);
-          ++mine;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o, 64);
-      if (lane == 0) atomicAdd(&sh.nsample, mine);
-      __syncthreads();
-      const double share = (double)sh.nsample / (double)nv;
-      const int target = (int)min<double>((double)sh.nsample, ceil(2.0 * B * share) + 64.0);
-      if (target >= 1) {
-        int tot_s;
-        find_bin(sh, sh.hist, kBins, target, &tot_s);
-        if (tot_s >= target) {
-          const uint32_t sb = (uint32_t)sh.bin;
-          const int need_s = target - sh.above;
-          zero_hist(sh);
-          __syncthreads();
-#pragma unroll
-          for (int k = 0; k < kPer; ++k)
-            if ((sok & (1u << k)) && (skey[k] >> 21) == sb) atomicAdd(&sh.hist[(skey[k] >> 10) & 2047u], 1u);
-          __syncthreads();
-          int tot2;
-          find_bin(sh, sh.hist, kBins, need_s, &tot2);
-          t_lo = (sb << 21) | ((uint32_t)sh.bin << 10);
-        }
-      }
-    }
-
-    // collect every valid key >= t_lo: one float compare per slot (the key
-    // order is the float order with -0 == +0; NaN only when t_lo is 0)
-    const bool take_all = t_lo == 0u;
-    const float t_f = key_to_float(t_lo);
-    constexpr int kCU = kCollectUnroll;
-    const int64_t ctile = (int64_t)kThreads * 4 * kCU;
-    int64_t t0 = 0;
-    for (; t0 + ctile <= nv; t0 += ctile) {   // full tiles: straight-line 128-bit loads
-      float4 raw[kCU];
-#pragma unroll
-      for (int j = 0; j < kCU; ++j)
-        raw[j] = *(const float4*)(srow + t0 + (int64_t)j * kThreads * 4 + (int64_t)tid * 4);
-      float v[4 * kCU];
-      uint32_t flags = 0;
-#pragma unroll
-      for (int j = 0; j < kCU; ++j) {
-        v[4 * j] = raw[j].x; v[4 * j + 1] = raw[j].y; v[4 * j + 2] = raw[j].z; v[4 * j + 3] = raw[j].w;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          bool take = take_all || v[4 * j + k] >= t_f;
-          if constexpr (CAND) take = take && slot_ok<CAND>(a, crow, t0 + (int64_t)j * kThreads * 4 + (int64_t)tid * 4 + k, nv);
-          flags |= (uint32_t)take << (4 * j + k);
-        }
-      }
-      wave_append<4 * kCU>(sh, v, t0 + (int64_t)tid * 4, flags, lane);
-    }
-    if (t0 < nv) {   // the partial last tile, clamped scalar loads
-      float v[4 * kCU];
-#pragma unroll
-      for (int j = 0; j < kCU; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          v[4 * j + k] = srow[min(t0 + (int64_t)j * kThreads * 4 + (int64_t)tid * 4 + k, nv - 1)];
-      uint32_t flags = 0;
-#pragma unroll
-      for (int j = 0; j < kCU; ++j)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const bool take = take_all || v[4 * j + k] >= t_f;
-          flags |= (uint32_t)(take && slot_ok<CAND>(a, crow, t0 + (int64_t)j * kThreads * 4 + (int64_t)tid * 4 + k, nv)) << (4 * j + k);
-        }
-      wave_append<4 * kCU>(sh, v, t0 + (int64_t)tid * 4, flags, lane);
-    }
-    __syncthreads();
-    ncand = sh.ncand;
-    if (ncand >= B && ncand <= kCap) {
-      in_lds = true;
-      found = true;
-      list_has_all = true;
-      uint32_t kmax = 0;
-      for (int i = tid; i < ncand; i += kThreads) kmax = max(kmax, sh.ckey[i]);
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
-      if (lane == 0) atomicMax(&sh.kmax, kmax);
-      __syncthreads();
-      need = B;
-      tau = refine_list(sh, ncand, t_lo, sh.kmax, &need, &ties_known);
-    } else {
-      zero_hist(sh);   // the guess failed: start the general path clean
-      __syncthreads();
-      if (tid == 0) sh.ncand = 0;
-      __syncthreads();
-    }
-  }
-
-  // ---------------- general path ----------------
-  if (!found) {
-    // pass A: histogram of every valid key; bm_tie temporarily holds "valid"
-    for (int64_t t0 = 0; t0 < nv; t0 += tile) {
-#pragma unroll
-      for (int j = 0; j < kUnroll; ++j) {
-        const int64_t s0 = t0 + (int64_t)j * kThreads * 4 + (int64_t)tid * 4;
-        uint32_t key[4];
-        bool ok[4];
-        load4<CAND>(a, srow, crow, s0, nv, key, ok);
-        uint32_t nib = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          if (ok[k]) {
-            atomicAdd(&sh.hist[key[k] >> 21], 1u);
-            nib |= 1u << k;
-          }
-        }
-        const uint32_t w = word_from_nibbles(nib, lane);
-        if ((lane & 7) == 0 && s0 < nv) bm_tie[s0 >> 5] = w;
-      }
-    }
-    __syncthreads();
-    int total;
-    find_bin(sh, sh.hist, kBins, B, &total);
-    if (total <= B) {
-      all = true;
-    } else {
-      const uint32_t b0 = (uint32_t)sh.bin;
-      need = B - sh.above;
-      const int cnt_b0 = (int)sh.hist[b0];
-      in_lds = cnt_b0 <= kCap;
-      for (int i = tid; i < nw; i += kThreads) bm_tie[i] = 0u;
-      __syncthreads();
-      // pass B: above b0 -> selected outright; inside b0 -> LDS list
-      for (int64_t t0 = 0; t0 < nv; t0 += tile) {
-#pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          const int64_t s0 = t0 + (int64_t)j * kThreads * 4 + (int64_t)tid * 4;
-          uint32_t key[4];
-          bool ok[4];
-          load4<CAND>(a, srow, crow, s0, nv, key, ok);
-          uint32_t nib = 0, flags = 0;
-          float val[4];
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            nib |= (uint32_t)(ok[k] && (key[k] >> 21) > b0) << k;
-            flags |= (uint32_t)(ok[k] && (key[k] >> 21) == b0) << k;
-            val[k] = key_to_float(key[k]);
-          }
-          const uint32_t w = word_from_nibbles(nib, lane);
-          if ((lane & 7) == 0 && s0 < nv) bm_sel[s0 >> 5] = w;
-          if (in_lds) wave_append<4>(sh, val, s0, flags, lane);
-        }
-      }
-      __syncthreads();
-      tau = b0 << 21;
-      if (in_lds) {
-        ncand = cnt_b0;
-        tau = refine_list(sh, ncand, b0 << 21, (b0 << 21) | 0x1fffffu, &need, &ties_known);
-      } else {
-        for (int level = 1; level <= 2; ++level) {
-          const int shift = level == 1 ? 10 : 0;
-          const int nb = level == 1 ? 2048 : 1024;
-          const uint32_t pmask = level == 1 ? 0xffe00000u : 0xfffffc00u;
-          zero_hist(sh);
-          __syncthreads();
-          for (int64_t t0 = 0; t0 < nv; t0 += tile) {
-#pragma unroll
-            for (int j = 0; j < kUnroll; ++j) {
-              const int64_t s0 = t0 + (int64_t)j * kThreads * 4 + (int64_t)tid * 4;
-              uint32_t key[4];
-              bool ok[4];
-              load4<CAND>(a, srow, crow, s0, nv, key, ok);
-#pragma unroll
-              for (int k = 0; k < 4; ++k)
-                if (ok[k] && (key[k] & pmask) == tau) atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1u);
-            }
-          }
-          __syncthreads();
-          int tl;
-          find_bin(sh, sh.hist, nb, need, &tl);
-          tau |= (uint32_t)sh.bin << shift;
-          need -= sh.above;
-        }
-      }
-    }
-  }
-
-  // ---------------- mark keys above tau, and the ties ----------------
-  const int wpt = (nw + kThreads - 1) / kThreads;
-  const int w0 = tid * wpt, w1 = min(nw, w0 + wpt);
-  if (!all) {
-    // keys equal to tau: from the list refine, or the last global level's bin
-    const int ties = ties_known >= 0 ? ties_known : (int)sh.hist[tau & 1023u];
-    __syncthreads();
-    if (in_lds) {
-      for (int i = tid; i < ncand; i += kThreads) {
-        const uint32_t key = sh.ckey[i];
-        const int32_t s = sh.cslot[i];
-        if (key > tau) atomicOr(&bm_sel[s >> 5], 1u << (s & 31));
-        else if (key == tau) atomicOr(&bm_tie[s >> 5], 1u << (s & 31));
-      }
-    } else {
-      const uint32_t b0 = tau >> 21;
-      for (int64_t t0 = 0; t0 < nv; t0 += tile) {
-#pragma unroll
-        for (int j = 0; j < kUnroll; ++j) {
-          const int64_t s0 = t0 + (int64_t)j * kThreads * 4 + (int64_t)tid * 4;
-          uint32_t key[4];
-          bool ok[4];
-          load4<CAND>(a, srow, crow, s0, nv, key, ok);
-          uint32_t ns = 0, nt = 0;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const bool inb = ok[k] && (key[k] >> 21) == b0;
-            ns |= (uint32_t)(inb && key[k] > tau) << k;
-            nt |= (uint32_t)(inb && key[k] == tau) << k;
-          }
-          const uint32_t ws = word_from_nibbles(ns, lane);
-          const uint32_t wt = word_from_nibbles(nt, lane);
-          if ((lane & 7) == 0 && s0 < nv) {
-            bm_sel[s0 >> 5] |= ws;
-            bm_tie[s0 >> 5] = wt;
-          }
-        }
-      }
-    }
-    __syncthreads();
-    // take the `need` lowest tie slots
-    if (need == ties) {
-      for (int w = w0; w < w1; ++w) bm_sel[w] |= bm_tie[w];
-    } else {
-      int c = 0;
-      for (int w = w0; w < w1; ++w) c += __popc(bm_tie[w]);
-      int tot_t;
-      const int before = block_exclusive_scan<kThreads>(c, sh.scan, &tot_t);
-      int rem = need - before;
-      for (int w = w0; w < w1 && rem > 0; ++w) {
-        uint32_t t = bm_tie[w];
-        const int pc = __popc(t);
-        if (pc <= rem) {
-          bm_sel[w] |= t;
-          rem -= pc;
-        } else {
-          uint32_t keep = 0;
-          while (rem > 0) {
-            const uint32_t low = t & (0u - t);
-            keep |= low;
-            t ^= low;
-            --rem;
-          }
-          bm_sel[w] |= keep;
-        }
-      }
-    }
-  } else {
-    for (int w = w0; w < w1; ++w) bm_sel[w] = bm_tie[w];
-  }
-  __syncthreads();
-
-  // ---------------- output: ascending positions ----------------
-  int c = 0;
-  for (int w = w0; w < w1; ++w) c += __popc(bm_sel[w]);
-  int count;
-  int off = block_exclusive_scan<kThreads>(c, sh.scan, &count);
-  int32_t* orow = a.out_idx + (int64_t)row * B;
-  float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
-  if (list_has_all) {
-    // bm_tie becomes the per-word prefix count of bm_sel; each listed slot
-    // that is selected finds its output position from it in parallel
-    for (int w = w0; w < w1; ++w) {
-      const uint32_t b = bm_sel[w];
-      bm_tie[w] = (uint32_t)off;
-      off += __popc(b);
-    }
-    __syncthreads();
-    for (int i = tid; i < ncand; i += kThreads) {
-      const int32_t s = sh.cslot[i];
-      const uint32_t word = bm_sel[s >> 5];
-      if ((word >> (s & 31)) & 1u) {
-        const int pos = (int)bm_tie[s >> 5] + __popc(word & ((1u << (s & 31)) - 1u));
-        if (pos < B) {
-          orow[pos] = slot_pos<CAND>(a, crow, s);
-          if (osc) osc[pos] = srow[s];
-        }
-      }
-    }
-  } else {
-    for (int w = w0; w < w1; ++w) {
-      uint32_t bits = bm_sel[w];
-      while (bits) {
-        const int b = __ffs(bits) - 1;
-        bits &= bits - 1;
-        const int64_t s = ((int64_t)w << 5) + b;
-        if (off < B) {
-          orow[off] = slot_pos<CAND>(a, crow, s);
-          if (osc) osc[off] = srow[s];
-        }
-        ++off;
-      }
-    }
-  }
-  for (int j = count + tid; j < B; j += kThreads) {
-    orow[j] = -1;
-    if (osc) osc[j] = -INFINITY;
-  }
-  if (tid == 0 && a.out_count) a.out_count[row] = min(count, B);
+  int64_t nv = a.n;
+  if (a.n_valid) nv = min<int64_t>(nv, (int64_t)max(0, a.n_valid[row]));
+  if (a.causal_group > 0) nv = min<int64_t>(nv, (int64_t)row / a.causal_group + 1);
+  select_row<CAND, GBM, PRE>(a, row, a.scores + (int64_t)row * a.scores_ld, nv, smem_raw);
 }
 
 template <bool CAND>

@@ -217,3 +217,46 @@ def test_hint_validation_and_layout():
     assert lib.lsa_topk_select(ctypes.byref(s), None, 0, None) == INVALID
     s = _select_desc(hint=0x5000, hint_count=8, hint_k=4, hint_ld=7)
     assert lib.lsa_topk_select(ctypes.byref(s), None, 0, None) == INVALID
+
+
+def _prefill_desc(**kw):
+    d = lsa.ScoreDesc()
+    d.struct_size = ctypes.sizeof(lsa.ScoreDesc)
+    d.mode, d.n_seq, d.n_kv_heads, d.n_keys, d.rank = lsa.MODE_PREFILL_CAUSAL, 1, 1, 65536, 64
+    d.q_idx = 0x1000
+    d.k_idx = 0x2000
+    d.k_idx_dtype = lsa.BF16
+    d.k_stride_head, d.k_stride_tok = 64, 64
+    d.topk = 2048
+    d.out_idx = 0x3000
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_prefill_fused_workspace_and_limits():
+    lib = lsa._lib()
+    ws = lib.lsa_score_workspace_bytes(ctypes.byref(_prefill_desc()))
+    # candidate sub-lists (8 x 1024 pairs per row) dominate: 64 KiB per row
+    assert ws >= 65536 * 8 * 1024 * 8
+    assert lib.lsa_score_workspace_bytes(ctypes.byref(_prefill_desc(n_keys=4096))) < ws
+    assert lsa.prefill_score_workspace_bytes_for(65536, 1, 64, 2048) == ws
+    # the workspace check comes after validation: a valid fused call without
+    # one is a workspace error (no HIP call is made)
+    assert _call_score(_prefill_desc()) == WORKSPACE
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("rank", 32, UNSUPPORTED),              # the MFMA path is built for r = 64
+    ("topk", 4097, UNSUPPORTED),            # candidates would not fit the sub-lists
+    ("n_keys", 262145, UNSUPPORTED),        # bitmaps beyond LDS
+    ("k_stride_tok", 68, INVALID),          # rows must stay 16-byte aligned
+    ("k_idx", 0x2008, INVALID),
+    ("q_idx", 0x1008, INVALID),
+    ("k_idx_dtype", lsa.F32, UNSUPPORTED),
+    ("out_idx", 0, INVALID),
+    ("topk", -1, INVALID),
+    ("n_seq", 2, INVALID),
+])
+def test_prefill_fused_validation(field, value, code):
+    assert _call_score(_prefill_desc(**{field: value})) == code

@@ -607,3 +607,148 @@ def test_segmented_select_candidates():
                         hint=dev(hint), hint_k=k)
     ref, _, _ = oracle.topk(x, B, cand=cand, cand_block=blk, n_positions=n_positions)
     np.testing.assert_array_equal(host(idx), ref)
+
+
+# --------------------------------------------------------------------------
+# causal prefill indexer: fused top-B == select over the unfused scores,
+# and both against the oracle
+# --------------------------------------------------------------------------
+
+def _prefill_qk(kind, L, Hkv, seed):
+    rng = np.random.default_rng(seed)
+    if kind == "c4":
+        case = synth.make_prefill_case(L, Hkv=Hkv, seed=seed)
+        return case.q_idx, case.k_idx
+    if kind == "int":      # integer-valued: exact scores, many exact ties
+        q = rng.integers(-3, 4, size=(L, Hkv, 64)).astype(np.float32)
+        k = rng.integers(-3, 4, size=(L, Hkv, 64)).astype(np.float32)
+        return synth.to_bf16_bits(q), synth.to_bf16_bits(k)
+    if kind == "const":    # every key equal: each row is one big tie
+        q = rng.standard_normal((L, Hkv, 64)).astype(np.float32)
+        k = np.broadcast_to(rng.standard_normal((1, Hkv, 64)).astype(np.float32), (L, Hkv, 64))
+        return synth.to_bf16_bits(q), synth.to_bf16_bits(np.ascontiguousarray(k))
+    raise KeyError(kind)
+
+
+def _prefill_fused(qd, kd, B):
+    L, Hkv, _ = kd.shape
+    idx = torch.empty(L, Hkv, B, dtype=torch.int32, device="cuda")
+    osc = torch.empty(L, Hkv, B, device="cuda")
+    lsa.lsa_index_score(kd, None, q_idx=qd, mode=lsa.MODE_PREFILL_CAUSAL, topk=B, out_idx=idx,
+                        out_score=osc)
+    return idx, osc
+
+
+def _prefill_unfused(qd, kd, B):
+    L, Hkv, _ = kd.shape
+    sc = torch.empty(L, Hkv, L + (4 - L % 4) % 4, device="cuda")[:, :, :L]
+    lsa.lsa_index_score(kd, sc, q_idx=qd, mode=lsa.MODE_PREFILL_CAUSAL)
+    idx = torch.empty(L * Hkv, B, dtype=torch.int32, device="cuda")
+    osc = torch.empty(L * Hkv, B, device="cuda")
+    lsa.lsa_topk_select(sc, B, idx, out_score=osc, causal_group=Hkv)
+    return sc, idx.view(L, Hkv, B), osc.view(L, Hkv, B)
+
+
+def _check_prefill_shape(idx, B):
+    L = idx.shape[0]
+    for i in range(L):
+        for g in range(idx.shape[1]):
+            row = idx[i, g]
+            c = min(B, i + 1)
+            assert (row[c:] == -1).all() and (row[:c] >= 0).all() and (row[:c] <= i).all(), (i, g)
+            if i + 1 <= B:
+                np.testing.assert_array_equal(row[:c], np.arange(i + 1))
+
+
+@pytest.mark.parametrize("kind,L,Hkv,B", [("c4", 4096, 1, 2048), ("c4", 4096, 2, 2048),
+                                          ("c4", 3000, 1, 700), ("c4", 1000, 1, 2048),
+                                          ("c4", 777, 2, 1), ("int", 4096, 1, 2048),
+                                          ("int", 2500, 2, 333), ("const", 12000, 1, 2048)])
+def test_prefill_fused_equals_unfused(kind, L, Hkv, B):
+    say("prefill fused vs unfused", kind, L, Hkv, B)
+    q, k = _prefill_qk(kind, L, Hkv, seed=L + B)
+    qd, kd = dev(q), dev(k)
+    idx, osc = _prefill_fused(qd, kd, B)
+    sc, idx2, osc2 = _prefill_unfused(qd, kd, B)
+    gi, gi2 = host(idx), host(idx2)
+    np.testing.assert_array_equal(gi, gi2)
+    np.testing.assert_array_equal(host(osc).view(np.uint32) & 0x7fffffff,
+                                  host(osc2).view(np.uint32) & 0x7fffffff)
+    np.testing.assert_array_equal(host(osc), host(osc2))
+    _check_prefill_shape(gi, B)
+    if L <= 4096:
+        # the scores against the oracle's fp64 ones, and the sets (near ties)
+        ref_sc = oracle.prefill_scores(q, k)                       # [L, Hkv, L]
+        qf, kf = decoded(q).astype(np.float64), decoded(k).astype(np.float64)
+        gsc = host(sc)
+        for g in range(Hkv):
+            guard = np.abs(qf[:, g]) @ np.abs(kf[:, g]).T
+            r_, s_ = ref_sc[:, g], gsc[:, g]
+            np.testing.assert_array_equal(np.isneginf(s_), np.isneginf(r_))
+            fin = np.isfinite(r_)
+            assert np.all(np.abs(s_[fin] - r_[fin]) <= 1e-3 * np.abs(r_[fin]) + 1e-5 * guard[fin])
+        ref_idx, _ = oracle.prefill_topk(q, k, B)
+        for g in range(Hkv):
+            check_index_sets(gi[:, g], ref_idx[:, g], [ref_sc[i, g] for i in range(L)], B)
+
+
+def test_prefill_fused_sample_overshoot():
+    """The per-row threshold comes from a key sample; keys planted at exactly
+    the sampled positions make it too high for many rows, which must then
+    be recomputed (the redo path) with the same result."""
+    L, Hkv, B = 6000, 1, 2048
+    say("prefill sample overshoot", L, Hkv, B)
+    q, k = _prefill_qk("c4", L, Hkv, seed=5)
+    qf = decoded(q).astype(np.float32)
+    kf = decoded(k).astype(np.float32)
+    # the kernel's sample: per block of 32 rows, m = min(prefix, 1024) keys,
+    # one per stratum at a fixed offset
+    # the last block of 32 rows samples m = 1024 of its nb = 6000 keys, one
+    # per stratum at a fixed offset: plant exactly those
+    nb, m = L, 1024
+    planted = np.array([kk * nb // m + ((kk * 2654435761) % 2**32 >> 8) % ((kk + 1) * nb // m - kk * nb // m)
+                        for kk in range(m)])
+    u = qf.mean(axis=(0, 1))
+    kf[planted, 0, :] += 6.0 * u / np.linalg.norm(u)
+    k = synth.to_bf16_bits(kf)
+    qd, kd = dev(q), dev(k)
+    idx, osc = _prefill_fused(qd, kd, B)
+    _, idx2, osc2 = _prefill_unfused(qd, kd, B)
+    np.testing.assert_array_equal(host(idx), host(idx2))
+    np.testing.assert_array_equal(host(osc), host(osc2))
+
+
+def test_prefill_c4_full_size():
+    """L = 65536, 1 KV head, B = 2048: every row against select over the
+    unfused scores (16 GiB), sampled rows against the oracle."""
+    case = synth.workload("prefill_l64k")
+    L, Hkv, B = case.L, case.Hkv, case.B
+    say("prefill C4 full size", L, Hkv, B)
+    qd, kd = dev(case.q_idx), dev(case.k_idx)
+    idx, osc = _prefill_fused(qd, kd, B)
+    gi = host(idx)
+    gs = host(osc)
+    del osc
+    sc, idx2, _ = _prefill_unfused(qd, kd, B)
+    del sc
+    np.testing.assert_array_equal(gi, host(idx2))
+    del idx2
+    torch.cuda.empty_cache()
+    rows = [0, 1, 31, 32, 2046, 2047, 2048, 2049, 4095, 4096, 32767, 65534, 65535]
+    rows += list(np.random.default_rng(9).integers(2050, L, size=19))
+    qf = decoded(case.q_idx).astype(np.float64)
+    kf = decoded(case.k_idx).astype(np.float64)
+    for i in rows:
+        ref, rs = oracle.prefill_topk(case.q_idx, case.k_idx, B, row_begin=i, row_end=i + 1)
+        s_full = np.full(L, -np.inf)
+        s_full[:i + 1] = kf[:i + 1, 0] @ qf[i, 0]
+        check_index_sets(gi[i:i + 1, 0], ref[:, 0], [s_full], B)
+        c = min(B, i + 1)
+        sel = gi[i, 0, :c]
+        guard = np.abs(kf[sel, 0]) @ np.abs(qf[i, 0])
+        assert np.all(np.abs(gs[i, 0, :c] - s_full[sel]) <= 1e-3 * np.abs(s_full[sel]) + 1e-5 * guard)
+    # structure of every row
+    for i in range(0, L, 97):
+        c = min(B, i + 1)
+        row = gi[i, 0]
+        assert (row[c:] == -1).all() and np.all(np.diff(row[:c]) > 0) and row[c - 1] <= i
