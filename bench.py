@@ -144,6 +144,43 @@ def prefill_leg(torch, lsa, synth, runs: int = 5) -> dict:
             "parity_pass": ok == len(rows)}
 
 
+def hierarchical_leg(torch, lsa, synth, pipeline, steps: int = 200) -> dict:
+    """Coarse-to-fine decode at T = 1048576 (1 sequence, GQA 32/8, block 64,
+    top-128 blocks, top-2048): warm back-to-back steps (centroid scores,
+    block select, candidate scores, token select, attention)."""
+    case = synth.workload("hier_t1m")
+    N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
+    blk, Bc = case.block, case.B_coarse
+    Q, W = to_dev(case.Q, torch), to_dev(case.W, torch)
+    K, V = to_dev(case.K, torch), to_dev(case.V, torch)
+    k_idx = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_project_keys(K, W, k_idx)
+    cent = torch.empty(N, Hkv, T // blk, r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_build_centroids(k_idx, blk, cent)
+    plan = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc)
+    stream = torch.cuda.current_stream()
+    for _ in range(20):
+        plan.run(Q, W, k_idx, cent, K, V)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        plan.run(Q, W, k_idx, cent, K, V)
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1000.0
+    nb = T // blk
+    alg = (N * Hkv * nb * r * 2 + N * Hkv * Bc * blk * r * 2 + N * Hkv * B * 2 * d * 2
+           + N * Hkv * (Bc + B) * 4 + N * Hq * d * (2 + 4))
+    planted = all(np.isin(case.planted[g], plan.idx[0, g].cpu().numpy()).all() for g in range(Hkv))
+    log(f"hierarchical: {us:.1f} us/step (warm), planted spans recovered: {planted}")
+    return {"workload": "hierarchical decode, 1 sequence x 1048576 tokens, GQA 32/8, d=128, r=64, "
+                        "block 64, top-128 blocks, top-2048, bf16, hot spans",
+            "us_per_step": us, "steps_per_s": 1e6 / us, "algorithmic_bytes_per_step": alg,
+            "hbm_frac": alg / (us * 1e-6) / (HBM_PEAK_GBPS * 1e9),
+            "planted_spans_recovered": bool(planted)}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +189,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="wall time budget of the CPU-oracle baseline (0 disables it)")
     ap.add_argument("--no-stages", action="store_true", help="skip the per-stage timing loops")
+    ap.add_argument("--no-hierarchical", action="store_true",
+                    help="skip the coarse-to-fine decode leg (T=1048576)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the causal prefill leg (L=65536 fused indexer + sparse attention)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -291,9 +330,14 @@ def main() -> int:
         del src, dst
 
     prefill = None
-    if not args.no_prefill:
+    hier = None
+    if not (args.no_prefill and args.no_hierarchical):
         del inst, plan
         torch.cuda.empty_cache()
+    if not args.no_hierarchical:
+        hier = hierarchical_leg(torch, lsa, synth, pipeline)
+        torch.cuda.empty_cache()
+    if not args.no_prefill:
         prefill = prefill_leg(torch, lsa, synth)
 
     traffic = measured_traffic(kidx_bytes)
@@ -323,6 +367,7 @@ def main() -> int:
                      "avg_launch_us": score_ms * 1000.0,
                      "traffic": traffic},
         "stages": stages,
+        "hierarchical": hier,
         "prefill": prefill,
         "cpu_baseline": cpu,
         "parity": parity,

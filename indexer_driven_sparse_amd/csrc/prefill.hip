@@ -12,19 +12,19 @@
 //
 // Fused selection, four kernels:
 //   sample  per block of 32 query rows, MFMA scores against a jittered
-//           stratified sample of at most 1024 keys of the causal prefix; per
+//           stratified sample of at most 4096 keys of the causal prefix; per
 //           row, two 8-bit radix levels give a threshold tau that the sample
-//           says about B plus a 4-sigma margin of the row's keys reach;
+//           says about B plus a 3.5-sigma margin of the row's keys reach;
 //   cand    per block of 128 query rows (4 waves x 32), all causal key tiles;
 //           each score >= tau of its row is appended, as (score bits, j), to
-//           one of the row's 8 candidate sub-lists (wave, lane half);
-//   final   per row: if the sub-lists did not overflow and hold at least
+//           the row's candidate list;
+//   final   per row: if the list did not overflow and holds at least
 //           min(B, i+1) entries, every key ranking above the B-th one is
 //           among them, so a radix select over them is exact; the positions
 //           go out ascending through an LDS bitmap. Otherwise the row is put
 //           on a redo list (the sample decides speed, never the result);
 //   redo    recomputes each listed row's scores (same MFMA sequence) into a
-//           scratch row and runs the general single-row select on it.
+//           scratch row, then the general single-row select runs on it.
 #include "select_row.hpp"
 
 namespace lsa {
@@ -40,12 +40,12 @@ constexpr int kT = 32;           // keys per MFMA tile = query rows per block
 constexpr int kCh = 4;           // rank 64 = four 16-deep chunks
 constexpr int kRank = 16 * kCh;
 
-constexpr int kSampleMax = 1024; // sampled keys per block of 32 query rows
+constexpr int kSampleMax = 4096; // sampled keys per block of 32 query rows
+constexpr int kHistLd = 257;     // padded histogram row: rows fall on different LDS banks
 constexpr int kRowsA = 128;      // query rows per candidate workgroup
-constexpr int kSub = 8;          // candidate sub-lists per row
-constexpr int kSubCap = 1024;    // entries per sub-list
+constexpr int kCandCap = 8192;   // candidate list entries per row
 constexpr int kFinThreads = 256;
-constexpr int kFinPer = kSub * kSubCap / kFinThreads;  // candidates per thread (32)
+constexpr int kFinPer = kCandCap / kFinThreads;  // candidates per thread (32)
 constexpr int kRedoBlocks = 256;
 
 // 8 bf16 of row p for chunk c and lane half h: elements 16c + 8h .. +8.
@@ -113,7 +113,8 @@ __global__ __launch_bounds__(64) void prefill_scores_mfma_kernel(PrefillTopkArgs
 // sample: per-row threshold tau
 // ---------------------------------------------------------------------------
 struct SampleShared {
-  uint32_t hist[kT][256];
+  uint32_t hist[kT][kHistLd];
+  int pos[kSampleMax];   // the block's sample positions, increasing
   int nvalid[kT];
   int target[kT];   // sample keys that should reach tau (0: no threshold)
   int bin1[kT];
@@ -179,7 +180,8 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
 #pragma unroll
     for (int c = 0; c < kCh; ++c) qb[c] = frag(qp, c, h);
   }
-  for (int q = tid; q < kT * 256; q += 256) (&sh.hist[0][0])[q] = 0u;
+  for (int q = tid; q < kT * kHistLd; q += 256) (&sh.hist[0][0])[q] = 0u;
+  for (int q = tid; q < m; q += 256) sh.pos[q] = sample_pos(q, m, nb);
   if (tid < kT) {
     sh.nvalid[tid] = 0;
     sh.bin1[tid] = -1;
@@ -192,14 +194,14 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
     const int b1 = pass ? sh.bin1[n] : 0;
     for (int t = w; t < ntiles; t += 4) {
       bf16x8 ka[kCh];
-      const uint16_t* kp = krow(a, g, sample_pos(min(t * kT + n, m - 1), m, nb));
+      const uint16_t* kp = krow(a, g, sh.pos[min(t * kT + n, m - 1)]);
 #pragma unroll
       for (int c = 0; c < kCh; ++c) ka[c] = frag(kp, c, h);
       const f32x16 acc = tile_scores(ka, qb);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int k = t * kT + tile_key(v, h);
-        if (k < m && i < a.L && sample_pos(k, m, nb) <= i) {
+        if (k < m && i < a.L && sh.pos[k] <= i) {
           const uint32_t key = order_key(acc[v]);
           if (pass == 0) {
             atomicAdd(&sh.hist[n][key >> 24], 1u);
@@ -213,14 +215,15 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
     if (pass == 0) atomicAdd(&sh.nvalid[n], nval);
     __syncthreads();
     if (pass == 0 && tid < kT) {
-      // sample keys expected to rank among the row's top B, plus a 4-sigma
-      // (binomial) margin and 8; 0 (no threshold) when that is the sample
+      // sample keys expected to rank among the row's top B, plus a
+      // 3.5-sigma (binomial) margin and 6; 0 (no threshold) when that is the
+      // whole sample. A miss costs a recomputed row, never the result.
       const int row = i0 + tid;
       const int mv = sh.nvalid[tid];
       int tgt = 0;
       if (row < a.L && mv > 0) {
         const double e = (double)a.B * mv / (double)(row + 1);
-        const double k = ceil(e + 4.0 * sqrt(e) + 8.0);
+        const double k = ceil(e + 3.5 * sqrt(e) + 6.0);
         tgt = k < (double)mv ? (int)k : 0;
       }
       sh.target[tid] = tgt;
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
     else sample_find(sh, sh.need2, sh.bin2);
     __syncthreads();
     if (pass == 0) {
-      for (int q = tid; q < kT * 256; q += 256) (&sh.hist[0][0])[q] = 0u;
+      for (int q = tid; q < kT * kHistLd; q += 256) (&sh.hist[0][0])[q] = 0u;
       __syncthreads();
     }
   }
@@ -253,15 +256,16 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
 __global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, const float* tau,
                                                            int2* cand, int* cnt) {
   __shared__ __align__(16) float stash[4][64][20];   // per wave, per lane: 16 scores (+pad)
+  __shared__ int rcnt[kRowsA];                       // candidates appended per row
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
   const int blk = gridDim.x - 1 - blockIdx.x;   // longest prefixes first
   const int g = blockIdx.y;
   const int r0 = blk * kRowsA;
   const int kend = min(a.L, r0 + kRowsA);      // keys [0, kend) reach some row here
+  if (tid < kRowsA) rcnt[tid] = 0;
   bf16x8 qb[4][kCh];
   float tq[4];
-  int c[4];
-  int64_t sub[4];
+  int2* list[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
     const int i = r0 + kT * b + n;
@@ -269,53 +273,64 @@ __global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, co
 #pragma unroll
     for (int ch = 0; ch < kCh; ++ch) qb[b][ch] = frag(qp, ch, h);
     tq[b] = i < a.L ? tau[(int64_t)i * a.Hkv + g] : INFINITY;
-    c[b] = 0;
-    sub[b] = (((int64_t)min(i, a.L - 1) * a.Hkv + g) * kSub + 2 * w + h) * kSubCap;
+    list[b] = cand + ((int64_t)min(i, a.L - 1) * a.Hkv + g) * kCandCap;
+  }
+  __syncthreads();
+  // Per tile: the four row blocks' MFMAs first (one wait for the tile's
+  // loads), then the next tile's loads, then the epilogues. Each row has
+  // one list; a lane reserves room for its candidates of the tile with one
+  // LDS atomic and writes them as a contiguous run, so every row's list
+  // grows at a single tail and the stores combine into full lines in L2.
+  bf16x8 ka[kCh];
+  {
+    const uint16_t* kp = krow(a, g, min(w * kT + n, a.L - 1));
+#pragma unroll
+    for (int ch = 0; ch < kCh; ++ch) ka[ch] = frag(kp, ch, h);
   }
   for (int t = w; t * kT < kend; t += 4) {
     const int j0 = t * kT;
-    bf16x8 ka[kCh];
-    {
-      const uint16_t* kp = krow(a, g, min(j0 + n, a.L - 1));
+    f32x16 acc[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[b] = tile_scores(ka, qb[b]);
+    if ((t + 4) * kT < kend) {
+      const uint16_t* kp = krow(a, g, min(j0 + 4 * kT + n, a.L - 1));
 #pragma unroll
       for (int ch = 0; ch < kCh; ++ch) ka[ch] = frag(kp, ch, h);
     }
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const int qlo = r0 + kT * b;
-      if (j0 > qlo + kT - 1) continue;           // the tile is above every row's diagonal
-      const f32x16 acc = tile_scores(ka, qb[b]);
+      if (j0 > qlo + kT - 1) continue;            // above every row's diagonal
       const int i = qlo + n;
       uint32_t flags = 0;
       if (j0 + kT - 1 <= qlo) {                   // the whole tile is causal for every row
 #pragma unroll
-        for (int v = 0; v < 16; ++v) flags |= (uint32_t)(acc[v] >= tq[b]) << v;
+        for (int v = 0; v < 16; ++v) flags |= (uint32_t)(acc[b][v] >= tq[b]) << v;
       } else {
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          flags |= (uint32_t)(acc[v] >= tq[b] && j0 + tile_key(v, h) <= i) << v;
+          flags |= (uint32_t)(acc[b][v] >= tq[b] && j0 + tile_key(v, h) <= i) << v;
       }
       if (__ballot(flags != 0)) {
+        int pos = 0;
+        if (flags) pos = atomicAdd(&rcnt[kT * b + n], __popc(flags));
         float4* st = reinterpret_cast<float4*>(&stash[w][lane][0]);
-        st[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
-        st[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
-        st[2] = make_float4(acc[8], acc[9], acc[10], acc[11]);
-        st[3] = make_float4(acc[12], acc[13], acc[14], acc[15]);
+        st[0] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
+        st[1] = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
+        st[2] = make_float4(acc[b][8], acc[b][9], acc[b][10], acc[b][11]);
+        st[3] = make_float4(acc[b][12], acc[b][13], acc[b][14], acc[b][15]);
         while (flags) {
           const int v = __ffs(flags) - 1;
           flags &= flags - 1;
-          if (c[b] < kSubCap)
-            cand[sub[b] + c[b]] = make_int2(__float_as_int(stash[w][lane][v]), j0 + tile_key(v, h));
-          ++c[b];
+          if (pos < kCandCap)
+            list[b][pos] = make_int2(__float_as_int(stash[w][lane][v]), j0 + tile_key(v, h));
+          ++pos;
         }
       }
     }
   }
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    const int i = r0 + kT * b + n;
-    if (i < a.L) cnt[((int64_t)i * a.Hkv + g) * kSub + 2 * w + h] = c[b];
-  }
+  __syncthreads();
+  if (tid < kRowsA && r0 + tid < a.L) cnt[(int64_t)(r0 + tid) * a.Hkv + g] = rcnt[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -381,17 +396,8 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
   const int nv = i + 1;
   const int Bq = min(a.B, nv);
   const int nw = (nv + 31) >> 5;
-  int pre[kSub + 1];
-  pre[0] = 0;
-  bool bad = false;
-#pragma unroll
-  for (int k = 0; k < kSub; ++k) {
-    const int ck = cnt[(int64_t)row * kSub + k];
-    bad = bad || ck > kSubCap;
-    pre[k + 1] = pre[k] + min(ck, kSubCap);
-  }
-  const int total = pre[kSub];
-  if (bad || total < Bq) {   // the threshold missed: recompute this row
+  const int total = cnt[row];
+  if (total > kCandCap || total < Bq) {   // the threshold missed: recompute this row
     if (tid == 0) redo[1 + atomicAdd(&redo[0], 1)] = row;
     return;
   }
@@ -400,10 +406,10 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
     sh.kmin = 0xffffffffu;
     sh.kmax = 0u;
   }
-  // candidates e = tid + 256 k, concatenated over the sub-lists
+  // candidates e = tid + 256 k of the row's list
   uint32_t key[kFinPer];
   int32_t jj[kFinPer];
-  const int2* crow = cand + (int64_t)row * kSub * kSubCap;
+  const int2* crow = cand + (int64_t)row * kCandCap;
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int k = 0; k < kFinPer; ++k) {
@@ -411,10 +417,7 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
     key[k] = 0u;
     jj[k] = -1;
     if (e < total) {
-      int s = 0;
-#pragma unroll
-      for (int q = 1; q < kSub; ++q) s += e >= pre[q];
-      const int2 x = crow[(int64_t)s * kSubCap + (e - pre[s])];
+      const int2 x = crow[e];
       if (x.y >= 0 && x.y <= i) {   // always, for lists the candidate kernel wrote
         key[k] = order_key(__int_as_float(x.x));
         jj[k] = x.y;
@@ -527,56 +530,88 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
 }
 
 // ---------------------------------------------------------------------------
-// redo: rows whose candidates did not settle the selection. Workgroup b
-// takes redo entries b, b + gridDim.x, ...: the row's causal scores go to
-// its own scratch row (same MFMA sequence, the query in every column), then
-// the general single-row select runs on them.
+// redo: rows whose candidates did not settle the selection. The first
+// kRedoBlocks listed rows: redo_scores writes row f's causal scores (same
+// MFMA sequence, the query in every column) to scratch row f, then
+// redo_select runs the general single-row select on it. Any further rows
+// (a pathological input) go through redo_loop, which does both per row in
+// one workgroup, kRedoBlocks rows at a time.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void prefill_redo_kernel(PrefillTopkArgs a, const int* redo,
-                                                                float* scratch) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
+// Causal scores of one row into srow; this workgroup takes the tiles
+// t = first + w, first + w + stride, ... (w its wave index).
+__device__ __forceinline__ void redo_row_scores(const PrefillTopkArgs& a, int row, float* srow,
+                                                int first, int stride) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int i = row / a.Hkv, g = row % a.Hkv;
+  bf16x8 qb[kCh];
+  {
+    const uint16_t* qp = qrow(a, g, i);
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) qb[c] = frag(qp, c, h);
+  }
+  for (int t = first + w; t * kT <= i; t += stride) {
+    const int j0 = t * kT;
+    bf16x8 ka[kCh];
+    const uint16_t* kp = krow(a, g, min(j0 + n, a.L - 1));
+#pragma unroll
+    for (int c = 0; c < kCh; ++c) ka[c] = frag(kp, c, h);
+    const f32x16 acc = tile_scores(ka, qb);
+    // every column holds the same 32 scores: lane (n < 16, h) stores value n
+    float x = acc[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) x = (n & 15) == v ? acc[v] : x;
+    const int j = j0 + tile_key(n & 15, h);
+    if (n < 16 && j <= i) srow[j] = x;
+  }
+}
+
+constexpr int kRedoSlices = 16;   // workgroups per redo row (16 waves each)
+
+__global__ __launch_bounds__(1024) void prefill_redo_scores_kernel(PrefillTopkArgs a, const int* redo,
+                                                                   float* scratch) {
+  const int f = blockIdx.x;
+  if (f >= redo[0]) return;
+  redo_row_scores(a, redo[1 + f], scratch + (int64_t)f * a.L, 16 * blockIdx.y, 16 * kRedoSlices);
+}
+
+__device__ __forceinline__ void redo_row_select(const PrefillTopkArgs& a, int row, const float* srow,
+                                                unsigned char* smem_raw) {
+  const int i = row / a.Hkv;
+  SelectArgs s{};
+  s.scores = srow;
+  s.scores_ld = a.L;
+  s.n = i + 1;
+  s.B = a.B;
+  s.cand_block = 1;
+  s.n_positions = i + 1;
+  s.out_idx = a.out_idx;
+  s.out_score = a.out_score;
+  select_row<false, false, false>(s, row, srow, (int64_t)i + 1, smem_raw);
+}
+
+__global__ __launch_bounds__(kThreads) void prefill_redo_select_kernel(PrefillTopkArgs a,
+                                                                       const int* redo,
+                                                                       const float* scratch) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const int f = blockIdx.x;
+  if (f >= redo[0]) return;
+  redo_row_select(a, redo[1 + f], scratch + (int64_t)f * a.L, smem_raw);
+}
+
+__global__ __launch_bounds__(kThreads) void prefill_redo_loop_kernel(PrefillTopkArgs a, const int* redo,
+                                                                     float* scratch) {
+  extern __shared__ __align__(16) unsigned char smem_raw[];
   float* srow = scratch + (int64_t)blockIdx.x * a.L;
   const int count = redo[0];
-  for (int f = blockIdx.x; f < count; f += gridDim.x) {
+  for (int f = kRedoBlocks + blockIdx.x; f < count; f += gridDim.x) {
     const int row = redo[1 + f];
-    const int i = row / a.Hkv, g = row % a.Hkv;
-    bf16x8 qb[kCh];
-    {
-      const uint16_t* qp = qrow(a, g, i);
-#pragma unroll
-      for (int c = 0; c < kCh; ++c) qb[c] = frag(qp, c, h);
-    }
-    for (int t = w; t * kT <= i; t += kWaves) {
-      const int j0 = t * kT;
-      bf16x8 ka[kCh];
-      const uint16_t* kp = krow(a, g, min(j0 + n, a.L - 1));
-#pragma unroll
-      for (int c = 0; c < kCh; ++c) ka[c] = frag(kp, c, h);
-      const f32x16 acc = tile_scores(ka, qb);
-      if (n == 0) {   // column 0 holds the tile's keys (all columns are equal)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int j = j0 + tile_key(v, h);
-          if (j <= i) srow[j] = acc[v];
-        }
-      }
-    }
+    redo_row_scores(a, row, srow, 0, kWaves);
     // the scratch row is complete and visible to the whole workgroup (the
     // acquire also drops lines the previous row left in the vector L1)
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    SelectArgs s{};
-    s.scores = srow;
-    s.scores_ld = a.L;
-    s.n = i + 1;
-    s.B = a.B;
-    s.cand_block = 1;
-    s.n_positions = i + 1;
-    s.out_idx = a.out_idx;
-    s.out_score = a.out_score;
-    select_row<false, false, false>(s, row, srow, (int64_t)i + 1, smem_raw);
+    redo_row_select(a, row, srow, smem_raw);
     __syncthreads();   // done with the scratch row before the next one
   }
 }
@@ -598,13 +633,13 @@ size_t prefill_layout(int L, int Hkv, void* base, PrefillWs* ws) {
   const size_t o_tau = off;
   off = align256(off + rows * sizeof(float));
   const size_t o_cnt = off;
-  off = align256(off + rows * kSub * sizeof(int));
+  off = align256(off + rows * sizeof(int));
   const size_t o_redo = off;
   off = align256(off + (rows + 1) * sizeof(int));
   const size_t o_scr = off;
   off = align256(off + (size_t)kRedoBlocks * L * sizeof(float));
   const size_t o_cand = off;
-  off += rows * kSub * kSubCap * sizeof(int2);
+  off += rows * kCandCap * sizeof(int2);
   if (ws) {
     ws->tau = reinterpret_cast<float*>(p + o_tau);
     ws->cnt = reinterpret_cast<int*>(p + o_cnt);
@@ -637,7 +672,10 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)fin_lds(kSelectLdsMaxSlots));
     if (e != hipSuccess) return e;
-    return hipFuncSetAttribute((const void*)prefill_redo_kernel,
+    e = hipFuncSetAttribute((const void*)prefill_redo_select_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)redo_lds(kSelectLdsMaxSlots));
+    if (e != hipSuccess) return e;
+    return hipFuncSetAttribute((const void*)prefill_redo_loop_kernel,
                                hipFuncAttributeMaxDynamicSharedMemorySize,
                                (int)redo_lds(kSelectLdsMaxSlots));
   }();
@@ -651,7 +689,11 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s) {
                      a, ws.tau, ws.cand, ws.cnt);
   hipLaunchKernelGGL(prefill_final_kernel, dim3(rows), dim3(kFinThreads), fin_lds(a.L), s, a,
                      ws.cand, ws.cnt, ws.redo);
-  hipLaunchKernelGGL(prefill_redo_kernel, dim3(kRedoBlocks), dim3(kThreads), redo_lds(a.L), s, a,
+  hipLaunchKernelGGL(prefill_redo_scores_kernel, dim3(kRedoBlocks, kRedoSlices), dim3(1024), 0, s, a,
+                     ws.redo, ws.scratch);
+  hipLaunchKernelGGL(prefill_redo_select_kernel, dim3(kRedoBlocks), dim3(kThreads), redo_lds(a.L), s,
+                     a, ws.redo, ws.scratch);
+  hipLaunchKernelGGL(prefill_redo_loop_kernel, dim3(kRedoBlocks), dim3(kThreads), redo_lds(a.L), s, a,
                      ws.redo, ws.scratch);
   return hipGetLastError();
 }

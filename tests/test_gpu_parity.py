@@ -752,3 +752,52 @@ def test_prefill_c4_full_size():
         c = min(B, i + 1)
         row = gi[i, 0]
         assert (row[c:] == -1).all() and np.all(np.diff(row[:c]) > 0) and row[c - 1] <= i
+
+
+# --------------------------------------------------------------------------
+# hierarchical coarse-to-fine decode, stage by stage against the oracle
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [131072, 1048576])
+def test_hierarchical_decode(T):
+    case = synth.workload("hier_t1m", T=T)
+    N, Hq, Hkv, d, r, B, blk, Bc = case.N, case.Hq, case.Hkv, case.d, case.r, case.B, case.block, case.B_coarse
+    say("hierarchical decode", T, Hkv, blk, Bc, B)
+    k_idx = oracle.project_keys(case.K, case.W, case.dtype)          # [N, Hkv, T, r]
+    cent = oracle.centroids(k_idx, blk)
+    from indexer_driven_sparse_amd import pipeline
+    Qd, Wd, Kd, Vd = dev(case.Q), dev(case.W), dev(case.K), dev(case.V)
+    kd = dev(k_idx)
+    cd = torch.empty(N, Hkv, T // blk, r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_build_centroids(kd, blk, cd)
+    np.testing.assert_array_equal(host(cd), cent)
+    plan = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc)
+    plan.run(Qd, Wd, kd, cd, Kd, Vd)
+    torch.cuda.synchronize()
+    qi = oracle.query_prep(case.Q, Hkv, case.W)
+    # coarse: centroid scores, kept blocks
+    csc = oracle.scores(qi, cent)
+    cq = decoded(cent)
+    assert_scores_close(host(plan.coarse).reshape(N * Hkv, -1), csc.reshape(N * Hkv, -1),
+                        qi.reshape(N * Hkv, r), cq.reshape(N * Hkv, -1, r))
+    gblocks = host(plan.blocks)
+    rblocks, _, _ = oracle.topk(csc.reshape(N * Hkv, -1), Bc)
+    check_index_sets(gblocks.reshape(N * Hkv, Bc), rblocks, list(csc.reshape(N * Hkv, -1)), Bc)
+    # fine, re-anchored on the GPU's blocks
+    fsc = oracle.scores(qi, k_idx, cand=gblocks, cand_block=blk)
+    ridx, _, _ = oracle.topk(fsc.reshape(N * Hkv, -1), B, cand=gblocks.reshape(N * Hkv, Bc),
+                             cand_block=blk, n_positions=T)
+    gidx = host(plan.idx).reshape(N * Hkv, B)
+    pos_scores = []
+    for row in range(N * Hkv):
+        full = np.full(T, -np.inf)
+        pos = (gblocks.reshape(N * Hkv, Bc)[row][:, None] * blk + np.arange(blk)[None, :]).reshape(-1)
+        full[pos] = fsc.reshape(N * Hkv, -1)[row]
+        pos_scores.append(full)
+        # the final set lies inside the kept blocks
+        assert np.isin(gidx[row] // blk, gblocks.reshape(N * Hkv, Bc)[row]).all()
+    check_index_sets(gidx, ridx, pos_scores, B)
+    # attention, re-anchored on the GPU's index set
+    out, lse = oracle.attention(case.Q, case.K, case.V, host(plan.idx))
+    np.testing.assert_allclose(host(plan.out), out, rtol=0, atol=ATTN_ATOL)
+    np.testing.assert_allclose(host(plan.lse), lse, rtol=0, atol=LSE_ATOL)
