@@ -236,26 +236,30 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K steps, HIP events around every scoring launch on the
-    # stream the kernels run on
+    # timed region: K steps; HIP events on the launch stream bracket the
+    # scoring launch of every 8th step (an event pair between two kernels
+    # costs a few microseconds, so timing every step would slow the step)
     steps = args.steps
-    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    sampled = list(range(0, steps, 8))
+    ev_s = {i: torch.cuda.Event(enable_timing=True) for i in sampled}
+    ev_e = {i: torch.cuda.Event(enable_timing=True) for i in sampled}
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(steps):
         K, V, k_idx = inst[i & 1]
-        ev_s[i].record(stream)
+        if i in ev_s:
+            ev_s[i].record(stream)
         plan.score(Q, W, k_idx)
-        ev_e[i].record(stream)
+        if i in ev_e:
+            ev_e[i].record(stream)
         plan.select()
         plan.attend(Q, K, V)
     end.record(stream)
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / steps
-    score_ms = float(np.mean([ev_s[i].elapsed_time(ev_e[i]) for i in range(steps)]))
+    score_ms = float(np.mean([ev_s[i].elapsed_time(ev_e[i]) for i in sampled]))
 
     keys = N * Hkv * T
     kidx_bytes = keys * r * 2
@@ -264,6 +268,27 @@ def main() -> int:
                                                                  N * Hkv * r * 4)
     steps_per_s = 1000.0 / ms_per_step
     score_gbps = kidx_bytes / (score_ms * 1e-3) / 1e9
+
+    # the same steps replayed from HIP graphs (one per cache instance): the
+    # whole step's launches are submitted at once
+    graphs = []
+    for k in range(2):
+        K_, V_, kidx_ = inst[k]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            plan.run(Q, W, kidx_, K_, V_)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i & 1].replay()
+    torch.cuda.synchronize()
+    ga, gb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ga.record(stream)
+    for i in range(steps):
+        graphs[i & 1].replay()
+    gb.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = ga.elapsed_time(gb) / steps
+    log(f"eager {ms_per_step * 1000:.1f} us/step, graph replay {graph_ms * 1000:.1f} us/step")
 
     stages = None
     if not args.no_stages:
@@ -366,6 +391,8 @@ def main() -> int:
                      "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
                      "avg_launch_us": score_ms * 1000.0,
                      "traffic": traffic},
+        "graph_replay": {"ms_per_step": graph_ms, "steps_per_s": 1000.0 / graph_ms,
+                         "hbm_frac_end_to_end": step_bytes / (graph_ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)},
         "stages": stages,
         "hierarchical": hier,
         "prefill": prefill,

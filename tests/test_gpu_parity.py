@@ -801,3 +801,32 @@ def test_hierarchical_decode(T):
     out, lse = oracle.attention(case.Q, case.K, case.V, host(plan.idx))
     np.testing.assert_allclose(host(plan.out), out, rtol=0, atol=ATTN_ATOL)
     np.testing.assert_allclose(host(plan.lse), lse, rtol=0, atol=LSE_ATOL)
+
+
+# --------------------------------------------------------------------------
+# the decode step captured in a HIP graph: every replay equals eager
+# --------------------------------------------------------------------------
+
+def test_decode_step_graph_replay():
+    from indexer_driven_sparse_amd import pipeline
+    case = synth.workload("decode_t32k_hitters")
+    say("decode graph replay", case.T)
+    Q, W, K, V = dev(case.Q), dev(case.W), dev(case.K), dev(case.V)
+    kd = torch.empty(case.N, case.Hkv, case.T, case.r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_project_keys(K, W, kd)
+    plan = pipeline.DecodePlan(case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B,
+                               with_idx_scores=True)
+    plan.run(Q, W, kd, K, V)           # eager, also warms one-time setup
+    torch.cuda.synchronize()
+    ref = {k: getattr(plan, k).clone() for k in ("idx", "idx_scores", "out", "lse", "q_idx")}
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.run(Q, W, kd, K, V)
+    for rep in range(4):
+        for t in (plan.idx, plan.out, plan.lse):   # eager work between replays
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k, v in ref.items():
+            assert torch.equal(getattr(plan, k), v), (rep, k)
