@@ -19,6 +19,9 @@ Sources it follows (cited per function):
 from .oracle import (  # noqa: F401
     BF16,
     F32,
+    FP8,
+    decode_fp8,
+    round_fp8,
     attention,
     build,
     centroids,

@@ -45,15 +45,54 @@
 #include <omp.h>
 #endif
 
-enum { REF_F32 = 0, REF_BF16 = 1 };
+enum { REF_F32 = 0, REF_BF16 = 1, REF_FP8 = 2 };
 
 /* ------------------------------------------------------------------------ */
 /* Element access                                                           */
 /* ------------------------------------------------------------------------ */
 
+/* OCP 8-bit float E4M3 (the "FN" variant: no infinities): sign, 4
+ * exponent bits with bias 7, 3 mantissa bits. Exponent field 0 holds the
+ * subnormals m * 2^-9; exponent 15 with mantissa 7 is NaN; the largest
+ * finite magnitude is 1.75 * 2^8 = 448. (The pages name FP8 projected-key
+ * caches -- JSSA Fig. 10 -- but not the format; this is the reading.) */
+static double fp8_decode(uint8_t b) {
+  int e = (b >> 3) & 15, m = b & 7;
+  double v;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0) v = ldexp((double)m, -9);
+  else v = ldexp(1.0 + m / 8.0, e - 7);
+  return (b & 0x80) ? -v : v;
+}
+
+/* Round a double to the nearest E4M3 value, ties to even, straight from the
+ * double; beyond the largest finite value the result saturates to +-448
+ * (the format has no infinity); NaN stays NaN. With x = f * 2^e,
+ * 0.5 <= |f| < 1, a normal E4M3 value keeps 4 significant bits, so the
+ * spacing is 2^(e-4); below the smallest normal (2^-6) it stays 2^-9. */
+static uint8_t f64_to_fp8(double x) {
+  if (isnan(x)) return 0x7F;
+  uint8_t sign = signbit(x) ? 0x80 : 0x00;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  int e;
+  frexp(a, &e);
+  if (e < -5) e = -5;
+  double q = ldexp(1.0, e - 4);
+  double y = nearbyint(a / q) * q; /* exact: the quotient is below 2^5 */
+  if (y > 448.0) y = 448.0;
+  if (y < ldexp(1.0, -6)) return sign | (uint8_t)(y / ldexp(1.0, -9)); /* subnormal (or 0) */
+  int E;
+  double f = frexp(y, &E); /* y = f * 2^E exactly, f in [0.5, 1) */
+  int field = E - 1 + 7;
+  int mant = (int)((2.0 * f - 1.0) * 8.0);
+  return sign | (uint8_t)(field << 3) | (uint8_t)mant;
+}
+
 /* Exact decode of one stored element to double. */
 static double elem(const void* p, int dtype, int64_t i) {
   if (dtype == REF_F32) return (double)((const float*)p)[i];
+  if (dtype == REF_FP8) return fp8_decode(((const uint8_t*)p)[i]);
   uint32_t bits = (uint32_t)((const uint16_t*)p)[i] << 16;
   float f;
   memcpy(&f, &bits, sizeof f);
@@ -83,12 +122,16 @@ static uint16_t f64_to_bf16(double x) {
 static void st(void* p, int dtype, int64_t i, double x) {
   if (dtype == REF_F32)
     ((float*)p)[i] = (float)x;
+  else if (dtype == REF_FP8)
+    ((uint8_t*)p)[i] = f64_to_fp8(x);
   else
     ((uint16_t*)p)[i] = f64_to_bf16(x);
 }
 
-/* Exposed so the tests can pin the rounding rule on its own. */
+/* Exposed so the tests can pin the rounding rules on their own. */
 uint16_t lsa_ref_round_bf16(double x) { return f64_to_bf16(x); }
+uint8_t lsa_ref_round_fp8(double x) { return f64_to_fp8(x); }
+double lsa_ref_decode_fp8(uint8_t b) { return fp8_decode(b); }
 
 void lsa_ref_set_threads(int n) {
 #ifdef _OPENMP

@@ -1,7 +1,8 @@
 """numpy front end of the CPU oracle (test infrastructure, never the product).
 
 Arrays: fp32 tensors are ``numpy.float32``; bf16 tensors are ``numpy.uint16``
-holding the raw bf16 bits. Every computation happens in ``lsa_oracle.c`` in
+holding the raw bf16 bits; OCP E4M3 fp8 tensors are ``numpy.uint8`` holding
+the raw bits. Every computation happens in ``lsa_oracle.c`` in
 double precision; results come back as ``numpy.float64`` except where the
 method stores a value (projected keys, centroids), which come back in the
 storage dtype.
@@ -16,6 +17,7 @@ import numpy as np
 
 F32 = 0
 BF16 = 1
+FP8 = 2      # OCP E4M3 ("FN": no infinities, max 448)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "lsa_oracle.c")
@@ -29,6 +31,8 @@ _D = ctypes.c_double
 
 _SIGS = {
     "lsa_ref_round_bf16": (ctypes.c_uint16, [_D]),
+    "lsa_ref_round_fp8": (ctypes.c_uint8, [_D]),
+    "lsa_ref_decode_fp8": (_D, [ctypes.c_uint8]),
     "lsa_ref_set_threads": (None, [_I]),
     "lsa_ref_get_threads": (_I, []),
     "lsa_ref_project_keys": (_I, [_P, _I, _L, _L, _L, _I, _I, _I, _I, _P, _I, _I, _P, _I]),
@@ -80,12 +84,29 @@ def round_bf16(x: float) -> int:
     return int(_get().lsa_ref_round_bf16(float(x)))
 
 
+def round_fp8(x: float) -> int:
+    """Bits of the E4M3 value nearest to the double x (ties to even,
+    saturating at +-448, NaN to 0x7F)."""
+    return int(_get().lsa_ref_round_fp8(float(x)))
+
+
+def decode_fp8(b: int) -> float:
+    """Exact value of the E4M3 bit pattern b."""
+    return float(_get().lsa_ref_decode_fp8(int(b)))
+
+
+_STORE = {F32: np.float32, BF16: np.uint16, FP8: np.uint8}
+
+
 def _dtype_code(a: np.ndarray) -> int:
     if a.dtype == np.float32:
         return F32
     if a.dtype == np.uint16:
         return BF16
-    raise TypeError(f"oracle takes float32 or uint16 (bf16 bits) arrays, got {a.dtype}")
+    if a.dtype == np.uint8:
+        return FP8
+    raise TypeError(f"oracle takes float32, uint16 (bf16 bits) or uint8 (E4M3 bits) arrays, "
+                    f"got {a.dtype}")
 
 
 def _estrides(a: np.ndarray):
@@ -112,7 +133,7 @@ def project_keys(K: np.ndarray, W: np.ndarray, out_dtype: int = BF16) -> np.ndar
     W = np.ascontiguousarray(W, dtype=np.float32)
     r = W.shape[-1]
     s = _estrides(K)
-    out = np.empty((N, Hkv, T, r), dtype=np.float32 if out_dtype == F32 else np.uint16)
+    out = np.empty((N, Hkv, T, r), dtype=_STORE[out_dtype])
     _check(_get().lsa_ref_project_keys(_ptr(K), _dtype_code(K), s[0], s[1], s[2], N, T, Hkv, d,
                                        _ptr(W), int(W.ndim == 3), r, _ptr(out), out_dtype),
            "project_keys")

@@ -514,3 +514,76 @@ def test_generators_are_deterministic():
     c = synth.workload("decode_t32k_hitters", T=2048)
     assert c.K.dtype == np.uint16 and len(c.planted) == 8
     assert all(len(p) == round(0.01 * 2048) for p in c.planted)
+
+
+# --------------------------------------------------------------------------
+# OCP E4M3 fp8 projected-key cache (JSSA Fig. 10 studies FP8 projected caches;
+# the format is the reading: OCP E4M3 "FN", ties to even, saturating)
+# --------------------------------------------------------------------------
+
+def _fp8_table():
+    """Every finite E4M3 value, from torch's independent decoder."""
+    vals = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    return vals
+
+
+def test_fp8_decode_matches_torch_for_all_bit_patterns():
+    ref = _fp8_table()
+    got = np.array([oracle.decode_fp8(b) for b in range(256)])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[fin], ref[fin])
+    assert math.copysign(1.0, oracle.decode_fp8(0x80)) < 0      # -0 keeps its sign
+
+
+def _nearest_even(x, table):
+    """Brute force: the representable value nearest x, ties to the one with
+    an even bit pattern (even mantissa), saturating beyond +-448."""
+    codes = [b for b in range(256) if not math.isnan(table[b])]
+    best = None
+    for b in codes:
+        dlt = abs(table[b] - x)
+        if best is None or dlt < best[0] or (dlt == best[0] and (b & 1) == 0 and (best[1] & 1)):
+            best = (dlt, b)
+    b = best[1]
+    if table[b] == 0.0:                        # the sign of zero follows x
+        b = 0x80 if math.copysign(1.0, x) < 0 else 0x00
+    return b
+
+
+def test_fp8_rounding_is_nearest_even_by_brute_force():
+    table = _fp8_table()
+    fin = sorted(set(v for v in table if not math.isnan(v)))
+    xs = list(fin)
+    xs += [(a + b) / 2 for a, b in zip(fin[:-1], fin[1:])]              # exact ties
+    xs += [(a + b) / 2 + 1e-12 * max(1.0, abs(a)) for a, b in zip(fin[:-1], fin[1:])]
+    xs += [(a + b) / 2 - 1e-12 * max(1.0, abs(a)) for a, b in zip(fin[:-1], fin[1:])]
+    rng = np.random.default_rng(3)
+    xs += list(rng.uniform(-448, 448, 300)) + list(rng.standard_normal(300) * 1e-2)
+    for x in xs:
+        assert oracle.round_fp8(x) == _nearest_even(x, table), x
+
+
+def test_fp8_rounding_matches_torch_and_saturates():
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.standard_normal(4000) * 30, rng.standard_normal(1000) * 1e-3])
+    x = x[np.abs(x) < 440].astype(np.float32)
+    tb = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ob = np.array([oracle.round_fp8(float(v)) for v in x], dtype=np.uint8)
+    np.testing.assert_array_equal(ob, tb)
+    # no infinity in the format: beyond the largest finite value, +-448
+    assert oracle.round_fp8(1e6) == 0x7E and oracle.round_fp8(-464.0001) == 0xFE
+    assert oracle.round_fp8(float("nan")) == 0x7F
+
+
+def test_project_keys_fp8_rounds_the_exact_sum_once():
+    """Integer K and W make every sum exact; the stored value must be the
+    brute-force nearest E4M3 of that sum."""
+    rng = np.random.default_rng(5)
+    K = rng.integers(-3, 4, size=(1, 64, 2, 16)).astype(np.float32)
+    W = (rng.integers(-2, 3, size=(16, 16)) / 4.0).astype(np.float32)
+    out = oracle.project_keys(K, W, oracle.FP8)
+    exact = np.einsum("ntgd,dr->ngtr", K.astype(np.float64), W.astype(np.float64))
+    table = _fp8_table()
+    want = np.vectorize(lambda v: _nearest_even(float(v), table))(exact).astype(np.uint8)
+    np.testing.assert_array_equal(out, want)
