@@ -58,7 +58,13 @@ extern "C" {
 #define LSA_ABI_VERSION 1
 
 /* Storage dtypes. */
-enum { LSA_F32 = 0, LSA_BF16 = 1 };
+/* Storage dtypes. LSA_FP8_E4M3 is the OCP 8-bit float E4M3 ("FN": no
+ * infinities, largest finite 448, NaN 0x7f/0xff), accepted for the
+ * projected-key cache only: decode scoring's k_idx, the output of
+ * lsa_project_keys and the block centroids (JSSA Fig. 10 studies FP8
+ * projected-key caches; the format is a reading). Values are rounded to it
+ * once from the exact fp64 sum, to nearest-even, saturating at +-448. */
+enum { LSA_F32 = 0, LSA_BF16 = 1, LSA_FP8_E4M3 = 2 };
 
 /* Status codes. */
 enum {
@@ -128,7 +134,7 @@ typedef struct lsa_score_desc {
   const float* w;            /* fp32 projection (with q) */
 
   const void* k_idx;         /* projected-key cache, innermost r contiguous */
-  int32_t k_idx_dtype;       /* LSA_F32 / LSA_BF16 */
+  int32_t k_idx_dtype;       /* LSA_F32 / LSA_BF16; decode also LSA_FP8_E4M3 */
   int32_t reserved0;
   int64_t k_stride_seq;      /* decode: between sequences */
   int64_t k_stride_head;     /* between KV heads */
@@ -275,14 +281,14 @@ typedef struct lsa_project_desc {
   int32_t rank;              /* r <= 256 */
   int32_t tok_begin;
   int32_t n_tok;
-  int32_t k_dtype;
+  int32_t k_dtype;           /* LSA_F32 / LSA_BF16 */
   const void* k;             /* K cache, innermost d contiguous */
   int64_t k_stride_seq;
   int64_t k_stride_tok;
   int64_t k_stride_head;
   const float* w;            /* [d,r] or [Hkv,d,r] fp32 */
   int32_t w_per_head;
-  int32_t out_dtype;
+  int32_t out_dtype;         /* LSA_F32 / LSA_BF16 / LSA_FP8_E4M3 */
   void* out;                 /* projected-key cache, innermost r contiguous */
   int64_t out_stride_seq;
   int64_t out_stride_head;
@@ -304,7 +310,7 @@ typedef struct lsa_centroid_desc {
   int32_t n_keys;            /* T */
   int32_t rank;              /* r <= 256 */
   int32_t block;             /* >= 1 */
-  int32_t dtype;             /* of both in and out */
+  int32_t dtype;             /* of both in and out: LSA_F32 / LSA_BF16 / LSA_FP8_E4M3 */
   const void* in;            /* projected-key cache */
   int64_t in_stride_seq;
   int64_t in_stride_head;

@@ -38,6 +38,28 @@ __device__ __forceinline__ uint16_t f64_to_bf16_rne(double x) {
   return sign | (uint16_t)(uint32_t)q;
 }
 
+// OCP 8-bit float E4M3 ("FN": no infinities, largest finite 448, NaN 0x7f
+// and 0xff): round a double to the nearest value, ties to even, straight
+// from the double; beyond 448 the result saturates (the format has no
+// infinity). Normal values keep 3 fraction bits: drop the low 49 of the 52
+// with add-and-carry; below 2^-6 count units of 2^-9 with rint (exact
+// scaling), which also rounds up into the smallest normal (0x08) correctly.
+__device__ __forceinline__ uint8_t f64_to_fp8_e4m3_rne(double x) {
+  const uint64_t u = (uint64_t)__double_as_longlong(x);
+  const uint8_t sign = (uint8_t)((u >> 56) & 0x80u);
+  const uint64_t a = u & 0x7fffffffffffffffull;
+  if (a > 0x7ff0000000000000ull) return 0x7f;               // NaN
+  const int e = (int)(a >> 52) - 1023;
+  if (e < -6) return sign | (uint8_t)(int)rint(fabs(x) * 0x1p9);   // 0..8 units of 2^-9
+  if (e > 8) return sign | 0x7e;                             // saturate (also inf)
+  const uint64_t m = a & 0x000fffffffffffffull;
+  const uint64_t r = m + ((1ull << 48) - 1) + ((m >> 49) & 1);
+  const int e2 = e + (int)(r >> 52);
+  const uint32_t f3 = (uint32_t)((r >> 49) & 7);
+  if (e2 > 8 || (e2 == 8 && f3 == 7)) return sign | 0x7e;
+  return sign | (uint8_t)(((uint32_t)(e2 + 7) << 3) | f3);
+}
+
 // Order-preserving key of an fp32 score: a larger score gives a larger key;
 // -0 maps to +0; every NaN maps to 0, below -inf (0x007fffff).
 __device__ __forceinline__ uint32_t order_key(float s) {

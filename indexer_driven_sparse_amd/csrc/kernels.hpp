@@ -27,15 +27,16 @@ struct ScoreDecodeArgs {
   uint32_t* hint;                    // optional selection hint [rows, hint_ld] (see below)
   int64_t hint_ld;
 };
-int score_chunk_slots(int n_out, int rows);
-// Selection hint of the decode scoring kernel: the row is cut into groups of
-// kScoreHintGroup slots (one wave's loads of one loop step); for each group
-// the hint is the largest 16-bit order-key prefix p (as p << 16) that at
-// least kScoreHintK of the group's keys reach. Groups are numbered in slot
-// order of their first slot, kScoreHintGroupsPerStep per step.
-int score_hint_count(int n_out);       // hint entries per row
-int score_hint_k();                     // keys each hint vouches for
-hipError_t launch_score_decode(const ScoreDecodeArgs& a, int rows, bool k_bf16, hipStream_t s);
+int score_chunk_slots(int n_out, int rows, int k_dt);
+// Selection hint of the decode scoring kernel: the row is cut into groups
+// of slots (one wave's loads of one loop step, 64 slots per group in flight;
+// the count depends on the cache dtype); for each group the hint is the
+// largest 16-bit order-key prefix p (as p << 16) that at least
+// score_hint_k of the group's keys reach. Groups are numbered in slot order
+// of their first slot, four per step.
+int score_hint_count(int n_out, int k_dt);   // hint entries per row
+int score_hint_k(int k_dt);                 // keys each hint vouches for
+hipError_t launch_score_decode(const ScoreDecodeArgs& a, int rows, int k_dt, hipStream_t s);
 
 struct ScorePrefillArgs {
   const void* q_idx;                 // [L, Hkv, r] (contiguous rows of r)
@@ -132,7 +133,8 @@ struct ProjectArgs {
   int64_t os_seq, os_head, os_tok;
   int N, Hkv, d, r, tok_begin, n_tok;
 };
-hipError_t launch_project(const ProjectArgs& a, bool k_bf16, bool out_bf16, hipStream_t s);
+// Storage dtypes: 0 fp32, 1 bf16, 2 OCP E4M3 fp8.
+hipError_t launch_project(const ProjectArgs& a, bool k_bf16, int out_dt, hipStream_t s);
 
 struct CentroidArgs {
   const void* in;
@@ -141,6 +143,6 @@ struct CentroidArgs {
   int64_t os_seq, os_head, os_blk;
   int N, Hkv, T, r, block;
 };
-hipError_t launch_centroids(const CentroidArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_centroids(const CentroidArgs& a, int dt, hipStream_t s);
 
 }  // namespace lsa

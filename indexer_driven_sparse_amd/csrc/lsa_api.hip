@@ -25,7 +25,12 @@ bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool mfma_rows_ok(const lsa_score_desc* d) {
   return al16(d->k_idx) && al16(d->q_idx) && d->k_stride_tok % 8 == 0 && d->k_stride_head % 8 == 0;
 }
-int esize(int dtype) { return dtype == LSA_BF16 ? 2 : dtype == LSA_F32 ? 4 : 0; }
+// Bytes per element of a storage dtype (0: unknown).
+int esize(int dtype) {
+  return dtype == LSA_BF16 ? 2 : dtype == LSA_F32 ? 4 : dtype == LSA_FP8_E4M3 ? 1 : 0;
+}
+// fp32 / bf16 only (queries, K/V, projection inputs, prefill caches).
+int esize_wide(int dtype) { return dtype == LSA_FP8_E4M3 ? 0 : esize(dtype); }
 bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 bool strides16(int es, int64_t a, int64_t b, int64_t c) {
   return a >= 0 && b >= 0 && c >= 0 && (a * es) % 16 == 0 && (b * es) % 16 == 0 && (c * es) % 16 == 0;
@@ -81,7 +86,7 @@ int validate_score(const lsa_score_desc* d, size_t* ws_need) {
     const int64_t rows = (int64_t)d->n_seq * d->n_kv_heads;
     if (rows > 65535) return LSA_ERR_UNSUPPORTED;
     if (d->q) {
-      if (esize(d->q_dtype) == 0) return LSA_ERR_UNSUPPORTED;
+      if (esize_wide(d->q_dtype) == 0) return LSA_ERR_UNSUPPORTED;
       if (d->n_q_heads < d->n_kv_heads || d->n_q_heads % d->n_kv_heads != 0) return LSA_ERR_INVALID_ARG;
       if (d->head_dim < 1 || d->head_dim > 512) return LSA_ERR_UNSUPPORTED;
       if (!d->w) return LSA_ERR_INVALID_ARG;
@@ -96,12 +101,13 @@ int validate_score(const lsa_score_desc* d, size_t* ws_need) {
     if (!d->scores || !al16(d->scores) || d->scores_ld % 4 != 0 || d->scores_ld < score_slots(d))
       return LSA_ERR_INVALID_ARG;
     if (d->topk != 0 || d->out_idx || d->out_score) return LSA_ERR_INVALID_ARG;
-    if (d->hint && (((uintptr_t)d->hint & 3u) || d->hint_ld < lsa::score_hint_count((int)score_slots(d))))
+    if (d->hint && (((uintptr_t)d->hint & 3u) || d->hint_ld < lsa::score_hint_count((int)score_slots(d), d->k_idx_dtype)))
       return LSA_ERR_INVALID_ARG;
     return LSA_OK;
   }
   if (d->mode == LSA_MODE_PREFILL_CAUSAL) {
     if (d->n_seq != 1 || !d->q_idx || d->q || d->cand || d->hint) return LSA_ERR_INVALID_ARG;
+    if (esize_wide(d->k_idx_dtype) == 0) return LSA_ERR_UNSUPPORTED;
     if (!al16(d->q_idx)) return LSA_ERR_INVALID_ARG;
     if (d->topk < 0) return LSA_ERR_INVALID_ARG;
     if (d->topk == 0) {
@@ -156,7 +162,7 @@ int validate_attn(const lsa_attn_desc* d, size_t* ws_need) {
   if (d->n_q_heads % d->n_kv_heads != 0) return LSA_ERR_INVALID_ARG;
   const int G = d->n_q_heads / d->n_kv_heads;
   if (!lsa::attention_supported(G, d->head_dim)) return LSA_ERR_UNSUPPORTED;
-  const int ke = esize(d->kv_dtype);
+  const int ke = esize_wide(d->kv_dtype);
   if (ke == 0 || d->q_dtype != d->kv_dtype) return LSA_ERR_UNSUPPORTED;
   if (!d->q || !d->k || !d->v || !d->idx || !d->out) return LSA_ERR_INVALID_ARG;
   if (!al16(d->k) || !al16(d->v)) return LSA_ERR_INVALID_ARG;
@@ -209,10 +215,10 @@ int lsa_index_score(const lsa_score_desc* d, void* ws, size_t ws_bytes, void* st
     a.scores = d->scores;
     a.scores_ld = d->scores_ld;
     const int rows = d->n_seq * d->n_kv_heads;
-    a.chunk = lsa::score_chunk_slots(a.n_out, rows);
+    a.chunk = lsa::score_chunk_slots(a.n_out, rows, d->k_idx_dtype);
     a.hint = d->hint;
     a.hint_ld = d->hint_ld;
-    e = lsa::launch_score_decode(a, rows, d->k_idx_dtype == LSA_BF16, s);
+    e = lsa::launch_score_decode(a, rows, d->k_idx_dtype, s);
   } else if (d->topk == 0 && d->k_idx_dtype == LSA_BF16 &&
              lsa::prefill_mfma_scores_supported(d->rank) && mfma_rows_ok(d)) {
     lsa::PrefillTopkArgs a{};
@@ -267,8 +273,8 @@ int lsa_score_hint_layout(const lsa_score_desc* d, int32_t* count_per_row, int32
     lsa_score_desc probe = *d;
     probe.hint = nullptr;   // the layout does not depend on the hint buffer itself
     if (validate_score(&probe, &need) == LSA_OK) {
-      c = lsa::score_hint_count((int)score_slots(d));
-      kk = lsa::score_hint_k();
+      c = lsa::score_hint_count((int)score_slots(d), d->k_idx_dtype);
+      kk = lsa::score_hint_k(d->k_idx_dtype);
     }
   }
   if (count_per_row) *count_per_row = c;
@@ -347,7 +353,7 @@ size_t lsa_attention_workspace_bytes(const lsa_attn_desc* d) {
 
 int lsa_project_keys(const lsa_project_desc* d, void* stream) {
   if (!d || d->struct_size != sizeof(lsa_project_desc)) return LSA_ERR_INVALID_ARG;
-  if (esize(d->k_dtype) == 0 || esize(d->out_dtype) == 0) return LSA_ERR_UNSUPPORTED;
+  if (esize_wide(d->k_dtype) == 0 || esize(d->out_dtype) == 0) return LSA_ERR_UNSUPPORTED;
   if (d->n_seq < 1 || d->n_kv_heads < 1 || d->head_dim < 1 || d->tok_begin < 0 || d->n_tok < 0)
     return LSA_ERR_INVALID_ARG;
   if (d->head_dim > 512 || !pow2(d->rank) || d->rank > 256) return LSA_ERR_UNSUPPORTED;
@@ -375,7 +381,7 @@ int lsa_project_keys(const lsa_project_desc* d, void* stream) {
   a.r = d->rank;
   a.tok_begin = d->tok_begin;
   a.n_tok = d->n_tok;
-  hipError_t e = lsa::launch_project(a, d->k_dtype == LSA_BF16, d->out_dtype == LSA_BF16, (hipStream_t)stream);
+  hipError_t e = lsa::launch_project(a, d->k_dtype == LSA_BF16, d->out_dtype, (hipStream_t)stream);
   return e == hipSuccess ? LSA_OK : hip_fail(e);
 }
 
@@ -404,7 +410,7 @@ int lsa_build_centroids(const lsa_centroid_desc* d, void* stream) {
   a.T = d->n_keys;
   a.r = d->rank;
   a.block = d->block;
-  hipError_t e = lsa::launch_centroids(a, d->dtype == LSA_BF16, (hipStream_t)stream);
+  hipError_t e = lsa::launch_centroids(a, d->dtype, (hipStream_t)stream);
   return e == hipSuccess ? LSA_OK : hip_fail(e);
 }
 

@@ -37,8 +37,11 @@ constexpr int kMaxR = 128;
 #ifndef LSA_SCORE_NT
 #define LSA_SCORE_NT 1       // stream the projected-key cache with nontemporal loads
 #endif
-constexpr int kGroupsInFlight = LSA_SCORE_GROUPS;
-constexpr int kHintK = 2 * kGroupsInFlight;   // keys a hint vouches for (1 in 32 of its slots)
+// 64-slot groups per wave in flight (the same for every cache dtype: more
+// groups for fp8 cost more occupancy than they gain)
+constexpr int groups_in_flight(int dt) { return (void)dt, LSA_SCORE_GROUPS; }
+// keys a hint vouches for: 1 in 32 of its group's slots
+constexpr int hint_k(int dt) { return 2 * groups_in_flight(dt); }
 
 __device__ __forceinline__ uint4 load_key16(const char* p) {
 #if LSA_SCORE_NT
@@ -50,9 +53,24 @@ __device__ __forceinline__ uint4 load_key16(const char* p) {
 #endif
 }
 
-template <bool BF16>
+// Storage dtypes of the projected-key cache: 0 fp32, 1 bf16, 2 OCP E4M3.
+template <int DT>
 __device__ __forceinline__ float dot16(const uint4& w, const float* q) {
-  if constexpr (BF16) {
+  if constexpr (DT == 2) {
+    // 16 fp8 values, two per hardware conversion (OCP E4M3 on gfx950)
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(ws[k], false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(ws[k], true);
+      s = k == 0 ? q[0] * lo[0] : fmaf(q[4 * k], lo[0], s);
+      s = fmaf(q[4 * k + 1], lo[1], s);
+      s = fmaf(q[4 * k + 2], hi[0], s);
+      s = fmaf(q[4 * k + 3], hi[1], s);
+    }
+    return s;
+  } else if constexpr (DT == 1) {
     float s = q[0] * bf16_lo(w.x);
     s = fmaf(q[1], bf16_hi(w.x), s);
     s = fmaf(q[2], bf16_lo(w.y), s);
@@ -85,9 +103,11 @@ __device__ __forceinline__ int64_t slot_position(const ScoreDecodeArgs& a, const
   }
 }
 
-template <bool BF16, int LPK, bool CAND>
+template <int DT, int LPK, bool CAND>
 __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecodeArgs a) {
-  constexpr int ESZ = BF16 ? 2 : 4;
+  constexpr int ESZ = DT == 2 ? 1 : DT == 1 ? 2 : 4;
+  constexpr int kGroupsInFlight = groups_in_flight(DT);
+  constexpr int kHintK = hint_k(DT);
   constexpr int E = 16 / ESZ;        // channels per lane
   constexpr int KPI = kWave / LPK;   // keys per wave-wide load
   __shared__ float s_qbar[kMaxD];
@@ -183,7 +203,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecode
       float mine = 0.f;
 #pragma unroll
       for (int it = 0; it < LPK; ++it) {
-        float s = sum_lanes<LPK>(dot16<BF16>(raw[u][it], qv));
+        float s = sum_lanes<LPK>(dot16<DT>(raw[u][it], qv));
         if (!ok[u][it]) s = -INFINITY;
         if (l == it) mine = s;
       }
@@ -238,52 +258,64 @@ __global__ __launch_bounds__(256) void score_prefill_kernel(ScorePrefillArgs a) 
   a.scores[(int64_t)row * a.scores_ld + j] = acc;
 }
 
-template <bool BF16, int LPK>
+template <int DT, int LPK>
 hipError_t launch_decode_lpk(const ScoreDecodeArgs& a, int rows, hipStream_t s) {
   dim3 grid((unsigned)((a.n_out + a.chunk - 1) / a.chunk), (unsigned)rows);
   if (a.cand)
-    hipLaunchKernelGGL((score_decode_kernel<BF16, LPK, true>), grid, dim3(kScoreThreads), 0, s, a);
+    hipLaunchKernelGGL((score_decode_kernel<DT, LPK, true>), grid, dim3(kScoreThreads), 0, s, a);
   else
-    hipLaunchKernelGGL((score_decode_kernel<BF16, LPK, false>), grid, dim3(kScoreThreads), 0, s, a);
+    hipLaunchKernelGGL((score_decode_kernel<DT, LPK, false>), grid, dim3(kScoreThreads), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int score_hint_count(int n_out) {
-  const int step = kGroupsInFlight * 4 * 64;
+int score_hint_count(int n_out, int k_dt) {
+  const int step = groups_in_flight(k_dt) * 4 * 64;
   return (n_out + step - 1) / step * 4;
 }
 
-int score_hint_k() { return kHintK; }
+int score_hint_k(int k_dt) { return hint_k(k_dt); }
 
-int score_chunk_slots(int n_out, int rows) {
-  // about LSA_SCORE_WG_TARGET workgroups; a chunk is a whole number of the
-  // slots one workgroup covers per loop step
-  const int64_t step = (int64_t)kGroupsInFlight * 4 * 64;
-  const int64_t per_row = (LSA_SCORE_WG_TARGET + rows - 1) / rows;
+int score_chunk_slots(int n_out, int rows, int k_dt) {
+  // about LSA_SCORE_WG_TARGET workgroups for a bf16 cache, scaled by the row
+  // bytes so every workgroup streams about as many bytes whatever the dtype;
+  // a chunk is a whole number of the slots one workgroup covers per step
+  const int esz = k_dt == 2 ? 1 : k_dt == 1 ? 2 : 4;
+  const int64_t step = (int64_t)groups_in_flight(k_dt) * 4 * 64;
+  const int64_t target = std::max<int64_t>(256, (int64_t)LSA_SCORE_WG_TARGET * esz / 2);
+  const int64_t per_row = (target + rows - 1) / rows;
   int64_t chunk = (n_out + per_row - 1) / per_row;
   chunk = (chunk + step - 1) / step * step;
   return (int)std::max<int64_t>(step, chunk);
 }
 
-hipError_t launch_score_decode(const ScoreDecodeArgs& a, int rows, bool k_bf16, hipStream_t s) {
-  const int lpk = a.r * (k_bf16 ? 2 : 4) / 16;
-  if (k_bf16) {
+hipError_t launch_score_decode(const ScoreDecodeArgs& a, int rows, int k_dt, hipStream_t s) {
+  const int esz = k_dt == 2 ? 1 : k_dt == 1 ? 2 : 4;
+  const int lpk = a.r * esz / 16;
+  if (k_dt == 2) {
     switch (lpk) {
-      case 1: return launch_decode_lpk<true, 1>(a, rows, s);
-      case 2: return launch_decode_lpk<true, 2>(a, rows, s);
-      case 4: return launch_decode_lpk<true, 4>(a, rows, s);
-      case 8: return launch_decode_lpk<true, 8>(a, rows, s);
-      case 16: return launch_decode_lpk<true, 16>(a, rows, s);
+      case 1: return launch_decode_lpk<2, 1>(a, rows, s);
+      case 2: return launch_decode_lpk<2, 2>(a, rows, s);
+      case 4: return launch_decode_lpk<2, 4>(a, rows, s);
+      case 8: return launch_decode_lpk<2, 8>(a, rows, s);
+      case 16: return launch_decode_lpk<2, 16>(a, rows, s);
+    }
+  } else if (k_dt == 1) {
+    switch (lpk) {
+      case 1: return launch_decode_lpk<1, 1>(a, rows, s);
+      case 2: return launch_decode_lpk<1, 2>(a, rows, s);
+      case 4: return launch_decode_lpk<1, 4>(a, rows, s);
+      case 8: return launch_decode_lpk<1, 8>(a, rows, s);
+      case 16: return launch_decode_lpk<1, 16>(a, rows, s);
     }
   } else {
     switch (lpk) {
-      case 1: return launch_decode_lpk<false, 1>(a, rows, s);
-      case 2: return launch_decode_lpk<false, 2>(a, rows, s);
-      case 4: return launch_decode_lpk<false, 4>(a, rows, s);
-      case 8: return launch_decode_lpk<false, 8>(a, rows, s);
-      case 16: return launch_decode_lpk<false, 16>(a, rows, s);
+      case 1: return launch_decode_lpk<0, 1>(a, rows, s);
+      case 2: return launch_decode_lpk<0, 2>(a, rows, s);
+      case 4: return launch_decode_lpk<0, 4>(a, rows, s);
+      case 8: return launch_decode_lpk<0, 8>(a, rows, s);
+      case 16: return launch_decode_lpk<0, 16>(a, rows, s);
     }
   }
   return hipErrorInvalidValue;

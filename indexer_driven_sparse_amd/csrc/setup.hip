@@ -18,13 +18,22 @@ namespace {
 constexpr int kProjThreads = 256;
 constexpr int kProjTokens = 32;
 
-template <bool OUT_BF16>
+// Storage dtypes: 0 fp32, 1 bf16, 2 OCP E4M3 fp8.
+template <int DT>
 __device__ __forceinline__ void store_rounded(void* out, int64_t i, double x) {
-  if constexpr (OUT_BF16) ((uint16_t*)out)[i] = f64_to_bf16_rne(x);
+  if constexpr (DT == 1) ((uint16_t*)out)[i] = f64_to_bf16_rne(x);
+  else if constexpr (DT == 2) ((uint8_t*)out)[i] = f64_to_fp8_e4m3_rne(x);
   else ((float*)out)[i] = (float)x;
 }
 
-template <bool K_BF16, bool OUT_BF16>
+template <int DT>
+__device__ __forceinline__ double load_stored(const void* p, int64_t i) {
+  if constexpr (DT == 1) return (double)bf16_to_f32(((const uint16_t*)p)[i]);
+  else if constexpr (DT == 2) return (double)__builtin_amdgcn_cvt_f32_fp8(((const uint8_t*)p)[i], 0);
+  else return (double)((const float*)p)[i];
+}
+
+template <bool K_BF16, int OUT_DT>
 __global__ __launch_bounds__(kProjThreads) void project_kernel(ProjectArgs a) {
   extern __shared__ float s_k[];  // [kProjTokens][d]
   const int g = blockIdx.y, n = blockIdx.z;
@@ -44,11 +53,11 @@ __global__ __launch_bounds__(kProjThreads) void project_kernel(ProjectArgs a) {
     const float* kt = s_k + t * a.d;
     for (int c = 0; c < a.d; ++c) acc = fma((double)kt[c], (double)W[(int64_t)c * a.r + j], acc);
     const int64_t o = (int64_t)n * a.os_seq + (int64_t)g * a.os_head + (int64_t)(t0 + t) * a.os_tok + j;
-    store_rounded<OUT_BF16>(a.out, o, acc);
+    store_rounded<OUT_DT>(a.out, o, acc);
   }
 }
 
-template <bool BF16>
+template <int DT>
 __global__ __launch_bounds__(256) void centroid_kernel(CentroidArgs a) {
   const int b = blockIdx.x, g = blockIdx.y, n = blockIdx.z;
   const int t0 = b * a.block, t1 = min(a.T, t0 + a.block);
@@ -56,35 +65,38 @@ __global__ __launch_bounds__(256) void centroid_kernel(CentroidArgs a) {
     double s = 0.0;
     for (int t = t0; t < t1; ++t) {
       const int64_t off = (int64_t)n * a.is_seq + (int64_t)g * a.is_head + (int64_t)t * a.is_tok + j;
-      s += BF16 ? (double)bf16_to_f32(((const uint16_t*)a.in)[off]) : (double)((const float*)a.in)[off];
+      s += load_stored<DT>(a.in, off);
     }
     const int64_t o = (int64_t)n * a.os_seq + (int64_t)g * a.os_head + (int64_t)b * a.os_blk + j;
-    store_rounded<BF16>(a.out, o, s / (double)(t1 - t0));
+    store_rounded<DT>(a.out, o, s / (double)(t1 - t0));
   }
+}
+
+template <bool K_BF16>
+void launch_project_k(const ProjectArgs& a, int out_dt, dim3 grid, size_t lds, hipStream_t s) {
+  if (out_dt == 1) hipLaunchKernelGGL((project_kernel<K_BF16, 1>), grid, dim3(kProjThreads), lds, s, a);
+  else if (out_dt == 2) hipLaunchKernelGGL((project_kernel<K_BF16, 2>), grid, dim3(kProjThreads), lds, s, a);
+  else hipLaunchKernelGGL((project_kernel<K_BF16, 0>), grid, dim3(kProjThreads), lds, s, a);
 }
 
 }  // namespace
 
-hipError_t launch_project(const ProjectArgs& a, bool k_bf16, bool out_bf16, hipStream_t s) {
+hipError_t launch_project(const ProjectArgs& a, bool k_bf16, int out_dt, hipStream_t s) {
   if (a.n_tok <= 0) return hipSuccess;
   dim3 grid((unsigned)((a.n_tok + kProjTokens - 1) / kProjTokens), (unsigned)a.Hkv, (unsigned)a.N);
   const size_t lds = (size_t)kProjTokens * a.d * sizeof(float);
-  if (k_bf16) {
-    if (out_bf16) hipLaunchKernelGGL((project_kernel<true, true>), grid, dim3(kProjThreads), lds, s, a);
-    else hipLaunchKernelGGL((project_kernel<true, false>), grid, dim3(kProjThreads), lds, s, a);
-  } else {
-    if (out_bf16) hipLaunchKernelGGL((project_kernel<false, true>), grid, dim3(kProjThreads), lds, s, a);
-    else hipLaunchKernelGGL((project_kernel<false, false>), grid, dim3(kProjThreads), lds, s, a);
-  }
+  if (k_bf16) launch_project_k<true>(a, out_dt, grid, lds, s);
+  else launch_project_k<false>(a, out_dt, grid, lds, s);
   return hipGetLastError();
 }
 
-hipError_t launch_centroids(const CentroidArgs& a, bool bf16, hipStream_t s) {
+hipError_t launch_centroids(const CentroidArgs& a, int dt, hipStream_t s) {
   const int nb = (a.T + a.block - 1) / a.block;
   if (nb <= 0) return hipSuccess;
   dim3 grid((unsigned)nb, (unsigned)a.Hkv, (unsigned)a.N);
-  if (bf16) hipLaunchKernelGGL((centroid_kernel<true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((centroid_kernel<false>), grid, dim3(256), 0, s, a);
+  if (dt == 1) hipLaunchKernelGGL((centroid_kernel<1>), grid, dim3(256), 0, s, a);
+  else if (dt == 2) hipLaunchKernelGGL((centroid_kernel<2>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((centroid_kernel<0>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

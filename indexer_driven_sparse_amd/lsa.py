@@ -19,6 +19,7 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblsa.so"
 
 F32 = 0
 BF16 = 1
+FP8_E4M3 = 2     # OCP E4M3 (torch.float8_e4m3fn): projected-key caches only
 MODE_DECODE = 0
 MODE_PREFILL_CAUSAL = 1
 
@@ -144,7 +145,9 @@ def _dt(t: torch.Tensor) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise TypeError(f"liblsa takes float32 or bfloat16 tensors, got {t.dtype}")
+    if t.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
+    raise TypeError(f"liblsa takes float32, bfloat16 or float8_e4m3fn tensors, got {t.dtype}")
 
 
 def _ptr(t) -> int | None:

@@ -22,6 +22,8 @@ from . import lsa
 
 
 def _code(dtype) -> int:
+    if dtype == torch.float8_e4m3fn:
+        return lsa.FP8_E4M3
     return lsa.BF16 if dtype == torch.bfloat16 else lsa.F32
 
 
@@ -35,10 +37,13 @@ def _select_ws(scores, B, idx, device, **kw):
 
 
 class DecodePlan:
-    """Buffers for one flat decode step of N sequences with T cached tokens."""
+    """Buffers for one flat decode step of N sequences with T cached tokens
+    (K/V in kv_dtype; the projected-key cache in kidx_dtype, default the
+    same; torch.float8_e4m3fn selects the OCP E4M3 cache)."""
 
     def __init__(self, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int,
-                 device="cuda", kv_dtype=torch.bfloat16, with_idx_scores: bool = False):
+                 device="cuda", kv_dtype=torch.bfloat16, with_idx_scores: bool = False,
+                 kidx_dtype=None):
         self.N, self.Hq, self.Hkv, self.T, self.d, self.r, self.B = N, Hq, Hkv, T, d, r, B
         self.with_idx_scores = with_idx_scores
         f32 = dict(dtype=torch.float32, device=device)
@@ -49,7 +54,8 @@ class DecodePlan:
         self.out = torch.empty(N, Hq, d, **f32)
         self.lse = torch.empty(N, Hq, **f32)
         # selection hint written by the scoring kernel, read by the select
-        self.hint_count, self.hint_k = lsa.score_hint_layout_for(N, Hkv, T, r, _code(kv_dtype))
+        kidx_code = _code(kv_dtype if kidx_dtype is None else kidx_dtype)
+        self.hint_count, self.hint_k = lsa.score_hint_layout_for(N, Hkv, T, r, kidx_code)
         self.hint = torch.empty(N * Hkv, max(1, self.hint_count), dtype=torch.int32, device=device)
         # attention and select workspaces, sized by the library for this shape
         need = lsa.attention_workspace_bytes_for(N, Hq, Hkv, d, B, T, _code(kv_dtype))
@@ -82,7 +88,7 @@ def decode_step(q, w, k_idx, k, v, B, stream=None) -> dict:
     """One flat decode step; returns the step's buffers (device tensors)."""
     N, Hkv, T, r = k_idx.shape
     plan = DecodePlan(N, q.shape[1], Hkv, T, q.shape[2], r, B, device=q.device, kv_dtype=k.dtype,
-                      with_idx_scores=True)
+                      with_idx_scores=True, kidx_dtype=k_idx.dtype)
     plan.run(q, w, k_idx, k, v, stream)
     return {"q_idx": plan.q_idx, "scores": plan.scores, "idx": plan.idx,
             "idx_scores": plan.idx_scores, "out": plan.out, "lse": plan.lse}
@@ -93,7 +99,7 @@ class HierarchicalPlan:
     (sequence, KV head), B_coarse kept blocks of `block` tokens, top-B."""
 
     def __init__(self, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int, block: int,
-                 B_coarse: int, device="cuda", kv_dtype=torch.bfloat16):
+                 B_coarse: int, device="cuda", kv_dtype=torch.bfloat16, kidx_dtype=None):
         self.N, self.Hq, self.Hkv, self.T, self.d, self.r = N, Hq, Hkv, T, d, r
         self.B, self.block, self.B_coarse = B, block, B_coarse
         self.n_blocks = (T + block - 1) // block
@@ -109,7 +115,7 @@ class HierarchicalPlan:
         self.lse = torch.empty(N, Hq, **f32)
         need = lsa.attention_workspace_bytes_for(N, Hq, Hkv, d, B, T, _code(kv_dtype))
         self.attn_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
-        code = _code(kv_dtype)
+        code = _code(kv_dtype if kidx_dtype is None else kidx_dtype)
         self.hc_count, self.hint_k = lsa.score_hint_layout_for(N, Hkv, self.n_blocks, r, code)
         self.hf_count, _ = lsa.score_hint_layout_for(N, Hkv, self.n_fine, r, code)
         self.hint_c = torch.empty(N * Hkv, max(1, self.hc_count), dtype=torch.int32, device=device)

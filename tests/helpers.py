@@ -22,22 +22,36 @@ LSE_ATOL = 2e-3
 
 
 def dev(a: np.ndarray) -> torch.Tensor:
-    """Host array -> device tensor (uint16 arrays are bf16 bits)."""
+    """Host array -> device tensor (uint16 arrays are bf16 bits, uint8
+    arrays OCP E4M3 bits)."""
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    if a.dtype == np.uint8:
+        return torch.from_numpy(np.ascontiguousarray(a)).view(torch.float8_e4m3fn).cuda()
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
 def host(t: torch.Tensor) -> np.ndarray:
-    """Device tensor -> host array (bf16 comes back as uint16 bits)."""
+    """Device tensor -> host array (bf16 comes back as uint16 bits, fp8 as
+    uint8 bits)."""
     t = t.detach().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
+_FP8 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+
+
 def decoded(a: np.ndarray) -> np.ndarray:
-    return synth.bf16_bits_to_f32(a).astype(np.float64) if a.dtype == np.uint16 else a.astype(np.float64)
+    """Stored values as float64 (bf16 bits, E4M3 bits or fp32)."""
+    if a.dtype == np.uint16:
+        return synth.bf16_bits_to_f32(a).astype(np.float64)
+    if a.dtype == np.uint8:
+        return _FP8[a]
+    return a.astype(np.float64)
 
 
 def assert_scores_close(gpu: np.ndarray, ref: np.ndarray, q: np.ndarray, k: np.ndarray) -> None:

@@ -380,16 +380,17 @@ def _compare_step(case, g, ref, rows_sel):
     return diff
 
 
-def _oracle_rows(case, rows_sel):
+def _oracle_rows(case, rows_sel, kidx_dtype=None):
     """Oracle decode step for selected (sequence, KV head) rows: project that
-    head's keys, score, select, attend. Outputs are stacked per selected row."""
+    head's keys (stored in kidx_dtype, default the case's dtype), score,
+    select, attend. Outputs are stacked per selected row."""
     outs = {"idx": [], "scores": [], "out": [], "lse": []}
     for row in rows_sel:
         n, g = divmod(row, case.Hkv)
         K1 = case.K[n:n + 1, :, g:g + 1]
         V1 = case.V[n:n + 1, :, g:g + 1]
         Q1 = case.Q[n:n + 1, g * case.G:(g + 1) * case.G]
-        k1 = oracle.project_keys(K1, case.W, case.dtype)
+        k1 = oracle.project_keys(K1, case.W, case.dtype if kidx_dtype is None else kidx_dtype)
         r = oracle.decode_step(Q1, case.W, k1, K1, V1, case.B)
         outs["idx"].append(r["idx"][0, 0])
         outs["scores"].append(r["scores"][0, 0])
@@ -830,3 +831,63 @@ def test_decode_step_graph_replay():
         torch.cuda.synchronize()
         for k, v in ref.items():
             assert torch.equal(getattr(plan, k), v), (rep, k)
+
+
+# --------------------------------------------------------------------------
+# OCP E4M3 fp8 projected-key cache (JSSA Fig. 10)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,per_head", [(1000, False), (4096, True)])
+def test_project_keys_fp8_bit_exact(T, per_head):
+    rng = np.random.default_rng(T)
+    N, Hkv, d, r = 2, 3, 128, 64
+    K = synth.to_bf16_bits(rng.standard_normal((N, T, Hkv, d)).astype(np.float32) * 3)
+    W = (rng.standard_normal((Hkv, d, r) if per_head else (d, r)) / math.sqrt(d)).astype(np.float32)
+    say("project fp8", T, per_head)
+    ref = oracle.project_keys(K, W, oracle.FP8)
+    out = torch.empty(N, Hkv, T, r, dtype=torch.float8_e4m3fn, device="cuda")
+    lsa.lsa_project_keys(dev(K), dev(W), out)
+    np.testing.assert_array_equal(host(out), ref)
+    # large values saturate at +-448 on both sides
+    Wbig = (W * 400).astype(np.float32)
+    ref2 = oracle.project_keys(K, Wbig, oracle.FP8)
+    lsa.lsa_project_keys(dev(K), dev(Wbig), out)
+    np.testing.assert_array_equal(host(out), ref2)
+    assert (np.abs(decoded(ref2)) == 448).any()
+
+
+def test_centroids_fp8_bit_exact():
+    rng = np.random.default_rng(8)
+    k = oracle.project_keys(synth.to_bf16_bits(rng.standard_normal((2, 1000, 3, 128)).astype(np.float32)),
+                            (rng.standard_normal((128, 64)) / 11.3).astype(np.float32), oracle.FP8)
+    say("centroids fp8")
+    ref = oracle.centroids(k, 64)
+    out = torch.empty(2, 3, ref.shape[2], 64, dtype=torch.float8_e4m3fn, device="cuda")
+    lsa.lsa_build_centroids(dev(k), 64, out)
+    np.testing.assert_array_equal(host(out), ref)
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,T", [(1, 32, 8, 5000), (2, 8, 2, 70001)])
+def test_decode_scores_fp8(N, Hq, Hkv, T):
+    case = synth.make_decode_case(N=N, Hq=Hq, Hkv=Hkv, T=T, d=128, r=64, B=16, dtype=synth.BF16,
+                                  seed=T + 1)
+    k_idx = oracle.project_keys(case.K, case.W, oracle.FP8)
+    say("scores fp8", N, Hq, Hkv, T)
+    q_ref = oracle.query_prep(case.Q, Hkv, case.W)
+    ref = oracle.scores(q_ref, k_idx)
+    sc = torch.empty(N, Hkv, T + (4 - T % 4) % 4, device="cuda")[:, :, :T]
+    lsa.lsa_index_score(dev(k_idx), sc, q=dev(case.Q), w=dev(case.W))
+    assert_scores_close(host(sc).reshape(N * Hkv, T), ref.reshape(N * Hkv, T),
+                        q_ref.reshape(N * Hkv, 64), decoded(k_idx).reshape(N * Hkv, T, 64))
+
+
+@pytest.mark.parametrize("name,over", [("decode_t32k_hitters", {}),
+                                       ("decode_t128k_b2048", {"N": 1, "T": 9000})])
+def test_decode_step_fp8_cache(name, over):
+    case = synth.workload(name, **over)
+    say("decode step fp8 cache", name, over)
+    k_idx = oracle.project_keys(case.K, case.W, oracle.FP8)
+    g = gpu_decode_step(case, dev(k_idx))
+    rows = list(range(case.N * case.Hkv))
+    ref = _oracle_rows(case, rows, kidx_dtype=oracle.FP8)
+    _compare_step(case, g, ref, rows)
