@@ -206,6 +206,87 @@ def fp8_leg(torch, lsa, pipeline, case, inst, Q, W, steps: int, warmup: int) -> 
             "parity_rows_identical": same, "parity_rows": len(rows)}
 
 
+def _time_us(torch, fn, n: int, warm: int = 10) -> float:
+    stream = torch.cuda.current_stream()
+    for i in range(warm):
+        fn(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n * 1000.0
+
+
+def paged_leg(torch, plan, case, inst, Q, n: int = 200) -> dict:
+    """Indexed attention of the headline step through a page-size-1 KV pool
+    (the serving layout of LSA-L's configs): every cached row of every
+    sequence is scattered into one pool, once in sequence order (identity
+    table: the translation's own cost) and once in random order (no DRAM
+    locality left between neighbouring positions). Outputs must equal the
+    unpaged attention bit for bit."""
+    N, Hkv, T, d = case.N, case.Hkv, case.T, case.d
+    K, V, _ = inst[0]
+    unpaged = _time_us(torch, lambda i: plan.attend(Q, inst[i & 1][0], inst[i & 1][1]), n)
+    plan.attend(Q, K, V)
+    ref = plan.out.clone()
+    res = {"workload": "attention of the headline step, K/V read through a slot table from a "
+                       f"pool of {N * T} rows",
+           "unpaged_us": unpaged}
+    g = torch.Generator().manual_seed(5)
+    for kind, rows in (("identity", torch.arange(N * T, dtype=torch.int32)),
+                       ("random", torch.randperm(N * T, generator=g).to(torch.int32))):
+        rows = rows.cuda()
+        pools = []
+        for Ki, Vi, _ in inst:
+            Kp = torch.empty(N * T, Hkv, d, dtype=Ki.dtype, device="cuda")
+            Vp = torch.empty_like(Kp)
+            Kp[rows.long()] = Ki.reshape(N * T, Hkv, d)
+            Vp[rows.long()] = Vi.reshape(N * T, Hkv, d)
+            pools.append((Kp, Vp))
+        table = rows.view(N, T)
+        us = _time_us(torch, lambda i: plan.attend(Q, pools[i & 1][0], pools[i & 1][1],
+                                                   slot_table=table), n)
+        plan.attend(Q, pools[0][0], pools[0][1], slot_table=table)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(plan.out.view(torch.int32), ref.view(torch.int32)))
+        res[f"{kind}_table_us"] = us
+        res[f"{kind}_equals_unpaged"] = same
+        log(f"paged attention ({kind} table): {us:.1f} us vs unpaged {unpaged:.1f} us; "
+            f"bit-identical: {same}")
+        del pools
+    return res
+
+
+def cross_layer_leg(torch, lsa, pipeline, case, inst, Q, W, steps: int,
+                    pattern: str = "FSSS") -> dict:
+    """Cross-layer index reuse on a stack of layers of the headline shape:
+    the first layer of `pattern` runs the indexer and attention, the shared
+    ones attention only on its top-B sets. Every layer has its own caches
+    (distinct memory), timed against the same stack with every layer full."""
+    N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
+    layers = [(K, V, k) for K, V, k in inst]
+    while len(layers) < len(pattern):
+        K, V = to_dev(case.K, torch), to_dev(case.V, torch)
+        k_idx = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+        lsa.lsa_project_keys(K, W, k_idx)
+        layers.append((K, V, k_idx))
+    args = [(Q, W, k, K, V) for K, V, k in layers[:len(pattern)]]
+    res = {"workload": f"{len(pattern)} decode layers of the headline shape, pattern {pattern} "
+                       "(F: own indexer, S: reuses the nearest full layer's top-B)"}
+    for pat in ("F" * len(pattern), pattern):
+        plan = pipeline.CrossLayerPlan(pat, N, Hq, Hkv, T, d, r, B)
+        us = _time_us(torch, lambda i: plan.run(args), max(20, steps // 4))
+        res["all_full_us" if pat.count("S") == 0 else "reuse_us"] = us
+        del plan
+    res["speedup"] = res["all_full_us"] / res["reuse_us"]
+    log(f"cross-layer {pattern}: {res['reuse_us']:.1f} us per {len(pattern)} layers vs "
+        f"{res['all_full_us']:.1f} us all full ({res['speedup']:.2f}x)")
+    return res
+
+
 def hierarchical_leg(torch, lsa, synth, pipeline, steps: int = 200) -> dict:
     """Coarse-to-fine decode at T = 1048576 (1 sequence, GQA 32/8, block 64,
     top-128 blocks, top-2048): warm back-to-back steps (centroid scores,
@@ -255,6 +336,10 @@ def main() -> int:
                     help="skip the same decode step over an OCP E4M3 projected-key cache")
     ap.add_argument("--no-hierarchical", action="store_true",
                     help="skip the coarse-to-fine decode leg (T=1048576)")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the page-size-1 pool attention leg")
+    ap.add_argument("--no-cross-layer", action="store_true",
+                    help="skip the cross-layer index reuse leg")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the causal prefill leg (L=65536 fused indexer + sparse attention)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -357,6 +442,13 @@ def main() -> int:
     fp8 = None
     if not args.no_fp8:
         fp8 = fp8_leg(torch, lsa, pipeline, case, inst, Q, W, steps, args.warmup)
+
+    paged = None if args.no_paged else paged_leg(torch, plan, case, inst, Q)
+    torch.cuda.empty_cache()
+    cross = None
+    if not args.no_cross_layer:
+        cross = cross_layer_leg(torch, lsa, pipeline, case, inst, Q, W, steps)
+        torch.cuda.empty_cache()
 
     stages = None
     if not args.no_stages:
@@ -463,6 +555,8 @@ def main() -> int:
                          "hbm_frac_end_to_end": step_bytes / (graph_ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)},
         "stages": stages,
         "fp8_cache": fp8,
+        "paged_kv": paged,
+        "cross_layer": cross,
         "hierarchical": hier,
         "prefill": prefill,
         "cpu_baseline": cpu,

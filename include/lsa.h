@@ -233,6 +233,20 @@ size_t lsa_select_workspace_bytes(const lsa_select_desc* desc);
  * accumulation; idx entries of one row must be distinct. Long index lists
  * are split across workgroups and merged by log-sum-exp, which needs
  * workspace (lsa_attention_workspace_bytes).
+ *
+ * Paged KV (page size 1, the KV-pool setting of LSA-L's serving configs,
+ * "Their 42x decode speedup never compiled on my GPU", section "What their
+ * numbers claim"): when slot_table is non-NULL,
+ * K and V are one pool of n_pool_rows rows, row p of KV head g at
+ * k + p*kv_stride_tok + g*kv_stride_head (kv_stride_seq is ignored), and
+ * position t of sequence seq lives in pool row slot_table[seq*slot_table_ld
+ * + t] for t < n_keys. A position outside [0, n_keys) or a pool row outside
+ * [0, n_pool_rows) is skipped like the -1 padding, so a stale table entry
+ * never reads outside the pool. The table is read once per selected entry,
+ * where the index list is staged; the K/V loads are the unpaged ones, and
+ * the result equals unpaged attention over K'[seq,t] = pool[table[seq,t]]
+ * bit for bit. slot_table: int32 [n_seq, slot_table_ld], device memory
+ * owned by the caller, slot_table_ld >= n_keys.
  */
 typedef struct lsa_attn_desc {
   uint32_t struct_size;      /* sizeof(lsa_attn_desc) */
@@ -256,6 +270,10 @@ typedef struct lsa_attn_desc {
   int32_t reserved0;
   float* out;                /* fp32 [rows,Hq,d] */
   float* lse;                /* fp32 [rows,Hq] or NULL */
+  const int32_t* slot_table; /* NULL (unpaged) or [n_seq, slot_table_ld] */
+  int64_t slot_table_ld;     /* >= n_keys when slot_table is set */
+  int32_t n_pool_rows;       /* >= 1 when slot_table is set */
+  int32_t reserved1;
 } lsa_attn_desc;
 
 int lsa_indexed_attention(const lsa_attn_desc* desc, void* workspace, size_t workspace_bytes,

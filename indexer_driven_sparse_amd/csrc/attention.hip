@@ -78,7 +78,17 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   const int k0 = split * a.keys_per_split;
   const int nk = max(0, min(a.B - k0, a.keys_per_split));
   const int32_t* irow = a.idx + ((int64_t)row * a.Hkv + g) * a.B + k0;
-  for (int i = tid; i < nk; i += kThreads) s_idx[i] = irow[i];
+  if (a.slot) {
+    // paged pool: translate position -> pool row once, here, so the row loads
+    // below are the unpaged ones
+    const int32_t* tab = a.slot + seq * a.slot_ld;
+    for (int i = tid; i < nk; i += kThreads) {
+      const int32_t t = irow[i];
+      s_idx[i] = (t >= 0 && t < a.T) ? tab[t] : -1;
+    }
+  } else {
+    for (int i = tid; i < nk; i += kThreads) s_idx[i] = irow[i];
+  }
 
   // this lane's query channels for the G heads, pre-scaled into log2 units
   float q[G][CH];
@@ -112,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
     for (int j = 0; j < kKC; ++j) {
       const int i = base + j;
       const int32_t t = i < nk ? s_idx[i] : -1;
-      ok[j] = t >= 0 && t < a.T;
+      ok[j] = t >= 0 && t < a.n_rows_kv;
       // unconditional loads (a skipped entry reads row 0, then is zeroed), so
       // all 2*kKC row requests of the step issue back to back
       const int64_t tc = ok[j] ? t : 0;

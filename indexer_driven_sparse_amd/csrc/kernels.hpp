@@ -117,6 +117,9 @@ struct AttnArgs {
   float* lse;
   float* partial;                    // [rows*Hkv, splits, G, d + 2] when splits > 1
   int splits, keys_per_split;
+  const int32_t* slot;               // paged: [n_seq, slot_ld] position -> pool row
+  int64_t slot_ld;
+  int n_rows_kv;                     // rows addressable per sequence (T, or the pool size)
 };
 void attention_plan(int rows, int Hkv, int G, int d, int B, int* splits, int* keys_per_split);
 size_t attention_workspace(int rows, int Hkv, int G, int d, int B);

@@ -166,7 +166,11 @@ int validate_attn(const lsa_attn_desc* d, size_t* ws_need) {
   if (ke == 0 || d->q_dtype != d->kv_dtype) return LSA_ERR_UNSUPPORTED;
   if (!d->q || !d->k || !d->v || !d->idx || !d->out) return LSA_ERR_INVALID_ARG;
   if (!al16(d->k) || !al16(d->v)) return LSA_ERR_INVALID_ARG;
-  if (!strides16(ke, d->kv_stride_seq, d->kv_stride_tok, d->kv_stride_head)) return LSA_ERR_INVALID_ARG;
+  const bool paged = d->slot_table != nullptr;
+  if (!strides16(ke, paged ? 0 : d->kv_stride_seq, d->kv_stride_tok, d->kv_stride_head))
+    return LSA_ERR_INVALID_ARG;
+  if (paged && (d->n_pool_rows < 1 || d->slot_table_ld < d->n_keys || (uintptr_t)d->slot_table % 4 != 0))
+    return LSA_ERR_INVALID_ARG;
   int sp, kps;
   lsa::attention_plan(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, &sp, &kps);
   if ((int64_t)d->rows * d->n_kv_heads * sp > INT_MAX) return LSA_ERR_UNSUPPORTED;
@@ -324,9 +328,13 @@ int lsa_indexed_attention(const lsa_attn_desc* d, void* ws, size_t ws_bytes, voi
   a.q = d->q;
   a.k = d->k;
   a.v = d->v;
-  a.s_seq = d->kv_stride_seq;
+  const bool paged = d->slot_table != nullptr;
+  a.s_seq = paged ? 0 : d->kv_stride_seq;   // a pool has no per-sequence base
   a.s_tok = d->kv_stride_tok;
   a.s_head = d->kv_stride_head;
+  a.slot = d->slot_table;
+  a.slot_ld = paged ? d->slot_table_ld : 0;
+  a.n_rows_kv = paged ? d->n_pool_rows : d->n_keys;
   a.idx = d->idx;
   a.rows = d->rows;
   a.Hq = d->n_q_heads;

@@ -68,7 +68,9 @@ class AttnDesc(_c.Structure):
                 ("n_kv_heads", _I32), ("head_dim", _I32), ("topk", _I32), ("n_keys", _I32),
                 ("q", _P), ("q_dtype", _I32), ("kv_dtype", _I32), ("k", _P), ("v", _P),
                 ("kv_stride_seq", _I64), ("kv_stride_tok", _I64), ("kv_stride_head", _I64),
-                ("idx", _P), ("scale", _F), ("reserved0", _I32), ("out", _P), ("lse", _P)]
+                ("idx", _P), ("scale", _F), ("reserved0", _I32), ("out", _P), ("lse", _P),
+                ("slot_table", _P), ("slot_table_ld", _I64), ("n_pool_rows", _I32),
+                ("reserved1", _I32)]
 
 
 class ProjectDesc(_c.Structure):
@@ -359,11 +361,24 @@ def lsa_select_workspace_bytes(scores, topk, out_idx, *, n=None, n_valid=None, c
     return int(_lib().lsa_select_workspace_bytes(_c.byref(d)))
 
 
-def _attn_desc(q, k, v, idx, out, lse, mode, scale):
+def _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table=None, n_keys=None):
     rows, Hq, hd = q.shape
-    S, T, Hkv, _ = k.shape
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides")
+    if slot_table is None:
+        S, T, Hkv, _ = k.shape
+        strides = (k.stride(0), k.stride(1), k.stride(2))
+    else:
+        if k.dim() != 3:
+            raise ValueError("a paged K/V pool is [pool_rows, Hkv, d]")
+        if slot_table.dtype != torch.int32 or slot_table.dim() != 2 or slot_table.stride(1) != 1:
+            raise ValueError("slot_table must be int32 [n_seq, ld] with unit inner stride")
+        P, Hkv, _ = k.shape
+        S = slot_table.shape[0]
+        T = slot_table.shape[1] if n_keys is None else int(n_keys)
+        if T > slot_table.shape[1]:
+            raise ValueError("n_keys exceeds the slot table's width")
+        strides = (0, k.stride(0), k.stride(1))
     if mode == MODE_DECODE and S < rows:
         raise ValueError(f"decode reads sequence `row` of k/v: {S} sequences < {rows} rows")
     if not q.is_contiguous() or not idx.is_contiguous() or not out.is_contiguous():
@@ -380,20 +395,27 @@ def _attn_desc(q, k, v, idx, out, lse, mode, scale):
     d.q_dtype = _dt(q)
     d.kv_dtype = _dt(k)
     d.k, d.v = _ptr(k), _ptr(v)
-    d.kv_stride_seq, d.kv_stride_tok, d.kv_stride_head = k.stride(0), k.stride(1), k.stride(2)
+    d.kv_stride_seq, d.kv_stride_tok, d.kv_stride_head = strides
     d.idx = _ptr(idx)
     d.scale = scale
     d.out = _ptr(out)
     d.lse = _ptr(lse)
+    if slot_table is not None:
+        d.slot_table = _ptr(slot_table)
+        d.slot_table_ld = slot_table.stride(0)
+        d.n_pool_rows = k.shape[0]
     return d
 
 
 def lsa_indexed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                           out: torch.Tensor, *, lse=None, mode: int = MODE_DECODE,
-                          scale: float = 0.0, workspace=None, stream=None) -> None:
+                          scale: float = 0.0, workspace=None, stream=None,
+                          slot_table=None, n_keys=None) -> None:
     """q [rows,Hq,d]; k, v [S,T,Hkv,d] viewed through their strides (same for
-    both); idx [rows,Hkv,B] int32; out fp32 [rows,Hq,d]; lse fp32 [rows,Hq]."""
-    d = _attn_desc(q, k, v, idx, out, lse, mode, scale)
+    both); idx [rows,Hkv,B] int32; out fp32 [rows,Hq,d]; lse fp32 [rows,Hq].
+    Paged: k, v are a pool [P,Hkv,d] and slot_table int32 [S, ld] maps
+    (sequence, position) to a pool row; n_keys defaults to the table width."""
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys)
     lib = _lib()
     ws, wsb = _workspace(lib.lsa_attention_workspace_bytes(_c.byref(d)), workspace, q.device)
     _check("lsa_indexed_attention",
@@ -401,8 +423,8 @@ def lsa_indexed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx
 
 
 def lsa_attention_workspace_bytes(q, k, v, idx, out, *, lse=None, mode=MODE_DECODE,
-                                  scale=0.0) -> int:
-    d = _attn_desc(q, k, v, idx, out, lse, mode, scale)
+                                  scale=0.0, slot_table=None, n_keys=None) -> int:
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys)
     return int(_lib().lsa_attention_workspace_bytes(_c.byref(d)))
 
 

@@ -73,14 +73,18 @@ class DecodePlan:
                             hint=self.hint if self.hint_count else None, hint_k=self.hint_k,
                             workspace=self.sel_ws, stream=stream)
 
-    def attend(self, q, k, v, stream=None):
-        lsa.lsa_indexed_attention(q, k, v, self.idx, self.out, lse=self.lse,
-                                  workspace=self.attn_ws, stream=stream)
+    def attend(self, q, k, v, stream=None, *, out=None, lse=None, slot_table=None):
+        """Attention over this plan's selection; out/lse default to the
+        plan's buffers. With slot_table, k and v are a page-size-1 pool."""
+        lsa.lsa_indexed_attention(q, k, v, self.idx, self.out if out is None else out,
+                                  lse=self.lse if lse is None else lse, workspace=self.attn_ws,
+                                  stream=stream, slot_table=slot_table,
+                                  n_keys=self.T if slot_table is not None else None)
 
-    def run(self, q, w, k_idx, k, v, stream=None):
+    def run(self, q, w, k_idx, k, v, stream=None, slot_table=None):
         self.score(q, w, k_idx, stream)
         self.select(stream)
-        self.attend(q, k, v, stream)
+        self.attend(q, k, v, stream, slot_table=slot_table)
         return self
 
 
@@ -92,6 +96,47 @@ def decode_step(q, w, k_idx, k, v, B, stream=None) -> dict:
     plan.run(q, w, k_idx, k, v, stream)
     return {"q_idx": plan.q_idx, "scores": plan.scores, "idx": plan.idx,
             "idx_scores": plan.idx_scores, "out": plan.out, "lse": plan.lse}
+
+
+class CrossLayerPlan:
+    """Cross-layer index reuse over a stack of decode layers (LongCat Sparse
+    Attention abstract, item 2; IndexCache and "You Only Index Once" in the
+    related-paper list): `pattern` names each layer "F" (full: runs its own
+    indexer, a1-a3, then attention) or "S" (shared: attention only, on the
+    top-B sets of the nearest full layer before it). The first layer must be
+    full. Every layer has its own Q, K, V and outputs; only full layers need
+    a projected-key cache and W."""
+
+    def __init__(self, pattern: str, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int,
+                 device="cuda", kv_dtype=torch.bfloat16, kidx_dtype=None):
+        if not pattern or pattern[0] != "F" or set(pattern) - {"F", "S"}:
+            raise ValueError("pattern is a string of 'F'/'S' starting with 'F'")
+        self.pattern = pattern
+        self.source = []                 # layer -> the full layer whose selection it uses
+        self.full = {}                   # full layer -> its DecodePlan
+        for i, c in enumerate(pattern):
+            if c == "F":
+                self.full[i] = DecodePlan(N, Hq, Hkv, T, d, r, B, device=device, kv_dtype=kv_dtype,
+                                          kidx_dtype=kidx_dtype)
+            self.source.append(i if c == "F" else self.source[-1])
+        f32 = dict(dtype=torch.float32, device=device)
+        self.out = [self.full[i].out if c == "F" else torch.empty(N, Hq, d, **f32)
+                    for i, c in enumerate(pattern)]
+        self.lse = [self.full[i].lse if c == "F" else torch.empty(N, Hq, **f32)
+                    for i, c in enumerate(pattern)]
+
+    def layer(self, i, q, w, k_idx, k, v, stream=None):
+        """Layer i's sparse attention; w and k_idx are read by full layers only."""
+        if self.pattern[i] == "F":
+            self.full[i].run(q, w, k_idx, k, v, stream)
+        else:
+            self.full[self.source[i]].attend(q, k, v, stream, out=self.out[i], lse=self.lse[i])
+
+    def run(self, layers, stream=None):
+        """layers: one (q, w, k_idx, k, v) per layer, in order."""
+        for i, (q, w, k_idx, k, v) in enumerate(layers):
+            self.layer(i, q, w, k_idx, k, v, stream)
+        return self
 
 
 class HierarchicalPlan:

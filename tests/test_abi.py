@@ -161,6 +161,27 @@ def test_attention_validation(field, value, code):
     assert lsa._lib().lsa_indexed_attention(ctypes.byref(d), None, 0, None) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(slot_table_ld=131071), INVALID),           # narrower than n_keys
+    (dict(n_pool_rows=0), INVALID),
+    (dict(slot_table=0x6002), INVALID),              # int32 table must be 4-byte aligned
+])
+def test_attention_paged_validation(kw, code):
+    base = dict(slot_table=0x6000, slot_table_ld=131072, n_pool_rows=4 * 131072)
+    base.update(kw)
+    d = _attn_desc(**base)
+    assert lsa._lib().lsa_indexed_attention(ctypes.byref(d), None, 0, None) == code
+
+
+def test_attention_paged_ignores_seq_stride():
+    # a pool has no per-sequence base: a misaligned kv_stride_seq is not looked at
+    lib = lsa._lib()
+    d = _attn_desc(slot_table=0x6000, slot_table_ld=131072, n_pool_rows=8, kv_stride_seq=3)
+    assert lib.lsa_indexed_attention(ctypes.byref(d), None, 0, None) == WORKSPACE
+    u = _attn_desc(kv_stride_seq=3)
+    assert lib.lsa_indexed_attention(ctypes.byref(u), None, 0, None) == INVALID
+
+
 def test_attention_workspace_sizing():
     lib = lsa._lib()
     d = _attn_desc()
@@ -260,3 +281,14 @@ def test_prefill_fused_workspace_and_limits():
 ])
 def test_prefill_fused_validation(field, value, code):
     assert _call_score(_prefill_desc(**{field: value})) == code
+
+
+def test_cross_layer_plan_sources():
+    # host logic only: which full layer's selection each layer attends with
+    from indexer_driven_sparse_amd import pipeline
+    p = pipeline.CrossLayerPlan("FSSFS", 2, 8, 2, 3000, 128, 64, 256, device="cpu")
+    assert p.source == [0, 0, 0, 3, 3] and sorted(p.full) == [0, 3]
+    assert p.out[0] is p.full[0].out and p.out[1] is not p.out[2]
+    for bad in ("", "SF", "FX"):
+        with pytest.raises(ValueError):
+            pipeline.CrossLayerPlan(bad, 2, 8, 2, 3000, 128, 64, 256, device="cpu")

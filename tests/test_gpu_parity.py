@@ -345,6 +345,80 @@ def test_attention_edge_entries():
     np.testing.assert_allclose(lse[fin], rlse[fin], rtol=0, atol=LSE_ATOL)
 
 
+def _paged_pool(K, V, seed, spare=0.25):
+    """Scatter a dense [S,T,Hkv,d] cache into a page-size-1 pool with the
+    rows in random order; unused pool rows hold NaN, so reading one would
+    show. Returns the pool K/V [P,Hkv,d] and the slot table [S,T]."""
+    S, T, Hkv, d = K.shape
+    rng = np.random.default_rng(seed)
+    P = S * T + int(spare * S * T) + 1
+    rows = rng.permutation(P)[: S * T].astype(np.int32)
+    table = rows.reshape(S, T)
+    Kp = np.full((P, Hkv, d), np.nan if K.dtype == np.float32 else 0x7fc0, K.dtype)
+    Vp = Kp.copy()
+    Kp[rows] = K.reshape(S * T, Hkv, d)
+    Vp[rows] = V.reshape(S * T, Hkv, d)
+    return Kp, Vp, table
+
+
+@pytest.mark.parametrize("rows,Hq,Hkv,T,d,B,dtype,prefill", [
+    (4, 32, 8, 16384, 128, 2048, synth.BF16, False),
+    (3, 8, 2, 5000, 128, 300, synth.F32, False),
+    (2, 16, 2, 999, 64, 77, synth.BF16, False),
+    (600, 8, 1, 600, 128, 256, synth.BF16, True),
+])
+def test_attention_paged_equals_unpaged(rows, Hq, Hkv, T, d, B, dtype, prefill):
+    """Page-size-1 pool: the same rows read through the slot table give the
+    unpaged result bit for bit, and the oracle's over the dense cache."""
+    q, K, V, idx = _attn_case(rows, Hq, Hkv, T, d, B, dtype, seed=7 * T + B, prefill=prefill,
+                              fill=0.9)
+    Kp, Vp, table = _paged_pool(K, V, seed=T)
+    say("attention paged", rows, Hq, Hkv, T, d, B, dtype, prefill, "pool", Kp.shape[0])
+    mode = lsa.MODE_PREFILL_CAUSAL if prefill else lsa.MODE_DECODE
+    out_u, lse_u = _run_attention(q, K, V, idx, "tok", prefill)
+    out = torch.full((rows, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((rows, Hq), float("nan"), device="cuda")
+    lsa.lsa_indexed_attention(dev(q), dev(Kp), dev(Vp), dev(idx), out, lse=lse, mode=mode,
+                              slot_table=dev(table))
+    out, lse = host(out), host(lse)
+    assert np.array_equal(out.view(np.uint32), out_u.view(np.uint32))
+    assert np.array_equal(lse.view(np.uint32), lse_u.view(np.uint32))
+    ref, rlse = oracle.attention(q, K, V, idx, prefill=prefill)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=ATTN_ATOL)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=LSE_ATOL)
+
+
+def test_attention_paged_stale_slots_are_skipped():
+    """Table entries outside the pool (negative, or past its end) are skipped
+    like -1 entries of the index list; so are positions >= n_keys, even when
+    the table is wider."""
+    rows, Hq, Hkv, T, d, B = 3, 8, 2, 512, 128, 128
+    q, K, V, idx = _attn_case(rows, Hq, Hkv, T, d, B, synth.BF16, seed=11)
+    Kp, Vp, table = _paged_pool(K, V, seed=12)
+    wide = np.concatenate([table, np.zeros((rows, 64), np.int32)], axis=1)   # ld = T + 64
+    dead = np.zeros((rows, T), bool)
+    dead[0, 5::7] = True
+    dead[1, 3::11] = True
+    wide[:, :T][dead] = np.where(np.arange(dead.sum()) % 2 == 0, -3, Kp.shape[0] + 9)
+    idx[2, 0, :4] = [T, T + 1, T + 2, T + 63]                     # inside the table, past n_keys
+    idx[2, 0] = np.sort(idx[2, 0])
+    expect = idx.copy()
+    for i in range(rows):
+        for g in range(Hkv):
+            e = expect[i, g]
+            bad = (e >= T) | ((e >= 0) & dead[i, np.clip(e, 0, T - 1)])
+            e[bad] = -1
+    say("attention paged stale slots")
+    out = torch.full((rows, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((rows, Hq), float("nan"), device="cuda")
+    lsa.lsa_indexed_attention(dev(q), dev(Kp), dev(Vp), dev(idx), out, lse=lse,
+                              slot_table=dev(wide), n_keys=T)
+    out, lse = host(out), host(lse)
+    ref, rlse = oracle.attention(q, K, V, expect)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=ATTN_ATOL)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=LSE_ATOL)
+
+
 # --------------------------------------------------------------------------
 # whole decode step
 # --------------------------------------------------------------------------
@@ -397,6 +471,43 @@ def _oracle_rows(case, rows_sel, kidx_dtype=None):
         outs["out"].append(r["out"][0])
         outs["lse"].append(r["lse"][0])
     return {k: np.stack(v) for k, v in outs.items()}
+
+
+def test_cross_layer_index_reuse():
+    """Layers "FSSFS": full layers run their own indexer; each shared layer
+    attends over its own Q/K/V with the top-B sets of the nearest full layer
+    before it."""
+    from indexer_driven_sparse_amd import pipeline
+    pattern = "FSSFS"
+    cases = [synth.make_decode_case(N=2, Hq=8, Hkv=2, T=3000, B=256, plant="hitters", seed=40 + i)
+             for i in range(len(pattern))]
+    c0 = cases[0]
+    say("cross-layer reuse", pattern, c0.N, c0.Hq, c0.Hkv, c0.T, c0.B)
+    plan = pipeline.CrossLayerPlan(pattern, c0.N, c0.Hq, c0.Hkv, c0.T, c0.d, c0.r, c0.B)
+    layers = []
+    for i, c in enumerate(cases):
+        W = dev(c.W)
+        K, V = dev(c.K), dev(c.V)
+        k_idx = None
+        if pattern[i] == "F":
+            k_idx = torch.empty(c.N, c.Hkv, c.T, c.r, dtype=torch.bfloat16, device="cuda")
+            lsa.lsa_project_keys(K, W, k_idx)
+        layers.append((dev(c.Q), W, k_idx, K, V))
+    plan.run(layers)
+    torch.cuda.synchronize()
+    rows = list(range(c0.N * c0.Hkv))
+    sets = {}
+    for i, c in enumerate(cases):
+        if pattern[i] == "F":
+            g = {"idx": host(plan.full[i].idx), "out": host(plan.out[i]), "lse": host(plan.lse[i])}
+            _compare_step(c, g, _oracle_rows(c, rows), rows)
+            sets[i] = g["idx"]        # checked above against the oracle's sets
+        else:
+            src = plan.source[i]
+            assert src == max(j for j in sets if j < i)
+            ref, rlse = oracle.attention(c.Q, c.K, c.V, sets[src])
+            np.testing.assert_allclose(host(plan.out[i]), ref, rtol=0, atol=ATTN_ATOL)
+            np.testing.assert_allclose(host(plan.lse[i]), rlse, rtol=0, atol=LSE_ATOL)
 
 
 @pytest.mark.parametrize("name,over", [
