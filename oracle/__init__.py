@@ -15,6 +15,9 @@ Sources it follows (cited per function):
   * LongCat -- "LongCat Sparse Attention: Taming the Lightning via
     Streaming-aware Hierarchical Cross-Layer Indexing", abstract (O(L^2)
     causal indexer scoring; item 3, hierarchical coarse-to-fine indexing).
+  * The LSA-L reproduction page ("Their 42x decode speedup never compiled on
+    my GPU"): the query_block_size option of its sparse-attention call, read
+    as one selection per block of query tokens.
 """
 from .oracle import (  # noqa: F401
     BF16,
@@ -27,6 +30,7 @@ from .oracle import (  # noqa: F401
     centroids,
     decode_step,
     hierarchical_decode_step,
+    prefill_block_topk,
     prefill_scores,
     prefill_topk,
     project_keys,

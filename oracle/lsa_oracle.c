@@ -408,6 +408,73 @@ int lsa_ref_prefill_topk(const void* q_idx, const void* k_idx, int dtype,
   return 0;
 }
 
+/* Query-block-shared prefill selection (the query_block_size option of
+ * LSA-L's sparse-attention call, "Their 42x decode speedup never compiled
+ * on my GPU", section "The failure that decided the verdict"; the page
+ * names the option only, so this is a reading). The L query tokens form
+ * blocks of qb consecutive tokens; block b covers tokens [b*qb,
+ * min(L,(b+1)*qb)). One selection serves the whole block:
+ *   qbar[b,g]  = mean of q_idx[i,g] over the block's tokens, stored in the
+ *                q_idx dtype (the same head-mean reduction the decode
+ *                prep applies to a GQA group, here over tokens);
+ *   S[b,g,j]   = qbar[b,g] . k_idx[j,g] for j < min(L,(b+1)*qb), the keys
+ *                visible to the block's last token;
+ *   then the top-B of that prefix in the selection order.
+ * Each token of the block later attends to the selection's positions
+ * j <= its own (lsa_ref_attention's query_block). out_idx / out_score are
+ * [ceil(L/qb), Hkv, B]. qb = 1 is lsa_ref_prefill_topk. */
+static void block_query(const void* q_idx, int dtype, int L, int Hkv, int r, int qb, int b,
+                        int g, double* q) {
+  int i0 = b * qb, i1 = (b + 1) * qb < L ? (b + 1) * qb : L;
+  for (int c = 0; c < r; ++c) {
+    double s = 0.0;
+    for (int i = i0; i < i1; ++i) s += elem(q_idx, dtype, ((int64_t)i * Hkv + g) * r + c);
+    double mean = s / (double)(i1 - i0);
+    if (dtype == REF_BF16) {
+      uint16_t bits = f64_to_bf16(mean);
+      q[c] = elem(&bits, REF_BF16, 0);
+    } else {
+      q[c] = (double)(float)mean;
+    }
+  }
+}
+
+int lsa_ref_prefill_block_topk(const void* q_idx, const void* k_idx, int dtype, int L, int Hkv,
+                               int r, int qb, int B, int32_t* out_idx, double* out_score,
+                               double* scores, int64_t ld) {
+  if (B < 0 || qb < 1 || (B == 0 && !scores)) return -1;
+  int nbk = (L + qb - 1) / qb;
+  int64_t tasks = (int64_t)nbk * Hkv;
+#pragma omp parallel
+  {
+    cand_t* buf = (cand_t*)malloc(sizeof(cand_t) * (size_t)L);
+    double* sc = (double*)malloc(sizeof(double) * (size_t)L);
+    double* q = (double*)malloc(sizeof(double) * (size_t)r);
+#pragma omp for schedule(dynamic, 1)
+    for (int64_t task = 0; task < tasks; ++task) {
+      int b = (int)(task / Hkv), g = (int)(task % Hkv);
+      block_query(q_idx, dtype, L, Hkv, r, qb, b, g, q);
+      int nv = (b + 1) * qb < L ? (b + 1) * qb : L;
+      for (int t = 0; t < L; ++t) {
+        double acc = -INFINITY;
+        if (t < nv) {
+          acc = 0.0;
+          for (int j = 0; j < r; ++j) acc += q[j] * elem(k_idx, dtype, ((int64_t)t * Hkv + g) * r + j);
+        }
+        sc[t] = acc;
+        if (scores) scores[task * ld + t] = acc;
+      }
+      if (B > 0)
+        select_row(sc, nv, NULL, 1, nv, B, buf, out_idx + task * B,
+                   out_score ? out_score + task * B : NULL);
+    }
+    free(buf);
+    free(sc);
+    free(q);
+  }
+  return 0;
+}
+
 /* Full causal score matrix for small L: scores[(i*Hkv+g)*ld + j] =
  * q_idx[i,g] . k_idx[j,g] for j <= i and -inf for j > i. */
 int lsa_ref_prefill_scores(const void* q_idx, const void* k_idx, int dtype,
@@ -439,17 +506,20 @@ int lsa_ref_prefill_scores(const void* q_idx, const void* k_idx, int dtype,
  *   z_t = scale * q[row,h] . K[seq, t, g]      for t in idx[row, g, :], t >= 0
  *   o   = sum_t softmax(z)_t V[seq, t, g],  lse = log sum_t exp(z_t)
  * mode 0 (decode): row is the sequence; mode 1 (prefill): every row is a
- * query token of sequence 0. q is [rows,Hq,d] contiguous; K and V share the
- * element strides (sequence, token, head), innermost d contiguous; idx is
- * [rows,Hkv,B]; entries outside [0,T) are skipped. scale <= 0 means
+ * query token of sequence 0, and causal: positions after the row's own token
+ * are skipped. q is [rows,Hq,d] contiguous; K and V share the element
+ * strides (sequence, token, head), innermost d contiguous; idx is
+ * [ceil(rows/qb),Hkv,B]: row `row` reads index row row/qb (qb = 1: one
+ * index row per row; qb > 1, prefill only: a selection shared by a block of
+ * qb query tokens); entries outside [0,T) are skipped. scale <= 0 means
  * 1/sqrt(d). */
 int lsa_ref_attention(int mode, int rows, int Hq, int Hkv, int d, int B,
                       const void* q, int q_dtype, const void* Kc,
                       const void* Vc, int kv_dtype, int64_t s_seq,
                       int64_t s_tok, int64_t s_head, int T,
-                      const int32_t* idx, double scale, double* out,
+                      const int32_t* idx, int qb, double scale, double* out,
                       double* lse) {
-  if (Hkv <= 0 || Hq % Hkv != 0) return -1;
+  if (Hkv <= 0 || Hq % Hkv != 0 || qb < 1 || (qb > 1 && mode != 1)) return -1;
   int G = Hq / Hkv;
   if (!(scale > 0.0)) scale = 1.0 / sqrt((double)d);
   int64_t tasks = (int64_t)rows * Hq;
@@ -460,12 +530,13 @@ int lsa_ref_attention(int mode, int rows, int Hq, int Hkv, int d, int B,
     for (int64_t task = 0; task < tasks; ++task) {
       int row = (int)(task / Hq), h = (int)(task % Hq), g = h / G;
       int64_t seq = mode == 0 ? row : 0;
-      const int32_t* I = idx + ((int64_t)row * Hkv + g) * B;
+      int64_t tmax = mode == 1 ? (row < T - 1 ? row : T - 1) : T - 1;  /* last visible position */
+      const int32_t* I = idx + ((int64_t)(row / qb) * Hkv + g) * B;
       int64_t qb = task * d;
       double m = -INFINITY;
       for (int b = 0; b < B; ++b) {
         int64_t t = I[b];
-        if (t < 0 || t >= T) continue;
+        if (t < 0 || t > tmax) continue;
         int64_t kb = seq * s_seq + t * s_tok + (int64_t)g * s_head;
         double acc = 0.0;
         for (int c = 0; c < d; ++c) acc += elem(q, q_dtype, qb + c) * elem(Kc, kv_dtype, kb + c);
@@ -481,7 +552,7 @@ int lsa_ref_attention(int mode, int rows, int Hq, int Hkv, int d, int B,
       double l = 0.0;
       for (int b = 0; b < B; ++b) {
         int64_t t = I[b];
-        if (t < 0 || t >= T) continue;
+        if (t < 0 || t > tmax) continue;
         double p = exp(z[b] - m);
         l += p;
         int64_t vb = seq * s_seq + t * s_tok + (int64_t)g * s_head;

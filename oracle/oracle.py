@@ -42,7 +42,9 @@ _SIGS = {
     "lsa_ref_topk": (_I, [_P, _I, _I, _L, _P, _I, _P, _I, _L, _I, _I, _P, _P, _P]),
     "lsa_ref_prefill_topk": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _P, _P]),
     "lsa_ref_prefill_scores": (_I, [_P, _P, _I, _I, _I, _I, _P, _L]),
-    "lsa_ref_attention": (_I, [_I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _I, _L, _L, _L, _I, _P, _D, _P, _P]),
+    "lsa_ref_prefill_block_topk": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _L]),
+    "lsa_ref_attention": (_I, [_I, _I, _I, _I, _I, _I, _P, _I, _P, _P, _I, _L, _L, _L, _I, _P, _I,
+                               _D, _P, _P]),
 }
 
 
@@ -233,6 +235,30 @@ def prefill_topk(q_idx: np.ndarray, k_idx: np.ndarray, B: int, row_begin: int = 
     return idx, osc
 
 
+def prefill_block_topk(q_idx: np.ndarray, k_idx: np.ndarray, B: int, query_block: int,
+                       want_scores: bool = False):
+    """Query-block-shared prefill selection (the query_block_size option
+    named on the LSA-L reproduction page; its meaning is a reading): tokens
+    form blocks of query_block; block b scores k_idx[j] for j <
+    min(L,(b+1)*query_block) with the block's mean q_idx, stored in the
+    q_idx dtype, and keeps the top-B (B = 0: scores only). Returns (idx
+    int32 [nb,Hkv,B], score float64 [nb,Hkv,B], scores float64 [nb,Hkv,L]
+    with -inf past the block's prefix, or None)."""
+    q_idx = np.ascontiguousarray(q_idx)
+    k_idx = np.ascontiguousarray(k_idx)
+    if q_idx.dtype != k_idx.dtype:
+        raise TypeError("q_idx and k_idx must share a dtype")
+    L, Hkv, r = k_idx.shape
+    nb = (L + query_block - 1) // query_block
+    idx = np.empty((nb, Hkv, max(B, 1)), dtype=np.int32)
+    osc = np.empty((nb, Hkv, max(B, 1)), dtype=np.float64)
+    sc = np.empty((nb, Hkv, L), dtype=np.float64) if (want_scores or B == 0) else None
+    _check(_get().lsa_ref_prefill_block_topk(_ptr(q_idx), _ptr(k_idx), _dtype_code(k_idx), L, Hkv,
+                                             r, int(query_block), int(B), _ptr(idx), _ptr(osc),
+                                             _ptr(sc), L), "prefill_block_topk")
+    return idx[..., :B], osc[..., :B], sc
+
+
 def prefill_scores(q_idx: np.ndarray, k_idx: np.ndarray) -> np.ndarray:
     """Full causal indexer score matrix for small L: [L,Hkv,L] float64, -inf
     above the diagonal."""
@@ -246,13 +272,15 @@ def prefill_scores(q_idx: np.ndarray, k_idx: np.ndarray) -> np.ndarray:
 
 
 def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
-              prefill: bool = False, scale: float | None = None):
+              prefill: bool = False, scale: float | None = None, query_block: int = 1):
     """Indexed attention (JSSA Fig. 1 and Key contributions): each query head
     attends over its KV head's selected positions, read from the standard
     GQA cache. q [rows,Hq,d]; K, V [S,T,Hkv,d] with identical strides (d
-    contiguous); idx [rows,Hkv,B] int32, -1 (or anything outside [0,T))
-    skipped. Decode: row n reads sequence n. Prefill: every row reads
-    sequence 0. Returns (out float64 [rows,Hq,d], lse float64 [rows,Hq])."""
+    contiguous); idx [ceil(rows/query_block),Hkv,B] int32, -1 (or anything
+    outside [0,T)) skipped. Decode: row n reads sequence n. Prefill: every
+    row reads sequence 0, causally (positions after the row are skipped),
+    and row i uses index row i // query_block. Returns (out float64
+    [rows,Hq,d], lse float64 [rows,Hq])."""
     q = np.ascontiguousarray(q)
     rows, Hq, d = q.shape
     S, T, Hkv, _ = K.shape
@@ -265,7 +293,7 @@ def attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx: np.ndarray,
     lse = np.empty((rows, Hq), dtype=np.float64)
     _check(_get().lsa_ref_attention(1 if prefill else 0, rows, Hq, Hkv, d, B, _ptr(q),
                                     _dtype_code(q), _ptr(K), _ptr(V), _dtype_code(K),
-                                    s[0], s[1], s[2], T, _ptr(idx),
+                                    s[0], s[1], s[2], T, _ptr(idx), int(query_block),
                                     0.0 if scale is None else float(scale),
                                     _ptr(out), _ptr(lse)), "attention")
     return out, lse

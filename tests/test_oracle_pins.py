@@ -483,6 +483,84 @@ def test_prefill_rows_are_prefix_decodes():
     np.testing.assert_array_equal(part, idx[100:130])
 
 
+@pytest.mark.parametrize("L,qb,B", [(300, 16, 20), (300, 64, 40), (97, 8, 5)])
+def test_block_selection_with_equal_queries_is_the_last_tokens_selection(L, qb, B):
+    """When every token of a block has the same q_idx, the block mean is that
+    row exactly, so the block's selection and scores are those of the
+    block's last token (whose prefix is exactly the keys the block sees);
+    the last block is partial when qb does not divide L."""
+    case = synth.make_prefill_case(L=L, Hq=4, Hkv=2, d=32, r=16, B=B, seed=21)
+    nb = (L + qb - 1) // qb
+    rep = np.repeat(case.q_idx[::qb][:nb], qb, axis=0)[:L]          # block b: token b*qb's row
+    idx, isc, sc = oracle.prefill_block_topk(rep, case.k_idx, B, qb, want_scores=True)
+    ref, rsc = oracle.prefill_topk(rep, case.k_idx, B)
+    last = np.minimum(np.arange(nb) * qb + qb, L) - 1
+    np.testing.assert_array_equal(idx, ref[last])
+    np.testing.assert_array_equal(isc, rsc[last])
+    for b in range(nb):
+        assert np.isneginf(sc[b, :, last[b] + 1:]).all() and np.isfinite(sc[b, :, :last[b] + 1]).all()
+
+
+def test_block_selection_of_block_size_one_is_the_per_token_selection():
+    case = synth.make_prefill_case(L=200, Hq=4, Hkv=2, d=32, r=16, B=16, seed=22)
+    idx, isc, _ = oracle.prefill_block_topk(case.q_idx, case.k_idx, case.B, 1)
+    ref, rsc = oracle.prefill_topk(case.q_idx, case.k_idx, case.B)
+    np.testing.assert_array_equal(idx, ref)
+    np.testing.assert_array_equal(isc, rsc)
+
+
+def test_block_selection_of_one_whole_block_scores_the_mean_query():
+    """A single block holding every token scores all L keys with the mean
+    of all query rows (rounded once to bf16): the decode-style scoring and
+    top-B of that one query; a sum instead of a mean, or a wrong divisor for
+    the partial block, changes the scores."""
+    L, Hkv, r, B = 150, 2, 16, 12
+    case = synth.make_prefill_case(L=L, Hq=4, Hkv=Hkv, d=32, r=r, B=B, seed=23)
+    for qb in (L, 256):
+        idx, isc, sc = oracle.prefill_block_topk(case.q_idx, case.k_idx, B, qb, want_scores=True)
+        assert idx.shape == (1, Hkv, B)
+        mean = dec(case.q_idx).mean(axis=0)                                   # [Hkv, r]
+        qbar = np.array([[oracle.round_bf16(float(x)) for x in row] for row in mean], np.uint16)
+        want = oracle.scores(dec(qbar)[None], case.k_idx.transpose(1, 0, 2)[None])[0]
+        np.testing.assert_array_equal(sc[0], want)
+        ri, rs, _ = oracle.topk(want, B)
+        np.testing.assert_array_equal(idx[0], ri)
+        np.testing.assert_array_equal(isc[0], rs)
+
+
+def test_attention_prefill_is_causal_and_query_block_maps_rows():
+    """Prefill attention skips positions after the row's own token, so a
+    selection shared by a block of tokens equals, row by row, that selection
+    with the row's future positions removed; decode rows are not masked."""
+    rng = np.random.default_rng(24)
+    L, Hq, Hkv, d, B, qb = 40, 4, 2, 8, 6, 8
+    q = bits(rng.standard_normal((L, Hq, d)))
+    K = bits(rng.standard_normal((1, L, Hkv, d)))
+    V = bits(rng.standard_normal((1, L, Hkv, d)))
+    nb = L // qb
+    blk = np.full((nb, Hkv, B), -1, np.int32)
+    for b in range(nb):
+        for g in range(Hkv):
+            hi = (b + 1) * qb
+            blk[b, g, :B] = np.sort(rng.choice(hi, B, replace=False))
+    out, lse = oracle.attention(q, K, V, blk, prefill=True, query_block=qb)
+    per = np.repeat(blk, qb, axis=0)
+    per = np.where(per <= np.arange(L)[:, None, None], per, -1).astype(np.int32)
+    out2, lse2 = oracle.attention(q, K, V, per, prefill=True)
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+    # the removal matters: some row had a future position in its block's set
+    assert (per != np.repeat(blk, qb, axis=0)).any()
+    # decode rows: no causal mask (sequence n reads all its cached tokens)
+    Kn = np.repeat(K, 2, axis=0)
+    Vn = np.repeat(V, 2, axis=0)
+    fut = np.full((2, Hkv, 1), L - 1, np.int32)
+    od, ld = oracle.attention(q[:2], Kn, Vn, fut)
+    assert np.isfinite(ld).all()
+    with pytest.raises(ValueError):
+        oracle.attention(q[:2], Kn, Vn, fut, query_block=2)
+
+
 # --------------------------------------------------------------------------
 # whole decode step: invariants
 # --------------------------------------------------------------------------
