@@ -133,6 +133,20 @@ def prefill_leg(torch, lsa, synth, runs: int = 5) -> dict:
         ok += int(len(rsel) == int((gv >= 0).sum()) and np.all(np.abs(s[sym] - s_b) <= tol))
     log(f"prefill: indexer {t_idx:.1f} us, attention {t_att:.1f} us, oracle rows {same}/{len(rows)} "
         f"identical, {ok}/{len(rows)} within the near-tie tolerance")
+    # the same inputs with one selection per block of qb tokens
+    del idx, osc, aws
+    torch.cuda.empty_cache()
+    from indexer_driven_sparse_amd import pipeline
+    qb = 64
+    plan = pipeline.PrefillPlan(L, case.Hq, Hkv, case.d, r, B, query_block=qb)
+    t_bidx = timed(lambda: plan.index(qd, kd))
+    t_batt = timed(lambda: plan.attend(Q, K, V))
+    log(f"prefill, one selection per {qb} tokens: indexer {t_bidx:.1f} us, attention {t_batt:.1f} us")
+    block = {"query_block": qb, "indexer_us": t_bidx, "attention_us": t_batt,
+             "index_bytes": (L // qb) * Hkv * B * 4,
+             "indexer_flop": 2.0 * r * sum(min(L, (b + 1) * qb) for b in range(L // qb)) * Hkv}
+    del plan
+    torch.cuda.empty_cache()
     return {"workload": "causal prefill, L=65536, 1 KV head / 8 query heads, d=128, r=64, "
                         "top-2048 per row, bf16, sinusoidal position component",
             "indexer_us": t_idx, "indexer_causal_pairs": pairs, "indexer_flop": flop,
@@ -141,7 +155,7 @@ def prefill_leg(torch, lsa, synth, runs: int = 5) -> dict:
             "attention_us": t_att, "attention_selected_pairs": sel_pairs,
             "attention_tflops": sel_pairs * 4.0 * case.d / (t_att * 1e-6) / 1e12,
             "parity_rows_identical": same, "parity_rows": len(rows),
-            "parity_pass": ok == len(rows)}
+            "parity_pass": ok == len(rows), "block_shared": block}
 
 
 def fp8_leg(torch, lsa, pipeline, case, inst, Q, W, steps: int, warmup: int) -> dict:

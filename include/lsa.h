@@ -108,6 +108,20 @@ enum { LSA_MODE_DECODE = 0, LSA_MODE_PREFILL_CAUSAL = 1 };
  *   not NULL) the matching scores. Needs workspace
  *   (lsa_score_workspace_bytes).
  *
+ * Query-block-shared prefill (query_block = qb > 1; the query_block_size
+ *   option of LSA-L's sparse-attention call, "Their 42x decode speedup
+ *   never compiled on my GPU", section "The failure that decided the
+ *   verdict"; its meaning there is not spelled out, this is the reading):
+ *   tokens form nb = ceil(L/qb) blocks. Block b's query is the mean of
+ *   q_idx over its tokens [b*qb, min(L,(b+1)*qb)), taken exactly and
+ *   rounded once to bf16 (nearest-even); it scores keys j < min(L,(b+1)*qb)
+ *   (those its last token sees). Rows are (block, KV head), row b*Hkv + g.
+ *   topk == 0: scores [nb*Hkv, scores_ld], -inf past the block's keys.
+ *   topk = B > 0: out_idx [nb,Hkv,B] (+ out_score) is lsa_topk_select over
+ *   those rows; scores, if given, also receive the block scores, else they
+ *   live in the workspace. bf16, r = 64 only. Attention then shares each
+ *   block's set among its tokens (lsa_attn_desc.query_block).
+ *
  * Accumulation is fp32 over exact products of the stored values.
  *
  * Selection hint (decode, optional): with `hint` set, the call also writes
@@ -149,7 +163,7 @@ typedef struct lsa_score_desc {
   int64_t scores_ld;
 
   int32_t topk;              /* prefill fused selection budget B, or 0 */
-  int32_t reserved1;
+  int32_t query_block;       /* prefill: 0 or 1 per token; qb > 1 one selection per qb tokens */
   int32_t* out_idx;          /* prefill fused: [L,Hkv,B] ascending, -1 padded */
   float* out_score;          /* prefill fused: [L,Hkv,B] or NULL */
 
@@ -203,7 +217,7 @@ typedef struct lsa_select_desc {
   const int32_t* cand;       /* [rows, cand_ld] or NULL */
   int64_t cand_ld;
   int32_t n_positions;       /* with cand: tokens >= n_positions are invalid */
-  int32_t reserved0;
+  int32_t causal_block;      /* with causal_group k: row r has (r/k + 1) * max(1, causal_block) valid */
   int32_t* out_idx;          /* [rows, B] */
   float* out_score;          /* [rows, B] or NULL */
   int32_t* out_count;        /* [rows] or NULL */
@@ -227,7 +241,10 @@ size_t lsa_select_workspace_bytes(const lsa_select_desc* desc);
  *     lse[row,h]   = log sum_t exp(z_t)
  * Entries outside [0, n_keys) (e.g. the -1 padding) are skipped; an empty
  * set gives out = 0 and lse = -inf. Decode: seq = row. Prefill: seq = 0 for
- * every row. K and V rows are read in place through their strides (the
+ * every row, and causal: entries after the row's own token are skipped.
+ * Prefill with query_block = qb > 1: idx is [ceil(rows/qb), Hkv, B] and
+ * row i reads index row i / qb (a selection shared by qb tokens), each
+ * token still masked causally. K and V rows are read in place through their strides (the
  * standard [N,T,Hkv,d] cache, or [N,Hkv,T,d]); nothing is gathered into a
  * copy (JSSA Key contributions; Fig. 6). Online softmax with fp32
  * accumulation; idx entries of one row must be distinct. Long index lists
@@ -267,7 +284,7 @@ typedef struct lsa_attn_desc {
   int64_t kv_stride_head;
   const int32_t* idx;        /* [rows, Hkv, B] int32 */
   float scale;               /* <= 0: 1/sqrt(d) */
-  int32_t reserved0;
+  int32_t query_block;       /* prefill: 0/1, or qb > 1: row i reads idx row i / qb */
   float* out;                /* fp32 [rows,Hq,d] */
   float* lse;                /* fp32 [rows,Hq] or NULL */
   const int32_t* slot_table; /* NULL (unpaged) or [n_seq, slot_table_ld] */

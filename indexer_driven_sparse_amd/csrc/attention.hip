@@ -77,17 +77,24 @@ __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   // stage this split's indices
   const int k0 = split * a.keys_per_split;
   const int nk = max(0, min(a.B - k0, a.keys_per_split));
-  const int32_t* irow = a.idx + ((int64_t)row * a.Hkv + g) * a.B + k0;
+  // prefill: a selection may be shared by qblk consecutive query tokens,
+  // and each token reads only positions up to its own (causal)
+  const int64_t isel = a.prefill ? row / a.qblk : row;
+  const int32_t* irow = a.idx + (isel * a.Hkv + g) * a.B + k0;
+  const int tlim = a.prefill ? min(a.T, row + 1) : a.T;   // readable positions [0, tlim)
   if (a.slot) {
     // paged pool: translate position -> pool row once, here, so the row loads
     // below are the unpaged ones
     const int32_t* tab = a.slot + seq * a.slot_ld;
     for (int i = tid; i < nk; i += kThreads) {
       const int32_t t = irow[i];
-      s_idx[i] = (t >= 0 && t < a.T) ? tab[t] : -1;
+      s_idx[i] = (t >= 0 && t < tlim) ? tab[t] : -1;
     }
   } else {
-    for (int i = tid; i < nk; i += kThreads) s_idx[i] = irow[i];
+    for (int i = tid; i < nk; i += kThreads) {
+      const int32_t t = irow[i];
+      s_idx[i] = t < tlim ? t : -1;
+    }
   }
 
   // this lane's query channels for the G heads, pre-scaled into log2 units

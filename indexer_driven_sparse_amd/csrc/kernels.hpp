@@ -50,10 +50,12 @@ hipError_t launch_score_prefill(const ScorePrefillArgs& a, bool bf16, hipStream_
 
 // Fused causal prefill indexer + exact top-B.
 struct PrefillTopkArgs {
-  const uint16_t* q_idx;             // [L, Hkv, r] bf16
+  const uint16_t* q_idx;             // [Lq, Hkv, r] bf16
   const uint16_t* k_idx;
   int64_t ks_head, ks_tok;
   int L, Hkv, r, B;
+  int Lq, qblk;                      // query rows and tokens per row: row i sees keys
+                                     // j < min(L, (i+1)*qblk); the fused path needs Lq = L, qblk = 1
   int32_t* out_idx;                  // [L, Hkv, B]
   float* out_score;                  // or nullptr
   void* ws;
@@ -68,6 +70,10 @@ bool prefill_topk_supported(int L, int r, int B);
 bool prefill_mfma_scores_supported(int r);
 hipError_t launch_prefill_scores_mfma(const PrefillTopkArgs& a, float* scores, int64_t ld,
                                       hipStream_t s);
+// Block queries for query-block-shared prefill: out[b,g,:] = bf16 of the
+// exact mean of q_idx[i,g,:] over the block's tokens (r = 64).
+hipError_t launch_block_queries(const uint16_t* q_idx, int L, int Hkv, int qblk, uint16_t* out,
+                                hipStream_t s);
 
 // ----- exact top-B selection -----------------------------------------------
 struct SelectArgs {
@@ -76,6 +82,7 @@ struct SelectArgs {
   int n, B;
   const int32_t* n_valid;
   int causal_group;
+  int causal_block;                  // with causal_group: (row/group + 1) * causal_block valid
   const int32_t* cand;
   int64_t cand_ld;
   int cand_block, n_positions;
@@ -117,6 +124,7 @@ struct AttnArgs {
   float* lse;
   float* partial;                    // [rows*Hkv, splits, G, d + 2] when splits > 1
   int splits, keys_per_split;
+  int qblk;                          // prefill: row i reads index row i / qblk
   const int32_t* slot;               // paged: [n_seq, slot_ld] position -> pool row
   int64_t slot_ld;
   int n_rows_kv;                     // rows addressable per sequence (T, or the pool size)

@@ -65,6 +65,36 @@ int check_device() {
 // ---------------------------------------------------------------------------
 // lsa_index_score
 // ---------------------------------------------------------------------------
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Query-block-shared prefill: workspace = block queries | block scores (when
+// the caller gives none) | the select's own workspace.
+struct BlockWs {
+  uint16_t* qbar;
+  float* scores;
+  int64_t ld;
+  void* sel;
+};
+size_t block_prefill_layout(const lsa_score_desc* d, void* base, BlockWs* w) {
+  const int qb = d->query_block;
+  const int nb = (d->n_keys + qb - 1) / qb;
+  const int rows = nb * d->n_kv_heads;
+  size_t off = align256((size_t)rows * d->rank * 2);
+  const int64_t ld = d->scores ? d->scores_ld : ((int64_t)d->n_keys + 3) / 4 * 4;
+  const size_t sc_off = off;
+  if (!d->scores) off += align256((size_t)rows * ld * sizeof(float));
+  const size_t sel_off = off;
+  if (d->topk > 0) off += lsa::select_workspace(rows, d->n_keys, d->topk, false);
+  if (w) {
+    char* b = (char*)base;
+    w->qbar = (uint16_t*)b;
+    w->scores = d->scores ? d->scores : (float*)(b + sc_off);
+    w->ld = ld;
+    w->sel = b + sel_off;
+  }
+  return off;
+}
+
 int64_t score_slots(const lsa_score_desc* d) {
   if (d->mode == LSA_MODE_DECODE && d->cand) return (int64_t)d->n_cand * d->cand_block;
   return d->n_keys;
@@ -100,7 +130,7 @@ int validate_score(const lsa_score_desc* d, size_t* ws_need) {
     }
     if (!d->scores || !al16(d->scores) || d->scores_ld % 4 != 0 || d->scores_ld < score_slots(d))
       return LSA_ERR_INVALID_ARG;
-    if (d->topk != 0 || d->out_idx || d->out_score) return LSA_ERR_INVALID_ARG;
+    if (d->topk != 0 || d->out_idx || d->out_score || d->query_block > 1) return LSA_ERR_INVALID_ARG;
     if (d->hint && (((uintptr_t)d->hint & 3u) || d->hint_ld < lsa::score_hint_count((int)score_slots(d), d->k_idx_dtype)))
       return LSA_ERR_INVALID_ARG;
     return LSA_OK;
@@ -109,7 +139,20 @@ int validate_score(const lsa_score_desc* d, size_t* ws_need) {
     if (d->n_seq != 1 || !d->q_idx || d->q || d->cand || d->hint) return LSA_ERR_INVALID_ARG;
     if (esize_wide(d->k_idx_dtype) == 0) return LSA_ERR_UNSUPPORTED;
     if (!al16(d->q_idx)) return LSA_ERR_INVALID_ARG;
-    if (d->topk < 0) return LSA_ERR_INVALID_ARG;
+    if (d->topk < 0 || d->query_block < 0) return LSA_ERR_INVALID_ARG;
+    if (d->query_block > 1) {
+      if (d->k_idx_dtype != LSA_BF16 || !lsa::prefill_mfma_scores_supported(d->rank) || !mfma_rows_ok(d))
+        return LSA_ERR_UNSUPPORTED;
+      const int nb = (d->n_keys + d->query_block - 1) / d->query_block;
+      if ((d->n_keys + 31) / 32 > 65535 || ((int64_t)nb * d->n_kv_heads + 31) / 32 > 65535)
+        return LSA_ERR_UNSUPPORTED;
+      if (d->scores && (!al16(d->scores) || d->scores_ld % 4 != 0 || d->scores_ld < d->n_keys))
+        return LSA_ERR_INVALID_ARG;
+      if (d->topk == 0 && (!d->scores || d->out_idx || d->out_score)) return LSA_ERR_INVALID_ARG;
+      if (d->topk > 0 && !d->out_idx) return LSA_ERR_INVALID_ARG;
+      *ws_need = block_prefill_layout(d, nullptr, nullptr);
+      return LSA_OK;
+    }
     if (d->topk == 0) {
       const bool mfma = d->k_idx_dtype == LSA_BF16 && lsa::prefill_mfma_scores_supported(d->rank) &&
                         mfma_rows_ok(d);
@@ -138,7 +181,8 @@ int validate_select(const lsa_select_desc* d, size_t* ws_need) {
   if (!d->scores || !al16(d->scores) || d->scores_ld % 4 != 0 || d->scores_ld < d->n)
     return LSA_ERR_INVALID_ARG;
   if (!d->out_idx) return LSA_ERR_INVALID_ARG;
-  if (d->causal_group < 0 || (d->causal_group > 0 && d->n_valid)) return LSA_ERR_INVALID_ARG;
+  if (d->causal_group < 0 || (d->causal_group > 0 && d->n_valid) || d->causal_block < 0)
+    return LSA_ERR_INVALID_ARG;
   if (d->cand) {
     if (d->cand_block < 1 || d->n_positions < 0) return LSA_ERR_INVALID_ARG;
     if (d->cand_ld < ((int64_t)d->n + d->cand_block - 1) / d->cand_block) return LSA_ERR_INVALID_ARG;
@@ -170,6 +214,8 @@ int validate_attn(const lsa_attn_desc* d, size_t* ws_need) {
   if (!strides16(ke, paged ? 0 : d->kv_stride_seq, d->kv_stride_tok, d->kv_stride_head))
     return LSA_ERR_INVALID_ARG;
   if (paged && (d->n_pool_rows < 1 || d->slot_table_ld < d->n_keys || (uintptr_t)d->slot_table % 4 != 0))
+    return LSA_ERR_INVALID_ARG;
+  if (d->query_block < 0 || (d->query_block > 1 && d->mode != LSA_MODE_PREFILL_CAUSAL))
     return LSA_ERR_INVALID_ARG;
   int sp, kps;
   lsa::attention_plan(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, &sp, &kps);
@@ -223,6 +269,42 @@ int lsa_index_score(const lsa_score_desc* d, void* ws, size_t ws_bytes, void* st
     a.hint = d->hint;
     a.hint_ld = d->hint_ld;
     e = lsa::launch_score_decode(a, rows, d->k_idx_dtype, s);
+  } else if (d->query_block > 1) {
+    // one selection per block of query tokens: block queries, block scores
+    // through the same MFMA tiles, then the select with a block-causal rule
+    BlockWs w;
+    block_prefill_layout(d, ws, &w);
+    const int qb = d->query_block;
+    const int nb = (d->n_keys + qb - 1) / qb;
+    const int rows = nb * d->n_kv_heads;
+    e = lsa::launch_block_queries((const uint16_t*)d->q_idx, d->n_keys, d->n_kv_heads, qb, w.qbar, s);
+    if (e == hipSuccess) {
+      lsa::PrefillTopkArgs a{};
+      a.q_idx = w.qbar;
+      a.k_idx = (const uint16_t*)d->k_idx;
+      a.ks_head = d->k_stride_head;
+      a.ks_tok = d->k_stride_tok;
+      a.L = d->n_keys;
+      a.Hkv = d->n_kv_heads;
+      a.r = d->rank;
+      a.Lq = nb;
+      a.qblk = qb;
+      e = lsa::launch_prefill_scores_mfma(a, w.scores, w.ld, s);
+    }
+    if (e == hipSuccess && d->topk > 0) {
+      lsa::SelectArgs sa{};
+      sa.scores = w.scores;
+      sa.scores_ld = w.ld;
+      sa.n = d->n_keys;
+      sa.B = d->topk;
+      sa.causal_group = d->n_kv_heads;
+      sa.causal_block = qb;
+      sa.cand_block = 1;
+      sa.out_idx = d->out_idx;
+      sa.out_score = d->out_score;
+      lsa::select_bind_workspace(sa, rows, w.sel);
+      e = lsa::launch_select(sa, rows, s);
+    }
   } else if (d->topk == 0 && d->k_idx_dtype == LSA_BF16 &&
              lsa::prefill_mfma_scores_supported(d->rank) && mfma_rows_ok(d)) {
     lsa::PrefillTopkArgs a{};
@@ -233,6 +315,8 @@ int lsa_index_score(const lsa_score_desc* d, void* ws, size_t ws_bytes, void* st
     a.L = d->n_keys;
     a.Hkv = d->n_kv_heads;
     a.r = d->rank;
+    a.Lq = d->n_keys;
+    a.qblk = 1;
     e = lsa::launch_prefill_scores_mfma(a, d->scores, d->scores_ld, s);
   } else if (d->topk == 0) {
     lsa::ScorePrefillArgs a{};
@@ -256,6 +340,8 @@ int lsa_index_score(const lsa_score_desc* d, void* ws, size_t ws_bytes, void* st
     a.Hkv = d->n_kv_heads;
     a.r = d->rank;
     a.B = d->topk;
+    a.Lq = d->n_keys;
+    a.qblk = 1;
     a.out_idx = d->out_idx;
     a.out_score = d->out_score;
     a.ws = ws;
@@ -298,6 +384,7 @@ int lsa_topk_select(const lsa_select_desc* d, void* ws, size_t ws_bytes, void* s
   a.B = d->topk;
   a.n_valid = d->n_valid;
   a.causal_group = d->causal_group;
+  a.causal_block = d->causal_block > 1 ? d->causal_block : 1;
   a.cand = d->cand;
   a.cand_ld = d->cand_ld;
   a.cand_block = d->cand ? d->cand_block : 1;
@@ -343,6 +430,7 @@ int lsa_indexed_attention(const lsa_attn_desc* d, void* ws, size_t ws_bytes, voi
   a.B = d->topk;
   a.T = d->n_keys;
   a.prefill = d->mode == LSA_MODE_PREFILL_CAUSAL;
+  a.qblk = d->query_block > 1 ? d->query_block : 1;
   const float scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->head_dim);
   a.scale_log2 = scale * 1.4426950408889634f;
   a.out = d->out;

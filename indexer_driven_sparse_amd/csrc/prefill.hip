@@ -72,9 +72,11 @@ __device__ __forceinline__ const uint16_t* qrow(const PrefillTopkArgs& a, int g,
 }
 
 // ---------------------------------------------------------------------------
-// Unfused scores (topk == 0): full causal rows, -inf above the diagonal.
-// One wave per 32 x 32 tile; the tile is transposed through LDS so each
-// row's 32 scores leave as 128 contiguous bytes.
+// Unfused scores (topk == 0): full causal rows, -inf past each row's keys.
+// Row i sees keys j < (i+1)*qblk (qblk = 1: j <= i; qblk > 1: the keys of a
+// block of qblk query tokens). One wave per 32 x 32 tile; the tile is
+// transposed through LDS so each row's 32 scores leave as 128 contiguous
+// bytes.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void prefill_scores_mfma_kernel(PrefillTopkArgs a, float* scores,
                                                                  int64_t ld) {
@@ -82,10 +84,10 @@ __global__ __launch_bounds__(64) void prefill_scores_mfma_kernel(PrefillTopkArgs
   const int lane = threadIdx.x, h = lane >> 5, n = lane & 31;
   const int kt = blockIdx.x, qt = blockIdx.y, g = blockIdx.z;
   const int j0 = kt * kT, i0 = qt * kT;
-  if (j0 <= i0 + kT - 1) {   // some key of the tile is causal for some row
+  if ((int64_t)j0 < (int64_t)(i0 + kT) * a.qblk) {   // some key of the tile is visible to some row
     bf16x8 ka[kCh], qb[kCh];
     const uint16_t* kp = krow(a, g, min(j0 + n, a.L - 1));
-    const uint16_t* qp = qrow(a, g, min(i0 + n, a.L - 1));
+    const uint16_t* qp = qrow(a, g, min(i0 + n, a.Lq - 1));
 #pragma unroll
     for (int c = 0; c < kCh; ++c) {
       ka[c] = frag(kp, c, h);
@@ -99,14 +101,28 @@ __global__ __launch_bounds__(64) void prefill_scores_mfma_kernel(PrefillTopkArgs
   // lane pair (2r, 2r+1) writes row r's 32 scores, 16 each
   const int r = lane >> 1, half = lane & 1;
   const int i = i0 + r;
-  if (i < a.L) {
+  if (i < a.Lq) {
+    const int64_t jend = (int64_t)(i + 1) * a.qblk;   // this row's keys: j < jend
     float* out = scores + ((int64_t)i * a.Hkv + g) * ld + j0 + 16 * half;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int j = j0 + 16 * half + q;
-      if (j < a.L) out[q] = (j <= i) ? tile[r][16 * half + q] : -INFINITY;
+      if (j < a.L) out[q] = (j < jend) ? tile[r][16 * half + q] : -INFINITY;
     }
   }
+}
+
+// Block queries: one workgroup of 64 lanes per (block, KV head); lane c
+// adds channel c of the block's tokens in fp64, in token order, divides by
+// the token count and rounds that mean once to bf16 (nearest-even). For
+// inputs of ordinary range the fp64 sum is exact.
+__global__ __launch_bounds__(kRank) void block_query_kernel(const uint16_t* q_idx, int L, int Hkv,
+                                                           int qblk, uint16_t* out) {
+  const int b = blockIdx.x, g = blockIdx.y, c = threadIdx.x;
+  const int i0 = b * qblk, i1 = min(L, i0 + qblk);
+  double s = 0.0;
+  for (int i = i0; i < i1; ++i) s += (double)bf16_to_f32(q_idx[((int64_t)i * Hkv + g) * kRank + c]);
+  out[((int64_t)b * Hkv + g) * kRank + c] = f64_to_bf16_rne(s / (double)(i1 - i0));
 }
 
 // ---------------------------------------------------------------------------
@@ -700,8 +716,15 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s) {
 
 hipError_t launch_prefill_scores_mfma(const PrefillTopkArgs& a, float* scores, int64_t ld,
                                       hipStream_t s) {
-  const dim3 grid((a.L + kT - 1) / kT, (a.L + kT - 1) / kT, a.Hkv);
+  const dim3 grid((a.L + kT - 1) / kT, (a.Lq + kT - 1) / kT, a.Hkv);
   hipLaunchKernelGGL(prefill_scores_mfma_kernel, grid, dim3(64), 0, s, a, scores, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_queries(const uint16_t* q_idx, int L, int Hkv, int qblk, uint16_t* out,
+                                hipStream_t s) {
+  const int nb = (L + qblk - 1) / qblk;
+  hipLaunchKernelGGL(block_query_kernel, dim3(nb, Hkv), dim3(kRank), 0, s, q_idx, L, Hkv, qblk, out);
   return hipGetLastError();
 }
 

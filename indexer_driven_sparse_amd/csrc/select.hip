@@ -86,7 +86,7 @@ __global__ __launch_bounds__(kSegThreads) void select_collect_kernel(SelectArgs 
   const int row = blockIdx.x / a.nseg, seg = blockIdx.x - row * a.nseg;
   int64_t nv = a.n;
   if (a.n_valid) nv = min<int64_t>(nv, (int64_t)max(0, a.n_valid[row]));
-  if (a.causal_group > 0) nv = min<int64_t>(nv, (int64_t)row / a.causal_group + 1);
+  if (a.causal_group > 0) nv = min<int64_t>(nv, ((int64_t)row / a.causal_group + 1) * a.causal_block);
   const int64_t s0 = (int64_t)seg * kSeg;
   int4* meta = a.seg_meta + (int64_t)row * a.nseg + seg;
   if (s0 >= nv) {   // nothing valid here (block-uniform)
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectArgs a) {
   const int row = blockIdx.x;
   int64_t nv = a.n;
   if (a.n_valid) nv = min<int64_t>(nv, (int64_t)max(0, a.n_valid[row]));
-  if (a.causal_group > 0) nv = min<int64_t>(nv, (int64_t)row / a.causal_group + 1);
+  if (a.causal_group > 0) nv = min<int64_t>(nv, ((int64_t)row / a.causal_group + 1) * a.causal_block);
   select_row<CAND, GBM, PRE>(a, row, a.scores + (int64_t)row * a.scores_ld, nv, smem_raw);
 }
 

@@ -50,7 +50,7 @@ class ScoreDesc(_c.Structure):
                 ("k_stride_seq", _I64), ("k_stride_head", _I64), ("k_stride_tok", _I64),
                 ("cand", _P), ("n_cand", _I32), ("cand_block", _I32), ("cand_ld", _I64),
                 ("scores", _P), ("scores_ld", _I64),
-                ("topk", _I32), ("reserved1", _I32), ("out_idx", _P), ("out_score", _P),
+                ("topk", _I32), ("query_block", _I32), ("out_idx", _P), ("out_score", _P),
                 ("hint", _P), ("hint_ld", _I64)]
 
 
@@ -58,7 +58,7 @@ class SelectDesc(_c.Structure):
     _fields_ = [("struct_size", _U32), ("rows", _I32), ("n", _I32), ("topk", _I32),
                 ("scores", _P), ("scores_ld", _I64), ("n_valid", _P),
                 ("causal_group", _I32), ("cand_block", _I32), ("cand", _P), ("cand_ld", _I64),
-                ("n_positions", _I32), ("reserved0", _I32),
+                ("n_positions", _I32), ("causal_block", _I32),
                 ("out_idx", _P), ("out_score", _P), ("out_count", _P),
                 ("hint", _P), ("hint_ld", _I64), ("hint_count", _I32), ("hint_k", _I32)]
 
@@ -68,7 +68,7 @@ class AttnDesc(_c.Structure):
                 ("n_kv_heads", _I32), ("head_dim", _I32), ("topk", _I32), ("n_keys", _I32),
                 ("q", _P), ("q_dtype", _I32), ("kv_dtype", _I32), ("k", _P), ("v", _P),
                 ("kv_stride_seq", _I64), ("kv_stride_tok", _I64), ("kv_stride_head", _I64),
-                ("idx", _P), ("scale", _F), ("reserved0", _I32), ("out", _P), ("lse", _P),
+                ("idx", _P), ("scale", _F), ("query_block", _I32), ("out", _P), ("lse", _P),
                 ("slot_table", _P), ("slot_table_ld", _I64), ("n_pool_rows", _I32),
                 ("reserved1", _I32)]
 
@@ -205,7 +205,7 @@ def _workspace(need: int, workspace, device):
 # ---------------------------------------------------------------------------
 
 def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score,
-                hint=None):
+                hint=None, query_block=0):
     d = ScoreDesc()
     d.struct_size = _c.sizeof(ScoreDesc)
     d.mode = mode
@@ -221,6 +221,8 @@ def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_id
     if k_idx.stride(-1) != 1:
         raise ValueError("k_idx: innermost dimension must be contiguous")
     d.n_seq, d.n_kv_heads, d.n_keys, d.rank = N, Hkv, T, r
+    qb = max(1, int(query_block))
+    n_rows = (T + qb - 1) // qb          # prefill rows: tokens, or blocks of qb tokens
     if q is not None and (q.dim() != 3 or q.shape[0] != N or not q.is_contiguous()):
         raise ValueError("q must be contiguous [N,Hq,d]")
     if q is not None and (w is None or w.shape[-1] != r or w.shape[-2] != q.shape[2]
@@ -232,10 +234,11 @@ def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_id
     if cand is not None and (not cand.is_contiguous() or cand.dtype != torch.int32
                              or tuple(cand.shape[:-1]) != (N, Hkv)):
         raise ValueError("cand must be contiguous int32 [N,Hkv,n_cand]")
-    if out_idx is not None and (not out_idx.is_contiguous() or out_idx.numel() != T * Hkv * topk):
-        raise ValueError("out_idx must be contiguous [L,Hkv,B]")
-    if out_score is not None and (not out_score.is_contiguous() or out_score.numel() != T * Hkv * topk):
-        raise ValueError("out_score must be contiguous [L,Hkv,B]")
+    if out_idx is not None and (not out_idx.is_contiguous() or out_idx.numel() != n_rows * Hkv * topk):
+        raise ValueError("out_idx must be contiguous [rows,Hkv,B] (rows = L, or ceil(L/query_block))")
+    if out_score is not None and (not out_score.is_contiguous() or
+                                  out_score.numel() != n_rows * Hkv * topk):
+        raise ValueError("out_score must be contiguous [rows,Hkv,B]")
     if q is not None:
         d.q = _ptr(q)
         d.q_dtype = _dt(q)
@@ -250,8 +253,9 @@ def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_id
         d.cand_ld = cand.stride(-2) if cand.dim() >= 2 else cand.shape[-1]
     if scores is not None:
         d.scores = _ptr(scores)
-        d.scores_ld = _rows2d(scores, N * Hkv if mode == MODE_DECODE else T * Hkv, "scores")
+        d.scores_ld = _rows2d(scores, N * Hkv if mode == MODE_DECODE else n_rows * Hkv, "scores")
     d.topk = topk
+    d.query_block = int(query_block)
     d.out_idx = _ptr(out_idx)
     d.out_score = _ptr(out_score)
     if hint is not None:
@@ -275,15 +279,17 @@ def lsa_score_hint_layout(k_idx, scores, *, q=None, w=None, q_idx=None, cand=Non
 def lsa_index_score(k_idx: torch.Tensor, scores: torch.Tensor | None, *, q=None, w=None,
                     q_idx=None, cand=None, cand_block: int = 1, mode: int = MODE_DECODE,
                     topk: int = 0, out_idx=None, out_score=None, hint=None, workspace=None,
-                    stream=None) -> None:
+                    stream=None, query_block: int = 0) -> None:
     """Indexer scores. Decode: k_idx [N,Hkv,T,r] (any strides, r contiguous);
     either q [N,Hq,d] with w [d,r] / [Hkv,d,r] (prep fused; q_idx, if given,
     receives fp32 [N,Hkv,r]) or q_idx fp32 [N,Hkv,r]; optional cand
     [N,Hkv,nc] int32 with cand_block; scores fp32 [N,Hkv,n_out].
     Prefill: k_idx [L,Hkv,r], q_idx [L,Hkv,r]; topk=0 writes scores
-    [L,Hkv,L]; topk=B fills out_idx [L,Hkv,B] (and out_score)."""
+    [L,Hkv,L]; topk=B fills out_idx [L,Hkv,B] (and out_score).
+    Prefill with query_block=qb > 1: one selection per block of qb tokens
+    (rows ceil(L/qb)): scores [nb,Hkv,L] and/or out_idx [nb,Hkv,B]."""
     d = _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score,
-                    hint)
+                    hint, query_block)
     lib = _lib()
     ws, wsb = _workspace(lib.lsa_score_workspace_bytes(_c.byref(d)), workspace, k_idx.device)
     _check("lsa_index_score", lib.lsa_index_score(_c.byref(d), _ptr(ws), wsb, _stream(stream)))
@@ -291,13 +297,14 @@ def lsa_index_score(k_idx: torch.Tensor, scores: torch.Tensor | None, *, q=None,
 
 def lsa_score_workspace_bytes(k_idx, scores, *, q=None, w=None, q_idx=None, cand=None,
                               cand_block=1, mode=MODE_DECODE, topk=0, out_idx=None,
-                              out_score=None) -> int:
-    d = _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score)
+                              out_score=None, query_block: int = 0) -> int:
+    d = _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_idx, out_score,
+                    None, query_block)
     return int(_lib().lsa_score_workspace_bytes(_c.byref(d)))
 
 
 def _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal_group, cand,
-                 cand_block, n_positions, hint=None, hint_k=0):
+                 cand_block, n_positions, hint=None, hint_k=0, causal_block=0):
     rows = scores.numel() // scores.shape[-1]
     if not out_idx.is_contiguous() or out_idx.numel() != rows * topk or out_idx.dtype != torch.int32:
         raise ValueError("out_idx must be contiguous int32 [rows, B]")
@@ -321,6 +328,7 @@ def _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal
     d.scores_ld = _rows2d(scores, rows, "scores")
     d.n_valid = _ptr(n_valid)
     d.causal_group = causal_group
+    d.causal_block = causal_block
     if cand is not None:
         d.cand = _ptr(cand)
         d.cand_block = cand_block
@@ -342,12 +350,13 @@ def _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal
 def lsa_topk_select(scores: torch.Tensor, topk: int, out_idx: torch.Tensor, *, n=None,
                     out_score=None, out_count=None, n_valid=None, causal_group: int = 0,
                     cand=None, cand_block: int = 1, n_positions: int = 0, hint=None,
-                    hint_k: int = 0, workspace=None, stream=None) -> None:
+                    hint_k: int = 0, workspace=None, stream=None, causal_block: int = 0) -> None:
     """Exact top-B per row of scores [..., n] (rows evenly spaced): ascending
     positions in out_idx [rows, B], -1 padded. hint/hint_k: the selection
-    hint of the scoring call (speed only, never the result)."""
+    hint of the scoring call (speed only, never the result). causal_group k:
+    row i has (i//k + 1) * max(1, causal_block) valid slots."""
     d = _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal_group, cand,
-                     cand_block, n_positions, hint, hint_k)
+                     cand_block, n_positions, hint, hint_k, causal_block)
     lib = _lib()
     ws, wsb = _workspace(lib.lsa_select_workspace_bytes(_c.byref(d)), workspace, scores.device)
     _check("lsa_topk_select", lib.lsa_topk_select(_c.byref(d), _ptr(ws), wsb, _stream(stream)))
@@ -361,7 +370,8 @@ def lsa_select_workspace_bytes(scores, topk, out_idx, *, n=None, n_valid=None, c
     return int(_lib().lsa_select_workspace_bytes(_c.byref(d)))
 
 
-def _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table=None, n_keys=None):
+def _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table=None, n_keys=None,
+               query_block=0):
     rows, Hq, hd = q.shape
     if k.stride() != v.stride() or k.shape != v.shape:
         raise ValueError("k and v must share shape and strides")
@@ -383,8 +393,9 @@ def _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table=None, n_keys=None
         raise ValueError(f"decode reads sequence `row` of k/v: {S} sequences < {rows} rows")
     if not q.is_contiguous() or not idx.is_contiguous() or not out.is_contiguous():
         raise ValueError("q, idx and out must be contiguous")
-    if tuple(idx.shape[:-1]) != (rows, Hkv) or tuple(out.shape) != (rows, Hq, hd):
-        raise ValueError("idx must be [rows,Hkv,B] and out [rows,Hq,d]")
+    qb = max(1, int(query_block))
+    if tuple(idx.shape[:-1]) != ((rows + qb - 1) // qb, Hkv) or tuple(out.shape) != (rows, Hq, hd):
+        raise ValueError("idx must be [ceil(rows/query_block),Hkv,B] and out [rows,Hq,d]")
     d = AttnDesc()
     d.struct_size = _c.sizeof(AttnDesc)
     d.mode = mode
@@ -398,6 +409,7 @@ def _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table=None, n_keys=None
     d.kv_stride_seq, d.kv_stride_tok, d.kv_stride_head = strides
     d.idx = _ptr(idx)
     d.scale = scale
+    d.query_block = int(query_block)
     d.out = _ptr(out)
     d.lse = _ptr(lse)
     if slot_table is not None:
@@ -410,12 +422,13 @@ def _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table=None, n_keys=None
 def lsa_indexed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                           out: torch.Tensor, *, lse=None, mode: int = MODE_DECODE,
                           scale: float = 0.0, workspace=None, stream=None,
-                          slot_table=None, n_keys=None) -> None:
+                          slot_table=None, n_keys=None, query_block: int = 0) -> None:
     """q [rows,Hq,d]; k, v [S,T,Hkv,d] viewed through their strides (same for
     both); idx [rows,Hkv,B] int32; out fp32 [rows,Hq,d]; lse fp32 [rows,Hq].
     Paged: k, v are a pool [P,Hkv,d] and slot_table int32 [S, ld] maps
-    (sequence, position) to a pool row; n_keys defaults to the table width."""
-    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys)
+    (sequence, position) to a pool row; n_keys defaults to the table width.
+    Prefill is causal; query_block=qb > 1 shares idx row i//qb among tokens."""
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys, query_block)
     lib = _lib()
     ws, wsb = _workspace(lib.lsa_attention_workspace_bytes(_c.byref(d)), workspace, q.device)
     _check("lsa_indexed_attention",
@@ -423,8 +436,9 @@ def lsa_indexed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx
 
 
 def lsa_attention_workspace_bytes(q, k, v, idx, out, *, lse=None, mode=MODE_DECODE,
-                                  scale=0.0, slot_table=None, n_keys=None) -> int:
-    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys)
+                                  scale=0.0, slot_table=None, n_keys=None,
+                                  query_block: int = 0) -> int:
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys, query_block)
     return int(_lib().lsa_attention_workspace_bytes(_c.byref(d)))
 
 
@@ -457,8 +471,10 @@ def score_hint_layout_for(N: int, Hkv: int, n_out: int, r: int = 64, dtype: int 
     return int(c.value), int(k.value)
 
 
-def prefill_score_workspace_bytes_for(L: int, Hkv: int, r: int, B: int) -> int:
-    """Workspace of the fused causal prefill indexer (bf16, [L,Hkv,r])."""
+def prefill_score_workspace_bytes_for(L: int, Hkv: int, r: int, B: int,
+                                      query_block: int = 0) -> int:
+    """Workspace of the fused causal prefill indexer (bf16, [L,Hkv,r]); with
+    query_block > 1, of the block-shared selection (scores in workspace)."""
     dd = ScoreDesc()
     dd.struct_size = _c.sizeof(ScoreDesc)
     dd.mode, dd.n_seq, dd.n_kv_heads, dd.n_keys, dd.rank = MODE_PREFILL_CAUSAL, 1, Hkv, L, r
@@ -466,6 +482,7 @@ def prefill_score_workspace_bytes_for(L: int, Hkv: int, r: int, B: int) -> int:
     dd.k_idx_dtype = BF16
     dd.k_stride_head, dd.k_stride_tok = r, Hkv * r
     dd.topk = B
+    dd.query_block = query_block
     return int(_lib().lsa_score_workspace_bytes(_c.byref(dd)))
 
 

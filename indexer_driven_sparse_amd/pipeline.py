@@ -190,19 +190,29 @@ class HierarchicalPlan:
 
 class PrefillPlan:
     """Buffers for causal prefill of one sequence of L tokens: per query row
-    the top-B keys of its causal prefix, then indexed attention."""
+    the top-B keys of its causal prefix, then indexed attention. With
+    query_block = qb > 1 one selection serves each block of qb tokens (the
+    block's mean query scores the keys its last token sees) and every token
+    of the block attends to it causally."""
 
     def __init__(self, L: int, Hq: int, Hkv: int, d: int, r: int, B: int, device="cuda",
-                 fused: bool = True):
+                 fused: bool = True, query_block: int = 1):
         self.L, self.Hq, self.Hkv, self.d, self.r, self.B = L, Hq, Hkv, d, r, B
         self.fused = fused
-        self.idx = torch.empty(L, Hkv, B, dtype=torch.int32, device=device)
-        self.idx_scores = torch.empty(L, Hkv, B, dtype=torch.float32, device=device)
+        self.query_block = qb = max(1, query_block)
+        nsel = (L + qb - 1) // qb
+        self.idx = torch.empty(nsel, Hkv, B, dtype=torch.int32, device=device)
+        self.idx_scores = torch.empty(nsel, Hkv, B, dtype=torch.float32, device=device)
         self.out = torch.empty(L, Hq, d, dtype=torch.float32, device=device)
         self.lse = torch.empty(L, Hq, dtype=torch.float32, device=device)
         self.scores = None
         self.score_ws = None
-        if fused:
+        if qb > 1:
+            # block queries, block scores and the select live in the workspace
+            self.fused = True
+            need = lsa.prefill_score_workspace_bytes_for(L, Hkv, r, B, query_block=qb)
+            self.score_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        elif fused:
             need = lsa.prefill_score_workspace_bytes_for(L, Hkv, r, B)
             self.score_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
         else:
@@ -212,7 +222,8 @@ class PrefillPlan:
         if self.fused:
             lsa.lsa_index_score(k_idx, None, q_idx=q_idx, mode=lsa.MODE_PREFILL_CAUSAL,
                                 topk=self.B, out_idx=self.idx, out_score=self.idx_scores,
-                                workspace=self.score_ws, stream=stream)
+                                workspace=self.score_ws, stream=stream,
+                                query_block=self.query_block)
         else:
             lsa.lsa_index_score(k_idx, self.scores, q_idx=q_idx, mode=lsa.MODE_PREFILL_CAUSAL,
                                 stream=stream)
@@ -222,7 +233,8 @@ class PrefillPlan:
 
     def attend(self, q, k, v, stream=None):
         lsa.lsa_indexed_attention(q, k, v, self.idx, self.out, lse=self.lse,
-                                  mode=lsa.MODE_PREFILL_CAUSAL, stream=stream)
+                                  mode=lsa.MODE_PREFILL_CAUSAL, stream=stream,
+                                  query_block=self.query_block)
 
     def run(self, q_idx, k_idx, q, k, v, stream=None):
         self.index(q_idx, k_idx, stream)

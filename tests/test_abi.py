@@ -292,3 +292,28 @@ def test_cross_layer_plan_sources():
     for bad in ("", "SF", "FX"):
         with pytest.raises(ValueError):
             pipeline.CrossLayerPlan(bad, 2, 8, 2, 3000, 128, 64, 256, device="cpu")
+
+
+def test_query_block_validation_and_workspace():
+    lib = lsa._lib()
+    pre = dict(mode=1, n_seq=1, n_kv_heads=1, n_keys=65536, k_stride_seq=0, k_stride_head=64,
+               k_stride_tok=64, scores=0, scores_ld=0, topk=2048, out_idx=0x7000)
+    assert _call_score(_score_desc(**pre, query_block=-1)) == INVALID
+    assert _call_score(_score_desc(**pre, query_block=64, k_idx_dtype=lsa.F32)) == UNSUPPORTED
+    assert _call_score(_score_desc(**dict(pre, out_idx=0), query_block=64)) == INVALID
+    assert _call_score(_score_desc(query_block=2)) == INVALID          # decode has no blocks
+    d = _score_desc(**pre, query_block=64)
+    need = lib.lsa_score_workspace_bytes(ctypes.byref(d))
+    assert need >= 1024 * 65536 * 4 + 1024 * 64 * 2                    # block scores + queries
+    assert _call_score(d) == WORKSPACE
+    # with a caller score buffer the workspace holds no scores
+    e = _score_desc(**dict(pre, scores=0x9000, scores_ld=65536), query_block=64)
+    assert 0 < lib.lsa_score_workspace_bytes(ctypes.byref(e)) < 1024 * 65536 * 4
+    # scores only (topk 0) need the caller's buffer
+    assert _call_score(_score_desc(**dict(pre, topk=0, out_idx=0), query_block=64)) == INVALID
+    s = _select_desc(causal_group=1, causal_block=-2)
+    assert lib.lsa_topk_select(ctypes.byref(s), None, 0, None) == INVALID
+    a = _attn_desc(query_block=2)                                       # decode rows are not blocked
+    assert lib.lsa_indexed_attention(ctypes.byref(a), None, 0, None) == INVALID
+    a = _attn_desc(query_block=-1, mode=1)
+    assert lib.lsa_indexed_attention(ctypes.byref(a), None, 0, None) == INVALID

@@ -867,6 +867,113 @@ def test_prefill_c4_full_size():
 
 
 # --------------------------------------------------------------------------
+# query-block-shared prefill selection
+# --------------------------------------------------------------------------
+
+def _block_select_gpu(qd, kd, B, qb, with_scores=True):
+    L, Hkv, _ = kd.shape
+    nb = (L + qb - 1) // qb
+    sc = None
+    if with_scores:
+        sc = torch.empty(nb, Hkv, L + (4 - L % 4) % 4, device="cuda")[:, :, :L]
+    idx = torch.full((nb, Hkv, B), -7, dtype=torch.int32, device="cuda")
+    osc = torch.empty(nb, Hkv, B, device="cuda")
+    lsa.lsa_index_score(kd, sc, q_idx=qd, mode=lsa.MODE_PREFILL_CAUSAL, topk=B, out_idx=idx,
+                        out_score=osc, query_block=qb)
+    return sc, idx, osc
+
+
+@pytest.mark.parametrize("kind,L,Hkv,qb,B", [("c4", 3000, 1, 64, 512), ("c4", 2500, 2, 16, 300),
+                                             ("int", 2000, 1, 32, 256), ("c4", 777, 2, 100, 50),
+                                             ("const", 4100, 1, 64, 2048)])
+def test_prefill_block_selection(kind, L, Hkv, qb, B):
+    """Block scores against the oracle's (fp32 MFMA vs fp64), the selection
+    exactly equal to the oracle's top-B over the GPU's own block scores, and
+    to the oracle's selection up to near-ties."""
+    say("prefill block selection", kind, L, Hkv, qb, B)
+    q, k = _prefill_qk(kind, L, Hkv, seed=L + qb)
+    qd, kd = dev(q), dev(k)
+    sc, idx, osc = _block_select_gpu(qd, kd, B, qb)
+    nb = (L + qb - 1) // qb
+    gsc = host(sc).reshape(nb * Hkv, L)
+    ridx, rsc, rscores = oracle.prefill_block_topk(q, k, B, qb, want_scores=True)
+    rscores = rscores.reshape(nb * Hkv, L)
+    qf = decoded(q).astype(np.float64)
+    kf = decoded(k).astype(np.float64)
+    qmax = np.abs(np.concatenate([qf, np.zeros((nb * qb - L, Hkv, qf.shape[2]))])
+                  ).reshape(nb, qb, Hkv, -1).max(axis=1).reshape(nb * Hkv, -1)   # bounds |block mean|
+    kk = np.broadcast_to(kf.transpose(1, 0, 2)[None], (nb, Hkv, L, kf.shape[2])).reshape(nb * Hkv, L, -1)
+    assert_scores_close(gsc, rscores, qmax, kk)
+    gi = host(idx).reshape(nb * Hkv, B)
+    valid = np.minimum(L, (np.arange(nb * Hkv) // Hkv + 1) * qb).astype(np.int32)
+    exact, esc, _ = oracle.topk(gsc, B, n_valid=valid)
+    np.testing.assert_array_equal(gi, exact)
+    np.testing.assert_array_equal(host(osc).reshape(nb * Hkv, B)[gi >= 0], esc[gi >= 0])
+    check_index_sets(gi, ridx.reshape(nb * Hkv, B), list(rscores), B)
+
+
+@pytest.mark.parametrize("L,Hq,Hkv,d,qb,B", [(1000, 8, 1, 128, 64, 256), (700, 8, 2, 128, 16, 100),
+                                             (333, 4, 1, 64, 50, 40)])
+def test_prefill_block_attention(L, Hq, Hkv, d, qb, B):
+    """Every token attends to its block's selection, masked causally."""
+    say("prefill block attention", L, Hq, Hkv, d, qb, B)
+    rng = np.random.default_rng(L + qb)
+    q = synth.to_bf16_bits(rng.standard_normal((L, Hq, d)).astype(np.float32))
+    K = synth.to_bf16_bits(rng.standard_normal((1, L, Hkv, d)).astype(np.float32))
+    V = synth.to_bf16_bits(rng.standard_normal((1, L, Hkv, d)).astype(np.float32))
+    nb = (L + qb - 1) // qb
+    blk = np.full((nb, Hkv, B), -1, np.int32)
+    for b in range(nb):
+        hi = min(L, (b + 1) * qb)
+        for g in range(Hkv):
+            c = min(B, hi)
+            blk[b, g, :c] = np.sort(rng.choice(hi, c, replace=False))
+    out = torch.full((L, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((L, Hq), float("nan"), device="cuda")
+    lsa.lsa_indexed_attention(dev(q), dev(K), dev(V), dev(blk), out, lse=lse,
+                              mode=lsa.MODE_PREFILL_CAUSAL, query_block=qb)
+    ref, rlse = oracle.attention(q, K, V, blk, prefill=True, query_block=qb)
+    np.testing.assert_allclose(host(out), ref, rtol=0, atol=ATTN_ATOL)
+    np.testing.assert_allclose(host(lse), rlse, rtol=0, atol=LSE_ATOL)
+
+
+def test_prefill_block_c4_full_size():
+    """L = 65536, 1 KV head, B = 2048, blocks of 64 tokens: every block row
+    against the oracle (near-ties tolerated), exactly against the oracle's
+    top-B over the GPU's block scores for sampled rows, and attention of
+    sampled tokens through the plan."""
+    from indexer_driven_sparse_amd import pipeline
+    case = synth.workload("prefill_l64k")
+    L, Hkv, B, qb = case.L, case.Hkv, case.B, 64
+    say("prefill block C4 full size", L, Hkv, B, qb)
+    qd, kd = dev(case.q_idx), dev(case.k_idx)
+    plan = pipeline.PrefillPlan(L, case.Hq, Hkv, case.d, case.r, B, query_block=qb)
+    Q, K, V = dev(case.Q), dev(case.K), dev(case.V)
+    plan.run(qd, kd, Q, K, V)
+    torch.cuda.synchronize()
+    gi = host(plan.idx).reshape(-1, B)
+    nb = L // qb
+    ridx, _, rscores = oracle.prefill_block_topk(case.q_idx, case.k_idx, B, qb, want_scores=True)
+    diff = check_index_sets(gi, ridx.reshape(nb, B), list(rscores.reshape(nb, L)), B)
+    assert len(diff) <= nb // 20, f"{len(diff)} block rows differ by near-ties"
+    sc, idx2, _ = _block_select_gpu(qd, kd, B, qb)
+    np.testing.assert_array_equal(host(idx2).reshape(-1, B), gi)      # plan == direct call
+    rows = [0, 1, 31, 32, 33, 511, 1023]
+    gsc = host(sc[rows]).reshape(len(rows), L)
+    exact, _, _ = oracle.topk(gsc, B, n_valid=np.minimum(L, (np.array(rows) + 1) * qb).astype(np.int32))
+    np.testing.assert_array_equal(gi[rows], exact)
+    del sc, idx2
+    toks = [0, 63, 64, 127, 2047, 2048, 40000, 65535]
+    out, lse = host(plan.out), host(plan.lse)
+    for i in toks:
+        sel = gi[i // qb]
+        sel = np.where((sel >= 0) & (sel <= i), sel, -1).astype(np.int32)[None, None]
+        o, l = oracle.attention(case.Q[i:i + 1], case.K, case.V, sel, prefill=False)
+        np.testing.assert_allclose(out[i], o[0], rtol=0, atol=ATTN_ATOL)
+        np.testing.assert_allclose(lse[i], l[0], rtol=0, atol=LSE_ATOL)
+
+
+# --------------------------------------------------------------------------
 # hierarchical coarse-to-fine decode, stage by stage against the oracle
 # --------------------------------------------------------------------------
 
