@@ -45,7 +45,7 @@ constexpr int kHistLd = 257;     // padded histogram row: rows fall on different
 constexpr int kRowsA = 128;      // query rows per candidate workgroup
 constexpr int kCandCap = 8192;   // candidate list entries per row
 constexpr int kFinThreads = 256;
-constexpr int kFinPer = kCandCap / kFinThreads;  // candidates per thread (32)
+constexpr int kFinPerMax = kCandCap / kFinThreads;  // candidates per thread, largest build (32)
 constexpr int kRedoBlocks = 256;
 
 // 8 bf16 of row p for chunk c and lane half h: elements 16c + 8h .. +8.
@@ -205,25 +205,53 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
     sh.need2[tid] = 0;
   }
   __syncthreads();
+  // Tiles wholly inside every row's prefix (the common case) skip the
+  // per-score checks; the order key here ignores the NaN and -0 cases,
+  // which can only move tau (speed), never a result.
+  const bool rows_in = i0 + kT <= a.L;
+  uint32_t* hrow = &sh.hist[n][0];
   for (int pass = 0; pass < 2; ++pass) {
     int nval = 0;
-    const int b1 = pass ? sh.bin1[n] : 0;
-    for (int t = w; t < ntiles; t += 4) {
-      bf16x8 ka[kCh];
-      const uint16_t* kp = krow(a, g, sh.pos[min(t * kT + n, m - 1)]);
+    const uint32_t b1 = pass ? (uint32_t)sh.bin1[n] : 0u;
+    bf16x8 ka[kCh];
+    if (w < ntiles) {
+      const uint16_t* kp = krow(a, g, sh.pos[min(w * kT + n, m - 1)]);
 #pragma unroll
       for (int c = 0; c < kCh; ++c) ka[c] = frag(kp, c, h);
-      const f32x16 acc = tile_scores(ka, qb);
+    }
+    for (int t = w; t < ntiles; t += 4) {
+      bf16x8 kc[kCh];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int k = t * kT + tile_key(v, h);
-        if (k < m && i < a.L && sh.pos[k] <= i) {
-          const uint32_t key = order_key(acc[v]);
-          if (pass == 0) {
-            atomicAdd(&sh.hist[n][key >> 24], 1u);
-            ++nval;
-          } else if ((int)(key >> 24) == b1) {
-            atomicAdd(&sh.hist[n][(key >> 16) & 255u], 1u);
+      for (int c = 0; c < kCh; ++c) kc[c] = ka[c];
+      if (t + 4 < ntiles) {   // the next tile's gathers fly during this one
+        const uint16_t* kp = krow(a, g, sh.pos[min((t + 4) * kT + n, m - 1)]);
+#pragma unroll
+        for (int c = 0; c < kCh; ++c) ka[c] = frag(kp, c, h);
+      }
+      const f32x16 acc = tile_scores(kc, qb);
+      const bool full = rows_in && (t + 1) * kT <= m && sh.pos[t * kT + kT - 1] <= i0;
+      if (full) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t u = __float_as_uint(acc[v]);
+          const uint32_t key = u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
+          if (pass == 0) atomicAdd(&hrow[key >> 24], 1u);
+          else if ((key >> 24) == b1) atomicAdd(&hrow[(key >> 16) & 255u], 1u);
+        }
+        nval += 16;
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int k = t * kT + tile_key(v, h);
+          if (k < m && i < a.L && sh.pos[k] <= i) {
+            const uint32_t u = __float_as_uint(acc[v]);
+            const uint32_t key = u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
+            if (pass == 0) {
+              atomicAdd(&hrow[key >> 24], 1u);
+              ++nval;
+            } else if ((key >> 24) == b1) {
+              atomicAdd(&hrow[(key >> 16) & 255u], 1u);
+            }
           }
         }
       }
@@ -366,8 +394,14 @@ __device__ __forceinline__ void fin_find_bin(FinShared& sh, int nb, int need) {
   const int per = (nb + kFinThreads - 1) / kFinThreads;
   const int hi = nb - 1 - t * per;
   int c = 0;
-  for (int k = 0; k < per; ++k)
-    if (hi - k >= 0) c += (int)sh.hist[hi - k];
+  if (per == 8) {   // 2048 bins: two 16-byte reads per thread, no bank conflicts
+    const uint4 x = *(const uint4*)&sh.hist[hi - 7];
+    const uint4 y = *(const uint4*)&sh.hist[hi - 3];
+    c = (int)(x.x + x.y + x.z + x.w + y.x + y.y + y.z + y.w);
+  } else {
+    for (int k = 0; k < per; ++k)
+      if (hi - k >= 0) c += (int)sh.hist[hi - k];
+  }
   int tot;
   int acc = block_exclusive_scan<kFinThreads>(c, sh.scan, &tot);
   for (int k = 0; k < per; ++k) {
@@ -388,6 +422,36 @@ __device__ __forceinline__ void word_prefix(FinShared& sh, const uint32_t* words
                                             int nw) {
   const int per = (nw + kFinThreads - 1) / kFinThreads;
   const int w0 = threadIdx.x * per, w1 = min(nw, w0 + per);
+  if (per == 8) {   // 32-byte runs: vector LDS access, no bank conflicts (the choice is block-uniform)
+    uint32_t wv[8];
+    if (w1 == w0 + 8) {
+      const uint4 x = *(const uint4*)&words[w0];
+      const uint4 y = *(const uint4*)&words[w0 + 4];
+      wv[0] = x.x; wv[1] = x.y; wv[2] = x.z; wv[3] = x.w;
+      wv[4] = y.x; wv[5] = y.y; wv[6] = y.z; wv[7] = y.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) wv[q] = w0 + q < w1 ? words[w0 + q] : 0u;
+    }
+    uint32_t p[8], c = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      p[q] = c;
+      c += __popc(wv[q]);
+    }
+    int tot;
+    const uint32_t off = (uint32_t)block_exclusive_scan<kFinThreads>((int)c, sh.scan, &tot);
+    if (w1 == w0 + 8) {
+      *(uint4*)&pre[w0] = make_uint4(off + p[0], off + p[1], off + p[2], off + p[3]);
+      *(uint4*)&pre[w0 + 4] = make_uint4(off + p[4], off + p[5], off + p[6], off + p[7]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (w0 + q < w1) pre[w0 + q] = off + p[q];
+    }
+    __syncthreads();
+    return;
+  }
   int c = 0;
   for (int q = w0; q < w1; ++q) c += __popc(words[q]);
   int tot;
@@ -399,6 +463,7 @@ __device__ __forceinline__ void word_prefix(FinShared& sh, const uint32_t* words
   __syncthreads();
 }
 
+template <int PER>   // candidates per thread: 16 (B <= 2048) or 32
 __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkArgs a,
                                                                    const int2* cand,
                                                                    const int* cnt, int* redo) {
@@ -412,28 +477,38 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
   const int nv = i + 1;
   const int Bq = min(a.B, nv);
   const int nw = (nv + 31) >> 5;
+  // the first 3/4 of the register slots are read together with the count
+  // (one memory latency; a typical list fills about that much), the rest
+  // only when the list is longer
+  constexpr int kSpec = PER * 3 / 4;
+  const int2* crow = cand + (int64_t)row * kCandCap;
+  int2 raw[PER];
+#pragma unroll
+  for (int k = 0; k < kSpec; ++k) raw[k] = crow[tid + kFinThreads * k];
   const int total = cnt[row];
-  if (total > kCandCap || total < Bq) {   // the threshold missed: recompute this row
+  if (total > kFinThreads * PER || total < Bq) {   // the threshold missed: recompute this row
     if (tid == 0) redo[1 + atomicAdd(&redo[0], 1)] = row;
     return;
   }
+#pragma unroll
+  for (int k = kSpec; k < PER; ++k)
+    if (kFinThreads * k < total) raw[k] = crow[tid + kFinThreads * k];
   for (int q = tid; q < nw; q += kFinThreads) bm[q] = 0u;
   if (tid == 0) {
     sh.kmin = 0xffffffffu;
     sh.kmax = 0u;
   }
   // candidates e = tid + 256 k of the row's list
-  uint32_t key[kFinPer];
-  int32_t jj[kFinPer];
-  const int2* crow = cand + (int64_t)row * kCandCap;
+  uint32_t key[PER];
+  int32_t jj[PER];
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
-  for (int k = 0; k < kFinPer; ++k) {
+  for (int k = 0; k < PER; ++k) {
     const int e = tid + kFinThreads * k;
     key[k] = 0u;
     jj[k] = -1;
     if (e < total) {
-      const int2 x = crow[e];
+      const int2 x = raw[k];
       if (x.y >= 0 && x.y <= i) {   // always, for lists the candidate kernel wrote
         key[k] = order_key(__int_as_float(x.x));
         jj[k] = x.y;
@@ -471,7 +546,7 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
       for (int q = tid; q < nb; q += kFinThreads) sh.hist[q] = 0u;
       __syncthreads();
 #pragma unroll
-      for (int k = 0; k < kFinPer; ++k)
+      for (int k = 0; k < PER; ++k)
         if (jj[k] >= 0 && (key[k] & pmask) == pfx) atomicAdd(&sh.hist[(key[k] >> shift) & (nb - 1)], 1u);
       __syncthreads();
       fin_find_bin(sh, nb, need);
@@ -493,12 +568,12 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
     for (int q = tid; q < nw; q += kFinThreads) aux[q] = 0u;
     __syncthreads();
 #pragma unroll
-    for (int k = 0; k < kFinPer; ++k)
+    for (int k = 0; k < PER; ++k)
       if (jj[k] >= 0 && key[k] == pfx) atomicOr(&aux[jj[k] >> 5], 1u << (jj[k] & 31));
     __syncthreads();
     word_prefix(sh, aux, bm, nw);   // bm holds the tie prefixes for now
 #pragma unroll
-    for (int k = 0; k < kFinPer; ++k) {
+    for (int k = 0; k < PER; ++k) {
       if (jj[k] >= 0 && key[k] == pfx) {
         const int j = jj[k];
         const int rank = (int)bm[j >> 5] + __popc(aux[j >> 5] & ((1u << (j & 31)) - 1u));
@@ -513,7 +588,7 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
   // mark the selected positions, then write them in ascending order
   uint32_t sel = 0u;
 #pragma unroll
-  for (int k = 0; k < kFinPer; ++k) {
+  for (int k = 0; k < PER; ++k) {
     if (jj[k] < 0) continue;
     bool take;
     if (all) take = true;
@@ -530,7 +605,7 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
   int32_t* orow = a.out_idx + (int64_t)row * a.B;
   float* osc = a.out_score ? a.out_score + (int64_t)row * a.B : nullptr;
 #pragma unroll
-  for (int k = 0; k < kFinPer; ++k) {
+  for (int k = 0; k < PER; ++k) {
     if (!((sel >> k) & 1u)) continue;
     const int j = jj[k];
     const int pos = (int)aux[j >> 5] + __popc(bm[j >> 5] & ((1u << (j & 31)) - 1u));
@@ -684,9 +759,12 @@ size_t prefill_topk_workspace(int L, int Hkv, int B) {
 
 hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s) {
   static const hipError_t attr = [] {
-    hipError_t e = hipFuncSetAttribute((const void*)prefill_final_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)prefill_final_kernel<16>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        (int)fin_lds(kSelectLdsMaxSlots));
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void*)prefill_final_kernel<kFinPerMax>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)fin_lds(kSelectLdsMaxSlots));
     if (e != hipSuccess) return e;
     e = hipFuncSetAttribute((const void*)prefill_redo_select_kernel,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)redo_lds(kSelectLdsMaxSlots));
@@ -703,8 +781,14 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s) {
                      ws.tau, ws.redo);
   hipLaunchKernelGGL(prefill_cand_kernel, dim3((a.L + kRowsA - 1) / kRowsA, a.Hkv), dim3(256), 0, s,
                      a, ws.tau, ws.cand, ws.cnt);
-  hipLaunchKernelGGL(prefill_final_kernel, dim3(rows), dim3(kFinThreads), fin_lds(a.L), s, a,
-                     ws.cand, ws.cnt, ws.redo);
+  // 16 register slots per thread hold 4096 candidates, twice a budget of
+  // 2048 (the sample aims at about 1.4 B); larger budgets take 32
+  if (a.B <= 2048)
+    hipLaunchKernelGGL(prefill_final_kernel<16>, dim3(rows), dim3(kFinThreads), fin_lds(a.L), s, a,
+                       ws.cand, ws.cnt, ws.redo);
+  else
+    hipLaunchKernelGGL(prefill_final_kernel<kFinPerMax>, dim3(rows), dim3(kFinThreads), fin_lds(a.L),
+                       s, a, ws.cand, ws.cnt, ws.redo);
   hipLaunchKernelGGL(prefill_redo_scores_kernel, dim3(kRedoBlocks, kRedoSlices), dim3(1024), 0, s, a,
                      ws.redo, ws.scratch);
   hipLaunchKernelGGL(prefill_redo_select_kernel, dim3(kRedoBlocks), dim3(kThreads), redo_lds(a.L), s,
