@@ -15,9 +15,11 @@
 //           stratified sample of at most 4096 keys of the causal prefix; per
 //           row, two 8-bit radix levels give a threshold tau that the sample
 //           says about B plus a 3.5-sigma margin of the row's keys reach;
-//   cand    per block of 128 query rows (4 waves x 32), all causal key tiles;
-//           each score >= tau of its row is appended, as (score bits, j), to
-//           the row's candidate list;
+//   cand    per block of 128 query rows (4 waves x 32) and one of two
+//           interleaved halves of its causal key tiles (two workgroups per
+//           block, so the longest blocks spread over two CUs); each score
+//           >= tau of its row is appended, as (score bits, j), to the row's
+//           sub-list for that half;
 //   final   per row: if the list did not overflow and holds at least
 //           min(B, i+1) entries, every key ranking above the B-th one is
 //           among them, so a radix select over them is exact; the positions
@@ -44,6 +46,8 @@ constexpr int kSampleMax = 4096; // sampled keys per block of 32 query rows
 constexpr int kHistLd = 257;     // padded histogram row: rows fall on different LDS banks
 constexpr int kRowsA = 128;      // query rows per candidate workgroup
 constexpr int kCandCap = 8192;   // candidate list entries per row
+constexpr int kSplit = 2;        // workgroups per block of rows, each with its own sub-list
+constexpr int kSubCap = kCandCap / kSplit;
 constexpr int kFinThreads = 256;
 constexpr int kFinPerMax = kCandCap / kFinThreads;  // candidates per thread, largest build (32)
 constexpr int kRedoBlocks = 256;
@@ -178,7 +182,8 @@ __device__ __forceinline__ void sample_find(SampleShared& sh, const int* tgts, i
 __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, float* tau,
                                                              int* redo) {
   __shared__ SampleShared sh;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int qt = blockIdx.x, g = blockIdx.y;
   const int i0 = qt * kT;
   if (qt == 0 && g == 0 && tid == 0) redo[0] = 0;   // the redo list starts empty
@@ -301,8 +306,12 @@ __global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, co
                                                            int2* cand, int* cnt) {
   __shared__ __align__(16) float stash[4][64][20];   // per wave, per lane: 16 scores (+pad)
   __shared__ int rcnt[kRowsA];                       // candidates appended per row
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
-  const int blk = gridDim.x - 1 - blockIdx.x;   // longest prefixes first
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
+  // kSplit workgroups share a block of rows: split s takes the groups of 4
+  // tiles whose index is s modulo kSplit and fills sub-list s of each row
+  const int job = gridDim.x - 1 - blockIdx.x;  // longest prefixes first
+  const int blk = job / kSplit, split = job % kSplit;
   const int g = blockIdx.y;
   const int r0 = blk * kRowsA;
   const int kend = min(a.L, r0 + kRowsA);      // keys [0, kend) reach some row here
@@ -317,7 +326,7 @@ __global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, co
 #pragma unroll
     for (int ch = 0; ch < kCh; ++ch) qb[b][ch] = frag(qp, ch, h);
     tq[b] = i < a.L ? tau[(int64_t)i * a.Hkv + g] : INFINITY;
-    list[b] = cand + ((int64_t)min(i, a.L - 1) * a.Hkv + g) * kCandCap;
+    list[b] = cand + ((int64_t)min(i, a.L - 1) * a.Hkv + g) * kCandCap + split * kSubCap;
   }
   __syncthreads();
   // Per tile: the four row blocks' MFMAs first (one wait for the tile's
@@ -325,19 +334,21 @@ __global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, co
   // one list; a lane reserves room for its candidates of the tile with one
   // LDS atomic and writes them as a contiguous run, so every row's list
   // grows at a single tail and the stores combine into full lines in L2.
+  constexpr int kStep = 4 * kSplit;            // tiles between a wave's consecutive tiles
+  const int t_first = 4 * split + w;
   bf16x8 ka[kCh];
   {
-    const uint16_t* kp = krow(a, g, min(w * kT + n, a.L - 1));
+    const uint16_t* kp = krow(a, g, min(t_first * kT + n, a.L - 1));
 #pragma unroll
     for (int ch = 0; ch < kCh; ++ch) ka[ch] = frag(kp, ch, h);
   }
-  for (int t = w; t * kT < kend; t += 4) {
+  for (int t = t_first; t * kT < kend; t += kStep) {
     const int j0 = t * kT;
     f32x16 acc[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[b] = tile_scores(ka, qb[b]);
-    if ((t + 4) * kT < kend) {
-      const uint16_t* kp = krow(a, g, min(j0 + 4 * kT + n, a.L - 1));
+    if ((t + kStep) * kT < kend) {
+      const uint16_t* kp = krow(a, g, min(j0 + kStep * kT + n, a.L - 1));
 #pragma unroll
       for (int ch = 0; ch < kCh; ++ch) ka[ch] = frag(kp, ch, h);
     }
@@ -366,7 +377,7 @@ __global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, co
         while (flags) {
           const int v = __ffs(flags) - 1;
           flags &= flags - 1;
-          if (pos < kCandCap)
+          if (pos < kSubCap)
             list[b][pos] = make_int2(__float_as_int(stash[w][lane][v]), j0 + tile_key(v, h));
           ++pos;
         }
@@ -374,7 +385,7 @@ __global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, co
     }
   }
   __syncthreads();
-  if (tid < kRowsA && r0 + tid < a.L) cnt[(int64_t)(r0 + tid) * a.Hkv + g] = rcnt[tid];
+  if (tid < kRowsA && r0 + tid < a.L) cnt[((int64_t)(r0 + tid) * a.Hkv + g) * kSplit + split] = rcnt[tid];
 }
 
 // ---------------------------------------------------------------------------
@@ -477,22 +488,33 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
   const int nv = i + 1;
   const int Bq = min(a.B, nv);
   const int nw = (nv + 31) >> 5;
-  // the first 3/4 of the register slots are read together with the count
+  // slot k reads sub-list k / kPer, entry tid + 256 (k mod kPer); the
+  // first 3/4 of each sub-list's slots are read together with the counts
   // (one memory latency; a typical list fills about that much), the rest
-  // only when the list is longer
-  constexpr int kSpec = PER * 3 / 4;
+  // only when the sub-list is longer
+  constexpr int kPer = PER / kSplit;
+  constexpr int kSpec = (kPer * 3 + 3) / 4;
   const int2* crow = cand + (int64_t)row * kCandCap;
   int2 raw[PER];
 #pragma unroll
-  for (int k = 0; k < kSpec; ++k) raw[k] = crow[tid + kFinThreads * k];
-  const int total = cnt[row];
-  if (total > kFinThreads * PER || total < Bq) {   // the threshold missed: recompute this row
+  for (int k = 0; k < PER; ++k)
+    if (k % kPer < kSpec) raw[k] = crow[(k / kPer) * kSubCap + tid + kFinThreads * (k % kPer)];
+  int tc[kSplit];
+  int total = 0, longest = 0;
+#pragma unroll
+  for (int q = 0; q < kSplit; ++q) {
+    tc[q] = cnt[(int64_t)row * kSplit + q];
+    total += tc[q];
+    longest = max(longest, tc[q]);
+  }
+  if (longest > kFinThreads * kPer || total < Bq) {   // the threshold missed: recompute this row
     if (tid == 0) redo[1 + atomicAdd(&redo[0], 1)] = row;
     return;
   }
 #pragma unroll
-  for (int k = kSpec; k < PER; ++k)
-    if (kFinThreads * k < total) raw[k] = crow[tid + kFinThreads * k];
+  for (int k = 0; k < PER; ++k)
+    if (k % kPer >= kSpec && kFinThreads * (k % kPer) < tc[k / kPer])
+      raw[k] = crow[(k / kPer) * kSubCap + tid + kFinThreads * (k % kPer)];
   for (int q = tid; q < nw; q += kFinThreads) bm[q] = 0u;
   if (tid == 0) {
     sh.kmin = 0xffffffffu;
@@ -504,10 +526,10 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
   uint32_t lo = 0xffffffffu, hi = 0u;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int e = tid + kFinThreads * k;
+    const int e = tid + kFinThreads * (k % kPer);
     key[k] = 0u;
     jj[k] = -1;
-    if (e < total) {
+    if (e < tc[k / kPer]) {
       const int2 x = raw[k];
       if (x.y >= 0 && x.y <= i) {   // always, for lists the candidate kernel wrote
         key[k] = order_key(__int_as_float(x.x));
@@ -632,7 +654,8 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
 // t = first + w, first + w + stride, ... (w its wave index).
 __device__ __forceinline__ void redo_row_scores(const PrefillTopkArgs& a, int row, float* srow,
                                                 int first, int stride) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, n = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, uniform
   const int i = row / a.Hkv, g = row % a.Hkv;
   bf16x8 qb[kCh];
   {
@@ -724,7 +747,7 @@ size_t prefill_layout(int L, int Hkv, void* base, PrefillWs* ws) {
   const size_t o_tau = off;
   off = align256(off + rows * sizeof(float));
   const size_t o_cnt = off;
-  off = align256(off + rows * sizeof(int));
+  off = align256(off + rows * kSplit * sizeof(int));
   const size_t o_redo = off;
   off = align256(off + (rows + 1) * sizeof(int));
   const size_t o_scr = off;
@@ -779,8 +802,8 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s) {
   const int rows = a.L * a.Hkv;
   hipLaunchKernelGGL(prefill_sample_kernel, dim3((a.L + kT - 1) / kT, a.Hkv), dim3(256), 0, s, a,
                      ws.tau, ws.redo);
-  hipLaunchKernelGGL(prefill_cand_kernel, dim3((a.L + kRowsA - 1) / kRowsA, a.Hkv), dim3(256), 0, s,
-                     a, ws.tau, ws.cand, ws.cnt);
+  hipLaunchKernelGGL(prefill_cand_kernel, dim3((a.L + kRowsA - 1) / kRowsA * kSplit, a.Hkv),
+                     dim3(256), 0, s, a, ws.tau, ws.cand, ws.cnt);
   // 16 register slots per thread hold 4096 candidates, twice a budget of
   // 2048 (the sample aims at about 1.4 B); larger budgets take 32
   if (a.B <= 2048)
