@@ -1,0 +1,429 @@
+// Prefill indexed attention on the matrix cores (JSSA, "Joint Subspace
+// Sparse Attention for Efficient Long-Context Decoding": Fig. 1 -- a KV
+// head's query heads attend to its selected positions; Key contributions
+// -- the selected rows are read in place from the standard GQA cache).
+//
+// Shape served: prefill, G = 8 query heads per KV head, head_dim 128, bf16.
+// One wave owns 32 MFMA rows: the 8 heads of one token (rows 8..31 idle)
+// when every token has its own selection, or the 8 heads of 4 tokens when a
+// selection is shared by a block of tokens (then a workgroup of 4 waves
+// serves 16 tokens of the block and gathers each key chunk once for all of
+// them). Keys go by in chunks of 32 selected positions:
+//   gather   the chunk's K rows into LDS row-major and its V rows transposed
+//            (channel-major), so both are MFMA B operands read with 16-byte
+//            LDS loads; the next chunk's rows are in flight meanwhile;
+//   QK       S[32 rows x 32 keys] = Q K^T, 8 v_mfma_f32_32x32x16_bf16;
+//   softmax  causal and list masks, scale, running row max (log2 domain),
+//            p = exp2(s - m) rounded to bf16 into LDS for the PV operand;
+//            the row sum stays a per-lane partial until the end;
+//   PV       O[32 x 128] += P V, 8 more MFMAs, O rescaled by the max step.
+// Accumulation is fp32 throughout. p enters the PV product as two bf16
+// terms, hi = bf16(p) and lo = bf16(p - hi), so its operand error is about
+// 2^-17 relative instead of bf16's 2^-9 (one more MFMA per PV step).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace lsa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kD = 128;          // head_dim
+constexpr int kG = 8;            // query heads per KV head
+constexpr int kKC = 32;          // keys per chunk
+constexpr int kVLd = 40;         // LDS V^T row (one channel): 32 bf16 + 8 pad (80 B)
+constexpr int kPLd = 40;         // LDS P row: 32 bf16 + 8 pad
+constexpr int kWaveBytes = (kD * kVLd + 2 * kKC * kPLd) * 2;   // per wave: V^T, P hi, P lo
+constexpr float kLn2f = 0.69314718055994530942f;
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);   // x is finite
+}
+// p as hi + lo bf16 terms (p finite, >= 0)
+__device__ __forceinline__ void split_bf16(float p, uint16_t& hi, uint16_t& lo) {
+  hi = f32_to_bf16_rne(p);
+  lo = f32_to_bf16_rne(p - __uint_as_float((uint32_t)hi << 16));
+}
+
+// TPW tokens per wave (1: per-token selections; 4: block-shared), NW waves
+// per workgroup. A workgroup serves the tokens [tok0, tok0 + TPW * NW) that
+// share index row `isel`.
+template <int TPW, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // per wave: V^T of the current chunk, then P
+  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + w * kWaveBytes);
+  uint16_t* sP = sV + kD * kVLd;
+  uint16_t* sPl = sP + kKC * kPLd;
+
+  // which tokens: per-token -> one workgroup per (token, KV head); block
+  // shared -> ceil(qblk / (TPW NW)) workgroups per (block, KV head)
+  const int g = blockIdx.y;
+  int tok0, isel, ntok;
+  if (TPW == 1) {
+    tok0 = blockIdx.x;
+    isel = tok0;
+    ntok = 1;
+  } else {
+    const int per_blk = (a.qblk + TPW * NW - 1) / (TPW * NW);
+    const int blk = blockIdx.x / per_blk, part = blockIdx.x % per_blk;
+    isel = blk;
+    tok0 = blk * a.qblk + part * TPW * NW;
+    ntok = min(min(TPW * NW, a.qblk - part * TPW * NW), a.rows - tok0);
+  }
+  const int32_t* ilist = a.idx + ((int64_t)isel * a.Hkv + g) * a.B;
+
+  // this wave's 32 rows: row r -> token w*TPW + r/8, head r%8 (TPW = 4);
+  // rows 0..7 -> heads of the one token (TPW = 1), rows 8..31 idle
+  bf16x8 qa[kD / 16];
+  {
+    const int r = n;
+    const int tt = TPW == 1 ? 0 : w * TPW + r / kG;
+    const bool live = (TPW == 1 ? r < kG : true) && tt < ntok;
+    const int64_t qoff = ((int64_t)(tok0 + (live ? tt : 0)) * a.Hq + (int64_t)g * kG + (r % kG)) * kD;
+    const uint16_t* qp = (const uint16_t*)a.q + qoff + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < kD / 16; ++c) {
+      u32x4 x = live ? *(const u32x4*)(qp + 16 * c) : u32x4{0u, 0u, 0u, 0u};
+      qa[c] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  // rows this lane holds in S and O (v = 0..15): 8(v/4) + 4hh + v%4; the
+  // token of row v is v/4 (TPW = 4) or 0 (TPW = 1, live for v < 4)
+  constexpr int kV = TPW == 1 ? 4 : 16;    // live row slots per lane
+  int ipos[kV];                            // each live row's token position (-1: none)
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    const int tt = TPW == 1 ? 0 : w * TPW + v / 4;
+    ipos[v] = tt < ntok ? tok0 + tt : -1;
+  }
+  if (TPW == 1) {   // idle rows 8..31 of P stay zero (their outputs are never written)
+    for (int e = lane; e < (kKC - kG) * kPLd; e += 64) sP[kG * kPLd + e] = sPl[kG * kPLd + e] = 0;
+  }
+
+  float m[kV], l[kV];
+  f32x16 o[kD / 32];
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    m[v] = -INFINITY;
+    l[v] = 0.f;
+  }
+#pragma unroll
+  for (int t = 0; t < kD / 32; ++t) o[t] = f32x16{};
+
+  const int nch = (a.B + kKC - 1) / kKC;
+  const int64_t tok_bytes = a.s_tok * 2;
+  const char* kb0 = (const char*)a.k + ((int64_t)g * a.s_head) * 2 + 16 * hh;
+  const char* vb0 = (const char*)a.v + ((int64_t)g * a.s_head) * 2 + 16 * hh;
+  const int tlim = a.T;
+  uint16_t* vT = sV + 8 * hh * kVLd + n;         // V^T: channel 8 hh, key n (+ 16 q channels)
+
+  // Lane (n, hh) reads key n's channels 16q + 8hh .. +7 (q < 8) of K and V:
+  // the K pieces are exactly this lane's MFMA B operand for QK (key n,
+  // 16-deep chunk q), so K never touches LDS; V goes through LDS
+  // transposed. kreg/vreg hold the next chunk while this one computes.
+  u32x4 kreg[8], vreg[8];
+  // key n of chunk c: its sequence position (-1: skipped -- list padding,
+  // outside [0, T), or a stale slot-table entry), after issuing its loads
+  auto fetch = [&](int c) -> int32_t {
+    const int e = c * kKC + n;
+    int32_t t = e < a.B ? ilist[e] : -1;
+    if (t < 0 || t >= tlim) t = -1;
+    int64_t row = t < 0 ? 0 : t;
+    if (a.slot && t >= 0) {
+      const int32_t pr = a.slot[t];
+      if (pr < 0 || pr >= a.n_rows_kv) t = -1;
+      row = t < 0 ? 0 : pr;
+    }
+    const char* kr = kb0 + row * tok_bytes;
+    const char* vr = vb0 + row * tok_bytes;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      kreg[q] = *(const u32x4*)(kr + 32 * q);
+      vreg[q] = *(const u32x4*)(vr + 32 * q);
+    }
+    return t;
+  };
+
+  int32_t posn = nch > 0 ? fetch(0) : -1;
+  for (int c = 0; c < nch; ++c) {
+    const int32_t pos = posn;   // key n of chunk c: its position in the sequence (-1: none)
+    // S = Q K^T over the chunk's 32 keys
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[q], __builtin_bit_cast(bf16x8, kreg[q]), s, 0, 0, 0);
+    // V^T of this chunk (the previous chunk's PV reads are done: same wave)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const uint32_t ww[4] = {vreg[q].x, vreg[q].y, vreg[q].z, vreg[q].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        vT[(16 * q + 2 * e) * kVLd] = (uint16_t)(ww[e] & 0xffffu);
+        vT[(16 * q + 2 * e + 1) * kVLd] = (uint16_t)(ww[e] >> 16);
+      }
+    }
+    if (c + 1 < nch) posn = fetch(c + 1);   // the next chunk's rows fly during softmax and PV
+    // masks and scale; O and l stay relative to a reference max m per row,
+    // raised (with a rescale of O and l) only when a score passes m + 8 in
+    // the log2 domain -- a few times per row -- so p = exp2(x - m) <= 256
+    // and the common chunk touches O only through the MFMA
+    const bool kvalid = pos >= 0;
+    float x[kV], mx[kV];
+    bool raise = false;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const bool ok = kvalid && pos <= ipos[v];
+      x[v] = ok ? s[v] * a.scale_log2 : -INFINITY;
+      raise |= x[v] > m[v] + 8.f || (m[v] == -INFINITY && x[v] != -INFINITY);
+    }
+    if (__builtin_amdgcn_ballot_w64(raise)) {
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        float mm = x[v];
+#pragma unroll
+        for (int off = 1; off < 32; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
+        mx[v] = fmaxf(m[v], mm);
+      }
+#pragma unroll
+      for (int v = 0; v < kV; ++v) {
+        const float alpha = mx[v] == -INFINITY || m[v] == -INFINITY ? 0.f : exp2f(m[v] - mx[v]);
+        l[v] *= alpha;
+#pragma unroll
+        for (int t = 0; t < kD / 32; ++t) o[t][v] *= alpha;
+        m[v] = mx[v];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+      const float p = m[v] == -INFINITY ? 0.f : exp2f(x[v] - m[v]);
+      l[v] += p;
+      const int r = 8 * (v >> 2) + 4 * hh + (v & 3);
+      split_bf16(p, sP[r * kPLd + n], sPl[r * kPLd + n]);
+    }
+    // O += P V (two 16-key halves of the chunk)
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc) {
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const u32x4*)(sP + n * kPLd + 16 * kc + 8 * hh));
+      const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(sPl + n * kPLd + 16 * kc + 8 * hh));
+#pragma unroll
+      for (int t = 0; t < kD / 32; ++t) {
+        const bf16x8 vb =
+            __builtin_bit_cast(bf16x8, *(const u32x4*)(sV + (32 * t + n) * kVLd + 16 * kc + 8 * hh));
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, vb, o[t], 0, 0, 0);
+      }
+    }
+  }
+
+  // row sums over the 32 key lanes, then out = O / L, lse = m + log2 L
+#pragma unroll
+  for (int v = 0; v < kV; ++v) {
+    float L = l[v];
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) L += __shfl_xor(L, off, 64);
+    const int r = 8 * (v >> 2) + 4 * hh + (v & 3);
+    const int tt = TPW == 1 ? 0 : w * TPW + v / 4;
+    if (ipos[v] < 0 || tt >= ntok) continue;
+    const int head = r % kG;
+    const int64_t oh = (int64_t)(tok0 + tt) * a.Hq + (int64_t)g * kG + head;
+    const bool empty = m[v] == -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kD / 32; ++t) a.out[oh * kD + 32 * t + n] = empty ? 0.f : o[t][v] / L;
+    if (n == 0 && a.lse) a.lse[oh] = empty ? -INFINITY : (m[v] + log2f(L)) * kLn2f;
+  }
+}
+
+// Per-token selections: one wave per (token, KV head) on 16x16x32 tiles:
+// rows = the 8 heads (+ 8 idle), columns = 16 keys. Lane l: A row / B
+// column / D column l % 16, operand k-elements 8 (l / 16) + e, D rows
+// 4 (l / 16) + v -- heads live in lanes 0..31. A 32-key chunk is two
+// 16-key column tiles for QK and one 32-deep step for PV.
+constexpr int kP16Ld = 40;   // LDS P row: 32 bf16 + 8 pad
+__global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) uint16_t sV[kD * kVLd];      // V^T of the chunk
+  __shared__ __align__(16) uint16_t sP[16 * kP16Ld];    // P hi (rows 8..15 stay zero)
+  __shared__ __align__(16) uint16_t sPl[16 * kP16Ld];   // P lo
+  const int lane = threadIdx.x, q4 = lane >> 4, c16 = lane & 15;
+  const int g = blockIdx.y;
+  const int tok = blockIdx.x;
+  const int32_t* ilist = a.idx + ((int64_t)tok * a.Hkv + g) * a.B;
+
+  // Q: row c16 = head c16 (< 8; idle rows are zero), channels 32c + 8 q4 ..
+  bf16x8 qa[kD / 32];
+  {
+    const bool live = c16 < kG;
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)tok * a.Hq + (int64_t)g * kG + (live ? c16 : 0)) * kD + 8 * q4;
+#pragma unroll
+    for (int c = 0; c < kD / 32; ++c) {
+      u32x4 x = live ? *(const u32x4*)(qp + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+      qa[c] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  for (int e = lane; e < 8 * kP16Ld; e += 64) sP[8 * kP16Ld + e] = sPl[8 * kP16Ld + e] = 0;
+
+  float m[4], l[4];   // rows 4 q4 + v (heads in lanes 0..31)
+  f32x4 o[kD / 16];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    m[v] = -INFINITY;
+    l[v] = 0.f;
+  }
+#pragma unroll
+  for (int t = 0; t < kD / 16; ++t) o[t] = f32x4{};
+
+  const int nch = (a.B + kKC - 1) / kKC;
+  const int64_t tok_bytes = a.s_tok * 2;
+  const char* kb0 = (const char*)a.k + ((int64_t)g * a.s_head) * 2 + 16 * q4;
+  const char* vb0 = (const char*)a.v + ((int64_t)g * a.s_head) * 2 + 16 * q4;
+  const int tlim = a.T;
+  // Lane (c16, q4) reads keys c16 and 16 + c16 of a chunk, channels
+  // 32c + 8 q4 .. +7 (c < 4): for K exactly its QK B operand (column
+  // tile, 32-deep step c); V goes to LDS transposed.
+  u32x4 kreg[2][4], vreg[2][4];
+  auto fetch = [&](int c, int32_t (&pos)[2]) {
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) {
+      const int e = c * kKC + 16 * tn + c16;
+      int32_t t = e < a.B ? ilist[e] : -1;
+      if (t < 0 || t >= tlim) t = -1;
+      int64_t row = t < 0 ? 0 : t;
+      if (a.slot && t >= 0) {
+        const int32_t pr = a.slot[t];
+        if (pr < 0 || pr >= a.n_rows_kv) t = -1;
+        row = t < 0 ? 0 : pr;
+      }
+      pos[tn] = t;
+      const char* kr = kb0 + row * tok_bytes;
+      const char* vr = vb0 + row * tok_bytes;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        kreg[tn][q] = *(const u32x4*)(kr + 64 * q);
+        vreg[tn][q] = *(const u32x4*)(vr + 64 * q);
+      }
+    }
+  };
+  int32_t posn[2] = {-1, -1};
+  if (nch > 0) fetch(0, posn);
+  for (int c = 0; c < nch; ++c) {
+    const int32_t pos0 = posn[0], pos1 = posn[1];
+    f32x4 s[2];
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) {
+      s[tn] = f32x4{};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        s[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q], __builtin_bit_cast(bf16x8, kreg[tn][q]), s[tn], 0, 0, 0);
+    }
+    // V^T of this chunk: key 16 tn + c16, channels 32q + 8 q4 + i
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t ww[4] = {vreg[tn][q].x, vreg[tn][q].y, vreg[tn][q].z, vreg[tn][q].w};
+        uint16_t* dst = sV + (32 * q + 8 * q4) * kVLd + 16 * tn + c16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          dst[(2 * i) * kVLd] = (uint16_t)(ww[i] & 0xffffu);
+          dst[(2 * i + 1) * kVLd] = (uint16_t)(ww[i] >> 16);
+        }
+      }
+    if (c + 1 < nch) fetch(c + 1, posn);   // the next chunk's rows fly during softmax and PV
+    // masks, scale; O and l relative to a reference max raised only when a
+    // score passes it by 8 (log2 domain), so p <= 256
+    const int i = tok;   // causal: positions up to the token's own
+    float x0[4], x1[4];
+    bool raise = false;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      x0[v] = (pos0 >= 0 && pos0 <= i) ? s[0][v] * a.scale_log2 : -INFINITY;
+      x1[v] = (pos1 >= 0 && pos1 <= i) ? s[1][v] * a.scale_log2 : -INFINITY;
+      const float xm = fmaxf(x0[v], x1[v]);
+      raise |= xm > m[v] + 8.f || (m[v] == -INFINITY && xm != -INFINITY);
+    }
+    if (__builtin_amdgcn_ballot_w64(raise && lane < 32)) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        float mm = fmaxf(x0[v], x1[v]);
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
+        const float mn = fmaxf(m[v], mm);
+        const float alpha = mn == -INFINITY || m[v] == -INFINITY ? 0.f : exp2f(m[v] - mn);
+        l[v] *= alpha;
+#pragma unroll
+        for (int t = 0; t < kD / 16; ++t) o[t][v] *= alpha;
+        m[v] = mn;
+      }
+    }
+    if (lane < 32) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p0 = m[v] == -INFINITY ? 0.f : exp2f(x0[v] - m[v]);
+        const float p1 = m[v] == -INFINITY ? 0.f : exp2f(x1[v] - m[v]);
+        l[v] += p0 + p1;
+        const int o16 = (4 * q4 + v) * kP16Ld + c16;
+        split_bf16(p0, sP[o16], sPl[o16]);
+        split_bf16(p1, sP[o16 + 16], sPl[o16 + 16]);
+      }
+    }
+    // O += P V: A = P (row c16, keys 8 q4 ..), B = V^T (channel 16t + c16)
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const u32x4*)(sP + c16 * kP16Ld + 8 * q4));
+    const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(sPl + c16 * kP16Ld + 8 * q4));
+#pragma unroll
+    for (int t = 0; t < kD / 16; ++t) {
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, *(const u32x4*)(sV + (16 * t + c16) * kVLd + 8 * q4));
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
+      o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[t], 0, 0, 0);
+    }
+  }
+
+  // heads 4 q4 + v (lanes 0..31): row sums over the 16 key lanes, out, lse
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float L = l[v];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) L += __shfl_xor(L, off, 64);
+    if (lane >= 32) continue;
+    const int head = 4 * q4 + v;
+    const int64_t oh = (int64_t)tok * a.Hq + (int64_t)g * kG + head;
+    const bool empty = m[v] == -INFINITY;
+#pragma unroll
+    for (int t = 0; t < kD / 16; ++t) a.out[oh * kD + 16 * t + c16] = empty ? 0.f : o[t][v] / L;
+    if (c16 == 0 && a.lse) a.lse[oh] = empty ? -INFINITY : (m[v] + log2f(L)) * kLn2f;
+  }
+}
+
+template <int TPW, int NW>
+hipError_t launch_mfma(const AttnArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)NW * kWaveBytes;
+  unsigned nx;
+  if (TPW == 1) {
+    nx = (unsigned)a.rows;
+  } else {
+    const int nsel = (a.rows + a.qblk - 1) / a.qblk;
+    nx = (unsigned)(nsel * ((a.qblk + TPW * NW - 1) / (TPW * NW)));
+  }
+  hipLaunchKernelGGL((attn_mfma_kernel<TPW, NW>), dim3(nx, (unsigned)a.Hkv), dim3(64 * NW), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool attention_mfma_supported(const AttnArgs& a, bool bf16) {
+  return bf16 && a.prefill && a.d == kD && a.Hq == kG * a.Hkv && a.B >= 1 && a.Hkv <= 65535 &&
+         a.rows <= 0x7fffffff;
+}
+
+hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s) {
+  if (a.qblk > 1) return launch_mfma<4, 4>(a, s);
+  hipLaunchKernelGGL(attn_mfma16_kernel, dim3((unsigned)a.rows, (unsigned)a.Hkv), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace lsa

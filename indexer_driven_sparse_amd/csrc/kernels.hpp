@@ -132,6 +132,10 @@ struct AttnArgs {
 void attention_plan(int rows, int Hkv, int G, int d, int B, int* splits, int* keys_per_split);
 size_t attention_workspace(int rows, int Hkv, int G, int d, int B);
 hipError_t launch_attention(const AttnArgs& a, bool q_bf16, bool kv_bf16, hipStream_t s);
+// Matrix-core path for prefill with 8 query heads per KV head, head_dim 128,
+// bf16 (no split partials, no workspace).
+bool attention_mfma_supported(const AttnArgs& a, bool bf16);
+hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s);
 bool attention_supported(int G, int d);
 
 // ----- setup -----------------------------------------------------------------

@@ -437,8 +437,11 @@ int lsa_indexed_attention(const lsa_attn_desc* d, void* ws, size_t ws_bytes, voi
   a.lse = d->lse;
   a.partial = (float*)ws;
   lsa::attention_plan(d->rows, d->n_kv_heads, a.Hq / a.Hkv, a.d, a.B, &a.splits, &a.keys_per_split);
-  hipError_t e = lsa::launch_attention(a, d->q_dtype == LSA_BF16, d->kv_dtype == LSA_BF16,
-                                       (hipStream_t)stream);
+  hipError_t e;
+  if (lsa::attention_mfma_supported(a, d->kv_dtype == LSA_BF16))
+    e = lsa::launch_attention_mfma(a, (hipStream_t)stream);
+  else
+    e = lsa::launch_attention(a, d->q_dtype == LSA_BF16, d->kv_dtype == LSA_BF16, (hipStream_t)stream);
   return e == hipSuccess ? LSA_OK : hip_fail(e);
 }
 
