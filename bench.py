@@ -329,13 +329,17 @@ def hierarchical_leg(torch, lsa, synth, pipeline, steps: int = 200) -> dict:
     nb = T // blk
     alg = (N * Hkv * nb * r * 2 + N * Hkv * Bc * blk * r * 2 + N * Hkv * B * 2 * d * 2
            + N * Hkv * (Bc + B) * 4 + N * Hq * d * (2 + 4))
-    planted = all(np.isin(case.planted[g], plan.idx[0, g].cpu().numpy()).all() for g in range(Hkv))
-    log(f"hierarchical: {us:.1f} us/step (warm), planted spans recovered: {planted}")
+    # planted tokens kept: coarse-to-fine is an approximation -- a span that
+    # only grazes a 64-token block barely moves that block's centroid
+    sel = plan.idx[0].cpu().numpy()
+    hit = sum(int(np.isin(case.planted[g], sel[g]).sum()) for g in range(Hkv))
+    tot = sum(len(case.planted[g]) for g in range(Hkv))
+    log(f"hierarchical: {us:.1f} us/step (warm), planted tokens kept {hit}/{tot}")
     return {"workload": "hierarchical decode, 1 sequence x 1048576 tokens, GQA 32/8, d=128, r=64, "
                         "block 64, top-128 blocks, top-2048, bf16, hot spans",
             "us_per_step": us, "steps_per_s": 1e6 / us, "algorithmic_bytes_per_step": alg,
             "hbm_frac": alg / (us * 1e-6) / (HBM_PEAK_GBPS * 1e9),
-            "planted_spans_recovered": bool(planted)}
+            "planted_tokens_kept": hit, "planted_tokens": tot}
 
 
 def main() -> int:
