@@ -154,6 +154,8 @@ def prefill_leg(torch, lsa, synth, runs: int = 5) -> dict:
             "indexer_mfma_peak_tflops": MFMA_BF16_PEAK / 1e12,
             "attention_us": t_att, "attention_selected_pairs": sel_pairs,
             "attention_tflops": sel_pairs * 4.0 * case.d / (t_att * 1e-6) / 1e12,
+            # each selected (row, key) gathers one K and one V row of d bf16
+            "attention_gather_GBps": sel_pairs // (case.Hq // Hkv) * 2 * case.d * 2 / (t_att * 1e-6) / 1e9,
             "parity_rows_identical": same, "parity_rows": len(rows),
             "parity_pass": ok == len(rows), "block_shared": block}
 
