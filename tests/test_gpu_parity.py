@@ -419,6 +419,57 @@ def test_attention_paged_stale_slots_are_skipped():
     np.testing.assert_allclose(lse, rlse, rtol=0, atol=LSE_ATOL)
 
 
+@pytest.mark.parametrize("rows,B", [(300, 77), (70, 1), (129, 33), (64, 64)])
+def test_attention_prefill_matrix_core_edges(rows, B):
+    """Prefill with 8 query heads per KV head and d = 128 runs on the matrix
+    cores: empty sets, -1 entries inside the list, entries past the cache,
+    entries after the row's own token (masked causally), and list lengths
+    that are not a multiple of the 32-key chunk."""
+    Hq, Hkv, T, d = 8, 1, rows, 128
+    q, K, V, idx = _attn_case(rows, Hq, Hkv, T, d, B, synth.BF16, seed=rows + B, prefill=True)
+    rng = np.random.default_rng(rows * B)
+    idx[0, 0, :] = -1                                         # row 0: empty set
+    if B > 2:
+        idx[rows // 2, 0, 1] = -1                             # a hole inside a list
+        idx[rows - 1, 0, 0] = T + 3                           # past the cache: skipped
+    fut = rng.integers(1, rows, size=min(8, rows - 1))        # future positions: masked
+    for i in fut:
+        idx[i - 1, 0, -1] = min(T - 1, i + 1 + int(rng.integers(0, 5)))
+    say("attention prefill matrix cores", rows, B)
+    ref, rlse = oracle.attention(q, K, V, idx, prefill=True)
+    out, lse = _run_attention(q, K, V, idx, "tok", True)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=ATTN_ATOL)
+    fin = np.isfinite(rlse)
+    assert np.array_equal(np.isneginf(lse), ~fin) and (out[~fin.any(axis=1)] == 0).all()
+    np.testing.assert_allclose(lse[fin], rlse[fin], rtol=0, atol=LSE_ATOL)
+
+
+@pytest.mark.parametrize("L,qb,B", [(1000, 50, 200), (257, 8, 64), (130, 130, 96)])
+def test_prefill_block_attention_matrix_core_shapes(L, qb, B):
+    """Block-shared selections on the matrix cores (8 heads, d = 128) with
+    blocks that are not a multiple of the 16 tokens a workgroup serves, a
+    block smaller than that, and a last partial block."""
+    Hq, Hkv, d = 8, 1, 128
+    rng = np.random.default_rng(L + qb + B)
+    q = synth.to_bf16_bits(rng.standard_normal((L, Hq, d)).astype(np.float32))
+    K = synth.to_bf16_bits(rng.standard_normal((1, L, Hkv, d)).astype(np.float32))
+    V = synth.to_bf16_bits(rng.standard_normal((1, L, Hkv, d)).astype(np.float32))
+    nb = (L + qb - 1) // qb
+    blk = np.full((nb, Hkv, B), -1, np.int32)
+    for b in range(nb):
+        hi = min(L, (b + 1) * qb)
+        c = min(B, hi)
+        blk[b, 0, :c] = np.sort(rng.choice(hi, c, replace=False))
+    say("prefill block attention matrix cores", L, qb, B)
+    out = torch.full((L, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((L, Hq), float("nan"), device="cuda")
+    lsa.lsa_indexed_attention(dev(q), dev(K), dev(V), dev(blk), out, lse=lse,
+                              mode=lsa.MODE_PREFILL_CAUSAL, query_block=qb)
+    ref, rlse = oracle.attention(q, K, V, blk, prefill=True, query_block=qb)
+    np.testing.assert_allclose(host(out), ref, rtol=0, atol=ATTN_ATOL)
+    np.testing.assert_allclose(host(lse), rlse, rtol=0, atol=LSE_ATOL)
+
+
 # --------------------------------------------------------------------------
 # whole decode step
 # --------------------------------------------------------------------------
