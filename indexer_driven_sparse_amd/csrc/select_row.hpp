@@ -202,6 +202,181 @@ constexpr int kSegUnits = kSegUnroll * kSegWaves;    // (loop step, wave) units,
 // bitmaps (GBM), the candidate map and the segment lists (PRE); srow holds
 // the row's scores and nv its valid length. smem_raw: sizeof(SelShared),
 // plus two bitmaps of n bits when !GBM.
+// Exact top-B of `total` (>= B) entries held in registers: thread t holds
+// entries i0 .. i0 + kPer - 1 (i0 = t * kPer) of a list in slot order, every
+// key of the list is >= t_lo and the largest is kmax. Radix levels of up to
+// 11 bits run below the common prefix of [t_lo, kmax] and stop as soon as
+// the B-th key's bin is taken whole; then the taken entries -- keys above
+// the bin and the first `nd` keys inside it, in slot order -- are written
+// in slot order with one packed prefix scan. Writes out_idx, out_score and
+// out_count (B). Every thread of the block must call it.
+template <bool CAND, int kPer>
+__device__ __forceinline__ void select_in_registers(const SelectArgs& a, SelShared& sh, int row,
+                                                    const int32_t* crow, const uint32_t (&key)[kPer],
+                                                    const float (&val)[kPer], const int32_t (&slot)[kPer],
+                                                    int i0, int total, uint32_t t_lo, uint32_t kmax) {
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  int fixed = t_lo == kmax ? 32 : __clz(t_lo ^ kmax);
+  uint32_t pre = fixed == 0 ? 0u : (t_lo & (~0u << (32 - fixed)));
+  int nd = B;
+  int lev = 0;
+  while (fixed < 32) {
+    const int width = min(11, 32 - fixed);
+    const int shift = 32 - fixed - width;
+    const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
+    const int nb = 1 << width;
+    uint32_t* h = lev == 0 ? sh.hist : reinterpret_cast<uint32_t*>(sh.cslot) + (lev - 1) * kBins;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (i0 + j < total && (key[j] & pmask) == pre) atomicAdd(&h[(key[j] >> shift) & (nb - 1)], 1u);
+    __syncthreads();
+    int tl;
+    find_bin(sh, h, nb, nd, &tl);
+    const int bin = sh.bin;
+    nd -= sh.above;
+    const int cnt_bin = (int)h[bin];
+    pre |= (uint32_t)bin << shift;
+    fixed += width;
+    ++lev;
+    if (cnt_bin == nd) break;   // the whole bin is taken
+  }
+  const uint32_t bmask = fixed >= 32 ? ~0u : (fixed == 0 ? 0u : (~0u << (32 - fixed)));
+  const uint32_t top = pre | ~bmask;
+  int na = 0, ni = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (i0 + j < total) {
+      na += key[j] > top;
+      ni += (key[j] & bmask) == pre;
+    }
+  }
+  int tot2;
+  const int pref = block_exclusive_scan<kThreads>(na | (ni << 16), sh.scan, &tot2);
+  int pa = pref & 0xffff, pi = pref >> 16;
+  int32_t* orow = a.out_idx + (int64_t)row * B;
+  float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (i0 + j >= total) continue;
+    int pos = -1;
+    if (key[j] > top) {
+      pos = pa + min(pi, nd);
+      ++pa;
+    } else if ((key[j] & bmask) == pre) {
+      if (pi < nd) pos = pa + pi;
+      ++pi;
+    }
+    if (pos >= 0) {
+      orow[pos] = slot_pos<CAND>(a, crow, slot[j]);
+      if (osc) osc[pos] = val[j];
+    }
+  }
+  if (tid == 0 && a.out_count) a.out_count[row] = B;
+}
+
+// Short rows (n <= kThreads * 8): every slot in registers, thread t holding
+// slots 8t .. 8t+7; invalid slots are dropped by a compaction in slot order
+// (one prefix scan), then the exact selection runs in registers. Returns
+// false (nothing written) when the row is longer.
+template <bool CAND>
+__device__ __forceinline__ bool select_short_row(const SelectArgs& a, SelShared& sh, int row,
+                                                 const float* srow, int64_t nv, const int32_t* crow) {
+  constexpr int kPer = 8;
+  if (nv > (int64_t)kThreads * kPer) return false;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int B = a.B;
+  const int s0 = tid * kPer;
+  float v[kPer];
+  if (s0 + kPer <= nv && (((uintptr_t)(srow + s0)) & 15u) == 0) {
+    const float4 x = *(const float4*)(srow + s0);
+    const float4 y = *(const float4*)(srow + s0 + 4);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w; v[4] = y.x; v[5] = y.y; v[6] = y.z; v[7] = y.w;
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = s0 + j < nv ? srow[s0 + j] : 0.f;
+  }
+  uint32_t ok = 0;
+  int mine = 0;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+  uint32_t k8[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    k8[j] = order_key(v[j]);
+    if (slot_ok<CAND>(a, crow, s0 + j, nv)) {
+      ok |= 1u << j;
+      ++mine;
+      lo = min(lo, k8[j]);
+      hi = max(hi, k8[j]);
+    }
+  }
+  // compact the valid slots, keeping slot order: thread t's entries start
+  // at the count of valid slots before it
+  if (tid == 0) {
+    sh.kmax = 0u;
+    sh.nsample = -1;           // reused below as the minimum key (0xffffffff as unsigned)
+  }
+  int total;
+  const int first = block_exclusive_scan<kThreads>(mine, sh.scan, &total);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+  }
+  if (lane == 0) {
+    atomicMax(&sh.kmax, hi);
+    atomicMin(reinterpret_cast<uint32_t*>(&sh.nsample), lo);
+  }
+  int32_t* orow = a.out_idx + (int64_t)row * B;
+  float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
+  if (total <= B) {   // every valid slot is taken, in slot order; pad
+    int pos = first;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (!((ok >> j) & 1u)) continue;
+      orow[pos] = slot_pos<CAND>(a, crow, s0 + j);
+      if (osc) osc[pos] = v[j];
+      ++pos;
+    }
+    for (int p = total + tid; p < B; p += kThreads) {
+      orow[p] = -1;
+      if (osc) osc[p] = -INFINITY;
+    }
+    if (tid == 0 && a.out_count) a.out_count[row] = total;
+    return true;
+  }
+  // the valid entries, compacted into the list layout select_in_registers
+  // expects (thread t: entries t*kPer ..), through the LDS key/slot lists
+  {
+    int pos = first;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (!((ok >> j) & 1u)) continue;
+      sh.ckey[pos] = __float_as_uint(v[j]);
+      sh.cslot[pos] = s0 + j;
+      ++pos;
+    }
+  }
+  __syncthreads();
+  uint32_t key[kPer];
+  float val[kPer];
+  int32_t slot[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = s0 + j;
+    val[j] = e < total ? __uint_as_float(sh.ckey[e]) : 0.f;
+    slot[j] = e < total ? sh.cslot[e] : 0;
+    key[j] = order_key(val[j]);
+  }
+  const uint32_t t_lo = (uint32_t)sh.nsample, kmax = sh.kmax;
+  __syncthreads();   // the refine histograms reuse cslot
+  for (int i = tid; i < 2 * kBins; i += kThreads) sh.cslot[i] = 0;
+  zero_hist(sh);
+  __syncthreads();
+  select_in_registers<CAND, kPer>(a, sh, row, crow, key, val, slot, s0, total, t_lo, kmax);
+  return true;
+}
+
 template <bool CAND, bool GBM, bool PRE>
 __device__ __forceinline__ void select_row(const SelectArgs& a, int row, const float* srow,
                                            int64_t nv, unsigned char* smem_raw) {
@@ -224,6 +399,9 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int row, const f
   // passes over the row walk block-uniform tiles of kThreads * 4 * kUnroll slots
   const int64_t tile = (int64_t)kThreads * 4 * kUnroll;
 
+  if constexpr (!PRE) {
+    if (select_short_row<CAND>(a, sh, row, srow, nv, crow)) return;
+  }
   zero_hist(sh);
   if constexpr (PRE) {
     // two more refine histograms, in the (still unused) slot list
@@ -311,67 +489,7 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int row, const f
         key[j] = order_key(val[j]);
         slot[j] = e.y;
       }
-      // radix levels below the common prefix of [t_lo, max key]; stop as
-      // soon as every key of the B-th key's bin is taken
-      const uint32_t kmax = sh.kmax;
-      int fixed = t_lo == kmax ? 32 : __clz(t_lo ^ kmax);
-      uint32_t pre = fixed == 0 ? 0u : (t_lo & (~0u << (32 - fixed)));
-      int nd = B;
-      int lev = 0;
-      while (fixed < 32) {
-        const int width = min(11, 32 - fixed);
-        const int shift = 32 - fixed - width;
-        const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
-        const int nb = 1 << width;
-        uint32_t* h = lev == 0 ? sh.hist : reinterpret_cast<uint32_t*>(sh.cslot) + (lev - 1) * kBins;
-#pragma unroll
-        for (int j = 0; j < kPer; ++j)
-          if (i0 + j < total && (key[j] & pmask) == pre) atomicAdd(&h[(key[j] >> shift) & (nb - 1)], 1u);
-        __syncthreads();
-        int tl;
-        find_bin(sh, h, nb, nd, &tl);
-        const int bin = sh.bin;
-        nd -= sh.above;
-        const int cnt_bin = (int)h[bin];
-        pre |= (uint32_t)bin << shift;
-        fixed += width;
-        ++lev;
-        if (cnt_bin == nd) break;   // the whole bin is taken
-      }
-      // taken: keys above the bin, and the first nd keys inside it (slot
-      // order); one packed scan gives both running counts
-      const uint32_t bmask = fixed >= 32 ? ~0u : (fixed == 0 ? 0u : (~0u << (32 - fixed)));
-      const uint32_t top = pre | ~bmask;
-      int na = 0, ni = 0;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if (i0 + j < total) {
-          na += key[j] > top;
-          ni += (key[j] & bmask) == pre;
-        }
-      }
-      int tot2;
-      const int pref = block_exclusive_scan<kThreads>(na | (ni << 16), sh.scan, &tot2);
-      int pa = pref & 0xffff, pi = pref >> 16;
-      int32_t* orow = a.out_idx + (int64_t)row * B;
-      float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
-#pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        if (i0 + j >= total) continue;
-        int pos = -1;
-        if (key[j] > top) {
-          pos = pa + min(pi, nd);
-          ++pa;
-        } else if ((key[j] & bmask) == pre) {
-          if (pi < nd) pos = pa + pi;
-          ++pi;
-        }
-        if (pos >= 0) {
-          orow[pos] = slot_pos<CAND>(a, crow, slot[j]);
-          if (osc) osc[pos] = val[j];
-        }
-      }
-      if (tid == 0 && a.out_count) a.out_count[row] = B;
+      select_in_registers<CAND, kPer>(a, sh, row, crow, key, val, slot, i0, total, t_lo, sh.kmax);
       return;
     }
     // the lists do not settle it: general path over the row
