@@ -158,10 +158,13 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[q], __builtin_bit_cast(bf16x8, kreg[q]), s, 0, 0, 0);
-    // V^T of this chunk (the previous chunk's PV reads are done: same wave)
+    // V^T of this chunk (the previous chunk's PV reads are done: same wave);
+    // a skipped key's row (row 0, or whatever a stale slot names) is zeroed,
+    // so its p = 0 never meets a NaN or Inf in the product
+    const uint32_t vkeep = pos >= 0 ? ~0u : 0u;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const uint32_t ww[4] = {vreg[q].x, vreg[q].y, vreg[q].z, vreg[q].w};
+      const uint32_t ww[4] = {vreg[q].x & vkeep, vreg[q].y & vkeep, vreg[q].z & vkeep, vreg[q].w & vkeep};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         vT[(16 * q + 2 * e) * kVLd] = (uint16_t)(ww[e] & 0xffffu);
@@ -321,12 +324,15 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
       for (int q = 0; q < 4; ++q)
         s[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q], __builtin_bit_cast(bf16x8, kreg[tn][q]), s[tn], 0, 0, 0);
     }
-    // V^T of this chunk: key 16 tn + c16, channels 32q + 8 q4 + i
+    // V^T of this chunk: key 16 tn + c16, channels 32q + 8 q4 + i; a skipped
+    // key's row is zeroed, so its p = 0 never meets a NaN or Inf
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t ww[4] = {vreg[tn][q].x, vreg[tn][q].y, vreg[tn][q].z, vreg[tn][q].w};
+        const uint32_t vkeep = (tn == 0 ? pos0 : pos1) >= 0 ? ~0u : 0u;
+        const uint32_t ww[4] = {vreg[tn][q].x & vkeep, vreg[tn][q].y & vkeep, vreg[tn][q].z & vkeep,
+                                vreg[tn][q].w & vkeep};
         uint16_t* dst = sV + (32 * q + 8 * q4) * kVLd + 16 * tn + c16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {

@@ -348,11 +348,13 @@ def test_attention_edge_entries():
 def _paged_pool(K, V, seed, spare=0.25):
     """Scatter a dense [S,T,Hkv,d] cache into a page-size-1 pool with the
     rows in random order; unused pool rows hold NaN, so reading one would
-    show. Returns the pool K/V [P,Hkv,d] and the slot table [S,T]."""
+    show. Pool row 0 is always unused: kernels that load a fixed row for a
+    skipped entry must keep its NaN out of the result. Returns the pool K/V
+    [P,Hkv,d] and the slot table [S,T]."""
     S, T, Hkv, d = K.shape
     rng = np.random.default_rng(seed)
     P = S * T + int(spare * S * T) + 1
-    rows = rng.permutation(P)[: S * T].astype(np.int32)
+    rows = (1 + rng.permutation(P - 1)[: S * T]).astype(np.int32)
     table = rows.reshape(S, T)
     Kp = np.full((P, Hkv, d), np.nan if K.dtype == np.float32 else 0x7fc0, K.dtype)
     Vp = Kp.copy()
@@ -468,6 +470,14 @@ def test_prefill_block_attention_matrix_core_shapes(L, qb, B):
     ref, rlse = oracle.attention(q, K, V, blk, prefill=True, query_block=qb)
     np.testing.assert_allclose(host(out), ref, rtol=0, atol=ATTN_ATOL)
     np.testing.assert_allclose(host(lse), rlse, rtol=0, atol=LSE_ATOL)
+    # the same through a page-size-1 pool: bit-identical
+    Kp, Vp, table = _paged_pool(K, V, seed=L)
+    out2 = torch.full((L, Hq, d), float("nan"), device="cuda")
+    lse2 = torch.full((L, Hq), float("nan"), device="cuda")
+    lsa.lsa_indexed_attention(dev(q), dev(Kp), dev(Vp), dev(blk), out2, lse=lse2,
+                              mode=lsa.MODE_PREFILL_CAUSAL, query_block=qb, slot_table=dev(table))
+    assert torch.equal(out2.view(torch.int32), out.view(torch.int32))
+    assert torch.equal(lse2.view(torch.int32), lse.view(torch.int32))
 
 
 # --------------------------------------------------------------------------
