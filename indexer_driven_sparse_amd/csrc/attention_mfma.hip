@@ -4,22 +4,27 @@
 // -- the selected rows are read in place from the standard GQA cache).
 //
 // Shape served: prefill, G = 8 query heads per KV head, head_dim 128, bf16.
-// One wave owns 32 MFMA rows: the 8 heads of one token (rows 8..31 idle)
-// when every token has its own selection, or the 8 heads of 4 tokens when a
-// selection is shared by a block of tokens (then a workgroup of 4 waves
-// serves 16 tokens of the block and gathers each key chunk once for all of
-// them). Keys go by in chunks of 32 selected positions:
-//   gather   the chunk's K rows into LDS row-major and its V rows transposed
-//            (channel-major), so both are MFMA B operands read with 16-byte
-//            LDS loads; the next chunk's rows are in flight meanwhile;
-//   QK       S[32 rows x 32 keys] = Q K^T, 8 v_mfma_f32_32x32x16_bf16;
-//   softmax  causal and list masks, scale, running row max (log2 domain),
-//            p = exp2(s - m) rounded to bf16 into LDS for the PV operand;
-//            the row sum stays a per-lane partial until the end;
-//   PV       O[32 x 128] += P V, 8 more MFMAs, O rescaled by the max step.
+// Two kernels:
+//   attn_mfma16_kernel  per-token selections: one wave per (token, KV head)
+//                       on 16x16x32 tiles, rows = the 8 heads (+8 idle);
+//   attn_mfma_kernel    selections shared by a block of tokens: a workgroup
+//                       of 4 waves serves 16 tokens of the block, each wave
+//                       32 rows (4 tokens x 8 heads) on 32x32x16 tiles.
+// Keys go by in chunks of 32 selected positions:
+//   gather   each lane loads its keys' K and V pieces; the K pieces are its
+//            QK B operand as loaded, V is transposed through LDS (channel-
+//            major) for the PV B operand; the next chunk's rows are in
+//            flight during the current chunk's softmax and PV;
+//   QK       S = Q K^T over the chunk's keys;
+//   softmax  causal and list masks, scale, log2 domain; O and the row sums
+//            stay relative to a reference max raised only when a score
+//            passes it by 8, so p <= 256 and most chunks touch O only
+//            through the MFMA; the row sum stays a per-lane partial;
+//   PV       O += P V.
 // Accumulation is fp32 throughout. p enters the PV product as two bf16
 // terms, hi = bf16(p) and lo = bf16(p - hi), so its operand error is about
-// 2^-17 relative instead of bf16's 2^-9 (one more MFMA per PV step).
+// 2^-17 relative instead of bf16's 2^-9 (one more MFMA per PV step). A
+// skipped key's V row is zeroed before the product.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -48,11 +53,12 @@ __device__ __forceinline__ void split_bf16(float p, uint16_t& hi, uint16_t& lo) 
   lo = f32_to_bf16_rne(p - __uint_as_float((uint32_t)hi << 16));
 }
 
-// TPW tokens per wave (1: per-token selections; 4: block-shared), NW waves
-// per workgroup. A workgroup serves the tokens [tok0, tok0 + TPW * NW) that
+// Block-shared selections: kTPW tokens per wave, kNW waves per workgroup; a
+// workgroup serves the tokens [tok0, tok0 + kTPW * kNW) of one block, which
 // share index row `isel`.
-template <int TPW, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
+constexpr int kTPW = 4, kNW = 4;
+__global__ __launch_bounds__(64 * kNW) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int TPW = kTPW, NW = kNW;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -61,30 +67,21 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
   uint16_t* sP = sV + kD * kVLd;
   uint16_t* sPl = sP + kKC * kPLd;
 
-  // which tokens: per-token -> one workgroup per (token, KV head); block
-  // shared -> ceil(qblk / (TPW NW)) workgroups per (block, KV head)
+  // ceil(qblk / (TPW NW)) workgroups per (block, KV head)
   const int g = blockIdx.y;
-  int tok0, isel, ntok;
-  if (TPW == 1) {
-    tok0 = blockIdx.x;
-    isel = tok0;
-    ntok = 1;
-  } else {
-    const int per_blk = (a.qblk + TPW * NW - 1) / (TPW * NW);
-    const int blk = blockIdx.x / per_blk, part = blockIdx.x % per_blk;
-    isel = blk;
-    tok0 = blk * a.qblk + part * TPW * NW;
-    ntok = min(min(TPW * NW, a.qblk - part * TPW * NW), a.rows - tok0);
-  }
+  const int per_blk = (a.qblk + TPW * NW - 1) / (TPW * NW);
+  const int blk = blockIdx.x / per_blk, part = blockIdx.x % per_blk;
+  const int isel = blk;
+  const int tok0 = blk * a.qblk + part * TPW * NW;
+  const int ntok = min(min(TPW * NW, a.qblk - part * TPW * NW), a.rows - tok0);
   const int32_t* ilist = a.idx + ((int64_t)isel * a.Hkv + g) * a.B;
 
-  // this wave's 32 rows: row r -> token w*TPW + r/8, head r%8 (TPW = 4);
-  // rows 0..7 -> heads of the one token (TPW = 1), rows 8..31 idle
+  // this wave's 32 rows: row r -> token w*TPW + r/8, head r%8
   bf16x8 qa[kD / 16];
   {
     const int r = n;
-    const int tt = TPW == 1 ? 0 : w * TPW + r / kG;
-    const bool live = (TPW == 1 ? r < kG : true) && tt < ntok;
+    const int tt = w * TPW + r / kG;
+    const bool live = tt < ntok;
     const int64_t qoff = ((int64_t)(tok0 + (live ? tt : 0)) * a.Hq + (int64_t)g * kG + (r % kG)) * kD;
     const uint16_t* qp = (const uint16_t*)a.q + qoff + 8 * hh;
 #pragma unroll
@@ -94,16 +91,13 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
     }
   }
   // rows this lane holds in S and O (v = 0..15): 8(v/4) + 4hh + v%4; the
-  // token of row v is v/4 (TPW = 4) or 0 (TPW = 1, live for v < 4)
-  constexpr int kV = TPW == 1 ? 4 : 16;    // live row slots per lane
+  // token of row v is v/4
+  constexpr int kV = 16;                   // row slots per lane
   int ipos[kV];                            // each live row's token position (-1: none)
 #pragma unroll
   for (int v = 0; v < kV; ++v) {
-    const int tt = TPW == 1 ? 0 : w * TPW + v / 4;
+    const int tt = w * TPW + v / 4;
     ipos[v] = tt < ntok ? tok0 + tt : -1;
-  }
-  if (TPW == 1) {   // idle rows 8..31 of P stay zero (their outputs are never written)
-    for (int e = lane; e < (kKC - kG) * kPLd; e += 64) sP[kG * kPLd + e] = sPl[kG * kPLd + e] = 0;
   }
 
   float m[kV], l[kV];
@@ -231,7 +225,7 @@ __global__ __launch_bounds__(64 * NW) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int off = 1; off < 32; off <<= 1) L += __shfl_xor(L, off, 64);
     const int r = 8 * (v >> 2) + 4 * hh + (v & 3);
-    const int tt = TPW == 1 ? 0 : w * TPW + v / 4;
+    const int tt = w * TPW + v / 4;
     if (ipos[v] < 0 || tt >= ntok) continue;
     const int head = r % kG;
     const int64_t oh = (int64_t)(tok0 + tt) * a.Hq + (int64_t)g * kG + head;
@@ -405,17 +399,11 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
   }
 }
 
-template <int TPW, int NW>
-hipError_t launch_mfma(const AttnArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)NW * kWaveBytes;
-  unsigned nx;
-  if (TPW == 1) {
-    nx = (unsigned)a.rows;
-  } else {
-    const int nsel = (a.rows + a.qblk - 1) / a.qblk;
-    nx = (unsigned)(nsel * ((a.qblk + TPW * NW - 1) / (TPW * NW)));
-  }
-  hipLaunchKernelGGL((attn_mfma_kernel<TPW, NW>), dim3(nx, (unsigned)a.Hkv), dim3(64 * NW), lds, s, a);
+hipError_t launch_mfma_blocks(const AttnArgs& a, hipStream_t s) {
+  const size_t lds = (size_t)kNW * kWaveBytes;
+  const int nsel = (a.rows + a.qblk - 1) / a.qblk;
+  const unsigned nx = (unsigned)(nsel * ((a.qblk + kTPW * kNW - 1) / (kTPW * kNW)));
+  hipLaunchKernelGGL(attn_mfma_kernel, dim3(nx, (unsigned)a.Hkv), dim3(64 * kNW), lds, s, a);
   return hipGetLastError();
 }
 
@@ -427,7 +415,7 @@ bool attention_mfma_supported(const AttnArgs& a, bool bf16) {
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s) {
-  if (a.qblk > 1) return launch_mfma<4, 4>(a, s);
+  if (a.qblk > 1) return launch_mfma_blocks(a, s);
   hipLaunchKernelGGL(attn_mfma16_kernel, dim3((unsigned)a.rows, (unsigned)a.Hkv), dim3(64), 0, s, a);
   return hipGetLastError();
 }
