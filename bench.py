@@ -236,6 +236,77 @@ def _time_us(torch, fn, n: int, warm: int = 10) -> float:
     return a.elapsed_time(b) / n * 1000.0
 
 
+def _cold_us(torch, fn, n: int, sweep_mib: int = 512) -> float:
+    """Median per-step time with the caches flushed before each step: a
+    sweep_mib read-modify-write of a scratch buffer (outside the events)
+    evicts the step's inputs from the 256 MB MALL and the L2s."""
+    stream = torch.cuda.current_stream()
+    scratch = torch.zeros(sweep_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    fn(0)
+    ts = []
+    for i in range(n):
+        scratch.add_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1000.0)
+    del scratch
+    return float(np.median(ts))
+
+
+def read_ceiling_leg(torch, lsa, mib: int = 1024, reps: int = 20) -> dict:
+    """The achievable streaming-read rate for scale: lsa_stream_read over one
+    of two alternating mib-MiB buffers (neither fits the MALL), 16-byte
+    nontemporal loads like the scoring stream."""
+    n = mib * (1 << 20) // 4
+    bufs = [torch.ones(n, dtype=torch.int32, device="cuda") for _ in range(2)]
+    sink = torch.zeros(lsa.STREAM_READ_SINK_WORDS, dtype=torch.int32, device="cuda")
+    us = _time_us(torch, lambda i: lsa.lsa_stream_read(bufs[i & 1], sink), reps, warm=4)
+    del bufs
+    torch.cuda.empty_cache()
+    gbps = n * 4 / (us * 1e-6) / 1e9
+    log(f"read ceiling (lsa_stream_read over {mib} MiB): {gbps:.0f} GB/s")
+    return {"kernel": f"lsa_stream_read over {mib} MiB", "GBps": gbps,
+            "frac_of_peak": gbps / HBM_PEAK_GBPS}
+
+
+def hitters_leg(torch, lsa, synth, pipeline, n_warm: int = 1000, n_cold: int = 50) -> dict:
+    """The 32K heavy-hitter decode step (1 sequence, GQA 32/8, 1% planted
+    positions per KV head, top-1024): warm (back-to-back, its 38 MB working
+    set resident in the MALL) and cold (caches flushed before each step);
+    every row's set checked against the oracle."""
+    case = synth.workload("decode_t32k_hitters")
+    N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
+    Q, W = to_dev(case.Q, torch), to_dev(case.W, torch)
+    K, V = to_dev(case.K, torch), to_dev(case.V, torch)
+    k_idx = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_project_keys(K, W, k_idx)
+    plan = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B)
+    warm = _time_us(torch, lambda i: plan.run(Q, W, k_idx, K, V), n_warm, warm=50)
+    cold = _cold_us(torch, lambda i: plan.run(Q, W, k_idx, K, V), n_cold)
+    plan.run(Q, W, k_idx, K, V)
+    torch.cuda.synchronize()
+    gidx, gout = plan.idx.cpu().numpy(), plan.out.cpu().numpy()
+    import oracle
+    ref_k = oracle.project_keys(case.K, case.W, oracle.BF16)
+    ref = oracle.decode_step(case.Q, case.W, ref_k, case.K, case.V, B)
+    same = int(sum(np.array_equal(gidx[0, g], ref["idx"][0, g]) for g in range(Hkv)))
+    err = float(np.abs(gout - ref["out"]).max())
+    alg = N * Hkv * T * r * 2 + N * Hkv * B * 2 * d * 2 + N * Hkv * B * 4 + N * Hq * d * 6 + N * Hkv * r * 4
+    log(f"heavy hitters 32K: warm {warm:.1f} us/step, cold {cold:.1f} us/step, "
+        f"oracle rows identical {same}/{Hkv}, max |out err| {err:.2e}")
+    return {"workload": "decode, 1 sequence x 32768 cached tokens, GQA 32/8, d=128, r=64, top-1024, "
+                        "bf16, 1% planted heavy hitters per KV head",
+            "warm_us_per_step": warm, "cold_us_per_step": cold,
+            "warm_steps_per_s": 1e6 / warm, "cold_steps_per_s": 1e6 / cold,
+            "algorithmic_bytes_per_step": alg,
+            "cold_hbm_frac": alg / (cold * 1e-6) / (HBM_PEAK_GBPS * 1e9),
+            "parity_rows_identical": same, "parity_rows": Hkv, "max_abs_out_err": err,
+            "parity_pass": same == Hkv and err <= 2e-3}
+
+
 def paged_leg(torch, plan, case, inst, Q, n: int = 200) -> dict:
     """Indexed attention of the headline step through a page-size-1 KV pool
     (the serving layout of LSA-L's configs): every cached row of every
@@ -306,7 +377,8 @@ def cross_layer_leg(torch, lsa, pipeline, case, inst, Q, W, steps: int,
 def hierarchical_leg(torch, lsa, synth, pipeline, steps: int = 200) -> dict:
     """Coarse-to-fine decode at T = 1048576 (1 sequence, GQA 32/8, block 64,
     top-128 blocks, top-2048): warm back-to-back steps (centroid scores,
-    block select, candidate scores, token select, attention)."""
+    block select, candidate scores, token select, attention), and cold steps
+    with the caches flushed before each."""
     case = synth.workload("hier_t1m")
     N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
     blk, Bc = case.block, case.B_coarse
@@ -328,6 +400,7 @@ def hierarchical_leg(torch, lsa, synth, pipeline, steps: int = 200) -> dict:
     b.record(stream)
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / steps * 1000.0
+    cold = _cold_us(torch, lambda i: plan.run(Q, W, k_idx, cent, K, V), 50)
     nb = T // blk
     alg = (N * Hkv * nb * r * 2 + N * Hkv * Bc * blk * r * 2 + N * Hkv * B * 2 * d * 2
            + N * Hkv * (Bc + B) * 4 + N * Hq * d * (2 + 4))
@@ -336,11 +409,12 @@ def hierarchical_leg(torch, lsa, synth, pipeline, steps: int = 200) -> dict:
     sel = plan.idx[0].cpu().numpy()
     hit = sum(int(np.isin(case.planted[g], sel[g]).sum()) for g in range(Hkv))
     tot = sum(len(case.planted[g]) for g in range(Hkv))
-    log(f"hierarchical: {us:.1f} us/step (warm), planted tokens kept {hit}/{tot}")
+    log(f"hierarchical: {us:.1f} us/step warm, {cold:.1f} us/step cold, planted tokens kept {hit}/{tot}")
     return {"workload": "hierarchical decode, 1 sequence x 1048576 tokens, GQA 32/8, d=128, r=64, "
                         "block 64, top-128 blocks, top-2048, bf16, hot spans",
             "us_per_step": us, "steps_per_s": 1e6 / us, "algorithmic_bytes_per_step": alg,
             "hbm_frac": alg / (us * 1e-6) / (HBM_PEAK_GBPS * 1e9),
+            "cold_us_per_step": cold, "cold_hbm_frac": alg / (cold * 1e-6) / (HBM_PEAK_GBPS * 1e9),
             "planted_tokens_kept": hit, "planted_tokens": tot}
 
 
@@ -360,6 +434,8 @@ def main() -> int:
                     help="skip the page-size-1 pool attention leg")
     ap.add_argument("--no-cross-layer", action="store_true",
                     help="skip the cross-layer index reuse leg")
+    ap.add_argument("--no-hitters", action="store_true",
+                    help="skip the 32K heavy-hitter decode leg (warm and cold)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="skip the causal prefill leg (L=65536 fused indexer + sparse attention)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -536,8 +612,15 @@ def main() -> int:
 
     prefill = None
     hier = None
-    if not (args.no_prefill and args.no_hierarchical):
+    hitters = None
+    ceiling = None
+    if not (args.no_prefill and args.no_hierarchical and args.no_hitters and args.no_stages):
         del inst, plan
+        torch.cuda.empty_cache()
+    if not args.no_stages:
+        ceiling = read_ceiling_leg(torch, lsa)
+    if not args.no_hitters:
+        hitters = hitters_leg(torch, lsa, synth, pipeline)
         torch.cuda.empty_cache()
     if not args.no_hierarchical:
         hier = hierarchical_leg(torch, lsa, synth, pipeline)
@@ -574,6 +657,8 @@ def main() -> int:
         "graph_replay": {"ms_per_step": graph_ms, "steps_per_s": 1000.0 / graph_ms,
                          "hbm_frac_end_to_end": step_bytes / (graph_ms * 1e-3) / (HBM_PEAK_GBPS * 1e9)},
         "stages": stages,
+        "read_ceiling": ceiling,
+        "heavy_hitters_32k": hitters,
         "fp8_cache": fp8,
         "paged_kv": paged,
         "cross_layer": cross,

@@ -359,6 +359,24 @@ typedef struct lsa_centroid_desc {
 int lsa_build_centroids(const lsa_centroid_desc* desc, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* lsa_stream_read (measurement)                                            */
+/* ------------------------------------------------------------------------ */
+/*
+ * A plain streaming read of `bytes` bytes at `buf`: the achievable HBM read
+ * bandwidth on this part, the reference beside the published peak for the
+ * memory-bound calls above (the scoring stream of lsa_index_score reads its
+ * projected-key cache the same way: 16-byte nontemporal loads). Not part of
+ * the method. buf: device memory, 16-byte aligned; bytes: a positive
+ * multiple of 16. sink: LSA_STREAM_READ_SINK_WORDS device uint32 words,
+ * all overwritten; the XOR of them all is the XOR of every 32-bit word of
+ * the buffer (which keeps the loads alive and makes the read checkable).
+ * Errors: LSA_ERR_INVALID_ARG for a null or misaligned pointer or a bad
+ * size.
+ */
+#define LSA_STREAM_READ_SINK_WORDS 8192
+int lsa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Helpers                                                                  */
 /* ------------------------------------------------------------------------ */
 const char* lsa_status_str(int status);   /* static string, never NULL */

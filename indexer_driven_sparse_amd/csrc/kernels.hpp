@@ -160,4 +160,10 @@ struct CentroidArgs {
 };
 hipError_t launch_centroids(const CentroidArgs& a, int dt, hipStream_t s);
 
+// Streaming read of bytes (a multiple of 16, 16-byte aligned) by
+// kStreamReadBlocks workgroups; sink[b] = the XOR of the 32-bit words
+// workgroup b read.
+constexpr unsigned kStreamReadBlocks = 8192;   // = LSA_STREAM_READ_SINK_WORDS
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t s);
+
 }  // namespace lsa

@@ -513,6 +513,16 @@ int lsa_build_centroids(const lsa_centroid_desc* d, void* stream) {
   return e == hipSuccess ? LSA_OK : hip_fail(e);
 }
 
+static_assert(lsa::kStreamReadBlocks == LSA_STREAM_READ_SINK_WORDS, "one sink word per workgroup");
+
+int lsa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || !al16(buf) || (uintptr_t)sink % 4 != 0)
+    return LSA_ERR_INVALID_ARG;
+  LSA_TRY(check_device());
+  hipError_t e = lsa::launch_stream_read(buf, bytes, sink, (hipStream_t)stream);
+  return e == hipSuccess ? LSA_OK : hip_fail(e);
+}
+
 const char* lsa_status_str(int status) {
   switch (status) {
     case LSA_OK: return "ok";

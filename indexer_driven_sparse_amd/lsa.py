@@ -101,6 +101,7 @@ _SIGS = {
     "lsa_score_hint_layout": (_I32, [_P, _P, _P]),
     "lsa_select_workspace_bytes": (_c.c_size_t, [_P]),
     "lsa_attention_workspace_bytes": (_c.c_size_t, [_P]),
+    "lsa_stream_read": (_I32, [_P, _c.c_size_t, _P, _P]),
     "lsa_status_str": (_c.c_char_p, [_I32]),
     "lsa_last_hip_error": (_I32, []),
     "lsa_abi_version": (_I32, []),
@@ -509,6 +510,21 @@ def lsa_project_keys(k: torch.Tensor, w: torch.Tensor, out: torch.Tensor, *, tok
     d.out = _ptr(out)
     d.out_stride_seq, d.out_stride_head, d.out_stride_tok = out.stride(0), out.stride(1), out.stride(2)
     _check("lsa_project_keys", _lib().lsa_project_keys(_c.byref(d), _stream(stream)))
+
+
+STREAM_READ_SINK_WORDS = 8192
+
+
+def lsa_stream_read(buf: torch.Tensor, sink: torch.Tensor, *, stream=None) -> None:
+    """Measurement helper: stream the bytes of a contiguous device tensor
+    (16-byte aligned, size a multiple of 16). sink: int32
+    [STREAM_READ_SINK_WORDS], overwritten; the XOR of its words is the XOR
+    of every 32-bit word of buf."""
+    if not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < STREAM_READ_SINK_WORDS:
+        raise ValueError("lsa_stream_read: contiguous buf and an int32 sink of "
+                         f"{STREAM_READ_SINK_WORDS} words are required")
+    nbytes = buf.numel() * buf.element_size()
+    _check("lsa_stream_read", _lib().lsa_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)))
 
 
 def lsa_build_centroids(k_idx: torch.Tensor, block: int, out: torch.Tensor, *, stream=None) -> None:

@@ -212,6 +212,16 @@ def test_setup_validation():
     assert lib.lsa_build_centroids(ctypes.byref(c), None) == INVALID
 
 
+def test_stream_read_validation():
+    lib = lsa._lib()
+    assert lib.lsa_stream_read(None, 1024, 0x2000, None) == INVALID
+    assert lib.lsa_stream_read(0x1000, 1024, None, None) == INVALID
+    assert lib.lsa_stream_read(0x1000, 0, 0x2000, None) == INVALID
+    assert lib.lsa_stream_read(0x1000, 1000, 0x2000, None) == INVALID     # not a multiple of 16
+    assert lib.lsa_stream_read(0x1008, 1024, 0x2000, None) == INVALID     # misaligned buffer
+    assert lib.lsa_stream_read(0x1000, 1024, 0x2002, None) == INVALID     # misaligned sink
+
+
 def test_binding_raises_on_bad_arguments():
     import torch
     k = torch.zeros(1, 1, 8, 48, dtype=torch.bfloat16)

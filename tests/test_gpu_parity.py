@@ -1087,6 +1087,19 @@ def test_hierarchical_decode(T):
 # the decode step captured in a HIP graph: every replay equals eager
 # --------------------------------------------------------------------------
 
+@pytest.mark.parametrize("nbytes", [16, 4096 * 16 + 48, 64 << 20])
+def test_stream_read_reads_every_word(nbytes):
+    # the bandwidth reference really reads the whole buffer: its sink words
+    # (all overwritten) fold to the XOR of the buffer's words
+    rng = np.random.default_rng(nbytes)
+    words = rng.integers(-2**31, 2**31, nbytes // 4, dtype=np.int64).astype(np.int32)
+    say("stream read", nbytes)
+    buf = dev(words)
+    sink = torch.full((lsa.STREAM_READ_SINK_WORDS,), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+    lsa.lsa_stream_read(buf, sink)
+    assert int(np.bitwise_xor.reduce(host(sink))) == int(np.bitwise_xor.reduce(words))
+
+
 def test_decode_step_graph_replay():
     from indexer_driven_sparse_amd import pipeline
     case = synth.workload("decode_t32k_hitters")
