@@ -482,7 +482,9 @@ __global__ __launch_bounds__(kFinThreads) void prefill_final_kernel(PrefillTopkA
   FinShared& sh = *reinterpret_cast<FinShared*>(smem);
   const int nw_max = (a.L + 31) >> 5;
   uint32_t* bm = reinterpret_cast<uint32_t*>(smem + sizeof(FinShared));   // selected
-  uint32_t* aux = bm + nw_max;                                            // ties, then prefixes
+  // ties, then prefixes: used only after the radix levels, so it shares the
+  // histogram's space when it fits (less LDS, more rows in flight per CU)
+  uint32_t* aux = nw_max <= kBins ? sh.hist : bm + nw_max;
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int i = row / a.Hkv;
   const int nv = i + 1;
@@ -764,7 +766,10 @@ size_t prefill_layout(int L, int Hkv, void* base, PrefillWs* ws) {
   return off;
 }
 
-size_t fin_lds(int L) { return sizeof(FinShared) + (size_t)2 * ((L + 31) / 32) * sizeof(uint32_t); }
+size_t fin_lds(int L) {
+  const size_t nw = (L + 31) / 32;
+  return sizeof(FinShared) + (nw <= (size_t)kBins ? 1 : 2) * nw * sizeof(uint32_t);
+}
 size_t redo_lds(int L) { return sizeof(SelShared) + (size_t)2 * ((L + 31) / 32) * sizeof(uint32_t); }
 
 }  // namespace
