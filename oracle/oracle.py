@@ -63,8 +63,12 @@ def build(force: bool = False) -> str:
 def _get():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB_PATH)
+        # LSA_ORACLE_LIB names another build of lsa_oracle.c (the sanitizer
+        # test loads one built with AddressSanitizer and UBSan)
+        path = os.environ.get("LSA_ORACLE_LIB")
+        if not path:
+            path = build()
+        lib = ctypes.CDLL(path)
         for name, (res, args) in _SIGS.items():
             fn = getattr(lib, name)
             fn.restype = res
