@@ -459,6 +459,10 @@ def main() -> int:
     t0 = time.time()
     case = synth.workload(WORKLOAD)
     log(f"generated inputs in {time.time() - t0:.1f}s")
+    # the record names its inputs: generator seed and a SHA-256 per array
+    inputs = {"generator": f"indexer_driven_sparse_amd.synth.workload({WORKLOAD!r})",
+              "seed": case.seed, "sha256": {k: hashlib.sha256(np.ascontiguousarray(getattr(case, k)).data).hexdigest()
+                                    for k in ("Q", "K", "V", "W")}}
     N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
 
     # two cache instances resident in HBM (identical content, distinct memory)
@@ -666,7 +670,10 @@ def main() -> int:
         "prefill": prefill,
         "cpu_baseline": cpu,
         "parity": parity,
+        "inputs": inputs,
         "device": dev_name,
+        "rocm": getattr(torch.version, "hip", None),
+        "host_cpu": platform.processor() or platform.machine(),
     }
     print(json.dumps(line), flush=True)
     return 0

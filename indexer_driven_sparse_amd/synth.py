@@ -66,6 +66,7 @@ class DecodeCase:
     planted: list | None = None   # per (n, g): sorted planted positions
     block: int = 64      # hierarchical block size
     B_coarse: int = 0    # hierarchical: blocks kept by the coarse pass (0 = flat)
+    seed: int = 0        # SeedSequence root of the draws
 
     @property
     def G(self) -> int:
@@ -122,7 +123,7 @@ def make_decode_case(N: int, Hq: int, Hkv: int, T: int, d: int = 128, r: int = 6
         V[n] = _encode(sv.standard_normal((T, Hkv, d), dtype=np.float32), dtype)
     return DecodeCase(name=name, N=N, Hq=Hq, Hkv=Hkv, T=T, d=d, r=r, B=B, dtype=dtype,
                       Q=_encode(Qf, dtype), K=K, V=V, W=W, planted=planted,
-                      B_coarse=B_coarse, block=block)
+                      B_coarse=B_coarse, block=block, seed=seed)
 
 
 @dataclasses.dataclass
