@@ -13,7 +13,8 @@
 //     (no LDS), and after LPK loads each lane owns one of 64 consecutive
 //     scores, so the fp32 score store is one coalesced 256-byte write;
 //   * the query prep (mean of the G heads, times W) runs at the top of each
-//     workgroup, so the step needs no separate launch for it.
+//     workgroup, so the step needs no separate launch for it, and its
+//     latency is hidden behind the workgroup's first cache loads.
 #include <algorithm>
 
 #include "common.hpp"
@@ -110,6 +111,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecode
   constexpr int kHintK = hint_k(DT);
   constexpr int E = 16 / ESZ;        // channels per lane
   constexpr int KPI = kWave / LPK;   // keys per wave-wide load
+  constexpr int64_t kStep = (int64_t)kGroupsInFlight * 4 * 64;   // slots per workgroup step
   __shared__ float s_qbar[kMaxD];
   __shared__ float s_part[kScoreThreads];
   __shared__ float s_q[kMaxR];
@@ -118,30 +120,91 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecode
   const int n = row / a.Hkv, g = row % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = a.r;
+  const int l = lane % LPK, kg = lane / LPK;
+
+  // this workgroup's chunk of slots
+  const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
+  const int64_t c1 = min((int64_t)a.n_out, c0 + a.chunk);
+  const char* kbase =
+      (const char*)a.k_idx + ((int64_t)n * a.ks_seq + (int64_t)g * a.ks_head) * ESZ + l * 16;
+  const int64_t tok_bytes = a.ks_tok * ESZ;
+  float* srow = a.scores + (int64_t)row * a.scores_ld;
+  const int32_t* crow = CAND ? a.cand + (int64_t)row * a.cand_ld : nullptr;
+
+  // one wave's loads of one step: kGroupsInFlight groups of 64 slots
+  uint4 raw[kGroupsInFlight][LPK];
+  bool ok[kGroupsInFlight][LPK];
+  auto issue_group = [&](int64_t gb, int u) {
+#pragma unroll
+    for (int it = 0; it < LPK; ++it) {
+      const int64_t slot = gb + (int64_t)u * 4 * 64 + it * KPI + kg;
+      bool valid = slot < c1;
+      int64_t pos = 0;
+      if (valid) {
+        pos = slot_position<CAND>(a, crow, slot);
+        valid = pos >= 0;
+      }
+      ok[u][it] = valid;
+      // unconditional load (row 0 stands in for a slot past the chunk or a
+      // missing position; its score is replaced by -inf below)
+      raw[u][it] = load_key16(kbase + (valid ? pos : 0) * tok_bytes);
+    }
+  };
 
   // ---- scoring preparation: q_idx = mean of the group's heads . W ----
-  // Thread (j, p) owns output channel j over input channels c = p + k*parts.
-  // Its W values are requested up front, before the query mean is formed, so
-  // the prologue costs about one memory round trip.
-  if (a.q != nullptr) {
-    const int G = a.Hq / a.Hkv;
-    const float* W = a.w + (a.w_per_head ? (int64_t)g * a.d * r : 0);
-    const int parts = kScoreThreads / r;  // r is a power of two <= 128
-    const int j = tid % r, p = tid / r;
-    constexpr int kPre = 32;
-    float wv[kPre];
+  // Vector loads complete in issue order, so the order of issue decides
+  // what the prep waits for: the prep's own loads (W: thread (j, p) owns
+  // output channel j over input channels c = p + k*parts; the query values,
+  // index clamped and value masked) go out first, then the first group of
+  // cache loads, and the prep's math waits only for its own loads while the
+  // cache loads are in flight. The empty asm statements keep the compiler
+  // from reordering the two batches.
+  const int64_t gfirst = c0 + (int64_t)wid * 64;
+  const bool prep = a.q != nullptr;
+  const int G = prep ? a.Hq / a.Hkv : 1;
+  const int parts = kScoreThreads / r;
+  const int j = tid % r, p = tid / r;
+  constexpr int kPre = 32;
+  float wv[kPre];
+  constexpr int kQG = 8;
+  uint32_t xbits[kQG];   // raw query bits, converted after the cache loads are issued
+  const float* W = prep ? a.w + (a.w_per_head ? (int64_t)g * a.d * r : 0) : nullptr;
+  if (prep) {
 #pragma unroll
-    for (int k = 0; k < kPre; ++k) {
-      const int c = p + k * parts;
-      wv[k] = c < a.d ? W[(int64_t)c * r + j] : 0.f;
+    for (int k = 0; k < kPre; ++k) wv[k] = W[(int64_t)min(p + k * parts, a.d - 1) * r + j];
+    const int cq = min(tid, a.d - 1);
+    const int64_t off0 = ((int64_t)n * a.Hq + (int64_t)g * G) * a.d + cq;
+    if (a.q_bf16) {
+#pragma unroll
+      for (int i = 0; i < kQG; ++i) xbits[i] = ((const uint16_t*)a.q)[off0 + (int64_t)min(i, G - 1) * a.d];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kQG; ++i) xbits[i] = ((const uint32_t*)a.q)[off0 + (int64_t)min(i, G - 1) * a.d];
     }
-    for (int c = tid; c < a.d; c += kScoreThreads) {
-      float s = 0.f;
+  }
+  asm volatile("" ::: "memory");
+  issue_group(gfirst, 0);   // unconditional: a wave past its chunk reads row 0, masked below
+  asm volatile("" ::: "memory");
+
+  if (prep) {
+    if (tid < a.d) {
+      float sq = 0.f;
+#pragma unroll
+      for (int i = 0; i < kQG; ++i)
+        if (i < G) sq += a.q_bf16 ? __uint_as_float(xbits[i] << 16) : __uint_as_float(xbits[i]);
+      const int64_t off0 = ((int64_t)n * a.Hq + (int64_t)g * G) * a.d + tid;
+      for (int i = kQG; i < G; ++i)
+        sq += a.q_bf16 ? bf16_to_f32(((const uint16_t*)a.q)[off0 + (int64_t)i * a.d])
+                       : ((const float*)a.q)[off0 + (int64_t)i * a.d];
+      s_qbar[tid] = sq / (float)G;
+    }
+    for (int c = kScoreThreads + tid; c < a.d; c += kScoreThreads) {
+      float sq = 0.f;
       for (int i = 0; i < G; ++i) {
         const int64_t off = ((int64_t)n * a.Hq + (int64_t)g * G + i) * a.d + c;
-        s += a.q_bf16 ? bf16_to_f32(((const uint16_t*)a.q)[off]) : ((const float*)a.q)[off];
+        sq += a.q_bf16 ? bf16_to_f32(((const uint16_t*)a.q)[off]) : ((const float*)a.q)[off];
       }
-      s_qbar[c] = s / (float)G;
+      s_qbar[c] = sq / (float)G;
     }
     __syncthreads();
     float acc = 0.f;
@@ -164,39 +227,15 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecode
   }
   __syncthreads();
 
-  const int l = lane % LPK, kg = lane / LPK;
   float qv[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) qv[e] = s_q[l * E + e];
 
-  // ---- stream this workgroup's chunk of slots ----
-  const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
-  const int64_t c1 = min((int64_t)a.n_out, c0 + a.chunk);
-  const char* kbase =
-      (const char*)a.k_idx + ((int64_t)n * a.ks_seq + (int64_t)g * a.ks_head) * ESZ + l * 16;
-  const int64_t tok_bytes = a.ks_tok * ESZ;
-  float* srow = a.scores + (int64_t)row * a.scores_ld;
-  const int32_t* crow = CAND ? a.cand + (int64_t)row * a.cand_ld : nullptr;
-
-  for (int64_t gb = c0 + (int64_t)wid * 64; gb < c1;
-       gb += (int64_t)kGroupsInFlight * 4 * 64) {
-    uint4 raw[kGroupsInFlight][LPK];
-    bool ok[kGroupsInFlight][LPK];
+  // ---- stream this workgroup's chunk ----
+  for (int64_t gb = gfirst; gb < c1; gb += kStep) {
 #pragma unroll
-    for (int u = 0; u < kGroupsInFlight; ++u) {
-#pragma unroll
-      for (int it = 0; it < LPK; ++it) {
-        const int64_t slot = gb + (int64_t)u * 4 * 64 + it * KPI + kg;
-        bool valid = slot < c1;
-        int64_t pos = 0;
-        if (valid) {
-          pos = slot_position<CAND>(a, crow, slot);
-          valid = pos >= 0;
-        }
-        ok[u][it] = valid;
-        raw[u][it] = valid ? load_key16(kbase + pos * tok_bytes) : make_uint4(0, 0, 0, 0);
-      }
-    }
+    for (int u = 0; u < kGroupsInFlight; ++u)   // the first step's group 0 is in flight already
+      if (gb != gfirst || u > 0) issue_group(gb, u);
     uint32_t hkey[kGroupsInFlight];
 #pragma unroll
     for (int u = 0; u < kGroupsInFlight; ++u) {
@@ -215,18 +254,18 @@ __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecode
       // selection hint of this wave's group of kGroupsInFlight*64 slots: the
       // largest 16-bit key prefix that at least kHintK of them reach, by
       // bisection with ballots (the same value on every lane)
-      uint32_t p = 0;
+      uint32_t hp = 0;
 #pragma unroll
       for (int bit = 15; bit >= 0; --bit) {
-        const uint32_t cand = (p | (1u << bit)) << 16;
+        const uint32_t cand = (hp | (1u << bit)) << 16;
         int cnt = 0;
 #pragma unroll
         for (int u = 0; u < kGroupsInFlight; ++u) cnt += __popcll(__ballot(hkey[u] >= cand));
-        if (cnt >= kHintK) p |= 1u << bit;
+        if (cnt >= kHintK) hp |= 1u << bit;
       }
       if (lane == 0) {
-        const int64_t step = (gb - (int64_t)wid * 64) / (kGroupsInFlight * 4 * 64);
-        a.hint[(int64_t)row * a.hint_ld + step * 4 + wid] = p << 16;
+        const int64_t step = (gb - (int64_t)wid * 64) / kStep;
+        a.hint[(int64_t)row * a.hint_ld + step * 4 + wid] = hp << 16;
       }
     }
   }
