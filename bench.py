@@ -133,6 +133,19 @@ def prefill_leg(torch, lsa, synth, runs: int = 5) -> dict:
         ok += int(len(rsel) == int((gv >= 0).sum()) and np.all(np.abs(s[sym] - s_b) <= tol))
     log(f"prefill: indexer {t_idx:.1f} us, attention {t_att:.1f} us, oracle rows {same}/{len(rows)} "
         f"identical, {ok}/{len(rows)} within the near-tie tolerance")
+    # the oracle's indexer on the host, on a bounded sample: 512 of the
+    # longest rows (their causal pairs, exact fp64 scores and top-B)
+    threads = len(os.sched_getaffinity(0))
+    oracle.set_threads(threads)
+    r0 = L - 512
+    t0 = time.time()
+    oracle.prefill_topk(case.q_idx, case.k_idx, B, row_begin=r0, row_end=L)
+    el = time.time() - t0
+    cpu_pairs = int(np.sum(np.arange(r0 + 1, L + 1, dtype=np.int64))) * Hkv
+    cpu = {"value": cpu_pairs / el, "unit": "causal pairs scored and selected/s", "cores": threads,
+           "kind": "oracle", "sample": f"rows {r0}..{L - 1} of the same workload ({cpu_pairs} causal pairs, "
+                                        f"fp64) in {el:.2f}s"}
+    log(f"prefill oracle: {cpu['value']:.3e} pairs/s on {threads} threads")
     # the same inputs with one selection per block of qb tokens
     del idx, osc, aws
     torch.cuda.empty_cache()
@@ -156,8 +169,9 @@ def prefill_leg(torch, lsa, synth, runs: int = 5) -> dict:
             "attention_tflops": sel_pairs * 4.0 * case.d / (t_att * 1e-6) / 1e12,
             # each selected (row, key) gathers one K and one V row of d bf16
             "attention_gather_GBps": sel_pairs // (case.Hq // Hkv) * 2 * case.d * 2 / (t_att * 1e-6) / 1e9,
+            "indexer_pairs_per_s": pairs / (t_idx * 1e-6),
             "parity_rows_identical": same, "parity_rows": len(rows),
-            "parity_pass": ok == len(rows), "block_shared": block}
+            "parity_pass": ok == len(rows), "block_shared": block, "cpu_baseline": cpu}
 
 
 def fp8_leg(torch, lsa, pipeline, case, inst, Q, W, steps: int, warmup: int) -> dict:
