@@ -96,49 +96,49 @@ __global__ __launch_bounds__(kSegThreads) void select_collect_kernel(SelectArgs 
   const float* srow = a.scores + (int64_t)row * a.scores_ld;
   const int32_t* crow = CAND ? a.cand + (int64_t)row * a.cand_ld : nullptr;
 
-  // 1. the hint loads go out first, then the segment's: vector loads
-  // complete in issue order, so the threshold search below waits only for
-  // the hints while the segment is in flight. Both batches are
-  // unconditional (indices clamped, values masked where used) so no branch
-  // makes the compiler wait for the whole batch.
+  // 1. the hint loads go out first (vector loads return in order, so the
+  // threshold search below then overlaps the segment's loads)
   const uint32_t* hrow = a.hint + (int64_t)row * a.hint_ld;
   const int m = (a.hint_count + 4 * kSegThreads - 1) / (4 * kSegThreads);
   const int ne = (a.hint_count + m - 1) / m;
   const int r = (a.B + m * a.hint_k - 1) / (m * a.hint_k);
   uint32_t p[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) p[q] = hrow[min((tid + q * kSegThreads) * m, a.hint_count - 1)];
-  asm volatile("" ::: "memory");
-  // the segment as 16-byte pieces; a piece past the valid slots re-reads the
-  // last valid piece of the row (in bounds: the row holds a multiple of 4
-  // slots) and its slots are masked by s < nv below
-  float v[4 * kSegUnroll];
-  const bool full = s0 + kSeg <= nv;
-  {
-    const float4* srow4 = reinterpret_cast<const float4*>(srow);
-    const int64_t last4 = (nv - 1) >> 2;
-#pragma unroll
-    for (int j = 0; j < kSegUnroll; ++j) {
-      const float4 x = srow4[min((s0 >> 2) + j * kSegThreads + tid, last4)];
-      v[4 * j] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
-    }
-  }
-  asm volatile("" ::: "memory");
-  if (m > 1) {   // long rows: fold m entries into their minimum (after the segment's loads)
+  if (m == 1) {   // plain loads, first used after the segment's loads are issued
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = tid + q * kSegThreads;
-      uint32_t val = p[q];
-      for (int mm = 1; mm < m; ++mm) {
+      p[q] = e < a.hint_count ? hrow[e] : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + q * kSegThreads;
+      uint32_t val = 0xffffffffu;
+      for (int mm = 0; mm < m; ++mm) {
         const int h = e * m + mm;
         val = min(val, h < a.hint_count ? hrow[h] : 0u);
       }
       p[q] = val;
     }
   }
+  float v[4 * kSegUnroll];
+  const bool full = s0 + kSeg <= nv;
+  if (full) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (tid + q * kSegThreads >= ne || (tid + q * kSegThreads) * m >= a.hint_count) p[q] = 0u;
+    for (int j = 0; j < kSegUnroll; ++j) {
+      const float4 x = *(const float4*)(srow + s0 + j * kSegThreads * 4 + tid * 4);
+      v[4 * j] = x.x; v[4 * j + 1] = x.y; v[4 * j + 2] = x.z; v[4 * j + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kSegUnroll; ++j)
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        v[4 * j + k] = srow[min(s0 + j * kSegThreads * 4 + tid * 4 + k, nv - 1)];
+    // keeps these clamped loads in this branch: merged with the branch
+    // above, every 128-bit load would become four 32-bit ones
+    asm volatile("" ::: "memory");
+  }
 
   // 2. t_lo from the hint (loaded above). Entry h vouches that hint_k valid
   // keys of its (disjoint) slot group reach it; folding m entries into
@@ -182,7 +182,7 @@ __global__ __launch_bounds__(kSegThreads) void select_collect_kernel(SelectArgs 
       if (!full) take = take && s < nv;
       if constexpr (CAND) take = take && slot_ok<CAND>(a, crow, s, nv);
       flags |= (uint32_t)take << (4 * j + k);
-      if (full || s < nv) vmax = fmaxf(vmax, v[4 * j + k]);   // an upper bound of the listed keys
+      vmax = fmaxf(vmax, v[4 * j + k]);   // an upper bound of the listed keys
     }
 
   // 4. ranks in slot order: unit (j, wave) holds 256 consecutive slots,
