@@ -249,7 +249,11 @@ size_t lsa_select_workspace_bytes(const lsa_select_desc* desc);
  * copy (JSSA Key contributions; Fig. 6). Online softmax with fp32
  * accumulation; idx entries of one row must be distinct. Long index lists
  * are split across workgroups and merged by log-sum-exp, which needs
- * workspace (lsa_attention_workspace_bytes).
+ * workspace (lsa_attention_workspace_bytes; it depends on the shape and
+ * dtypes only, not on pointer values). Decode in bf16 with head_dim 128 and
+ * 4 or 8 query heads per KV head runs on the matrix cores when q is 16-byte
+ * aligned; p then enters the P.V product as two bf16 terms (about 2^-17
+ * relative). Every other case runs on the vector units.
  *
  * Paged KV (page size 1, the KV-pool setting of LSA-L's serving configs,
  * "Their 42x decode speedup never compiled on my GPU", section "What their

@@ -307,12 +307,33 @@ hipError_t launch_g(const AttnArgs& a, int G, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  if (a.splits < 1 || a.splits > kMaxSplits) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(a.rows * a.Hkv));
+#define LSA_MERGE(GG, DD)                                                            \
+  if (G == GG && a.d == DD) {                                                        \
+    hipLaunchKernelGGL((attn_merge_kernel<GG, DD>), grid, dim3(GG * DD), 0, s, a);   \
+    return hipGetLastError();                                                        \
+  }
+  LSA_MERGE(4, 128)
+  LSA_MERGE(8, 128)
+#undef LSA_MERGE
+  return hipErrorInvalidValue;
+}
+
 bool attention_supported(int G, int d) {
   return (d == 64 || d == 128) && (G == 1 || G == 2 || G == 4 || G == 8);
 }
 
-void attention_plan(int rows, int Hkv, int G, int d, int B, int* splits, int* keys_per_split) {
+void attention_plan(int rows, int Hkv, int G, int d, int B, bool mfma_decode, int* splits,
+                    int* keys_per_split) {
   (void)d;
+  if (mfma_decode) {   // one workgroup per kDecodeSplit list entries
+    *keys_per_split = kDecodeSplit;
+    *splits = (B + kDecodeSplit - 1) / kDecodeSplit;
+    return;
+  }
   const int64_t units = (int64_t)rows * Hkv;
   const int unit_keys = kGroups * (G <= 4 ? 8 : 4);   // keys one workgroup covers per step
   int max_splits = min(kMaxSplits, (B + unit_keys - 1) / unit_keys);
@@ -325,9 +346,9 @@ void attention_plan(int rows, int Hkv, int G, int d, int B, int* splits, int* ke
   *keys_per_split = kps;
 }
 
-size_t attention_workspace(int rows, int Hkv, int G, int d, int B) {
+size_t attention_workspace(int rows, int Hkv, int G, int d, int B, bool mfma_decode) {
   int sp, kps;
-  attention_plan(rows, Hkv, G, d, B, &sp, &kps);
+  attention_plan(rows, Hkv, G, d, B, mfma_decode, &sp, &kps);
   if (sp == 1) return 0;
   return (size_t)rows * Hkv * sp * G * (d + 2) * sizeof(float);
 }

@@ -3,13 +3,16 @@
 // head's query heads attend to its selected positions; Key contributions
 // -- the selected rows are read in place from the standard GQA cache).
 //
-// Shape served: prefill, G = 8 query heads per KV head, head_dim 128, bf16.
-// Two kernels:
+// Shapes served: bf16, head_dim 128; prefill with G = 8 query heads per KV
+// head, decode with G = 4 or 8. Three kernels:
 //   attn_mfma16_kernel  per-token selections: one wave per (token, KV head)
 //                       on 16x16x32 tiles, rows = the 8 heads (+8 idle);
 //   attn_mfma_kernel    selections shared by a block of tokens: a workgroup
 //                       of 4 waves serves 16 tokens of the block, each wave
-//                       32 rows (4 tokens x 8 heads) on 32x32x16 tiles.
+//                       32 rows (4 tokens x 8 heads) on 32x32x16 tiles;
+//   attn_decode_mfma_kernel  decode: a workgroup of 4 waves per (sequence,
+//                       KV head, split of 128 entries), one 32-key chunk per
+//                       wave, combined in LDS into a split partial.
 // Keys go by in chunks of 32 selected positions:
 //   gather   each lane loads its keys' K and V pieces; the K pieces are its
 //            QK B operand as loaded, V is transposed through LDS (channel-
@@ -34,6 +37,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// 128-bit reads of LDS tiles that were stored 16 bits at a time: the type
+// aliases anything, so the compiler keeps them after those stores
+typedef uint32_t lds_x4 __attribute__((ext_vector_type(4), __may_alias__));
 
 constexpr int kD = 128;          // head_dim
 constexpr int kG = 8;            // query heads per KV head
@@ -206,12 +212,12 @@ __global__ __launch_bounds__(64 * kNW) void attn_mfma_kernel(AttnArgs a) {
     // O += P V (two 16-key halves of the chunk)
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc) {
-      const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const u32x4*)(sP + n * kPLd + 16 * kc + 8 * hh));
-      const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(sPl + n * kPLd + 16 * kc + 8 * hh));
+      const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sP + n * kPLd + 16 * kc + 8 * hh));
+      const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sPl + n * kPLd + 16 * kc + 8 * hh));
 #pragma unroll
       for (int t = 0; t < kD / 32; ++t) {
         const bf16x8 vb =
-            __builtin_bit_cast(bf16x8, *(const u32x4*)(sV + (32 * t + n) * kVLd + 16 * kc + 8 * hh));
+            __builtin_bit_cast(bf16x8, *(const lds_x4*)(sV + (32 * t + n) * kVLd + 16 * kc + 8 * hh));
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, o[t], 0, 0, 0);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, vb, o[t], 0, 0, 0);
       }
@@ -373,11 +379,11 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
       }
     }
     // O += P V: A = P (row c16, keys 8 q4 ..), B = V^T (channel 16t + c16)
-    const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const u32x4*)(sP + c16 * kP16Ld + 8 * q4));
-    const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const u32x4*)(sPl + c16 * kP16Ld + 8 * q4));
+    const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sP + c16 * kP16Ld + 8 * q4));
+    const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sPl + c16 * kP16Ld + 8 * q4));
 #pragma unroll
     for (int t = 0; t < kD / 16; ++t) {
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, *(const u32x4*)(sV + (16 * t + c16) * kVLd + 8 * q4));
+      const bf16x8 vb = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sV + (16 * t + c16) * kVLd + 8 * q4));
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[t], 0, 0, 0);
     }
@@ -399,6 +405,175 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
   }
 }
 
+// Decode on the matrix cores: a workgroup of 4 waves per (sequence, KV
+// head, split of 128 list entries), one wave per 32 of them, on the
+// 16x16x32 tiles and lane layouts of the per-token kernel above (rows = the
+// GL heads of the group, the rest idle; columns = 16 keys). Each wave
+// gathers its 32 keys' K and V rows (one round trip), computes S = Q K^T,
+// its chunk's softmax relative to the chunk's max, and O = P V with p as
+// hi + lo bf16 terms; the 4 waves' (max, sum, O) are combined through LDS
+// into the split partial that the merge kernel combines by log-sum-exp.
+constexpr int kDecWaves = 4;
+template <int GL>
+__global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnArgs a) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) uint16_t sVall[kDecWaves][kD * kVLd];     // V^T of the chunk, then the wave's partial
+  __shared__ __align__(16) uint16_t sPall[kDecWaves][16 * kP16Ld];   // P hi (rows >= 8 stay zero)
+  __shared__ __align__(16) uint16_t sPlall[kDecWaves][16 * kP16Ld];  // P lo
+  const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4, c16 = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* sV = sVall[w];
+  uint16_t* sP = sPall[w];
+  uint16_t* sPl = sPlall[w];
+  const int split = (int)(blockIdx.x % a.splits);
+  const int64_t rowg = blockIdx.x / a.splits;
+  const int g = (int)(rowg % a.Hkv), row = (int)(rowg / a.Hkv);
+  const int e0 = split * (kDecWaves * kKC) + w * kKC;   // this wave's first list entry
+  const int32_t* ilist = a.idx + rowg * a.B;
+
+  // list entries and rows first (lane (c16, q4): keys c16 and 16 + c16,
+  // channels 32q + 8 q4 .. +7 of each), so the gather starts at once
+  int32_t pos[2];
+  u32x4 kreg[2][4], vreg[2][4];
+  const int64_t tok_bytes = a.s_tok * 2;
+  const int64_t base = ((int64_t)row * a.s_seq + (int64_t)g * a.s_head) * 2 + 16 * q4;
+  const int32_t* tab = a.slot ? a.slot + (int64_t)row * a.slot_ld : nullptr;
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn) {
+    const int e = e0 + 16 * tn + c16;
+    int32_t t = e < a.B ? ilist[e] : -1;
+    if (t < 0 || t >= a.T) t = -1;
+    int64_t r = t < 0 ? 0 : t;
+    if (tab && t >= 0) {
+      const int32_t pr = tab[t];
+      if (pr < 0 || pr >= a.n_rows_kv) t = -1;
+      r = t < 0 ? 0 : pr;
+    }
+    pos[tn] = t;
+    const char* kr = (const char*)a.k + base + r * tok_bytes;
+    const char* vr = (const char*)a.v + base + r * tok_bytes;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      kreg[tn][q] = *(const u32x4*)(kr + 64 * q);
+      vreg[tn][q] = *(const u32x4*)(vr + 64 * q);
+    }
+  }
+  // Q: row c16 = head c16 (< GL; idle rows are zero), channels 32c + 8 q4 ..
+  bf16x8 qa[kD / 32];
+  {
+    const bool live = c16 < GL;
+    const uint16_t* qp = (const uint16_t*)a.q + ((int64_t)row * a.Hq + (int64_t)g * GL + (live ? c16 : 0)) * kD + 8 * q4;
+#pragma unroll
+    for (int c = 0; c < kD / 32; ++c) {
+      u32x4 x = live ? *(const u32x4*)(qp + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+      qa[c] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  for (int e = lane; e < 8 * kP16Ld; e += 64) sP[8 * kP16Ld + e] = sPl[8 * kP16Ld + e] = 0;
+
+  f32x4 s[2];
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn) {
+    s[tn] = f32x4{};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      s[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q], __builtin_bit_cast(bf16x8, kreg[tn][q]), s[tn], 0, 0, 0);
+  }
+  // V^T: key 16 tn + c16, channels 32q + 8 q4 + i; a skipped key's row is
+  // zeroed, so its p = 0 never meets a NaN or Inf
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t vkeep = pos[tn] >= 0 ? ~0u : 0u;
+      const uint32_t ww[4] = {vreg[tn][q].x & vkeep, vreg[tn][q].y & vkeep, vreg[tn][q].z & vkeep,
+                              vreg[tn][q].w & vkeep};
+      uint16_t* dst = sV + (32 * q + 8 * q4) * kVLd + 16 * tn + c16;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dst[(2 * i) * kVLd] = (uint16_t)(ww[i] & 0xffffu);
+        dst[(2 * i + 1) * kVLd] = (uint16_t)(ww[i] >> 16);
+      }
+    }
+  // softmax over the chunk, heads 4 q4 + v in lanes 0..31 (log2 domain)
+  float m[4], l[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const float x0 = pos[0] >= 0 ? s[0][v] * a.scale_log2 : -INFINITY;
+    const float x1 = pos[1] >= 0 ? s[1][v] * a.scale_log2 : -INFINITY;
+    float mm = fmaxf(x0, x1);
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
+    m[v] = mm;
+    const float p0 = mm == -INFINITY ? 0.f : exp2f(x0 - mm);
+    const float p1 = mm == -INFINITY ? 0.f : exp2f(x1 - mm);
+    l[v] = p0 + p1;
+    if (lane < 32) {
+      const int o16 = (4 * q4 + v) * kP16Ld + c16;
+      split_bf16(p0, sP[o16], sPl[o16]);
+      split_bf16(p1, sP[o16 + 16], sPl[o16 + 16]);
+    }
+  }
+  // O = P V: A = P (row c16, keys 8 q4 ..), B = V^T (channel 16t + c16)
+  const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sP + c16 * kP16Ld + 8 * q4));
+  const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sPl + c16 * kP16Ld + 8 * q4));
+  f32x4 o[kD / 16];
+#pragma unroll
+  for (int t = 0; t < kD / 16; ++t) {
+    const bf16x8 vb = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sV + (16 * t + c16) * kVLd + 8 * q4));
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, f32x4{}, 0, 0, 0);
+    o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[t], 0, 0, 0);
+  }
+  // this wave's (max, sum, O) of heads 4 q4 + v < GL into its own V^T space
+  // (its reads of V^T are done: a wave's LDS accesses execute in order)
+  float* wp = reinterpret_cast<float*>(sV);   // [GL][kD + 2]
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    float L = l[v];
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) L += __shfl_xor(L, off, 64);
+    const int head = 4 * q4 + v;
+    if (lane >= 32 || head >= GL) continue;
+    float* hp = wp + head * (kD + 2);
+    if (c16 == 0) {
+      hp[0] = m[v];
+      hp[1] = L;
+    }
+#pragma unroll
+    for (int t = 0; t < kD / 16; ++t) hp[2 + 16 * t + c16] = o[t][v];
+  }
+  __syncthreads();
+  // combine the waves: thread (head, channel) pairs, written as the split's partial
+  for (int e = tid; e < GL * kD; e += 64 * kDecWaves) {
+    const int h = e / kD, c = e % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < kDecWaves; ++q) M = fmaxf(M, reinterpret_cast<const float*>(sVall[q])[h * (kD + 2)]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int q = 0; q < kDecWaves; ++q) {
+        const float* hp = reinterpret_cast<const float*>(sVall[q]) + h * (kD + 2);
+        const float f = exp2f(hp[0] - M);
+        L += hp[1] * f;
+        O += hp[2 + c] * f;
+      }
+    }
+    if (a.splits == 1) {   // the whole list: the output itself
+      const int64_t oh = (int64_t)row * a.Hq + (int64_t)g * GL + h;
+      a.out[oh * kD + c] = M == -INFINITY ? 0.f : O / L;
+      if (c == 0 && a.lse) a.lse[oh] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2f;
+      continue;
+    }
+    float* pr = a.partial + ((rowg * a.splits + split) * GL + h) * (kD + 2);
+    pr[2 + c] = O;
+    if (c == 0) {
+      pr[0] = M;
+      pr[1] = L;
+    }
+  }
+}
+
 hipError_t launch_mfma_blocks(const AttnArgs& a, hipStream_t s) {
   const size_t lds = (size_t)kNW * kWaveBytes;
   const int nsel = (a.rows + a.qblk - 1) / a.qblk;
@@ -412,6 +587,25 @@ hipError_t launch_mfma_blocks(const AttnArgs& a, hipStream_t s) {
 bool attention_mfma_supported(const AttnArgs& a, bool bf16) {
   return bf16 && a.prefill && a.d == kD && a.Hq == kG * a.Hkv && a.B >= 1 && a.Hkv <= 65535 &&
          a.rows <= 0x7fffffff;
+}
+
+bool attention_decode_mfma_supported(int G, int d, int B, bool bf16) {
+  return bf16 && d == kD && (G == 4 || G == 8) && B >= 1 && (B + kDecodeSplit - 1) / kDecodeSplit <= 64;
+}
+
+hipError_t launch_attention_decode_mfma(const AttnArgs& a, hipStream_t s) {
+  static_assert(kDecodeSplit == kDecWaves * kKC, "a split is one 32-key MFMA step per wave");
+  const int G = a.Hq / a.Hkv;
+  const dim3 grid((unsigned)((int64_t)a.rows * a.Hkv * a.splits));
+  if (G == 4)
+    hipLaunchKernelGGL(attn_decode_mfma_kernel<4>, grid, dim3(64 * kDecWaves), 0, s, a);
+  else if (G == 8)
+    hipLaunchKernelGGL(attn_decode_mfma_kernel<8>, grid, dim3(64 * kDecWaves), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.splits == 1) return e;
+  return launch_attention_merge(a, s);
 }
 
 hipError_t launch_attention_mfma(const AttnArgs& a, hipStream_t s) {

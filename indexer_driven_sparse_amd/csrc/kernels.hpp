@@ -129,8 +129,16 @@ struct AttnArgs {
   int64_t slot_ld;
   int n_rows_kv;                     // rows addressable per sequence (T, or the pool size)
 };
-void attention_plan(int rows, int Hkv, int G, int d, int B, int* splits, int* keys_per_split);
-size_t attention_workspace(int rows, int Hkv, int G, int d, int B);
+// Decode on the matrix cores (bf16, d = 128, G = 4 or 8, at most 64
+// splits): one workgroup per split of kDecodeSplit list entries, writing a
+// split partial, merged by launch_attention_merge.
+constexpr int kDecodeSplit = 128;
+bool attention_decode_mfma_supported(int G, int d, int B, bool bf16);
+hipError_t launch_attention_decode_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s);
+void attention_plan(int rows, int Hkv, int G, int d, int B, bool mfma_decode, int* splits,
+                    int* keys_per_split);
+size_t attention_workspace(int rows, int Hkv, int G, int d, int B, bool mfma_decode);
 hipError_t launch_attention(const AttnArgs& a, bool q_bf16, bool kv_bf16, hipStream_t s);
 // Matrix-core path for prefill with 8 query heads per KV head, head_dim 128,
 // bf16 (no split partials, no workspace).

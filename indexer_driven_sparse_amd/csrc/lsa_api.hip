@@ -197,6 +197,18 @@ int validate_select(const lsa_select_desc* d, size_t* ws_need) {
 
 // ---------------------------------------------------------------------------
 // lsa_indexed_attention
+// Decode shapes the matrix cores take: bf16, d = 128, G = 4 or 8, and a
+// grid of 256-thread workgroups under 2^32 threads. The launch also wants
+// q 16-byte aligned (its rows are read 16 bytes at a time); the workspace
+// is sized for either path, so it depends on the shape alone.
+bool decode_mfma_shape(const lsa_attn_desc* d) {
+  if (d->mode != LSA_MODE_DECODE) return false;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (!lsa::attention_decode_mfma_supported(G, d->head_dim, d->topk, d->kv_dtype == LSA_BF16)) return false;
+  const int64_t splits = (d->topk + lsa::kDecodeSplit - 1) / lsa::kDecodeSplit;
+  return (int64_t)d->rows * d->n_kv_heads * splits < (int64_t{1} << 24);
+}
+
 // ---------------------------------------------------------------------------
 int validate_attn(const lsa_attn_desc* d, size_t* ws_need) {
   if (!d || d->struct_size != sizeof(lsa_attn_desc)) return LSA_ERR_INVALID_ARG;
@@ -218,9 +230,12 @@ int validate_attn(const lsa_attn_desc* d, size_t* ws_need) {
   if (d->query_block < 0 || (d->query_block > 1 && d->mode != LSA_MODE_PREFILL_CAUSAL))
     return LSA_ERR_INVALID_ARG;
   int sp, kps;
-  lsa::attention_plan(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, &sp, &kps);
+  lsa::attention_plan(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, false, &sp, &kps);
   if ((int64_t)d->rows * d->n_kv_heads * sp > INT_MAX) return LSA_ERR_UNSUPPORTED;
-  *ws_need = lsa::attention_workspace(d->rows, d->n_kv_heads, G, d->head_dim, d->topk);
+  size_t need = lsa::attention_workspace(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, false);
+  if (decode_mfma_shape(d))
+    need = std::max(need, lsa::attention_workspace(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, true));
+  *ws_need = need;
   return LSA_OK;
 }
 
@@ -436,9 +451,13 @@ int lsa_indexed_attention(const lsa_attn_desc* d, void* ws, size_t ws_bytes, voi
   a.out = d->out;
   a.lse = d->lse;
   a.partial = (float*)ws;
-  lsa::attention_plan(d->rows, d->n_kv_heads, a.Hq / a.Hkv, a.d, a.B, &a.splits, &a.keys_per_split);
+  const bool mfma_decode = decode_mfma_shape(d) && al16(d->q);
+  lsa::attention_plan(d->rows, d->n_kv_heads, a.Hq / a.Hkv, a.d, a.B, mfma_decode, &a.splits,
+                      &a.keys_per_split);
   hipError_t e;
-  if (lsa::attention_mfma_supported(a, d->kv_dtype == LSA_BF16))
+  if (mfma_decode)
+    e = lsa::launch_attention_decode_mfma(a, (hipStream_t)stream);
+  else if (lsa::attention_mfma_supported(a, d->kv_dtype == LSA_BF16))
     e = lsa::launch_attention_mfma(a, (hipStream_t)stream);
   else
     e = lsa::launch_attention(a, d->q_dtype == LSA_BF16, d->kv_dtype == LSA_BF16, (hipStream_t)stream);

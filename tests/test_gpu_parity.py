@@ -314,6 +314,10 @@ def _run_attention(q, K, V, idx, layout, prefill):
     (2, 8, 8, 999, 64, 77, synth.BF16, False, "tok", 0.9),
     (2, 16, 2, 999, 64, 77, synth.F32, False, "tok", 1.0),
     (5, 4, 4, 100, 128, 1, synth.BF16, False, "tok", 1.0),
+    (2, 16, 2, 3000, 128, 700, synth.BF16, False, "tok", 0.8),    # G = 8, ragged last split
+    (1, 8, 2, 20000, 128, 8192, synth.BF16, False, "tok", 1.0),  # the most splits on matrix cores
+    (1, 8, 2, 20000, 128, 8200, synth.BF16, False, "tok", 1.0),  # one split too many: vector path
+    (2, 8, 1, 500, 128, 1, synth.BF16, False, "tok", 1.0),       # G = 8, one entry
     (600, 8, 1, 600, 128, 256, synth.BF16, True, "tok", 1.0),
 ])
 def test_attention(rows, Hq, Hkv, T, d, B, dtype, prefill, layout, fill):
@@ -326,6 +330,24 @@ def test_attention(rows, Hq, Hkv, T, d, B, dtype, prefill, layout, fill):
     out, lse = _run_attention(q, K, V, idx, layout, prefill)
     np.testing.assert_allclose(out, ref, rtol=0, atol=ATTN_ATOL)
     np.testing.assert_allclose(lse, rlse, rtol=0, atol=LSE_ATOL)
+
+
+def test_attention_decode_unaligned_q():
+    # q 2 bytes past a 16-byte boundary: decode leaves the matrix-core path
+    # (which reads q rows 16 bytes at a time) for the vector one
+    rows, Hq, Hkv, T, d, B = 2, 8, 2, 3000, 128, 500
+    q, K, V, idx = _attn_case(rows, Hq, Hkv, T, d, B, synth.BF16, seed=11)
+    say("attention unaligned q")
+    ref, rlse = oracle.attention(q, K, V, idx)
+    flat = torch.empty(q.size + 1, dtype=torch.bfloat16, device="cuda")
+    qd = flat[1:].view(q.shape)
+    qd.copy_(dev(q))
+    assert qd.data_ptr() % 16 == 2
+    out = torch.full((rows, Hq, d), float("nan"), device="cuda")
+    lse = torch.full((rows, Hq), float("nan"), device="cuda")
+    lsa.lsa_indexed_attention(qd, dev(K), dev(V), dev(idx), out, lse=lse, mode=lsa.MODE_DECODE)
+    np.testing.assert_allclose(host(out), ref, rtol=0, atol=ATTN_ATOL)
+    np.testing.assert_allclose(host(lse), rlse, rtol=0, atol=LSE_ATOL)
 
 
 def test_attention_edge_entries():
