@@ -53,6 +53,41 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
   const uint32_t u = __float_as_uint(x);
   return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);   // x is finite
 }
+// K and V of a 32-key chunk in LDS: one 256-byte row per key, its 16-byte
+// pieces permuted by XOR with a per-key pattern. The gather fills them with
+// each quad of lanes reading 64 contiguous bytes of one row (one L1 access
+// per quad); the matrix-core operands are read back from them:
+//   K: f(k) = 4 (k % 4) + (k / 4) % 4. The gather's stores (4 keys x 64
+//      bytes per 16 lanes) and the QK B-operand reads (16 keys, one piece
+//      each) touch every bank once.
+//   V: f(k) = 4 (k % 4) + 2 ((k / 8) % 2). The stores as for K, and the P.V
+//      B operand comes from gfx950's transposing LDS read: it gives lane j
+//      of each 16-lane block element j%4 of the 8 bytes that lane 4e + j/4
+//      of the block loaded, as its element e. For the 16x16x32 operand
+//      (lane l: keys 8(l/16) + e, e = 0..7, of channel 16t + l%16), lane i
+//      of block b loads channels 16t + 4(i%4)..+3 of key 8b + 4h + i/4, for
+//      h = 0 and h = 1; the 8 keys a half wave reads sit in 8 bank groups.
+constexpr int kRowBytes = 2 * kD;   // one key's K or V row
+__device__ __forceinline__ int ktile_byte(int key, int byte) {
+  const int f = 4 * (key & 3) + ((key >> 2) & 3);
+  return key * kRowBytes + (((byte >> 4) ^ f) << 4) + (byte & 15);
+}
+__device__ __forceinline__ int vtile_byte(int key, int byte) {
+  const int f = 4 * (key & 3) + 2 * ((key >> 3) & 1);
+  return key * kRowBytes + (((byte >> 4) ^ f) << 4) + (byte & 15);
+}
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
+// the B operand of O += P V for channels 16t..16t+15 over keys 0..31
+__device__ __forceinline__ bf16x8 vtile_operand16(const uint8_t* sV, int t, int lane) {
+  const int i = lane & 15, key = 8 * (lane >> 4) + (i >> 2), byte = 32 * t + 8 * (i & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(sV + vtile_byte(key, byte)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(sV + vtile_byte(key + 4, byte)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // p as hi + lo bf16 terms (p finite, >= 0)
 __device__ __forceinline__ void split_bf16(float p, uint16_t& hi, uint16_t& lo) {
   hi = f32_to_bf16_rne(p);
@@ -250,7 +285,8 @@ __global__ __launch_bounds__(64 * kNW) void attn_mfma_kernel(AttnArgs a) {
 constexpr int kP16Ld = 40;   // LDS P row: 32 bf16 + 8 pad
 __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
-  __shared__ __align__(16) uint16_t sV[kD * kVLd];      // V^T of the chunk
+  __shared__ __align__(16) uint8_t sK[kKC * kRowBytes];   // K of the chunk
+  __shared__ __align__(16) uint8_t sV[kKC * kRowBytes];   // V of the chunk
   __shared__ __align__(16) uint16_t sP[16 * kP16Ld];    // P hi (rows 8..15 stay zero)
   __shared__ __align__(16) uint16_t sPl[16 * kP16Ld];   // P lo
   const int lane = threadIdx.x, q4 = lane >> 4, c16 = lane & 15;
@@ -283,18 +319,27 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
 
   const int nch = (a.B + kKC - 1) / kKC;
   const int64_t tok_bytes = a.s_tok * 2;
-  const char* kb0 = (const char*)a.k + ((int64_t)g * a.s_head) * 2 + 16 * q4;
-  const char* vb0 = (const char*)a.v + ((int64_t)g * a.s_head) * 2 + 16 * q4;
+  // The gather: lane l reads bytes 64j + 16(l%4) (j < 4) of the K and V
+  // rows of keys l/4 and 16 + l/4 of a chunk -- a quad per 64 contiguous
+  // bytes -- and stores them to the LDS tiles.
+  const int kq = lane >> 2, r4 = lane & 3;
+  const char* kb0 = (const char*)a.k + ((int64_t)g * a.s_head) * 2 + 16 * r4;
+  const char* vb0 = (const char*)a.v + ((int64_t)g * a.s_head) * 2 + 16 * r4;
   const int tlim = a.T;
-  // Lane (c16, q4) reads keys c16 and 16 + c16 of a chunk, channels
-  // 32c + 8 q4 .. +7 (c < 4): for K exactly its QK B operand (column
-  // tile, 32-deep step c); V goes to LDS transposed.
+  // A chunk's list entries are loaded a chunk ahead of its rows (clamped
+  // into the list, unconditionally, and checked only when used), so the
+  // gather never waits for its own index load.
   u32x4 kreg[2][4], vreg[2][4];
-  auto fetch = [&](int c, int32_t (&pos)[2]) {
+  auto load_entries = [&](int c, int32_t (&ent)[2]) {
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) ent[tn] = ilist[min(c * kKC + 16 * tn + kq, a.B - 1)];
+  };
+  // pos: this lane's gather keys (-1 = skipped); posc: the keys of its
+  // score columns c16 and 16 + c16
+  auto fetch = [&](int c, const int32_t (&ent)[2], int32_t (&pos)[2], int32_t (&posc)[2]) {
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
-      const int e = c * kKC + 16 * tn + c16;
-      int32_t t = e < a.B ? ilist[e] : -1;
+      int32_t t = c * kKC + 16 * tn + kq < a.B ? ent[tn] : -1;
       if (t < 0 || t >= tlim) t = -1;
       int64_t row = t < 0 ? 0 : t;
       if (a.slot && t >= 0) {
@@ -306,41 +351,50 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
       const char* kr = kb0 + row * tok_bytes;
       const char* vr = vb0 + row * tok_bytes;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        kreg[tn][q] = *(const u32x4*)(kr + 64 * q);
-        vreg[tn][q] = *(const u32x4*)(vr + 64 * q);
+      for (int j = 0; j < 4; ++j) {
+        kreg[tn][j] = *(const u32x4*)(kr + 64 * j);
+        vreg[tn][j] = *(const u32x4*)(vr + 64 * j);
       }
     }
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) posc[tn] = __shfl(pos[tn], 4 * c16, 64);
   };
-  int32_t posn[2] = {-1, -1};
-  if (nch > 0) fetch(0, posn);
+  int32_t posg[2] = {-1, -1}, posn[2] = {-1, -1}, ent[2] = {-1, -1};
+  if (nch > 0) {
+    load_entries(0, ent);
+    fetch(0, ent, posg, posn);
+    load_entries(1, ent);
+  }
   for (int c = 0; c < nch; ++c) {
     const int32_t pos0 = posn[0], pos1 = posn[1];
+    // this chunk's rows to LDS (the previous chunk's reads are done: same
+    // wave); a skipped key's V row is zeroed, so its p = 0 never meets a
+    // NaN or Inf
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn) {
+      const uint32_t vkeep = posg[tn] >= 0 ? ~0u : 0u;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        *(lds_x4*)(sK + ktile_byte(16 * tn + kq, 64 * j + 16 * r4)) = kreg[tn][j];
+        *(lds_x4*)(sV + vtile_byte(16 * tn + kq, 64 * j + 16 * r4)) = vreg[tn][j] & vkeep;
+      }
+    }
+    if (c + 1 < nch) {   // the next chunk's rows fly during this chunk's products
+      const int32_t cur[2] = {ent[0], ent[1]};
+      fetch(c + 1, cur, posg, posn);
+      load_entries(c + 2, ent);
+    }
+    // S = Q K^T: B = K (key 16 tn + c16, channels 32q + 8 q4 ..)
     f32x4 s[2];
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
       s[tn] = f32x4{};
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        s[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q], __builtin_bit_cast(bf16x8, kreg[tn][q]), s[tn], 0, 0, 0);
-    }
-    // V^T of this chunk: key 16 tn + c16, channels 32q + 8 q4 + i; a skipped
-    // key's row is zeroed, so its p = 0 never meets a NaN or Inf
-#pragma unroll
-    for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t vkeep = (tn == 0 ? pos0 : pos1) >= 0 ? ~0u : 0u;
-        const uint32_t ww[4] = {vreg[tn][q].x & vkeep, vreg[tn][q].y & vkeep, vreg[tn][q].z & vkeep,
-                                vreg[tn][q].w & vkeep};
-        uint16_t* dst = sV + (32 * q + 8 * q4) * kVLd + 16 * tn + c16;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          dst[(2 * i) * kVLd] = (uint16_t)(ww[i] & 0xffffu);
-          dst[(2 * i + 1) * kVLd] = (uint16_t)(ww[i] >> 16);
-        }
+        const u32x4 kb = *(const lds_x4*)(sK + ktile_byte(16 * tn + c16, 64 * q + 16 * q4));
+        s[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q], __builtin_bit_cast(bf16x8, kb), s[tn], 0, 0, 0);
       }
-    if (c + 1 < nch) fetch(c + 1, posn);   // the next chunk's rows fly during softmax and PV
+    }
     // masks, scale; O and l relative to a reference max raised only when a
     // score passes it by 8 (log2 domain), so p <= 256
     const int i = tok;   // causal: positions up to the token's own
@@ -378,12 +432,12 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
         split_bf16(p1, sP[o16 + 16], sPl[o16 + 16]);
       }
     }
-    // O += P V: A = P (row c16, keys 8 q4 ..), B = V^T (channel 16t + c16)
+    // O += P V: A = P (row c16, keys 8 q4 ..), B = V (keys 8 q4 .., channel 16t + c16)
     const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sP + c16 * kP16Ld + 8 * q4));
     const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sPl + c16 * kP16Ld + 8 * q4));
 #pragma unroll
     for (int t = 0; t < kD / 16; ++t) {
-      const bf16x8 vb = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sV + (16 * t + c16) * kVLd + 8 * q4));
+      const bf16x8 vb = vtile_operand16(sV, t, lane);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[t], 0, 0, 0);
       o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[t], 0, 0, 0);
     }
