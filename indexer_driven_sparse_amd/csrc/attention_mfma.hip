@@ -471,12 +471,15 @@ constexpr int kDecWaves = 4;
 template <int GL>
 __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnArgs a) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
-  __shared__ __align__(16) uint16_t sVall[kDecWaves][kD * kVLd];     // V^T of the chunk, then the wave's partial
-  __shared__ __align__(16) uint16_t sPall[kDecWaves][16 * kP16Ld];   // P hi (rows >= 8 stay zero)
-  __shared__ __align__(16) uint16_t sPlall[kDecWaves][16 * kP16Ld];  // P lo
+  __shared__ __align__(16) uint8_t sKall[kDecWaves][kKC * kRowBytes];   // K of the chunk
+  __shared__ __align__(16) uint8_t sVall[kDecWaves][kKC * kRowBytes];   // V of the chunk, then the wave's partial
+  __shared__ __align__(16) uint16_t sPall[kDecWaves][16 * kP16Ld];      // P hi (rows >= 8 stay zero)
+  __shared__ __align__(16) uint16_t sPlall[kDecWaves][16 * kP16Ld];     // P lo
   const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4, c16 = lane & 15;
+  const int kq = lane >> 2, r4 = lane & 3;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint16_t* sV = sVall[w];
+  uint8_t* sK = sKall[w];
+  uint8_t* sV = sVall[w];
   uint16_t* sP = sPall[w];
   uint16_t* sPl = sPlall[w];
   const int split = (int)(blockIdx.x % a.splits);
@@ -485,16 +488,17 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnAr
   const int e0 = split * (kDecWaves * kKC) + w * kKC;   // this wave's first list entry
   const int32_t* ilist = a.idx + rowg * a.B;
 
-  // list entries and rows first (lane (c16, q4): keys c16 and 16 + c16,
-  // channels 32q + 8 q4 .. +7 of each), so the gather starts at once
+  // list entries and rows first, so the gather starts at once: lane l reads
+  // bytes 64j + 16(l%4) of the K and V rows of keys l/4 and 16 + l/4 (a
+  // quad per 64 contiguous bytes)
   int32_t pos[2];
   u32x4 kreg[2][4], vreg[2][4];
   const int64_t tok_bytes = a.s_tok * 2;
-  const int64_t base = ((int64_t)row * a.s_seq + (int64_t)g * a.s_head) * 2 + 16 * q4;
+  const int64_t base = ((int64_t)row * a.s_seq + (int64_t)g * a.s_head) * 2 + 16 * r4;
   const int32_t* tab = a.slot ? a.slot + (int64_t)row * a.slot_ld : nullptr;
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn) {
-    const int e = e0 + 16 * tn + c16;
+    const int e = e0 + 16 * tn + kq;
     int32_t t = e < a.B ? ilist[e] : -1;
     if (t < 0 || t >= a.T) t = -1;
     int64_t r = t < 0 ? 0 : t;
@@ -507,9 +511,9 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnAr
     const char* kr = (const char*)a.k + base + r * tok_bytes;
     const char* vr = (const char*)a.v + base + r * tok_bytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      kreg[tn][q] = *(const u32x4*)(kr + 64 * q);
-      vreg[tn][q] = *(const u32x4*)(vr + 64 * q);
+    for (int j = 0; j < 4; ++j) {
+      kreg[tn][j] = *(const u32x4*)(kr + 64 * j);
+      vreg[tn][j] = *(const u32x4*)(vr + 64 * j);
     }
   }
   // Q: row c16 = head c16 (< GL; idle rows are zero), channels 32c + 8 q4 ..
@@ -525,36 +529,38 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnAr
   }
   for (int e = lane; e < 8 * kP16Ld; e += 64) sP[8 * kP16Ld + e] = sPl[8 * kP16Ld + e] = 0;
 
+  // the rows to the LDS tiles; a skipped key's V row is zeroed, so its
+  // p = 0 never meets a NaN or Inf
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn) {
+    const uint32_t vkeep = pos[tn] >= 0 ? ~0u : 0u;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      *(lds_x4*)(sK + ktile_byte(16 * tn + kq, 64 * j + 16 * r4)) = kreg[tn][j];
+      *(lds_x4*)(sV + vtile_byte(16 * tn + kq, 64 * j + 16 * r4)) = vreg[tn][j] & vkeep;
+    }
+  }
+  // the keys of this lane's score columns c16 and 16 + c16
+  int32_t posc[2];
+#pragma unroll
+  for (int tn = 0; tn < 2; ++tn) posc[tn] = __shfl(pos[tn], 4 * c16, 64);
+  // S = Q K^T: B = K (key 16 tn + c16, channels 32q + 8 q4 ..)
   f32x4 s[2];
 #pragma unroll
   for (int tn = 0; tn < 2; ++tn) {
     s[tn] = f32x4{};
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      s[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q], __builtin_bit_cast(bf16x8, kreg[tn][q]), s[tn], 0, 0, 0);
-  }
-  // V^T: key 16 tn + c16, channels 32q + 8 q4 + i; a skipped key's row is
-  // zeroed, so its p = 0 never meets a NaN or Inf
-#pragma unroll
-  for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint32_t vkeep = pos[tn] >= 0 ? ~0u : 0u;
-      const uint32_t ww[4] = {vreg[tn][q].x & vkeep, vreg[tn][q].y & vkeep, vreg[tn][q].z & vkeep,
-                              vreg[tn][q].w & vkeep};
-      uint16_t* dst = sV + (32 * q + 8 * q4) * kVLd + 16 * tn + c16;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        dst[(2 * i) * kVLd] = (uint16_t)(ww[i] & 0xffffu);
-        dst[(2 * i + 1) * kVLd] = (uint16_t)(ww[i] >> 16);
-      }
+      const u32x4 kb = *(const lds_x4*)(sK + ktile_byte(16 * tn + c16, 64 * q + 16 * q4));
+      s[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q], __builtin_bit_cast(bf16x8, kb), s[tn], 0, 0, 0);
     }
+  }
   // softmax over the chunk, heads 4 q4 + v in lanes 0..31 (log2 domain)
   float m[4], l[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    const float x0 = pos[0] >= 0 ? s[0][v] * a.scale_log2 : -INFINITY;
-    const float x1 = pos[1] >= 0 ? s[1][v] * a.scale_log2 : -INFINITY;
+    const float x0 = posc[0] >= 0 ? s[0][v] * a.scale_log2 : -INFINITY;
+    const float x1 = posc[1] >= 0 ? s[1][v] * a.scale_log2 : -INFINITY;
     float mm = fmaxf(x0, x1);
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
@@ -568,18 +574,18 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnAr
       split_bf16(p1, sP[o16 + 16], sPl[o16 + 16]);
     }
   }
-  // O = P V: A = P (row c16, keys 8 q4 ..), B = V^T (channel 16t + c16)
+  // O = P V: A = P (row c16, keys 8 q4 ..), B = V (keys 8 q4 .., channel 16t + c16)
   const bf16x8 pa = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sP + c16 * kP16Ld + 8 * q4));
   const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sPl + c16 * kP16Ld + 8 * q4));
   f32x4 o[kD / 16];
 #pragma unroll
   for (int t = 0; t < kD / 16; ++t) {
-    const bf16x8 vb = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sV + (16 * t + c16) * kVLd + 8 * q4));
+    const bf16x8 vb = vtile_operand16(sV, t, lane);
     o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, f32x4{}, 0, 0, 0);
     o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[t], 0, 0, 0);
   }
-  // this wave's (max, sum, O) of heads 4 q4 + v < GL into its own V^T space
-  // (its reads of V^T are done: a wave's LDS accesses execute in order)
+  // this wave's (max, sum, O) of heads 4 q4 + v < GL into its own V tile
+  // (its reads of the tile are done: a wave's LDS accesses execute in order)
   float* wp = reinterpret_cast<float*>(sV);   // [GL][kD + 2]
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
