@@ -26,6 +26,9 @@ FLAGS = [
     "-Wall",
     # packed fp32 VALU ops stay off: plain fp32 code is used throughout
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the attention softmax
+    # rescales O between products, which otherwise costs AGPR copies
+    "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

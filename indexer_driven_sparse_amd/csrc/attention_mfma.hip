@@ -88,6 +88,16 @@ __device__ __forceinline__ bf16x8 vtile_operand16(const uint8_t* sV, int t, int 
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// two p values as hi + lo bf16 terms, hi = bf16(p) and lo = bf16(p - hi),
+// both round-to-nearest-even by gfx950's packed conversion; element 0 in
+// the low halves
+__device__ __forceinline__ void split2_bf16(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
+  const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0 - h0, p1 - h1}, bf16x2));
+}
 // p as hi + lo bf16 terms (p finite, >= 0)
 __device__ __forceinline__ void split_bf16(float p, uint16_t& hi, uint16_t& lo) {
   hi = f32_to_bf16_rne(p);
@@ -370,13 +380,20 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
     // this chunk's rows to LDS (the previous chunk's reads are done: same
     // wave); a skipped key's V row is zeroed, so its p = 0 never meets a
     // NaN or Inf
+    if (__builtin_amdgcn_ballot_w64(posg[0] < 0 || posg[1] < 0)) {
+#pragma unroll
+      for (int tn = 0; tn < 2; ++tn) {
+        const uint32_t vkeep = posg[tn] >= 0 ? ~0u : 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vreg[tn][j] &= vkeep;
+      }
+    }
 #pragma unroll
     for (int tn = 0; tn < 2; ++tn) {
-      const uint32_t vkeep = posg[tn] >= 0 ? ~0u : 0u;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         *(lds_x4*)(sK + ktile_byte(16 * tn + kq, 64 * j + 16 * r4)) = kreg[tn][j];
-        *(lds_x4*)(sV + vtile_byte(16 * tn + kq, 64 * j + 16 * r4)) = vreg[tn][j] & vkeep;
+        *(lds_x4*)(sV + vtile_byte(16 * tn + kq, 64 * j + 16 * r4)) = vreg[tn][j];
       }
     }
     if (c + 1 < nch) {   // the next chunk's rows fly during this chunk's products
@@ -395,22 +412,24 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
         s[tn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[q], __builtin_bit_cast(bf16x8, kb), s[tn], 0, 0, 0);
       }
     }
-    // masks, scale; O and l relative to a reference max raised only when a
-    // score passes it by 8 (log2 domain), so p <= 256
+    // masks and scale; O and l relative to a reference max m raised only
+    // when a score passes it by 8 (log2 domain), so p <= 256. y = the
+    // scaled score minus m (-inf where masked; +inf while m is -inf).
     const int i = tok;   // causal: positions up to the token's own
-    float x0[4], x1[4];
+    const bool ok0 = pos0 >= 0 && pos0 <= i, ok1 = pos1 >= 0 && pos1 <= i;
+    const float sc = a.scale_log2;
+    float y0[4], y1[4];
     bool raise = false;
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      x0[v] = (pos0 >= 0 && pos0 <= i) ? s[0][v] * a.scale_log2 : -INFINITY;
-      x1[v] = (pos1 >= 0 && pos1 <= i) ? s[1][v] * a.scale_log2 : -INFINITY;
-      const float xm = fmaxf(x0[v], x1[v]);
-      raise |= xm > m[v] + 8.f || (m[v] == -INFINITY && xm != -INFINITY);
+      y0[v] = ok0 ? fmaf(s[0][v], sc, -m[v]) : -INFINITY;
+      y1[v] = ok1 ? fmaf(s[1][v], sc, -m[v]) : -INFINITY;
+      raise |= fmaxf(y0[v], y1[v]) > 8.f;
     }
     if (__builtin_amdgcn_ballot_w64(raise && lane < 32)) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        float mm = fmaxf(x0[v], x1[v]);
+        float mm = fmaxf(ok0 ? s[0][v] * sc : -INFINITY, ok1 ? s[1][v] * sc : -INFINITY);
 #pragma unroll
         for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
         const float mn = fmaxf(m[v], mm);
@@ -419,17 +438,24 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
 #pragma unroll
         for (int t = 0; t < kD / 16; ++t) o[t][v] *= alpha;
         m[v] = mn;
+        y0[v] = ok0 ? fmaf(s[0][v], sc, -mn) : -INFINITY;
+        y1[v] = ok1 ? fmaf(s[1][v], sc, -mn) : -INFINITY;
       }
     }
     if (lane < 32) {
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float p0 = m[v] == -INFINITY ? 0.f : exp2f(x0[v] - m[v]);
-        const float p1 = m[v] == -INFINITY ? 0.f : exp2f(x1[v] - m[v]);
+        // y <= 8 or -inf here: the raw exp2 (no denormal rescaling) suffices
+        const float p0 = __builtin_amdgcn_exp2f(y0[v]);
+        const float p1 = __builtin_amdgcn_exp2f(y1[v]);
         l[v] += p0 + p1;
+        uint32_t hi, lo;
+        split2_bf16(p0, p1, hi, lo);
         const int o16 = (4 * q4 + v) * kP16Ld + c16;
-        split_bf16(p0, sP[o16], sPl[o16]);
-        split_bf16(p1, sP[o16 + 16], sPl[o16 + 16]);
+        sP[o16] = (uint16_t)hi;
+        sP[o16 + 16] = (uint16_t)(hi >> 16);
+        sPl[o16] = (uint16_t)lo;
+        sPl[o16 + 16] = (uint16_t)(lo >> 16);
       }
     }
     // O += P V: A = P (row c16, keys 8 q4 ..), B = V (keys 8 q4 .., channel 16t + c16)
