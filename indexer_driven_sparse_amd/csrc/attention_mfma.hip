@@ -44,9 +44,7 @@ typedef uint32_t lds_x4 __attribute__((ext_vector_type(4), __may_alias__));
 constexpr int kD = 128;          // head_dim
 constexpr int kG = 8;            // query heads per KV head
 constexpr int kKC = 32;          // keys per chunk
-constexpr int kVLd = 40;         // LDS V^T row (one channel): 32 bf16 + 8 pad (80 B)
 constexpr int kPLd = 40;         // LDS P row: 32 bf16 + 8 pad
-constexpr int kWaveBytes = (kD * kVLd + 2 * kKC * kPLd) * 2;   // per wave: V^T, P hi, P lo
 constexpr float kLn2f = 0.69314718055994530942f;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
@@ -106,16 +104,36 @@ __device__ __forceinline__ void split_bf16(float p, uint16_t& hi, uint16_t& lo) 
 
 // Block-shared selections: kTPW tokens per wave, kNW waves per workgroup; a
 // workgroup serves the tokens [tok0, tok0 + kTPW * kNW) of one block, which
-// share index row `isel`.
+// share index row `isel`. The workgroup gathers each 32-key chunk once, into
+// K and V tiles in LDS (double-buffered: the next chunk's rows are in flight
+// while every wave computes on this one), one barrier per chunk.
 constexpr int kTPW = 4, kNW = 4;
+constexpr int kTileBytes = kKC * kRowBytes;                    // one K or V tile
+constexpr int kBlkWaveBytes = 2 * kKC * kPLd * 2;              // per wave: P hi, P lo
+constexpr int kBlkLds = 2 * (2 * kTileBytes + kKC * 4) + kNW * kBlkWaveBytes;
+
+// the B operand of O += P V on 32x32x16 tiles for channels 32t..32t+31 and
+// keys 16kc..16kc+15 (lane l: keys 16kc + 8(l/32) + e of channel 32t +
+// l%32): lane i of 16-lane block b loads channels 32t + 16(b%2) + 4(i%4)..+3
+// of key 16kc + 8(b/2) + 4h + i/4, for h = 0 and h = 1
+__device__ __forceinline__ bf16x8 vtile_operand32(const uint8_t* sV, int t, int kc, int lane) {
+  const int b = lane >> 4, i = lane & 15;
+  const int key = 16 * kc + 8 * (b >> 1) + (i >> 2), byte = 64 * t + 32 * (b & 1) + 8 * (i & 3);
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(sV + vtile_byte(key, byte)));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(sV + vtile_byte(key + 4, byte)));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 __global__ __launch_bounds__(64 * kNW) void attn_mfma_kernel(AttnArgs a) {
   constexpr int TPW = kTPW, NW = kNW;
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, lane = tid & 63, hh = lane >> 5, n = lane & 31;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // per wave: V^T of the current chunk, then P
-  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + w * kWaveBytes);
-  uint16_t* sP = sV + kD * kVLd;
+  // two buffers of (K tile, V tile, key positions), then each wave's P
+  uint8_t* sBuf = smem;
+  uint16_t* sP = reinterpret_cast<uint16_t*>(smem + 2 * (2 * kTileBytes + kKC * 4) + w * kBlkWaveBytes);
   uint16_t* sPl = sP + kKC * kPLd;
 
   // ceil(qblk / (TPW NW)) workgroups per (block, KV head)
@@ -163,20 +181,18 @@ __global__ __launch_bounds__(64 * kNW) void attn_mfma_kernel(AttnArgs a) {
 
   const int nch = (a.B + kKC - 1) / kKC;
   const int64_t tok_bytes = a.s_tok * 2;
-  const char* kb0 = (const char*)a.k + ((int64_t)g * a.s_head) * 2 + 16 * hh;
-  const char* vb0 = (const char*)a.v + ((int64_t)g * a.s_head) * 2 + 16 * hh;
   const int tlim = a.T;
-  uint16_t* vT = sV + 8 * hh * kVLd + n;         // V^T: channel 8 hh, key n (+ 16 q channels)
-
-  // Lane (n, hh) reads key n's channels 16q + 8hh .. +7 (q < 8) of K and V:
-  // the K pieces are exactly this lane's MFMA B operand for QK (key n,
-  // 16-deep chunk q), so K never touches LDS; V goes through LDS
-  // transposed. kreg/vreg hold the next chunk while this one computes.
-  u32x4 kreg[8], vreg[8];
-  // key n of chunk c: its sequence position (-1: skipped -- list padding,
-  // outside [0, T), or a stale slot-table entry), after issuing its loads
-  auto fetch = [&](int c) -> int32_t {
-    const int e = c * kKC + n;
+  // The gather: thread t reads pieces t%8 and 8 + t%8 (16 bytes each) of
+  // the K and V rows of one key of a chunk -- a quad per 64 contiguous
+  // bytes. Threads 8j..8j+7 serve key gk(j), a bijection on 0..31 that gives
+  // each 16 threads two keys whose tile pieces land in opposite bank halves.
+  const int gk = ((tid >> 5) << 2) | (((tid >> 3) & 1) << 1) | ((tid >> 4) & 1), gp = tid & 7;
+  const char* kb0 = (const char*)a.k + ((int64_t)g * a.s_head) * 2 + 16 * gp;
+  const char* vb0 = (const char*)a.v + ((int64_t)g * a.s_head) * 2 + 16 * gp;
+  u32x4 kreg[2], vreg[2];
+  int32_t gpos = -1;   // key gk of the chunk in flight: its position (-1: skipped)
+  auto fetch = [&](int c) {
+    const int e = c * kKC + gk;
     int32_t t = e < a.B ? ilist[e] : -1;
     if (t < 0 || t >= tlim) t = -1;
     int64_t row = t < 0 ? 0 : t;
@@ -185,38 +201,43 @@ __global__ __launch_bounds__(64 * kNW) void attn_mfma_kernel(AttnArgs a) {
       if (pr < 0 || pr >= a.n_rows_kv) t = -1;
       row = t < 0 ? 0 : pr;
     }
+    gpos = t;
     const char* kr = kb0 + row * tok_bytes;
     const char* vr = vb0 + row * tok_bytes;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      kreg[q] = *(const u32x4*)(kr + 32 * q);
-      vreg[q] = *(const u32x4*)(vr + 32 * q);
+    for (int u = 0; u < 2; ++u) {
+      kreg[u] = *(const u32x4*)(kr + 128 * u);
+      vreg[u] = *(const u32x4*)(vr + 128 * u);
     }
-    return t;
   };
 
-  int32_t posn = nch > 0 ? fetch(0) : -1;
+  if (nch > 0) fetch(0);
   for (int c = 0; c < nch; ++c) {
-    const int32_t pos = posn;   // key n of chunk c: its position in the sequence (-1: none)
-    // S = Q K^T over the chunk's 32 keys
+    uint8_t* sK = sBuf + (c & 1) * (2 * kTileBytes + kKC * 4);
+    uint8_t* sV = sK + kTileBytes;
+    int32_t* sPos = reinterpret_cast<int32_t*>(sV + kTileBytes);
+    // this chunk's rows to the tiles; a skipped key's V row is zeroed, so
+    // its p = 0 never meets a NaN or Inf (the buffer was last read two
+    // chunks ago, before the previous barrier)
+    {
+      const uint32_t vkeep = gpos >= 0 ? ~0u : 0u;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        *(lds_x4*)(sK + ktile_byte(gk, 16 * gp + 128 * u)) = kreg[u];
+        *(lds_x4*)(sV + vtile_byte(gk, 16 * gp + 128 * u)) = vreg[u] & vkeep;
+      }
+      if (gp == 0) sPos[gk] = gpos;
+    }
+    __syncthreads();
+    if (c + 1 < nch) fetch(c + 1);   // the next chunk's rows fly during this chunk's products
+    const int32_t pos = sPos[n];     // key n of chunk c: its position in the sequence (-1: none)
+    // S = Q K^T over the chunk's 32 keys: B = K (key n, channels 16q + 8hh ..)
     f32x16 s = f32x16{};
 #pragma unroll
-    for (int q = 0; q < 8; ++q)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[q], __builtin_bit_cast(bf16x8, kreg[q]), s, 0, 0, 0);
-    // V^T of this chunk (the previous chunk's PV reads are done: same wave);
-    // a skipped key's row (row 0, or whatever a stale slot names) is zeroed,
-    // so its p = 0 never meets a NaN or Inf in the product
-    const uint32_t vkeep = pos >= 0 ? ~0u : 0u;
-#pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const uint32_t ww[4] = {vreg[q].x & vkeep, vreg[q].y & vkeep, vreg[q].z & vkeep, vreg[q].w & vkeep};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        vT[(16 * q + 2 * e) * kVLd] = (uint16_t)(ww[e] & 0xffffu);
-        vT[(16 * q + 2 * e + 1) * kVLd] = (uint16_t)(ww[e] >> 16);
-      }
+      const u32x4 kb = *(const lds_x4*)(sK + ktile_byte(n, 32 * q + 16 * hh));
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[q], __builtin_bit_cast(bf16x8, kb), s, 0, 0, 0);
     }
-    if (c + 1 < nch) posn = fetch(c + 1);   // the next chunk's rows fly during softmax and PV
     // masks and scale; O and l stay relative to a reference max m per row,
     // raised (with a rescale of O and l) only when a score passes m + 8 in
     // the log2 domain -- a few times per row -- so p = exp2(x - m) <= 256
@@ -248,11 +269,19 @@ __global__ __launch_bounds__(64 * kNW) void attn_mfma_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int v = 0; v < kV; ++v) {
-      const float p = m[v] == -INFINITY ? 0.f : exp2f(x[v] - m[v]);
-      l[v] += p;
-      const int r = 8 * (v >> 2) + 4 * hh + (v & 3);
-      split_bf16(p, sP[r * kPLd + n], sPl[r * kPLd + n]);
+    for (int v = 0; v < kV; v += 2) {
+      // x - m <= 8 or -inf here: the raw exp2 (no denormal rescaling) suffices
+      const float p0 = m[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[v] - m[v]);
+      const float p1 = m[v + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[v + 1] - m[v + 1]);
+      l[v] += p0;
+      l[v + 1] += p1;
+      uint32_t hi, lo;
+      split2_bf16(p0, p1, hi, lo);
+      const int r0 = 8 * (v >> 2) + 4 * hh + (v & 3);
+      sP[r0 * kPLd + n] = (uint16_t)hi;
+      sP[(r0 + 1) * kPLd + n] = (uint16_t)(hi >> 16);
+      sPl[r0 * kPLd + n] = (uint16_t)lo;
+      sPl[(r0 + 1) * kPLd + n] = (uint16_t)(lo >> 16);
     }
     // O += P V (two 16-key halves of the chunk)
 #pragma unroll
@@ -261,8 +290,7 @@ __global__ __launch_bounds__(64 * kNW) void attn_mfma_kernel(AttnArgs a) {
       const bf16x8 pl = __builtin_bit_cast(bf16x8, *(const lds_x4*)(sPl + n * kPLd + 16 * kc + 8 * hh));
 #pragma unroll
       for (int t = 0; t < kD / 32; ++t) {
-        const bf16x8 vb =
-            __builtin_bit_cast(bf16x8, *(const lds_x4*)(sV + (32 * t + n) * kVLd + 16 * kc + 8 * hh));
+        const bf16x8 vb = vtile_operand32(sV, t, kc, lane);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa, vb, o[t], 0, 0, 0);
         o[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl, vb, o[t], 0, 0, 0);
       }
@@ -661,7 +689,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnAr
 }
 
 hipError_t launch_mfma_blocks(const AttnArgs& a, hipStream_t s) {
-  const size_t lds = (size_t)kNW * kWaveBytes;
+  const size_t lds = (size_t)kBlkLds;
   const int nsel = (a.rows + a.qblk - 1) / a.qblk;
   const unsigned nx = (unsigned)(nsel * ((a.qblk + kTPW * kNW - 1) / (kTPW * kNW)));
   hipLaunchKernelGGL(attn_mfma_kernel, dim3(nx, (unsigned)a.Hkv), dim3(64 * kNW), lds, s, a);
