@@ -241,38 +241,40 @@ __global__ __launch_bounds__(64 * kNW) void attn_mfma_kernel(AttnArgs a) {
     // masks and scale; O and l stay relative to a reference max m per row,
     // raised (with a rescale of O and l) only when a score passes m + 8 in
     // the log2 domain -- a few times per row -- so p = exp2(x - m) <= 256
-    // and the common chunk touches O only through the MFMA
+    // and the common chunk touches O only through the MFMA. y = the scaled
+    // score minus m (-inf where masked; +inf while m is -inf).
     const bool kvalid = pos >= 0;
-    float x[kV], mx[kV];
+    const float sc = a.scale_log2;
+    bool ok[4];   // rows v hold token v/4
+#pragma unroll
+    for (int tq = 0; tq < 4; ++tq) ok[tq] = kvalid && pos <= ipos[4 * tq];
+    float y[kV];
     bool raise = false;
 #pragma unroll
     for (int v = 0; v < kV; ++v) {
-      const bool ok = kvalid && pos <= ipos[v];
-      x[v] = ok ? s[v] * a.scale_log2 : -INFINITY;
-      raise |= x[v] > m[v] + 8.f || (m[v] == -INFINITY && x[v] != -INFINITY);
+      y[v] = ok[v >> 2] ? fmaf(s[v], sc, -m[v]) : -INFINITY;
+      raise |= y[v] > 8.f;
     }
     if (__builtin_amdgcn_ballot_w64(raise)) {
 #pragma unroll
       for (int v = 0; v < kV; ++v) {
-        float mm = x[v];
+        float mm = ok[v >> 2] ? s[v] * sc : -INFINITY;
 #pragma unroll
         for (int off = 1; off < 32; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
-        mx[v] = fmaxf(m[v], mm);
-      }
-#pragma unroll
-      for (int v = 0; v < kV; ++v) {
-        const float alpha = mx[v] == -INFINITY || m[v] == -INFINITY ? 0.f : exp2f(m[v] - mx[v]);
+        const float mn = fmaxf(m[v], mm);
+        const float alpha = mn == -INFINITY || m[v] == -INFINITY ? 0.f : exp2f(m[v] - mn);
         l[v] *= alpha;
 #pragma unroll
         for (int t = 0; t < kD / 32; ++t) o[t][v] *= alpha;
-        m[v] = mx[v];
+        m[v] = mn;
+        y[v] = ok[v >> 2] ? fmaf(s[v], sc, -mn) : -INFINITY;
       }
     }
 #pragma unroll
     for (int v = 0; v < kV; v += 2) {
-      // x - m <= 8 or -inf here: the raw exp2 (no denormal rescaling) suffices
-      const float p0 = m[v] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[v] - m[v]);
-      const float p1 = m[v + 1] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x[v + 1] - m[v + 1]);
+      // y <= 8 or -inf here: the raw exp2 (no denormal rescaling) suffices
+      const float p0 = __builtin_amdgcn_exp2f(y[v]);
+      const float p1 = __builtin_amdgcn_exp2f(y[v + 1]);
       l[v] += p0;
       l[v + 1] += p1;
       uint32_t hi, lo;
