@@ -75,6 +75,31 @@ __device__ __forceinline__ const uint16_t* qrow(const PrefillTopkArgs& a, int g,
   return a.q_idx + ((int64_t)i * a.Hkv + g) * kRank;
 }
 
+// A tile of 32 rank-64 bf16 rows (keys or queries, 128 bytes each) staged
+// through LDS. Loading operands straight from the rows puts a different row
+// in each adjacent lane, so every lane's 16 bytes cost an L1 access of
+// their own; the staged load reads each row with 8 lanes (lane l, step i:
+// row 8i + l/8, 16-byte piece l%8), one access per 64 bytes. Piece p of
+// row m sits at slot p ^ ((m/2) % 8), so the stores (two rows per 16
+// lanes) and the operand reads (16 rows, one piece each per 16 lanes) both
+// touch every bank once.
+typedef uint32_t lds_x4 __attribute__((ext_vector_type(4), __may_alias__));
+constexpr int kRowB = 2 * kRank;   // bytes per row
+__device__ __forceinline__ int rtile_byte(int row, int piece) {
+  return row * kRowB + 16 * (piece ^ ((row >> 1) & 7));
+}
+// step i of the staged load: 16 bytes of row 8i + l/8 (p = that row)
+__device__ __forceinline__ u32x4 rtile_piece(const uint16_t* p, int lane) {
+  return *(const u32x4*)(p + 8 * (lane & 7));
+}
+__device__ __forceinline__ void rtile_put(uint8_t* t, int i, int lane, u32x4 x) {
+  *(lds_x4*)(t + rtile_byte(8 * i + (lane >> 3), lane & 7)) = x;
+}
+// the MFMA fragment frag() would load for row n, chunk c, lane half h
+__device__ __forceinline__ bf16x8 rtile_frag(const uint8_t* t, int n, int c, int h) {
+  return __builtin_bit_cast(bf16x8, *(const lds_x4*)(t + rtile_byte(n, 2 * c + h)));
+}
+
 // ---------------------------------------------------------------------------
 // Unfused scores (topk == 0): full causal rows, -inf past each row's keys.
 // Row i sees keys j < (i+1)*qblk (qblk = 1: j <= i; qblk > 1: the keys of a
@@ -84,25 +109,61 @@ __device__ __forceinline__ const uint16_t* qrow(const PrefillTopkArgs& a, int g,
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void prefill_scores_mfma_kernel(PrefillTopkArgs a, float* scores,
                                                                  int64_t ld) {
-  __shared__ float tile[kT][kT + 1];
+  // the key and query tiles, then (once the operands are in registers) the
+  // score tile over the same bytes: one wave, so its LDS reads of the
+  // operands complete before its stores of the scores
+  __shared__ __align__(16) uint8_t smem[2 * kT * kRowB];
+  static_assert(sizeof(float) * kT * (kT + 1) <= sizeof(smem), "score tile fits");
+  uint8_t* sk = smem;
+  uint8_t* sq = smem + kT * kRowB;
+  float (*tile)[kT + 1] = reinterpret_cast<float (*)[kT + 1]>(smem);
   const int lane = threadIdx.x, h = lane >> 5, n = lane & 31;
   const int kt = blockIdx.x, qt = blockIdx.y, g = blockIdx.z;
   const int j0 = kt * kT, i0 = qt * kT;
   if ((int64_t)j0 < (int64_t)(i0 + kT) * a.qblk) {   // some key of the tile is visible to some row
+    u32x4 xk[4], xq[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = 8 * i + (lane >> 3);
+      xk[i] = rtile_piece(krow(a, g, min(j0 + m, a.L - 1)), lane);
+      xq[i] = rtile_piece(qrow(a, g, min(i0 + m, a.Lq - 1)), lane);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rtile_put(sk, i, lane, xk[i]);
+      rtile_put(sq, i, lane, xq[i]);
+    }
+    // one wave: its LDS stores complete before its reads
     bf16x8 ka[kCh], qb[kCh];
-    const uint16_t* kp = krow(a, g, min(j0 + n, a.L - 1));
-    const uint16_t* qp = qrow(a, g, min(i0 + n, a.Lq - 1));
 #pragma unroll
     for (int c = 0; c < kCh; ++c) {
-      ka[c] = frag(kp, c, h);
-      qb[c] = frag(qp, c, h);
+      ka[c] = rtile_frag(sk, n, c, h);
+      qb[c] = rtile_frag(sq, n, c, h);
     }
     const f32x16 acc = tile_scores(ka, qb);
 #pragma unroll
     for (int v = 0; v < 16; ++v) tile[n][tile_key(v, h)] = acc[v];
   }
   __syncthreads();
-  // lane pair (2r, 2r+1) writes row r's 32 scores, 16 each
+  if (j0 + kT <= a.L && (ld & 3) == 0 && ((uintptr_t)scores & 15) == 0) {
+    // 8 lanes per row, 16 bytes each: rows 8s + l/8, columns 4(l%8)..+3
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int r = 8 * s4 + (lane >> 3), q0 = 4 * (lane & 7);
+      const int i = i0 + r;
+      if (i >= a.Lq) continue;
+      const int64_t jend = (int64_t)(i + 1) * a.qblk;   // this row's keys: j < jend
+      float4 v;
+      v.x = j0 + q0 < jend ? tile[r][q0] : -INFINITY;
+      v.y = j0 + q0 + 1 < jend ? tile[r][q0 + 1] : -INFINITY;
+      v.z = j0 + q0 + 2 < jend ? tile[r][q0 + 2] : -INFINITY;
+      v.w = j0 + q0 + 3 < jend ? tile[r][q0 + 3] : -INFINITY;
+      *reinterpret_cast<float4*>(scores + ((int64_t)i * a.Hkv + g) * ld + j0 + q0) = v;
+    }
+    return;
+  }
+  // the last tile of a row, or an unaligned output: lane pair (2r, 2r+1)
+  // writes row r's scores, 16 each
   const int r = lane >> 1, half = lane & 1;
   const int i = i0 + r;
   if (i < a.Lq) {
