@@ -37,8 +37,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-// 128-bit reads of LDS tiles that were stored 16 bits at a time: the type
-// aliases anything, so the compiler keeps them after those stores
+// 128-bit LDS accesses of tiles that are also read or written at other
+// widths (16-bit stores, transposing reads, float partials): the type
+// aliases anything, so the compiler keeps them in program order
 typedef uint32_t lds_x4 __attribute__((ext_vector_type(4), __may_alias__));
 
 constexpr int kD = 128;          // head_dim
@@ -47,10 +48,6 @@ constexpr int kKC = 32;          // keys per chunk
 constexpr int kPLd = 40;         // LDS P row: 32 bf16 + 8 pad
 constexpr float kLn2f = 0.69314718055994530942f;
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);   // x is finite
-}
 // K and V of a 32-key chunk in LDS: one 256-byte row per key, its 16-byte
 // pieces permuted by XOR with a per-key pattern. The gather fills them with
 // each quad of lanes reading 64 contiguous bytes of one row (one L1 access
@@ -95,11 +92,6 @@ __device__ __forceinline__ void split2_bf16(float p0, float p1, uint32_t& hi, ui
   hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, bf16x2));
   const float h0 = __uint_as_float(hi << 16), h1 = __uint_as_float(hi & 0xffff0000u);
   lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0 - h0, p1 - h1}, bf16x2));
-}
-// p as hi + lo bf16 terms (p finite, >= 0)
-__device__ __forceinline__ void split_bf16(float p, uint16_t& hi, uint16_t& lo) {
-  hi = f32_to_bf16_rne(p);
-  lo = f32_to_bf16_rne(p - __uint_as_float((uint32_t)hi << 16));
 }
 
 // Block-shared selections: kTPW tokens per wave, kNW waves per workgroup; a
@@ -621,13 +613,18 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnAr
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
     m[v] = mm;
-    const float p0 = mm == -INFINITY ? 0.f : exp2f(x0 - mm);
-    const float p1 = mm == -INFINITY ? 0.f : exp2f(x1 - mm);
+    // x - mm <= 0 or -inf: the raw exp2 (no denormal rescaling) suffices
+    const float p0 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x0 - mm);
+    const float p1 = mm == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(x1 - mm);
     l[v] = p0 + p1;
     if (lane < 32) {
+      uint32_t hi, lo;
+      split2_bf16(p0, p1, hi, lo);
       const int o16 = (4 * q4 + v) * kP16Ld + c16;
-      split_bf16(p0, sP[o16], sPl[o16]);
-      split_bf16(p1, sP[o16 + 16], sPl[o16 + 16]);
+      sP[o16] = (uint16_t)hi;
+      sP[o16 + 16] = (uint16_t)(hi >> 16);
+      sPl[o16] = (uint16_t)lo;
+      sPl[o16 + 16] = (uint16_t)(lo >> 16);
     }
   }
   // O = P V: A = P (row c16, keys 8 q4 ..), B = V (keys 8 q4 .., channel 16t + c16)
