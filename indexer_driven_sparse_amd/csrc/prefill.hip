@@ -162,8 +162,9 @@ __global__ __launch_bounds__(64) void prefill_scores_mfma_kernel(PrefillTopkArgs
     }
     return;
   }
-  // the last tile of a row, or an unaligned output: lane pair (2r, 2r+1)
-  // writes row r's scores, 16 each
+  // the last tile of a row (the API keeps rows 16-byte aligned; the check
+  // above also guards direct callers): lane pair (2r, 2r+1) writes row r's
+  // scores, 16 each
   const int r = lane >> 1, half = lane & 1;
   const int i = i0 + r;
   if (i < a.Lq) {

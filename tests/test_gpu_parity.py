@@ -844,6 +844,28 @@ def _prefill_unfused(qd, kd, B):
     return sc, idx.view(L, Hkv, B), osc.view(L, Hkv, B)
 
 
+def test_prefill_unfused_scores_row_strides():
+    # a row's full tiles leave as 16-byte pieces and its last tile (L = 1000
+    # ends 8 keys into one) as 4-byte stores; the row stride must keep rows
+    # 16-byte aligned, and the scores do not depend on it
+    L, Hkv = 1000, 2
+    q, k = _prefill_qk("c4", L, Hkv, 21)
+    qd, kd = dev(q), dev(k)
+    say("prefill unfused scores, row strides", L, Hkv)
+    outs = []
+    for ld in (L, L + 12):
+        sc = torch.full((L, Hkv, ld), float("nan"), device="cuda")[:, :, :L]
+        lsa.lsa_index_score(kd, sc, q_idx=qd, mode=lsa.MODE_PREFILL_CAUSAL)
+        outs.append(host(sc))
+    np.testing.assert_array_equal(outs[0], outs[1])
+    tri = np.tril(np.ones((L, L), bool))
+    for g in range(Hkv):
+        assert np.isneginf(outs[0][:, g][~tri]).all() and np.isfinite(outs[0][:, g][tri]).all()
+    odd = torch.empty(L, Hkv, L + 1, device="cuda")[:, :, :L]
+    with pytest.raises(lsa.LsaError):
+        lsa.lsa_index_score(kd, odd, q_idx=qd, mode=lsa.MODE_PREFILL_CAUSAL)
+
+
 def _check_prefill_shape(idx, B):
     L = idx.shape[0]
     for i in range(L):
