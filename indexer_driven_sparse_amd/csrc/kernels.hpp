@@ -132,7 +132,7 @@ struct AttnArgs {
 // Decode on the matrix cores (bf16, d = 128, G = 4 or 8, at most 64
 // splits): one workgroup per split of kDecodeSplit list entries, writing a
 // split partial, merged by launch_attention_merge.
-constexpr int kDecodeSplit = 128;
+constexpr int kDecodeSplit = 256;
 bool attention_decode_mfma_supported(int G, int d, int B, bool bf16);
 hipError_t launch_attention_decode_mfma(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attention_merge(const AttnArgs& a, hipStream_t s);

@@ -198,7 +198,7 @@ int validate_select(const lsa_select_desc* d, size_t* ws_need) {
 // ---------------------------------------------------------------------------
 // lsa_indexed_attention
 // Decode shapes the matrix cores take: bf16, d = 128, G = 4 or 8, and a
-// grid of 256-thread workgroups under 2^32 threads. The launch also wants
+// grid of 512-thread workgroups under 2^32 threads. The launch also wants
 // q 16-byte aligned (its rows are read 16 bytes at a time); the workspace
 // is sized for either path, so it depends on the shape alone.
 bool decode_mfma_shape(const lsa_attn_desc* d) {
@@ -206,7 +206,7 @@ bool decode_mfma_shape(const lsa_attn_desc* d) {
   const int G = d->n_q_heads / d->n_kv_heads;
   if (!lsa::attention_decode_mfma_supported(G, d->head_dim, d->topk, d->kv_dtype == LSA_BF16)) return false;
   const int64_t splits = (d->topk + lsa::kDecodeSplit - 1) / lsa::kDecodeSplit;
-  return (int64_t)d->rows * d->n_kv_heads * splits < (int64_t{1} << 24);
+  return (int64_t)d->rows * d->n_kv_heads * splits < (int64_t{1} << 23);
 }
 
 // ---------------------------------------------------------------------------

@@ -315,8 +315,8 @@ def _run_attention(q, K, V, idx, layout, prefill):
     (2, 16, 2, 999, 64, 77, synth.F32, False, "tok", 1.0),
     (5, 4, 4, 100, 128, 1, synth.BF16, False, "tok", 1.0),
     (2, 16, 2, 3000, 128, 700, synth.BF16, False, "tok", 0.8),    # G = 8, ragged last split
-    (1, 8, 2, 20000, 128, 8192, synth.BF16, False, "tok", 1.0),  # the most splits on matrix cores
-    (1, 8, 2, 20000, 128, 8200, synth.BF16, False, "tok", 1.0),  # one split too many: vector path
+    (1, 8, 2, 20000, 128, 16384, synth.BF16, False, "tok", 1.0),  # the most splits on matrix cores
+    (1, 8, 2, 20000, 128, 16400, synth.BF16, False, "tok", 1.0),  # one split too many: vector path
     (2, 8, 1, 500, 128, 1, synth.BF16, False, "tok", 1.0),       # G = 8, one entry
     (600, 8, 1, 600, 128, 256, synth.BF16, True, "tok", 1.0),
 ])
