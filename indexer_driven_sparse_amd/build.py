@@ -38,14 +38,33 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source into indexer_driven_sparse_amd/liblsa.so."""
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every HIP source (one object each, in parallel) and link them
+    into indexer_driven_sparse_amd/liblsa.so. Every call compiles."""
+    import concurrent.futures
+    import tempfile
+
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+    jobs = jobs or min(len(sources()), os.cpu_count() or 1, 16)
+    with tempfile.TemporaryDirectory(prefix="lsa_build_") as tmpdir:
+        objs = []
+        cmds = []
+        for src in sources():
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            objs.append(obj)
+            cmds.append([HIPCC, *compile_flags, "-c", src, "-o", obj])
+        with concurrent.futures.ThreadPoolExecutor(jobs) as pool:
+            for cmd, rc in zip(cmds, pool.map(lambda c: subprocess.call(c), cmds)):
+                if verbose or rc != 0:
+                    print(" ".join(cmd), flush=True)
+                if rc != 0:
+                    raise subprocess.CalledProcessError(rc, cmd)
+        tmp = LIB + ".tmp"
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.check_call(link)
+        os.replace(tmp, LIB)
     return LIB
 
 

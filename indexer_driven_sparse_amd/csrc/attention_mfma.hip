@@ -14,10 +14,14 @@
 //                       KV head, split of 256 entries), one 32-key chunk per
 //                       wave, combined in LDS into a split partial.
 // Keys go by in chunks of 32 selected positions:
-//   gather   each lane loads its keys' K and V pieces; the K pieces are its
-//            QK B operand as loaded, V is transposed through LDS (channel-
-//            major) for the PV B operand; the next chunk's rows are in
-//            flight during the current chunk's softmax and PV;
+//   gather   each quad of lanes reads 64 contiguous bytes of one selected
+//            K or V row (a wave covers whole 256-byte rows), and the rows
+//            land in K and V tiles in LDS, one row per key with its 16-byte
+//            pieces XOR-permuted per key so the stores and the operand reads
+//            touch every bank once; QK reads its B operand from the K tile
+//            with 128-bit LDS loads, PV reads V through gfx950's transposing
+//            LDS read (ds_read_b64_tr_b16); the next chunk's list entries
+//            and rows are in flight during the current chunk's products;
 //   QK       S = Q K^T over the chunk's keys;
 //   softmax  causal and list masks, scale, log2 domain; O and the row sums
 //            stay relative to a reference max raised only when a score

@@ -188,6 +188,20 @@ def _rows2d(t: torch.Tensor, rows: int, name: str) -> int:
     return ld
 
 
+def _need(t, name: str, dtype=None, shape=None) -> None:
+    """The binding is the only layer that sees tensor sizes (the C ABI takes
+    bare pointers), so it checks what the kernels will read or write:
+    dtype, contiguity and exact shape."""
+    if t is None:
+        return
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _check(fn: str, rc: int) -> None:
     if rc != 0:
         raise LsaError(fn, rc, int(_lib().lsa_last_hip_error()))
@@ -224,8 +238,20 @@ def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_id
     d.n_seq, d.n_kv_heads, d.n_keys, d.rank = N, Hkv, T, r
     qb = max(1, int(query_block))
     n_rows = (T + qb - 1) // qb          # prefill rows: tokens, or blocks of qb tokens
+    if q is not None and mode != MODE_DECODE:
+        raise ValueError("q (the fused scoring prep) is a decode input")
     if q is not None and (q.dim() != 3 or q.shape[0] != N or not q.is_contiguous()):
         raise ValueError("q must be contiguous [N,Hq,d]")
+    if w is not None and w.dtype != torch.float32:
+        raise ValueError("w must be float32")
+    if q_idx is not None and q_idx.dtype != (torch.float32 if mode == MODE_DECODE else k_idx.dtype):
+        raise ValueError("q_idx must be float32 (decode) or k_idx's dtype (prefill)")
+    if scores is not None and scores.dtype != torch.float32:
+        raise ValueError("scores must be float32")
+    if out_idx is not None and out_idx.dtype != torch.int32:
+        raise ValueError("out_idx must be int32")
+    if out_score is not None and out_score.dtype != torch.float32:
+        raise ValueError("out_score must be float32")
     if q is not None and (w is None or w.shape[-1] != r or w.shape[-2] != q.shape[2]
                           or not w.is_contiguous() or (w.dim() == 3 and w.shape[0] != Hkv)):
         raise ValueError("w must be contiguous [d,r] or [Hkv,d,r]")
@@ -262,6 +288,8 @@ def _score_desc(k_idx, scores, q, w, q_idx, cand, cand_block, mode, topk, out_id
     if hint is not None:
         if hint.dtype != torch.int32 or not hint.is_contiguous():
             raise ValueError("hint must be a contiguous int32 (bit pattern uint32) tensor")
+        if hint.numel() // max(1, hint.shape[-1]) != N * Hkv:
+            raise ValueError("hint must be [N*Hkv, hint_ld]")
         d.hint = _ptr(hint)
         d.hint_ld = hint.shape[-1]
     return d
@@ -306,15 +334,24 @@ def lsa_score_workspace_bytes(k_idx, scores, *, q=None, w=None, q_idx=None, cand
 
 def _select_desc(scores, topk, out_idx, n, out_score, out_count, n_valid, causal_group, cand,
                  cand_block, n_positions, hint=None, hint_k=0, causal_block=0):
+    if scores.dtype != torch.float32:
+        raise ValueError("scores must be float32")
     rows = scores.numel() // scores.shape[-1]
     if not out_idx.is_contiguous() or out_idx.numel() != rows * topk or out_idx.dtype != torch.int32:
         raise ValueError("out_idx must be contiguous int32 [rows, B]")
-    if out_score is not None and (not out_score.is_contiguous() or out_score.numel() != rows * topk):
-        raise ValueError("out_score must be contiguous [rows, B]")
-    if out_count is not None and (not out_count.is_contiguous() or out_count.numel() != rows):
-        raise ValueError("out_count must be contiguous [rows]")
-    if n_valid is not None and (not n_valid.is_contiguous() or n_valid.numel() != rows):
-        raise ValueError("n_valid must be contiguous [rows]")
+    if out_score is not None and (not out_score.is_contiguous() or out_score.numel() != rows * topk
+                                  or out_score.dtype != torch.float32):
+        raise ValueError("out_score must be contiguous float32 [rows, B]")
+    if out_count is not None and (not out_count.is_contiguous() or out_count.numel() != rows
+                                  or out_count.dtype != torch.int32):
+        raise ValueError("out_count must be contiguous int32 [rows]")
+    if n_valid is not None and (not n_valid.is_contiguous() or n_valid.numel() != rows
+                                or n_valid.dtype != torch.int32):
+        raise ValueError("n_valid must be contiguous int32 [rows]")
+    if cand is not None and cand.dtype != torch.int32:
+        raise ValueError("cand must be int32")
+    if hint is not None and hint.dtype != torch.int32:
+        raise ValueError("hint must be int32 (bit pattern uint32)")
     if n is not None and n > scores.shape[-1]:
         raise ValueError("n exceeds the row length")
     if cand is not None and (not cand.is_contiguous() or cand.numel() // cand.shape[-1] != rows
@@ -373,9 +410,17 @@ def lsa_select_workspace_bytes(scores, topk, out_idx, *, n=None, n_valid=None, c
 
 def _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table=None, n_keys=None,
                query_block=0):
+    if q.dim() != 3:
+        raise ValueError("q must be [rows,Hq,d]")
     rows, Hq, hd = q.shape
-    if k.stride() != v.stride() or k.shape != v.shape:
-        raise ValueError("k and v must share shape and strides")
+    if k.stride() != v.stride() or k.shape != v.shape or k.dtype != v.dtype:
+        raise ValueError("k and v must share shape, strides and dtype")
+    if k.shape[-1] != hd:
+        raise ValueError(f"k/v head dim {k.shape[-1]} differs from q's {hd}")
+    if idx.dtype != torch.int32:
+        raise ValueError("idx must be int32")
+    _need(out, "out", torch.float32)
+    _need(lse, "lse", torch.float32, (rows, Hq))
     if slot_table is None:
         S, T, Hkv, _ = k.shape
         strides = (k.stride(0), k.stride(1), k.stride(2))
@@ -501,6 +546,10 @@ def lsa_project_keys(k: torch.Tensor, w: torch.Tensor, out: torch.Tensor, *, tok
         raise ValueError("token range outside k or out")
     if tuple(out.shape[:2]) != (N, Hkv) or out.shape[3] != w.shape[-1] or w.shape[-2] != hd:
         raise ValueError("out must be [N,Hkv,T,r] and w [d,r] or [Hkv,d,r]")
+    if w.dtype != torch.float32 or not w.is_contiguous() or (w.dim() == 3 and w.shape[0] != Hkv):
+        raise ValueError("w must be contiguous float32 [d,r] or [Hkv,d,r]")
+    if out.stride(-1) != 1 or k.stride(-1) != 1:
+        raise ValueError("k and out must be contiguous in their last dimension")
     d.k_dtype = _dt(k)
     d.k = _ptr(k)
     d.k_stride_seq, d.k_stride_tok, d.k_stride_head = k.stride(0), k.stride(1), k.stride(2)

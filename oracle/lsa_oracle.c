@@ -532,14 +532,14 @@ int lsa_ref_attention(int mode, int rows, int Hq, int Hkv, int d, int B,
       int64_t seq = mode == 0 ? row : 0;
       int64_t tmax = mode == 1 ? (row < T - 1 ? row : T - 1) : T - 1;  /* last visible position */
       const int32_t* I = idx + ((int64_t)(row / qb) * Hkv + g) * B;
-      int64_t qb = task * d;
+      int64_t q_off = task * d;   /* this (row, head)'s query vector */
       double m = -INFINITY;
       for (int b = 0; b < B; ++b) {
         int64_t t = I[b];
         if (t < 0 || t > tmax) continue;
         int64_t kb = seq * s_seq + t * s_tok + (int64_t)g * s_head;
         double acc = 0.0;
-        for (int c = 0; c < d; ++c) acc += elem(q, q_dtype, qb + c) * elem(Kc, kv_dtype, kb + c);
+        for (int c = 0; c < d; ++c) acc += elem(q, q_dtype, q_off + c) * elem(Kc, kv_dtype, kb + c);
         z[b] = acc * scale;
         if (z[b] > m) m = z[b];
       }

@@ -230,6 +230,8 @@ def prefill_topk(q_idx: np.ndarray, k_idx: np.ndarray, B: int, row_begin: int = 
     L, Hkv, r = k_idx.shape
     if row_end is None:
         row_end = L
+    if not 0 <= row_begin <= row_end <= L or q_idx.shape != k_idx.shape:
+        raise ValueError(f"rows [{row_begin}, {row_end}) must lie in [0, {L}] and q_idx match k_idx")
     nr = row_end - row_begin
     idx = np.empty((nr, Hkv, B), dtype=np.int32)
     osc = np.empty((nr, Hkv, B), dtype=np.float64)

@@ -327,3 +327,84 @@ def test_query_block_validation_and_workspace():
     assert lib.lsa_indexed_attention(ctypes.byref(a), None, 0, None) == INVALID
     a = _attn_desc(query_block=-1, mode=1)
     assert lib.lsa_indexed_attention(ctypes.byref(a), None, 0, None) == INVALID
+
+
+def test_binding_rejects_buffers_the_kernels_would_overrun():
+    """The C ABI takes bare pointers, so the binding checks every tensor's
+    dtype, contiguity and shape before building a descriptor: each case
+    below would otherwise make a kernel read or write past a buffer."""
+    import torch
+    rows, Hq, Hkv, T, d, B = 2, 8, 2, 64, 128, 16
+    q = torch.zeros(rows, Hq, d, dtype=torch.bfloat16)
+    k = torch.zeros(rows, T, Hkv, d, dtype=torch.bfloat16)
+    idx = torch.zeros(rows, Hkv, B, dtype=torch.int32)
+    out = torch.zeros(rows, Hq, d)
+    lse = torch.zeros(rows, Hq)
+    bad_attn = [
+        dict(k=torch.zeros(rows, T, Hkv, 64, dtype=torch.bfloat16),
+             v=torch.zeros(rows, T, Hkv, 64, dtype=torch.bfloat16)),     # head dim differs from q
+        dict(idx=idx.long()),                                             # int64 index lists
+        dict(out=out.to(torch.bfloat16)),                                 # kernels write fp32
+        dict(lse=torch.zeros(1)),                                         # too short
+        dict(lse=torch.zeros(rows, Hq, dtype=torch.float64)),             # wrong dtype
+        dict(lse=torch.zeros(Hq, rows).t()),                              # not contiguous
+        dict(v=k.to(torch.float32)),                                      # k and v differ in dtype
+        dict(q=q[0]),                                                     # not [rows,Hq,d]
+    ]
+    for over in bad_attn:
+        kw = dict(q=q, k=k, v=k.clone(), idx=idx, out=out, lse=lse)
+        kw.update(over)
+        with pytest.raises(ValueError):
+            lsa._attn_desc(kw["q"], kw["k"], kw["v"], kw["idx"], kw["out"], kw["lse"],
+                           lsa.MODE_DECODE, 0.0)
+    lsa._attn_desc(q, k, k.clone(), idx, out, lse, lsa.MODE_DECODE, 0.0)   # the good case builds
+
+    N, r = 2, 64
+    kx = torch.zeros(N, Hkv, T, r, dtype=torch.bfloat16)
+    sc = torch.zeros(N, Hkv, T)
+    qi = torch.zeros(N, Hkv, r)
+    bad_score = [
+        dict(scores=sc.to(torch.bfloat16)),                               # kernels write fp32
+        dict(q_idx=qi.to(torch.bfloat16)),                                # decode q_idx is fp32
+        dict(q=torch.zeros(N, Hq, d), w=torch.zeros(d, r, dtype=torch.float64)),
+        dict(hint=torch.zeros(1, 4, dtype=torch.int32)),                  # too few hint rows
+    ]
+    for over in bad_score:
+        kw = dict(scores=sc, q_idx=qi)
+        kw.update(over)
+        with pytest.raises(ValueError):
+            lsa._score_desc(kx, kw["scores"], kw.get("q"), kw.get("w"), kw.get("q_idx"), None, 1,
+                            lsa.MODE_DECODE, 0, None, None, kw.get("hint"))
+    L = 128
+    kp = torch.zeros(L, 1, r, dtype=torch.bfloat16)
+    qp = torch.zeros(L, 1, r, dtype=torch.bfloat16)
+    for over in [dict(out_idx=torch.zeros(L, 1, B, dtype=torch.int64)),
+                 dict(out_score=torch.zeros(L, 1, B, dtype=torch.bfloat16)),
+                 dict(q_idx=qp.float())]:
+        kw = dict(out_idx=torch.zeros(L, 1, B, dtype=torch.int32), out_score=None, q_idx=qp)
+        kw.update(over)
+        with pytest.raises(ValueError):
+            lsa._score_desc(kp, None, None, None, kw["q_idx"], None, 1, lsa.MODE_PREFILL_CAUSAL, B,
+                            kw["out_idx"], kw["out_score"])
+
+    scs = torch.zeros(4, 100)
+    oi = torch.zeros(4, B, dtype=torch.int32)
+    bad_sel = [
+        dict(scores=scs.double()),
+        dict(out_score=torch.zeros(4, B, dtype=torch.bfloat16)),
+        dict(out_count=torch.zeros(4, dtype=torch.int64)),
+        dict(n_valid=torch.zeros(4, dtype=torch.int64)),
+        dict(cand=torch.zeros(4, 100, dtype=torch.int64)),
+        dict(hint=torch.zeros(4, 2, dtype=torch.float32), hint_k=4),
+    ]
+    for over in bad_sel:
+        kw = dict(scores=scs, out_score=None, out_count=None, n_valid=None, cand=None, hint=None,
+                  hint_k=0)
+        kw.update(over)
+        with pytest.raises(ValueError):
+            lsa._select_desc(kw["scores"], B, oi, None, kw["out_score"], kw["out_count"],
+                             kw["n_valid"], 0, kw["cand"], 1, 100, kw["hint"], kw["hint_k"])
+
+    with pytest.raises(ValueError):
+        lsa.lsa_project_keys(k, torch.zeros(d, r, dtype=torch.float64),
+                             torch.zeros(rows, Hkv, T, r, dtype=torch.bfloat16), stream=0)

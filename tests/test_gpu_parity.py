@@ -608,16 +608,17 @@ def test_decode_step_full(name, over):
     _compare_step(case, g, ref, rows)
 
 
-def test_decode_step_headline_workload_sampled():
+def test_decode_step_headline_workload_every_row():
     """Decode, 4 sequences, T=131072, GQA 32/8, d=128, r=64, B=2048, bf16 --
     the benchmarked workload at full size, in the benchmark's launch shape;
-    the oracle checks sampled (sequence, KV head) rows."""
+    every one of the 32 (sequence, KV head) rows against the oracle: its
+    projected keys, index set, output and lse."""
     case = synth.workload("decode_t128k_b2048")
-    say("decode step headline 4x131072 B=2048")
+    say("decode step headline 4x131072 B=2048, every row")
     kd = torch.empty(case.N, case.Hkv, case.T, case.r, dtype=torch.bfloat16, device="cuda")
     lsa.lsa_project_keys(dev(case.K), dev(case.W), kd)
-    rows = [0, 13, 31]
-    # the GPU-built cache must equal the oracle's on the sampled rows
+    rows = list(range(case.N * case.Hkv))
+    # the GPU-built cache must equal the oracle's on every row
     for row in rows:
         n, gh = divmod(row, case.Hkv)
         ref_k = oracle.project_keys(case.K[n:n + 1, :, gh:gh + 1], case.W, case.dtype)
@@ -969,6 +970,38 @@ def test_prefill_c4_full_size():
         c = min(B, i + 1)
         row = gi[i, 0]
         assert (row[c:] == -1).all() and np.all(np.diff(row[:c]) > 0) and row[c - 1] <= i
+
+
+def test_prefill_attention_c4_full_size_sampled_tokens():
+    """L = 65536, 8 query heads on 1 KV head, d = 128, B = 2048: the fused
+    indexer's own top-2048 lists feed per-token causal prefill attention in
+    the benchmark's launch shape; sampled tokens against the oracle's fp64
+    attention over the same lists (positions after the token masked: the
+    oracle sees the cache cut at the token)."""
+    case = synth.workload("prefill_l64k")
+    L, Hkv, B, Hq, d = case.L, case.Hkv, case.B, case.Hq, case.d
+    say("prefill attention C4 full size, sampled tokens", L, Hq, Hkv, d, B)
+    qd, kd = dev(case.q_idx), dev(case.k_idx)
+    idx = torch.empty(L, Hkv, B, dtype=torch.int32, device="cuda")
+    lsa.lsa_index_score(kd, None, q_idx=qd, mode=lsa.MODE_PREFILL_CAUSAL, topk=B, out_idx=idx)
+    del qd, kd
+    torch.cuda.empty_cache()
+    Q, K, V = dev(case.Q), dev(case.K), dev(case.V)
+    out = torch.empty(L, Hq, d, device="cuda")
+    lse = torch.empty(L, Hq, device="cuda")
+    lsa.lsa_indexed_attention(Q, K, V, idx, out, lse=lse, mode=lsa.MODE_PREFILL_CAUSAL)
+    torch.cuda.synchronize()
+    gi, go, gl = host(idx), host(out), host(lse)
+    tokens = [0, 1, 2, 31, 32, 2046, 2047, 2048, 2049, 4095, 4096, 32767, 32768, 65534, 65535]
+    tokens += sorted(int(t) for t in np.random.default_rng(11).choice(np.arange(3, L - 1), 25,
+                                                                       replace=False))
+    for i in tokens:
+        c = min(B, i + 1)
+        row = gi[i, 0]
+        assert (row[c:] == -1).all() and (row[:c] >= 0).all() and (row[:c] <= i).all(), i
+        o, l = oracle.attention(case.Q[i:i + 1], case.K[:, :i + 1], case.V[:, :i + 1], gi[i:i + 1])
+        np.testing.assert_allclose(go[i], o[0], rtol=0, atol=ATTN_ATOL, err_msg=f"token {i}")
+        np.testing.assert_allclose(gl[i], l[0], rtol=0, atol=LSE_ATOL, err_msg=f"token {i}")
 
 
 @pytest.mark.timeout(900)
