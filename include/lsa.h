@@ -41,7 +41,8 @@
  *     misalignment is rejected (there is no slow path).
  *   - Query head h belongs to KV head h / (Hq / Hkv).
  *   - Reentrant and thread-safe; the only global state is a per-device cache
- *     of "is this a gfx950" answers.
+ *     of "is this a gfx950" answers and, for lsa_indexed_attention_noalloc,
+ *     one static scratch buffer per device (and its looked-up address).
  *   - Return value: LSA_OK (0) or a negative lsa_status. After LSA_ERR_HIP,
  *     lsa_last_hip_error() gives the HIP error code (thread-local).
  */
@@ -73,7 +74,8 @@ enum {
   LSA_ERR_UNSUPPORTED = -2,    /* valid but not built: dtype combo, r, d, G */
   LSA_ERR_WORKSPACE = -3,      /* workspace missing or smaller than required */
   LSA_ERR_NO_DEVICE_CODE = -4, /* current device is not gfx950 */
-  LSA_ERR_HIP = -5             /* a HIP call failed; see lsa_last_hip_error */
+  LSA_ERR_HIP = -5,            /* a HIP call failed; see lsa_last_hip_error */
+  LSA_ERR_SCRATCH_LIMIT = -6   /* the shape needs more than the static scratch (noalloc calls) */
 };
 
 /* Modes. Decode: a row is one (sequence, KV head). Prefill: a row is one
@@ -300,6 +302,32 @@ typedef struct lsa_attn_desc {
 int lsa_indexed_attention(const lsa_attn_desc* desc, void* workspace, size_t workspace_bytes,
                           void* stream);
 size_t lsa_attention_workspace_bytes(const lsa_attn_desc* desc);
+
+/*
+ * lsa_indexed_attention_noalloc: lsa_indexed_attention with no workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * The split partials live in a static device buffer of
+ * LSA_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends; the call itself allocates and frees nothing.
+ *   - Same descriptor, semantics and outputs as lsa_indexed_attention (the
+ *     same kernels; results are bit-identical).
+ *   - A shape whose lsa_attention_workspace_bytes exceeds
+ *     LSA_NOALLOC_SCRATCH_BYTES is rejected with LSA_ERR_SCRATCH_LIMIT
+ *     before anything is launched. 4 MiB holds the partials of decode with
+ *     up to 252 (sequence, KV head) rows of 4 query heads at B = 2048 and
+ *     head_dim 128 (16640 bytes per row); the 4 x 8-row step at that shape
+ *     needs 1.06 MB.
+ *   - Every call on one GPU shares that GPU's buffer, which keeps the last
+ *     call's contents: calls ordered on one stream are safe; calls that
+ *     overlap in time on one GPU (other streams, other threads) race. No
+ *     part of the buffer needs to start at zero: a call writes every
+ *     partial it reads.
+ *   - The first call on a device, with that device current, looks up the
+ *     device's copy of the buffer (hipGetSymbolAddress) and keeps it.
+ */
+#define LSA_NOALLOC_SCRATCH_BYTES (4u << 20)
+int lsa_indexed_attention_noalloc(const lsa_attn_desc* desc, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Setup calls                                                              */

@@ -245,6 +245,79 @@ int check_ws(void* ws, size_t have, size_t need) {
   return LSA_OK;
 }
 
+// Launch an attention call whose descriptor has been validated; ws holds
+// the split partials (the caller's workspace, or the static scratch).
+int run_attention(const lsa_attn_desc* d, void* ws, void* stream) {
+  lsa::AttnArgs a{};
+  a.q = d->q;
+  a.k = d->k;
+  a.v = d->v;
+  const bool paged = d->slot_table != nullptr;
+  a.s_seq = paged ? 0 : d->kv_stride_seq;   // a pool has no per-sequence base
+  a.s_tok = d->kv_stride_tok;
+  a.s_head = d->kv_stride_head;
+  a.slot = d->slot_table;
+  a.slot_ld = paged ? d->slot_table_ld : 0;
+  a.n_rows_kv = paged ? d->n_pool_rows : d->n_keys;
+  a.idx = d->idx;
+  a.rows = d->rows;
+  a.Hq = d->n_q_heads;
+  a.Hkv = d->n_kv_heads;
+  a.d = d->head_dim;
+  a.B = d->topk;
+  a.T = d->n_keys;
+  a.prefill = d->mode == LSA_MODE_PREFILL_CAUSAL;
+  a.qblk = d->query_block > 1 ? d->query_block : 1;
+  const float scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->head_dim);
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.out = d->out;
+  a.lse = d->lse;
+  a.partial = (float*)ws;
+  const bool mfma_decode = decode_mfma_shape(d) && al16(d->q);
+  lsa::attention_plan(d->rows, d->n_kv_heads, a.Hq / a.Hkv, a.d, a.B, mfma_decode, &a.splits,
+                      &a.keys_per_split);
+  hipError_t e;
+  if (mfma_decode)
+    e = lsa::launch_attention_decode_mfma(a, (hipStream_t)stream);
+  else if (lsa::attention_mfma_supported(a, d->kv_dtype == LSA_BF16))
+    e = lsa::launch_attention_mfma(a, (hipStream_t)stream);
+  else
+    e = lsa::launch_attention(a, d->q_dtype == LSA_BF16, d->kv_dtype == LSA_BF16, (hipStream_t)stream);
+  return e == hipSuccess ? LSA_OK : hip_fail(e);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Static scratch of lsa_indexed_attention_noalloc: each GPU the library runs
+// on holds one copy until the process ends. Host code never uses this name
+// as an address (on the host it is only a stand-in for the device symbol);
+// it uses the per-device pointer that scratch_ptr looks up once.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[LSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::atomic<void*> g_scratch[kMaxDevices];   // device address of `scratch`, per device
+
+// The current device's copy of `scratch`, looked up on the first call on
+// that device (with it current) and kept.
+int scratch_ptr(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e);
+  if (dev < 0 || dev >= kMaxDevices) return LSA_ERR_NO_DEVICE_CODE;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e);
+    if (p == nullptr || !al16(p)) return LSA_ERR_HIP;
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return LSA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -426,42 +499,17 @@ int lsa_indexed_attention(const lsa_attn_desc* d, void* ws, size_t ws_bytes, voi
   LSA_TRY(validate_attn(d, &need));
   LSA_TRY(check_ws(ws, ws_bytes, need));
   LSA_TRY(check_device());
-  lsa::AttnArgs a{};
-  a.q = d->q;
-  a.k = d->k;
-  a.v = d->v;
-  const bool paged = d->slot_table != nullptr;
-  a.s_seq = paged ? 0 : d->kv_stride_seq;   // a pool has no per-sequence base
-  a.s_tok = d->kv_stride_tok;
-  a.s_head = d->kv_stride_head;
-  a.slot = d->slot_table;
-  a.slot_ld = paged ? d->slot_table_ld : 0;
-  a.n_rows_kv = paged ? d->n_pool_rows : d->n_keys;
-  a.idx = d->idx;
-  a.rows = d->rows;
-  a.Hq = d->n_q_heads;
-  a.Hkv = d->n_kv_heads;
-  a.d = d->head_dim;
-  a.B = d->topk;
-  a.T = d->n_keys;
-  a.prefill = d->mode == LSA_MODE_PREFILL_CAUSAL;
-  a.qblk = d->query_block > 1 ? d->query_block : 1;
-  const float scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->head_dim);
-  a.scale_log2 = scale * 1.4426950408889634f;
-  a.out = d->out;
-  a.lse = d->lse;
-  a.partial = (float*)ws;
-  const bool mfma_decode = decode_mfma_shape(d) && al16(d->q);
-  lsa::attention_plan(d->rows, d->n_kv_heads, a.Hq / a.Hkv, a.d, a.B, mfma_decode, &a.splits,
-                      &a.keys_per_split);
-  hipError_t e;
-  if (mfma_decode)
-    e = lsa::launch_attention_decode_mfma(a, (hipStream_t)stream);
-  else if (lsa::attention_mfma_supported(a, d->kv_dtype == LSA_BF16))
-    e = lsa::launch_attention_mfma(a, (hipStream_t)stream);
-  else
-    e = lsa::launch_attention(a, d->q_dtype == LSA_BF16, d->kv_dtype == LSA_BF16, (hipStream_t)stream);
-  return e == hipSuccess ? LSA_OK : hip_fail(e);
+  return run_attention(d, ws, stream);
+}
+
+int lsa_indexed_attention_noalloc(const lsa_attn_desc* d, void* stream) {
+  size_t need = 0;
+  LSA_TRY(validate_attn(d, &need));
+  if (need > LSA_NOALLOC_SCRATCH_BYTES) return LSA_ERR_SCRATCH_LIMIT;
+  LSA_TRY(check_device());
+  void* ws = nullptr;
+  LSA_TRY(scratch_ptr(&ws));
+  return run_attention(d, ws, stream);
 }
 
 size_t lsa_attention_workspace_bytes(const lsa_attn_desc* d) {
@@ -550,6 +598,7 @@ const char* lsa_status_str(int status) {
     case LSA_ERR_WORKSPACE: return "workspace missing or too small";
     case LSA_ERR_NO_DEVICE_CODE: return "current device is not gfx950";
     case LSA_ERR_HIP: return "HIP error";
+    case LSA_ERR_SCRATCH_LIMIT: return "needs more scratch than the static buffer holds";
   }
   return "unknown status";
 }

@@ -24,7 +24,9 @@ MODE_DECODE = 0
 MODE_PREFILL_CAUSAL = 1
 
 STATUS = {0: "LSA_OK", -1: "LSA_ERR_INVALID_ARG", -2: "LSA_ERR_UNSUPPORTED",
-          -3: "LSA_ERR_WORKSPACE", -4: "LSA_ERR_NO_DEVICE_CODE", -5: "LSA_ERR_HIP"}
+          -3: "LSA_ERR_WORKSPACE", -4: "LSA_ERR_NO_DEVICE_CODE", -5: "LSA_ERR_HIP",
+          -6: "LSA_ERR_SCRATCH_LIMIT"}
+NOALLOC_SCRATCH_BYTES = 4 << 20     # LSA_NOALLOC_SCRATCH_BYTES
 
 
 class LsaError(RuntimeError):
@@ -95,6 +97,7 @@ _SIGS = {
     "lsa_index_score": (_I32, [_P, _P, _c.c_size_t, _P]),
     "lsa_topk_select": (_I32, [_P, _P, _c.c_size_t, _P]),
     "lsa_indexed_attention": (_I32, [_P, _P, _c.c_size_t, _P]),
+    "lsa_indexed_attention_noalloc": (_I32, [_P, _P]),
     "lsa_project_keys": (_I32, [_P, _P]),
     "lsa_build_centroids": (_I32, [_P, _P]),
     "lsa_score_workspace_bytes": (_c.c_size_t, [_P]),
@@ -479,6 +482,20 @@ def lsa_indexed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx
     ws, wsb = _workspace(lib.lsa_attention_workspace_bytes(_c.byref(d)), workspace, q.device)
     _check("lsa_indexed_attention",
            lib.lsa_indexed_attention(_c.byref(d), _ptr(ws), wsb, _stream(stream)))
+
+
+def lsa_indexed_attention_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                  idx: torch.Tensor, out: torch.Tensor, *, lse=None,
+                                  mode: int = MODE_DECODE, scale: float = 0.0, stream=None,
+                                  slot_table=None, n_keys=None, query_block: int = 0) -> None:
+    """lsa_indexed_attention with its split partials in the library's static
+    per-GPU scratch (NOALLOC_SCRATCH_BYTES): no workspace, no allocation --
+    for callers that cannot allocate. Same arguments and bit-identical
+    results; a shape needing more scratch raises LsaError
+    (LSA_ERR_SCRATCH_LIMIT). Calls overlapping in time on one GPU race."""
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys, query_block)
+    _check("lsa_indexed_attention_noalloc",
+           _lib().lsa_indexed_attention_noalloc(_c.byref(d), _stream(stream)))
 
 
 def lsa_attention_workspace_bytes(q, k, v, idx, out, *, lse=None, mode=MODE_DECODE,

@@ -40,7 +40,7 @@ def test_descriptor_sizes_and_abi_version():
         assert lib.lsa_desc_size(which) == ctypes.sizeof(cls)
     assert lib.lsa_desc_size(99) == 0
     assert lsa.abi_version() == 1
-    for st in [0, -1, -2, -3, -4, -5]:
+    for st in [0, -1, -2, -3, -4, -5, -6]:
         assert lib.lsa_status_str(st)
     assert lib.lsa_status_str(12345) == b"unknown status"
 
@@ -408,3 +408,22 @@ def test_binding_rejects_buffers_the_kernels_would_overrun():
     with pytest.raises(ValueError):
         lsa.lsa_project_keys(k, torch.zeros(d, r, dtype=torch.float64),
                              torch.zeros(rows, Hkv, T, r, dtype=torch.bfloat16), stream=0)
+
+
+def test_noalloc_attention_rejects_shapes_beyond_its_scratch():
+    """The no-allocation attention call validates like lsa_indexed_attention
+    and refuses, before touching the device, any shape whose partials would
+    not fit its static scratch."""
+    lib = lsa._lib()
+    SCRATCH_LIMIT = -6
+    # the headline decode shape (4 x 8 rows, 8 splits) fits
+    assert lib.lsa_attention_workspace_bytes(ctypes.byref(_attn_desc())) <= lsa.NOALLOC_SCRATCH_BYTES
+    # decode, 4096 sequences x 8 KV heads x 4 query heads, B = 2048: 8 splits
+    # of fp32 partials (130 floats per head) = 133 MB > 4 MiB
+    big = _attn_desc(rows=4096, n_q_heads=32, n_kv_heads=8, head_dim=128, topk=2048,
+                     n_keys=131072, q_dtype=lsa.BF16, kv_dtype=lsa.BF16)
+    need = lib.lsa_attention_workspace_bytes(ctypes.byref(big))
+    assert need > lsa.NOALLOC_SCRATCH_BYTES
+    assert lib.lsa_indexed_attention_noalloc(ctypes.byref(big), None) == SCRATCH_LIMIT
+    bad = _attn_desc(rows=0)
+    assert lib.lsa_indexed_attention_noalloc(ctypes.byref(bad), None) == INVALID
