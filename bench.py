@@ -658,6 +658,14 @@ def main() -> int:
     score_window(10)
     score_ms = float(np.median([score_window(20) for _ in range(7)]))
 
+    # the same step as the three separate calls (scoring, select, attention)
+    plan3 = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, fused=False)
+    three_us = _windows_us(torch, lambda i: plan3.run(Q, W, inst[i & 1][2], inst[i & 1][0], inst[i & 1][1]),
+                           max(steps, 7), warm=args.warmup)
+    del plan3
+    log(f"the same step as three separate calls: {three_us:.1f} us/step; fused path: "
+        f"{plan.step_ws is not None and lsa.lsa_step_is_fused(Q, W, inst[0][2], inst[0][0], inst[0][1], plan.idx, plan.out, one_launch=plan.one_launch)}")
+
     keys = N * Hkv * T
     kidx_bytes = keys * r * 2
     sel_kv_bytes = N * Hkv * B * 2 * d * 2
@@ -680,6 +688,7 @@ def main() -> int:
     # the step's outputs on instance 0, for the same-run parity check
     step(0)
     torch.cuda.synchronize()
+    plan_error = plan.step_error()
     gpu_idx = plan.idx.cpu().numpy()
     gpu_out = plan.out.cpu().numpy()
     gpu_lse = plan.lse.cpu().numpy()
@@ -758,7 +767,7 @@ def main() -> int:
         prefill = prefill_leg(torch, lsa, synth)
 
     # no throughput figure without same-run parity of the timed step
-    ok = parity["pass"]
+    ok = parity["pass"] and plan_error == 0
     steps_per_s = 1000.0 / ms_per_step if ok else None
     traffic = measured_traffic(kidx_bytes)
     line = {
@@ -789,6 +798,8 @@ def main() -> int:
                      "avg_launch_us": score_ms * 1000.0,
                      "launch_timing": "median of 7 windows of 20 back-to-back launches",
                      "traffic": traffic},
+        "three_calls_us_per_step": three_us if ok else None,
+        "step_error_word": plan_error,
         "graph_replay": {"us_per_step": graph_us if ok else None,
                          "steps_per_s": 1e6 / graph_us if ok else None,
                          "hbm_frac_end_to_end": (step_bytes / (graph_us * 1e-6) / (HBM_PEAK_GBPS * 1e9)

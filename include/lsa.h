@@ -330,6 +330,86 @@ size_t lsa_attention_workspace_bytes(const lsa_attn_desc* desc);
 int lsa_indexed_attention_noalloc(const lsa_attn_desc* desc, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* lsa_decode_step                                                          */
+/* ------------------------------------------------------------------------ */
+/*
+ * One whole flat decode step (JSSA Fig. 1, the four stages of Fig. 9): for
+ * every (sequence, KV head) row, the scoring preparation, the projected-key
+ * scores, the exact top-B selection and the indexed attention. The results
+ * are exactly those of the sequence
+ *     lsa_index_score   (decode, q and w given, selection hint on)
+ *     lsa_topk_select   (with that hint)
+ *     lsa_indexed_attention
+ * on the same arguments: out_idx (and q_idx, out_score) bit-identical,
+ * out / lse within the attention's own rounding. By default the call runs
+ * those three calls in sequence. With flags = LSA_STEP_ONE_LAUNCH, shapes
+ * with a bf16 or fp8 projected-key cache of 64 or 128 bytes per key, head
+ * dim 128, 1, 2, 4 or 8 query heads per KV head, B a multiple of 32 that
+ * the scoring hints vouch for (T >= 32 B), at most 32 chunks of 4096 keys
+ * per row and out_idx on a 128-byte boundary run instead as one persistent
+ * launch: each (sequence, KV head) row is cut into chunks of 4096 keys, one
+ * workgroup per chunk, all of a row's workgroups on one XCD (its L2 carries
+ * the row's hand-offs); the chunk's scorer keeps its scores in LDS, the
+ * row's last scorer derives the threshold from the hints, every chunk lists
+ * its keys above it, the row's last lister selects the exact top B, every
+ * chunk attends over its share of the selection and the last one merges
+ * the partials. Either way the call is asynchronous on `stream`, allocates
+ * nothing and takes one workspace (lsa_step_workspace_bytes, for the same
+ * flags) that holds the scores, hints, lists, attention partials and, at
+ * its head, the persistent launch's control words.
+ * Workspace contract: the workspace must be all zero before the first call
+ * that uses it (allocate it zeroed, or clear it once); every call leaves
+ * the control words zero again, except the 32-bit error word at byte
+ * offset 36, which stays set (bit 0) once a call gives up an internal
+ * wait; the outputs of such a call are not valid. Two calls that share a
+ * workspace must not overlap in time.
+ */
+typedef struct lsa_step_desc {
+  uint32_t struct_size;      /* sizeof(lsa_step_desc) */
+  int32_t n_seq;             /* N */
+  int32_t n_q_heads;         /* Hq, a multiple of Hkv */
+  int32_t n_kv_heads;        /* Hkv */
+  int32_t head_dim;          /* d */
+  int32_t rank;              /* r */
+  int32_t n_keys;            /* T cached positions */
+  int32_t topk;              /* B >= 1 */
+  const void* q;             /* [N,Hq,d] contiguous, q_dtype (LSA_F32 / LSA_BF16) */
+  int32_t q_dtype;
+  int32_t w_per_head;        /* 0: w is [d,r]; 1: w is [Hkv,d,r] */
+  const float* w;            /* fp32 projection */
+  const void* k_idx;         /* projected-key cache [N,Hkv,T,r], innermost r contiguous */
+  int32_t k_idx_dtype;       /* LSA_F32 / LSA_BF16 / LSA_FP8_E4M3 */
+  int32_t kv_dtype;          /* dtype of K and V (= q_dtype) */
+  int64_t k_stride_seq;      /* projected-key cache strides (elements) */
+  int64_t k_stride_head;
+  int64_t k_stride_tok;
+  const void* k;             /* K cache, default [N,T,Hkv,d], through its strides */
+  const void* v;             /* V cache, same strides */
+  int64_t kv_stride_seq;
+  int64_t kv_stride_tok;
+  int64_t kv_stride_head;
+  float scale;               /* <= 0: 1/sqrt(d) */
+  int32_t flags;             /* 0, or LSA_STEP_ONE_LAUNCH */
+  float* q_idx;              /* optional out: fp32 [N,Hkv,r] */
+  int32_t* out_idx;          /* [N,Hkv,B] ascending positions, -1 padded */
+  float* out_score;          /* optional out: fp32 [N,Hkv,B] */
+  float* out;                /* fp32 [N,Hq,d] */
+  float* lse;                /* optional out: fp32 [N,Hq] */
+} lsa_step_desc;
+
+/* flags: run the one-launch kernel (scoring, selection and attention in a
+ * single persistent launch) where the shape allows it; without the flag the
+ * step always runs the three calls. */
+#define LSA_STEP_ONE_LAUNCH 1
+
+int lsa_decode_step(const lsa_step_desc* desc, void* workspace, size_t workspace_bytes, void* stream);
+size_t lsa_step_workspace_bytes(const lsa_step_desc* desc);
+/* 1 when the descriptor (its shape and flags) runs as the one persistent
+ * launch, 0 when it runs the three calls in sequence, -1 when the
+ * descriptor is invalid. */
+int lsa_step_is_fused(const lsa_step_desc* desc);
+
+/* ------------------------------------------------------------------------ */
 /* Setup calls                                                              */
 /* ------------------------------------------------------------------------ */
 /*
@@ -415,7 +495,7 @@ const char* lsa_status_str(int status);   /* static string, never NULL */
 int lsa_last_hip_error(void);             /* HIP error of this thread's last LSA_ERR_HIP */
 int lsa_abi_version(void);                /* LSA_ABI_VERSION */
 /* sizeof of a descriptor, for bindings: 0 score, 1 select, 2 attention,
- * 3 project, 4 centroid; 0 for anything else. */
+ * 3 project, 4 centroid, 5 step; 0 for anything else. */
 size_t lsa_desc_size(int which);
 
 #ifdef __cplusplus

@@ -110,6 +110,46 @@ int select_segments(int n, int B, bool hint_usable);
 void select_bind_workspace(SelectArgs& a, int rows, void* ws);
 hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s);
 
+// ----- fused decode step (scoring, selection and attention in one launch) -----
+// Control words at the head of the step workspace: [8] the count of finished
+// workgroups, [9] an error word (bit 0: a wait gave up), then six counters
+// and flags per row. Zero before the first launch; each launch leaves them
+// zero again, except the error word.
+struct StepArgs {
+  ScoreDecodeArgs sc;                // scoring of every row (prep fused, hints on)
+  int B;
+  int hint_count, hint_k;
+  int2* lists;                       // [rows, wpr, step_chunk_slots()] (score bits, slot)
+  int4* meta;                        // [rows, wpr, step_meta_stride()] {count, max key, t_lo, 0}
+  int32_t* out_idx;                  // [rows, B]
+  float* out_score;                  // [rows, B] or nullptr
+  const void* q;                     // attention: [N,Hq,d]
+  const void* k;
+  const void* v;
+  int64_t kv_s_seq, kv_s_tok, kv_s_head;
+  int kv_bf16;
+  int Hq, Hkv, T;
+  float scale_log2;
+  float* out;
+  float* lse;
+  float* partial;                    // [rows, wpr, step_partial_stride(G)]: G x (max, sum, d outputs)
+  uint32_t* ctrl;                    // step_ctrl_words(rows) control words
+  int rows;
+  int wpr;                           // workgroups per row: ceil(T / step_chunk_slots())
+  int nxcc;                          // the device's XCDs (1..8): row r runs on XCD r % nxcc
+};
+int step_ctrl_words(int rows);
+int step_chunk_slots();
+int step_meta_stride();              // int4 per part of meta
+int step_partial_stride(int G);      // floats per part of partial
+// The fused step takes bf16 / fp8 projected-key caches of 64 or 128 bytes
+// per key, fp32 / bf16 K/V with head_dim 128 and 1, 2, 4 or 8 query heads
+// per KV head, rows of at most 32 chunks, B a multiple of 32, and hints
+// that vouch for B keys; selected positions must start on a 128-byte line.
+bool decode_step_supported(int rows, int n, int B, int r, int k_dt, int kv_dt, int G, int d, int hint_count,
+                           int hint_k);
+hipError_t launch_decode_step(const StepArgs& a, int k_dt, hipStream_t s);
+
 // ----- indexed attention -----------------------------------------------------
 struct AttnArgs {
   const void* q;

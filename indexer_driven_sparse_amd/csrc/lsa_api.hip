@@ -56,6 +56,20 @@ int check_device() {
   return st == 1 ? LSA_OK : LSA_ERR_NO_DEVICE_CODE;
 }
 
+// XCD count of the current device, cached per device (0 when unknown).
+std::atomic<int> g_device_xccs[kMaxDevices];
+
+int device_xccs() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = g_device_xccs[dev].load(std::memory_order_acquire);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess) return 0;
+    g_device_xccs[dev].store(n, std::memory_order_release);
+  }
+  return n;
+}
+
 #define LSA_TRY(expr)              \
   do {                             \
     int _rc = (expr);              \
@@ -288,6 +302,138 @@ int run_attention(const lsa_attn_desc* d, void* ws, void* stream) {
 
 }  // namespace
 
+namespace {
+
+// ---------------------------------------------------------------------------
+// lsa_decode_step: the three calls' descriptors, built from one step
+// descriptor, and the workspace layout they share.
+// ---------------------------------------------------------------------------
+struct StepPlan {
+  lsa_score_desc score;
+  lsa_select_desc select;
+  lsa_attn_desc attn;
+  bool fused;
+  int rows, wpr;
+  size_t off_scores, off_hint, off_sel, off_attn;           // three calls
+  size_t off_lists, off_meta, off_partial;                  // fused
+  size_t total;
+  size_t sel_bytes, attn_bytes;
+};
+
+int plan_step(const lsa_step_desc* d, StepPlan* p) {
+  if (!d || d->struct_size != sizeof(lsa_step_desc)) return LSA_ERR_INVALID_ARG;
+  if (d->n_seq < 1 || d->n_kv_heads < 1 || d->n_keys < 1 || d->topk < 1) return LSA_ERR_INVALID_ARG;
+  if (d->flags & ~LSA_STEP_ONE_LAUNCH) return LSA_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)d->n_seq * d->n_kv_heads;
+  if (rows > 65535) return LSA_ERR_UNSUPPORTED;
+  const int64_t ld = ((int64_t)d->n_keys + 31) / 32 * 32;   // rows of whole 128-byte lines
+  const int hint_count = lsa::score_hint_count(d->n_keys, d->k_idx_dtype);
+  const size_t ctrl_bytes = align256((size_t)lsa::step_ctrl_words((int)rows) * 4);
+  p->rows = (int)rows;
+  p->off_scores = ctrl_bytes;
+  p->off_hint = p->off_scores + align256((size_t)rows * ld * sizeof(float));
+  p->off_sel = p->off_hint + align256((size_t)rows * hint_count * sizeof(uint32_t));
+
+  lsa_score_desc& sd = p->score;
+  std::memset(&sd, 0, sizeof(sd));
+  sd.struct_size = sizeof(sd);
+  sd.mode = LSA_MODE_DECODE;
+  sd.n_seq = d->n_seq;
+  sd.n_kv_heads = d->n_kv_heads;
+  sd.n_keys = d->n_keys;
+  sd.rank = d->rank;
+  sd.q_idx = d->q_idx;
+  sd.q = d->q;
+  sd.q_dtype = d->q_dtype;
+  sd.n_q_heads = d->n_q_heads;
+  sd.head_dim = d->head_dim;
+  sd.w_per_head = d->w_per_head;
+  sd.w = d->w;
+  sd.k_idx = d->k_idx;
+  sd.k_idx_dtype = d->k_idx_dtype;
+  sd.k_stride_seq = d->k_stride_seq;
+  sd.k_stride_head = d->k_stride_head;
+  sd.k_stride_tok = d->k_stride_tok;
+  sd.scores = (float*)(uintptr_t)(p->off_scores + 256);   // placeholders: validation checks alignment only
+  sd.scores_ld = ld;
+  sd.hint = (uint32_t*)(uintptr_t)(p->off_hint + 256);
+  sd.hint_ld = hint_count;
+  if (!d->q) return LSA_ERR_INVALID_ARG;
+  size_t need = 0;
+  LSA_TRY(validate_score(&sd, &need));
+
+  lsa_select_desc& se = p->select;
+  std::memset(&se, 0, sizeof(se));
+  se.struct_size = sizeof(se);
+  se.rows = (int)rows;
+  se.n = d->n_keys;
+  se.topk = d->topk;
+  se.scores = sd.scores;
+  se.scores_ld = ld;
+  se.cand_block = 1;
+  se.out_idx = d->out_idx;
+  se.out_score = d->out_score;
+  se.hint = sd.hint;
+  se.hint_ld = hint_count;
+  se.hint_count = hint_count;
+  se.hint_k = lsa::score_hint_k(d->k_idx_dtype);
+  LSA_TRY(validate_select(&se, &p->sel_bytes));
+
+  lsa_attn_desc& at = p->attn;
+  std::memset(&at, 0, sizeof(at));
+  at.struct_size = sizeof(at);
+  at.mode = LSA_MODE_DECODE;
+  at.rows = d->n_seq;
+  at.n_q_heads = d->n_q_heads;
+  at.n_kv_heads = d->n_kv_heads;
+  at.head_dim = d->head_dim;
+  at.topk = d->topk;
+  at.n_keys = d->n_keys;
+  at.q = d->q;
+  at.q_dtype = d->q_dtype;
+  at.kv_dtype = d->kv_dtype;
+  at.k = d->k;
+  at.v = d->v;
+  at.kv_stride_seq = d->kv_stride_seq;
+  at.kv_stride_tok = d->kv_stride_tok;
+  at.kv_stride_head = d->kv_stride_head;
+  at.idx = d->out_idx;
+  at.scale = d->scale;
+  at.out = d->out;
+  at.lse = d->lse;
+  LSA_TRY(validate_attn(&at, &p->attn_bytes));
+
+  p->off_attn = p->off_sel + align256(p->sel_bytes);
+  p->total = p->off_attn + p->attn_bytes;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  p->fused = (d->flags & LSA_STEP_ONE_LAUNCH) &&
+             lsa::decode_step_supported((int)rows, d->n_keys, d->topk, d->rank, d->k_idx_dtype, d->kv_dtype,
+                                        G, d->head_dim, hint_count, se.hint_k) &&
+             ((uintptr_t)d->out_idx & 127u) == 0;
+  if (p->fused) {
+    const int chunk = lsa::step_chunk_slots();
+    p->wpr = (d->n_keys + chunk - 1) / chunk;
+    const size_t parts = (size_t)rows * p->wpr;
+    p->off_lists = p->off_sel;
+    p->off_meta = p->off_lists + align256(parts * chunk * sizeof(int2));
+    p->off_partial = p->off_meta + align256(parts * lsa::step_meta_stride() * sizeof(int4));
+    const size_t fused_total = p->off_partial + parts * lsa::step_partial_stride(G) * sizeof(float);
+    p->total = std::max(p->total, fused_total);
+  }
+  return LSA_OK;
+}
+
+// Points the plan's descriptors at the workspace.
+void bind_step(StepPlan* p, void* ws) {
+  char* b = (char*)ws;
+  p->score.scores = (float*)(b + p->off_scores);
+  p->score.hint = (uint32_t*)(b + p->off_hint);
+  p->select.scores = p->score.scores;
+  p->select.hint = p->score.hint;
+}
+
+}  // namespace
+
 // ---------------------------------------------------------------------------
 // Static scratch of lsa_indexed_attention_noalloc: each GPU the library runs
 // on holds one copy until the process ends. Host code never uses this name
@@ -512,6 +658,82 @@ int lsa_indexed_attention_noalloc(const lsa_attn_desc* d, void* stream) {
   return run_attention(d, ws, stream);
 }
 
+int lsa_decode_step(const lsa_step_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  StepPlan p;
+  LSA_TRY(plan_step(d, &p));
+  LSA_TRY(check_ws(ws, ws_bytes, p.total));
+  LSA_TRY(check_device());
+  bind_step(&p, ws);
+  char* b = (char*)ws;
+  hipStream_t s = (hipStream_t)stream;
+  const int nxcc = p.fused ? device_xccs() : 0;
+  if (nxcc >= 1 && nxcc <= 8) {
+    lsa::StepArgs a{};
+    lsa::ScoreDecodeArgs& sc = a.sc;
+    sc.k_idx = d->k_idx;
+    sc.ks_seq = d->k_stride_seq;
+    sc.ks_head = d->k_stride_head;
+    sc.ks_tok = d->k_stride_tok;
+    sc.Hkv = d->n_kv_heads;
+    sc.T = d->n_keys;
+    sc.r = d->rank;
+    sc.q = d->q;
+    sc.q_idx_out = d->q_idx;
+    sc.q_bf16 = d->q_dtype == LSA_BF16;
+    sc.Hq = d->n_q_heads;
+    sc.d = d->head_dim;
+    sc.w_per_head = d->w_per_head;
+    sc.w = d->w;
+    sc.cand_block = 1;
+    sc.n_out = d->n_keys;
+    sc.scores = p.score.scores;
+    sc.scores_ld = p.score.scores_ld;
+    sc.hint = p.score.hint;
+    sc.hint_ld = p.score.hint_ld;
+    a.B = d->topk;
+    a.hint_count = p.select.hint_count;
+    a.hint_k = p.select.hint_k;
+    a.lists = (int2*)(b + p.off_lists);
+    a.meta = (int4*)(b + p.off_meta);
+    a.out_idx = d->out_idx;
+    a.out_score = d->out_score;
+    a.q = d->q;
+    a.k = d->k;
+    a.v = d->v;
+    a.kv_s_seq = d->kv_stride_seq;
+    a.kv_s_tok = d->kv_stride_tok;
+    a.kv_s_head = d->kv_stride_head;
+    a.kv_bf16 = d->kv_dtype == LSA_BF16;
+    a.Hq = d->n_q_heads;
+    a.Hkv = d->n_kv_heads;
+    a.T = d->n_keys;
+    const float scale = d->scale > 0.f ? d->scale : 1.0f / std::sqrt((float)d->head_dim);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out = d->out;
+    a.lse = d->lse;
+    a.partial = (float*)(b + p.off_partial);
+    a.ctrl = (uint32_t*)b;
+    a.rows = p.rows;
+    a.wpr = p.wpr;
+    a.nxcc = nxcc;
+    hipError_t e = lsa::launch_decode_step(a, d->k_idx_dtype, s);
+    return e == hipSuccess ? LSA_OK : hip_fail(e);
+  }
+  LSA_TRY(lsa_index_score(&p.score, nullptr, 0, stream));
+  LSA_TRY(lsa_topk_select(&p.select, b + p.off_sel, p.sel_bytes, stream));
+  return run_attention(&p.attn, p.attn_bytes ? b + p.off_attn : nullptr, stream);
+}
+
+size_t lsa_step_workspace_bytes(const lsa_step_desc* d) {
+  StepPlan p;
+  return plan_step(d, &p) == LSA_OK ? p.total : 0;
+}
+
+int lsa_step_is_fused(const lsa_step_desc* d) {
+  StepPlan p;
+  return plan_step(d, &p) == LSA_OK ? (p.fused ? 1 : 0) : -1;
+}
+
 size_t lsa_attention_workspace_bytes(const lsa_attn_desc* d) {
   size_t need = 0;
   return validate_attn(d, &need) == LSA_OK ? need : 0;
@@ -614,6 +836,7 @@ size_t lsa_desc_size(int which) {
     case 2: return sizeof(lsa_attn_desc);
     case 3: return sizeof(lsa_project_desc);
     case 4: return sizeof(lsa_centroid_desc);
+    case 5: return sizeof(lsa_step_desc);
   }
   return 0;
 }

@@ -1,0 +1,826 @@
+// Fused decode step: one launch computes the whole step of every
+// (sequence, KV head) row -- scoring preparation, projected-key scores,
+// exact top-B and indexed attention (JSSA, "Joint Subspace Sparse Attention
+// for Efficient Long-Context Decoding", Fig. 1, and the four stages of
+// Fig. 9).
+//
+// Why one launch: scoring is a long HBM stream, while the selection and the
+// attention are chains of short, latency-bound steps over a few MB. Run as
+// separate kernels, every boundary adds a ramp and a drain (several
+// microseconds each on MI355X) and the selection re-reads every score.
+//
+// Layout: the device's XCDs each take rows x, x + nxcc, ... (nxcc XCDs):
+// a workgroup reads its XCD from the hardware, draws a ticket from that
+// XCD's queue and becomes one (row, chunk) of kChunk slots, so all of a
+// row's workgroups share one L2. Each scores its chunk (the stream of
+// score_body.hpp, unchanged) and keeps the scores in LDS. After that the
+// row's workgroups work together, with no further pass over the scores:
+//   1. threshold  the last workgroup of the row to finish scoring derives a
+//                 lower bound t_lo of the row's B-th key from the row's
+//                 selection hints (the r-th largest of hints that each
+//                 vouch for hint_k keys) and publishes it;
+//   2. collect    every workgroup lists its slots whose key reaches t_lo,
+//                 in slot order, as (score bits, slot), straight from its
+//                 LDS; the last one to finish runs the exact
+//                 selection over the row's lists (8-bit radix levels in
+//                 registers, positions written in ascending order by one
+//                 prefix scan; a list that cannot settle it falls back to a
+//                 radix selection over the row's stored scores);
+//   3. attend     every workgroup attends over its share of the row's B
+//                 selected positions (each K and V row read in place, one
+//                 256-byte row per wave-wide load, softmax in fp32 in the
+//                 log2 domain) and writes a partial (max, sum, output);
+//                 the last one merges the row's partials by log-sum-exp.
+// The hand-offs stay inside the row's XCD (the rules are stated beside
+// add_l below). The waits in 1-3 only ever wait for workgroups of the same
+// row, which hold consecutive tickets of one XCD's queue; every wait is
+// bounded, and a timeout only sets an error bit, so every wave exits. The
+// last workgroup out leaves the control words zero for the next launch.
+//
+// The indices equal those of the separate scoring and select calls bit for
+// bit (both are the exact top-B of the same scores); the attention's
+// arithmetic differs from the separate call's kernels only in summation
+// order.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "score_body.hpp"
+#include "select_row.hpp"
+
+#ifndef LSA_STEP_WG_PER_CU
+#define LSA_STEP_WG_PER_CU 4   // resident workgroups per CU the register budget allows
+#endif
+
+namespace lsa {
+namespace {
+
+using namespace scoring;
+using namespace sel;
+
+constexpr int kWgThreads = 256;
+static_assert(kWgThreads == kScoreThreads, "the scoring body is written for 256 threads");
+constexpr int kGroups = 2;                       // groups_in_flight(): 64-slot groups per wave step
+constexpr int kWgStep = kGroups * 4 * 64;        // slots one workgroup covers per step
+constexpr int kSteps = 8;                        // steps per chunk
+constexpr int kChunk = kSteps * kWgStep;         // 4096 slots per workgroup
+constexpr int kKeep = kSteps * kGroups;          // scores each lane keeps
+constexpr int kFinPer = 32;                      // list entries per thread in the exact selection
+constexpr int kFinCap = kWgThreads * kFinPer;      // longest list refined in registers
+constexpr int kMaxG = 8;                         // query heads per KV head (attention)
+constexpr int kD = 128;                          // head dim (attention: two channels per lane)
+constexpr int kBatch = 8;                        // list entries per wave per attention batch
+constexpr int kMaxParts = 32;                    // workgroups per row (merge weights in LDS)
+constexpr int kSpinLimit = 1 << 21;              // polls before a wait gives up
+// floats per part's partial (G heads of max, sum and kD outputs), rounded
+// up to whole 128-byte lines
+__host__ __device__ constexpr int partial_stride(int G) { return (G * (kD + 2) + 31) / 32 * 32; }
+
+// control words: [0..7] per-XCD tickets, [8] finished workgroups, [9] error
+// bits (device-coherent), then one block per row, each in its own 4 KiB,
+// used only by the row's XCD
+enum { kCtlQueue = 0, kCtlDone = 8, kCtlErr = 9, kCtlRow0 = 1024, kCtlPerRow = 1024 };
+enum { kRowScored = 0, kRowThr = 2, kRowCollected = 3, kRowSelected = 4, kRowAttended = 5 };
+constexpr int kMetaStride = 8;   // int4 per part's meta: one 128-byte line each
+
+__device__ __forceinline__ void st_c(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_c(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Hand-off inside one XCD. A row's workgroups all run on one XCD and so
+// share one L2; the L1 of each CU writes through to it. The row's counters
+// and flags, and the hints, are read and written only by atomics, which are
+// performed in that L2 (a plain load could be served by a stale L1 line).
+// The other shared data (scores, lists, meta, selected positions, partials)
+// is stored plainly and loaded plainly, under two rules that keep every L1
+// line a reader hits current: every 128-byte line of it has one writing
+// workgroup, and nothing loads it before the counter that publishes it has
+// been seen (the L1s start each launch empty). A writer waits for its
+// stores before it bumps the counter.
+__device__ __forceinline__ uint32_t add_l(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+// An atomic read: an OR with zero, the zero hidden from the compiler (which
+// would otherwise turn the idempotent atomic into a load).
+__device__ __forceinline__ uint32_t ld_l(uint32_t* p) {
+  uint32_t zero;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(zero));
+  return __hip_atomic_fetch_or(p, zero, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+__device__ __forceinline__ unsigned xcd_id() {
+  return __builtin_amdgcn_s_getreg((15 << 11) | 20) & 15u;   // HW_REG_XCC_ID
+}
+
+// Every memory operation of the workgroup has completed before thread 0
+// publishes it.
+__device__ __forceinline__ void all_done() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// Thread 0 polls the XCD-local word *p until it reaches target (bounded);
+// a timeout sets error bit 0. Returns the value seen last, to every thread
+// (through *slot in LDS).
+__device__ __forceinline__ uint32_t wait_until(uint32_t* p, uint32_t target, uint32_t* err, int* slot) {
+  if (threadIdx.x == 0) {
+    int spins = 0;
+    uint32_t v;
+    while ((v = ld_l(p)) < target && spins < kSpinLimit) {
+      __builtin_amdgcn_s_sleep(4);
+      ++spins;
+    }
+    if (spins >= kSpinLimit) __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *slot = (int)v;
+  }
+  __syncthreads();
+  const uint32_t v = (uint32_t)*slot;
+  __syncthreads();   // the slot is reused
+  return v;
+}
+
+struct FinShared {
+  uint32_t hist[256];
+  int scan[kWgThreads / 64 + 1];
+  int seg_off[kWgThreads + 1];
+  uint32_t kmax;
+  int bin, above;
+};
+
+struct CollectShared {
+  int cnt[kSteps * kGroups * 4];
+  int off[kSteps * kGroups * 4];
+  uint32_t wmax[4];
+  int total;
+};
+
+struct AttnShared {
+  int32_t idx[kWgThreads];
+  float m[4][kMaxG];
+  float l[4][kMaxG];
+  float o[4][kMaxG][kD];
+  float w[kMaxParts][kMaxG];   // merge: per-partial weights
+  float mstar[kMaxG];
+};
+
+struct StepShared {
+  ScoreShared score;
+  float keep[kKeep * kWgThreads];   // this workgroup's scores, kept for the collect
+  union {
+    SegShared seg;       // threshold
+    CollectShared col;
+    FinShared fin;
+    AttnShared att;
+  } u;
+  int flag;   // a role decision (ticket, last arrival), read by every wave
+  int wval;   // a value waited for or published to the workgroup
+};
+
+// ---------------------------------------------------------------------------
+// 1. the row's threshold from its hints (the r-th largest of folded hint
+// entries, on 16-bit prefixes, by two 8-bit radix levels; 0 = take all)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t row_threshold(uint32_t* hrow, int hint_count, int hint_k, int B, SegShared& sh) {
+  const int tid = threadIdx.x;
+  const int m = (hint_count + 4 * kWgThreads - 1) / (4 * kWgThreads);
+  const int ne = (hint_count + m - 1) / m;
+  const int r = (B + m * hint_k - 1) / (m * hint_k);
+  uint32_t p[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = tid + q * kWgThreads;
+    uint32_t val = 0xffffffffu;
+    for (int mm = 0; mm < m; ++mm) {
+      const int h = e * m + mm;
+      val = min(val, h < hint_count ? ld_l(hrow + h) : 0u);
+    }
+    p[q] = (e < ne ? val : 0u) >> 16;
+  }
+  sh.h1[tid] = 0u;
+  sh.h2[tid] = 0u;
+  if (tid == 0) sh.bin = -1;
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (tid + q * kWgThreads < ne) atomicAdd(&sh.h1[p[q] >> 8], 1u);
+  __syncthreads();
+  uint32_t t_lo = 0u;
+  if (r <= ne) {
+    seg_level(sh, sh.h1, r);
+    const int b1 = sh.bin, r2 = r - sh.above;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (tid + q * kWgThreads < ne && (int)(p[q] >> 8) == b1) atomicAdd(&sh.h2[p[q] & 255u], 1u);
+    __syncthreads();
+    seg_level(sh, sh.h2, r2);
+    t_lo = ((uint32_t)b1 << 24) | ((uint32_t)sh.bin << 16);
+  }
+  return t_lo;
+}
+
+// ---------------------------------------------------------------------------
+// 2b. exact top-B of a row from its lists (every key >= t_lo, in slot order)
+// ---------------------------------------------------------------------------
+template <int kPer>
+__device__ __forceinline__ int radix_level_regs(FinShared& sh, const uint32_t (&key)[kPer], int i0,
+                                                int total, uint32_t& pre, int& fixed, int& nd) {
+  const int tid = threadIdx.x;
+  const int width = min(8, 32 - fixed);
+  const int shift = 32 - fixed - width;
+  const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
+  const int nb = 1 << width;
+  sh.hist[tid] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (i0 + j < total && (key[j] & pmask) == pre) atomicAdd(&sh.hist[(key[j] >> shift) & (nb - 1)], 1u);
+  __syncthreads();
+  const int c = tid < nb ? (int)sh.hist[nb - 1 - tid] : 0;
+  int tot;
+  const int excl = block_exclusive_scan<kWgThreads>(c, sh.scan, &tot);
+  if (tid < nb && excl < nd && nd <= excl + c) {
+    sh.bin = nb - 1 - tid;
+    sh.above = excl;
+  }
+  __syncthreads();
+  const int bin = sh.bin;
+  nd -= sh.above;
+  const int cnt = (int)sh.hist[bin];
+  pre |= (uint32_t)bin << shift;
+  fixed += width;
+  __syncthreads();   // hist and bin are reused by the next level
+  return cnt;
+}
+
+// Exact top-B of a whole row straight from its stored scores (every slot
+// valid): 8-bit radix levels over the row, then the positions in ascending
+// order, the lowest positions first among keys equal to the B-th. The path
+// for rows whose lists cannot settle it.
+__device__ __forceinline__ void select_row_general(const StepArgs& a, FinShared& sh, int row) {
+  const int tid = threadIdx.x;
+  const int B = a.B;
+  const int64_t nv = a.sc.n_out;
+  const float* srow = a.sc.scores + (int64_t)row * a.sc.scores_ld;
+  int32_t* orow = a.out_idx + (int64_t)row * B;
+  float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
+  uint32_t pre = 0u;
+  int fixed = 0, nd = B;
+  while (fixed < 32) {
+    const int shift = 24 - fixed;
+    const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
+    sh.hist[tid] = 0u;
+    __syncthreads();
+    for (int64_t i = tid; i < nv; i += kWgThreads) {
+      const uint32_t key = order_key(srow[i]);
+      if ((key & pmask) == pre) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    const int c = (int)sh.hist[255 - tid];
+    int tot;
+    const int excl = block_exclusive_scan<kWgThreads>(c, sh.scan, &tot);
+    if (excl < nd && nd <= excl + c) {
+      sh.bin = 255 - tid;
+      sh.above = excl;
+    }
+    __syncthreads();
+    const int bin = sh.bin;
+    nd -= sh.above;
+    const int cnt = (int)sh.hist[bin];
+    pre |= (uint32_t)bin << shift;
+    fixed += 8;
+    __syncthreads();
+    if (cnt == nd) break;
+  }
+  const uint32_t bmask = fixed >= 32 ? ~0u : (~0u << (32 - fixed));
+  const uint32_t top = pre | ~bmask;
+  // slot order, 4 slots per thread per tile: a taken key's position is the
+  // count of keys above the bin before it plus its rank among the in-bin
+  // keys before it (only the first nd of those are taken)
+  int a_before = 0, i_before = 0;
+  for (int64_t t0 = 0; t0 < nv; t0 += 4 * kWgThreads) {
+    uint32_t key[4];
+    bool ok[4];
+    int na = 0, ni = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int64_t i = t0 + 4 * tid + k;
+      ok[k] = i < nv;
+      key[k] = ok[k] ? order_key(srow[i]) : 0u;
+      na += ok[k] && key[k] > top;
+      ni += ok[k] && (key[k] & bmask) == pre;
+    }
+    int tot;
+    const int pref = block_exclusive_scan<kWgThreads>(na | (ni << 16), sh.scan, &tot);
+    int pa = a_before + (pref & 0xffff), pi = i_before + (pref >> 16);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (!ok[k]) continue;
+      const int64_t i = t0 + 4 * tid + k;
+      int pos = -1;
+      if (key[k] > top) {
+        pos = pa + min(pi, nd);
+        ++pa;
+      } else if ((key[k] & bmask) == pre) {
+        if (pi < nd) pos = pa + pi;
+        ++pi;
+      }
+      if (pos >= 0) {
+        orow[pos] = (int32_t)i;
+        if (osc) osc[pos] = srow[i];
+      }
+    }
+    a_before += tot & 0xffff;
+    i_before += tot >> 16;
+  }
+}
+
+__device__ __forceinline__ void select_row_exact(const StepArgs& a, FinShared& sh, int row) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int B = a.B, nseg = a.wpr;
+  const int4* meta = a.meta + (int64_t)row * nseg * kMetaStride;
+  int cnt = 0;
+  uint32_t km = 0u;
+  if (tid < nseg) {
+    const uint64_t lo = *(const uint64_t*)(meta + tid * kMetaStride);
+    cnt = (int)(uint32_t)lo;
+    km = (uint32_t)(lo >> 32);
+  }
+  const uint32_t t_lo = ((const uint32_t*)meta)[2];
+  if (tid == 0) sh.kmax = 0u;
+  int total;
+  const int off = block_exclusive_scan<kWgThreads>(cnt, sh.scan, &total);
+  if (tid < nseg) sh.seg_off[tid] = off;
+  if (tid == 0) sh.seg_off[nseg] = total;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) km = max(km, (uint32_t)__shfl_xor((int)km, o, 64));
+  if (lane == 0) atomicMax(&sh.kmax, km);
+  __syncthreads();
+  if (total < B || total > kFinCap) {
+    select_row_general(a, sh, row);
+    return;
+  }
+  // thread t holds list entries t*kFinPer .. (list order is slot order)
+  const int i0 = tid * kFinPer;
+  int sg = 0;
+  if (i0 < total) {
+    int lo = 0, hi = nseg - 1;   // last segment starting at or before i0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (sh.seg_off[mid] <= i0) lo = mid; else hi = mid - 1;
+    }
+    sg = lo;
+  }
+  // the keys stay in registers; the slots are read again (from the L2) for
+  // the entries that are taken. Every entry's address is worked out (from
+  // the LDS segment offsets) before the loads go out, so they are all in
+  // flight at once rather than one round trip each.
+  const uint32_t* lrow = (const uint32_t*)(a.lists + (int64_t)row * nseg * kChunk);
+  const int sg0 = sg;
+  uint32_t key[kFinPer];
+  {
+    int addr[kFinPer];
+#pragma unroll
+    for (int j = 0; j < kFinPer; ++j) {
+      const int i = i0 + j;
+      addr[j] = -1;
+      if (i < total) {
+        while (sh.seg_off[sg + 1] <= i) ++sg;
+        addr[j] = sg * kChunk + (i - sh.seg_off[sg]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kFinPer; ++j) key[j] = order_key(__uint_as_float(addr[j] >= 0 ? lrow[2 * addr[j]] : 0u));
+  }
+  const uint32_t kmax = sh.kmax;
+  int fixed = t_lo == kmax ? 32 : __clz(t_lo ^ kmax);
+  uint32_t pre = fixed == 0 ? 0u : (t_lo & (~0u << (32 - fixed)));
+  int nd = B;
+  while (fixed < 32)
+    if (radix_level_regs<kFinPer>(sh, key, i0, total, pre, fixed, nd) == nd) break;
+  const uint32_t bmask = fixed >= 32 ? ~0u : (fixed == 0 ? 0u : (~0u << (32 - fixed)));
+  const uint32_t top = pre | ~bmask;
+  int na = 0, ni = 0;
+#pragma unroll
+  for (int j = 0; j < kFinPer; ++j) {
+    if (i0 + j < total) {
+      na += key[j] > top;
+      ni += (key[j] & bmask) == pre;
+    }
+  }
+  int tot2;
+  const int pref = block_exclusive_scan<kWgThreads>(na | (ni << 16), sh.scan, &tot2);
+  int pa = pref & 0xffff, pi = pref >> 16;
+  int32_t* orow = a.out_idx + (int64_t)row * B;
+  float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
+  const uint64_t* lrow64 = (const uint64_t*)lrow;
+  sg = sg0;
+  // output in batches of kOutBatch entries: positions and addresses first,
+  // then the batch's loads together, then its stores
+  constexpr int kOutBatch = 8;
+#pragma unroll
+  for (int j0 = 0; j0 < kFinPer; j0 += kOutBatch) {
+    int pos[kOutBatch], addr[kOutBatch];
+#pragma unroll
+    for (int jj = 0; jj < kOutBatch; ++jj) {
+      const int j = j0 + jj, i = i0 + j;
+      pos[jj] = -1;
+      addr[jj] = 0;
+      if (i < total) {
+        while (sh.seg_off[sg + 1] <= i) ++sg;
+        addr[jj] = sg * kChunk + (i - sh.seg_off[sg]);
+        if (key[j] > top) {
+          pos[jj] = pa + min(pi, nd);
+          ++pa;
+        } else if ((key[j] & bmask) == pre) {
+          if (pi < nd) pos[jj] = pa + pi;
+          ++pi;
+        }
+      }
+    }
+    uint64_t e[kOutBatch];
+#pragma unroll
+    for (int jj = 0; jj < kOutBatch; ++jj) e[jj] = pos[jj] >= 0 ? lrow64[addr[jj]] : 0ull;
+#pragma unroll
+    for (int jj = 0; jj < kOutBatch; ++jj) {
+      if (pos[jj] < 0) continue;
+      orow[pos[jj]] = (int32_t)(e[jj] >> 32);
+      if (osc) osc[pos[jj]] = __uint_as_float((uint32_t)e[jj]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. attention over this workgroup's share of the row's list: a partial
+// (max m, sum l, output o; log2 domain) per query head
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__device__ __forceinline__ void load_ch2(const void* base, int64_t off, bool ok, float& x0, float& x1) {
+  // channels 2 * lane and 2 * lane + 1 of one row; a skipped entry reads
+  // row 0 and is masked
+  if constexpr (BF16) {
+    const uint32_t w = *((const uint32_t*)((const uint16_t*)base + (ok ? off : 0)) + threadIdx.x % 64);
+    x0 = bf16_lo(w);
+    x1 = bf16_hi(w);
+  } else {
+    const float2 v = *((const float2*)((const float*)base + (ok ? off : 0)) + threadIdx.x % 64);
+    x0 = v.x;
+    x1 = v.y;
+  }
+}
+
+template <bool BF16, int G>
+__device__ __forceinline__ void attend_part(const StepArgs& a, AttnShared& sh, int row, int part) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int n = row / a.Hkv, g = row % a.Hkv;
+  const int B = a.B;
+  const int per = (B + a.wpr - 1) / a.wpr;
+  const int e0 = part * per, e1 = min(B, e0 + per);
+  const int ne = max(0, e1 - e0);
+  const int32_t* irow = a.out_idx + (int64_t)row * B;
+  // the part's list entries (written by another workgroup of the row)
+  for (int i = tid; i < ne; i += kWgThreads) sh.idx[i] = irow[e0 + i];
+  // this lane's two channels of each of the group's query heads
+  float q0[G], q1[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    const int64_t qo = ((int64_t)n * a.Hq + (int64_t)g * G + h) * kD;
+    load_ch2<BF16>(a.q, qo, true, q0[h], q1[h]);
+  }
+  __syncthreads();
+  const int64_t kv0 = (int64_t)n * a.kv_s_seq + (int64_t)g * a.kv_s_head;
+  float m[G], l[G], o0[G], o1[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+    o0[h] = 0.f;
+    o1[h] = 0.f;
+  }
+  // wave wid takes batches wid, wid + 4, ... of kBatch entries
+  for (int b0 = wid * kBatch; b0 < ne; b0 += 4 * kBatch) {
+    float k0[kBatch], k1[kBatch], v0[kBatch], v1[kBatch];
+    bool ok[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int t = b0 + i < ne ? sh.idx[b0 + i] : -1;
+      ok[i] = t >= 0 && t < a.T;
+      const int64_t off = kv0 + (int64_t)t * a.kv_s_tok;
+      load_ch2<BF16>(a.k, off, ok[i], k0[i], k1[i]);
+      load_ch2<BF16>(a.v, off, ok[i], v0[i], v1[i]);
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      float z[kBatch];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        float s = sum_lanes<16>(fmaf(q0[h], k0[i], q1[h] * k1[i]));
+        s += __shfl_xor(s, 16, 64);
+        s += __shfl_xor(s, 32, 64);
+        z[i] = ok[i] ? s * a.scale_log2 : -INFINITY;
+        mb = fmaxf(mb, z[i]);
+      }
+      const float mn = fmaxf(m[h], mb);
+      if (mn == -INFINITY) continue;   // nothing valid yet for this head
+      const float f = exp2f(m[h] - mn);   // 0 when m was -inf
+      l[h] *= f;
+      o0[h] *= f;
+      o1[h] *= f;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const float pz = exp2f(z[i] - mn);
+        l[h] += pz;
+        o0[h] = fmaf(pz, v0[i], o0[h]);
+        o1[h] = fmaf(pz, v1[i], o1[h]);
+      }
+      m[h] = mn;
+    }
+  }
+  // combine the four waves into the workgroup's partial
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    if (lane == 0) {
+      sh.m[wid][h] = m[h];
+      sh.l[wid][h] = l[h];
+    }
+    sh.o[wid][h][2 * lane] = o0[h];
+    sh.o[wid][h][2 * lane + 1] = o1[h];
+  }
+  __syncthreads();
+  float* pbase = a.partial + ((int64_t)row * a.wpr + part) * partial_stride(G);
+  for (int e = tid; e < G * kD; e += kWgThreads) {
+    const int h = e / kD, c = e % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sh.m[w][h]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = exp2f(sh.m[w][h] - M);
+        L = fmaf(sh.l[w][h], f, L);
+        O = fmaf(sh.o[w][h][c], f, O);
+      }
+    }
+    float* ph = pbase + h * (kD + 2);
+    ph[2 + c] = O;
+    if (c == 0) {
+      ph[0] = M;
+      ph[1] = L;
+    }
+  }
+}
+
+// Merge of the row's partials by log-sum-exp into out and lse.
+template <int G>
+__device__ __forceinline__ void merge_row(const StepArgs& a, AttnShared& sh, int row) {
+  const int tid = threadIdx.x;
+  const int n = row / a.Hkv, g = row % a.Hkv;
+  const int P = a.wpr;
+  const float* base = a.partial + (int64_t)row * P * partial_stride(G);
+  for (int e = tid; e < P * G; e += kWgThreads) {
+    const int p = e / G, h = e % G;
+    sh.w[p][h] = base[(int64_t)p * partial_stride(G) + h * (kD + 2)];
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int p = 0; p < P; ++p) M = fmaxf(M, sh.w[p][tid]);
+    sh.mstar[tid] = M;
+  }
+  __syncthreads();
+  for (int e = tid; e < P * G; e += kWgThreads) {
+    const int p = e / G, h = e % G;
+    const float M = sh.mstar[h];
+    sh.w[p][h] = M == -INFINITY ? 0.f : exp2f(sh.w[p][h] - M);
+  }
+  __syncthreads();
+  // thread (h, c): c < kD the head's output channel, c == kD its sum; the
+  // parts' values are loaded eight at a time, all in flight together
+  for (int e = tid; e < G * (kD + 1); e += kWgThreads) {
+    const int h = e / (kD + 1), c = e % (kD + 1);
+    const float* col = base + h * (kD + 2) + (c == kD ? 1 : 2 + c);
+    float acc = 0.f;
+    for (int p0 = 0; p0 < P; p0 += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = p0 + u < P ? col[(int64_t)(p0 + u) * partial_stride(G)] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (p0 + u < P) acc = fmaf(sh.w[p0 + u][h], x[u], acc);
+    }
+    if (c == kD) sh.l[0][h] = acc;
+    else sh.o[0][h][c] = acc;
+  }
+  __syncthreads();
+  const float kLn2 = 0.69314718055994531f;
+  for (int e = tid; e < G * kD; e += kWgThreads) {
+    const int h = e / kD, c = e % kD;
+    const float L = sh.l[0][h];
+    const int64_t oh = (int64_t)n * a.Hq + (int64_t)g * G + h;
+    a.out[oh * kD + c] = L > 0.f ? sh.o[0][h][c] / L : 0.f;
+    if (c == 0 && a.lse) a.lse[oh] = L > 0.f ? (sh.mstar[h] + log2f(L)) * kLn2 : -INFINITY;
+  }
+}
+
+// The last workgroup out clears the launch-wide words (tickets, count)
+// for the next launch; the error word stays set for the caller to read.
+__device__ __forceinline__ void finish_launch(const StepArgs& a) {
+  if (threadIdx.x == 0) {
+    uint32_t* const ctl = a.ctrl;
+    if (add_c(ctl + kCtlDone, 1u) == gridDim.x - 1u) {
+      for (int i = 0; i < 8; ++i) st_c(ctl + kCtlQueue + i, 0u);
+      st_c(ctl + kCtlDone, 0u);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int DT, int LPK, bool BF16, int G>
+__global__ __launch_bounds__(kWgThreads, LSA_STEP_WG_PER_CU) void decode_step_kernel(StepArgs a) {
+  __shared__ StepShared sh;
+  constexpr int KPI = kWave / LPK;
+  constexpr uint64_t kColumn = LPK == 8 ? 0x0101010101010101ull : 0x1111111111111111ull;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  uint32_t* const ctl = a.ctrl;
+  uint32_t* const err = ctl + kCtlErr;
+  // this workgroup's (row, part), from its XCD's queue: of nxcc XCDs, XCD x
+  // serves rows x, x + nxcc, ..., so all of a row's workgroups share one L2
+  const int nx = a.nxcc;
+  const int x = (int)(xcd_id() % (unsigned)nx);
+  if (tid == 0) sh.flag = (int)add_c(ctl + kCtlQueue + x, 1u);
+  __syncthreads();
+  const int ticket = __builtin_amdgcn_readfirstlane(sh.flag);
+  const int nr = x < a.rows ? (a.rows - x + nx - 1) / nx : 0;
+  __syncthreads();
+  if (ticket >= nr * a.wpr) {   // more workgroups landed on this XCD than it has work
+    finish_launch(a);
+    return;
+  }
+  const int row = x + nx * (ticket / a.wpr), part = ticket % a.wpr;
+  uint32_t* const rc = ctl + kCtlRow0 + row * kCtlPerRow;
+  const int64_t c0 = (int64_t)part * kChunk;
+  const int64_t c1 = min((int64_t)a.sc.n_out, c0 + kChunk);
+
+  // ---- scoring (the unchanged stream), keeping the scores in LDS ----
+  score_chunk<DT, LPK, false, true, kSteps, false>(a.sc, row, c0, c1, sh.score, true, sh.keep);
+  all_done();
+
+  // ---- 1. threshold: the row's last scorer derives it from the hints ----
+  if (tid == 0) sh.flag = add_l(rc + kRowScored, 1u) == (uint32_t)a.wpr - 1u;
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(sh.flag)) {
+    const uint32_t t = row_threshold(a.sc.hint + (int64_t)row * a.sc.hint_ld, a.hint_count, a.hint_k, a.B,
+                                     sh.u.seg);
+    // the threshold's low 16 bits are zero: bit 0 marks the word as set
+    if (tid == 0) add_l(rc + kRowThr, t | 1u);
+    if (tid == 0) sh.wval = (int)t;
+    __syncthreads();
+  } else {
+    wait_until(rc + kRowThr, 1u, err, &sh.wval);
+  }
+  const uint32_t t_lo = __builtin_amdgcn_readfirstlane((uint32_t)sh.wval) & ~0xffffu;
+
+  // ---- 2. collect from LDS: keys >= t_lo, in slot order ----
+  {
+    const int l = lane % LPK;
+    // lanes of column b (lane % LPK == b) hold slots b * KPI + lane / LPK of
+    // a 64-slot group, so a lane's rank in slot order counts the taken lanes
+    // of the lower columns and the lower taken lanes of its own column
+    const uint64_t colmask = kColumn << l;
+    // the ballot of group (s, u): which lanes take their slot (computed again
+    // when the entries are written, rather than held in registers)
+    auto taken = [&](int s, int u, uint32_t* key_out) {
+      const int64_t slot = c0 + (int64_t)s * kWgStep + u * 256 + wid * 64 + l * KPI + lane / LPK;
+      const uint32_t key = order_key(sh.keep[(s * kGroups + u) * kWgThreads + tid]);
+      *key_out = key;
+      return slot < c1 && (t_lo == 0u || key >= t_lo);
+    };
+    uint32_t kmax = 0u;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) {
+        uint32_t key;
+        const bool take = taken(s, u, &key);
+        const uint64_t bm = ballot64(take);
+        if (take) kmax = max(kmax, key);
+        if (lane == 0) sh.u.col.cnt[s * 8 + u * 4 + wid] = __popcll(bm);
+      }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+    if (lane == 0) sh.u.col.wmax[wid] = kmax;
+    __syncthreads();
+    if (wid == 0) {   // groups in slot order: (step, u, wave)
+      const int c = sh.u.col.cnt[lane];
+      int v = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(v, o, 64);
+        if (lane >= o) v += y;
+      }
+      sh.u.col.off[lane] = v - c;
+      if (lane == 63) sh.u.col.total = v;
+    }
+    __syncthreads();
+    uint64_t* lout = (uint64_t*)(a.lists + ((int64_t)row * a.wpr + part) * kChunk);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+      for (int u = 0; u < kGroups; ++u) {
+        uint32_t key;
+        const uint64_t bm = ballot64(taken(s, u, &key));
+        if (!((bm >> lane) & 1ull)) continue;
+        int rank = rank_below(bm & colmask);
+#pragma unroll
+        for (int b = 0; b < LPK; ++b)
+          if (b < l) rank += __popcll(bm & (kColumn << b));
+        const int64_t slot = c0 + (int64_t)s * kWgStep + u * 256 + wid * 64 + l * KPI + lane / LPK;
+        const int pos = sh.u.col.off[s * 8 + u * 4 + wid] + rank;
+        lout[pos] = (((uint64_t)(uint32_t)slot << 32) |
+                     __float_as_uint(sh.keep[(s * kGroups + u) * kWgThreads + tid]));
+      }
+    if (tid == 0) {
+      uint32_t km = sh.u.col.wmax[0];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) km = max(km, sh.u.col.wmax[w]);
+      uint64_t* mt = (uint64_t*)(a.meta + ((int64_t)row * a.wpr + part) * kMetaStride);
+      mt[0] = ((uint64_t)km << 32) | (uint32_t)sh.u.col.total;
+      mt[1] = (uint64_t)t_lo;
+    }
+  }
+  all_done();
+  if (tid == 0) sh.flag = add_l(rc + kRowCollected, 1u) == (uint32_t)a.wpr - 1u;
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(sh.flag)) {
+    select_row_exact(a, sh.u.fin, row);
+    all_done();
+    if (tid == 0) add_l(rc + kRowSelected, 1u);
+  } else {
+    wait_until(rc + kRowSelected, 1u, err, &sh.wval);
+  }
+
+  // ---- 3. attention over this workgroup's share of the row's positions ----
+  attend_part<BF16, G>(a, sh.u.att, row, part);
+  all_done();
+  if (tid == 0) sh.flag = add_l(rc + kRowAttended, 1u) == (uint32_t)a.wpr - 1u;
+  __syncthreads();
+  if (__builtin_amdgcn_readfirstlane(sh.flag)) {
+    merge_row<G>(a, sh.u.att, row);
+    // every workgroup of the row is past its last use of the row's words:
+    // clear them here, in the L2 that holds them, for the next launch
+    if (tid < 6) rc[tid] = 0u;
+  }
+  finish_launch(a);
+}
+
+template <int DT, int LPK, bool BF16>
+hipError_t launch_g(const StepArgs& a, hipStream_t s) {
+  // workgroups are dealt to the XCDs in turn: nxcc equal shares
+  const dim3 grid((unsigned)(a.nxcc * ((a.rows + a.nxcc - 1) / a.nxcc) * a.wpr));
+  switch (a.Hq / a.Hkv) {
+    case 1: hipLaunchKernelGGL((decode_step_kernel<DT, LPK, BF16, 1>), grid, dim3(kWgThreads), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((decode_step_kernel<DT, LPK, BF16, 2>), grid, dim3(kWgThreads), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((decode_step_kernel<DT, LPK, BF16, 4>), grid, dim3(kWgThreads), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((decode_step_kernel<DT, LPK, BF16, 8>), grid, dim3(kWgThreads), 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int step_ctrl_words(int rows) { return kCtlRow0 + kCtlPerRow * rows; }
+int step_chunk_slots() { return kChunk; }
+
+bool decode_step_supported(int rows, int n, int B, int r, int k_dt, int kv_dt, int G, int d, int hint_count,
+                           int hint_k_) {
+  const int esz = k_dt == 2 ? 1 : k_dt == 1 ? 2 : 4;
+  const int lpk = r * esz / 16;
+  if ((k_dt != 1 && k_dt != 2) || (lpk != 4 && lpk != 8)) return false;
+  if (kv_dt != 0 && kv_dt != 1) return false;
+  if (d != kD || (G != 1 && G != 2 && G != 4 && G != 8)) return false;
+  const int64_t wpr = ((int64_t)n + kChunk - 1) / kChunk;
+  if (wpr > kMaxParts || rows < 1 || (int64_t)rows * wpr > (1 << 20)) return false;
+  if ((int64_t)B > (int64_t)wpr * kWgThreads) return false;      // a part's entries fit the LDS list
+  if ((int64_t)hint_count * hint_k_ < B) return false;        // the hints vouch for B keys
+  // whole 128-byte lines of selected positions per row (one writer each)
+  if (B % 32 != 0) return false;
+  return B <= kFinCap && B <= n;
+}
+
+int step_meta_stride() { return kMetaStride; }
+int step_partial_stride(int G) { return partial_stride(G); }
+
+hipError_t launch_decode_step(const StepArgs& a, int k_dt, hipStream_t s) {
+  if (a.nxcc < 1 || a.nxcc > 8) return hipErrorInvalidValue;
+  const int esz = k_dt == 2 ? 1 : 2;
+  const int lpk = a.sc.r * esz / 16;
+  if (k_dt == 1 && lpk == 8) return a.kv_bf16 ? launch_g<1, 8, true>(a, s) : launch_g<1, 8, false>(a, s);
+  if (k_dt == 1 && lpk == 4) return a.kv_bf16 ? launch_g<1, 4, true>(a, s) : launch_g<1, 4, false>(a, s);
+  if (k_dt == 2 && lpk == 4) return a.kv_bf16 ? launch_g<2, 4, true>(a, s) : launch_g<2, 4, false>(a, s);
+  if (k_dt == 2 && lpk == 8) return a.kv_bf16 ? launch_g<2, 8, true>(a, s) : launch_g<2, 8, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace lsa

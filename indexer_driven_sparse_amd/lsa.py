@@ -91,7 +91,19 @@ class CentroidDesc(_c.Structure):
                 ("out_stride_blk", _I64)]
 
 
-DESCS = {0: ScoreDesc, 1: SelectDesc, 2: AttnDesc, 3: ProjectDesc, 4: CentroidDesc}
+class StepDesc(_c.Structure):
+    _fields_ = [("struct_size", _U32), ("n_seq", _I32), ("n_q_heads", _I32), ("n_kv_heads", _I32),
+                ("head_dim", _I32), ("rank", _I32), ("n_keys", _I32), ("topk", _I32),
+                ("q", _P), ("q_dtype", _I32), ("w_per_head", _I32), ("w", _P),
+                ("k_idx", _P), ("k_idx_dtype", _I32), ("kv_dtype", _I32),
+                ("k_stride_seq", _I64), ("k_stride_head", _I64), ("k_stride_tok", _I64),
+                ("k", _P), ("v", _P),
+                ("kv_stride_seq", _I64), ("kv_stride_tok", _I64), ("kv_stride_head", _I64),
+                ("scale", _F), ("flags", _I32),
+                ("q_idx", _P), ("out_idx", _P), ("out_score", _P), ("out", _P), ("lse", _P)]
+
+
+DESCS = {0: ScoreDesc, 1: SelectDesc, 2: AttnDesc, 3: ProjectDesc, 4: CentroidDesc, 5: StepDesc}
 
 _SIGS = {
     "lsa_index_score": (_I32, [_P, _P, _c.c_size_t, _P]),
@@ -105,6 +117,9 @@ _SIGS = {
     "lsa_select_workspace_bytes": (_c.c_size_t, [_P]),
     "lsa_attention_workspace_bytes": (_c.c_size_t, [_P]),
     "lsa_stream_read": (_I32, [_P, _c.c_size_t, _P, _P]),
+    "lsa_decode_step": (_I32, [_P, _P, _c.c_size_t, _P]),
+    "lsa_step_workspace_bytes": (_c.c_size_t, [_P]),
+    "lsa_step_is_fused": (_I32, [_P]),
     "lsa_status_str": (_c.c_char_p, [_I32]),
     "lsa_last_hip_error": (_I32, []),
     "lsa_abi_version": (_I32, []),
@@ -547,6 +562,82 @@ def prefill_score_workspace_bytes_for(L: int, Hkv: int, r: int, B: int,
     dd.topk = B
     dd.query_block = query_block
     return int(_lib().lsa_score_workspace_bytes(_c.byref(dd)))
+
+
+STEP_ONE_LAUNCH = 1   # lsa_step_desc.flags: the one persistent launch where the shape allows
+
+
+def _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch=False):
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [N,Hq,d]")
+    N, Hq, hd = q.shape
+    if k_idx.dim() != 4 or k_idx.stride(-1) != 1:
+        raise ValueError("k_idx must be [N,Hkv,T,r] with r contiguous")
+    _, Hkv, T, r = k_idx.shape
+    if k_idx.shape[0] != N:
+        raise ValueError("k_idx must hold the N sequences of q")
+    if k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("k and v must share shape [N,T,Hkv,d], strides and dtype")
+    if k.shape[0] < N or k.shape[1] != T or k.shape[2] != Hkv or k.shape[3] != hd:
+        raise ValueError("k/v must be [N,T,Hkv,d] matching q and k_idx")
+    if w.dtype != torch.float32 or not w.is_contiguous() or w.shape[-1] != r or w.shape[-2] != hd \
+            or (w.dim() == 3 and w.shape[0] != Hkv):
+        raise ValueError("w must be contiguous float32 [d,r] or [Hkv,d,r]")
+    B = out_idx.shape[-1]
+    _need(out_idx, "out_idx", torch.int32, (N, Hkv, B))
+    _need(out, "out", torch.float32, (N, Hq, hd))
+    _need(lse, "lse", torch.float32, (N, Hq))
+    _need(q_idx, "q_idx", torch.float32, (N, Hkv, r))
+    _need(out_score, "out_score", torch.float32, (N, Hkv, B))
+    d = StepDesc()
+    d.struct_size = _c.sizeof(StepDesc)
+    d.n_seq, d.n_q_heads, d.n_kv_heads, d.head_dim, d.rank, d.n_keys, d.topk = N, Hq, Hkv, hd, r, T, B
+    d.q, d.q_dtype = _ptr(q), _dt(q)
+    d.w, d.w_per_head = _ptr(w), 1 if w.dim() == 3 else 0
+    d.k_idx, d.k_idx_dtype = _ptr(k_idx), _dt(k_idx)
+    d.k_stride_seq, d.k_stride_head, d.k_stride_tok = k_idx.stride(0), k_idx.stride(1), k_idx.stride(2)
+    d.k, d.v, d.kv_dtype = _ptr(k), _ptr(v), _dt(k)
+    d.kv_stride_seq, d.kv_stride_tok, d.kv_stride_head = k.stride(0), k.stride(1), k.stride(2)
+    d.scale = scale
+    d.flags = STEP_ONE_LAUNCH if one_launch else 0
+    d.q_idx, d.out_idx, d.out_score, d.out, d.lse = (_ptr(q_idx), _ptr(out_idx), _ptr(out_score),
+                                                     _ptr(out), _ptr(lse))
+    return d
+
+
+def lsa_decode_step(q, w, k_idx, k, v, out_idx, out, *, lse=None, q_idx=None, out_score=None,
+                    scale: float = 0.0, workspace=None, stream=None, one_launch: bool = False) -> None:
+    """One whole flat decode step (scoring prep, scores, exact top-B, indexed
+    attention): q [N,Hq,d], w [d,r] fp32, k_idx [N,Hkv,T,r], k/v [N,T,Hkv,d];
+    out_idx int32 [N,Hkv,B], out fp32 [N,Hq,d]. workspace: uint8 of at least
+    lsa_step_workspace_bytes, all zero before its first use (the call leaves
+    its control words zero); allocated zeroed here when not given.
+    one_launch: the single persistent launch where the shape allows it."""
+    d = _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch)
+    lib = _lib()
+    need = lib.lsa_step_workspace_bytes(_c.byref(d))
+    if need == 0:
+        _check("lsa_decode_step", lib.lsa_decode_step(_c.byref(d), None, 0, _stream(stream)))
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check("lsa_decode_step", lib.lsa_decode_step(_c.byref(d), _ptr(workspace), wsb, _stream(stream)))
+
+
+def lsa_step_workspace_bytes(q, w, k_idx, k, v, out_idx, out, *, lse=None, q_idx=None,
+                             out_score=None, scale: float = 0.0, one_launch: bool = False) -> int:
+    d = _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch)
+    return int(_lib().lsa_step_workspace_bytes(_c.byref(d)))
+
+
+def lsa_step_is_fused(q, w, k_idx, k, v, out_idx, out, **kw) -> bool:
+    """Whether the step (shape and one_launch flag) runs as one persistent launch."""
+    d = _step_desc(q, w, k_idx, k, v, out_idx, out, kw.get("lse"), kw.get("q_idx"),
+                   kw.get("out_score"), kw.get("scale", 0.0), kw.get("one_launch", False))
+    return int(_lib().lsa_step_is_fused(_c.byref(d))) == 1
+
+
+STEP_ERROR_WORD = 9    # 32-bit word index of the step workspace's error word
 
 
 def lsa_project_keys(k: torch.Tensor, w: torch.Tensor, out: torch.Tensor, *, tok_begin: int = 0,

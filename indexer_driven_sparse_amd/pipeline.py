@@ -43,9 +43,12 @@ class DecodePlan:
 
     def __init__(self, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int,
                  device="cuda", kv_dtype=torch.bfloat16, with_idx_scores: bool = False,
-                 kidx_dtype=None):
+                 kidx_dtype=None, fused: bool = True, one_launch: bool = False):
         self.N, self.Hq, self.Hkv, self.T, self.d, self.r, self.B = N, Hq, Hkv, T, d, r, B
         self.with_idx_scores = with_idx_scores
+        self.fused = fused
+        self.one_launch = one_launch
+        self.step_ws = None
         f32 = dict(dtype=torch.float32, device=device)
         self.scores = torch.empty(N, Hkv, _ld4(T), **f32)[:, :, :T]
         self.q_idx = torch.empty(N, Hkv, r, **f32)
@@ -81,7 +84,27 @@ class DecodePlan:
                                   stream=stream, slot_table=slot_table,
                                   n_keys=self.T if slot_table is not None else None)
 
+    def step(self, q, w, k_idx, k, v, stream=None):
+        """The whole step through one lsa_decode_step call (with one_launch,
+        the single persistent launch where the shape allows it)."""
+        if self.step_ws is None:
+            need = lsa.lsa_step_workspace_bytes(q, w, k_idx, k, v, self.idx, self.out, lse=self.lse,
+                                                q_idx=self.q_idx, one_launch=self.one_launch)
+            self.step_ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+        lsa.lsa_decode_step(q, w, k_idx, k, v, self.idx, self.out, lse=self.lse, q_idx=self.q_idx,
+                            out_score=self.idx_scores if self.with_idx_scores else None,
+                            workspace=self.step_ws, stream=stream, one_launch=self.one_launch)
+
+    def step_error(self) -> int:
+        """The step workspace's error word (0 when every call was clean)."""
+        if self.step_ws is None:
+            return 0
+        return int(self.step_ws[:64].view(torch.int32)[lsa.STEP_ERROR_WORD].item())
+
     def run(self, q, w, k_idx, k, v, stream=None, slot_table=None):
+        if self.fused and slot_table is None:
+            self.step(q, w, k_idx, k, v, stream)
+            return self
         self.score(q, w, k_idx, stream)
         self.select(stream)
         self.attend(q, k, v, stream, slot_table=slot_table)
@@ -92,7 +115,7 @@ def decode_step(q, w, k_idx, k, v, B, stream=None) -> dict:
     """One flat decode step; returns the step's buffers (device tensors)."""
     N, Hkv, T, r = k_idx.shape
     plan = DecodePlan(N, q.shape[1], Hkv, T, q.shape[2], r, B, device=q.device, kv_dtype=k.dtype,
-                      with_idx_scores=True, kidx_dtype=k_idx.dtype)
+                      with_idx_scores=True, kidx_dtype=k_idx.dtype, fused=False)
     plan.run(q, w, k_idx, k, v, stream)
     return {"q_idx": plan.q_idx, "scores": plan.scores, "idx": plan.idx,
             "idx_scores": plan.idx_scores, "out": plan.out, "lse": plan.lse}

@@ -8,6 +8,7 @@ import re
 
 import pytest
 
+import torch
 from indexer_driven_sparse_amd import lsa
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -427,3 +428,35 @@ def test_noalloc_attention_rejects_shapes_beyond_its_scratch():
     assert lib.lsa_indexed_attention_noalloc(ctypes.byref(big), None) == SCRATCH_LIMIT
     bad = _attn_desc(rows=0)
     assert lib.lsa_indexed_attention_noalloc(ctypes.byref(bad), None) == INVALID
+
+
+def test_step_plan_flags_and_one_launch_conditions():
+    """lsa_decode_step's planner (host only): the one persistent launch only
+    with LSA_STEP_ONE_LAUNCH, B a multiple of 32 and out_idx on a 128-byte
+    line; unknown flag bits are rejected."""
+    lib = lsa._lib()
+    N, Hq, Hkv, T, d, r = 1, 32, 8, 40000, 128, 64
+    bf = dict(dtype=torch.bfloat16)
+    q = torch.empty(N, Hq, d, **bf)
+    w = torch.empty(d, r, dtype=torch.float32)
+    kd = torch.empty(N, Hkv, T, r, **bf)
+    k = torch.empty(N, T, Hkv, d, **bf)
+    v = torch.empty(N, T, Hkv, d, **bf)
+    out = torch.empty(N, Hq, d, dtype=torch.float32)
+
+    def fused(B, one_launch, shift=0):
+        buf = torch.empty(N * Hkv * B + 64, dtype=torch.int32)
+        base = (-buf.data_ptr() // 4) % 32 + shift    # element offset of a 128-byte line (+ shift)
+        idx = buf[base:base + N * Hkv * B].view(N, Hkv, B)
+        return lsa.lsa_step_is_fused(q, w, kd, k, v, idx, out, one_launch=one_launch)
+
+    assert not fused(1024, False)
+    assert fused(1024, True)
+    assert not fused(1000, True)                # B not a multiple of 32
+    assert not fused(1024, True, shift=1)       # selected positions off a 128-byte line
+    idx = torch.empty(N, Hkv, 1024, dtype=torch.int32)
+    d_ = lsa._step_desc(q, w, kd, k, v, idx, out, None, None, None, 0.0, True)
+    assert lib.lsa_step_workspace_bytes(ctypes.byref(d_)) > 0
+    d_.flags = 2
+    assert lib.lsa_step_workspace_bytes(ctypes.byref(d_)) == 0
+    assert lib.lsa_step_is_fused(ctypes.byref(d_)) == -1

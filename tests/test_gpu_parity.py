@@ -626,6 +626,128 @@ def test_decode_step_headline_workload_every_row():
     g = gpu_decode_step(case, kd)
     ref = _oracle_rows(case, rows)
     _compare_step(case, g, ref, rows)
+    # one lsa_decode_step call (the benchmark's path), and the single
+    # persistent launch, against the same oracle rows
+    from indexer_driven_sparse_amd import pipeline
+    for one_launch in (False, True):
+        plan = pipeline.DecodePlan(case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B,
+                                   fused=True, one_launch=one_launch)
+        plan.run(dev(case.Q), dev(case.W), kd, dev(case.K), dev(case.V))
+        torch.cuda.synchronize()
+        assert plan.step_error() == 0
+        gf = {"idx": host(plan.idx), "out": host(plan.out), "lse": host(plan.lse)}
+        _compare_step(case, gf, ref, rows)
+
+
+def _fused_vs_three_calls(case, kd, reps=1):
+    """The fused lsa_decode_step against the three calls in sequence on the
+    same inputs: indices, q_idx and per-entry scores bit for bit (both are
+    the exact top-B of the same scores); out and lse over those indices
+    within 1e-5 (fp32 attention summed in another order), and against the
+    oracle's attention over the same indices within the attention bar.
+    Returns the fused plan."""
+    from indexer_driven_sparse_amd import pipeline
+    N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
+    Q, W, K, V = dev(case.Q), dev(case.W), dev(case.K), dev(case.V)
+    ref = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, with_idx_scores=True, kidx_dtype=kd.dtype,
+                              fused=False)
+    ref.run(Q, W, kd, K, V)
+    fus = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, with_idx_scores=True, kidx_dtype=kd.dtype,
+                              fused=True, one_launch=True)
+    for _ in range(reps):
+        fus.run(Q, W, kd, K, V)
+    torch.cuda.synchronize()
+    assert fus.step_error() == 0
+    for name in ("idx", "q_idx", "idx_scores"):
+        a, b = getattr(fus, name), getattr(ref, name)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name
+    for name in ("out", "lse"):
+        np.testing.assert_allclose(host(getattr(fus, name)), host(getattr(ref, name)), rtol=0, atol=1e-5,
+                                   err_msg=name)
+    o, l = oracle.attention(case.Q, case.K, case.V, host(fus.idx))
+    np.testing.assert_allclose(host(fus.out), o, rtol=0, atol=ATTN_ATOL)
+    np.testing.assert_allclose(host(fus.lse), l, rtol=0, atol=LSE_ATOL)
+    return fus
+
+
+@pytest.mark.parametrize("name,over,fused", [
+    ("decode_t128k_b2048", {"N": 1, "T": 40000, "B": 1024}, True),    # 8 rows, ragged chunks
+    ("decode_t128k_b2048", {"N": 2, "Hq": 24, "Hkv": 6, "T": 20000, "B": 512}, True),  # 12 rows
+    ("decode_t128k_b2048", {"N": 1, "T": 40000}, False),           # hints vouch for < B keys
+    ("decode_t128k_b2048", {"N": 4}, True),                        # the headline shape
+    ("decode_t32k_hitters", {}, True),
+    ("decode_t4k_fp32", {}, False),                                # one row: the three calls
+])
+def test_decode_step_fused_equals_three_calls(name, over, fused):
+    case = synth.workload(name, **over)
+    say("fused decode step vs three calls", name, over)
+    kd = torch.empty(case.N, case.Hkv, case.T, case.r, dtype=torch_dtype(case.dtype), device="cuda")
+    lsa.lsa_project_keys(dev(case.K), dev(case.W), kd)
+    plan = _fused_vs_three_calls(case, kd, reps=3)
+    assert lsa.lsa_step_is_fused(dev(case.Q), dev(case.W), kd, dev(case.K), dev(case.V), plan.idx,
+                                 plan.out, one_launch=True) == fused
+
+
+def test_decode_step_fused_fp8_cache_and_ties():
+    """The fused step over an E4M3 projected-key cache, and over a cache in
+    which every key of a head is the same (each row one big tie: the hint
+    lists overflow and the final selection falls back to the whole row)."""
+    case = synth.workload("decode_t128k_b2048", N=1, T=30000, B=896)
+    say("fused decode step, fp8 cache")
+    k8 = torch.empty(case.N, case.Hkv, case.T, case.r, dtype=torch.float8_e4m3fn, device="cuda")
+    lsa.lsa_project_keys(dev(case.K), dev(case.W), k8)
+    assert lsa.lsa_step_is_fused(dev(case.Q), dev(case.W), k8, dev(case.K), dev(case.V),
+                                 _fused_vs_three_calls(case, k8).idx,
+                                 torch.empty(case.N, case.Hq, case.d, device="cuda"), one_launch=True)
+    say("fused decode step, constant keys per head")
+    K = case.K.copy()
+    K[:, :, :, :] = K[:, :1, :, :]
+    case.K = K
+    kd = torch.empty(case.N, case.Hkv, case.T, case.r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_project_keys(dev(case.K), dev(case.W), kd)
+    fus = _fused_vs_three_calls(case, kd)
+    gi = host(fus.idx)
+    for g in range(case.Hkv):          # a tie over the whole row keeps the lowest positions
+        np.testing.assert_array_equal(gi[0, g], np.arange(case.B))
+
+
+def test_decode_step_fused_graph_replay():
+    """The fused step captured in a HIP graph: every replay (with eager work
+    and synchronizations between them, alternating two caches) equals the
+    eager call, and the control words come back zero each time."""
+    from indexer_driven_sparse_amd import pipeline
+    case = synth.workload("decode_t128k_b2048", N=1, T=50000, B=1024)
+    say("fused decode step, graph replay")
+    N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
+    Q, W, K, V = dev(case.Q), dev(case.W), dev(case.K), dev(case.V)
+    caches = []
+    for s in (0, 1):
+        Kc = K if s == 0 else torch.roll(K, shifts=777, dims=1).contiguous()
+        kd = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+        lsa.lsa_project_keys(Kc, W, kd)
+        caches.append((Kc, kd))
+    plan = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, fused=True, one_launch=True)
+    want = []
+    for Kc, kd in caches:
+        plan.run(Q, W, kd, Kc, V)
+        torch.cuda.synchronize()
+        want.append((plan.idx.clone(), plan.out.clone()))
+    graphs = []
+    for Kc, kd in caches:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            plan.run(Q, W, kd, Kc, V)
+        graphs.append(g)
+    for i in range(6):
+        graphs[i % 2].replay()
+        torch.cuda.synchronize()
+        wi, wo = want[i % 2]
+        assert torch.equal(plan.idx, wi), i
+        assert torch.equal(plan.out.view(torch.int32), wo.view(torch.int32)), i
+        ctl = plan.step_ws[:256].view(torch.int32)
+        assert int(ctl[lsa.STEP_ERROR_WORD]) == 0
+        assert int(ctl.abs().sum()) == 0, i      # control words left zero
+        plan.out.zero_()
 
 
 def test_decode_step_budget_T_is_dense_attention():
