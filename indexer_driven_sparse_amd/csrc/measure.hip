@@ -3,10 +3,13 @@
 // the hot path are judged (its rate, not the published peak alone, is what
 // a memory-bound kernel can reach on this part).
 //
-// Every lane streams 16-byte nontemporal loads, four in flight per loop
-// step, over a grid-stride range; the words are XOR-folded so the loads
-// cannot be dropped, and workgroup b stores its fold to sink[b] (plain
-// stores: no atomics contend on one address).
+// Workgroup b streams one contiguous share of the buffer (its 16-byte
+// words [b * n16 / nb, (b + 1) * n16 / nb)), every lane issuing eight
+// 16-byte nontemporal loads per loop step, each wave-wide load 1 KB of
+// consecutive bytes. Contiguous shares read about a seventh faster on
+// MI355X than a grid-stride sweep of the same buffer. The words are
+// XOR-folded so the loads cannot be dropped, and workgroup b stores its
+// fold to sink[b] (plain stores: no atomics contend on one address).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -20,17 +23,18 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __global__ __launch_bounds__(kReadThreads) void stream_read_kernel(const u32x4* p, size_t n16,
                                                                    uint32_t* sink) {
   __shared__ uint32_t s_fold[kReadThreads / 64];
-  const size_t stride = (size_t)gridDim.x * kReadThreads;
-  size_t i = (size_t)blockIdx.x * kReadThreads + threadIdx.x;
+  constexpr int kU = 8;
+  const size_t b0 = n16 * blockIdx.x / gridDim.x, b1 = n16 * (blockIdx.x + 1) / gridDim.x;
   u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 a = __builtin_nontemporal_load(p + i);
-    const u32x4 b = __builtin_nontemporal_load(p + i + stride);
-    const u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
-    const u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
-    acc ^= a ^ b ^ c ^ d;
+  size_t i = b0 + threadIdx.x;
+  for (; i + (kU - 1) * kReadThreads < b1; i += kU * kReadThreads) {
+    u32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kReadThreads);
+#pragma unroll
+    for (int u = 0; u < kU; ++u) acc ^= v[u];
   }
-  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+  for (; i < b1; i += kReadThreads) acc ^= __builtin_nontemporal_load(p + i);
   uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x ^= (uint32_t)__shfl_xor((int)x, o, 64);

@@ -7,7 +7,7 @@
 #include "score_body.hpp"
 
 #ifndef LSA_SCORE_WG_TARGET
-#define LSA_SCORE_WG_TARGET 2048   // workgroups per scoring launch (about 8 per CU)
+#define LSA_SCORE_WG_TARGET 1024   // workgroups per scoring launch: one resident round (4 per CU)
 #endif
 
 namespace lsa {
@@ -15,12 +15,16 @@ namespace {
 
 using namespace scoring;
 
+constexpr int kStageSlots = 4096;   // scores one workgroup gathers in LDS before writing them
+
 template <int DT, int LPK, bool CAND>
 __global__ __launch_bounds__(kScoreThreads) void score_decode_kernel(ScoreDecodeArgs a) {
   __shared__ ScoreShared sh;
+  __shared__ __align__(16) float stage[kStageSlots];   // a.chunk <= kStageSlots
+  __shared__ uint32_t hstage[kStageSlots / 64];         // 4 hint entries per step of >= 256 slots
   const int64_t c0 = (int64_t)blockIdx.x * a.chunk;
   const int64_t c1 = min((int64_t)a.n_out, c0 + a.chunk);
-  score_chunk<DT, LPK, CAND>(a, (int)blockIdx.y, c0, c1, sh);
+  score_chunk<DT, LPK, CAND>(a, (int)blockIdx.y, c0, c1, sh, true, nullptr, stage, hstage);
 }
 
 // Small-L causal score matrix (unfused prefill scoring, for checking the
@@ -78,6 +82,8 @@ int score_chunk_slots(int n_out, int rows, int k_dt) {
   const int64_t per_row = (target + rows - 1) / rows;
   int64_t chunk = (n_out + per_row - 1) / per_row;
   chunk = (chunk + step - 1) / step * step;
+  // at most kStageSlots, the LDS staging of the chunk's scores
+  chunk = std::min<int64_t>(chunk, kStageSlots / step * step);
   return (int)std::max<int64_t>(step, chunk);
 }
 

@@ -116,6 +116,17 @@ __device__ __forceinline__ void store_u32(uint32_t* p, uint32_t v) {
   if constexpr (COHERENT) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else *p = v;
 }
+template <bool COHERENT>
+__device__ __forceinline__ void store_u32x4(uint32_t* p, uint4 v) {
+  if constexpr (COHERENT) {
+    store_u32<true>(p, v.x);
+    store_u32<true>(p + 1, v.y);
+    store_u32<true>(p + 2, v.z);
+    store_u32<true>(p + 3, v.w);
+  } else {
+    *reinterpret_cast<uint4*>(p) = v;
+  }
+}
 
 // Scores (and selection hints) of slots [c0, c1) of one row, by one
 // 256-thread workgroup; c0 is a multiple of the workgroup step. Every
@@ -126,10 +137,19 @@ __device__ __forceinline__ void store_u32(uint32_t* p, uint32_t v) {
 // unrolled, and each thread also keeps its scores in the LDS array keep, at
 // keep[(s * G + u) * 256 + thread] (step s, group u; slots past c1 hold
 // NaN). COHERENT: scores and hints are stored device-coherently, for
-// readers on other XCDs inside the same launch.
+// readers on other XCDs inside the same launch. stage (STEPS == 0 only):
+// an LDS array of at least c1 - c0 floats, hstage one of the chunk's hint
+// entries (4 per step); scores and hints are gathered there and written out
+// in one burst (16-byte stores for the scores) after the chunk's last load,
+// every hint entry of the chunk's steps included (0 for a wave that had no
+// slot left in the last step).
+// Scattered score stores in the middle of the cache stream cost the stream
+// far more than their share of the bytes on MI355X; one burst per chunk
+// costs little.
 template <int DT, int LPK, bool CAND, bool PREP = true, int STEPS = 0, bool COHERENT = false>
 __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, int64_t c0, int64_t c1,
-                                            ScoreShared& sh, bool do_prep = true, float* keep = nullptr) {
+                                            ScoreShared& sh, bool do_prep = true, float* keep = nullptr,
+                                            float* stage = nullptr, uint32_t* hstage = nullptr) {
   constexpr int ESZ = DT == 2 ? 1 : DT == 1 ? 2 : 4;
   constexpr int kGroupsInFlight = groups_in_flight(DT);
   constexpr int kHintK = hint_k(DT);
@@ -179,6 +199,9 @@ __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, i
   // cache loads are in flight. The empty asm statements keep the compiler
   // from reordering the two batches.
   const int64_t gfirst = c0 + (int64_t)wid * 64;
+  const int n_hst = (int)((c1 - c0 + kStep - 1) / kStep) * 4;   // hint entries of the chunk's steps
+  if (STEPS == 0 && stage != nullptr)
+    for (int k = tid; k < n_hst; k += kScoreThreads) hstage[k] = 0u;   // ordered by the prep's barrier
   const bool prep = PREP && a.q != nullptr && do_prep;
   const int G = prep ? a.Hq / a.Hkv : 1;
   const int parts = kScoreThreads / r;
@@ -266,7 +289,10 @@ __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, i
         if (l == it) mine = s;
       }
       const int64_t myslot = gb + (int64_t)u * 4 * 64 + (int64_t)l * KPI + kg;
-      if (myslot < c1) store_u32<COHERENT>(reinterpret_cast<uint32_t*>(srow + myslot), __float_as_uint(mine));
+      if (myslot < c1) {
+        if (STEPS == 0 && stage != nullptr) stage[myslot - c0] = mine;
+        else store_u32<COHERENT>(reinterpret_cast<uint32_t*>(srow + myslot), __float_as_uint(mine));
+      }
       if constexpr (STEPS > 0)
         keep[(si * kGroupsInFlight + u) * kScoreThreads + tid] = myslot < c1 ? mine : __builtin_nanf("");
       hkey[u] = myslot < c1 ? order_key(mine) : 0u;
@@ -286,12 +312,27 @@ __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, i
       }
       if (lane == 0) {
         const int64_t step = (gb - (int64_t)wid * 64) / kStep;
-        store_u32<COHERENT>(a.hint + (int64_t)row * a.hint_ld + step * 4 + wid, hp << 16);
+        if (STEPS == 0 && stage != nullptr) hstage[(step - c0 / kStep) * 4 + wid] = hp << 16;
+        else store_u32<COHERENT>(a.hint + (int64_t)row * a.hint_ld + step * 4 + wid, hp << 16);
       }
     }
   };
   if constexpr (STEPS == 0) {
     for (int64_t gb = gfirst; gb < c1; gb += kStep) one_step(gb, 0);
+    if (stage != nullptr) {
+      // srow + c0 is 16-byte aligned (16-byte aligned rows, c0 a multiple of the step)
+      __syncthreads();
+      const int n = (int)(c1 - c0), nq = n / 4;
+      float* dst = srow + c0;
+      for (int k = tid; k < nq; k += kScoreThreads)
+        store_u32x4<COHERENT>(reinterpret_cast<uint32_t*>(dst + 4 * k), *reinterpret_cast<const uint4*>(stage + 4 * k));
+      for (int k = 4 * nq + tid; k < n; k += kScoreThreads)
+        store_u32<COHERENT>(reinterpret_cast<uint32_t*>(dst + k), __float_as_uint(stage[k]));
+      if (a.hint != nullptr) {
+        uint32_t* hdst = a.hint + (int64_t)row * a.hint_ld + c0 / kStep * 4;
+        for (int k = tid; k < n_hst; k += kScoreThreads) store_u32<COHERENT>(hdst + k, hstage[k]);
+      }
+    }
   } else {
 #pragma unroll
     for (int si = 0; si < STEPS; ++si) {

@@ -27,6 +27,10 @@
 // Rows longer than kSelectLdsMaxSlots keep their bitmaps in workspace.
 #include "select_row.hpp"
 
+#ifndef LSA_SELECT_SEGMENTED
+#define LSA_SELECT_SEGMENTED 1   // long hinted rows: segmented collect, then the row select
+#endif
+
 namespace lsa {
 namespace {
 
@@ -78,7 +82,7 @@ size_t bitmap_bytes(int rows, int n) {
 }  // namespace
 
 int select_segments(int n, int B, bool hint_usable) {
-  if (!hint_usable || B > kCap / 2 || n < 2 * kSeg) return 0;
+  if (!LSA_SELECT_SEGMENTED || !hint_usable || B > kCap / 2 || n < 2 * kSeg) return 0;
   const int nseg = (n + kSeg - 1) / kSeg;
   return nseg <= kThreads ? nseg : 0;   // the row kernel scans one count per thread
 }
