@@ -33,7 +33,8 @@ METRIC = "sparse-attn decode steps/s at 128K,B=2048; indexer keys scored/s; % HB
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK = 2.5e15   # dense bf16 MFMA flop/s (MI355X)
 WORKLOAD = "decode_t128k_b2048"
-SCORE_SOURCES = ["indexer_driven_sparse_amd/csrc/score.hip", "indexer_driven_sparse_amd/csrc/common.hpp"]
+SCORE_SOURCES = ["indexer_driven_sparse_amd/csrc/score.hip", "indexer_driven_sparse_amd/csrc/score_body.hpp",
+                 "indexer_driven_sparse_amd/csrc/common.hpp"]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_decode_t128k_pmc.json")
 
 
