@@ -328,11 +328,12 @@ int plan_step(const lsa_step_desc* d, StepPlan* p) {
   if (rows > 65535) return LSA_ERR_UNSUPPORTED;
   const int64_t ld = ((int64_t)d->n_keys + 31) / 32 * 32;   // rows of whole 128-byte lines
   const int hint_count = lsa::score_hint_count(d->n_keys, d->k_idx_dtype);
+  const int hint_ld = (hint_count + 31) / 32 * 32;   // rows of whole 128-byte lines
   const size_t ctrl_bytes = align256((size_t)lsa::step_ctrl_words((int)rows) * 4);
   p->rows = (int)rows;
   p->off_scores = ctrl_bytes;
   p->off_hint = p->off_scores + align256((size_t)rows * ld * sizeof(float));
-  p->off_sel = p->off_hint + align256((size_t)rows * hint_count * sizeof(uint32_t));
+  p->off_sel = p->off_hint + align256((size_t)rows * hint_ld * sizeof(uint32_t));
 
   lsa_score_desc& sd = p->score;
   std::memset(&sd, 0, sizeof(sd));
@@ -357,7 +358,7 @@ int plan_step(const lsa_step_desc* d, StepPlan* p) {
   sd.scores = (float*)(uintptr_t)(p->off_scores + 256);   // placeholders: validation checks alignment only
   sd.scores_ld = ld;
   sd.hint = (uint32_t*)(uintptr_t)(p->off_hint + 256);
-  sd.hint_ld = hint_count;
+  sd.hint_ld = hint_ld;
   if (!d->q) return LSA_ERR_INVALID_ARG;
   size_t need = 0;
   LSA_TRY(validate_score(&sd, &need));
@@ -374,7 +375,7 @@ int plan_step(const lsa_step_desc* d, StepPlan* p) {
   se.out_idx = d->out_idx;
   se.out_score = d->out_score;
   se.hint = sd.hint;
-  se.hint_ld = hint_count;
+  se.hint_ld = hint_ld;
   se.hint_count = hint_count;
   se.hint_k = lsa::score_hint_k(d->k_idx_dtype);
   LSA_TRY(validate_select(&se, &p->sel_bytes));

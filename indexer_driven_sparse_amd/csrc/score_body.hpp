@@ -134,9 +134,10 @@ __device__ __forceinline__ void store_u32x4(uint32_t* p, uint4 v) {
 // computed here (overlapped with the first cache loads) when PREP and
 // do_prep; otherwise the caller has left it in sh.q.
 // STEPS > 0: the chunk is at most STEPS workgroup steps long, the loop is
-// unrolled, and each thread also keeps its scores in the LDS array keep, at
+// unrolled, and each thread keeps its scores in the LDS array keep, at
 // keep[(s * G + u) * 256 + thread] (step s, group u; slots past c1 hold
-// NaN). COHERENT: scores and hints are stored device-coherently, for
+// NaN), instead of storing them to a.scores; every hint entry of a step that
+// starts inside the row is written (0 for a wave left with no slot). COHERENT: scores and hints are stored device-coherently, for
 // readers on other XCDs inside the same launch. stage (STEPS == 0 only):
 // an LDS array of at least c1 - c0 floats, hstage one of the chunk's hint
 // entries (4 per step); scores and hints are gathered there and written out
@@ -289,9 +290,11 @@ __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, i
         if (l == it) mine = s;
       }
       const int64_t myslot = gb + (int64_t)u * 4 * 64 + (int64_t)l * KPI + kg;
-      if (myslot < c1) {
-        if (STEPS == 0 && stage != nullptr) stage[myslot - c0] = mine;
-        else store_u32<COHERENT>(reinterpret_cast<uint32_t*>(srow + myslot), __float_as_uint(mine));
+      if constexpr (STEPS == 0) {
+        if (myslot < c1) {
+          if (stage != nullptr) stage[myslot - c0] = mine;
+          else store_u32<COHERENT>(reinterpret_cast<uint32_t*>(srow + myslot), __float_as_uint(mine));
+        }
       }
       if constexpr (STEPS > 0)
         keep[(si * kGroupsInFlight + u) * kScoreThreads + tid] = myslot < c1 ? mine : __builtin_nanf("");
@@ -343,6 +346,11 @@ __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, i
 #pragma unroll
         for (int u = 0; u < kGroupsInFlight; ++u)
           keep[(si * kGroupsInFlight + u) * kScoreThreads + tid] = __builtin_nanf("");
+        // a step that starts inside the row but leaves this wave no slot:
+        // its hint entry vouches for nothing
+        const int64_t step0 = c0 + (int64_t)si * kStep;
+        if (a.hint != nullptr && lane == 0 && step0 < a.n_out)
+          store_u32<COHERENT>(a.hint + (int64_t)row * a.hint_ld + step0 / kStep * 4 + wid, 0u);
       }
     }
   }

@@ -65,6 +65,8 @@ constexpr int kChunk = kSteps * kWgStep;         // 4096 slots per workgroup
 constexpr int kKeep = kSteps * kGroups;          // scores each lane keeps
 constexpr int kFinPer = 32;                      // list entries per thread in the exact selection
 constexpr int kFinCap = kWgThreads * kFinPer;      // longest list refined in registers
+constexpr int kCompCap = 1024;                     // keys of one histogram bin bisected from LDS
+static_assert(kCompCap <= kKeep * kWgThreads && kCompCap % kWgThreads == 0, "the compaction reuses the keep array");
 constexpr int kMaxG = 8;                         // query heads per KV head (attention)
 constexpr int kD = 128;                          // head dim (attention: two channels per lane)
 constexpr int kBatch = 8;                        // list entries per wave per attention batch
@@ -90,14 +92,15 @@ __device__ __forceinline__ uint32_t add_c(uint32_t* p, uint32_t v) {
 
 // Hand-off inside one XCD. A row's workgroups all run on one XCD and so
 // share one L2; the L1 of each CU writes through to it. The row's counters
-// and flags, and the hints, are read and written only by atomics, which are
-// performed in that L2 (a plain load could be served by a stale L1 line).
-// The other shared data (scores, lists, meta, selected positions, partials)
-// is stored plainly and loaded plainly, under two rules that keep every L1
-// line a reader hits current: every 128-byte line of it has one writing
-// workgroup, and nothing loads it before the counter that publishes it has
-// been seen (the L1s start each launch empty). A writer waits for its
-// stores before it bumps the counter.
+// and flags are read and written only by atomics, which are performed in
+// that L2 (a polled plain load would be served by a stale L1 line). The
+// shared data (hints, lists, meta, selected positions, partials) is stored
+// plainly and loaded plainly, under two rules that keep every L1 line a
+// reader hits current: every 128-byte line of it has one writing workgroup
+// (a chunk's 32 hint words fill one line of a 128-byte-aligned hint row),
+// and nothing loads it before the counter that publishes it has been seen
+// (the L1s start each launch empty). A writer waits for its stores before
+// it bumps the counter.
 __device__ __forceinline__ uint32_t add_l(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
@@ -142,7 +145,9 @@ __device__ __forceinline__ uint32_t wait_until(uint32_t* p, uint32_t target, uin
 struct FinShared {
   uint32_t hist[256];
   int scan[kWgThreads / 64 + 1];
-  int seg_off[kWgThreads + 1];
+  int seg_off[kMaxParts + 1];
+  int cnt[2][kWgThreads / 64];   // per-wave counts of a bisection step (two steps in flight)
+  int ncomp;                     // keys compacted for the bisection
   uint32_t kmax;
   int bin, above;
 };
@@ -180,7 +185,7 @@ struct StepShared {
 // 1. the row's threshold from its hints (the r-th largest of folded hint
 // entries, on 16-bit prefixes, by two 8-bit radix levels; 0 = take all)
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t row_threshold(uint32_t* hrow, int hint_count, int hint_k, int B, SegShared& sh) {
+__device__ __forceinline__ uint32_t row_threshold(const uint32_t* hrow, int hint_count, int hint_k, int B, SegShared& sh) {
   const int tid = threadIdx.x;
   const int m = (hint_count + 4 * kWgThreads - 1) / (4 * kWgThreads);
   const int ne = (hint_count + m - 1) / m;
@@ -192,7 +197,7 @@ __device__ __forceinline__ uint32_t row_threshold(uint32_t* hrow, int hint_count
     uint32_t val = 0xffffffffu;
     for (int mm = 0; mm < m; ++mm) {
       const int h = e * m + mm;
-      val = min(val, h < hint_count ? ld_l(hrow + h) : 0u);
+      val = min(val, h < hint_count ? hrow[h] : 0u);
     }
     p[q] = (e < ne ? val : 0u) >> 16;
   }
@@ -219,48 +224,18 @@ __device__ __forceinline__ uint32_t row_threshold(uint32_t* hrow, int hint_count
 }
 
 // ---------------------------------------------------------------------------
-// 2b. exact top-B of a row from its lists (every key >= t_lo, in slot order)
+// 2b. exact top-B of a row from its lists (every key >= t_lo, in slot order;
+// the hints guarantee at least B of them)
 // ---------------------------------------------------------------------------
-template <int kPer>
-__device__ __forceinline__ int radix_level_regs(FinShared& sh, const uint32_t (&key)[kPer], int i0,
-                                                int total, uint32_t& pre, int& fixed, int& nd) {
-  const int tid = threadIdx.x;
-  const int width = min(8, 32 - fixed);
-  const int shift = 32 - fixed - width;
-  const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
-  const int nb = 1 << width;
-  sh.hist[tid] = 0u;
-  __syncthreads();
-#pragma unroll
-  for (int j = 0; j < kPer; ++j)
-    if (i0 + j < total && (key[j] & pmask) == pre) atomicAdd(&sh.hist[(key[j] >> shift) & (nb - 1)], 1u);
-  __syncthreads();
-  const int c = tid < nb ? (int)sh.hist[nb - 1 - tid] : 0;
-  int tot;
-  const int excl = block_exclusive_scan<kWgThreads>(c, sh.scan, &tot);
-  if (tid < nb && excl < nd && nd <= excl + c) {
-    sh.bin = nb - 1 - tid;
-    sh.above = excl;
-  }
-  __syncthreads();
-  const int bin = sh.bin;
-  nd -= sh.above;
-  const int cnt = (int)sh.hist[bin];
-  pre |= (uint32_t)bin << shift;
-  fixed += width;
-  __syncthreads();   // hist and bin are reused by the next level
-  return cnt;
-}
 
-// Exact top-B of a whole row straight from its stored scores (every slot
-// valid): 8-bit radix levels over the row, then the positions in ascending
-// order, the lowest positions first among keys equal to the B-th. The path
-// for rows whose lists cannot settle it.
-__device__ __forceinline__ void select_row_general(const StepArgs& a, FinShared& sh, int row) {
+// Rows whose lists hold more than kFinCap entries: 8-bit radix levels over
+// the lists in memory, then the positions in list (= slot) order, the lowest
+// slots first among keys equal to the B-th. Each level is one pass over the
+// lists; the case needs a flat or heavily tied row.
+__device__ __forceinline__ void select_lists_general(const StepArgs& a, FinShared& sh, int row, int total) {
   const int tid = threadIdx.x;
-  const int B = a.B;
-  const int64_t nv = a.sc.n_out;
-  const float* srow = a.sc.scores + (int64_t)row * a.sc.scores_ld;
+  const int B = a.B, nseg = a.wpr;
+  const uint64_t* lrow = (const uint64_t*)(a.lists + (int64_t)row * nseg * kChunk);
   int32_t* orow = a.out_idx + (int64_t)row * B;
   float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
   uint32_t pre = 0u;
@@ -270,9 +245,12 @@ __device__ __forceinline__ void select_row_general(const StepArgs& a, FinShared&
     const uint32_t pmask = fixed == 0 ? 0u : (~0u << (32 - fixed));
     sh.hist[tid] = 0u;
     __syncthreads();
-    for (int64_t i = tid; i < nv; i += kWgThreads) {
-      const uint32_t key = order_key(srow[i]);
-      if ((key & pmask) == pre) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+    for (int p = 0; p < nseg; ++p) {
+      const int n = sh.seg_off[p + 1] - sh.seg_off[p];
+      for (int i = tid; i < n; i += kWgThreads) {
+        const uint32_t key = order_key(__uint_as_float((uint32_t)lrow[(int64_t)p * kChunk + i]));
+        if ((key & pmask) == pre) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      }
     }
     __syncthreads();
     const int c = (int)sh.hist[255 - tid];
@@ -293,49 +271,61 @@ __device__ __forceinline__ void select_row_general(const StepArgs& a, FinShared&
   }
   const uint32_t bmask = fixed >= 32 ? ~0u : (~0u << (32 - fixed));
   const uint32_t top = pre | ~bmask;
-  // slot order, 4 slots per thread per tile: a taken key's position is the
-  // count of keys above the bin before it plus its rank among the in-bin
-  // keys before it (only the first nd of those are taken)
+  // list order, 4 entries per thread per tile of each part: a taken entry's
+  // position counts the keys above the bin before it plus its rank among
+  // the in-bin keys before it (only the first nd of those are taken)
   int a_before = 0, i_before = 0;
-  for (int64_t t0 = 0; t0 < nv; t0 += 4 * kWgThreads) {
-    uint32_t key[4];
-    bool ok[4];
-    int na = 0, ni = 0;
+  for (int p = 0; p < nseg; ++p) {
+    const int n = sh.seg_off[p + 1] - sh.seg_off[p];
+    for (int t0 = 0; t0 < n; t0 += 4 * kWgThreads) {
+      uint64_t e[4];
+      uint32_t key[4];
+      bool ok[4];
+      int na = 0, ni = 0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int64_t i = t0 + 4 * tid + k;
-      ok[k] = i < nv;
-      key[k] = ok[k] ? order_key(srow[i]) : 0u;
-      na += ok[k] && key[k] > top;
-      ni += ok[k] && (key[k] & bmask) == pre;
-    }
-    int tot;
-    const int pref = block_exclusive_scan<kWgThreads>(na | (ni << 16), sh.scan, &tot);
-    int pa = a_before + (pref & 0xffff), pi = i_before + (pref >> 16);
+      for (int k = 0; k < 4; ++k) {
+        const int i = t0 + 4 * tid + k;
+        ok[k] = i < n;
+        e[k] = ok[k] ? lrow[(int64_t)p * kChunk + i] : 0ull;
+        key[k] = order_key(__uint_as_float((uint32_t)e[k]));
+        na += ok[k] && key[k] > top;
+        ni += ok[k] && (key[k] & bmask) == pre;
+      }
+      int tot;
+      const int pref = block_exclusive_scan<kWgThreads>(na | (ni << 16), sh.scan, &tot);
+      int pa = a_before + (pref & 0xffff), pi = i_before + (pref >> 16);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (!ok[k]) continue;
-      const int64_t i = t0 + 4 * tid + k;
-      int pos = -1;
-      if (key[k] > top) {
-        pos = pa + min(pi, nd);
-        ++pa;
-      } else if ((key[k] & bmask) == pre) {
-        if (pi < nd) pos = pa + pi;
-        ++pi;
+      for (int k = 0; k < 4; ++k) {
+        if (!ok[k]) continue;
+        int pos = -1;
+        if (key[k] > top) {
+          pos = pa + min(pi, nd);
+          ++pa;
+        } else if ((key[k] & bmask) == pre) {
+          if (pi < nd) pos = pa + pi;
+          ++pi;
+        }
+        if (pos >= 0) {
+          orow[pos] = (int32_t)(e[k] >> 32);
+          if (osc) osc[pos] = __uint_as_float((uint32_t)e[k]);
+        }
       }
-      if (pos >= 0) {
-        orow[pos] = (int32_t)i;
-        if (osc) osc[pos] = srow[i];
-      }
+      a_before += tot & 0xffff;
+      i_before += tot >> 16;
     }
-    a_before += tot & 0xffff;
-    i_before += tot >> 16;
   }
 }
 
-__device__ __forceinline__ void select_row_exact(const StepArgs& a, FinShared& sh, int row) {
-  const int tid = threadIdx.x, lane = tid & 63;
+// The row's lists are loaded once, kFinPer entries per thread in list
+// order (every address worked out from the LDS segment offsets first, so
+// all loads are in flight together). The B-th key tau is found by bisection
+// on the bits below the common prefix of t_lo and the row's largest key:
+// each step counts the keys at or above a candidate with one ballot per
+// register slot and one barrier. One prefix scan then writes the positions
+// in ascending order, the lowest slots first among keys equal to tau.
+__device__ __forceinline__ void select_row_exact(const StepArgs& a, FinShared& sh, int row, uint32_t* err,
+                                                 float* keep_lds) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int B = a.B, nseg = a.wpr;
   const int4* meta = a.meta + (int64_t)row * nseg * kMetaStride;
   int cnt = 0;
@@ -355,96 +345,179 @@ __device__ __forceinline__ void select_row_exact(const StepArgs& a, FinShared& s
   for (int o = 32; o >= 1; o >>= 1) km = max(km, (uint32_t)__shfl_xor((int)km, o, 64));
   if (lane == 0) atomicMax(&sh.kmax, km);
   __syncthreads();
-  if (total < B || total > kFinCap) {
-    select_row_general(a, sh, row);
+  if (total < B) {   // cannot happen: the hints vouch for B keys >= t_lo
+    if (tid == 0) __hip_atomic_fetch_or(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
-  // thread t holds list entries t*kFinPer .. (list order is slot order)
-  const int i0 = tid * kFinPer;
-  int sg = 0;
-  if (i0 < total) {
-    int lo = 0, hi = nseg - 1;   // last segment starting at or before i0
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sh.seg_off[mid] <= i0) lo = mid; else hi = mid - 1;
-    }
-    sg = lo;
+  if (total > kFinCap) {
+    select_lists_general(a, sh, row, total);
+    return;
   }
-  // the keys stay in registers; the slots are read again (from the L2) for
-  // the entries that are taken. Every entry's address is worked out (from
-  // the LDS segment offsets) before the loads go out, so they are all in
-  // flight at once rather than one round trip each.
-  const uint32_t* lrow = (const uint32_t*)(a.lists + (int64_t)row * nseg * kChunk);
-  const int sg0 = sg;
+  const int i0 = tid * kFinPer;
+  const int nv = max(0, min(kFinPer, total - i0));   // this thread's valid entries
+  const uint64_t* lrow = (const uint64_t*)(a.lists + (int64_t)row * nseg * kChunk);
   uint32_t key[kFinPer];
   {
     int addr[kFinPer];
+    int sg = 0;
+    if (nv > 0) {
+      int lo = 0, hi = nseg - 1;   // last segment starting at or before i0
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sh.seg_off[mid] <= i0) lo = mid; else hi = mid - 1;
+      }
+      sg = lo;
+    }
+    int next = sh.seg_off[sg + 1];
 #pragma unroll
     for (int j = 0; j < kFinPer; ++j) {
       const int i = i0 + j;
       addr[j] = -1;
-      if (i < total) {
-        while (sh.seg_off[sg + 1] <= i) ++sg;
+      if (j < nv) {
+        while (next <= i) next = sh.seg_off[++sg + 1];
         addr[j] = sg * kChunk + (i - sh.seg_off[sg]);
       }
     }
 #pragma unroll
-    for (int j = 0; j < kFinPer; ++j) key[j] = order_key(__uint_as_float(addr[j] >= 0 ? lrow[2 * addr[j]] : 0u));
-  }
-  const uint32_t kmax = sh.kmax;
-  int fixed = t_lo == kmax ? 32 : __clz(t_lo ^ kmax);
-  uint32_t pre = fixed == 0 ? 0u : (t_lo & (~0u << (32 - fixed)));
-  int nd = B;
-  while (fixed < 32)
-    if (radix_level_regs<kFinPer>(sh, key, i0, total, pre, fixed, nd) == nd) break;
-  const uint32_t bmask = fixed >= 32 ? ~0u : (fixed == 0 ? 0u : (~0u << (32 - fixed)));
-  const uint32_t top = pre | ~bmask;
-  int na = 0, ni = 0;
-#pragma unroll
-  for (int j = 0; j < kFinPer; ++j) {
-    if (i0 + j < total) {
-      na += key[j] > top;
-      ni += (key[j] & bmask) == pre;
+    for (int j = 0; j < kFinPer; ++j) {
+      const uint64_t e = addr[j] >= 0 ? lrow[addr[j]] : 0ull;
+      key[j] = order_key(__uint_as_float((uint32_t)e));
     }
   }
-  int tot2;
-  const int pref = block_exclusive_scan<kWgThreads>(na | (ni << 16), sh.scan, &tot2);
-  int pa = pref & 0xffff, pi = pref >> 16;
-  int32_t* orow = a.out_idx + (int64_t)row * B;
-  float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
-  const uint64_t* lrow64 = (const uint64_t*)lrow;
-  sg = sg0;
-  // output in batches of kOutBatch entries: positions and addresses first,
-  // then the batch's loads together, then its stores
-  constexpr int kOutBatch = 8;
+  // tau = the largest t with at least B keys >= t. The keys share the
+  // common prefix of t_lo and the row's largest key; one 256-bin LDS
+  // histogram fixes the next 8 bits, the keys of the chosen bin (usually a
+  // few hundred) are compacted into LDS, and bisection over their
+  // remaining bits finishes it, each step one compare per entry, a ballot
+  // and a barrier. A bin too big for the compaction is bisected in the
+  // registers instead.
+  const uint32_t kmax = sh.kmax;
+  const int fixed = t_lo == kmax ? 32 : __clz(t_lo ^ kmax);
+  uint32_t tau = fixed == 0 ? 0u : (t_lo & (~0u << (32 - fixed)));
+  if (fixed < 32) {
+    const int wA = min(8, 32 - fixed), shA = 32 - fixed - wA;
+    const int nb = 1 << wA;
+    sh.hist[tid] = 0u;
+    __syncthreads();
 #pragma unroll
-  for (int j0 = 0; j0 < kFinPer; j0 += kOutBatch) {
-    int pos[kOutBatch], addr[kOutBatch];
+    for (int j = 0; j < kFinPer; ++j)
+      if (j < nv) atomicAdd(&sh.hist[(key[j] >> shA) & (uint32_t)(nb - 1)], 1u);
+    __syncthreads();
+    const int c = tid < nb ? (int)sh.hist[nb - 1 - tid] : 0;
+    int tot;
+    const int excl = block_exclusive_scan<kWgThreads>(c, sh.scan, &tot);
+    if (tid < nb && excl < B && B <= excl + c) {
+      sh.bin = nb - 1 - tid;
+      sh.above = excl;
+    }
+    if (tid == 0) sh.ncomp = 0;
+    __syncthreads();
+    const uint32_t b1 = (uint32_t)sh.bin;
+    const int need = B - sh.above;        // keys of the bin at or above tau
+    const int c1 = (int)sh.hist[b1];
+    tau |= b1 << shA;
+    if (shA > 0) {
+      const uint32_t top = tau >> shA;
+      if (c1 <= kCompCap) {
+        uint32_t* comp = (uint32_t*)keep_lds;
 #pragma unroll
-    for (int jj = 0; jj < kOutBatch; ++jj) {
-      const int j = j0 + jj, i = i0 + j;
-      pos[jj] = -1;
-      addr[jj] = 0;
-      if (i < total) {
-        while (sh.seg_off[sg + 1] <= i) ++sg;
-        addr[jj] = sg * kChunk + (i - sh.seg_off[sg]);
-        if (key[j] > top) {
-          pos[jj] = pa + min(pi, nd);
-          ++pa;
-        } else if ((key[j] & bmask) == pre) {
-          if (pi < nd) pos[jj] = pa + pi;
-          ++pi;
+        for (int j = 0; j < kFinPer; ++j) {
+          const bool in = j < nv && (key[j] >> shA) == top;
+          const uint64_t bm = ballot64(in);
+          if (bm == 0ull) continue;
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&sh.ncomp, __popcll(bm));
+          base = __shfl(base, 0, 64);
+          if (in) comp[base + rank_below(bm)] = key[j];
+        }
+        __syncthreads();
+        uint32_t ck[kCompCap / kWgThreads];
+#pragma unroll
+        for (int q = 0; q < kCompCap / kWgThreads; ++q) {
+          const int i = tid + q * kWgThreads;
+          ck[q] = i < c1 ? comp[i] : 0u;
+        }
+        for (int bit = shA - 1; bit >= 0; --bit) {
+          const uint32_t cand = tau | (1u << bit);
+          int cc = 0;
+#pragma unroll
+          for (int q = 0; q < kCompCap / kWgThreads; ++q)
+            cc += __popcll(ballot64(tid + q * kWgThreads < c1 && ck[q] >= cand));
+          if (lane == 0) sh.cnt[bit & 1][wid] = cc;
+          __syncthreads();
+          int tc = 0;
+#pragma unroll
+          for (int w = 0; w < kWgThreads / 64; ++w) tc += sh.cnt[bit & 1][w];
+          if (tc >= need) tau = cand;
+        }
+      } else {
+        for (int bit = shA - 1; bit >= 0; --bit) {
+          const uint32_t cand = tau | (1u << bit);
+          int cc = 0;
+#pragma unroll
+          for (int j = 0; j < kFinPer; ++j) cc += __popcll(ballot64(j < nv && key[j] >= cand));
+          if (lane == 0) sh.cnt[bit & 1][wid] = cc;
+          __syncthreads();
+          int tc = 0;
+#pragma unroll
+          for (int w = 0; w < kWgThreads / 64; ++w) tc += sh.cnt[bit & 1][w];
+          if (tc >= B) tau = cand;
         }
       }
     }
+  }
+  int na = 0, ni = 0;
+#pragma unroll
+  for (int j = 0; j < kFinPer; ++j) {
+    na += j < nv && key[j] > tau;
+    ni += j < nv && key[j] == tau;
+  }
+  int tot2;
+  const int pref = block_exclusive_scan<kWgThreads>(na | (ni << 16), sh.scan, &tot2);
+  const int nd = B - (tot2 & 0xffff);   // keys equal to tau that are taken
+  int pa = pref & 0xffff, pi = pref >> 16;
+  // each taken entry's position and list address, packed in one word (the
+  // keys die as they go), then the taken entries are read again from the
+  // lists kOutBatch at a time, all in flight together
+  static_assert(kFinCap <= (1 << 14) && kChunk * kMaxParts <= (1 << 17), "position and address pack in 31 bits");
+  int packed[kFinPer];
+  {
+    int sg = 0;
+    if (nv > 0)
+      while (sh.seg_off[sg + 1] <= i0) ++sg;
+    int next = sh.seg_off[sg + 1];
+#pragma unroll
+    for (int j = 0; j < kFinPer; ++j) {
+      const int i = i0 + j;
+      packed[j] = -1;
+      if (j >= nv) continue;
+      while (next <= i) next = sh.seg_off[++sg + 1];
+      int pos = -1;
+      if (key[j] > tau) {
+        pos = pa + min(pi, nd);
+        ++pa;
+      } else if (key[j] == tau) {
+        if (pi < nd) pos = pa + pi;
+        ++pi;
+      }
+      if (pos >= 0) packed[j] = (pos << 17) | (sg * kChunk + (i - sh.seg_off[sg]));
+    }
+  }
+  int32_t* orow = a.out_idx + (int64_t)row * B;
+  float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
+  constexpr int kOutBatch = 16;
+#pragma unroll
+  for (int j0 = 0; j0 < kFinPer; j0 += kOutBatch) {
     uint64_t e[kOutBatch];
 #pragma unroll
-    for (int jj = 0; jj < kOutBatch; ++jj) e[jj] = pos[jj] >= 0 ? lrow64[addr[jj]] : 0ull;
+    for (int jj = 0; jj < kOutBatch; ++jj)
+      e[jj] = packed[j0 + jj] >= 0 ? lrow[packed[j0 + jj] & 0x1ffff] : 0ull;
 #pragma unroll
     for (int jj = 0; jj < kOutBatch; ++jj) {
-      if (pos[jj] < 0) continue;
-      orow[pos[jj]] = (int32_t)(e[jj] >> 32);
-      if (osc) osc[pos[jj]] = __uint_as_float((uint32_t)e[jj]);
+      const int pk = packed[j0 + jj];
+      if (pk < 0) continue;
+      orow[pk >> 17] = (int32_t)(e[jj] >> 32);
+      if (osc) osc[pk >> 17] = __uint_as_float((uint32_t)e[jj]);   // the score's own bits
     }
   }
 }
@@ -470,6 +543,9 @@ __device__ __forceinline__ void load_ch2(const void* base, int64_t off, bool ok,
 
 template <bool BF16, int G>
 __device__ __forceinline__ void attend_part(const StepArgs& a, AttnShared& sh, int row, int part) {
+  // list entries per wave per batch: with four or fewer heads a wave holds
+  // 16 K and V rows at once (a part of 64 entries is one round trip)
+  constexpr int KB = G <= 4 ? 2 * kBatch : kBatch;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int n = row / a.Hkv, g = row % a.Hkv;
   const int B = a.B;
@@ -496,12 +572,12 @@ __device__ __forceinline__ void attend_part(const StepArgs& a, AttnShared& sh, i
     o0[h] = 0.f;
     o1[h] = 0.f;
   }
-  // wave wid takes batches wid, wid + 4, ... of kBatch entries
-  for (int b0 = wid * kBatch; b0 < ne; b0 += 4 * kBatch) {
-    float k0[kBatch], k1[kBatch], v0[kBatch], v1[kBatch];
-    bool ok[kBatch];
+  // wave wid takes batches wid, wid + 4, ... of KB entries
+  for (int b0 = wid * KB; b0 < ne; b0 += 4 * KB) {
+    float k0[KB], k1[KB], v0[KB], v1[KB];
+    bool ok[KB];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
+    for (int i = 0; i < KB; ++i) {
       const int t = b0 + i < ne ? sh.idx[b0 + i] : -1;
       ok[i] = t >= 0 && t < a.T;
       const int64_t off = kv0 + (int64_t)t * a.kv_s_tok;
@@ -510,10 +586,10 @@ __device__ __forceinline__ void attend_part(const StepArgs& a, AttnShared& sh, i
     }
 #pragma unroll
     for (int h = 0; h < G; ++h) {
-      float z[kBatch];
+      float z[KB];
       float mb = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
+      for (int i = 0; i < KB; ++i) {
         float s = sum_lanes<16>(fmaf(q0[h], k0[i], q1[h] * k1[i]));
         s += __shfl_xor(s, 16, 64);
         s += __shfl_xor(s, 32, 64);
@@ -527,7 +603,7 @@ __device__ __forceinline__ void attend_part(const StepArgs& a, AttnShared& sh, i
       o0[h] *= f;
       o1[h] *= f;
 #pragma unroll
-      for (int i = 0; i < kBatch; ++i) {
+      for (int i = 0; i < KB; ++i) {
         const float pz = exp2f(z[i] - mn);
         l[h] += pz;
         o0[h] = fmaf(pz, v0[i], o0[h]);
@@ -596,19 +672,17 @@ __device__ __forceinline__ void merge_row(const StepArgs& a, AttnShared& sh, int
   }
   __syncthreads();
   // thread (h, c): c < kD the head's output channel, c == kD its sum; the
-  // parts' values are loaded eight at a time, all in flight together
+  // parts' values are loaded all at once
   for (int e = tid; e < G * (kD + 1); e += kWgThreads) {
     const int h = e / (kD + 1), c = e % (kD + 1);
     const float* col = base + h * (kD + 2) + (c == kD ? 1 : 2 + c);
+    float x[kMaxParts];
+#pragma unroll
+    for (int q = 0; q < kMaxParts; ++q) x[q] = q < P ? col[(int64_t)q * partial_stride(G)] : 0.f;
     float acc = 0.f;
-    for (int p0 = 0; p0 < P; p0 += 8) {
-      float x[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) x[u] = p0 + u < P ? col[(int64_t)(p0 + u) * partial_stride(G)] : 0.f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (p0 + u < P) acc = fmaf(sh.w[p0 + u][h], x[u], acc);
-    }
+    for (int q = 0; q < kMaxParts; ++q)
+      if (q < P) acc = fmaf(sh.w[q][h], x[q], acc);
     if (c == kD) sh.l[0][h] = acc;
     else sh.o[0][h][c] = acc;
   }
@@ -753,7 +827,7 @@ __global__ __launch_bounds__(kWgThreads, LSA_STEP_WG_PER_CU) void decode_step_ke
   if (tid == 0) sh.flag = add_l(rc + kRowCollected, 1u) == (uint32_t)a.wpr - 1u;
   __syncthreads();
   if (__builtin_amdgcn_readfirstlane(sh.flag)) {
-    select_row_exact(a, sh.u.fin, row);
+    select_row_exact(a, sh.u.fin, row, err, sh.keep);   // the scores kept in LDS are spent
     all_done();
     if (tid == 0) add_l(rc + kRowSelected, 1u);
   } else {
