@@ -30,6 +30,9 @@
 #ifndef LSA_SELECT_SEGMENTED
 #define LSA_SELECT_SEGMENTED 1   // long hinted rows: segmented collect, then the row select
 #endif
+#ifndef LSA_SELECT_SEG_MIN
+#define LSA_SELECT_SEG_MIN 16384   // shortest row that takes the segmented collect
+#endif
 
 namespace lsa {
 namespace {
@@ -82,7 +85,7 @@ size_t bitmap_bytes(int rows, int n) {
 }  // namespace
 
 int select_segments(int n, int B, bool hint_usable) {
-  if (!LSA_SELECT_SEGMENTED || !hint_usable || B > kCap / 2 || n < 2 * kSeg) return 0;
+  if (!LSA_SELECT_SEGMENTED || !hint_usable || B > kCap / 2 || n < 2 * kSeg || n < LSA_SELECT_SEG_MIN) return 0;
   const int nseg = (n + kSeg - 1) / kSeg;
   return nseg <= kThreads ? nseg : 0;   // the row kernel scans one count per thread
 }
