@@ -377,6 +377,92 @@ __device__ __forceinline__ bool select_short_row(const SelectArgs& a, SelShared&
   return true;
 }
 
+// Rows of kThreads * 8 < n <= kThreads * 16 slots, all of them valid: every
+// slot in registers (thread t holding slots 16t .. 16t+15, already in list
+// order), then the exact selection in registers. Returns false (nothing
+// written) for other rows or when a slot is invalid.
+template <bool CAND>
+__device__ __forceinline__ bool select_short_row16(const SelectArgs& a, SelShared& sh, int row,
+                                                   const float* srow, int64_t nv, const int32_t* crow) {
+  constexpr int kPer = 16;
+  if (nv <= (int64_t)kThreads * 8 || nv > (int64_t)kThreads * kPer) return false;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int B = a.B;
+  const int s0 = tid * kPer;
+  float val[kPer];
+  if (s0 + kPer <= nv && (((uintptr_t)(srow + s0)) & 15u) == 0) {
+#pragma unroll
+    for (int q = 0; q < kPer / 4; ++q) {
+      const float4 x = *(const float4*)(srow + s0 + 4 * q);
+      val[4 * q] = x.x; val[4 * q + 1] = x.y; val[4 * q + 2] = x.z; val[4 * q + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) val[j] = s0 + j < nv ? srow[s0 + j] : 0.f;
+  }
+  uint32_t key[kPer];
+  int32_t slot[kPer];
+  int bad = 0;
+  uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    key[j] = order_key(val[j]);
+    slot[j] = s0 + j;
+    if (s0 + j < nv) {
+      if (slot_ok<CAND>(a, crow, s0 + j, nv)) {
+        lo = min(lo, key[j]);
+        hi = max(hi, key[j]);
+      } else {
+        ++bad;
+      }
+    }
+  }
+  if (tid == 0) {
+    sh.kmax = 0u;
+    sh.nsample = -1;           // the minimum key (0xffffffff as unsigned)
+    sh.ncand = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o, 64));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o, 64));
+    bad += __shfl_xor(bad, o, 64);
+  }
+  if (lane == 0) {
+    atomicMax(&sh.kmax, hi);
+    atomicMin(reinterpret_cast<uint32_t*>(&sh.nsample), lo);
+    if (bad) atomicAdd(&sh.ncand, bad);
+  }
+  __syncthreads();
+  const bool any_bad = sh.ncand != 0;
+  const uint32_t t_lo = (uint32_t)sh.nsample, kmax = sh.kmax;
+  __syncthreads();   // the general path resets these words
+  if (any_bad) return false;
+  const int total = (int)nv;
+  if (total <= B) {   // every slot is taken, in slot order; pad
+    int32_t* orow = a.out_idx + (int64_t)row * B;
+    float* osc = a.out_score ? a.out_score + (int64_t)row * B : nullptr;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (s0 + j >= total) continue;
+      orow[s0 + j] = slot_pos<CAND>(a, crow, s0 + j);
+      if (osc) osc[s0 + j] = val[j];
+    }
+    for (int p = total + tid; p < B; p += kThreads) {
+      orow[p] = -1;
+      if (osc) osc[p] = -INFINITY;
+    }
+    if (tid == 0 && a.out_count) a.out_count[row] = total;
+    return true;
+  }
+  for (int i = tid; i < 2 * kBins; i += kThreads) sh.cslot[i] = 0;   // the refine histograms
+  zero_hist(sh);
+  __syncthreads();
+  select_in_registers<CAND, kPer>(a, sh, row, crow, key, val, slot, s0, total, t_lo, kmax);
+  return true;
+}
+
 template <bool CAND, bool GBM, bool PRE>
 __device__ __forceinline__ void select_row(const SelectArgs& a, int row, const float* srow,
                                            int64_t nv, unsigned char* smem_raw) {
@@ -401,6 +487,7 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int row, const f
 
   if constexpr (!PRE) {
     if (select_short_row<CAND>(a, sh, row, srow, nv, crow)) return;
+    if (select_short_row16<CAND>(a, sh, row, srow, nv, crow)) return;
   }
   zero_hist(sh);
   if constexpr (PRE) {

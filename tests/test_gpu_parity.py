@@ -226,6 +226,10 @@ def _assert_select_equal(sc32, B, **kw):
     (2, 50000, 9000, "normal"),       # boundary bin with more keys than fit in LDS
     (2, 3001, 64, "special"),         # NaN, +-0, +-inf
     (2, 300000, 2048, "normal"),      # bitmaps in workspace
+    (3, 16384, 128, "normal"),        # rows of up to 16384 slots in registers, 16 per thread
+    (2, 12000, 3000, "ints"),         # ... with many exact ties
+    (2, 8193, 2048, "special"),       # ... one slot past the 8-per-thread rows
+    (2, 16384, 16384, "normal"),      # ... every slot taken
 ])
 def test_select_exact(rows, n, B, kind):
     rng = np.random.default_rng(n + B)
@@ -254,6 +258,11 @@ def test_select_valid_counts_causal_and_candidates():
     Hkv = 2
     scl2 = rng.standard_normal((400 * Hkv, 400)).astype(np.float32)
     _assert_select_equal(scl2, 64, causal_group=Hkv)
+    say("select candidates, 200 blocks of 64 (rows of 12800 slots in registers)")
+    cand16 = np.stack([np.sort(rng.choice(16384, 200, replace=False)) for _ in range(3)]).astype(np.int32)
+    cand16[1, -3:] = -1                        # invalid blocks: the row takes the general path
+    sc16 = rng.standard_normal((3, 200 * 64)).astype(np.float32)
+    _assert_select_equal(sc16, 1500, cand=cand16, cand_block=64, n_positions=16384 * 64 - 20)
     say("select candidates")
     rows, nc, blk = 4, 128, 64
     cand = np.stack([np.sort(rng.choice(16384, nc, replace=False)) for _ in range(rows)]).astype(np.int32)
