@@ -360,9 +360,11 @@ int lsa_indexed_attention_noalloc(const lsa_attn_desc* desc, void* stream);
  * Workspace contract: the workspace must be all zero before the first call
  * that uses it (allocate it zeroed, or clear it once); every call leaves
  * the control words zero again, except the 32-bit error word at byte
- * offset 36, which stays set (bit 0) once a call gives up an internal
- * wait; the outputs of such a call are not valid. Two calls that share a
- * workspace must not overlap in time.
+ * offset 36, which stays set once a call of the persistent launch gives
+ * up an internal wait (bit 0) or finds a row listing fewer than B keys
+ * above its threshold (bit 1, which the kernel's own hints rule out); the
+ * outputs of such a call are not valid. Two calls that share a workspace
+ * must not overlap in time.
  */
 typedef struct lsa_step_desc {
   uint32_t struct_size;      /* sizeof(lsa_step_desc) */
