@@ -663,9 +663,19 @@ def main() -> int:
     plan3 = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, fused=False)
     three_us = _windows_us(torch, lambda i: plan3.run(Q, W, inst[i & 1][2], inst[i & 1][0], inst[i & 1][1]),
                            max(steps, 7), warm=args.warmup)
-    del plan3
-    log(f"the same step as three separate calls: {three_us:.1f} us/step; fused path: "
-        f"{plan.step_ws is not None and lsa.lsa_step_is_fused(Q, W, inst[0][2], inst[0][0], inst[0][1], plan.idx, plan.out, one_launch=plan.one_launch)}")
+    # the opt-in single persistent launch of the same step (LSA_STEP_ONE_LAUNCH):
+    # timed the same way, its index sets compared with the timed path's below
+    plan1 = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, fused=True, one_launch=True)
+    one_us = _windows_us(torch, lambda i: plan1.run(Q, W, inst[i & 1][2], inst[i & 1][0], inst[i & 1][1]),
+                         max(steps, 7), warm=args.warmup)
+    plan1.run(Q, W, inst[0][2], inst[0][0], inst[0][1])
+    torch.cuda.synchronize()
+    one_idx, one_err = plan1.idx.cpu().numpy(), plan1.step_error()
+    one_is = lsa.lsa_step_is_fused(Q, W, inst[0][2], inst[0][0], inst[0][1], plan1.idx, plan1.out,
+                                   one_launch=True)
+    del plan1
+    log(f"the same step as three separate calls: {three_us:.1f} us/step; as one persistent launch "
+        f"(opt-in): {one_us:.1f} us/step (runs as one launch: {one_is})")
 
     keys = N * Hkv * T
     kidx_bytes = keys * r * 2
@@ -691,6 +701,8 @@ def main() -> int:
     torch.cuda.synchronize()
     plan_error = plan.step_error()
     gpu_idx = plan.idx.cpu().numpy()
+    one_launch = {"us_per_step": one_us, "runs_as_one_launch": bool(one_is),
+                  "error_word": int(one_err), "idx_equal_to_timed_step": bool(np.array_equal(one_idx, gpu_idx))}
     gpu_out = plan.out.cpu().numpy()
     gpu_lse = plan.lse.cpu().numpy()
 
@@ -800,6 +812,7 @@ def main() -> int:
                      "launch_timing": "median of 7 windows of 20 back-to-back launches",
                      "traffic": traffic},
         "three_calls_us_per_step": three_us if ok else None,
+        "one_launch_step": one_launch if ok else None,
         "step_error_word": plan_error,
         "graph_replay": {"us_per_step": graph_us if ok else None,
                          "steps_per_s": 1e6 / graph_us if ok else None,
