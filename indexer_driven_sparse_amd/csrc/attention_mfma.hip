@@ -522,6 +522,61 @@ __global__ __launch_bounds__(64) void attn_mfma16_kernel(AttnArgs a) {
 // (8 waves rather than 4 halve the partials the merge reads: 4.4 us against
 // 5.0 for the merge at the 4 x 8-head, top-2048 decode shape.)
 constexpr int kDecWaves = 8;
+// floats per split partial when the splits are merged in the launch: G heads
+// of (max, sum, kD outputs), rounded up to whole 128-byte lines
+__host__ __device__ constexpr int dec_partial_stride(int G) { return (G * (kD + 2) + 31) / 32 * 32; }
+
+// The last workgroup out clears the launch-wide control words.
+__device__ __forceinline__ void decode_launch_done(const AttnArgs& a) {
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(a.ctrl + 8, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1u) {
+    for (int i = 0; i < 9; ++i) __hip_atomic_store(a.ctrl + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Log-sum-exp merge of a (sequence, KV head)'s split partials into out and
+// lse, with the merge kernel's arithmetic in the same order (so the results
+// are the same bits). lds: at least 2 * splits * GL floats.
+template <int GL>
+__device__ __forceinline__ void decode_merge_row(const AttnArgs& a, int64_t rowg, float* lds) {
+  const int t = threadIdx.x, S = a.splits;
+  const int row = (int)(rowg / a.Hkv), g = (int)(rowg % a.Hkv);
+  const int ps = dec_partial_stride(GL);
+  const float* base = a.partial + rowg * S * ps;
+  float* s_m = lds;
+  float* s_l = lds + S * GL;
+  for (int e = t; e < S * GL; e += 64 * kDecWaves) {
+    const int sp = e / GL, hh = e % GL;
+    s_m[e] = base[sp * ps + hh * (kD + 2)];
+    s_l[e] = base[sp * ps + hh * (kD + 2) + 1];
+  }
+  __syncthreads();
+  for (int e = t; e < GL * kD; e += 64 * kDecWaves) {
+    const int h = e / kD, c = e % kD;
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, s_m[sp * GL + h]);
+    float L = 0.f, O = 0.f;
+    for (int s0 = 0; s0 < S; s0 += 8) {   // eight splits' values in flight at once
+      float o[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) o[u] = s0 + u < S ? base[(s0 + u) * ps + h * (kD + 2) + 2 + c] : 0.f;
+      if (M != -INFINITY) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (s0 + u < S) {
+            const float f = exp2f(s_m[(s0 + u) * GL + h] - M);
+            L += s_l[(s0 + u) * GL + h] * f;
+            O += o[u] * f;
+          }
+        }
+      }
+    }
+    const int64_t oh = (int64_t)row * a.Hq + (int64_t)g * GL + h;
+    a.out[oh * kD + c] = M == -INFINITY ? 0.f : O / L;
+    if (c == 0 && a.lse) a.lse[oh] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2f;
+  }
+}
+
 template <int GL>
 __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnArgs a) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -536,8 +591,28 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnAr
   uint8_t* sV = sVall[w];
   uint16_t* sP = sPall[w];
   uint16_t* sPl = sPlall[w];
-  const int split = (int)(blockIdx.x % a.splits);
-  const int64_t rowg = blockIdx.x / a.splits;
+  __shared__ int s_flag;
+  int split;
+  int64_t rowg;
+  if (a.ctrl != nullptr) {   // (row, split) from this XCD's queue: a row's splits share its L2
+    const int nx = a.nxcc;
+    const int x = (int)((__builtin_amdgcn_s_getreg((15 << 11) | 20) & 15u) % (unsigned)nx);   // HW_REG_XCC_ID
+    if (tid == 0) s_flag = (int)__hip_atomic_fetch_add(a.ctrl + x, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    const int ticket = __builtin_amdgcn_readfirstlane(s_flag);
+    const int64_t nrg = (int64_t)a.rows * a.Hkv;
+    const int nr = x < nrg ? (int)((nrg - x + nx - 1) / nx) : 0;
+    __syncthreads();
+    if (ticket >= nr * a.splits) {   // more workgroups landed on this XCD than it has splits
+      decode_launch_done(a);
+      return;
+    }
+    rowg = x + (int64_t)nx * (ticket / a.splits);
+    split = ticket % a.splits;
+  } else {
+    split = (int)(blockIdx.x % a.splits);
+    rowg = blockIdx.x / a.splits;
+  }
   const int g = (int)(rowg % a.Hkv), row = (int)(rowg / a.Hkv);
   const int e0 = split * (kDecWaves * kKC) + w * kKC;   // this wave's first list entry
   const int32_t* ilist = a.idx + rowg * a.B;
@@ -684,13 +759,30 @@ __global__ __launch_bounds__(64 * kDecWaves) void attn_decode_mfma_kernel(AttnAr
       if (c == 0 && a.lse) a.lse[oh] = M == -INFINITY ? -INFINITY : (M + log2f(L)) * kLn2f;
       continue;
     }
-    float* pr = a.partial + ((rowg * a.splits + split) * GL + h) * (kD + 2);
+    float* pr = a.ctrl ? a.partial + (rowg * a.splits + split) * dec_partial_stride(GL) + h * (kD + 2)
+                       : a.partial + ((rowg * a.splits + split) * GL + h) * (kD + 2);
     pr[2 + c] = O;
     if (c == 0) {
       pr[0] = M;
       pr[1] = L;
     }
   }
+  if (a.ctrl != nullptr && a.splits > 1) {
+    // the last split of the row merges: the partials are in this XCD's L2,
+    // one writing workgroup per 128-byte line, read only after the arrival
+    // count (an atomic, performed in that L2) shows every split done
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0)
+      s_flag = __hip_atomic_fetch_add(a.ctrl + 16 + rowg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) ==
+               (uint32_t)a.splits - 1u;
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_flag)) {
+      if (tid == 0) __hip_atomic_store(a.ctrl + 16 + rowg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+      decode_merge_row<GL>(a, rowg, reinterpret_cast<float*>(&sVall[0][0]));
+    }
+  }
+  if (a.ctrl != nullptr) decode_launch_done(a);
 }
 
 hipError_t launch_mfma_blocks(const AttnArgs& a, hipStream_t s) {
@@ -712,10 +804,14 @@ bool attention_decode_mfma_supported(int G, int d, int B, bool bf16) {
   return bf16 && d == kD && (G == 4 || G == 8) && B >= 1 && (B + kDecodeSplit - 1) / kDecodeSplit <= 64;
 }
 
+int decode_partial_stride(int G) { return dec_partial_stride(G); }
+
 hipError_t launch_attention_decode_mfma(const AttnArgs& a, hipStream_t s) {
   static_assert(kDecodeSplit == kDecWaves * kKC, "a split is one 32-key MFMA step per wave");
   const int G = a.Hq / a.Hkv;
-  const dim3 grid((unsigned)((int64_t)a.rows * a.Hkv * a.splits));
+  const int64_t nrg = (int64_t)a.rows * a.Hkv;
+  if (a.ctrl != nullptr && (a.nxcc < 1 || a.nxcc > 8 || nrg > 1000)) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(a.ctrl ? a.nxcc * ((nrg + a.nxcc - 1) / a.nxcc) * a.splits : nrg * a.splits));
   if (G == 4)
     hipLaunchKernelGGL(attn_decode_mfma_kernel<4>, grid, dim3(64 * kDecWaves), 0, s, a);
   else if (G == 8)
@@ -723,7 +819,7 @@ hipError_t launch_attention_decode_mfma(const AttnArgs& a, hipStream_t s) {
   else
     return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
+  if (e != hipSuccess || a.splits == 1 || a.ctrl != nullptr) return e;
   return launch_attention_merge(a, s);
 }
 

@@ -168,7 +168,15 @@ struct AttnArgs {
   const int32_t* slot;               // paged: [n_seq, slot_ld] position -> pool row
   int64_t slot_ld;
   int n_rows_kv;                     // rows addressable per sequence (T, or the pool size)
+  // decode on the matrix cores only: with ctrl set, a (sequence, KV head)'s
+  // splits run on one XCD (tickets per XCD, nxcc XCDs) and the last split to
+  // finish merges them in place of the merge kernel; partials then sit
+  // decode_partial_stride(G) floats apart. ctrl: zero before the launch and
+  // left zero ([0..7] tickets, [8] finished workgroups, [16 + rowg] arrivals)
+  uint32_t* ctrl = nullptr;
+  int nxcc = 0;
 };
+int decode_partial_stride(int G);   // floats per split partial when merged in the launch
 // Decode on the matrix cores (bf16, d = 128, G = 4 or 8, at most 64
 // splits): one workgroup per split of kDecodeSplit list entries, writing a
 // split partial, merged by launch_attention_merge.

@@ -261,7 +261,9 @@ int check_ws(void* ws, size_t have, size_t need) {
 
 // Launch an attention call whose descriptor has been validated; ws holds
 // the split partials (the caller's workspace, or the static scratch).
-int run_attention(const lsa_attn_desc* d, void* ws, void* stream) {
+// ctrl/nxcc: the decode step's zeroed control words and the XCD count; with
+// them the matrix-core decode path merges its splits in the launch.
+int run_attention(const lsa_attn_desc* d, void* ws, void* stream, uint32_t* ctrl = nullptr, int nxcc = 0) {
   lsa::AttnArgs a{};
   a.q = d->q;
   a.k = d->k;
@@ -291,6 +293,10 @@ int run_attention(const lsa_attn_desc* d, void* ws, void* stream) {
   lsa::attention_plan(d->rows, d->n_kv_heads, a.Hq / a.Hkv, a.d, a.B, mfma_decode, &a.splits,
                       &a.keys_per_split);
   hipError_t e;
+  if (mfma_decode && ctrl != nullptr && nxcc >= 1 && nxcc <= 8 && (int64_t)d->rows * d->n_kv_heads <= 1000) {
+    a.ctrl = ctrl;
+    a.nxcc = nxcc;
+  }
   if (mfma_decode)
     e = lsa::launch_attention_decode_mfma(a, (hipStream_t)stream);
   else if (lsa::attention_mfma_supported(a, d->kv_dtype == LSA_BF16))
@@ -403,6 +409,12 @@ int plan_step(const lsa_step_desc* d, StepPlan* p) {
   at.out = d->out;
   at.lse = d->lse;
   LSA_TRY(validate_attn(&at, &p->attn_bytes));
+  {   // the in-launch merge keeps each split partial on whole 128-byte lines
+    const int Gq = d->n_q_heads / d->n_kv_heads;
+    int sp = 1, kps = 0;
+    lsa::attention_plan((int)rows / d->n_kv_heads, d->n_kv_heads, Gq, d->head_dim, d->topk, true, &sp, &kps);
+    p->attn_bytes = std::max(p->attn_bytes, (size_t)rows * sp * lsa::decode_partial_stride(Gq) * sizeof(float));
+  }
 
   p->off_attn = p->off_sel + align256(p->sel_bytes);
   p->total = p->off_attn + p->attn_bytes;
@@ -722,7 +734,7 @@ int lsa_decode_step(const lsa_step_desc* d, void* ws, size_t ws_bytes, void* str
   }
   LSA_TRY(lsa_index_score(&p.score, nullptr, 0, stream));
   LSA_TRY(lsa_topk_select(&p.select, b + p.off_sel, p.sel_bytes, stream));
-  return run_attention(&p.attn, p.attn_bytes ? b + p.off_attn : nullptr, stream);
+  return run_attention(&p.attn, p.attn_bytes ? b + p.off_attn : nullptr, stream, (uint32_t*)b, device_xccs());
 }
 
 size_t lsa_step_workspace_bytes(const lsa_step_desc* d) {

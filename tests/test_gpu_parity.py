@@ -679,6 +679,40 @@ def _fused_vs_three_calls(case, kd, reps=1):
     return fus
 
 
+@pytest.mark.parametrize("name,over", [
+    ("decode_t128k_b2048", {"N": 1, "T": 100000, "B": 1024}),       # 4 splits per row
+    ("decode_t128k_b2048", {"N": 3, "Hq": 12, "Hkv": 3, "T": 70000, "B": 512}),  # 9 rows over 8 XCDs
+    ("decode_t128k_b2048", {"N": 2, "Hq": 32, "Hkv": 4, "T": 50000, "B": 1500}),  # 8 heads per group, a ragged split
+    ("decode_t128k_b2048", {"N": 2, "T": 50000, "B": 256}),         # one split: nothing to merge
+    ("decode_t128k_b2048", {"N": 4}),                               # the headline shape
+])
+def test_decode_step_equals_separate_calls(name, over):
+    """lsa_decode_step's default path (the matrix-core attention merging its
+    splits in the launch, each row's splits on one XCD) against the separate
+    calls lsa_index_score, lsa_topk_select and lsa_indexed_attention (whose
+    merge is a kernel of its own): indices, per-entry scores, q_idx, out and
+    lse bit for bit; run twice on one workspace, whose control words are
+    left zero."""
+    from indexer_driven_sparse_amd import pipeline
+    case = synth.workload(name, **over)
+    say("decode step vs separate calls", name, over)
+    N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
+    Q, W, K, V = dev(case.Q), dev(case.W), dev(case.K), dev(case.V)
+    kd = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_project_keys(K, W, kd)
+    ref = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, with_idx_scores=True, fused=False)
+    ref.run(Q, W, kd, K, V)
+    one = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, with_idx_scores=True, fused=True)
+    for _ in range(2):
+        one.run(Q, W, kd, K, V)
+    torch.cuda.synchronize()
+    assert one.step_error() == 0
+    for name_ in ("idx", "q_idx", "idx_scores", "out", "lse"):
+        a, b = getattr(one, name_), getattr(ref, name_)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name_
+    assert int(one.step_ws[:4096].view(torch.int32).abs().sum().item()) == 0
+
+
 @pytest.mark.parametrize("name,over,fused", [
     ("decode_t128k_b2048", {"N": 1, "T": 40000, "B": 1024}, True),    # 8 rows, ragged chunks
     ("decode_t128k_b2048", {"N": 2, "Hq": 24, "Hkv": 6, "T": 20000, "B": 512}, True),  # 12 rows
