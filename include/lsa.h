@@ -342,7 +342,11 @@ int lsa_indexed_attention_noalloc(const lsa_attn_desc* desc, void* stream);
  *     lsa_indexed_attention
  * on the same arguments: out_idx (and q_idx, out_score) bit-identical,
  * out / lse within the attention's own rounding. By default the call runs
- * those three calls in sequence. With flags = LSA_STEP_ONE_LAUNCH, shapes
+ * those three calls in sequence, except that the matrix-core decode
+ * attention merges its splits within its own launch (each row's splits on
+ * one XCD, the last to finish merging them; the control words at the
+ * workspace head make that possible), with the same results bit for bit.
+ * With flags = LSA_STEP_ONE_LAUNCH, shapes
  * with a bf16 or fp8 projected-key cache of 64 or 128 bytes per key, head
  * dim 128, 1, 2, 4 or 8 query heads per KV head, B a multiple of 32 that
  * the scoring hints vouch for (T >= 32 B), at most 32 chunks of 4096 keys
