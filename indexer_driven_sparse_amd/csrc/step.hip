@@ -5,9 +5,12 @@
 // Fig. 9).
 //
 // Why one launch: scoring is a long HBM stream, while the selection and the
-// attention are chains of short, latency-bound steps over a few MB. Run as
-// separate kernels, every boundary adds a ramp and a drain (several
-// microseconds each on MI355X) and the selection re-reads every score.
+// attention are chains of short, latency-bound steps over a few MB; in one
+// launch the scores never leave LDS and no kernel boundary separates the
+// phases. (Measured on MI355X a boundary costs only about 1 us on one
+// stream, and with every workgroup resident the rows finish scoring
+// together, so the phases do not overlap the stream: this launch is slower
+// than the separate kernels and is opt-in.)
 //
 // Layout: the device's XCDs each take rows x, x + nxcc, ... (nxcc XCDs):
 // a workgroup reads its XCD from the hardware, draws a ticket from that
@@ -21,11 +24,11 @@
 //                 vouch for hint_k keys) and publishes it;
 //   2. collect    every workgroup lists its slots whose key reaches t_lo,
 //                 in slot order, as (score bits, slot), straight from its
-//                 LDS; the last one to finish runs the exact
-//                 selection over the row's lists (8-bit radix levels in
-//                 registers, positions written in ascending order by one
-//                 prefix scan; a list that cannot settle it falls back to a
-//                 radix selection over the row's stored scores);
+//                 LDS; the last one to finish runs the exact selection over
+//                 the row's lists (an LDS histogram, then bisection, the
+//                 positions written in ascending order by one prefix scan;
+//                 lists too long for the registers are selected by radix
+//                 passes over the lists in memory);
 //   3. attend     every workgroup attends over its share of the row's B
 //                 selected positions (each K and V row read in place, one
 //                 256-byte row per wave-wide load, softmax in fp32 in the
