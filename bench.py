@@ -646,23 +646,44 @@ def main() -> int:
     log(f"timed {steps} steps in {n_win} windows: median {ms_per_step * 1000:.1f} us/step, "
         f"mean {total_ms / steps * 1000:.1f}, windows {[round(x * 1000, 1) for x in win_ms]}")
 
-    # the dominant kernel alone: back-to-back scoring launches (alternating
-    # cache instances), events only around each window of launches
-    def score_window(n):
+    # the dominant kernel alone: back-to-back launches of the timed step's
+    # scoring part (alternating cache instances), events only around each
+    # window of launches; and the plain scoring kernel of the three calls
+    step_path = lsa.lsa_step_path(Q, W, inst[0][2], inst[0][0], inst[0][1], plan.idx, plan.out)
+
+    def score_part(i):
+        K_, V_, kd_ = inst[i & 1]
+        plan.part(lsa.STEP_PART_SCORE, Q, W, kd_, K_, V_)
+
+    def score_window(fn, n):
         a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a_.record(stream)
         for i in range(n):
-            plan.score(Q, W, inst[i & 1][2])
+            fn(i)
         b_.record(stream)
         torch.cuda.synchronize()
         return a_.elapsed_time(b_) / n
-    score_window(10)
-    score_ms = float(np.median([score_window(20) for _ in range(7)]))
+    score_window(score_part, 10)
+    score_ms = float(np.median([score_window(score_part, 20) for _ in range(7)]))
+    plain_fn = lambda i: plan.score(Q, W, inst[i & 1][2])   # noqa: E731
+    score_window(plain_fn, 10)
+    plain_score_ms = float(np.median([score_window(plain_fn, 20) for _ in range(7)]))
+    score_kernel = ("score_emit_kernel (scoring prep, projected-key scoring and the select's candidate lists)"
+                    if step_path == "listed" else "score_decode_kernel (scoring prep + projected-key scoring)")
+    log(f"timed step path: {step_path}; its scoring launch {score_ms * 1000:.1f} us, "
+        f"the plain scoring kernel {plain_score_ms * 1000:.1f} us")
 
     # the same step as the three separate calls (scoring, select, attention)
     plan3 = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, fused=False)
     three_us = _windows_us(torch, lambda i: plan3.run(Q, W, inst[i & 1][2], inst[i & 1][0], inst[i & 1][1]),
                            max(steps, 7), warm=args.warmup)
+    # one lsa_decode_step call with LSA_STEP_THREE_CALLS (the select's own
+    # collect launch instead of the listing scoring launch)
+    plan3f = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, three_calls=True)
+    three_flag_us = _windows_us(torch, lambda i: plan3f.run(Q, W, inst[i & 1][2], inst[i & 1][0], inst[i & 1][1]),
+                                max(steps, 7), warm=args.warmup)
+    del plan3f
+    log(f"the same call with LSA_STEP_THREE_CALLS: {three_flag_us:.1f} us/step")
     # the opt-in single persistent launch of the same step (LSA_STEP_ONE_LAUNCH):
     # timed the same way, its index sets compared with the timed path's below
     plan1 = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, fused=True, one_launch=True)
@@ -719,11 +740,19 @@ def main() -> int:
 
     stages = None
     if not args.no_stages:
+        # the timed path's three parts, each in windows of back-to-back launches
+        def part_fn(parts):
+            return lambda i: plan.part(parts, Q, W, inst[i & 1][2], inst[i & 1][0], inst[i & 1][1])
         stages = {
-            "score_us": _windows_us(torch, lambda i: plan.score(Q, W, inst[i & 1][2]), 140),
-            "select_us": _windows_us(torch, lambda i: plan.select(), 140),
-            "attention_us": _windows_us(torch, lambda i: plan.attend(Q, inst[i & 1][0], inst[i & 1][1]),
-                                        140),
+            "path": step_path,
+            "score_us": _windows_us(torch, part_fn(lsa.STEP_PART_SCORE), 140),
+            "select_us": _windows_us(torch, part_fn(lsa.STEP_PART_SELECT), 140),
+            "attention_us": _windows_us(torch, part_fn(lsa.STEP_PART_ATTEND), 140),
+            "three_call_kernels": {
+                "score_us": _windows_us(torch, lambda i: plan.score(Q, W, inst[i & 1][2]), 140),
+                "select_us": _windows_us(torch, lambda i: plan.select(), 140),
+                "attention_us": _windows_us(torch, lambda i: plan.attend(Q, inst[i & 1][0], inst[i & 1][1]),
+                                            140)},
         }
         stages["attended_kv_GBps"] = sel_kv_bytes / (stages["attention_us"] * 1e-6) / 1e9
 
@@ -805,13 +834,16 @@ def main() -> int:
         "keys_scored_per_s": keys * steps_per_s if ok else None,
         "hbm_frac_end_to_end": step_bytes / (ms_per_step * 1e-3) / (HBM_PEAK_GBPS * 1e9) if ok else None,
         "algorithmic_bytes_per_step": step_bytes,
-        "roofline": {"kernel": "score_decode_kernel (scoring prep + projected-key scoring)",
+        "roofline": {"kernel": score_kernel,
                      "bound": "hbm", "achieved": score_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": score_gbps / HBM_PEAK_GBPS,
                      "avg_launch_us": score_ms * 1000.0,
                      "launch_timing": "median of 7 windows of 20 back-to-back launches",
                      "traffic": traffic},
+        "step_path": step_path,
+        "plain_score_kernel_us": plain_score_ms * 1000.0,
         "three_calls_us_per_step": three_us if ok else None,
+        "three_calls_flag_us_per_step": three_flag_us if ok else None,
         "one_launch_step": one_launch if ok else None,
         "step_error_word": plan_error,
         "graph_replay": {"us_per_step": graph_us if ok else None,

@@ -342,10 +342,28 @@ int lsa_indexed_attention_noalloc(const lsa_attn_desc* desc, void* stream);
  *     lsa_indexed_attention
  * on the same arguments: out_idx (and q_idx, out_score) bit-identical,
  * out / lse within the attention's own rounding. By default the call runs
- * those three calls in sequence, except that the matrix-core decode
- * attention merges its splits within its own launch (each row's splits on
- * one XCD, the last to finish merging them; the control words at the
- * workspace head make that possible), with the same results bit for bit.
+ * those three calls in sequence with two changes that keep the results bit
+ * for bit:
+ *   - where the shape allows it (a bf16, fp8 or fp32 projected-key cache of
+ *     4, 8 or 16 sixteen-byte pieces per key, B < T, a sample rank k, below,
+ *     of at most half the sample and 64 k <= 6553), the scoring launch also
+ *     does the select's collect, so no collect launch runs: each chunk of a
+ *     row first scores its share of a sample of the row (one key in each
+ *     group of 64 slots, at an offset hashed from the group and the row);
+ *     after its stream it reads the whole row's sample, takes as threshold
+ *     the 16-bit key prefix of the sample's k-th largest key,
+ *     k = ceil(mu + 3.5 sqrt(mu) + 6) with mu = (samples) B / T, and lists
+ *     its keys at or above the threshold; no hint is computed. The select then
+ *     refines the lists, or, where they hold fewer than B keys or more than
+ *     its list path takes (or a chunk found the sample incomplete), selects from
+ *     the scores, which are written in full as before (the sample decides
+ *     speed, never the result). lsa_step_path tells which path a shape takes;
+ *   - the matrix-core decode attention merges its splits within its own
+ *     launch (each row's splits on one XCD, the last to finish merging
+ *     them).
+ * The control words at the workspace head make both possible. With flags =
+ * LSA_STEP_THREE_CALLS the call runs the three calls exactly as listed,
+ * with the select's own collect launch.
  * With flags = LSA_STEP_ONE_LAUNCH, shapes
  * with a bf16 or fp8 projected-key cache of 64 or 128 bytes per key, head
  * dim 128, 1, 2, 4 or 8 query heads per KV head, B a multiple of 32 that
@@ -395,7 +413,7 @@ typedef struct lsa_step_desc {
   int64_t kv_stride_tok;
   int64_t kv_stride_head;
   float scale;               /* <= 0: 1/sqrt(d) */
-  int32_t flags;             /* 0, or LSA_STEP_ONE_LAUNCH */
+  int32_t flags;             /* 0, LSA_STEP_ONE_LAUNCH or LSA_STEP_THREE_CALLS */
   float* q_idx;              /* optional out: fp32 [N,Hkv,r] */
   int32_t* out_idx;          /* [N,Hkv,B] ascending positions, -1 padded */
   float* out_score;          /* optional out: fp32 [N,Hkv,B] */
@@ -407,13 +425,41 @@ typedef struct lsa_step_desc {
  * single persistent launch) where the shape allows it; without the flag the
  * step always runs the three calls. */
 #define LSA_STEP_ONE_LAUNCH 1
+/* flags: run the three calls exactly as listed above, with the select's own
+ * collect launch, instead of the default path's listing scoring launch. */
+#define LSA_STEP_THREE_CALLS 2
 
 int lsa_decode_step(const lsa_step_desc* desc, void* workspace, size_t workspace_bytes, void* stream);
 size_t lsa_step_workspace_bytes(const lsa_step_desc* desc);
+
+/* The launches of lsa_decode_step's default path one group at a time:
+ * `parts` is a nonzero OR of the flags below, and the call issues the named
+ * parts, in order, exactly as lsa_decode_step issues them (the same
+ * descriptor, flags and workspace). Calling SCORE, SELECT and ATTEND in
+ * that order on one stream equals one lsa_decode_step call, bit for bit. A
+ * caller may put its own work between the parts, or time one part alone
+ * (a part may be repeated: each call of SCORE leaves the workspace's control
+ * words zero again). Reads and writes: SCORE the scores, q_idx, lists and
+ * samples in the workspace; SELECT those, writing out_idx / out_score;
+ * ATTEND out_idx, writing out / lse. Returns LSA_ERR_UNSUPPORTED for a
+ * descriptor that runs as the one persistent launch (it has no parts), and
+ * LSA_ERR_INVALID_ARG for parts outside 1..7. */
+#define LSA_STEP_PART_SCORE 1    /* scoring prep and scores (with the select's lists where listed) */
+#define LSA_STEP_PART_SELECT 2   /* exact top-B (the collect and the row select, or the row select) */
+#define LSA_STEP_PART_ATTEND 4   /* indexed attention, splits merged in the launch */
+#define LSA_STEP_PART_ALL 7
+int lsa_decode_step_part(const lsa_step_desc* desc, int parts, void* workspace, size_t workspace_bytes,
+                         void* stream);
 /* 1 when the descriptor (its shape and flags) runs as the one persistent
  * launch, 0 when it runs the three calls in sequence, -1 when the
  * descriptor is invalid. */
 int lsa_step_is_fused(const lsa_step_desc* desc);
+/* The path a descriptor (its shape and flags) runs: LSA_STEP_PATH_*, or -1
+ * when the descriptor is invalid. */
+#define LSA_STEP_PATH_THREE_CALLS 0
+#define LSA_STEP_PATH_LISTED 1
+#define LSA_STEP_PATH_ONE_LAUNCH 2
+int lsa_step_path(const lsa_step_desc* desc);
 
 /* ------------------------------------------------------------------------ */
 /* Setup calls                                                              */

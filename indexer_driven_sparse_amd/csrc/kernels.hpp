@@ -38,6 +38,42 @@ int score_hint_count(int n_out, int k_dt);   // hint entries per row
 int score_hint_k(int k_dt);                 // keys each hint vouches for
 hipError_t launch_score_decode(const ScoreDecodeArgs& a, int rows, int k_dt, hipStream_t s);
 
+// Decode scoring that also lists each chunk's candidates for the row
+// select (the decode step's collect, done in the scoring launch). Every
+// chunk first scores a sample of its row -- slot 64*i + j(i) for each
+// 64-slot group i, j(i) in [0, 64) a fixed hash of i and the row -- and
+// writes each sample key's 16-bit prefix, marked, to the row's sample
+// entries. After its stream every chunk reads all of the row's entries and
+// takes as threshold t_lo the 16-bit prefix (as p << 16) of the k_rank-th
+// largest; it lists its slots whose keys reach t_lo, in slot order, as
+// (score bits, slot) pairs, with {count, max key, t_lo, 0} in its meta
+// word: what the row select's list path reads. A chunk that finds an
+// entry not yet written lists nothing and writes count = no_list (more than
+// the select takes), sending the row to the select's path over the scores,
+// which the select then recomputes (SelectArgs::rs_*): the kernel writes
+// no scores, only q_idx (q_idx_out, which it needs). No chunk waits for
+// another. samples: zero before the first launch; ctrl: per
+// row one zeroed word at ctrl + row * ctrl_stride (the count of finished
+// chunks). The row's last chunk out zeroes both again.
+struct ScoreEmitArgs {
+  uint32_t* samples;                 // [rows, s_ld] sample keys
+  int64_t s_ld;
+  int k_rank;
+  int wpr;                           // chunks per row
+  uint32_t* ctrl;
+  int64_t ctrl_stride;
+  int2* lists;                       // [rows, wpr, list_stride]
+  int list_stride;
+  int4* meta;                        // [rows, wpr]
+  int no_list;
+};
+// Whether a decode step of this shape can use launch_score_emit, and the
+// sample rank it takes (0: not supported).
+int score_emit_rank(int n_out, int rows, int B, int r, int k_dt, int seg_cap, int max_segs, int max_listed);
+int score_emit_samples(int n_out);   // sample keys per row (s_ld is at least this)
+hipError_t launch_score_emit(const ScoreDecodeArgs& a, const ScoreEmitArgs& e, int rows, int k_dt,
+                             hipStream_t s);
+
 struct ScorePrefillArgs {
   const void* q_idx;                 // [L, Hkv, r] (contiguous rows of r)
   const void* k_idx;
@@ -98,6 +134,14 @@ struct SelectArgs {
   int2* seg_list;
   int4* seg_meta;
   int nseg;
+  // Lists from the listing scoring launch, which writes no scores: where
+  // the lists do not settle a row, the row's scores are first recomputed
+  // into `scores` with the scoring kernels' arithmetic (rs_k_idx set; 4, 8
+  // or 16 sixteen-byte pieces per key)
+  const void* rs_k_idx;
+  int64_t rs_ks_seq, rs_ks_head, rs_ks_tok;   // elements
+  const float* rs_q_idx;                      // [rows, rs_r]
+  int rs_r, rs_dt, rs_Hkv;
 };
 constexpr int kSelectLdsMaxSlots = 262144;
 // Workspace of a select: bitmaps of rows longer than kSelectLdsMaxSlots,
@@ -109,6 +153,13 @@ int select_segments(int n, int B, bool hint_usable);
 // sets nseg; needs n, B and the hint fields set.
 void select_bind_workspace(SelectArgs& a, int rows, void* ws);
 hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s);
+// The row select alone over lists already collected (seg_list / seg_meta /
+// nseg set, kSeg entries per segment of seg_list): what launch_select runs
+// after its own collect.
+hipError_t launch_select_lists(const SelectArgs& a, int rows, hipStream_t s);
+int select_list_stride();            // entries per segment of seg_list
+int select_list_max();               // most listed entries the list path takes
+int select_list_max_segments();      // most segments per row the list path takes
 
 // ----- fused decode step (scoring, selection and attention in one launch) -----
 // Control words at the head of the step workspace: [8] the count of finished
@@ -139,6 +190,8 @@ struct StepArgs {
   int nxcc;                          // the device's XCDs (1..8): row r runs on XCD r % nxcc
 };
 int step_ctrl_words(int rows);
+int step_ctrl_row0();                 // first per-row control word
+int step_ctrl_per_row();              // control words per row
 int step_chunk_slots();
 int step_meta_stride();              // int4 per part of meta
 int step_partial_stride(int G);      // floats per part of partial

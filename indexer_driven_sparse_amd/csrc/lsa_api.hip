@@ -319,7 +319,11 @@ struct StepPlan {
   lsa_select_desc select;
   lsa_attn_desc attn;
   bool fused;
+  bool listed;                 // the scoring launch lists the select's candidates
   int rows, wpr;
+  int list_rank, list_chunk, list_wpr;
+  int64_t s_ld;
+  size_t off_samples, off_lmeta, off_lists2, off_qidx;
   size_t off_scores, off_hint, off_sel, off_attn;           // three calls
   size_t off_lists, off_meta, off_partial;                  // fused
   size_t total;
@@ -329,7 +333,7 @@ struct StepPlan {
 int plan_step(const lsa_step_desc* d, StepPlan* p) {
   if (!d || d->struct_size != sizeof(lsa_step_desc)) return LSA_ERR_INVALID_ARG;
   if (d->n_seq < 1 || d->n_kv_heads < 1 || d->n_keys < 1 || d->topk < 1) return LSA_ERR_INVALID_ARG;
-  if (d->flags & ~LSA_STEP_ONE_LAUNCH) return LSA_ERR_INVALID_ARG;
+  if (d->flags & ~(LSA_STEP_ONE_LAUNCH | LSA_STEP_THREE_CALLS)) return LSA_ERR_INVALID_ARG;
   const int64_t rows = (int64_t)d->n_seq * d->n_kv_heads;
   if (rows > 65535) return LSA_ERR_UNSUPPORTED;
   const int64_t ld = ((int64_t)d->n_keys + 31) / 32 * 32;   // rows of whole 128-byte lines
@@ -432,6 +436,26 @@ int plan_step(const lsa_step_desc* d, StepPlan* p) {
     p->off_partial = p->off_meta + align256(parts * lsa::step_meta_stride() * sizeof(int4));
     const size_t fused_total = p->off_partial + parts * lsa::step_partial_stride(G) * sizeof(float);
     p->total = std::max(p->total, fused_total);
+  }
+  // default path: the scoring launch also lists each chunk's candidates,
+  // and the select runs over those lists (no separate collect launch)
+  p->listed = false;
+  if (!p->fused && !(d->flags & LSA_STEP_THREE_CALLS)) {
+    const int k = lsa::score_emit_rank(d->n_keys, (int)rows, d->topk, d->rank, d->k_idx_dtype,
+                                       lsa::select_list_stride(), lsa::select_list_max_segments(),
+                                       lsa::select_list_max());
+    if (k > 0) {
+      p->listed = true;
+      p->list_rank = k;
+      p->list_chunk = lsa::score_chunk_slots(d->n_keys, (int)rows, d->k_idx_dtype);
+      p->list_wpr = (d->n_keys + p->list_chunk - 1) / p->list_chunk;
+      p->s_ld = ((int64_t)lsa::score_emit_samples(d->n_keys) + 63) / 64 * 64;
+      p->off_samples = align256(p->total);
+      p->off_lmeta = p->off_samples + align256((size_t)rows * p->s_ld * sizeof(uint32_t));
+      p->off_lists2 = p->off_lmeta + align256((size_t)rows * p->list_wpr * sizeof(int4));
+      p->off_qidx = p->off_lists2 + align256((size_t)rows * p->list_wpr * lsa::select_list_stride() * sizeof(int2));
+      p->total = p->off_qidx + (size_t)rows * d->rank * sizeof(float);
+    }
   }
   return LSA_OK;
 }
@@ -671,6 +695,85 @@ int lsa_indexed_attention_noalloc(const lsa_attn_desc* d, void* stream) {
   return run_attention(d, ws, stream);
 }
 
+namespace {
+
+// The default path's launches, those named in `parts`, in order.
+int run_step_parts(const lsa_step_desc* d, StepPlan& p, char* b, hipStream_t s, int parts) {
+  void* stream = (void*)s;
+  if (p.listed) {
+    // q_idx: the caller's buffer, or the workspace's (the select's fallback reads it)
+    float* q_idx = d->q_idx ? d->q_idx : (float*)(b + p.off_qidx);
+    lsa::ScoreDecodeArgs sc{};
+    sc.k_idx = d->k_idx;
+    sc.ks_seq = d->k_stride_seq;
+    sc.ks_head = d->k_stride_head;
+    sc.ks_tok = d->k_stride_tok;
+    sc.Hkv = d->n_kv_heads;
+    sc.T = d->n_keys;
+    sc.r = d->rank;
+    sc.q = d->q;
+    sc.q_idx_out = q_idx;
+    sc.q_bf16 = d->q_dtype == LSA_BF16;
+    sc.Hq = d->n_q_heads;
+    sc.d = d->head_dim;
+    sc.w_per_head = d->w_per_head;
+    sc.w = d->w;
+    sc.cand_block = 1;
+    sc.n_out = d->n_keys;
+    sc.scores = nullptr;   // the lists carry the scores the select needs
+    sc.scores_ld = p.score.scores_ld;
+    sc.chunk = p.list_chunk;
+    lsa::ScoreEmitArgs e{};
+    e.samples = (uint32_t*)(b + p.off_samples);
+    e.s_ld = p.s_ld;
+    e.k_rank = p.list_rank;
+    e.wpr = p.list_wpr;
+    e.ctrl = (uint32_t*)b + lsa::step_ctrl_row0();   // one word per row: finished chunks
+    e.ctrl_stride = lsa::step_ctrl_per_row();
+    e.lists = (int2*)(b + p.off_lists2);
+    e.list_stride = lsa::select_list_stride();
+    e.meta = (int4*)(b + p.off_lmeta);
+    e.no_list = lsa::select_list_max() + 1;
+    if (parts & LSA_STEP_PART_SCORE) {
+      const hipError_t err = lsa::launch_score_emit(sc, e, p.rows, d->k_idx_dtype, s);
+      if (err != hipSuccess) return hip_fail(err);
+    }
+    lsa::SelectArgs a{};
+    a.scores = p.score.scores;
+    a.scores_ld = p.score.scores_ld;
+    a.n = d->n_keys;
+    a.B = d->topk;
+    a.cand_block = 1;
+    a.out_idx = d->out_idx;
+    a.out_score = d->out_score;
+    // bitmaps of rows too long for LDS lead the select workspace
+    a.gbitmap = d->n_keys > lsa::kSelectLdsMaxSlots ? (uint32_t*)(b + p.off_sel) : nullptr;
+    a.seg_list = e.lists;
+    a.seg_meta = e.meta;
+    a.nseg = p.list_wpr;
+    a.rs_k_idx = d->k_idx;   // a row the lists do not settle is rescored
+    a.rs_ks_seq = d->k_stride_seq;
+    a.rs_ks_head = d->k_stride_head;
+    a.rs_ks_tok = d->k_stride_tok;
+    a.rs_q_idx = q_idx;
+    a.rs_r = d->rank;
+    a.rs_dt = d->k_idx_dtype;
+    a.rs_Hkv = d->n_kv_heads;
+    if (parts & LSA_STEP_PART_SELECT) {
+      const hipError_t err = lsa::launch_select_lists(a, p.rows, s);
+      if (err != hipSuccess) return hip_fail(err);
+    }
+  } else {
+    if (parts & LSA_STEP_PART_SCORE) LSA_TRY(lsa_index_score(&p.score, nullptr, 0, stream));
+    if (parts & LSA_STEP_PART_SELECT) LSA_TRY(lsa_topk_select(&p.select, b + p.off_sel, p.sel_bytes, stream));
+  }
+  if (parts & LSA_STEP_PART_ATTEND)
+    return run_attention(&p.attn, p.attn_bytes ? b + p.off_attn : nullptr, stream, (uint32_t*)b, device_xccs());
+  return LSA_OK;
+}
+
+}  // namespace
+
 int lsa_decode_step(const lsa_step_desc* d, void* ws, size_t ws_bytes, void* stream) {
   StepPlan p;
   LSA_TRY(plan_step(d, &p));
@@ -732,9 +835,19 @@ int lsa_decode_step(const lsa_step_desc* d, void* ws, size_t ws_bytes, void* str
     hipError_t e = lsa::launch_decode_step(a, d->k_idx_dtype, s);
     return e == hipSuccess ? LSA_OK : hip_fail(e);
   }
-  LSA_TRY(lsa_index_score(&p.score, nullptr, 0, stream));
-  LSA_TRY(lsa_topk_select(&p.select, b + p.off_sel, p.sel_bytes, stream));
-  return run_attention(&p.attn, p.attn_bytes ? b + p.off_attn : nullptr, stream, (uint32_t*)b, device_xccs());
+  return run_step_parts(d, p, b, s, LSA_STEP_PART_ALL);
+}
+
+
+int lsa_decode_step_part(const lsa_step_desc* d, int parts, void* ws, size_t ws_bytes, void* stream) {
+  if (parts < 1 || parts > LSA_STEP_PART_ALL) return LSA_ERR_INVALID_ARG;
+  StepPlan p;
+  LSA_TRY(plan_step(d, &p));
+  if (p.fused) return LSA_ERR_UNSUPPORTED;   // the one launch has no parts
+  LSA_TRY(check_ws(ws, ws_bytes, p.total));
+  LSA_TRY(check_device());
+  bind_step(&p, ws);
+  return run_step_parts(d, p, (char*)ws, (hipStream_t)stream, parts);
 }
 
 size_t lsa_step_workspace_bytes(const lsa_step_desc* d) {
@@ -745,6 +858,12 @@ size_t lsa_step_workspace_bytes(const lsa_step_desc* d) {
 int lsa_step_is_fused(const lsa_step_desc* d) {
   StepPlan p;
   return plan_step(d, &p) == LSA_OK ? (p.fused ? 1 : 0) : -1;
+}
+
+int lsa_step_path(const lsa_step_desc* d) {
+  StepPlan p;
+  if (plan_step(d, &p) != LSA_OK) return -1;
+  return p.fused ? LSA_STEP_PATH_ONE_LAUNCH : p.listed ? LSA_STEP_PATH_LISTED : LSA_STEP_PATH_THREE_CALLS;
 }
 
 size_t lsa_attention_workspace_bytes(const lsa_attn_desc* d) {

@@ -147,10 +147,21 @@ __device__ __forceinline__ void store_u32x4(uint32_t* p, uint4 v) {
 // Scattered score stores in the middle of the cache stream cost the stream
 // far more than their share of the bytes on MI355X; one burst per chunk
 // costs little.
-template <int DT, int LPK, bool CAND, bool PREP = true, int STEPS = 0, bool COHERENT = false>
+// after_prep(qv), if given, runs on every thread once the row's q_idx is
+// ready (qv: this lane's E channels of it) and before the chunk's stream
+// goes on; before_burst(), if given, runs on every thread after the
+// chunk's last cache load has been used and before the staged scores are
+// written (STEPS == 0 with stage). Either may contain barriers.
+struct NoHook {
+  template <class... T>
+  __device__ __forceinline__ void operator()(const T&...) const {}
+};
+template <int DT, int LPK, bool CAND, bool PREP = true, int STEPS = 0, bool COHERENT = false,
+          class Hook = NoHook, class Hook2 = NoHook>
 __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, int64_t c0, int64_t c1,
                                             ScoreShared& sh, bool do_prep = true, float* keep = nullptr,
-                                            float* stage = nullptr, uint32_t* hstage = nullptr) {
+                                            float* stage = nullptr, uint32_t* hstage = nullptr,
+                                            Hook after_prep = Hook{}, Hook2 before_burst = Hook2{}) {
   constexpr int ESZ = DT == 2 ? 1 : DT == 1 ? 2 : 4;
   constexpr int kGroupsInFlight = groups_in_flight(DT);
   constexpr int kHintK = hint_k(DT);
@@ -168,7 +179,7 @@ __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, i
   const char* kbase =
       (const char*)a.k_idx + ((int64_t)n * a.ks_seq + (int64_t)g * a.ks_head) * ESZ + l * 16;
   const int64_t tok_bytes = a.ks_tok * ESZ;
-  float* srow = a.scores + (int64_t)row * a.scores_ld;
+  float* srow = a.scores != nullptr ? a.scores + (int64_t)row * a.scores_ld : nullptr;
   const int32_t* crow = CAND ? a.cand + (int64_t)row * a.cand_ld : nullptr;
 
   // one wave's loads of one step: kGroupsInFlight groups of 64 slots
@@ -273,6 +284,7 @@ __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, i
   float qv[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) qv[e] = s_q[l * E + e];
+  after_prep(qv);
 
   // ---- stream this workgroup's chunk ----
   auto one_step = [&](int64_t gb, int si) {
@@ -323,9 +335,10 @@ __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, i
   if constexpr (STEPS == 0) {
     for (int64_t gb = gfirst; gb < c1; gb += kStep) one_step(gb, 0);
     if (stage != nullptr) {
+      before_burst();
       // srow + c0 is 16-byte aligned (16-byte aligned rows, c0 a multiple of the step)
       __syncthreads();
-      const int n = (int)(c1 - c0), nq = n / 4;
+      const int n = a.scores != nullptr ? (int)(c1 - c0) : 0, nq = n / 4;   // no scores: none written
       float* dst = srow + c0;
       for (int k = tid; k < nq; k += kScoreThreads)
         store_u32x4<COHERENT>(reinterpret_cast<uint32_t*>(dst + 4 * k), *reinterpret_cast<const uint4*>(stage + 4 * k));

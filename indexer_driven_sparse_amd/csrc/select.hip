@@ -118,9 +118,10 @@ void select_bind_workspace(SelectArgs& a, int rows, void* ws) {
   }
 }
 
-hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
-  // allow the largest LDS footprint (SelShared + two bitmaps of the longest
-  // LDS-resident row); a function-local static runs this once, thread-safely
+namespace {
+// allow the largest LDS footprint (SelShared + two bitmaps of the longest
+// LDS-resident row); a function-local static runs this once, thread-safely
+hipError_t select_attributes() {
   static const hipError_t attr = [] {
     const int lds = (int)(sizeof(SelShared) + (size_t)2 * (kSelectLdsMaxSlots / 32) * sizeof(uint32_t));
     const void* fns[] = {(const void*)select_kernel<false, false, false>,
@@ -133,8 +134,32 @@ hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
     }
     return hipSuccess;
   }();
+  return attr;
+}
+}  // namespace
+
+hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
+  const hipError_t attr = select_attributes();
   if (attr != hipSuccess) return attr;
   return a.cand ? launch_select_t<true>(a, rows, s) : launch_select_t<false>(a, rows, s);
 }
+
+hipError_t launch_select_lists(const SelectArgs& a, int rows, hipStream_t s) {
+  if (a.nseg < 1 || a.nseg > kThreads || a.cand != nullptr || !a.seg_list || !a.seg_meta)
+    return hipErrorInvalidValue;
+  const hipError_t attr = select_attributes();
+  if (attr != hipSuccess) return attr;
+  const int nw = (a.n + 31) / 32;
+  const size_t lds = a.gbitmap ? sizeof(SelShared) : sizeof(SelShared) + (size_t)2 * nw * sizeof(uint32_t);
+  if (a.gbitmap)
+    hipLaunchKernelGGL((select_kernel<false, true, true>), dim3(rows), dim3(kThreads), lds, s, a);
+  else
+    hipLaunchKernelGGL((select_kernel<false, false, true>), dim3(rows), dim3(kThreads), lds, s, a);
+  return hipGetLastError();
+}
+
+int select_list_stride() { return kSeg; }
+int select_list_max() { return kCap; }
+int select_list_max_segments() { return kThreads; }
 
 }  // namespace lsa

@@ -5,6 +5,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "score_body.hpp"
 
 namespace lsa {
 namespace sel {
@@ -196,6 +197,57 @@ constexpr int kSegWaves = kSegThreads / 64;
 constexpr int kSegUnroll = 8;
 constexpr int kSeg = kSegThreads * 4 * kSegUnroll;   // 8192 slots
 constexpr int kSegUnits = kSegUnroll * kSegWaves;    // (loop step, wave) units, in slot order
+
+// The scores of slots [0, nv) of a row recomputed into srow with the
+// scoring kernels' arithmetic: each 16-byte piece of the key dotted with
+// its q_idx channels (scoring::dot16), the P pieces summed pairwise in the
+// tree the scoring kernels' lane sums form (((p0+p1)+(p2+p3))+...), so
+// every score is bit-identical to the scoring launch's. The whole
+// workgroup calls it; the scores are complete and visible to the
+// workgroup on return.
+template <int DT, int P>
+__device__ void rescore_row_t(const SelectArgs& a, int row, float* srow, int64_t nv, float* sq) {
+  constexpr int ESZ = DT == 2 ? 1 : DT == 1 ? 2 : 4;
+  constexpr int E = 16 / ESZ;
+  const int n = row / a.rs_Hkv, g = row % a.rs_Hkv;
+  const char* base = (const char*)a.rs_k_idx + ((int64_t)n * a.rs_ks_seq + (int64_t)g * a.rs_ks_head) * ESZ;
+  for (int64_t t = threadIdx.x; t < nv; t += kThreads) {
+    const char* kr = base + t * a.rs_ks_tok * ESZ;
+    float p[P];
+#pragma unroll
+    for (int l = 0; l < P; ++l) p[l] = scoring::dot16<DT>(*(const uint4*)(kr + 16 * l), sq + l * E);
+#pragma unroll
+    for (int w = P; w > 1; w >>= 1)
+#pragma unroll
+      for (int i = 0; i < w / 2; ++i) p[i] = p[2 * i] + p[2 * i + 1];
+    srow[t] = p[0];
+  }
+}
+
+__device__ __noinline__ void rescore_row(const SelectArgs& a, int row, float* srow, int64_t nv) {
+  __shared__ float sq[scoring::kMaxR];
+  for (int c = threadIdx.x; c < a.rs_r; c += kThreads) sq[c] = a.rs_q_idx[(int64_t)row * a.rs_r + c];
+  __syncthreads();
+  const int esz = a.rs_dt == 2 ? 1 : a.rs_dt == 1 ? 2 : 4;
+  const int P = a.rs_r * esz / 16;
+  if (a.rs_dt == 2) {
+    if (P == 4) rescore_row_t<2, 4>(a, row, srow, nv, sq);
+    else if (P == 8) rescore_row_t<2, 8>(a, row, srow, nv, sq);
+    else if (P == 16) rescore_row_t<2, 16>(a, row, srow, nv, sq);
+  } else if (a.rs_dt == 1) {
+    if (P == 4) rescore_row_t<1, 4>(a, row, srow, nv, sq);
+    else if (P == 8) rescore_row_t<1, 8>(a, row, srow, nv, sq);
+    else if (P == 16) rescore_row_t<1, 16>(a, row, srow, nv, sq);
+  } else {
+    if (P == 4) rescore_row_t<0, 4>(a, row, srow, nv, sq);
+    else if (P == 8) rescore_row_t<0, 8>(a, row, srow, nv, sq);
+    else if (P == 16) rescore_row_t<0, 16>(a, row, srow, nv, sq);
+  }
+  // every store is complete before any thread of the workgroup reads the
+  // row (the lines were never read in this launch, so no L1 copy is stale)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
 
 // One row of the selection, run by a whole kThreads-thread workgroup.
 // `row` indexes the outputs (out_idx, out_score, out_count), the workspace
@@ -525,12 +577,15 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int row, const f
     const int4* meta = a.seg_meta + (int64_t)row * a.nseg;
     int cnt = 0;
     uint32_t km = 0u;
+    const uint32_t t_lo = (uint32_t)meta[0].z;
+    bool other_t = false;   // a segment listed against another threshold
     if (tid < a.nseg) {
       const int4 mm = meta[tid];
       cnt = mm.x;
       km = (uint32_t)mm.y;
+      other_t = (uint32_t)mm.z != t_lo;
     }
-    const uint32_t t_lo = (uint32_t)meta[0].z;
+    const bool same_t = !__syncthreads_or(other_t);
     int total;
     const int off = block_exclusive_scan<kThreads>(cnt, sh.scan, &total);
     if (tid < a.nseg) seg_off[tid] = off;
@@ -539,7 +594,7 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int row, const f
     for (int o = 32; o >= 1; o >>= 1) km = max(km, (uint32_t)__shfl_xor((int)km, o, 64));
     if (lane == 0) atomicMax(&sh.kmax, km);
     __syncthreads();
-    if (total >= B && total <= kCap) {
+    if (same_t && total >= B && total <= kCap) {
       // Every key >= t_lo of the row is listed and at least B are, so the
       // B-th key is among them. Thread t holds entries 8t .. 8t+7 (list
       // order is slot order) in registers.
@@ -579,7 +634,9 @@ __device__ __forceinline__ void select_row(const SelectArgs& a, int row, const f
       select_in_registers<CAND, kPer>(a, sh, row, crow, key, val, slot, i0, total, t_lo, sh.kmax);
       return;
     }
-    // the lists do not settle it: general path over the row
+    // the lists do not settle it: general path over the row (its scores
+    // recomputed first when the listing launch wrote none)
+    if (a.rs_k_idx != nullptr) rescore_row(a, row, const_cast<float*>(srow), nv);
     for (int i = tid; i < nw; i += kThreads) {
       bm_sel[i] = 0u;
       bm_tie[i] = 0u;

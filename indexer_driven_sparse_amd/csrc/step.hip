@@ -868,6 +868,8 @@ hipError_t launch_g(const StepArgs& a, hipStream_t s) {
 }  // namespace
 
 int step_ctrl_words(int rows) { return kCtlRow0 + kCtlPerRow * rows; }
+int step_ctrl_row0() { return kCtlRow0; }
+int step_ctrl_per_row() { return kCtlPerRow; }
 int step_chunk_slots() { return kChunk; }
 
 bool decode_step_supported(int rows, int n, int B, int r, int k_dt, int kv_dt, int G, int d, int hint_count,

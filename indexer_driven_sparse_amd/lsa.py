@@ -120,6 +120,8 @@ _SIGS = {
     "lsa_decode_step": (_I32, [_P, _P, _c.c_size_t, _P]),
     "lsa_step_workspace_bytes": (_c.c_size_t, [_P]),
     "lsa_step_is_fused": (_I32, [_P]),
+    "lsa_step_path": (_I32, [_P]),
+    "lsa_decode_step_part": (_I32, [_P, _I32, _P, _c.c_size_t, _P]),
     "lsa_status_str": (_c.c_char_p, [_I32]),
     "lsa_last_hip_error": (_I32, []),
     "lsa_abi_version": (_I32, []),
@@ -565,9 +567,11 @@ def prefill_score_workspace_bytes_for(L: int, Hkv: int, r: int, B: int,
 
 
 STEP_ONE_LAUNCH = 1   # lsa_step_desc.flags: the one persistent launch where the shape allows
+STEP_THREE_CALLS = 2  # lsa_step_desc.flags: the three calls, with the select's own collect launch
 
 
-def _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch=False):
+def _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch=False,
+               three_calls=False):
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be contiguous [N,Hq,d]")
     N, Hq, hd = q.shape
@@ -599,21 +603,23 @@ def _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, on
     d.k, d.v, d.kv_dtype = _ptr(k), _ptr(v), _dt(k)
     d.kv_stride_seq, d.kv_stride_tok, d.kv_stride_head = k.stride(0), k.stride(1), k.stride(2)
     d.scale = scale
-    d.flags = STEP_ONE_LAUNCH if one_launch else 0
+    d.flags = (STEP_ONE_LAUNCH if one_launch else 0) | (STEP_THREE_CALLS if three_calls else 0)
     d.q_idx, d.out_idx, d.out_score, d.out, d.lse = (_ptr(q_idx), _ptr(out_idx), _ptr(out_score),
                                                      _ptr(out), _ptr(lse))
     return d
 
 
 def lsa_decode_step(q, w, k_idx, k, v, out_idx, out, *, lse=None, q_idx=None, out_score=None,
-                    scale: float = 0.0, workspace=None, stream=None, one_launch: bool = False) -> None:
+                    scale: float = 0.0, workspace=None, stream=None, one_launch: bool = False,
+                    three_calls: bool = False) -> None:
     """One whole flat decode step (scoring prep, scores, exact top-B, indexed
     attention): q [N,Hq,d], w [d,r] fp32, k_idx [N,Hkv,T,r], k/v [N,T,Hkv,d];
     out_idx int32 [N,Hkv,B], out fp32 [N,Hq,d]. workspace: uint8 of at least
     lsa_step_workspace_bytes, all zero before its first use (the call leaves
     its control words zero); allocated zeroed here when not given.
-    one_launch: the single persistent launch where the shape allows it."""
-    d = _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch)
+    one_launch: the single persistent launch where the shape allows it;
+    three_calls: the three calls with the select's own collect launch."""
+    d = _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch, three_calls)
     lib = _lib()
     need = lib.lsa_step_workspace_bytes(_c.byref(d))
     if need == 0:
@@ -624,17 +630,50 @@ def lsa_decode_step(q, w, k_idx, k, v, out_idx, out, *, lse=None, q_idx=None, ou
     _check("lsa_decode_step", lib.lsa_decode_step(_c.byref(d), _ptr(workspace), wsb, _stream(stream)))
 
 
+STEP_PART_SCORE, STEP_PART_SELECT, STEP_PART_ATTEND, STEP_PART_ALL = 1, 2, 4, 7
+
+
+def lsa_decode_step_part(parts: int, q, w, k_idx, k, v, out_idx, out, *, workspace, lse=None,
+                         q_idx=None, out_score=None, scale: float = 0.0, stream=None,
+                         three_calls: bool = False) -> None:
+    """The default decode step's launches named in `parts` (an OR of
+    STEP_PART_SCORE, STEP_PART_SELECT, STEP_PART_ATTEND), issued as
+    lsa_decode_step issues them; workspace as for lsa_decode_step."""
+    d = _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, False, three_calls)
+    wsb = workspace.numel() * workspace.element_size()
+    _check("lsa_decode_step_part",
+           _lib().lsa_decode_step_part(_c.byref(d), int(parts), _ptr(workspace), wsb, _stream(stream)))
+
+
 def lsa_step_workspace_bytes(q, w, k_idx, k, v, out_idx, out, *, lse=None, q_idx=None,
-                             out_score=None, scale: float = 0.0, one_launch: bool = False) -> int:
-    d = _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch)
+                             out_score=None, scale: float = 0.0, one_launch: bool = False,
+                             three_calls: bool = False) -> int:
+    d = _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch, three_calls)
     return int(_lib().lsa_step_workspace_bytes(_c.byref(d)))
 
 
 def lsa_step_is_fused(q, w, k_idx, k, v, out_idx, out, **kw) -> bool:
     """Whether the step (shape and one_launch flag) runs as one persistent launch."""
     d = _step_desc(q, w, k_idx, k, v, out_idx, out, kw.get("lse"), kw.get("q_idx"),
-                   kw.get("out_score"), kw.get("scale", 0.0), kw.get("one_launch", False))
+                   kw.get("out_score"), kw.get("scale", 0.0), kw.get("one_launch", False),
+                   kw.get("three_calls", False))
     return int(_lib().lsa_step_is_fused(_c.byref(d))) == 1
+
+
+STEP_PATHS = {0: "three_calls", 1: "listed", 2: "one_launch"}
+
+
+def lsa_step_path(q, w, k_idx, k, v, out_idx, out, **kw) -> str:
+    """Which path the step takes for this shape and these flags:
+    'three_calls', 'listed' (the scoring launch lists the select's
+    candidates) or 'one_launch'."""
+    d = _step_desc(q, w, k_idx, k, v, out_idx, out, kw.get("lse"), kw.get("q_idx"),
+                   kw.get("out_score"), kw.get("scale", 0.0), kw.get("one_launch", False),
+                   kw.get("three_calls", False))
+    code = int(_lib().lsa_step_path(_c.byref(d)))
+    if code < 0:
+        raise ValueError("lsa_step_path: invalid step descriptor")
+    return STEP_PATHS[code]
 
 
 STEP_ERROR_WORD = 9    # 32-bit word index of the step workspace's error word

@@ -43,11 +43,13 @@ class DecodePlan:
 
     def __init__(self, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int,
                  device="cuda", kv_dtype=torch.bfloat16, with_idx_scores: bool = False,
-                 kidx_dtype=None, fused: bool = True, one_launch: bool = False):
+                 kidx_dtype=None, fused: bool = True, one_launch: bool = False,
+                 three_calls: bool = False):
         self.N, self.Hq, self.Hkv, self.T, self.d, self.r, self.B = N, Hq, Hkv, T, d, r, B
         self.with_idx_scores = with_idx_scores
         self.fused = fused
         self.one_launch = one_launch
+        self.three_calls = three_calls
         self.step_ws = None
         f32 = dict(dtype=torch.float32, device=device)
         self.scores = torch.empty(N, Hkv, _ld4(T), **f32)[:, :, :T]
@@ -89,11 +91,22 @@ class DecodePlan:
         the single persistent launch where the shape allows it)."""
         if self.step_ws is None:
             need = lsa.lsa_step_workspace_bytes(q, w, k_idx, k, v, self.idx, self.out, lse=self.lse,
-                                                q_idx=self.q_idx, one_launch=self.one_launch)
+                                                q_idx=self.q_idx, one_launch=self.one_launch,
+                                                three_calls=self.three_calls)
             self.step_ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
         lsa.lsa_decode_step(q, w, k_idx, k, v, self.idx, self.out, lse=self.lse, q_idx=self.q_idx,
                             out_score=self.idx_scores if self.with_idx_scores else None,
-                            workspace=self.step_ws, stream=stream, one_launch=self.one_launch)
+                            workspace=self.step_ws, stream=stream, one_launch=self.one_launch,
+                            three_calls=self.three_calls)
+
+    def part(self, parts, q, w, k_idx, k, v, stream=None):
+        """Some of the launches of step() (lsa_decode_step_part: an OR of
+        lsa.STEP_PART_SCORE, _SELECT, _ATTEND), on this plan's workspace;
+        step() must have run once (it allocates the workspace)."""
+        lsa.lsa_decode_step_part(parts, q, w, k_idx, k, v, self.idx, self.out, workspace=self.step_ws,
+                                 lse=self.lse, q_idx=self.q_idx,
+                                 out_score=self.idx_scores if self.with_idx_scores else None,
+                                 stream=stream, three_calls=self.three_calls)
 
     def step_error(self) -> int:
         """The step workspace's error word (0 when every call was clean)."""

@@ -457,6 +457,65 @@ def test_step_plan_flags_and_one_launch_conditions():
     idx = torch.empty(N, Hkv, 1024, dtype=torch.int32)
     d_ = lsa._step_desc(q, w, kd, k, v, idx, out, None, None, None, 0.0, True)
     assert lib.lsa_step_workspace_bytes(ctypes.byref(d_)) > 0
-    d_.flags = 2
+    d_.flags = 4
     assert lib.lsa_step_workspace_bytes(ctypes.byref(d_)) == 0
     assert lib.lsa_step_is_fused(ctypes.byref(d_)) == -1
+    assert lib.lsa_step_path(ctypes.byref(d_)) == -1
+
+
+def test_step_plan_listed_path_conditions():
+    """lsa_decode_step's planner (host only): the default path lists the
+    select's candidates in the scoring launch where the sampled threshold
+    is useful (B well below T); LSA_STEP_THREE_CALLS, the one launch and
+    budgets near T take the other paths; the listing path's workspace
+    holds its samples, lists and metadata."""
+    N, Hq, Hkv, d, r = 1, 32, 8, 128, 64
+    bf = dict(dtype=torch.bfloat16)
+
+    def path(T, B, kd_dtype=torch.bfloat16, **kw):
+        q = torch.empty(N, Hq, d, **bf)
+        w = torch.empty(d, r, dtype=torch.float32)
+        kd = torch.empty(N, Hkv, T, r, dtype=kd_dtype)
+        k = torch.empty(N, T, Hkv, d, **bf)
+        out = torch.empty(N, Hq, d, dtype=torch.float32)
+        buf = torch.empty(N * Hkv * B + 64, dtype=torch.int32)
+        base = (-buf.data_ptr() // 4) % 32          # positions on a 128-byte line (the one launch needs it)
+        idx = buf[base:base + N * Hkv * B].view(N, Hkv, B)
+        return (lsa.lsa_step_path(q, w, kd, k, k, idx, out, **kw),
+                lsa.lsa_step_workspace_bytes(q, w, kd, k, k, idx, out, **kw))
+
+    p_list, ws_list = path(131072, 2048)
+    p_three, ws_three = path(131072, 2048, three_calls=True)
+    assert (p_list, p_three) == ("listed", "three_calls")
+    # samples (one key per 64 slots), metadata and 8-byte list entries of
+    # each row's 32 chunks on top of the three calls' workspace
+    assert ws_list >= ws_three + N * Hkv * 32 * 8192 * 8
+    assert path(131072, 2048, one_launch=True)[0] == "one_launch"
+    assert path(40000, 1024)[0] == "listed"
+    assert path(40000, 1024, kd_dtype=torch.float8_e4m3fn)[0] == "listed"
+    assert path(4096, 256, kd_dtype=torch.float32)[0] == "listed"
+    assert path(512, 512)[0] == "three_calls"              # B = T: nothing to select
+    assert path(8192, 4096)[0] == "three_calls"            # half the row: the sample cannot help
+    assert path(131072, 8192)[0] == "three_calls"          # more listed keys than the list path takes
+
+
+def test_step_parts_argument_checks():
+    """lsa_decode_step_part rejects parts outside 1..7 and the one-launch
+    path (which has no parts) before any HIP call."""
+    lib = lsa._lib()
+    N, Hq, Hkv, T, d, r, B = 1, 32, 8, 131072, 128, 64, 2048
+    bf = dict(dtype=torch.bfloat16)
+    q = torch.empty(N, Hq, d, **bf)
+    w = torch.empty(d, r, dtype=torch.float32)
+    kd = torch.empty(N, Hkv, T, r, **bf)
+    k = torch.empty(N, T, Hkv, d, **bf)
+    out = torch.empty(N, Hq, d, dtype=torch.float32)
+    buf = torch.empty(N * Hkv * B + 64, dtype=torch.int32)
+    base = (-buf.data_ptr() // 4) % 32
+    idx = buf[base:base + N * Hkv * B].view(N, Hkv, B)
+    ws = torch.empty(16, dtype=torch.uint8)
+    for parts in (0, 8, -1):
+        d_ = lsa._step_desc(q, w, kd, k, k, idx, out, None, None, None, 0.0)
+        assert lib.lsa_decode_step_part(ctypes.byref(d_), parts, ws.data_ptr(), 16, None) == -1   # LSA_ERR_INVALID_ARG
+    d_ = lsa._step_desc(q, w, kd, k, k, idx, out, None, None, None, 0.0, True)
+    assert lib.lsa_decode_step_part(ctypes.byref(d_), 1, ws.data_ptr(), 16, None) == -2   # LSA_ERR_UNSUPPORTED

@@ -710,7 +710,161 @@ def test_decode_step_equals_separate_calls(name, over):
     for name_ in ("idx", "q_idx", "idx_scores", "out", "lse"):
         a, b = getattr(one, name_), getattr(ref, name_)
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name_
-    assert int(one.step_ws[:4096].view(torch.int32).abs().sum().item()) == 0
+    _assert_step_ctrl_zero(one, N * Hkv)
+
+
+def _assert_step_ctrl_zero(plan, rows):
+    """The step workspace's control words (1024 launch-wide words, then 1024
+    per row) are all zero again after a call."""
+    ctl = plan.step_ws[:4 * (1024 + 1024 * rows)].view(torch.int32)
+    assert int(ctl.abs().sum().item()) == 0
+
+
+def _sample_slot(gi, row, n):
+    """Slot of the listing scoring launch's sample in 64-slot group gi of a
+    row: the offset hashed from the group and the row (the rule the step's
+    header states), clamped to the row."""
+    h = ((gi * 0x9E3779B1) & 0xFFFFFFFF) ^ ((row * 0x85EBCA77) & 0xFFFFFFFF)
+    return min(gi * 64 + (((h * 0xC2B2AE3D) & 0xFFFFFFFF) >> 26), n - 1)
+
+
+def _listed_vs_three_calls(case, kd, reps=2):
+    """lsa_decode_step's listing path against LSA_STEP_THREE_CALLS on the
+    same inputs: indices, per-entry scores and q_idx bit for bit, out and
+    lse bit for bit (the same attention launch); the control words left
+    zero after every call. Returns the listing plan."""
+    from indexer_driven_sparse_amd import pipeline
+    N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
+    Q, W, K, V = dev(case.Q), dev(case.W), dev(case.K), dev(case.V)
+    ref = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, with_idx_scores=True, kidx_dtype=kd.dtype,
+                              three_calls=True)
+    ref.run(Q, W, kd, K, V)
+    one = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, with_idx_scores=True, kidx_dtype=kd.dtype)
+    assert lsa.lsa_step_path(Q, W, kd, K, V, one.idx, one.out) == "listed"
+    assert lsa.lsa_step_path(Q, W, kd, K, V, one.idx, one.out, three_calls=True) == "three_calls"
+    for _ in range(reps):
+        one.run(Q, W, kd, K, V)
+        torch.cuda.synchronize()
+        _assert_step_ctrl_zero(one, N * Hkv)
+    for name_ in ("idx", "q_idx", "idx_scores", "out", "lse"):
+        a, b = getattr(one, name_), getattr(ref, name_)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), name_
+    return one
+
+
+@pytest.mark.parametrize("name,over", [
+    ("decode_t128k_b2048", {"N": 4}),                               # the headline shape
+    ("decode_t128k_b2048", {"N": 1, "T": 40961, "B": 1024}),        # a ragged last chunk and sample group
+    ("decode_t32k_hitters", {}),                                    # chunks of 512 slots
+    ("decode_t4k_fp32", {}),                                        # an fp32 cache, one chunk per row
+])
+def test_decode_step_listed_equals_three_calls(name, over):
+    """The default path's scoring launch lists the select's candidates (a
+    sampled threshold per row); the result equals the three calls bit for
+    bit."""
+    case = synth.workload(name, **over)
+    say("listed decode step vs three calls", name, over)
+    kd = torch.empty(case.N, case.Hkv, case.T, case.r, dtype=torch_dtype(case.dtype), device="cuda")
+    lsa.lsa_project_keys(dev(case.K), dev(case.W), kd)
+    _listed_vs_three_calls(case, kd)
+
+
+def test_decode_step_listed_fallbacks():
+    """The listing path where its lists cannot settle a row, so the select
+    takes the scores: (1) every key of a head equal (each row one big tie:
+    every key reaches the threshold, more than the list path takes), whose
+    selection is the lowest B positions; (2) keys planted at exactly the
+    sampled slots, so the sampled threshold lets fewer than B keys through;
+    (3) an fp8 cache. Each equals the three calls bit for bit, and (2) the
+    oracle."""
+    case = synth.workload("decode_t128k_b2048", N=1, T=40000, B=1024)
+    say("listed decode step, constant keys per head")
+    K = case.K.copy()
+    K[:, :, :, :] = K[:, :1, :, :]
+    tie = synth.workload("decode_t128k_b2048", N=1, T=40000, B=1024)
+    tie.K = K
+    kd = torch.empty(tie.N, tie.Hkv, tie.T, tie.r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_project_keys(dev(tie.K), dev(tie.W), kd)
+    gi = host(_listed_vs_three_calls(tie, kd).idx)
+    for g in range(tie.Hkv):
+        np.testing.assert_array_equal(gi[0, g], np.arange(tie.B))
+
+    say("listed decode step, keys planted at the sampled slots")
+    k_idx = oracle.project_keys(case.K, case.W, case.dtype)
+    q_idx = oracle.query_prep(case.Q, case.Hkv, case.W)
+    n_groups = (case.T + 63) // 64
+    assert n_groups < case.B          # the sample alone cannot reach B
+    for g in range(case.Hkv):
+        qd = q_idx[0, g] / np.linalg.norm(q_idx[0, g])
+        big = synth.to_bf16_bits((6.0 * qd).astype(np.float32))
+        for gi_ in range(n_groups):
+            k_idx[0, g, _sample_slot(gi_, g, case.T)] = big
+    kd = dev(k_idx)
+    one = _listed_vs_three_calls(case, kd)
+    rows = list(range(case.N * case.Hkv))
+    ref = oracle.decode_step(case.Q, case.W, k_idx, case.K, case.V, case.B)
+    R = case.N * case.Hkv
+    want = {"idx": ref["idx"].reshape(R, case.B), "scores": ref["scores"].reshape(R, case.T),
+            "out": ref["out"].reshape(R, case.G, case.d), "lse": ref["lse"].reshape(R, case.G)}
+    _compare_step(case, {"idx": host(one.idx), "out": host(one.out), "lse": host(one.lse)}, want, rows)
+
+    say("listed decode step, fp8 cache")
+    k8 = torch.empty(case.N, case.Hkv, case.T, case.r, dtype=torch.float8_e4m3fn, device="cuda")
+    lsa.lsa_project_keys(dev(case.K), dev(case.W), k8)
+    _listed_vs_three_calls(case, k8)
+
+
+@pytest.mark.parametrize("name,over,kdt", [
+    ("decode_t128k_b2048", {"N": 1, "T": 40000, "B": 1024}, torch.float8_e4m3fn),   # 4 pieces per key
+    ("decode_t4k_fp32", {}, torch.float32),                                          # 16 pieces per key
+    ("decode_t128k_b2048", {"N": 1, "T": 40000, "B": 1024, "r": 128}, torch.bfloat16),  # 16 pieces
+])
+def test_decode_step_listed_rescored_rows(name, over, kdt):
+    """Rows the listing path's lists cannot settle are rescored by the
+    select with the scoring arithmetic (the listing launch writes no
+    scores): constant keys per head (every key ties, so every row is
+    rescored) over each projected-cache layout; indices and per-entry scores
+    bit for bit against the three calls, and the lowest B positions."""
+    case = synth.workload(name, **over)
+    say("listed decode step, rescored rows", name, over, kdt)
+    K = case.K.copy()
+    K[:, :, :, :] = K[:, :1, :, :]
+    case.K = K
+    kd = torch.empty(case.N, case.Hkv, case.T, case.r, dtype=kdt, device="cuda")
+    lsa.lsa_project_keys(dev(case.K), dev(case.W), kd)
+    gi = host(_listed_vs_three_calls(case, kd).idx)
+    for g in range(case.Hkv):
+        np.testing.assert_array_equal(gi[0, g], np.arange(case.B))
+
+
+def test_decode_step_parts_equal_one_call():
+    """lsa_decode_step_part: the score, select and attend parts issued one
+    at a time (the score part twice, as a timing loop does) equal one
+    lsa_decode_step call bit for bit, on the listing and the three-call
+    paths."""
+    from indexer_driven_sparse_amd import pipeline
+    case = synth.workload("decode_t128k_b2048", N=2, T=50000, B=1024)
+    say("decode step parts")
+    N, Hq, Hkv, T, d, r, B = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B
+    Q, W, K, V = dev(case.Q), dev(case.W), dev(case.K), dev(case.V)
+    kd = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_project_keys(K, W, kd)
+    for three in (False, True):
+        one = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, with_idx_scores=True, three_calls=three)
+        one.run(Q, W, kd, K, V)
+        parts = pipeline.DecodePlan(N, Hq, Hkv, T, d, r, B, with_idx_scores=True, three_calls=three)
+        parts.step(Q, W, kd, K, V)            # allocates the workspace
+        parts.idx.fill_(-5)
+        parts.out.fill_(7.0)
+        kw = dict(workspace=parts.step_ws, lse=parts.lse, q_idx=parts.q_idx, out_score=parts.idx_scores,
+                  three_calls=three)
+        for p_ in (lsa.STEP_PART_SCORE, lsa.STEP_PART_SCORE, lsa.STEP_PART_SELECT, lsa.STEP_PART_ATTEND):
+            lsa.lsa_decode_step_part(p_, Q, W, kd, K, V, parts.idx, parts.out, **kw)
+        torch.cuda.synchronize()
+        for name_ in ("idx", "q_idx", "idx_scores", "out", "lse"):
+            a_, b_ = getattr(parts, name_), getattr(one, name_)
+            assert torch.equal(a_.view(torch.int32), b_.view(torch.int32)), (three, name_)
+        _assert_step_ctrl_zero(parts, N * Hkv)
 
 
 @pytest.mark.parametrize("name,over,fused", [
