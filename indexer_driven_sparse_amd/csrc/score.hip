@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_emit_kernel(ScoreDecodeAr
   constexpr int SJ = (kStageSlots / 64 + NG - 1) / NG;          // sample keys per lane group
   constexpr int kSB = 8;                                        // sample entries per thread and batch
   constexpr uint32_t kMark = 1u << 16;                          // an entry written in this call
+  constexpr int kSampleRetries = 16;                            // re-reads of an incomplete sample
   __shared__ ScoreShared sh;
   __shared__ __align__(16) float stage[kStageSlots];
   __shared__ uint32_t hstage[kStageSlots / 64];
@@ -155,17 +156,28 @@ __global__ __launch_bounds__(kScoreThreads) void score_emit_kernel(ScoreDecodeAr
           if (i0 + q * kScoreThreads + tid < S) fn(ent[q]);
       }
     };
+    // With short chunks a chunk can get here before a later chunk of its
+    // row has written its entries: the entries are read again, a bounded
+    // number of times (each writer is already running and writes its
+    // entries right after its query prep), before the chunk gives up.
+    for (int attempt = 0;; ++attempt) {
+      if (tid == 0) res[2] = 0;
+      __syncthreads();
+      int unmarked = 0;
+      each_entry([&](uint32_t v) { unmarked += (v >> 16) != 1u; });
+      if (unmarked) atomicAdd(&res[2], unmarked);
+      __syncthreads();
+      complete = res[2] == 0;
+      if (complete || attempt == kSampleRetries) break;
+      __builtin_amdgcn_s_sleep(32);
+      load_batch(0);
+    }
+    if (S > kSB * kScoreThreads) load_batch(0);
     hist[tid] = 0u;
-    if (tid == 0) res[0] = 0, res[1] = 0, res[2] = 0;
+    if (tid == 0) res[0] = 0, res[1] = 0;
     __syncthreads();
-    int unmarked = 0;
-    each_entry([&](uint32_t v) {
-      if ((v >> 16) != 1u) ++unmarked;
-      else atomicAdd(&hist[(v >> 8) & 255u], 1u);
-    });
-    if (unmarked) atomicAdd(&res[2], unmarked);
+    each_entry([&](uint32_t v) { atomicAdd(&hist[(v >> 8) & 255u], 1u); });
     __syncthreads();
-    complete = res[2] == 0;
     emit_top_bin(hist, e.k_rank, wsum, res);
     const uint32_t b1 = (uint32_t)res[0];
     const int need = e.k_rank - res[1];
