@@ -297,7 +297,21 @@ typedef struct lsa_attn_desc {
   int64_t slot_table_ld;     /* >= n_keys when slot_table is set */
   int32_t n_pool_rows;       /* >= 1 when slot_table is set */
   int32_t reserved1;
+  uint32_t* merge_ctrl;      /* NULL, or LSA_ATTN_MERGE_CTRL_WORDS zeroed device words (below) */
 } lsa_attn_desc;
+
+/* merge_ctrl: with it set, decode on the matrix cores (bf16, head_dim 128,
+ * G = 4 or 8, q 16-byte aligned, at most 1000 (sequence, KV head) rows)
+ * merges its split partials inside the attention launch, as
+ * lsa_decode_step's attention does: each row's splits are placed on one
+ * XCD through per-XCD queues in these words, and the row's last split to
+ * finish merges them (the same arithmetic, in the same order, as the merge
+ * kernel, so the results are identical bit for bit). The words must be
+ * zero before the first call that uses them; every call leaves them zero.
+ * Two calls that share the words must not overlap in time. The workspace
+ * (lsa_attention_workspace_bytes of the same descriptor) then holds the
+ * partials on whole 128-byte lines. Other shapes ignore it. */
+#define LSA_ATTN_MERGE_CTRL_WORDS 1024
 
 int lsa_indexed_attention(const lsa_attn_desc* desc, void* workspace, size_t workspace_bytes,
                           void* stream);
@@ -462,6 +476,77 @@ int lsa_step_is_fused(const lsa_step_desc* desc);
 int lsa_step_path(const lsa_step_desc* desc);
 
 /* ------------------------------------------------------------------------ */
+/* lsa_hier_decode_step                                                     */
+/* ------------------------------------------------------------------------ */
+/*
+ * One whole coarse-to-fine decode step (LongCat Sparse Attention abstract,
+ * hierarchical indexing; JSSA Fig. 1 for the scoring and attention): for
+ * every (sequence, KV head) row, the block summaries (centroids, from
+ * lsa_build_centroids) are scored with the row's q_idx (the scoring prep
+ * runs here), the n_blocks_kept best blocks are kept, every token of the
+ * kept blocks is scored and the exact top-B of those tokens is attended.
+ * The results are exactly those of the sequence
+ *     lsa_index_score   (decode over the centroids, q and w given, hint on)
+ *     lsa_topk_select   (top n_blocks_kept blocks, that hint)
+ *     lsa_index_score   (decode over the kept blocks' tokens: cand = the
+ *                        blocks, cand_block = block, q_idx from the first)
+ *     lsa_topk_select   (top B, the same candidate map, n_positions = T)
+ *     lsa_indexed_attention
+ * on the same arguments: out_blocks, out_idx, q_idx, out_score bit-identical,
+ * out / lse within the attention's own rounding. By default the fine
+ * scoring launch lists the final select's candidates (the listing path of
+ * lsa_decode_step, over the candidate map) where the shape allows it, and
+ * the attention merges its splits in its own launch; flags =
+ * LSA_STEP_THREE_CALLS runs the fine stage as the two separate calls.
+ * Asynchronous on `stream`; allocates nothing; one workspace
+ * (lsa_hier_step_workspace_bytes, same descriptor), all zero before its
+ * first use; every call leaves its control words zero again. Two calls
+ * sharing a workspace must not overlap in time. Returns the LSA_ERR_* code
+ * of the first of the calls above that rejects its part of the descriptor.
+ */
+typedef struct lsa_hier_step_desc {
+  uint32_t struct_size;      /* sizeof(lsa_hier_step_desc) */
+  int32_t n_seq;             /* N */
+  int32_t n_q_heads;         /* Hq, a multiple of Hkv */
+  int32_t n_kv_heads;        /* Hkv */
+  int32_t head_dim;          /* d */
+  int32_t rank;              /* r */
+  int32_t n_keys;            /* T cached positions */
+  int32_t topk;              /* B */
+  int32_t block;             /* tokens per block */
+  int32_t n_blocks_kept;     /* blocks kept per row (B_coarse) */
+  const void* q;             /* [N,Hq,d] contiguous, q_dtype */
+  int32_t q_dtype;
+  int32_t w_per_head;        /* 0: w is [d,r]; 1: w is [Hkv,d,r] */
+  const float* w;
+  const void* k_idx;         /* projected-key cache [N,Hkv,T,r] through its strides */
+  int32_t k_idx_dtype;
+  int32_t kv_dtype;          /* dtype of K and V (= q_dtype) */
+  int64_t k_stride_seq, k_stride_head, k_stride_tok;
+  const void* centroids;     /* [N,Hkv,ceil(T/block),r], k_idx_dtype, through its strides */
+  int64_t c_stride_seq, c_stride_head, c_stride_blk;
+  const void* k;             /* K cache [N,T,Hkv,d] through its strides */
+  const void* v;             /* V cache, same strides */
+  int64_t kv_stride_seq, kv_stride_tok, kv_stride_head;
+  float scale;               /* <= 0: 1/sqrt(d) */
+  int32_t flags;             /* 0 or LSA_STEP_THREE_CALLS */
+  float* q_idx;              /* optional out: fp32 [N,Hkv,r] */
+  int32_t* out_blocks;       /* optional out: [N,Hkv,n_blocks_kept] ascending block numbers */
+  int32_t* out_idx;          /* [N,Hkv,B] ascending positions, -1 padded */
+  float* out_score;          /* optional out: fp32 [N,Hkv,B] */
+  float* out;                /* fp32 [N,Hq,d] */
+  float* lse;                /* optional out: fp32 [N,Hq] */
+} lsa_hier_step_desc;
+
+int lsa_hier_decode_step(const lsa_hier_step_desc* desc, void* workspace, size_t workspace_bytes,
+                         void* stream);
+size_t lsa_hier_step_workspace_bytes(const lsa_hier_step_desc* desc);
+/* LSA_STEP_PATH_LISTED when the fine stage lists its candidates in the
+ * scoring launch, LSA_STEP_PATH_THREE_CALLS when it runs the separate calls,
+ * -1 for an invalid descriptor. */
+int lsa_hier_step_path(const lsa_hier_step_desc* desc);
+
+/* ------------------------------------------------------------------------ */
 /* Setup calls                                                              */
 /* ------------------------------------------------------------------------ */
 /*
@@ -547,7 +632,7 @@ const char* lsa_status_str(int status);   /* static string, never NULL */
 int lsa_last_hip_error(void);             /* HIP error of this thread's last LSA_ERR_HIP */
 int lsa_abi_version(void);                /* LSA_ABI_VERSION */
 /* sizeof of a descriptor, for bindings: 0 score, 1 select, 2 attention,
- * 3 project, 4 centroid, 5 step; 0 for anything else. */
+ * 3 project, 4 centroid, 5 step, 6 hierarchical step; 0 for anything else. */
 size_t lsa_desc_size(int which);
 
 #ifdef __cplusplus

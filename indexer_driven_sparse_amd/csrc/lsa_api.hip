@@ -247,8 +247,15 @@ int validate_attn(const lsa_attn_desc* d, size_t* ws_need) {
   lsa::attention_plan(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, false, &sp, &kps);
   if ((int64_t)d->rows * d->n_kv_heads * sp > INT_MAX) return LSA_ERR_UNSUPPORTED;
   size_t need = lsa::attention_workspace(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, false);
-  if (decode_mfma_shape(d))
+  if (decode_mfma_shape(d)) {
     need = std::max(need, lsa::attention_workspace(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, true));
+    if (d->merge_ctrl) {   // the in-launch merge keeps each split partial on whole 128-byte lines
+      int sp2 = 1, kps2 = 0;
+      lsa::attention_plan(d->rows, d->n_kv_heads, G, d->head_dim, d->topk, true, &sp2, &kps2);
+      need = std::max(need, (size_t)d->rows * d->n_kv_heads * sp2 * lsa::decode_partial_stride(G) * sizeof(float));
+    }
+  }
+  if (d->merge_ctrl && (uintptr_t)d->merge_ctrl % 4 != 0) return LSA_ERR_INVALID_ARG;
   *ws_need = need;
   return LSA_OK;
 }
@@ -682,7 +689,7 @@ int lsa_indexed_attention(const lsa_attn_desc* d, void* ws, size_t ws_bytes, voi
   LSA_TRY(validate_attn(d, &need));
   LSA_TRY(check_ws(ws, ws_bytes, need));
   LSA_TRY(check_device());
-  return run_attention(d, ws, stream);
+  return d->merge_ctrl ? run_attention(d, ws, stream, d->merge_ctrl, device_xccs()) : run_attention(d, ws, stream);
 }
 
 int lsa_indexed_attention_noalloc(const lsa_attn_desc* d, void* stream) {
@@ -692,8 +699,292 @@ int lsa_indexed_attention_noalloc(const lsa_attn_desc* d, void* stream) {
   LSA_TRY(check_device());
   void* ws = nullptr;
   LSA_TRY(scratch_ptr(&ws));
-  return run_attention(d, ws, stream);
+  return d->merge_ctrl ? run_attention(d, ws, stream, d->merge_ctrl, device_xccs()) : run_attention(d, ws, stream);
 }
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// lsa_hier_decode_step: the five calls' descriptors and their workspace.
+// ---------------------------------------------------------------------------
+struct HierPlan {
+  lsa_score_desc cs, fs;          // coarse and fine scoring
+  lsa_select_desc csel, fsel;     // coarse and fine selection
+  lsa_attn_desc attn;
+  int rows, nb, n_fine;
+  bool listed;
+  int list_rank, list_chunk, list_wpr;
+  int64_t s_ld;
+  size_t off_cscore, off_chint, off_csel, off_blocks, off_qidx, off_fscore, off_fhint, off_fsel;
+  size_t off_samples, off_lmeta, off_lists, off_attn, total;
+  size_t csel_bytes, fsel_bytes, attn_bytes;
+};
+
+lsa_score_desc decode_score_desc(const lsa_hier_step_desc* d) {
+  lsa_score_desc sd;
+  std::memset(&sd, 0, sizeof(sd));
+  sd.struct_size = sizeof(sd);
+  sd.mode = LSA_MODE_DECODE;
+  sd.n_seq = d->n_seq;
+  sd.n_kv_heads = d->n_kv_heads;
+  sd.rank = d->rank;
+  sd.k_idx_dtype = d->k_idx_dtype;
+  return sd;
+}
+
+int plan_hier(const lsa_hier_step_desc* d, HierPlan* p) {
+  if (!d || d->struct_size != sizeof(lsa_hier_step_desc)) return LSA_ERR_INVALID_ARG;
+  if (d->n_seq < 1 || d->n_kv_heads < 1 || d->n_keys < 1 || d->topk < 1 || d->block < 1 ||
+      d->n_blocks_kept < 1 || !d->q || !d->centroids)
+    return LSA_ERR_INVALID_ARG;
+  if (d->flags & ~LSA_STEP_THREE_CALLS) return LSA_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)d->n_seq * d->n_kv_heads;
+  if (rows > 65535) return LSA_ERR_UNSUPPORTED;
+  const int64_t nb = ((int64_t)d->n_keys + d->block - 1) / d->block;
+  if (d->n_blocks_kept > nb || (int64_t)d->n_blocks_kept * d->block > INT_MAX) return LSA_ERR_INVALID_ARG;
+  p->rows = (int)rows;
+  p->nb = (int)nb;
+  p->n_fine = d->n_blocks_kept * d->block;
+  const int dt = d->k_idx_dtype;
+  auto ld32 = [](int64_t n) { return (n + 31) / 32 * 32; };   // rows of whole 128-byte lines
+  size_t off = align256((size_t)lsa::step_ctrl_words((int)rows) * 4);
+  // placeholders (offset + 256): validation checks alignment only; bind_hier sets the addresses
+  auto at = [](size_t o) { return (void*)(uintptr_t)(o + 256); };
+
+  // coarse: score every block summary, keep the n_blocks_kept best blocks
+  lsa_score_desc& cs = p->cs;
+  cs = decode_score_desc(d);
+  cs.n_keys = p->nb;
+  cs.q = d->q;
+  cs.q_dtype = d->q_dtype;
+  cs.n_q_heads = d->n_q_heads;
+  cs.head_dim = d->head_dim;
+  cs.w_per_head = d->w_per_head;
+  cs.w = d->w;
+  cs.k_idx = d->centroids;
+  cs.k_stride_seq = d->c_stride_seq;
+  cs.k_stride_head = d->c_stride_head;
+  cs.k_stride_tok = d->c_stride_blk;
+  p->off_qidx = off;
+  off = align256(off + (size_t)rows * d->rank * sizeof(float));
+  cs.q_idx = at(p->off_qidx);
+  p->off_cscore = off;
+  cs.scores_ld = ld32(p->nb);
+  off = align256(off + (size_t)rows * cs.scores_ld * sizeof(float));
+  cs.scores = (float*)at(p->off_cscore);
+  const int chint = lsa::score_hint_count(p->nb, dt);
+  p->off_chint = off;
+  cs.hint_ld = ld32(chint);
+  off = align256(off + (size_t)rows * cs.hint_ld * sizeof(uint32_t));
+  cs.hint = (uint32_t*)at(p->off_chint);
+  size_t need = 0;
+  LSA_TRY(validate_score(&cs, &need));
+
+  lsa_select_desc& csel = p->csel;
+  std::memset(&csel, 0, sizeof(csel));
+  csel.struct_size = sizeof(csel);
+  csel.rows = (int)rows;
+  csel.n = p->nb;
+  csel.topk = d->n_blocks_kept;
+  csel.scores = cs.scores;
+  csel.scores_ld = cs.scores_ld;
+  csel.cand_block = 1;
+  p->off_blocks = off;
+  off = align256(off + (size_t)rows * d->n_blocks_kept * sizeof(int32_t));
+  csel.out_idx = (int32_t*)at(p->off_blocks);
+  csel.hint = cs.hint;
+  csel.hint_ld = cs.hint_ld;
+  csel.hint_count = chint;
+  csel.hint_k = lsa::score_hint_k(dt);
+  LSA_TRY(validate_select(&csel, &p->csel_bytes));
+  p->off_csel = off;
+  off = align256(off + p->csel_bytes);
+
+  // fine: score the kept blocks' tokens, keep the top B
+  lsa_score_desc& fs = p->fs;
+  fs = decode_score_desc(d);
+  fs.n_keys = d->n_keys;
+  fs.q_idx = cs.q_idx;   // q_idx from the coarse call
+  fs.k_idx = d->k_idx;
+  fs.k_stride_seq = d->k_stride_seq;
+  fs.k_stride_head = d->k_stride_head;
+  fs.k_stride_tok = d->k_stride_tok;
+  fs.cand = csel.out_idx;
+  fs.n_cand = d->n_blocks_kept;
+  fs.cand_block = d->block;
+  fs.cand_ld = d->n_blocks_kept;
+  p->off_fscore = off;
+  fs.scores_ld = ld32(p->n_fine);
+  off = align256(off + (size_t)rows * fs.scores_ld * sizeof(float));
+  fs.scores = (float*)at(p->off_fscore);
+  const int fhint = lsa::score_hint_count(p->n_fine, dt);
+  p->off_fhint = off;
+  fs.hint_ld = ld32(fhint);
+  off = align256(off + (size_t)rows * fs.hint_ld * sizeof(uint32_t));
+  fs.hint = (uint32_t*)at(p->off_fhint);
+  LSA_TRY(validate_score(&fs, &need));
+
+  lsa_select_desc& fsel = p->fsel;
+  std::memset(&fsel, 0, sizeof(fsel));
+  fsel.struct_size = sizeof(fsel);
+  fsel.rows = (int)rows;
+  fsel.n = p->n_fine;
+  fsel.topk = d->topk;
+  fsel.scores = fs.scores;
+  fsel.scores_ld = fs.scores_ld;
+  fsel.cand = fs.cand;
+  fsel.cand_ld = fs.cand_ld;
+  fsel.cand_block = d->block;
+  fsel.n_positions = d->n_keys;
+  fsel.out_idx = d->out_idx;
+  fsel.out_score = d->out_score;
+  fsel.hint = fs.hint;
+  fsel.hint_ld = fs.hint_ld;
+  fsel.hint_count = fhint;
+  fsel.hint_k = lsa::score_hint_k(dt);
+  LSA_TRY(validate_select(&fsel, &p->fsel_bytes));
+  p->off_fsel = off;
+  off = align256(off + p->fsel_bytes);
+
+  // the fine stage's listing launch, where the shape allows it
+  p->listed = false;
+  if (!(d->flags & LSA_STEP_THREE_CALLS)) {
+    const int k = lsa::score_emit_rank(p->n_fine, (int)rows, d->topk, d->rank, dt, lsa::select_list_stride(),
+                                       lsa::select_list_max_segments(), lsa::select_list_max());
+    if (k > 0) {
+      p->listed = true;
+      p->list_rank = k;
+      p->list_chunk = lsa::score_chunk_slots(p->n_fine, (int)rows, dt);
+      p->list_wpr = (p->n_fine + p->list_chunk - 1) / p->list_chunk;
+      p->s_ld = ((int64_t)lsa::score_emit_samples(p->n_fine) + 63) / 64 * 64;
+      p->off_samples = off;
+      off = align256(off + (size_t)rows * p->s_ld * sizeof(uint32_t));
+      p->off_lmeta = off;
+      off = align256(off + (size_t)rows * p->list_wpr * sizeof(int4));
+      p->off_lists = off;
+      off = align256(off + (size_t)rows * p->list_wpr * lsa::select_list_stride() * sizeof(int2));
+    }
+  }
+
+  // attention over the selection, its splits merged in the launch
+  lsa_attn_desc& at_ = p->attn;
+  std::memset(&at_, 0, sizeof(at_));
+  at_.struct_size = sizeof(at_);
+  at_.mode = LSA_MODE_DECODE;
+  at_.rows = d->n_seq;
+  at_.n_q_heads = d->n_q_heads;
+  at_.n_kv_heads = d->n_kv_heads;
+  at_.head_dim = d->head_dim;
+  at_.topk = d->topk;
+  at_.n_keys = d->n_keys;
+  at_.q = d->q;
+  at_.q_dtype = d->q_dtype;
+  at_.kv_dtype = d->kv_dtype;
+  at_.k = d->k;
+  at_.v = d->v;
+  at_.kv_stride_seq = d->kv_stride_seq;
+  at_.kv_stride_tok = d->kv_stride_tok;
+  at_.kv_stride_head = d->kv_stride_head;
+  at_.idx = d->out_idx;
+  at_.scale = d->scale;
+  at_.out = d->out;
+  at_.lse = d->lse;
+  at_.merge_ctrl = (uint32_t*)at(0);
+  LSA_TRY(validate_attn(&at_, &p->attn_bytes));
+  p->off_attn = off;
+  p->total = off + p->attn_bytes;
+  return LSA_OK;
+}
+
+// Points the plan's descriptors at the workspace (and the caller's optional outputs).
+void bind_hier(HierPlan* p, const lsa_hier_step_desc* d, void* ws) {
+  char* b = (char*)ws;
+  float* q_idx = d->q_idx ? d->q_idx : (float*)(b + p->off_qidx);
+  int32_t* blocks = d->out_blocks ? d->out_blocks : (int32_t*)(b + p->off_blocks);
+  p->cs.q_idx = q_idx;
+  p->cs.scores = (float*)(b + p->off_cscore);
+  p->cs.hint = (uint32_t*)(b + p->off_chint);
+  p->csel.scores = p->cs.scores;
+  p->csel.hint = p->cs.hint;
+  p->csel.out_idx = blocks;
+  p->fs.q_idx = q_idx;
+  p->fs.cand = blocks;
+  p->fs.scores = (float*)(b + p->off_fscore);
+  p->fs.hint = (uint32_t*)(b + p->off_fhint);
+  p->fsel.scores = p->fs.scores;
+  p->fsel.hint = p->fs.hint;
+  p->fsel.cand = blocks;
+  p->attn.merge_ctrl = (uint32_t*)b;
+}
+
+int run_hier(const lsa_hier_step_desc* d, HierPlan& p, char* b, hipStream_t s) {
+  void* stream = (void*)s;
+  LSA_TRY(lsa_index_score(&p.cs, nullptr, 0, stream));
+  LSA_TRY(lsa_topk_select(&p.csel, b + p.off_csel, p.csel_bytes, stream));
+  if (p.listed) {
+    lsa::ScoreDecodeArgs sc{};
+    sc.k_idx = d->k_idx;
+    sc.ks_seq = d->k_stride_seq;
+    sc.ks_head = d->k_stride_head;
+    sc.ks_tok = d->k_stride_tok;
+    sc.Hkv = d->n_kv_heads;
+    sc.T = d->n_keys;
+    sc.r = d->rank;
+    sc.q_idx_in = (const float*)p.fs.q_idx;
+    sc.cand = p.fs.cand;
+    sc.cand_ld = p.fs.cand_ld;
+    sc.cand_block = d->block;
+    sc.n_out = p.n_fine;
+    sc.scores = nullptr;   // the lists carry the scores the select needs
+    sc.scores_ld = p.fs.scores_ld;
+    sc.chunk = p.list_chunk;
+    lsa::ScoreEmitArgs e{};
+    e.samples = (uint32_t*)(b + p.off_samples);
+    e.s_ld = p.s_ld;
+    e.k_rank = p.list_rank;
+    e.wpr = p.list_wpr;
+    e.ctrl = (uint32_t*)b + lsa::step_ctrl_row0();   // one word per row: finished chunks
+    e.ctrl_stride = lsa::step_ctrl_per_row();
+    e.lists = (int2*)(b + p.off_lists);
+    e.list_stride = lsa::select_list_stride();
+    e.meta = (int4*)(b + p.off_lmeta);
+    e.no_list = lsa::select_list_max() + 1;
+    hipError_t err = lsa::launch_score_emit(sc, e, p.rows, d->k_idx_dtype, s);
+    if (err != hipSuccess) return hip_fail(err);
+    lsa::SelectArgs a{};
+    a.scores = p.fs.scores;
+    a.scores_ld = p.fs.scores_ld;
+    a.n = p.n_fine;
+    a.B = d->topk;
+    a.cand = p.fs.cand;
+    a.cand_ld = p.fs.cand_ld;
+    a.cand_block = d->block;
+    a.n_positions = d->n_keys;
+    a.out_idx = d->out_idx;
+    a.out_score = d->out_score;
+    a.gbitmap = p.n_fine > lsa::kSelectLdsMaxSlots ? (uint32_t*)(b + p.off_fsel) : nullptr;
+    a.seg_list = e.lists;
+    a.seg_meta = e.meta;
+    a.nseg = p.list_wpr;
+    a.rs_k_idx = d->k_idx;   // a row the lists do not settle is rescored
+    a.rs_ks_seq = d->k_stride_seq;
+    a.rs_ks_head = d->k_stride_head;
+    a.rs_ks_tok = d->k_stride_tok;
+    a.rs_q_idx = (const float*)p.fs.q_idx;
+    a.rs_r = d->rank;
+    a.rs_dt = d->k_idx_dtype;
+    a.rs_Hkv = d->n_kv_heads;
+    err = lsa::launch_select_lists(a, p.rows, s);
+    if (err != hipSuccess) return hip_fail(err);
+  } else {
+    LSA_TRY(lsa_index_score(&p.fs, nullptr, 0, stream));
+    LSA_TRY(lsa_topk_select(&p.fsel, b + p.off_fsel, p.fsel_bytes, stream));
+  }
+  return run_attention(&p.attn, p.attn_bytes ? b + p.off_attn : nullptr, stream, p.attn.merge_ctrl,
+                       device_xccs());
+}
+
+}  // namespace
 
 namespace {
 
@@ -866,6 +1157,26 @@ int lsa_step_path(const lsa_step_desc* d) {
   return p.fused ? LSA_STEP_PATH_ONE_LAUNCH : p.listed ? LSA_STEP_PATH_LISTED : LSA_STEP_PATH_THREE_CALLS;
 }
 
+int lsa_hier_decode_step(const lsa_hier_step_desc* d, void* ws, size_t ws_bytes, void* stream) {
+  HierPlan p;
+  LSA_TRY(plan_hier(d, &p));
+  LSA_TRY(check_ws(ws, ws_bytes, p.total));
+  LSA_TRY(check_device());
+  bind_hier(&p, d, ws);
+  return run_hier(d, p, (char*)ws, (hipStream_t)stream);
+}
+
+size_t lsa_hier_step_workspace_bytes(const lsa_hier_step_desc* d) {
+  HierPlan p;
+  return plan_hier(d, &p) == LSA_OK ? p.total : 0;
+}
+
+int lsa_hier_step_path(const lsa_hier_step_desc* d) {
+  HierPlan p;
+  if (plan_hier(d, &p) != LSA_OK) return -1;
+  return p.listed ? LSA_STEP_PATH_LISTED : LSA_STEP_PATH_THREE_CALLS;
+}
+
 size_t lsa_attention_workspace_bytes(const lsa_attn_desc* d) {
   size_t need = 0;
   return validate_attn(d, &need) == LSA_OK ? need : 0;
@@ -969,6 +1280,7 @@ size_t lsa_desc_size(int which) {
     case 3: return sizeof(lsa_project_desc);
     case 4: return sizeof(lsa_centroid_desc);
     case 5: return sizeof(lsa_step_desc);
+    case 6: return sizeof(lsa_hier_step_desc);
   }
   return 0;
 }

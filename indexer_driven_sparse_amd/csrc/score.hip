@@ -71,7 +71,7 @@ __device__ __forceinline__ void emit_top_bin(const uint32_t* hist, int need, int
   __syncthreads();
 }
 
-template <int DT, int LPK>
+template <int DT, int LPK, bool CAND>
 __global__ __launch_bounds__(kScoreThreads) void score_emit_kernel(ScoreDecodeArgs a, ScoreEmitArgs e) {
   constexpr int ESZ = DT == 2 ? 1 : DT == 1 ? 2 : 4;
   constexpr int E = 16 / ESZ;
@@ -105,16 +105,30 @@ __global__ __launch_bounds__(kScoreThreads) void score_emit_kernel(ScoreDecodeAr
   // back or invalidates a whole L2). An entry without the mark (not yet
   // written) makes the chunk list nothing. The row's last chunk out clears
   // the entries for the next call.
+  // sample slots are slots of the row (through the candidate map, when
+  // there is one, like every slot: a slot that covers no token scores -inf)
+  const int32_t* crow = CAND ? a.cand + (int64_t)row * a.cand_ld : nullptr;
+  int64_t spos[SJ];
+#pragma unroll
+  for (int j = 0; j < SJ; ++j) spos[j] = sample_slot(c0 / 64 + min(grp + j * NG, ns - 1), row, a.n_out);
+  if constexpr (CAND) {
+    int32_t cb[SJ];
+#pragma unroll
+    for (int j = 0; j < SJ; ++j) cb[j] = crow[spos[j] / a.cand_block];   // map entries first, then keys
+#pragma unroll
+    for (int j = 0; j < SJ; ++j) {
+      const int64_t p = cb[j] < 0 ? -1 : (int64_t)cb[j] * a.cand_block + spos[j] % a.cand_block;
+      spos[j] = p < a.T ? p : -1;
+    }
+  }
   uint4 sraw[SJ];
 #pragma unroll
-  for (int j = 0; j < SJ; ++j) {
-    const int i = min(grp + j * NG, ns - 1);
-    sraw[j] = load_key16(kbase + sample_slot(c0 / 64 + i, row, a.n_out) * a.ks_tok * ESZ);
-  }
+  for (int j = 0; j < SJ; ++j) sraw[j] = load_key16(kbase + (spos[j] > 0 ? spos[j] : (int64_t)0) * a.ks_tok * ESZ);
   auto contribute = [&](const float (&qv)[E]) {
 #pragma unroll
     for (int j = 0; j < SJ; ++j) {
-      const float sc = sum_lanes<LPK>(dot16<DT>(sraw[j], qv));
+      float sc = sum_lanes<LPK>(dot16<DT>(sraw[j], qv));
+      if (spos[j] < 0) sc = -INFINITY;
       const int i = grp + j * NG;
       if (l == 0 && i < ns)
         __hip_atomic_store(sent + c0 / 64 + i, kMark | (order_key(sc) >> 16), __ATOMIC_RELAXED,
@@ -133,7 +147,7 @@ __global__ __launch_bounds__(kScoreThreads) void score_emit_kernel(ScoreDecodeAr
   // only read it; its load is issued while the staged scores go out.
   uint64_t* tword = reinterpret_cast<uint64_t*>(rc + 2);
   uint64_t tw = 0;
-  score_chunk<DT, LPK, false>(a, row, c0, c1, sh, true, nullptr, stage, hstage, contribute, [&]() {
+  score_chunk<DT, LPK, CAND>(a, row, c0, c1, sh, true, nullptr, stage, hstage, contribute, [&]() {
     if (tid == 0) tw = __hip_atomic_load(tword, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   });
   if (tid == 0) res[3] = (tw >> 32) ? (int)(uint32_t)tw : -1;
@@ -346,13 +360,16 @@ template <int DT, int LPK>
 hipError_t launch_emit_lpk(const ScoreDecodeArgs& a, const ScoreEmitArgs& e, int rows, hipStream_t s) {
   dim3 grid((unsigned)((a.n_out + a.chunk - 1) / a.chunk), (unsigned)rows);
   if ((int)grid.x != e.wpr) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((score_emit_kernel<DT, LPK>), grid, dim3(kScoreThreads), 0, s, a, e);
+  if (a.cand)
+    hipLaunchKernelGGL((score_emit_kernel<DT, LPK, true>), grid, dim3(kScoreThreads), 0, s, a, e);
+  else
+    hipLaunchKernelGGL((score_emit_kernel<DT, LPK, false>), grid, dim3(kScoreThreads), 0, s, a, e);
   return hipGetLastError();
 }
 
 hipError_t launch_score_emit(const ScoreDecodeArgs& a, const ScoreEmitArgs& e, int rows, int k_dt,
                              hipStream_t s) {
-  if (a.cand != nullptr || a.hint != nullptr || a.chunk > kStageSlots || a.chunk % 4 != 0 ||
+  if ((a.cand != nullptr && a.cand_block < 1) || a.hint != nullptr || a.chunk > kStageSlots || a.chunk % 4 != 0 ||
       e.list_stride < a.chunk || e.s_ld < score_emit_samples(a.n_out) || e.k_rank < 1)
     return hipErrorInvalidValue;
   const int esz = k_dt == 2 ? 1 : k_dt == 1 ? 2 : 4;

@@ -186,13 +186,29 @@ __device__ __forceinline__ void score_chunk(const ScoreDecodeArgs& a, int row, i
   uint4 raw[kGroupsInFlight][LPK];
   bool ok[kGroupsInFlight][LPK];
   auto issue_group = [&](int64_t gb, int u) {
+    // with a candidate map, every map entry of the group is loaded before
+    // any key: vector loads complete in order, so a key load issued between
+    // two map loads would make the second map entry wait for it
+    int32_t cpos[LPK];
+    if constexpr (CAND) {
+#pragma unroll
+      for (int it = 0; it < LPK; ++it) {
+        const int64_t slot = gb + (int64_t)u * 4 * 64 + it * KPI + kg;
+        cpos[it] = slot < c1 ? crow[slot / a.cand_block] : -1;
+      }
+    }
 #pragma unroll
     for (int it = 0; it < LPK; ++it) {
       const int64_t slot = gb + (int64_t)u * 4 * 64 + it * KPI + kg;
       bool valid = slot < c1;
       int64_t pos = 0;
       if (valid) {
-        pos = slot_position<CAND>(a, crow, slot);
+        if constexpr (CAND) {
+          pos = cpos[it] < 0 ? -1 : (int64_t)cpos[it] * a.cand_block + slot % a.cand_block;
+          if (pos >= a.T) pos = -1;
+        } else {
+          pos = slot;
+        }
         valid = pos >= 0;
       }
       ok[u][it] = valid;

@@ -145,16 +145,22 @@ hipError_t launch_select(const SelectArgs& a, int rows, hipStream_t s) {
 }
 
 hipError_t launch_select_lists(const SelectArgs& a, int rows, hipStream_t s) {
-  if (a.nseg < 1 || a.nseg > kThreads || a.cand != nullptr || !a.seg_list || !a.seg_meta)
-    return hipErrorInvalidValue;
+  if (a.nseg < 1 || a.nseg > kThreads || !a.seg_list || !a.seg_meta) return hipErrorInvalidValue;
   const hipError_t attr = select_attributes();
   if (attr != hipSuccess) return attr;
   const int nw = (a.n + 31) / 32;
   const size_t lds = a.gbitmap ? sizeof(SelShared) : sizeof(SelShared) + (size_t)2 * nw * sizeof(uint32_t);
-  if (a.gbitmap)
-    hipLaunchKernelGGL((select_kernel<false, true, true>), dim3(rows), dim3(kThreads), lds, s, a);
-  else
-    hipLaunchKernelGGL((select_kernel<false, false, true>), dim3(rows), dim3(kThreads), lds, s, a);
+  if (a.cand) {
+    if (a.gbitmap)
+      hipLaunchKernelGGL((select_kernel<true, true, true>), dim3(rows), dim3(kThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((select_kernel<true, false, true>), dim3(rows), dim3(kThreads), lds, s, a);
+  } else {
+    if (a.gbitmap)
+      hipLaunchKernelGGL((select_kernel<false, true, true>), dim3(rows), dim3(kThreads), lds, s, a);
+    else
+      hipLaunchKernelGGL((select_kernel<false, false, true>), dim3(rows), dim3(kThreads), lds, s, a);
+  }
   return hipGetLastError();
 }
 

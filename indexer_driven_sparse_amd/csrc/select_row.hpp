@@ -213,12 +213,23 @@ __device__ __forceinline__ void rescore_row_t(const SelectArgs& a, int row, floa
   static_assert(P % 4 == 0 && P <= 16, "4, 8 or 16 pieces");
   const int n = row / a.rs_Hkv, g = row % a.rs_Hkv;
   const char* base = (const char*)a.rs_k_idx + ((int64_t)n * a.rs_ks_seq + (int64_t)g * a.rs_ks_head) * ESZ;
+  const int32_t* crow = a.cand ? a.cand + (int64_t)row * a.cand_ld : nullptr;
 #pragma unroll 1
   for (int64_t t = threadIdx.x; t < nv; t += kThreads) {
     // q_idx is read from LDS for every key: held in registers across the
     // loop, its up to 128 values would crowd the whole kernel into spills
     asm volatile("" ::: "memory");
-    const char* kr = base + t * a.rs_ks_tok * ESZ;
+    int64_t pos = t;   // slot t's position (through the candidate map), or -1
+    if (crow) {
+      const int32_t c = crow[t / a.cand_block];
+      pos = c < 0 ? -1 : (int64_t)c * a.cand_block + t % a.cand_block;
+      if (pos >= a.n_positions) pos = -1;
+    }
+    if (pos < 0) {   // a slot that covers no token scores -inf, as in the scoring kernels
+      srow[t] = -INFINITY;
+      continue;
+    }
+    const char* kr = base + pos * a.rs_ks_tok * ESZ;
     // pieces four at a time: ((p0+p1)+(p2+p3)) per group, then the groups
     // pairwise -- the same tree as pairwise over all P pieces
     float grp[P / 4];

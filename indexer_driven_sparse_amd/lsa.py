@@ -72,7 +72,9 @@ class AttnDesc(_c.Structure):
                 ("kv_stride_seq", _I64), ("kv_stride_tok", _I64), ("kv_stride_head", _I64),
                 ("idx", _P), ("scale", _F), ("query_block", _I32), ("out", _P), ("lse", _P),
                 ("slot_table", _P), ("slot_table_ld", _I64), ("n_pool_rows", _I32),
-                ("reserved1", _I32)]
+                ("reserved1", _I32), ("merge_ctrl", _P)]
+
+ATTN_MERGE_CTRL_WORDS = 1024   # lsa_attn_desc.merge_ctrl: zeroed int32 words for the in-launch merge
 
 
 class ProjectDesc(_c.Structure):
@@ -103,7 +105,23 @@ class StepDesc(_c.Structure):
                 ("q_idx", _P), ("out_idx", _P), ("out_score", _P), ("out", _P), ("lse", _P)]
 
 
-DESCS = {0: ScoreDesc, 1: SelectDesc, 2: AttnDesc, 3: ProjectDesc, 4: CentroidDesc, 5: StepDesc}
+class HierStepDesc(_c.Structure):
+    _fields_ = [("struct_size", _U32), ("n_seq", _I32), ("n_q_heads", _I32), ("n_kv_heads", _I32),
+                ("head_dim", _I32), ("rank", _I32), ("n_keys", _I32), ("topk", _I32),
+                ("block", _I32), ("n_blocks_kept", _I32),
+                ("q", _P), ("q_dtype", _I32), ("w_per_head", _I32), ("w", _P),
+                ("k_idx", _P), ("k_idx_dtype", _I32), ("kv_dtype", _I32),
+                ("k_stride_seq", _I64), ("k_stride_head", _I64), ("k_stride_tok", _I64),
+                ("centroids", _P), ("c_stride_seq", _I64), ("c_stride_head", _I64), ("c_stride_blk", _I64),
+                ("k", _P), ("v", _P),
+                ("kv_stride_seq", _I64), ("kv_stride_tok", _I64), ("kv_stride_head", _I64),
+                ("scale", _F), ("flags", _I32),
+                ("q_idx", _P), ("out_blocks", _P), ("out_idx", _P), ("out_score", _P), ("out", _P),
+                ("lse", _P)]
+
+
+DESCS = {0: ScoreDesc, 1: SelectDesc, 2: AttnDesc, 3: ProjectDesc, 4: CentroidDesc, 5: StepDesc,
+         6: HierStepDesc}
 
 _SIGS = {
     "lsa_index_score": (_I32, [_P, _P, _c.c_size_t, _P]),
@@ -122,6 +140,9 @@ _SIGS = {
     "lsa_step_is_fused": (_I32, [_P]),
     "lsa_step_path": (_I32, [_P]),
     "lsa_decode_step_part": (_I32, [_P, _I32, _P, _c.c_size_t, _P]),
+    "lsa_hier_decode_step": (_I32, [_P, _P, _c.c_size_t, _P]),
+    "lsa_hier_step_workspace_bytes": (_c.c_size_t, [_P]),
+    "lsa_hier_step_path": (_I32, [_P]),
     "lsa_status_str": (_c.c_char_p, [_I32]),
     "lsa_last_hip_error": (_I32, []),
     "lsa_abi_version": (_I32, []),
@@ -429,7 +450,7 @@ def lsa_select_workspace_bytes(scores, topk, out_idx, *, n=None, n_valid=None, c
 
 
 def _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table=None, n_keys=None,
-               query_block=0):
+               query_block=0, merge_ctrl=None):
     if q.dim() != 3:
         raise ValueError("q must be [rows,Hq,d]")
     rows, Hq, hd = q.shape
@@ -482,19 +503,27 @@ def _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table=None, n_keys=None
         d.slot_table = _ptr(slot_table)
         d.slot_table_ld = slot_table.stride(0)
         d.n_pool_rows = k.shape[0]
+    if merge_ctrl is not None:
+        if (merge_ctrl.device != q.device or not merge_ctrl.is_contiguous()
+                or merge_ctrl.numel() * merge_ctrl.element_size() < 4 * ATTN_MERGE_CTRL_WORDS):
+            raise ValueError(f"merge_ctrl must be {ATTN_MERGE_CTRL_WORDS} contiguous zeroed 32-bit words "
+                             "on q's device")
+        d.merge_ctrl = _ptr(merge_ctrl)
     return d
 
 
 def lsa_indexed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor,
                           out: torch.Tensor, *, lse=None, mode: int = MODE_DECODE,
                           scale: float = 0.0, workspace=None, stream=None,
-                          slot_table=None, n_keys=None, query_block: int = 0) -> None:
+                          slot_table=None, n_keys=None, query_block: int = 0, merge_ctrl=None) -> None:
     """q [rows,Hq,d]; k, v [S,T,Hkv,d] viewed through their strides (same for
     both); idx [rows,Hkv,B] int32; out fp32 [rows,Hq,d]; lse fp32 [rows,Hq].
     Paged: k, v are a pool [P,Hkv,d] and slot_table int32 [S, ld] maps
     (sequence, position) to a pool row; n_keys defaults to the table width.
-    Prefill is causal; query_block=qb > 1 shares idx row i//qb among tokens."""
-    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys, query_block)
+    Prefill is causal; query_block=qb > 1 shares idx row i//qb among tokens.
+    merge_ctrl: ATTN_MERGE_CTRL_WORDS zeroed int32 words, for the split
+    merge inside the attention launch (bf16 decode on the matrix cores)."""
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys, query_block, merge_ctrl)
     lib = _lib()
     ws, wsb = _workspace(lib.lsa_attention_workspace_bytes(_c.byref(d)), workspace, q.device)
     _check("lsa_indexed_attention",
@@ -504,29 +533,33 @@ def lsa_indexed_attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, idx
 def lsa_indexed_attention_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                   idx: torch.Tensor, out: torch.Tensor, *, lse=None,
                                   mode: int = MODE_DECODE, scale: float = 0.0, stream=None,
-                                  slot_table=None, n_keys=None, query_block: int = 0) -> None:
+                                  slot_table=None, n_keys=None, query_block: int = 0,
+                                  merge_ctrl=None) -> None:
     """lsa_indexed_attention with its split partials in the library's static
     per-GPU scratch (NOALLOC_SCRATCH_BYTES): no workspace, no allocation --
     for callers that cannot allocate. Same arguments and bit-identical
     results; a shape needing more scratch raises LsaError
     (LSA_ERR_SCRATCH_LIMIT). Calls overlapping in time on one GPU race."""
-    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys, query_block)
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys, query_block, merge_ctrl)
     _check("lsa_indexed_attention_noalloc",
            _lib().lsa_indexed_attention_noalloc(_c.byref(d), _stream(stream)))
 
 
 def lsa_attention_workspace_bytes(q, k, v, idx, out, *, lse=None, mode=MODE_DECODE,
                                   scale=0.0, slot_table=None, n_keys=None,
-                                  query_block: int = 0) -> int:
-    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys, query_block)
+                                  query_block: int = 0, merge_ctrl=None) -> int:
+    d = _attn_desc(q, k, v, idx, out, lse, mode, scale, slot_table, n_keys, query_block, merge_ctrl)
     return int(_lib().lsa_attention_workspace_bytes(_c.byref(d)))
 
 
 def attention_workspace_bytes_for(rows: int, Hq: int, Hkv: int, d: int, B: int, T: int,
-                                  kv_dtype: int = BF16, mode: int = MODE_DECODE) -> int:
+                                  kv_dtype: int = BF16, mode: int = MODE_DECODE,
+                                  merge_in_launch: bool = False) -> int:
     """Workspace lsa_indexed_attention needs for a shape (no tensors needed:
-    the size depends on the shape only)."""
+    the size depends on the shape only); merge_in_launch: with merge_ctrl."""
     dd = AttnDesc()
+    if merge_in_launch:
+        dd.merge_ctrl = 256                              # placeholder: sizing never dereferences
     dd.struct_size = _c.sizeof(AttnDesc)
     dd.mode, dd.rows, dd.n_q_heads, dd.n_kv_heads, dd.head_dim, dd.topk, dd.n_keys = \
         mode, rows, Hq, Hkv, d, B, T
@@ -738,3 +771,94 @@ def lsa_build_centroids(k_idx: torch.Tensor, block: int, out: torch.Tensor, *, s
     d.out = _ptr(out)
     d.out_stride_seq, d.out_stride_head, d.out_stride_blk = out.stride(0), out.stride(1), out.stride(2)
     _check("lsa_build_centroids", _lib().lsa_build_centroids(_c.byref(d), _stream(stream)))
+
+
+def _hier_desc(q, w, k_idx, centroids, k, v, block, out_blocks, out_idx, out, lse, q_idx, out_score,
+               scale, three_calls):
+    if q.dim() != 3 or not q.is_contiguous():
+        raise ValueError("q must be contiguous [N,Hq,d]")
+    N, Hq, hd = q.shape
+    if k_idx.dim() != 4 or k_idx.stride(-1) != 1 or k_idx.shape[0] != N:
+        raise ValueError("k_idx must be [N,Hkv,T,r] with r contiguous")
+    _, Hkv, T, r = k_idx.shape
+    nb = (T + block - 1) // block
+    if (centroids.dim() != 4 or centroids.stride(-1) != 1 or tuple(centroids.shape) != (N, Hkv, nb, r)
+            or centroids.dtype != k_idx.dtype):
+        raise ValueError("centroids must be [N,Hkv,ceil(T/block),r] in k_idx's dtype, r contiguous")
+    if k.dim() != 4 or k.shape != v.shape or k.stride() != v.stride() or k.dtype != v.dtype:
+        raise ValueError("k and v must share shape [N,T,Hkv,d], strides and dtype")
+    if k.shape[0] < N or k.shape[1] != T or k.shape[2] != Hkv or k.shape[3] != hd:
+        raise ValueError("k/v must be [N,T,Hkv,d] matching q and k_idx")
+    if w.dtype != torch.float32 or not w.is_contiguous() or w.shape[-1] != r or w.shape[-2] != hd \
+            or (w.dim() == 3 and w.shape[0] != Hkv):
+        raise ValueError("w must be contiguous float32 [d,r] or [Hkv,d,r]")
+    B = out_idx.shape[-1]
+    Bc = out_blocks.shape[-1] if out_blocks is not None else None
+    _need(out_idx, "out_idx", torch.int32, (N, Hkv, B))
+    if out_blocks is not None:
+        _need(out_blocks, "out_blocks", torch.int32, (N, Hkv, Bc))
+    _need(out, "out", torch.float32, (N, Hq, hd))
+    _need(lse, "lse", torch.float32, (N, Hq))
+    _need(q_idx, "q_idx", torch.float32, (N, Hkv, r))
+    _need(out_score, "out_score", torch.float32, (N, Hkv, B))
+    d = HierStepDesc()
+    d.struct_size = _c.sizeof(HierStepDesc)
+    d.n_seq, d.n_q_heads, d.n_kv_heads, d.head_dim, d.rank, d.n_keys, d.topk = N, Hq, Hkv, hd, r, T, B
+    d.block = block
+    d.q, d.q_dtype = _ptr(q), _dt(q)
+    d.w, d.w_per_head = _ptr(w), 1 if w.dim() == 3 else 0
+    d.k_idx, d.k_idx_dtype = _ptr(k_idx), _dt(k_idx)
+    d.k_stride_seq, d.k_stride_head, d.k_stride_tok = k_idx.stride(0), k_idx.stride(1), k_idx.stride(2)
+    d.centroids = _ptr(centroids)
+    d.c_stride_seq, d.c_stride_head, d.c_stride_blk = centroids.stride(0), centroids.stride(1), centroids.stride(2)
+    d.k, d.v, d.kv_dtype = _ptr(k), _ptr(v), _dt(k)
+    d.kv_stride_seq, d.kv_stride_tok, d.kv_stride_head = k.stride(0), k.stride(1), k.stride(2)
+    d.scale = scale
+    d.flags = STEP_THREE_CALLS if three_calls else 0
+    d.q_idx, d.out_blocks, d.out_idx, d.out_score, d.out, d.lse = (
+        _ptr(q_idx), _ptr(out_blocks), _ptr(out_idx), _ptr(out_score), _ptr(out), _ptr(lse))
+    return d
+
+
+def lsa_hier_decode_step(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept: int, out_idx, out, *,
+                         out_blocks=None, lse=None, q_idx=None, out_score=None, scale: float = 0.0,
+                         workspace=None, stream=None, three_calls: bool = False) -> None:
+    """One coarse-to-fine decode step: centroids [N,Hkv,ceil(T/block),r]
+    scored and the n_blocks_kept best blocks kept, their tokens scored and
+    the top B (= out_idx.shape[-1]) attended. out_blocks int32
+    [N,Hkv,n_blocks_kept] optional. workspace: uint8 of at least
+    lsa_hier_step_workspace_bytes, all zero before its first use (allocated
+    zeroed here when not given). three_calls: the fine stage as the
+    separate scoring and select calls."""
+    d = _hier_desc(q, w, k_idx, centroids, k, v, block, out_blocks, out_idx, out, lse, q_idx, out_score,
+                   scale, three_calls)
+    d.n_blocks_kept = n_blocks_kept
+    lib = _lib()
+    need = lib.lsa_hier_step_workspace_bytes(_c.byref(d))
+    if need == 0:
+        _check("lsa_hier_decode_step", lib.lsa_hier_decode_step(_c.byref(d), None, 0, _stream(stream)))
+    if workspace is None:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    wsb = workspace.numel() * workspace.element_size()
+    _check("lsa_hier_decode_step", lib.lsa_hier_decode_step(_c.byref(d), _ptr(workspace), wsb, _stream(stream)))
+
+
+def lsa_hier_step_workspace_bytes(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept: int, out_idx,
+                                  out, *, out_blocks=None, lse=None, q_idx=None, out_score=None,
+                                  scale: float = 0.0, three_calls: bool = False) -> int:
+    d = _hier_desc(q, w, k_idx, centroids, k, v, block, out_blocks, out_idx, out, lse, q_idx, out_score,
+                   scale, three_calls)
+    d.n_blocks_kept = n_blocks_kept
+    return int(_lib().lsa_hier_step_workspace_bytes(_c.byref(d)))
+
+
+def lsa_hier_step_path(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept: int, out_idx, out,
+                       **kw) -> str:
+    """'listed' or 'three_calls': how the step runs its fine stage."""
+    d = _hier_desc(q, w, k_idx, centroids, k, v, block, kw.get("out_blocks"), out_idx, out, kw.get("lse"),
+                   kw.get("q_idx"), kw.get("out_score"), kw.get("scale", 0.0), kw.get("three_calls", False))
+    d.n_blocks_kept = n_blocks_kept
+    code = int(_lib().lsa_hier_step_path(_c.byref(d)))
+    if code < 0:
+        raise ValueError("lsa_hier_step_path: invalid descriptor")
+    return STEP_PATHS[code]

@@ -180,9 +180,12 @@ class HierarchicalPlan:
     (sequence, KV head), B_coarse kept blocks of `block` tokens, top-B."""
 
     def __init__(self, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int, block: int,
-                 B_coarse: int, device="cuda", kv_dtype=torch.bfloat16, kidx_dtype=None):
+                 B_coarse: int, device="cuda", kv_dtype=torch.bfloat16, kidx_dtype=None,
+                 fused: bool = True, three_calls: bool = False):
         self.N, self.Hq, self.Hkv, self.T, self.d, self.r = N, Hq, Hkv, T, d, r
         self.B, self.block, self.B_coarse = B, block, B_coarse
+        self.fused, self.three_calls = fused, three_calls
+        self.step_ws = None
         self.n_blocks = (T + block - 1) // block
         f32 = dict(dtype=torch.float32, device=device)
         self.q_idx = torch.empty(N, Hkv, r, **f32)
@@ -194,8 +197,10 @@ class HierarchicalPlan:
         self.idx_scores = torch.empty(N, Hkv, B, **f32)
         self.out = torch.empty(N, Hq, d, **f32)
         self.lse = torch.empty(N, Hq, **f32)
-        need = lsa.attention_workspace_bytes_for(N, Hq, Hkv, d, B, T, _code(kv_dtype))
+        # the attention merges its splits in its own launch (zeroed control words)
+        need = lsa.attention_workspace_bytes_for(N, Hq, Hkv, d, B, T, _code(kv_dtype), merge_in_launch=True)
         self.attn_ws = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+        self.attn_ctrl = torch.zeros(lsa.ATTN_MERGE_CTRL_WORDS, dtype=torch.int32, device=device)
         code = _code(kv_dtype if kidx_dtype is None else kidx_dtype)
         self.hc_count, self.hint_k = lsa.score_hint_layout_for(N, Hkv, self.n_blocks, r, code)
         self.hf_count, _ = lsa.score_hint_layout_for(N, Hkv, self.n_fine, r, code)
@@ -206,7 +211,25 @@ class HierarchicalPlan:
         self.ws_f = _select_ws(self.fine, B, self.idx, device, cand=self.blocks, cand_block=block,
                                n_positions=T, hint=self.hint_f, hint_k=self.hint_k)
 
+    def step(self, q, w, k_idx, centroids, k, v, stream=None):
+        """The whole step through one lsa_hier_decode_step call."""
+        kw = dict(out_blocks=self.blocks, lse=self.lse, q_idx=self.q_idx, out_score=self.idx_scores,
+                  three_calls=self.three_calls)
+        if self.step_ws is None:
+            need = lsa.lsa_hier_step_workspace_bytes(q, w, k_idx, centroids, k, v, self.block, self.B_coarse,
+                                                     self.idx, self.out, **kw)
+            self.step_ws = torch.zeros(max(need, 16), dtype=torch.uint8, device=q.device)
+        lsa.lsa_hier_decode_step(q, w, k_idx, centroids, k, v, self.block, self.B_coarse, self.idx, self.out,
+                                 workspace=self.step_ws, stream=stream, **kw)
+
+    def path(self, q, w, k_idx, centroids, k, v) -> str:
+        return lsa.lsa_hier_step_path(q, w, k_idx, centroids, k, v, self.block, self.B_coarse, self.idx,
+                                      self.out, out_blocks=self.blocks, three_calls=self.three_calls)
+
     def run(self, q, w, k_idx, centroids, k, v, stream=None):
+        if self.fused:
+            self.step(q, w, k_idx, centroids, k, v, stream)
+            return self
         # coarse: score every block summary, keep the top B_coarse blocks
         lsa.lsa_index_score(centroids, self.coarse, q=q, w=w, q_idx=self.q_idx, hint=self.hint_c,
                             stream=stream)
@@ -220,7 +243,7 @@ class HierarchicalPlan:
                             hint=self.hint_f, hint_k=self.hint_k, workspace=self.ws_f,
                             stream=stream)
         lsa.lsa_indexed_attention(q, k, v, self.idx, self.out, lse=self.lse,
-                                  workspace=self.attn_ws, stream=stream)
+                                  workspace=self.attn_ws, stream=stream, merge_ctrl=self.attn_ctrl)
         return self
 
 

@@ -837,6 +837,42 @@ def test_decode_step_listed_rescored_rows(name, over, kdt):
         np.testing.assert_array_equal(gi[0, g], np.arange(case.B))
 
 
+@pytest.mark.parametrize("N,Hq,Hkv,T,B", [(1, 32, 8, 50000, 2048), (4, 32, 8, 20000, 1024), (2, 32, 4, 9000, 1500),
+                                        (3, 12, 3, 30000, 256)])
+def test_attention_merge_in_launch(N, Hq, Hkv, T, B):
+    """lsa_indexed_attention with merge_ctrl (the split partials merged in
+    the attention launch) against the same call without it (the merge
+    kernel): out and lse bit for bit, twice on the same control words,
+    which are left zero; and the no-allocation entry with the same words."""
+    case = synth.make_decode_case(N=N, Hq=Hq, Hkv=Hkv, T=T, B=B, dtype=synth.BF16, seed=77)
+    say("attention, merge in launch", N, Hq, Hkv, T, B)
+    Q, K, V = dev(case.Q), dev(case.K), dev(case.V)
+    rng = np.random.default_rng(5)
+    idx = np.sort(np.stack([np.stack([rng.choice(T, B, replace=False) for _ in range(Hkv)]) for _ in range(N)]),
+                  axis=-1).astype(np.int32)
+    idx_d = dev(idx)
+    out0 = torch.empty(N, Hq, case.d, device="cuda")
+    lse0 = torch.empty(N, Hq, device="cuda")
+    lsa.lsa_indexed_attention(Q, K, V, idx_d, out0, lse=lse0)
+    ctrl = torch.zeros(lsa.ATTN_MERGE_CTRL_WORDS, dtype=torch.int32, device="cuda")
+    for rep in range(2):
+        out1 = torch.full_like(out0, 3.0)
+        lse1 = torch.full_like(lse0, 3.0)
+        lsa.lsa_indexed_attention(Q, K, V, idx_d, out1, lse=lse1, merge_ctrl=ctrl)
+        torch.cuda.synchronize()
+        assert torch.equal(out1.view(torch.int32), out0.view(torch.int32)), rep
+        assert torch.equal(lse1.view(torch.int32), lse0.view(torch.int32)), rep
+        assert int(ctrl.abs().sum().item()) == 0, rep
+    out2 = torch.full_like(out0, 3.0)
+    lsa.lsa_indexed_attention_noalloc(Q, K, V, idx_d, out2, lse=lse1, merge_ctrl=ctrl)
+    torch.cuda.synchronize()
+    assert torch.equal(out2.view(torch.int32), out0.view(torch.int32))
+    assert int(ctrl.abs().sum().item()) == 0
+    o, l = oracle.attention(case.Q, case.K, case.V, idx)
+    np.testing.assert_allclose(host(out1), o, rtol=0, atol=ATTN_ATOL)
+    np.testing.assert_allclose(host(lse1), l, rtol=0, atol=LSE_ATOL)
+
+
 def test_decode_step_parts_equal_one_call():
     """lsa_decode_step_part: the score, select and attend parts issued one
     at a time (the score part twice, as a timing loop does) equal one
@@ -1479,7 +1515,7 @@ def test_hierarchical_decode(T):
     cd = torch.empty(N, Hkv, T // blk, r, dtype=torch.bfloat16, device="cuda")
     lsa.lsa_build_centroids(kd, blk, cd)
     np.testing.assert_array_equal(host(cd), cent)
-    plan = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc)
+    plan = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, fused=False)   # the five calls
     plan.run(Qd, Wd, kd, cd, Kd, Vd)
     torch.cuda.synchronize()
     qi = oracle.query_prep(case.Q, Hkv, case.W)
@@ -1611,3 +1647,49 @@ def test_decode_step_fp8_cache(name, over):
     rows = list(range(case.N * case.Hkv))
     ref = _oracle_rows(case, rows, kidx_dtype=oracle.FP8)
     _compare_step(case, g, ref, rows)
+
+
+@pytest.mark.parametrize("T,ties", [(131072, False), (1048576, False), (100000, False), (131072, True)])
+def test_hier_step_equals_separate_calls(T, ties):
+    """lsa_hier_decode_step (the fine stage listed in its scoring launch,
+    and with LSA_STEP_THREE_CALLS) against the five separate calls:
+    kept blocks, indices, per-entry scores, q_idx, out and lse bit for bit,
+    twice on one workspace whose control words are left zero. T=100000 has
+    a partial last block; with every key of a head equal every fine row
+    ties throughout, so its lists overflow and the select rescores the row
+    through the candidate map."""
+    from indexer_driven_sparse_amd import pipeline
+    case = synth.workload("hier_t1m", T=T)
+    say("hierarchical step vs separate calls", T, ties)
+    N, Hq, Hkv, d, r, B, blk, Bc = case.N, case.Hq, case.Hkv, case.d, case.r, case.B, case.block, case.B_coarse
+    Qd, Wd, Vd = dev(case.Q), dev(case.W), dev(case.V)
+    Kd = dev(case.K)
+    if ties:
+        Kd = Kd[:, :1].expand(N, T, Hkv, d).contiguous()
+    kd = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_project_keys(Kd, Wd, kd)
+    nb = (T + blk - 1) // blk
+    cd = torch.empty(N, Hkv, nb, r, dtype=torch.bfloat16, device="cuda")
+    lsa.lsa_build_centroids(kd, blk, cd)
+    ref = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, fused=False)
+    ref.run(Qd, Wd, kd, cd, Kd, Vd)
+    for three in (False, True):
+        one = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, three_calls=three)
+        assert one.path(Qd, Wd, kd, cd, Kd, Vd) == ("three_calls" if three else "listed")
+        for rep in range(2):
+            one.idx.fill_(-9)
+            one.out.fill_(5.0)
+            one.run(Qd, Wd, kd, cd, Kd, Vd)
+            torch.cuda.synchronize()
+            for name_ in ("blocks", "idx", "idx_scores", "q_idx", "out", "lse"):
+                a_, b_ = getattr(one, name_), getattr(ref, name_)
+                assert torch.equal(a_.view(torch.int32), b_.view(torch.int32)), (three, rep, name_)
+            rows = N * Hkv
+            ctl = one.step_ws[:4 * (1024 + 1024 * rows)].view(torch.int32)
+            assert int(ctl.abs().sum().item()) == 0, (three, rep)
+    if ties:   # a tie over the whole row keeps the lowest positions of the kept blocks
+        gi, gb = host(one.idx), host(one.blocks)
+        for g in range(Hkv):
+            pos = np.sort((gb[0, g][:, None] * blk + np.arange(blk)[None, :]).reshape(-1))
+            pos = pos[pos < T]
+            np.testing.assert_array_equal(gi[0, g], pos[:B])
