@@ -773,8 +773,8 @@ def lsa_build_centroids(k_idx: torch.Tensor, block: int, out: torch.Tensor, *, s
     _check("lsa_build_centroids", _lib().lsa_build_centroids(_c.byref(d), _stream(stream)))
 
 
-def _hier_desc(q, w, k_idx, centroids, k, v, block, out_blocks, out_idx, out, lse, q_idx, out_score,
-               scale, three_calls):
+def _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, out_blocks, out_idx, out, lse, q_idx,
+               out_score, scale, three_calls):
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be contiguous [N,Hq,d]")
     N, Hq, hd = q.shape
@@ -793,10 +793,8 @@ def _hier_desc(q, w, k_idx, centroids, k, v, block, out_blocks, out_idx, out, ls
             or (w.dim() == 3 and w.shape[0] != Hkv):
         raise ValueError("w must be contiguous float32 [d,r] or [Hkv,d,r]")
     B = out_idx.shape[-1]
-    Bc = out_blocks.shape[-1] if out_blocks is not None else None
     _need(out_idx, "out_idx", torch.int32, (N, Hkv, B))
-    if out_blocks is not None:
-        _need(out_blocks, "out_blocks", torch.int32, (N, Hkv, Bc))
+    _need(out_blocks, "out_blocks", torch.int32, (N, Hkv, n_blocks_kept))
     _need(out, "out", torch.float32, (N, Hq, hd))
     _need(lse, "lse", torch.float32, (N, Hq))
     _need(q_idx, "q_idx", torch.float32, (N, Hkv, r))
@@ -804,7 +802,7 @@ def _hier_desc(q, w, k_idx, centroids, k, v, block, out_blocks, out_idx, out, ls
     d = HierStepDesc()
     d.struct_size = _c.sizeof(HierStepDesc)
     d.n_seq, d.n_q_heads, d.n_kv_heads, d.head_dim, d.rank, d.n_keys, d.topk = N, Hq, Hkv, hd, r, T, B
-    d.block = block
+    d.block, d.n_blocks_kept = block, n_blocks_kept
     d.q, d.q_dtype = _ptr(q), _dt(q)
     d.w, d.w_per_head = _ptr(w), 1 if w.dim() == 3 else 0
     d.k_idx, d.k_idx_dtype = _ptr(k_idx), _dt(k_idx)
@@ -830,9 +828,8 @@ def lsa_hier_decode_step(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept
     lsa_hier_step_workspace_bytes, all zero before its first use (allocated
     zeroed here when not given). three_calls: the fine stage as the
     separate scoring and select calls."""
-    d = _hier_desc(q, w, k_idx, centroids, k, v, block, out_blocks, out_idx, out, lse, q_idx, out_score,
-                   scale, three_calls)
-    d.n_blocks_kept = n_blocks_kept
+    d = _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, out_blocks, out_idx, out, lse, q_idx,
+                   out_score, scale, three_calls)
     lib = _lib()
     need = lib.lsa_hier_step_workspace_bytes(_c.byref(d))
     if need == 0:
@@ -846,18 +843,17 @@ def lsa_hier_decode_step(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept
 def lsa_hier_step_workspace_bytes(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept: int, out_idx,
                                   out, *, out_blocks=None, lse=None, q_idx=None, out_score=None,
                                   scale: float = 0.0, three_calls: bool = False) -> int:
-    d = _hier_desc(q, w, k_idx, centroids, k, v, block, out_blocks, out_idx, out, lse, q_idx, out_score,
-                   scale, three_calls)
-    d.n_blocks_kept = n_blocks_kept
+    d = _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, out_blocks, out_idx, out, lse, q_idx,
+                   out_score, scale, three_calls)
     return int(_lib().lsa_hier_step_workspace_bytes(_c.byref(d)))
 
 
 def lsa_hier_step_path(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept: int, out_idx, out,
                        **kw) -> str:
     """'listed' or 'three_calls': how the step runs its fine stage."""
-    d = _hier_desc(q, w, k_idx, centroids, k, v, block, kw.get("out_blocks"), out_idx, out, kw.get("lse"),
-                   kw.get("q_idx"), kw.get("out_score"), kw.get("scale", 0.0), kw.get("three_calls", False))
-    d.n_blocks_kept = n_blocks_kept
+    d = _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, kw.get("out_blocks"), out_idx, out,
+                   kw.get("lse"), kw.get("q_idx"), kw.get("out_score"), kw.get("scale", 0.0),
+                   kw.get("three_calls", False))
     code = int(_lib().lsa_hier_step_path(_c.byref(d)))
     if code < 0:
         raise ValueError("lsa_hier_step_path: invalid descriptor")

@@ -519,3 +519,50 @@ def test_step_parts_argument_checks():
         assert lib.lsa_decode_step_part(ctypes.byref(d_), parts, ws.data_ptr(), 16, None) == -1   # LSA_ERR_INVALID_ARG
     d_ = lsa._step_desc(q, w, kd, k, k, idx, out, None, None, None, 0.0, True)
     assert lib.lsa_decode_step_part(ctypes.byref(d_), 1, ws.data_ptr(), 16, None) == -2   # LSA_ERR_UNSUPPORTED
+
+
+def test_binding_rejects_bad_hierarchical_step_buffers():
+    """lsa_hier_decode_step's descriptor: every output the step writes is
+    checked for dtype, contiguity and exact shape (out_blocks against
+    n_blocks_kept), and the inputs against one another, before any call."""
+    import torch
+    N, Hq, Hkv, T, d, r, B, blk, Bc = 1, 8, 2, 1024, 128, 64, 64, 64, 4
+    nb = T // blk
+    q = torch.zeros(N, Hq, d, dtype=torch.bfloat16)
+    w = torch.zeros(d, r)
+    kx = torch.zeros(N, Hkv, T, r, dtype=torch.bfloat16)
+    cent = torch.zeros(N, Hkv, nb, r, dtype=torch.bfloat16)
+    k = torch.zeros(N, T, Hkv, d, dtype=torch.bfloat16)
+    good = dict(q=q, w=w, k_idx=kx, centroids=cent, k=k, v=k.clone(), n_blocks_kept=Bc,
+                out_blocks=torch.zeros(N, Hkv, Bc, dtype=torch.int32),
+                out_idx=torch.zeros(N, Hkv, B, dtype=torch.int32), out=torch.zeros(N, Hq, d),
+                lse=torch.zeros(N, Hq), q_idx=torch.zeros(N, Hkv, r), out_score=torch.zeros(N, Hkv, B))
+
+    def build(kw):
+        return lsa._hier_desc(kw["q"], kw["w"], kw["k_idx"], kw["centroids"], kw["k"], kw["v"], blk,
+                              kw["n_blocks_kept"], kw["out_blocks"], kw["out_idx"], kw["out"], kw["lse"],
+                              kw["q_idx"], kw["out_score"], 0.0, False)
+
+    d0 = build(good)   # the good case builds
+    assert (d0.n_keys, d0.topk, d0.block, d0.n_blocks_kept) == (T, B, blk, Bc)
+    bad = [
+        dict(out_blocks=torch.zeros(N, Hkv, Bc - 1, dtype=torch.int32)),   # fewer slots than blocks kept
+        dict(n_blocks_kept=Bc + 1),                                         # the same, the other way
+        dict(out_blocks=torch.zeros(N, Hkv, Bc, dtype=torch.int64)),
+        dict(out_idx=torch.zeros(N, Hkv, B, dtype=torch.int64)),
+        dict(out=torch.zeros(N, Hq, d, dtype=torch.bfloat16)),              # kernels write fp32
+        dict(lse=torch.zeros(N, Hq + 1)),
+        dict(q_idx=torch.zeros(N, Hkv, r, dtype=torch.bfloat16)),
+        dict(out_score=torch.zeros(N, Hkv, B - 1)),
+        dict(centroids=torch.zeros(N, Hkv, nb - 1, r, dtype=torch.bfloat16)),   # a block short
+        dict(centroids=torch.zeros(N, Hkv, nb, r, dtype=torch.float32)),        # not k_idx's dtype
+        dict(v=torch.zeros(N, T, Hkv, d, dtype=torch.float32)),                  # k and v differ
+        dict(w=torch.zeros(d, r, dtype=torch.float64)),
+        dict(k=torch.zeros(N, T, Hkv, 64, dtype=torch.bfloat16),
+             v=torch.zeros(N, T, Hkv, 64, dtype=torch.bfloat16)),              # head dim differs from q
+    ]
+    for over in bad:
+        kw = dict(good)
+        kw.update(over)
+        with pytest.raises(ValueError):
+            build(kw)
