@@ -1649,32 +1649,36 @@ def test_decode_step_fp8_cache(name, over):
     _compare_step(case, g, ref, rows)
 
 
-@pytest.mark.parametrize("T,ties", [(131072, False), (1048576, False), (100000, False), (131072, True)])
-def test_hier_step_equals_separate_calls(T, ties):
+@pytest.mark.parametrize("T,ties,kdt", [(131072, False, torch.bfloat16), (1048576, False, torch.bfloat16),
+                                         (100000, False, torch.bfloat16), (131072, True, torch.bfloat16),
+                                         (131072, False, torch.float8_e4m3fn),
+                                         (100000, True, torch.float8_e4m3fn)])
+def test_hier_step_equals_separate_calls(T, ties, kdt):
     """lsa_hier_decode_step (the fine stage listed in its scoring launch,
     and with LSA_STEP_THREE_CALLS) against the five separate calls:
     kept blocks, indices, per-entry scores, q_idx, out and lse bit for bit,
     twice on one workspace whose control words are left zero. T=100000 has
     a partial last block; with every key of a head equal every fine row
     ties throughout, so its lists overflow and the select rescores the row
-    through the candidate map."""
+    through the candidate map. The fp8 cases run the E4M3 projected-key
+    cache (block summaries in E4M3 as well)."""
     from indexer_driven_sparse_amd import pipeline
     case = synth.workload("hier_t1m", T=T)
-    say("hierarchical step vs separate calls", T, ties)
+    say("hierarchical step vs separate calls", T, ties, kdt)
     N, Hq, Hkv, d, r, B, blk, Bc = case.N, case.Hq, case.Hkv, case.d, case.r, case.B, case.block, case.B_coarse
     Qd, Wd, Vd = dev(case.Q), dev(case.W), dev(case.V)
     Kd = dev(case.K)
     if ties:
         Kd = Kd[:, :1].expand(N, T, Hkv, d).contiguous()
-    kd = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+    kd = torch.empty(N, Hkv, T, r, dtype=kdt, device="cuda")
     lsa.lsa_project_keys(Kd, Wd, kd)
     nb = (T + blk - 1) // blk
-    cd = torch.empty(N, Hkv, nb, r, dtype=torch.bfloat16, device="cuda")
+    cd = torch.empty(N, Hkv, nb, r, dtype=kdt, device="cuda")
     lsa.lsa_build_centroids(kd, blk, cd)
-    ref = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, fused=False)
+    ref = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, fused=False, kidx_dtype=kdt)
     ref.run(Qd, Wd, kd, cd, Kd, Vd)
     for three in (False, True):
-        one = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, three_calls=three)
+        one = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, three_calls=three, kidx_dtype=kdt)
         assert one.path(Qd, Wd, kd, cd, Kd, Vd) == ("three_calls" if three else "listed")
         for rep in range(2):
             one.idx.fill_(-9)
