@@ -1697,3 +1697,50 @@ def test_hier_step_equals_separate_calls(T, ties, kdt):
             pos = np.sort((gb[0, g][:, None] * blk + np.arange(blk)[None, :]).reshape(-1))
             pos = pos[pos < T]
             np.testing.assert_array_equal(gi[0, g], pos[:B])
+
+
+def test_hier_step_graph_replay():
+    """The one-call hierarchical step captured in HIP graphs (two caches,
+    alternating): every replay, with eager work and synchronizations between
+    replays, equals the eager call bit for bit, and the workspace's control
+    words come back zero each time."""
+    from indexer_driven_sparse_amd import pipeline
+    case = synth.workload("hier_t1m", T=131072)
+    say("hierarchical step, graph replay")
+    N, Hq, Hkv, T, d, r, B, blk, Bc = case.N, case.Hq, case.Hkv, case.T, case.d, case.r, case.B, case.block, \
+        case.B_coarse
+    Qd, Wd, Vd = dev(case.Q), dev(case.W), dev(case.V)
+    K0 = dev(case.K)
+    caches = []
+    for s in (0, 1):
+        Kc = K0 if s == 0 else torch.roll(K0, shifts=4099, dims=1).contiguous()
+        kd = torch.empty(N, Hkv, T, r, dtype=torch.bfloat16, device="cuda")
+        lsa.lsa_project_keys(Kc, Wd, kd)
+        cd = torch.empty(N, Hkv, T // blk, r, dtype=torch.bfloat16, device="cuda")
+        lsa.lsa_build_centroids(kd, blk, cd)
+        caches.append((Kc, kd, cd))
+    plan = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc)
+    names = ("blocks", "idx", "idx_scores", "q_idx", "out", "lse")
+    want = []
+    for Kc, kd, cd in caches:
+        plan.run(Qd, Wd, kd, cd, Kc, Vd)
+        torch.cuda.synchronize()
+        want.append({k: getattr(plan, k).clone() for k in names})
+    assert not torch.equal(want[0]["idx"], want[1]["idx"])   # the two caches select differently
+    graphs = []
+    for Kc, kd, cd in caches:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            plan.run(Qd, Wd, kd, cd, Kc, Vd)
+        graphs.append(g)
+    rows = N * Hkv
+    for i in range(6):
+        for t in (plan.idx, plan.out, plan.lse):   # eager work between replays
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        graphs[i % 2].replay()
+        torch.cuda.synchronize()
+        for k in names:
+            assert torch.equal(getattr(plan, k).view(torch.int32), want[i % 2][k].view(torch.int32)), (i, k)
+        ctl = plan.step_ws[:4 * (1024 + 1024 * rows)].view(torch.int32)
+        assert int(ctl.abs().sum().item()) == 0, i
