@@ -406,42 +406,49 @@ __global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, co
   }
   for (int t = t_first; t * kT < kend; t += kStep) {
     const int j0 = t * kT;
-    f32x16 acc[4];
+    // the tile's four row blocks in two halves of two: two accumulators
+    // live instead of four (a third wave per SIMD fits in the registers);
+    // the next tile's loads go out after the last products
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[b] = tile_scores(ka, qb[b]);
-    if ((t + kStep) * kT < kend) {
-      const uint16_t* kp = krow(a, g, min(j0 + kStep * kT + n, a.L - 1));
+    for (int hb = 0; hb < 2; ++hb) {
+      f32x16 acc[2];
 #pragma unroll
-      for (int ch = 0; ch < kCh; ++ch) ka[ch] = frag(kp, ch, h);
-    }
+      for (int bb = 0; bb < 2; ++bb) acc[bb] = tile_scores(ka, qb[2 * hb + bb]);
+      if (hb == 1 && (t + kStep) * kT < kend) {
+        const uint16_t* kp = krow(a, g, min(j0 + kStep * kT + n, a.L - 1));
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const int qlo = r0 + kT * b;
-      if (j0 > qlo + kT - 1) continue;            // above every row's diagonal
-      const int i = qlo + n;
-      uint32_t flags = 0;
-      if (j0 + kT - 1 <= qlo) {                   // the whole tile is causal for every row
-#pragma unroll
-        for (int v = 0; v < 16; ++v) flags |= (uint32_t)(acc[b][v] >= tq[b]) << v;
-      } else {
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          flags |= (uint32_t)(acc[b][v] >= tq[b] && j0 + tile_key(v, h) <= i) << v;
+        for (int ch = 0; ch < kCh; ++ch) ka[ch] = frag(kp, ch, h);
       }
-      if (__ballot(flags != 0)) {
-        int pos = 0;
-        if (flags) pos = atomicAdd(&rcnt[kT * b + n], __popc(flags));
-        float4* st = reinterpret_cast<float4*>(&stash[w][lane][0]);
-        st[0] = make_float4(acc[b][0], acc[b][1], acc[b][2], acc[b][3]);
-        st[1] = make_float4(acc[b][4], acc[b][5], acc[b][6], acc[b][7]);
-        st[2] = make_float4(acc[b][8], acc[b][9], acc[b][10], acc[b][11]);
-        st[3] = make_float4(acc[b][12], acc[b][13], acc[b][14], acc[b][15]);
-        while (flags) {
-          const int v = __ffs(flags) - 1;
-          flags &= flags - 1;
-          if (pos < kSubCap)
-            list[b][pos] = make_int2(__float_as_int(stash[w][lane][v]), j0 + tile_key(v, h));
-          ++pos;
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const int b = 2 * hb + bb;
+        const int qlo = r0 + kT * b;
+        if (j0 > qlo + kT - 1) continue;            // above every row's diagonal
+        const int i = qlo + n;
+        uint32_t flags = 0;
+        if (j0 + kT - 1 <= qlo) {                   // the whole tile is causal for every row
+#pragma unroll
+          for (int v = 0; v < 16; ++v) flags |= (uint32_t)(acc[bb][v] >= tq[b]) << v;
+        } else {
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            flags |= (uint32_t)(acc[bb][v] >= tq[b] && j0 + tile_key(v, h) <= i) << v;
+        }
+        if (__ballot(flags != 0)) {
+          int pos = 0;
+          if (flags) pos = atomicAdd(&rcnt[kT * b + n], __popc(flags));
+          float4* st = reinterpret_cast<float4*>(&stash[w][lane][0]);
+          st[0] = make_float4(acc[bb][0], acc[bb][1], acc[bb][2], acc[bb][3]);
+          st[1] = make_float4(acc[bb][4], acc[bb][5], acc[bb][6], acc[bb][7]);
+          st[2] = make_float4(acc[bb][8], acc[bb][9], acc[bb][10], acc[bb][11]);
+          st[3] = make_float4(acc[bb][12], acc[bb][13], acc[bb][14], acc[bb][15]);
+          while (flags) {
+            const int v = __ffs(flags) - 1;
+            flags &= flags - 1;
+            if (pos < kSubCap)
+              list[b][pos] = make_int2(__float_as_int(stash[w][lane][v]), j0 + tile_key(v, h));
+            ++pos;
+          }
         }
       }
     }
