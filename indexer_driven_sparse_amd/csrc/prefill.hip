@@ -391,8 +391,9 @@ __global__ __launch_bounds__(256) void prefill_cand_kernel(PrefillTopkArgs a, co
     list[b] = cand + ((int64_t)min(i, a.L - 1) * a.Hkv + g) * kCandCap + split * kSubCap;
   }
   __syncthreads();
-  // Per tile: the four row blocks' MFMAs first (one wait for the tile's
-  // loads), then the next tile's loads, then the epilogues. Each row has
+  // Per tile: two row blocks' MFMAs, their epilogues, then the other two
+  // blocks' MFMAs (after which the next tile's key loads go out) and their
+  // epilogues. Each row has
   // one list; a lane reserves room for its candidates of the tile with one
   // LDS atomic and writes them as a contiguous run, so every row's list
   // grows at a single tail and the stores combine into full lines in L2.
