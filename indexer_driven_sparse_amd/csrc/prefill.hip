@@ -194,8 +194,11 @@ __global__ __launch_bounds__(kRank) void block_query_kernel(const uint16_t* q_id
 // ---------------------------------------------------------------------------
 // sample: per-row threshold tau
 // ---------------------------------------------------------------------------
+// The histograms of two rows share words (row 2p in the low half of row
+// p's words, row 2p + 1 in the high half): a count never exceeds
+// kSampleMax < 2^16, and the halved size lets four workgroups share a CU.
 struct SampleShared {
-  uint32_t hist[kT][kHistLd];
+  uint32_t hist[kT / 2][kHistLd];
   int pos[kSampleMax];   // the block's sample positions, increasing
   int nvalid[kT];
   int target[kT];   // sample keys that should reach tau (0: no threshold)
@@ -218,8 +221,10 @@ __device__ __forceinline__ int sample_pos(int k, int m, int nb) {
 __device__ __forceinline__ void sample_find(SampleShared& sh, const int* tgts, int* bin_out) {
   const int tid = threadIdx.x, row = tid >> 3, part = tid & 7;
   const int tgt = tgts[row];
+  const uint32_t* hr = sh.hist[row >> 1];
+  const int sh16 = 16 * (row & 1);
   int c = 0;
-  for (int q = 0; q < 32; ++q) c += (int)sh.hist[row][255 - 32 * part - q];
+  for (int q = 0; q < 32; ++q) c += (int)((hr[255 - 32 * part - q] >> sh16) & 0xffffu);
   int incl = c;
 #pragma unroll
   for (int o = 1; o < 8; o <<= 1) {
@@ -230,7 +235,7 @@ __device__ __forceinline__ void sample_find(SampleShared& sh, const int* tgts, i
   if (tgt > 0 && acc < tgt && tgt <= incl) {
     for (int q = 0; q < 32; ++q) {
       const int b = 255 - 32 * part - q;
-      const int hb = (int)sh.hist[row][b];
+      const int hb = (int)((hr[b] >> sh16) & 0xffffu);
       if (acc + hb >= tgt) {
         bin_out[row] = b;
         sh.need2[row] = tgt - acc;
@@ -241,7 +246,9 @@ __device__ __forceinline__ void sample_find(SampleShared& sh, const int* tgts, i
   }
 }
 
-__global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, float* tau,
+// at most 128 VGPRs: with the shared histogram words (33 KiB of LDS) four
+// workgroups fit per CU, so more of the sample's gathers are in flight
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void prefill_sample_kernel(PrefillTopkArgs a, float* tau,
                                                              int* redo) {
   __shared__ SampleShared sh;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, n = lane & 31;
@@ -263,7 +270,7 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
 #pragma unroll
     for (int c = 0; c < kCh; ++c) qb[c] = frag(qp, c, h);
   }
-  for (int q = tid; q < kT * kHistLd; q += 256) (&sh.hist[0][0])[q] = 0u;
+  for (int q = tid; q < kT / 2 * kHistLd; q += 256) (&sh.hist[0][0])[q] = 0u;
   for (int q = tid; q < m; q += 256) sh.pos[q] = sample_pos(q, m, nb);
   if (tid < kT) {
     sh.nvalid[tid] = 0;
@@ -276,7 +283,8 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
   // per-score checks; the order key here ignores the NaN and -0 cases,
   // which can only move tau (speed), never a result.
   const bool rows_in = i0 + kT <= a.L;
-  uint32_t* hrow = &sh.hist[n][0];
+  uint32_t* hrow = &sh.hist[n >> 1][0];
+  const uint32_t one = 1u << (16 * (n & 1));   // this row's half of the shared words
   for (int pass = 0; pass < 2; ++pass) {
     int nval = 0;
     const uint32_t b1 = pass ? (uint32_t)sh.bin1[n] : 0u;
@@ -302,8 +310,8 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
         for (int v = 0; v < 16; ++v) {
           const uint32_t u = __float_as_uint(acc[v]);
           const uint32_t key = u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
-          if (pass == 0) atomicAdd(&hrow[key >> 24], 1u);
-          else if ((key >> 24) == b1) atomicAdd(&hrow[(key >> 16) & 255u], 1u);
+          if (pass == 0) atomicAdd(&hrow[key >> 24], one);
+          else if ((key >> 24) == b1) atomicAdd(&hrow[(key >> 16) & 255u], one);
         }
         nval += 16;
       } else {
@@ -314,10 +322,10 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
             const uint32_t u = __float_as_uint(acc[v]);
             const uint32_t key = u ^ ((uint32_t)((int)u >> 31) | 0x80000000u);
             if (pass == 0) {
-              atomicAdd(&hrow[key >> 24], 1u);
+              atomicAdd(&hrow[key >> 24], one);
               ++nval;
             } else if ((key >> 24) == b1) {
-              atomicAdd(&hrow[(key >> 16) & 255u], 1u);
+              atomicAdd(&hrow[(key >> 16) & 255u], one);
             }
           }
         }
@@ -344,7 +352,7 @@ __global__ __launch_bounds__(256) void prefill_sample_kernel(PrefillTopkArgs a, 
     else sample_find(sh, sh.need2, sh.bin2);
     __syncthreads();
     if (pass == 0) {
-      for (int q = tid; q < kT * kHistLd; q += 256) (&sh.hist[0][0])[q] = 0u;
+      for (int q = tid; q < kT / 2 * kHistLd; q += 256) (&sh.hist[0][0])[q] = 0u;
       __syncthreads();
     }
   }
