@@ -1649,11 +1649,12 @@ def test_decode_step_fp8_cache(name, over):
     _compare_step(case, g, ref, rows)
 
 
-@pytest.mark.parametrize("T,ties,kdt", [(131072, False, torch.bfloat16), (1048576, False, torch.bfloat16),
-                                         (100000, False, torch.bfloat16), (131072, True, torch.bfloat16),
-                                         (131072, False, torch.float8_e4m3fn),
-                                         (100000, True, torch.float8_e4m3fn)])
-def test_hier_step_equals_separate_calls(T, ties, kdt):
+@pytest.mark.parametrize("T,ties,kdt,N", [(131072, False, torch.bfloat16, 1), (1048576, False, torch.bfloat16, 1),
+                                           (100000, False, torch.bfloat16, 1), (131072, True, torch.bfloat16, 1),
+                                           (131072, False, torch.float8_e4m3fn, 1),
+                                           (100000, True, torch.float8_e4m3fn, 1),
+                                           (60000, False, torch.bfloat16, 3)])
+def test_hier_step_equals_separate_calls(T, ties, kdt, N):
     """lsa_hier_decode_step (the fine stage listed in its scoring launch,
     and with LSA_STEP_THREE_CALLS) against the five separate calls:
     kept blocks, indices, per-entry scores, q_idx, out and lse bit for bit,
@@ -1661,10 +1662,10 @@ def test_hier_step_equals_separate_calls(T, ties, kdt):
     a partial last block; with every key of a head equal every fine row
     ties throughout, so its lists overflow and the select rescores the row
     through the candidate map. The fp8 cases run the E4M3 projected-key
-    cache (block summaries in E4M3 as well)."""
+    cache (block summaries in E4M3 as well); N=3 runs several sequences."""
     from indexer_driven_sparse_amd import pipeline
-    case = synth.workload("hier_t1m", T=T)
-    say("hierarchical step vs separate calls", T, ties, kdt)
+    case = synth.workload("hier_t1m", T=T, N=N)
+    say("hierarchical step vs separate calls", T, ties, kdt, N)
     N, Hq, Hkv, d, r, B, blk, Bc = case.N, case.Hq, case.Hkv, case.d, case.r, case.B, case.block, case.B_coarse
     Qd, Wd, Vd = dev(case.Q), dev(case.W), dev(case.V)
     Kd = dev(case.K)
