@@ -759,13 +759,20 @@ __device__ __forceinline__ void redo_row_scores(const PrefillTopkArgs& a, int ro
   }
 }
 
-constexpr int kRedoSlices = 16;   // workgroups per redo row (16 waves each)
+constexpr int kRedoSlices = 16;      // workgroups per redo row when all kRedoBlocks rows are listed
+constexpr int kRedoSlicesMax = 128;  // ... and at most, when few are (16 waves each)
 
+// The kRedoBlocks x kRedoSlices workgroups are shared by the listed rows:
+// S = kRedoBlocks * kRedoSlices / n per row (at most kRedoSlicesMax), so a
+// single listed row is scored by 2048 waves instead of 256.
 __global__ __launch_bounds__(1024) void prefill_redo_scores_kernel(PrefillTopkArgs a, const int* redo,
                                                                    float* scratch) {
-  const int f = blockIdx.x;
-  if (f >= redo[0]) return;
-  redo_row_scores(a, redo[1 + f], scratch + (int64_t)f * a.L, 16 * blockIdx.y, 16 * kRedoSlices);
+  const int n = min(redo[0], kRedoBlocks);
+  if (n == 0) return;
+  const int S = min(kRedoSlicesMax, kRedoBlocks * kRedoSlices / n);
+  const int f = blockIdx.x / S, slice = blockIdx.x % S;
+  if (f >= n) return;
+  redo_row_scores(a, redo[1 + f], scratch + (int64_t)f * a.L, 16 * slice, 16 * S);
 }
 
 __device__ __forceinline__ void redo_row_select(const PrefillTopkArgs& a, int row, const float* srow,
@@ -895,7 +902,7 @@ hipError_t launch_prefill_topk(const PrefillTopkArgs& a, hipStream_t s) {
   else
     hipLaunchKernelGGL(prefill_final_kernel<kFinPerMax>, dim3(rows), dim3(kFinThreads), fin_lds(a.L),
                        s, a, ws.cand, ws.cnt, ws.redo);
-  hipLaunchKernelGGL(prefill_redo_scores_kernel, dim3(kRedoBlocks, kRedoSlices), dim3(1024), 0, s, a,
+  hipLaunchKernelGGL(prefill_redo_scores_kernel, dim3(kRedoBlocks * kRedoSlices), dim3(1024), 0, s, a,
                      ws.redo, ws.scratch);
   hipLaunchKernelGGL(prefill_redo_select_kernel, dim3(kRedoBlocks), dim3(kThreads), redo_lds(a.L), s,
                      a, ws.redo, ws.scratch);
