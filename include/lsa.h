@@ -493,11 +493,15 @@ int lsa_step_path(const lsa_step_desc* desc);
  *     lsa_topk_select   (top B, the same candidate map, n_positions = T)
  *     lsa_indexed_attention
  * on the same arguments: out_blocks, out_idx, q_idx, out_score bit-identical,
- * out / lse within the attention's own rounding. By default the fine
- * scoring launch lists the final select's candidates (the listing path of
- * lsa_decode_step, over the candidate map) where the shape allows it, and
- * the attention merges its splits in its own launch; flags =
- * LSA_STEP_THREE_CALLS runs the fine stage as the two separate calls.
+ * out / lse within the attention's own rounding. The attention merges its
+ * splits in its own launch. By default the fine stage runs as the two
+ * separate calls when the kept blocks cover fewer than
+ * LSA_HIER_LIST_MIN_SLOTS slots per row (measured faster there: 57.1 against
+ * 59.0 us per step at 128 blocks of 64), and otherwise its scoring launch
+ * lists the final select's candidates (the listing path of lsa_decode_step,
+ * over the candidate map) where the shape allows it. flags =
+ * LSA_STEP_THREE_CALLS always runs the separate calls; LSA_STEP_LISTED takes
+ * the listing launch wherever the shape allows it.
  * Asynchronous on `stream`; allocates nothing; one workspace
  * (lsa_hier_step_workspace_bytes, same descriptor), all zero before its
  * first use; every call leaves its control words zero again. Two calls
@@ -529,7 +533,7 @@ typedef struct lsa_hier_step_desc {
   const void* v;             /* V cache, same strides */
   int64_t kv_stride_seq, kv_stride_tok, kv_stride_head;
   float scale;               /* <= 0: 1/sqrt(d) */
-  int32_t flags;             /* 0 or LSA_STEP_THREE_CALLS */
+  int32_t flags;             /* 0, LSA_STEP_THREE_CALLS or LSA_STEP_LISTED */
   float* q_idx;              /* optional out: fp32 [N,Hkv,r] */
   int32_t* out_blocks;       /* optional out: [N,Hkv,n_blocks_kept] ascending block numbers */
   int32_t* out_idx;          /* [N,Hkv,B] ascending positions, -1 padded */
@@ -537,6 +541,13 @@ typedef struct lsa_hier_step_desc {
   float* out;                /* fp32 [N,Hq,d] */
   float* lse;                /* optional out: fp32 [N,Hq] */
 } lsa_hier_step_desc;
+
+/* flags of lsa_hier_decode_step: the fine stage's listing launch wherever
+ * the shape allows it, whatever the row length */
+#define LSA_STEP_LISTED 4
+/* fine-stage row length (n_blocks_kept * block) from which the default
+ * path takes the listing launch */
+#define LSA_HIER_LIST_MIN_SLOTS 32768
 
 int lsa_hier_decode_step(const lsa_hier_step_desc* desc, void* workspace, size_t workspace_bytes,
                          void* stream);

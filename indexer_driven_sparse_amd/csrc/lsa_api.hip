@@ -737,7 +737,9 @@ int plan_hier(const lsa_hier_step_desc* d, HierPlan* p) {
   if (d->n_seq < 1 || d->n_kv_heads < 1 || d->n_keys < 1 || d->topk < 1 || d->block < 1 ||
       d->n_blocks_kept < 1 || !d->q || !d->centroids)
     return LSA_ERR_INVALID_ARG;
-  if (d->flags & ~LSA_STEP_THREE_CALLS) return LSA_ERR_INVALID_ARG;
+  if ((d->flags & ~(LSA_STEP_THREE_CALLS | LSA_STEP_LISTED)) ||
+      (d->flags & (LSA_STEP_THREE_CALLS | LSA_STEP_LISTED)) == (LSA_STEP_THREE_CALLS | LSA_STEP_LISTED))
+    return LSA_ERR_INVALID_ARG;
   const int64_t rows = (int64_t)d->n_seq * d->n_kv_heads;
   if (rows > 65535) return LSA_ERR_UNSUPPORTED;
   const int64_t nb = ((int64_t)d->n_keys + d->block - 1) / d->block;
@@ -846,9 +848,13 @@ int plan_hier(const lsa_hier_step_desc* d, HierPlan* p) {
   p->off_fsel = off;
   off = align256(off + p->fsel_bytes);
 
-  // the fine stage's listing launch, where the shape allows it
+  // the fine stage's listing launch, where the shape allows it: by default
+  // only for rows of at least LSA_HIER_LIST_MIN_SLOTS slots (on shorter rows
+  // the separate scoring and select calls were measured faster)
   p->listed = false;
-  if (!(d->flags & LSA_STEP_THREE_CALLS)) {
+  const bool want_list = (d->flags & LSA_STEP_LISTED) ||
+                         (!(d->flags & LSA_STEP_THREE_CALLS) && p->n_fine >= LSA_HIER_LIST_MIN_SLOTS);
+  if (want_list) {
     const int k = lsa::score_emit_rank(p->n_fine, (int)rows, d->topk, d->rank, dt, lsa::select_list_stride(),
                                        lsa::select_list_max_segments(), lsa::select_list_max());
     if (k > 0) {

@@ -601,6 +601,8 @@ def prefill_score_workspace_bytes_for(L: int, Hkv: int, r: int, B: int,
 
 STEP_ONE_LAUNCH = 1   # lsa_step_desc.flags: the one persistent launch where the shape allows
 STEP_THREE_CALLS = 2  # lsa_step_desc.flags: the three calls, with the select's own collect launch
+STEP_LISTED = 4       # lsa_hier_step_desc.flags: the fine stage's listing launch wherever the shape allows
+HIER_LIST_MIN_SLOTS = 32768   # fine rows from which lsa_hier_decode_step lists by default
 
 
 def _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch=False,
@@ -774,7 +776,7 @@ def lsa_build_centroids(k_idx: torch.Tensor, block: int, out: torch.Tensor, *, s
 
 
 def _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, out_blocks, out_idx, out, lse, q_idx,
-               out_score, scale, three_calls):
+               out_score, scale, three_calls, listed=False):
     if q.dim() != 3 or not q.is_contiguous():
         raise ValueError("q must be contiguous [N,Hq,d]")
     N, Hq, hd = q.shape
@@ -812,7 +814,7 @@ def _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, out_blocks, o
     d.k, d.v, d.kv_dtype = _ptr(k), _ptr(v), _dt(k)
     d.kv_stride_seq, d.kv_stride_tok, d.kv_stride_head = k.stride(0), k.stride(1), k.stride(2)
     d.scale = scale
-    d.flags = STEP_THREE_CALLS if three_calls else 0
+    d.flags = (STEP_THREE_CALLS if three_calls else 0) | (STEP_LISTED if listed else 0)
     d.q_idx, d.out_blocks, d.out_idx, d.out_score, d.out, d.lse = (
         _ptr(q_idx), _ptr(out_blocks), _ptr(out_idx), _ptr(out_score), _ptr(out), _ptr(lse))
     return d
@@ -820,16 +822,19 @@ def _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, out_blocks, o
 
 def lsa_hier_decode_step(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept: int, out_idx, out, *,
                          out_blocks=None, lse=None, q_idx=None, out_score=None, scale: float = 0.0,
-                         workspace=None, stream=None, three_calls: bool = False) -> None:
+                         workspace=None, stream=None, three_calls: bool = False,
+                         listed: bool = False) -> None:
     """One coarse-to-fine decode step: centroids [N,Hkv,ceil(T/block),r]
     scored and the n_blocks_kept best blocks kept, their tokens scored and
     the top B (= out_idx.shape[-1]) attended. out_blocks int32
     [N,Hkv,n_blocks_kept] optional. workspace: uint8 of at least
     lsa_hier_step_workspace_bytes, all zero before its first use (allocated
     zeroed here when not given). three_calls: the fine stage as the
-    separate scoring and select calls."""
+    separate scoring and select calls (by default they run when the kept
+    blocks cover fewer than 32768 slots per row); listed: the listing
+    launch wherever the shape allows."""
     d = _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, out_blocks, out_idx, out, lse, q_idx,
-                   out_score, scale, three_calls)
+                   out_score, scale, three_calls, listed)
     lib = _lib()
     need = lib.lsa_hier_step_workspace_bytes(_c.byref(d))
     if need == 0:
@@ -842,9 +847,9 @@ def lsa_hier_decode_step(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept
 
 def lsa_hier_step_workspace_bytes(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept: int, out_idx,
                                   out, *, out_blocks=None, lse=None, q_idx=None, out_score=None,
-                                  scale: float = 0.0, three_calls: bool = False) -> int:
+                                  scale: float = 0.0, three_calls: bool = False, listed: bool = False) -> int:
     d = _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, out_blocks, out_idx, out, lse, q_idx,
-                   out_score, scale, three_calls)
+                   out_score, scale, three_calls, listed)
     return int(_lib().lsa_hier_step_workspace_bytes(_c.byref(d)))
 
 
@@ -853,7 +858,7 @@ def lsa_hier_step_path(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept: 
     """'listed' or 'three_calls': how the step runs its fine stage."""
     d = _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, kw.get("out_blocks"), out_idx, out,
                    kw.get("lse"), kw.get("q_idx"), kw.get("out_score"), kw.get("scale", 0.0),
-                   kw.get("three_calls", False))
+                   kw.get("three_calls", False), kw.get("listed", False))
     code = int(_lib().lsa_hier_step_path(_c.byref(d)))
     if code < 0:
         raise ValueError("lsa_hier_step_path: invalid descriptor")

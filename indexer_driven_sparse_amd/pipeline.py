@@ -181,10 +181,10 @@ class HierarchicalPlan:
 
     def __init__(self, N: int, Hq: int, Hkv: int, T: int, d: int, r: int, B: int, block: int,
                  B_coarse: int, device="cuda", kv_dtype=torch.bfloat16, kidx_dtype=None,
-                 fused: bool = True, three_calls: bool = False):
+                 fused: bool = True, three_calls: bool = False, listed: bool = False):
         self.N, self.Hq, self.Hkv, self.T, self.d, self.r = N, Hq, Hkv, T, d, r
         self.B, self.block, self.B_coarse = B, block, B_coarse
-        self.fused, self.three_calls = fused, three_calls
+        self.fused, self.three_calls, self.listed = fused, three_calls, listed
         self.step_ws = None
         self.n_blocks = (T + block - 1) // block
         f32 = dict(dtype=torch.float32, device=device)
@@ -214,7 +214,7 @@ class HierarchicalPlan:
     def step(self, q, w, k_idx, centroids, k, v, stream=None):
         """The whole step through one lsa_hier_decode_step call."""
         kw = dict(out_blocks=self.blocks, lse=self.lse, q_idx=self.q_idx, out_score=self.idx_scores,
-                  three_calls=self.three_calls)
+                  three_calls=self.three_calls, listed=self.listed)
         if self.step_ws is None:
             need = lsa.lsa_hier_step_workspace_bytes(q, w, k_idx, centroids, k, v, self.block, self.B_coarse,
                                                      self.idx, self.out, **kw)
@@ -224,7 +224,8 @@ class HierarchicalPlan:
 
     def path(self, q, w, k_idx, centroids, k, v) -> str:
         return lsa.lsa_hier_step_path(q, w, k_idx, centroids, k, v, self.block, self.B_coarse, self.idx,
-                                      self.out, out_blocks=self.blocks, three_calls=self.three_calls)
+                                      self.out, out_blocks=self.blocks, three_calls=self.three_calls,
+                                      listed=self.listed)
 
     def run(self, q, w, k_idx, centroids, k, v, stream=None):
         if self.fused:

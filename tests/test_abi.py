@@ -566,3 +566,26 @@ def test_binding_rejects_bad_hierarchical_step_buffers():
         kw.update(over)
         with pytest.raises(ValueError):
             build(kw)
+
+
+def test_hier_step_path_choice():
+    """lsa_hier_step_path (host-only planning, no device work): the default
+    runs the fine stage as separate calls on rows shorter than
+    LSA_HIER_LIST_MIN_SLOTS and lists it on longer ones; LSA_STEP_LISTED and
+    LSA_STEP_THREE_CALLS force a path; both together are invalid."""
+    import ctypes as c
+    import torch
+    N, Hq, Hkv, T, d, r, B, blk = 1, 32, 8, 131072, 128, 64, 2048, 64
+    q = torch.zeros(N, Hq, d, dtype=torch.bfloat16)
+    w = torch.zeros(d, r)
+    kx = torch.zeros(N, Hkv, T, r, dtype=torch.bfloat16)
+    cent = torch.zeros(N, Hkv, T // blk, r, dtype=torch.bfloat16)
+    k = torch.zeros(N, T, Hkv, d, dtype=torch.bfloat16)
+    oi = torch.zeros(N, Hkv, B, dtype=torch.int32)
+    out = torch.zeros(N, Hq, d)
+    assert lsa.HIER_LIST_MIN_SLOTS == 32768
+    cases = [(False, False, 128, 0), (True, False, 128, 0), (False, True, 128, 1),
+             (False, False, 512, 1), (True, False, 512, 0), (True, True, 128, -1)]
+    for three, listed, kept, want in cases:
+        dd = lsa._hier_desc(q, w, kx, cent, k, k, blk, kept, None, oi, out, None, None, None, 0.0, three, listed)
+        assert lsa._lib().lsa_hier_step_path(c.byref(dd)) == want, (three, listed, kept)

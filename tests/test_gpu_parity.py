@@ -1655,8 +1655,9 @@ def test_decode_step_fp8_cache(name, over):
                                            (100000, True, torch.float8_e4m3fn, 1),
                                            (60000, False, torch.bfloat16, 3)])
 def test_hier_step_equals_separate_calls(T, ties, kdt, N):
-    """lsa_hier_decode_step (the fine stage listed in its scoring launch,
-    and with LSA_STEP_THREE_CALLS) against the five separate calls:
+    """lsa_hier_decode_step (the fine stage listed in its scoring launch
+    with LSA_STEP_LISTED, as separate calls with LSA_STEP_THREE_CALLS, and
+    the default, which picks by row length) against the five separate calls:
     kept blocks, indices, per-entry scores, q_idx, out and lse bit for bit,
     twice on one workspace whose control words are left zero. T=100000 has
     a partial last block; with every key of a head equal every fine row
@@ -1678,9 +1679,11 @@ def test_hier_step_equals_separate_calls(T, ties, kdt, N):
     lsa.lsa_build_centroids(kd, blk, cd)
     ref = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, fused=False, kidx_dtype=kdt)
     ref.run(Qd, Wd, kd, cd, Kd, Vd)
-    for three in (False, True):
-        one = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, three_calls=three, kidx_dtype=kdt)
-        assert one.path(Qd, Wd, kd, cd, Kd, Vd) == ("three_calls" if three else "listed")
+    default_path = "listed" if Bc * blk >= lsa.HIER_LIST_MIN_SLOTS else "three_calls"
+    for mode, want_path in (("listed", "listed"), ("three", "three_calls"), ("default", default_path)):
+        one = pipeline.HierarchicalPlan(N, Hq, Hkv, T, d, r, B, blk, Bc, three_calls=mode == "three",
+                                        listed=mode == "listed", kidx_dtype=kdt)
+        assert one.path(Qd, Wd, kd, cd, Kd, Vd) == want_path
         for rep in range(2):
             one.idx.fill_(-9)
             one.out.fill_(5.0)
@@ -1688,10 +1691,10 @@ def test_hier_step_equals_separate_calls(T, ties, kdt, N):
             torch.cuda.synchronize()
             for name_ in ("blocks", "idx", "idx_scores", "q_idx", "out", "lse"):
                 a_, b_ = getattr(one, name_), getattr(ref, name_)
-                assert torch.equal(a_.view(torch.int32), b_.view(torch.int32)), (three, rep, name_)
+                assert torch.equal(a_.view(torch.int32), b_.view(torch.int32)), (mode, rep, name_)
             rows = N * Hkv
             ctl = one.step_ws[:4 * (1024 + 1024 * rows)].view(torch.int32)
-            assert int(ctl.abs().sum().item()) == 0, (three, rep)
+            assert int(ctl.abs().sum().item()) == 0, (mode, rep)
     if ties:   # a tie over the whole row keeps the lowest positions of the kept blocks
         gi, gb = host(one.idx), host(one.blocks)
         for g in range(Hkv):
