@@ -494,14 +494,16 @@ int lsa_step_path(const lsa_step_desc* desc);
  *     lsa_indexed_attention
  * on the same arguments: out_blocks, out_idx, q_idx, out_score bit-identical,
  * out / lse within the attention's own rounding. The attention merges its
- * splits in its own launch. By default the fine stage runs as the two
- * separate calls when the kept blocks cover fewer than
- * LSA_HIER_LIST_MIN_SLOTS slots per row (measured faster there: 57.1 against
- * 59.0 us per step at 128 blocks of 64), and otherwise its scoring launch
- * lists the final select's candidates (the listing path of lsa_decode_step,
- * over the candidate map) where the shape allows it. flags =
- * LSA_STEP_THREE_CALLS always runs the separate calls; LSA_STEP_LISTED takes
- * the listing launch wherever the shape allows it.
+ * splits in its own launch. Each stage (coarse over the block summaries,
+ * fine over the kept blocks' tokens, through the candidate map) runs either
+ * as its two separate calls or as one scoring launch that lists its
+ * select's candidates (the listing path of lsa_decode_step) followed by the
+ * select over the lists. By default a stage lists when its rows hold at
+ * least LSA_HIER_LIST_MIN_SLOTS slots and the shape allows it; on shorter
+ * rows the separate calls were measured faster (56.8 us per step at 16384
+ * summaries and 128 blocks of 64, against 59.0 with the fine stage listed
+ * and 64.7 with both). flags = LSA_STEP_THREE_CALLS always runs the separate
+ * calls; LSA_STEP_LISTED lists both stages wherever the shape allows it.
  * Asynchronous on `stream`; allocates nothing; one workspace
  * (lsa_hier_step_workspace_bytes, same descriptor), all zero before its
  * first use; every call leaves its control words zero again. Two calls
@@ -542,11 +544,11 @@ typedef struct lsa_hier_step_desc {
   float* lse;                /* optional out: fp32 [N,Hq] */
 } lsa_hier_step_desc;
 
-/* flags of lsa_hier_decode_step: the fine stage's listing launch wherever
- * the shape allows it, whatever the row length */
+/* flags of lsa_hier_decode_step: both stages' listing launches wherever
+ * the shape allows them, whatever the row length */
 #define LSA_STEP_LISTED 4
-/* fine-stage row length (n_blocks_kept * block) from which the default
- * path takes the listing launch */
+/* row length (slots: summaries for the coarse stage, n_blocks_kept * block
+ * for the fine stage) from which the default path lists a stage */
 #define LSA_HIER_LIST_MIN_SLOTS 32768
 
 int lsa_hier_decode_step(const lsa_hier_step_desc* desc, void* workspace, size_t workspace_bytes,
@@ -554,7 +556,8 @@ int lsa_hier_decode_step(const lsa_hier_step_desc* desc, void* workspace, size_t
 size_t lsa_hier_step_workspace_bytes(const lsa_hier_step_desc* desc);
 /* LSA_STEP_PATH_LISTED when the fine stage lists its candidates in the
  * scoring launch, LSA_STEP_PATH_THREE_CALLS when it runs the separate calls,
- * -1 for an invalid descriptor. */
+ * -1 for an invalid descriptor (the coarse stage follows the same rule on
+ * its own row length). */
 int lsa_hier_step_path(const lsa_hier_step_desc* desc);
 
 /* ------------------------------------------------------------------------ */

@@ -601,8 +601,8 @@ def prefill_score_workspace_bytes_for(L: int, Hkv: int, r: int, B: int,
 
 STEP_ONE_LAUNCH = 1   # lsa_step_desc.flags: the one persistent launch where the shape allows
 STEP_THREE_CALLS = 2  # lsa_step_desc.flags: the three calls, with the select's own collect launch
-STEP_LISTED = 4       # lsa_hier_step_desc.flags: the fine stage's listing launch wherever the shape allows
-HIER_LIST_MIN_SLOTS = 32768   # fine rows from which lsa_hier_decode_step lists by default
+STEP_LISTED = 4       # lsa_hier_step_desc.flags: both stages' listing launches wherever the shape allows
+HIER_LIST_MIN_SLOTS = 32768   # row length from which lsa_hier_decode_step lists a stage by default
 
 
 def _step_desc(q, w, k_idx, k, v, out_idx, out, lse, q_idx, out_score, scale, one_launch=False,
@@ -830,9 +830,9 @@ def lsa_hier_decode_step(q, w, k_idx, centroids, k, v, block: int, n_blocks_kept
     [N,Hkv,n_blocks_kept] optional. workspace: uint8 of at least
     lsa_hier_step_workspace_bytes, all zero before its first use (allocated
     zeroed here when not given). three_calls: the fine stage as the
-    separate scoring and select calls (by default they run when the kept
-    blocks cover fewer than 32768 slots per row); listed: the listing
-    launch wherever the shape allows."""
+    separate scoring and select calls in both stages (by default a stage
+    runs them when its rows hold fewer than 32768 slots); listed: both
+    stages' listing launches wherever the shape allows."""
     d = _hier_desc(q, w, k_idx, centroids, k, v, block, n_blocks_kept, out_blocks, out_idx, out, lse, q_idx,
                    out_score, scale, three_calls, listed)
     lib = _lib()

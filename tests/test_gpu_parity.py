@@ -1655,7 +1655,7 @@ def test_decode_step_fp8_cache(name, over):
                                            (100000, True, torch.float8_e4m3fn, 1),
                                            (60000, False, torch.bfloat16, 3)])
 def test_hier_step_equals_separate_calls(T, ties, kdt, N):
-    """lsa_hier_decode_step (the fine stage listed in its scoring launch
+    """lsa_hier_decode_step (both stages listed in their scoring launches
     with LSA_STEP_LISTED, as separate calls with LSA_STEP_THREE_CALLS, and
     the default, which picks by row length) against the five separate calls:
     kept blocks, indices, per-entry scores, q_idx, out and lse bit for bit,
