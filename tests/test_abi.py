@@ -589,3 +589,28 @@ def test_hier_step_path_choice():
     for three, listed, kept, want in cases:
         dd = lsa._hier_desc(q, w, kx, cent, k, k, blk, kept, None, oi, out, None, None, None, 0.0, three, listed)
         assert lsa._lib().lsa_hier_step_path(c.byref(dd)) == want, (three, listed, kept)
+
+
+def test_step_paths_and_flags_on_the_host():
+    """lsa_step_path (host-only planning): the flat decode step takes the
+    listing path by default at the headline shape, the three calls with
+    LSA_STEP_THREE_CALLS, and rejects flags it does not know, including
+    the hierarchical step's LSA_STEP_LISTED."""
+    import ctypes as c
+    import torch
+    N, Hq, Hkv, T, d, r, B = 4, 32, 8, 131072, 128, 64, 2048
+    q = torch.zeros(N, Hq, d, dtype=torch.bfloat16)
+    w = torch.zeros(d, r)
+    kx = torch.zeros(N, Hkv, T, r, dtype=torch.bfloat16)
+    k = torch.zeros(N, T, Hkv, d, dtype=torch.bfloat16)
+    oi = torch.zeros(N, Hkv, B, dtype=torch.int32)
+    out = torch.zeros(N, Hq, d)
+    lib = lsa._lib()
+    dd = lsa._step_desc(q, w, kx, k, k, oi, out, None, None, None, 0.0)
+    assert lib.lsa_step_path(c.byref(dd)) == 1                     # listed
+    dd = lsa._step_desc(q, w, kx, k, k, oi, out, None, None, None, 0.0, three_calls=True)
+    assert lib.lsa_step_path(c.byref(dd)) == 0                     # three calls
+    for bad in (lsa.STEP_LISTED, 8, 1 << 20):
+        dd = lsa._step_desc(q, w, kx, k, k, oi, out, None, None, None, 0.0)
+        dd.flags = bad
+        assert lib.lsa_step_path(c.byref(dd)) == -1, bad
