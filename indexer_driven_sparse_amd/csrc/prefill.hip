@@ -295,15 +295,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
       for (int c = 0; c < kCh; ++c) ka[c] = frag(kp, c, h);
     }
     for (int t = w; t < ntiles; t += 4) {
-      bf16x8 kc[kCh];
-#pragma unroll
-      for (int c = 0; c < kCh; ++c) kc[c] = ka[c];
-      if (t + 4 < ntiles) {   // the next tile's gathers fly during this one
+      // the products first, then the next tile's gathers into the same
+      // registers: they fly during this tile's histogram work
+      const f32x16 acc = tile_scores(ka, qb);
+      if (t + 4 < ntiles) {
         const uint16_t* kp = krow(a, g, sh.pos[min((t + 4) * kT + n, m - 1)]);
 #pragma unroll
         for (int c = 0; c < kCh; ++c) ka[c] = frag(kp, c, h);
       }
-      const f32x16 acc = tile_scores(kc, qb);
       const bool full = rows_in && (t + 1) * kT <= m && sh.pos[t * kT + kT - 1] <= i0;
       if (full) {
 #pragma unroll
